@@ -1,0 +1,199 @@
+"""Benchmark: one training step of a Llama-3-8B-shaped TP=8 MLP layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is the whole path for one batch: RMSNorm, for each of the 8 shards the
+gate/up GEMM with SwiGLU and the down GEMM to an fp32 partial, the forward
+partial sum with residual and bias, for each shard the four backward GEMMs,
+the backward partial sum, RMSNorm's backward, and SGD on every parameter.
+Inputs are resident in HBM before the timed region; SGD writes new parameter
+buffers so every timed step does identical work.
+
+Prints one JSON line.  `value` is the algorithmic GEMM TFLOP/s of the whole
+step (18 T H F_full flops per step for SwiGLU); per-kernel times come from
+HIP events the library records on its launch stream during the timed steps.
+The CPU oracle is timed on a bounded token slice of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd TFLOP/s per TP-shard SwiGLU MLP, % of bf16 MFMA peak; tokens/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def gemm_flops(w) -> dict:
+    """Algorithmic flops of one launch of each GEMM, by kernel name."""
+    T, H, F = w.tokens, w.hidden, w.ffn_local
+    if w.act == "swiglu":
+        return {"gemm_gate_up_swiglu": 2 * T * 2 * F * H, "gemm_down_partial": 2 * T * H * F,
+                "gemm_down_residual": 2 * T * H * F, "gemm_dact_swiglu_bwd": 2 * T * F * H,
+                "gemm_wgrad_down": 2 * H * F * T, "gemm_dgrad_normed": 2 * T * H * 2 * F,
+                "gemm_wgrad_gate_up": 2 * 2 * F * H * T}
+    return {"gemm_fc1_gelu": 2 * T * F * H, "gemm_down_partial": 2 * T * H * F, "gemm_down_residual": 2 * T * H * F,
+            "gemm_dact_gelu_bwd": 2 * T * F * H, "gemm_wgrad_down": 2 * H * F * T,
+            "gemm_dgrad_normed": 2 * T * H * F, "gemm_wgrad_fc1": 2 * F * H * T}
+
+
+def hbm_bytes_per_step(w) -> dict:
+    """Algorithmic HBM bytes per step of each bandwidth-bound kernel
+    (compulsory reads + writes of its operands), by kernel name."""
+    T, H, F, S = w.tokens, w.hidden, w.ffn_local, w.n_run
+    es = 2 if w.dtype == "bf16" else 4
+    n_params = H + H + S * (2 * F * H + H * F + (F if w.act == "gelu" else 0))
+    per_param = (4 + 4 + 4 + es) if w.master else (es + 4 + es)
+    return {
+        "rmsnorm_fwd": T * H * 2 * es + 4 * T + H * es,                 # x in, N out, rstd out, w in
+        "partial_sum_residual": S * 4 * T * H + 2 * es * T * H + H * es,  # S fp32 partials + x in, out
+        "partial_sum": S * 4 * T * H + 4 * T * H,                        # S fp32 partials in, dN out
+        "rmsnorm_bwd": T * H * (4 + 3 * es) + 4 * T + H * es,           # dN, x, dY in, dx out
+        "sgd": n_params * per_param,                                     # p (or master), g in; p (+master) out
+    }
+
+
+def roofline_entry(name, launches, total_ms, w, steps):
+    secs = total_ms / 1e3
+    fl = gemm_flops(w)
+    if name in fl:
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        ach = fl[name] * launches / secs / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
+                "per_launch": fl[name], "avg_ms": total_ms / launches, "launches": launches}
+    by = hbm_bytes_per_step(w)
+    if name in by:
+        ach = by[name] * steps / secs / 1e9
+        return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                "per_launch": by[name] * steps // launches, "avg_ms": total_ms / launches, "launches": launches}
+    return {"bound": None, "avg_ms": total_ms / launches, "launches": launches}
+
+
+def cpu_baseline(w, t, budget_s: float = 15.0) -> dict:
+    """The oracle as it stands (fp64 numpy, sharded step) on a token slice of
+    the workload, sized to roughly ``budget_s`` of CPU time."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from oracle.mlp import Params
+
+    c = synth.to_numpy64
+    p = Params(c(t["norm_w"]), c(t["w_in"]), c(t["w_down"]), c(t["b_down"]), c(t["b_in"]))
+    x = c(t["x"])
+
+    def run(tp):
+        t0 = time.perf_counter()
+        oracle.sharded_step(x[:tp], p, w.act, w.eps, w.lr, w.n_run)
+        return time.perf_counter() - t0
+
+    probe = min(64, w.tokens)
+    t_probe = run(probe)
+    tp = int(min(w.tokens, max(probe, (budget_s / max(t_probe, 1e-3)) * probe)))
+    tp = max(probe, (tp // 64) * 64)
+    secs = run(tp)
+    mult = 18 if w.act == "swiglu" else 12
+    flops = mult * tp * w.hidden * w.ffn_local * w.n_run
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        cores = 1
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"oracle.sharded_step (fp64 numpy) on the first {tp} of {w.tokens} tokens, all "
+                      f"{w.n_run} shards, full H and F; {secs:.2f} s; tokens/s {tp / secs:.1f}",
+            "host_cpus": os.cpu_count()}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b_tp8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the tensor-parallel shards are "
+                                   "processed in sequence on one device and there is no multi-GPU path",
+                          "n_gpus": args.gpus}), flush=True)
+        return 2
+
+    import torch
+
+    import synth
+    from tensor_transformer_mlp_rmsnorm_amd import _lib as L
+    from tensor_transformer_mlp_rmsnorm_amd.step import ShardedStep
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        return 1
+    torch.cuda.set_device(0)
+    w = synth.workload(args.workload)
+    t = synth.draw(w)
+    st = ShardedStep(w, t, device="cuda:0", out_of_place_sgd=True)
+    for _ in range(args.warmup):
+        st.step()
+    torch.cuda.synchronize()
+
+    L.tp_mlp_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        st.step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    L.tp_mlp_profile_enable(False)
+    prof = L.tp_mlp_profile_entries()
+
+    ms = elapsed / args.steps * 1e3
+    flops = w.flops_per_step
+    tflops = flops / (ms / 1e3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    kernels = {k: roofline_entry(k, n, tot, w, args.steps) for k, (n, tot) in prof.items()}
+    gemm_ms = sum(tot for k, (n, tot) in prof.items() if k in gemm_flops(w)) / args.steps
+    # dominant kernel: the largest total time in the timed region
+    dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
+    d = kernels[dom]
+    roof = {"kernel": dom, "bound": d.get("bound"), "achieved": d.get("achieved"), "peak": d.get("peak"),
+            "unit": d.get("unit"), "frac": d.get("frac"), "traffic": None,
+            "per_launch": d.get("per_launch"), "avg_ms": d.get("avg_ms")}
+    out = {
+        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
+                   "ffn_full": w.ffn_full, "ffn_local": w.ffn_local, "shards": w.shards, "shards_run": w.n_run,
+                   "act": w.act, "parallelism": f"tp{w.shards} emulated: shards in sequence on one GPU"},
+        "pct_of_bf16_peak": 100.0 * tflops / peak,
+        "tokens_per_s": w.tokens / (ms / 1e3),
+        "shard_tokens_per_s": w.tokens / (ms / 1e3 / w.n_run),
+        "flops_per_step": flops,
+        "gemm_ms_per_step": gemm_ms,
+        "gemm_tflops": flops / (gemm_ms / 1e3) / 1e12 if gemm_ms > 0 else None,
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        del st
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(w, t, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

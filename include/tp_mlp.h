@@ -1,0 +1,228 @@
+/*
+ * tp_mlp.h - C ABI of one tensor-parallel rank's share of the pre-RMSNorm
+ * MLP sublayer (forward, backward, SGD) on an AMD Instinct MI355X (gfx950).
+ *
+ * The block is the one rebuilt in "Megatron tensor-parallel MLP"
+ * (synapticradio.com), section "Start with the dense block":
+ *     N   = rms_norm(x, norm_w)
+ *     A   = SiLU(N Wg^T) * (N Wu^T)          (gate/up stacked as w_in[2, F, H])
+ *     out = x + A Wd^T + b_down              (Wd = w_down[H, F])
+ * and its GeLU variant from "Megatron-LM walkthrough", Part II:
+ *     A   = gelu(N W1^T + b1)                (w_in[F, H], b_in[F])
+ * A rank owns F = F_full / S channels of the FFN axis ("Split the expansion",
+ * "Split the contraction").  Its down projection yields a full-width
+ * partial; the partials are summed (the forward all-reduce), then residual
+ * and bias are added once.  In backward each rank's gradient of the
+ * replicated N is a partial that is summed (the backward all-reduce) before
+ * RMSNorm's backward ("Put the other collective in backward").  In this
+ * library both sums are tp_partial_sum, an on-device reduction over shard
+ * partials computed one after the other on the same GPU, never a collective.
+ *
+ * Conventions for every call
+ *   - All tensor arguments are DEVICE pointers, row-major and contiguous,
+ *     16-byte aligned, owned by the caller.  The library allocates no device
+ *     memory and keeps no device state between calls.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only
+ *     enqueue work on it and return; synchronisation is the caller's.
+ *   - Shapes: T = tokens (any value >= 0), H = hidden, F = ffn_local.  H and
+ *     F must be positive multiples of 8; H <= 16384.  T = 0 is a no-op.
+ *   - dtype TP_MLP_F32: every tensor fp32.  dtype TP_MLP_BF16: parameters and
+ *     activations bf16 (round to nearest even), accumulation fp32; partial
+ *     sums, rstd and every parameter gradient are fp32 in both cases.
+ *   - Return 0 on success or a negative TP_MLP_E* code; tp_mlp_last_error()
+ *     then describes the failure.  Argument errors are detected before any
+ *     work is enqueued.  No exception crosses the ABI.
+ */
+#ifndef TP_MLP_H
+#define TP_MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  TP_MLP_OK = 0,
+  TP_MLP_EINVAL = -1,     /* null pointer, negative size, bad enum */
+  TP_MLP_ESHAPE = -2,     /* H or F not a positive multiple of 8, H too large,
+                             F_full not divisible by the shard count */
+  TP_MLP_EDTYPE = -3,     /* unknown dtype / dtype combination */
+  TP_MLP_EALIGN = -4,     /* a pointer is not 16-byte aligned */
+  TP_MLP_EWORKSPACE = -5, /* workspace missing or smaller than required */
+  TP_MLP_EHIP = -6        /* the HIP runtime reported an error on launch */
+};
+
+enum { TP_MLP_ACT_SWIGLU = 0, TP_MLP_ACT_GELU = 1 };
+enum { TP_MLP_F32 = 0, TP_MLP_BF16 = 1 };
+
+/* tp_mlp_desc.flags */
+enum {
+  /* Forward: write out = x + z + b_down (act dtype) directly from the down
+   * projection instead of the fp32 partial z.  Only valid for an unsharded
+   * block (S = 1), where the partial sum has a single term. */
+  TP_MLP_FUSE_EPILOGUE = 1,
+  /* Forward: `normed` and `rstd` already hold rms_norm(x) from an earlier call
+   * with the same x and norm_w (the replicated input of another shard), so
+   * the norm is not recomputed. */
+  TP_MLP_NORMED_READY = 2
+};
+
+typedef struct {
+  int64_t tokens;    /* T */
+  int64_t hidden;    /* H */
+  int64_t ffn_local; /* F: channels of the FFN axis owned by this shard */
+  int32_t act;       /* TP_MLP_ACT_* */
+  int32_t dtype;     /* TP_MLP_F32 | TP_MLP_BF16 */
+  float eps;         /* RMSNorm epsilon, added to mean(x^2) under the root */
+  int32_t flags;     /* TP_MLP_FUSE_EPILOGUE | TP_MLP_NORMED_READY */
+} tp_mlp_desc;
+
+/*
+ * tp_mlp_forward - one shard's forward: RMSNorm, column-parallel expansion
+ * with its activation, row-parallel down projection.
+ *   ("Start with the dense block"; "Split the expansion"; "Split the
+ *    contraction", synapticradio.com)
+ *
+ *   x        [T, H]    dtype   block input; also the residual
+ *   norm_w   [H]       dtype   RMSNorm weight (replicated)
+ *   w_in     SwiGLU [2, F, H] (plane 0 gate, plane 1 up) | GeLU [F, H], dtype
+ *   b_in     GeLU: [F] dtype fc1 bias; SwiGLU: must be NULL
+ *   w_down   [H, F]    dtype   this shard's columns of the down weight
+ *   normed   [T, H]    dtype   out: N = x * rstd * norm_w (in, with NORMED_READY)
+ *   rstd     [T]       fp32    out: 1 / sqrt(mean_H(x^2) + eps) (in, with NORMED_READY)
+ *   pre_act  SwiGLU [T, 2F] (cols [0,F) gate, [F,2F) up) | GeLU [T, F], dtype
+ *                              out: pre-activations, saved for backward
+ *   act      [T, F]    dtype   out: SiLU(g) * u  |  gelu(h), saved for backward
+ *   out      without FUSE_EPILOGUE: [T, H] fp32, this shard's partial z = A Wd^T
+ *            with FUSE_EPILOGUE:    [T, H] dtype, x + z + b_down
+ *   b_down   [H] dtype; read only with FUSE_EPILOGUE (else may be NULL)
+ */
+int tp_mlp_forward(const tp_mlp_desc* d, const void* x, const void* norm_w, const void* w_in,
+                   const void* b_in, const void* w_down, void* normed, float* rstd,
+                   void* pre_act, void* act, void* out, const void* b_down, void* stream);
+
+/*
+ * tp_partial_sum - the sum that stands in for the all-reduce at the two
+ * tensor-parallel boundaries ("Split the contraction": partial outputs summed,
+ * then residual and bias added once; "Put the other collective in backward":
+ * the shards' gradients of N summed before RMSNorm's backward).
+ *
+ *   out[r, c] = ((parts[0][r,c] + parts[1][r,c]) + ...) + residual[r,c] + bias[c]
+ *
+ *   parts     HOST array of n_parts DEVICE pointers, each [rows, cols] fp32;
+ *             summed in index order with fp32 accumulation (deterministic).
+ *             1 <= n_parts <= 64.  No part is written.
+ *   residual  [rows, cols] in `in_dtype`, or NULL
+ *   bias      [cols] in `in_dtype`, or NULL
+ *   out       [rows, cols] in `out_dtype` (TP_MLP_F32 or TP_MLP_BF16); may
+ *             not alias a part.
+ *   cols must be a multiple of 4.
+ */
+int tp_partial_sum(const float* const* parts, int32_t n_parts, int64_t rows, int64_t cols,
+                   const void* residual, const void* bias, int32_t in_dtype, void* out,
+                   int32_t out_dtype, void* stream);
+
+/* Backward phases (see tp_mlp_backward). */
+enum { TP_MLP_BWD_SHARD = 0, TP_MLP_BWD_NORM = 1 };
+
+typedef struct {
+  /* saved from tp_mlp_forward */
+  const void* x;          /* [T, H]  dtype */
+  const void* normed;     /* [T, H]  dtype */
+  const float* rstd;      /* [T]     fp32  */
+  const void* pre_act;    /* [T, 2F] | [T, F] dtype */
+  const void* act;        /* [T, F]  dtype */
+  /* parameters */
+  const void* norm_w;     /* [H] dtype */
+  const void* w_in;       /* [2, F, H] | [F, H] dtype */
+  const void* w_down;     /* [H, F] dtype */
+  /* upstream gradient of the block output, [T, H] dtype (with the page's
+     loss sum(out^2)/2 this is out itself) */
+  const void* d_out;
+  /* SHARD phase outputs */
+  void* d_pre;            /* [T, 2F] | [T, F] dtype: gradient of the pre-activations */
+  float* d_w_in;          /* [2, F, H] | [F, H] fp32 */
+  float* d_b_in;          /* GeLU: [F] fp32; SwiGLU: NULL */
+  float* d_w_down;        /* [H, F] fp32 */
+  float* d_normed_part;   /* [T, H] fp32: this shard's partial of dL/dN */
+  /* NORM phase input and outputs */
+  const float* d_normed;  /* [T, H] fp32: dL/dN summed over shards */
+  void* d_x;              /* [T, H] dtype */
+  float* d_norm_w;        /* [H] fp32 */
+  float* d_b_down;        /* [H] fp32 */
+  /* scratch for deterministic column reductions, caller-owned */
+  void* workspace;
+  size_t workspace_bytes;
+} tp_mlp_bwd_args;
+
+/*
+ * tp_mlp_backward - the backward of tp_mlp_forward, in two phases split at
+ * the backward all-reduce ("Put the other collective in backward": the sum of
+ * the shards' dN must happen before RMSNorm's backward).
+ *
+ * phase TP_MLP_BWD_SHARD (per shard, before the sum):
+ *   d_act        = d_out Wd                         (the forward sum's backward is the identity)
+ *   d_pre        = SwiGLU: dg = d_act * u * s(g) (1 + g (1 - s(g))), du = d_act * SiLU(g)
+ *                  GeLU:   dh = d_act * gelu'(h)
+ *   d_w_down     = d_out^T act
+ *   d_w_in       = d_pre^T normed          (fp32, [2F, H] rows gate then up | [F, H])
+ *   d_b_in       = sum_t dh                (GeLU only)
+ *   d_normed_part= d_pre w_in              (fp32 partial, summed by tp_partial_sum)
+ *   This phase reads normed, pre_act, act, w_in, w_down and d_out.
+ * phase TP_MLP_BWD_NORM (once, after the sum):
+ *   c_t      = (1/H) sum_i d_normed[t,i] norm_w[i] x[t,i]
+ *   d_x      = d_out + rstd d_normed norm_w - x rstd^3 c        (residual + RMSNorm)
+ *   d_norm_w = sum_t d_normed x rstd,   d_b_down = sum_t d_out
+ * Column sums are reduced in a fixed order (run-to-run deterministic).
+ * Workspace: at least tp_mlp_workspace_bytes(d, phase) bytes.
+ */
+int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* a, void* stream);
+
+/* Bytes of workspace tp_mlp_backward needs for this descriptor and phase. */
+size_t tp_mlp_workspace_bytes(const tp_mlp_desc* d, int32_t phase);
+
+/*
+ * tp_mlp_sgd_step - one plain SGD update, p <- p - lr * g (the page's one SGD
+ * update of every parameter, "Reproduce one dense training step").
+ *   param_in  [n] in param_dtype, param_out [n] in param_dtype (may equal
+ *             param_in: in-place); grad [n] fp32.
+ *   master_in == NULL: param_out = round(param_in - lr * grad), in fp32.
+ *   master_in != NULL: fp32 master copies, master_out = master_in - lr * grad
+ *             and param_out = round_bf16(master_out); param_dtype must be BF16
+ *             and master_out non-NULL (may equal master_in).
+ *   n >= 0 (n = 0 is a no-op).  Partially overlapping in/out ranges are an
+ *   error only in the sense that results are then undefined.
+ */
+int tp_mlp_sgd_step(const void* param_in, void* param_out, const float* grad, const float* master_in,
+                    float* master_out, int64_t n, int32_t param_dtype, float lr, void* stream);
+
+/*
+ * Kernel timing, a measurement aid (off by default).  While enabled, every
+ * kernel the library launches is bracketed by two hipEvents recorded on the
+ * launch's own stream; durations are aggregated per kernel name.
+ *   tp_mlp_profile_enable(1) clears earlier records and starts recording;
+ *   tp_mlp_profile_enable(0) stops recording (records are kept).
+ *   tp_mlp_profile_count() waits for the recorded events and returns the
+ *   number of distinct kernel names (or a negative error code);
+ *   tp_mlp_profile_entry(i, ...) returns entry i: name (valid until the next
+ *   enable(1) or count call), number of launches and total milliseconds.
+ * Event recording adds a few microseconds per launch; leave it off outside
+ * measurements.
+ */
+int tp_mlp_profile_enable(int32_t on);
+int32_t tp_mlp_profile_count(void);
+int tp_mlp_profile_entry(int32_t i, const char** name, int64_t* launches, double* total_ms);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* tp_mlp_last_error(void);
+
+/* Library version string. */
+const char* tp_mlp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_MLP_H */

@@ -33,3 +33,4 @@ from .mlp import (  # noqa: F401
     row_forward_backward,
     MODES,
 )
+from .sampled import sampled_step  # noqa: F401,E402

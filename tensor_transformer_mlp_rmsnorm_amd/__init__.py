@@ -1,0 +1,25 @@
+"""One tensor-parallel rank's share of the pre-RMSNorm MLP sublayer on MI355X.
+
+The compute lives in ``libtpmlp.so`` (HIP kernels for gfx950 behind the C
+ABI of ``include/tp_mlp.h``).  ``_lib`` binds its entry points under the same
+names; ``step`` sequences them over the shards of one training step.
+Importing this package does not load the library; the first call does, and
+raises if it has not been built.
+"""
+
+from ._lib import (  # noqa: F401
+    TPMLPError,
+    tp_mlp_forward,
+    tp_partial_sum,
+    tp_mlp_backward,
+    tp_mlp_workspace_bytes,
+    tp_mlp_sgd_step,
+    tp_mlp_last_error,
+    tp_mlp_version,
+    make_desc,
+)
+
+__all__ = [
+    "TPMLPError", "tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_workspace_bytes",
+    "tp_mlp_sgd_step", "tp_mlp_last_error", "tp_mlp_version", "make_desc",
+]

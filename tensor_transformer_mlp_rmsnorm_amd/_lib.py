@@ -1,0 +1,178 @@
+"""ctypes binding of libtpmlp (include/tp_mlp.h): argument marshalling only.
+
+Each function takes torch tensors (device memory) or ints and calls the C
+entry point of the same name on the current HIP stream.  A non-zero return
+code raises TPMLPError with the library's message.  There is no fallback:
+if the shared library is missing, loading raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpmlp.so")
+
+OK, EINVAL, ESHAPE, EDTYPE, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
+ACT_SWIGLU, ACT_GELU = 0, 1
+F32, BF16 = 0, 1
+FUSE_EPILOGUE, NORMED_READY = 1, 2
+BWD_SHARD, BWD_NORM = 0, 1
+
+# every symbol include/tp_mlp.h declares
+EXPORTED = ("tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_workspace_bytes",
+            "tp_mlp_sgd_step", "tp_mlp_last_error", "tp_mlp_version", "tp_mlp_profile_enable",
+            "tp_mlp_profile_count", "tp_mlp_profile_entry")
+
+
+class TPMLPError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libtpmlp error {code}: {msg}")
+        self.code = code
+
+
+class tp_mlp_desc(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("hidden", ctypes.c_int64), ("ffn_local", ctypes.c_int64),
+                ("act", ctypes.c_int32), ("dtype", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("flags", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+
+
+class tp_mlp_bwd_args(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("x", "normed", "rstd", "pre_act", "act", "norm_w", "w_in", "w_down", "d_out",
+                                   "d_pre", "d_w_in", "d_b_in", "d_w_down", "d_normed_part", "d_normed", "d_x",
+                                   "d_norm_w", "d_b_down", "workspace")] + [("workspace_bytes", ctypes.c_size_t)]
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtpmlp.so (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m tensor_transformer_mlp_rmsnorm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.tp_mlp_forward.argtypes = [ctypes.POINTER(tp_mlp_desc)] + [_vp] * 12
+        L.tp_mlp_forward.restype = ctypes.c_int
+        L.tp_partial_sum.argtypes = [ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, _vp, _vp,
+                                     ctypes.c_int32, _vp, ctypes.c_int32, _vp]
+        L.tp_partial_sum.restype = ctypes.c_int
+        L.tp_mlp_backward.argtypes = [ctypes.POINTER(tp_mlp_desc), ctypes.c_int32, ctypes.POINTER(tp_mlp_bwd_args),
+                                      _vp]
+        L.tp_mlp_backward.restype = ctypes.c_int
+        L.tp_mlp_workspace_bytes.argtypes = [ctypes.POINTER(tp_mlp_desc), ctypes.c_int32]
+        L.tp_mlp_workspace_bytes.restype = ctypes.c_size_t
+        L.tp_mlp_sgd_step.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, _vp]
+        L.tp_mlp_sgd_step.restype = ctypes.c_int
+        L.tp_mlp_last_error.argtypes = []
+        L.tp_mlp_last_error.restype = ctypes.c_char_p
+        L.tp_mlp_version.argtypes = []
+        L.tp_mlp_version.restype = ctypes.c_char_p
+        L.tp_mlp_profile_enable.argtypes = [ctypes.c_int32]
+        L.tp_mlp_profile_enable.restype = ctypes.c_int
+        L.tp_mlp_profile_count.argtypes = []
+        L.tp_mlp_profile_count.restype = ctypes.c_int32
+        L.tp_mlp_profile_entry.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_char_p),
+                                           ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
+        L.tp_mlp_profile_entry.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _check(rc: int) -> None:
+    if rc != OK:
+        raise TPMLPError(rc, lib().tp_mlp_last_error().decode())
+
+
+def make_desc(tokens: int, hidden: int, ffn_local: int, act: int, dtype: int, eps: float,
+              flags: int = 0) -> tp_mlp_desc:
+    return tp_mlp_desc(tokens, hidden, ffn_local, act, dtype, eps, flags)
+
+
+def tp_mlp_forward(desc: tp_mlp_desc, x, norm_w, w_in, b_in, w_down, normed, rstd, pre_act, act, out,
+                   b_down=None, stream=None) -> None:
+    _check(lib().tp_mlp_forward(ctypes.byref(desc), _ptr(x), _ptr(norm_w), _ptr(w_in), _ptr(b_in), _ptr(w_down),
+                                _ptr(normed), _ptr(rstd), _ptr(pre_act), _ptr(act), _ptr(out), _ptr(b_down),
+                                _stream(stream)))
+
+
+def tp_partial_sum(parts: Sequence, rows: int, cols: int, residual, bias, in_dtype: int, out, out_dtype: int,
+                   stream=None) -> None:
+    arr = (_vp * max(1, len(parts)))(*[_ptr(p) for p in parts])
+    _check(lib().tp_partial_sum(arr, len(parts), rows, cols, _ptr(residual), _ptr(bias), in_dtype, _ptr(out),
+                                out_dtype, _stream(stream)))
+
+
+def tp_mlp_workspace_bytes(desc: tp_mlp_desc, phase: int) -> int:
+    return int(lib().tp_mlp_workspace_bytes(ctypes.byref(desc), phase))
+
+
+def tp_mlp_backward(desc: tp_mlp_desc, phase: int, stream=None, **tensors) -> None:
+    """``tensors`` are the fields of tp_mlp_bwd_args (torch tensors or None);
+    ``workspace`` may be given, ``workspace_bytes`` defaults to its size."""
+    a = tp_mlp_bwd_args()
+    for name, _ in tp_mlp_bwd_args._fields_:
+        if name == "workspace_bytes":
+            continue
+        v = tensors.pop(name, None)
+        setattr(a, name, _ptr(v))
+        if name == "workspace" and v is not None and not isinstance(v, int):
+            a.workspace_bytes = v.numel() * v.element_size()
+    if "workspace_bytes" in tensors:
+        a.workspace_bytes = tensors.pop("workspace_bytes")
+    if tensors:
+        raise TypeError(f"unknown backward arguments: {sorted(tensors)}")
+    _check(lib().tp_mlp_backward(ctypes.byref(desc), phase, ctypes.byref(a), _stream(stream)))
+
+
+def tp_mlp_sgd_step(param_in, param_out, grad, master_in, master_out, n: int, param_dtype: int, lr: float,
+                    stream=None) -> None:
+    _check(lib().tp_mlp_sgd_step(_ptr(param_in), _ptr(param_out), _ptr(grad), _ptr(master_in), _ptr(master_out),
+                                 n, param_dtype, lr, _stream(stream)))
+
+
+def tp_mlp_last_error() -> str:
+    return lib().tp_mlp_last_error().decode()
+
+
+def tp_mlp_version() -> str:
+    return lib().tp_mlp_version().decode()
+
+
+def tp_mlp_profile_enable(on: bool) -> None:
+    _check(lib().tp_mlp_profile_enable(1 if on else 0))
+
+
+def tp_mlp_profile_entries() -> dict:
+    """{kernel name: (launches, total_ms)} of the recorded launches."""
+    n = lib().tp_mlp_profile_count()
+    if n < 0:
+        _check(n)
+    out = {}
+    for i in range(n):
+        name, cnt, ms = ctypes.c_char_p(), ctypes.c_int64(), ctypes.c_double()
+        _check(lib().tp_mlp_profile_entry(i, ctypes.byref(name), ctypes.byref(cnt), ctypes.byref(ms)))
+        out[name.value.decode()] = (int(cnt.value), float(ms.value))
+    return out

@@ -1,0 +1,303 @@
+// C ABI of libtpmlp (declared in include/tp_mlp.h): argument checking and the
+// sequence of kernel launches for each call.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/tp_mlp.h"
+#include "kernels.h"
+
+using namespace tpmlp;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(TP_MLP_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                              \
+  do {                                                                              \
+    if (!(p)) return fail(TP_MLP_EINVAL, "%s: argument '%s' is NULL", fn, #p);      \
+    if (!aligned16(p)) return fail(TP_MLP_EALIGN, "%s: '%s' is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+#define CHECK_HIP(expr, where)                  \
+  do {                                          \
+    const hipError_t e_ = (expr);               \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+int check_desc(const tp_mlp_desc* d, const char* fn) {
+  if (!d) return fail(TP_MLP_EINVAL, "%s: descriptor is NULL", fn);
+  if (d->tokens < 0) return fail(TP_MLP_EINVAL, "%s: tokens < 0", fn);
+  if (d->hidden <= 0 || d->hidden % 8) return fail(TP_MLP_ESHAPE, "%s: hidden must be a positive multiple of 8", fn);
+  if (d->hidden > 16384) return fail(TP_MLP_ESHAPE, "%s: hidden > 16384 is not supported", fn);
+  if (d->ffn_local <= 0 || d->ffn_local % 8)
+    return fail(TP_MLP_ESHAPE, "%s: ffn_local must be a positive multiple of 8", fn);
+  if (d->act != TP_MLP_ACT_SWIGLU && d->act != TP_MLP_ACT_GELU) return fail(TP_MLP_EINVAL, "%s: unknown act", fn);
+  if (d->dtype != TP_MLP_F32 && d->dtype != TP_MLP_BF16) return fail(TP_MLP_EDTYPE, "%s: unknown dtype", fn);
+  if (d->flags & ~(TP_MLP_FUSE_EPILOGUE | TP_MLP_NORMED_READY)) return fail(TP_MLP_EINVAL, "%s: unknown flags", fn);
+  if (!(d->eps >= 0.0f)) return fail(TP_MLP_EINVAL, "%s: eps must be >= 0", fn);
+  // Element counts stay below 2^31 so per-tensor int arithmetic in the
+  // launchers is safe; byte offsets are 64-bit throughout.
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t T = d->tokens, H = d->hidden, F = d->ffn_local;
+  if (T * H >= lim || T * 2 * F >= lim || 2 * F * H >= lim)
+    return fail(TP_MLP_ESHAPE, "%s: a tensor would hold 2^31 or more elements", fn);
+  return TP_MLP_OK;
+}
+
+DType dt_of(int32_t d) { return d == TP_MLP_BF16 ? kBF16 : kF32; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_mlp_last_error(void) { return g_err; }
+
+const char* tp_mlp_version(void) { return "libtpmlp 0.1 gfx950"; }
+
+int tp_mlp_forward(const tp_mlp_desc* d, const void* x, const void* norm_w, const void* w_in, const void* b_in,
+                   const void* w_down, void* normed, float* rstd, void* pre_act, void* act, void* out,
+                   const void* b_down, void* stream) {
+  const char* fn = "tp_mlp_forward";
+  g_err[0] = 0;
+  int rc = check_desc(d, fn);
+  if (rc) return rc;
+  const int64_t T = d->tokens, H = d->hidden, F = d->ffn_local;
+  const bool swiglu = d->act == TP_MLP_ACT_SWIGLU;
+  const bool fuse = d->flags & TP_MLP_FUSE_EPILOGUE;
+  REQUIRE_PTR(norm_w);
+  REQUIRE_PTR(w_in);
+  REQUIRE_PTR(w_down);
+  if (swiglu && b_in) return fail(TP_MLP_EINVAL, "%s: b_in must be NULL for SwiGLU", fn);
+  if (!swiglu) REQUIRE_PTR(b_in);
+  if (fuse) REQUIRE_PTR(b_down);
+  if (T == 0) return TP_MLP_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(normed);
+  REQUIRE_PTR(rstd);
+  REQUIRE_PTR(pre_act);
+  REQUIRE_PTR(act);
+  REQUIRE_PTR(out);
+  const DType dt = dt_of(d->dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (!(d->flags & TP_MLP_NORMED_READY))
+    CHECK_HIP(launch_rmsnorm_fwd(dt, x, norm_w, normed, rstd, T, H, d->eps, s), "rmsnorm forward");
+
+  // Expansion: [T, H] x [2F | F, H]^T with the activation fused.
+  GemmArgs g{};
+  g.M = T;
+  g.N = swiglu ? 2 * F : F;
+  g.K = H;
+  g.A = normed;
+  g.lda = H;
+  g.B = w_in;
+  g.ldb = H;
+  g.pre = pre_act;
+  g.act = act;
+  g.bias = b_in;
+  g.ffn = F;
+  g.tag = swiglu ? "gemm_gate_up_swiglu" : "gemm_fc1_gelu";
+  CHECK_HIP(launch_gemm(dt, true, true, swiglu ? kEpiSwigluFwd : kEpiGeluFwd, g, s), "expansion GEMM");
+
+  // Contraction: [T, F] x [H, F]^T -> fp32 partial, or x + z + b_down.
+  GemmArgs c{};
+  c.M = T;
+  c.N = H;
+  c.K = F;
+  c.A = act;
+  c.lda = F;
+  c.B = w_down;
+  c.ldb = F;
+  c.C = out;
+  c.ldc = H;
+  c.aux = x;
+  c.bias = b_down;
+  c.ffn = F;
+  c.tag = fuse ? "gemm_down_residual" : "gemm_down_partial";
+  CHECK_HIP(launch_gemm(dt, true, true, fuse ? kEpiResidual : kEpiStoreF32, c, s), "down GEMM");
+  return TP_MLP_OK;
+}
+
+int tp_partial_sum(const float* const* parts, int32_t n_parts, int64_t rows, int64_t cols, const void* residual,
+                   const void* bias, int32_t in_dtype, void* out, int32_t out_dtype, void* stream) {
+  const char* fn = "tp_partial_sum";
+  g_err[0] = 0;
+  if (!parts) return fail(TP_MLP_EINVAL, "%s: parts is NULL", fn);
+  if (n_parts < 1 || n_parts > 64) return fail(TP_MLP_EINVAL, "%s: n_parts must be in [1, 64]", fn);
+  if (rows < 0 || cols < 0) return fail(TP_MLP_EINVAL, "%s: negative size", fn);
+  if (cols % 4) return fail(TP_MLP_ESHAPE, "%s: cols must be a multiple of 4", fn);
+  if ((in_dtype != TP_MLP_F32 && in_dtype != TP_MLP_BF16) || (out_dtype != TP_MLP_F32 && out_dtype != TP_MLP_BF16))
+    return fail(TP_MLP_EDTYPE, "%s: unknown dtype", fn);
+  if (rows == 0 || cols == 0) return TP_MLP_OK;
+  REQUIRE_PTR(out);
+  for (int i = 0; i < n_parts; ++i) {
+    if (!parts[i]) return fail(TP_MLP_EINVAL, "%s: parts[%d] is NULL", fn, i);
+    if (!aligned16(parts[i])) return fail(TP_MLP_EALIGN, "%s: parts[%d] is not 16-byte aligned", fn, i);
+    if ((const void*)parts[i] == out) return fail(TP_MLP_EINVAL, "%s: out aliases parts[%d]", fn, i);
+  }
+  if (residual && !aligned16(residual)) return fail(TP_MLP_EALIGN, "%s: residual is not 16-byte aligned", fn);
+  if (bias && !aligned16(bias)) return fail(TP_MLP_EALIGN, "%s: bias is not 16-byte aligned", fn);
+  CHECK_HIP(launch_partial_sum(parts, n_parts, rows, cols, residual, bias, dt_of(in_dtype), out, dt_of(out_dtype),
+                               static_cast<hipStream_t>(stream)),
+            "partial sum");
+  return TP_MLP_OK;
+}
+
+size_t tp_mlp_workspace_bytes(const tp_mlp_desc* d, int32_t phase) {
+  if (!d || d->tokens < 0 || d->hidden <= 0 || d->ffn_local <= 0) return 0;
+  if (phase == TP_MLP_BWD_NORM) return rmsnorm_bwd_workspace(d->tokens, d->hidden);
+  if (phase == TP_MLP_BWD_SHARD && d->act == TP_MLP_ACT_GELU) return colsum_workspace(d->tokens, d->ffn_local);
+  return 0;
+}
+
+int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* a, void* stream) {
+  const char* fn = "tp_mlp_backward";
+  g_err[0] = 0;
+  int rc = check_desc(d, fn);
+  if (rc) return rc;
+  if (!a) return fail(TP_MLP_EINVAL, "%s: args is NULL", fn);
+  if (phase != TP_MLP_BWD_SHARD && phase != TP_MLP_BWD_NORM) return fail(TP_MLP_EINVAL, "%s: unknown phase", fn);
+  const int64_t T = d->tokens, H = d->hidden, F = d->ffn_local;
+  const bool swiglu = d->act == TP_MLP_ACT_SWIGLU;
+  const DType dt = dt_of(d->dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t need = tp_mlp_workspace_bytes(d, phase);
+  if (need > 0) {
+    if (!a->workspace || a->workspace_bytes < need)
+      return fail(TP_MLP_EWORKSPACE, "%s: workspace of %zu bytes required, %zu given", fn, need,
+                  a->workspace ? a->workspace_bytes : (size_t)0);
+    if (!aligned16(a->workspace)) return fail(TP_MLP_EALIGN, "%s: workspace is not 16-byte aligned", fn);
+  }
+
+  if (phase == TP_MLP_BWD_NORM) {
+    REQUIRE_PTR(a->norm_w);
+    REQUIRE_PTR(a->d_norm_w);
+    REQUIRE_PTR(a->d_b_down);
+    if (T > 0) {
+      REQUIRE_PTR(a->d_normed);
+      REQUIRE_PTR(a->x);
+      REQUIRE_PTR(a->d_out);
+      REQUIRE_PTR(a->rstd);
+      REQUIRE_PTR(a->d_x);
+    }
+    CHECK_HIP(launch_rmsnorm_bwd(dt, a->d_normed, a->x, a->d_out, a->rstd, a->norm_w, a->d_x, a->d_norm_w,
+                                 a->d_b_down, a->workspace, T, H, s),
+              "rmsnorm backward");
+    return TP_MLP_OK;
+  }
+
+  // SHARD phase
+  REQUIRE_PTR(a->w_in);
+  REQUIRE_PTR(a->w_down);
+  REQUIRE_PTR(a->d_w_in);
+  REQUIRE_PTR(a->d_w_down);
+  if (!swiglu) REQUIRE_PTR(a->d_b_in);
+  if (swiglu && a->d_b_in) return fail(TP_MLP_EINVAL, "%s: d_b_in must be NULL for SwiGLU", fn);
+  if (T > 0) {
+    REQUIRE_PTR(a->d_out);
+    REQUIRE_PTR(a->normed);
+    REQUIRE_PTR(a->pre_act);
+    REQUIRE_PTR(a->act);
+    REQUIRE_PTR(a->d_pre);
+    REQUIRE_PTR(a->d_normed_part);
+  }
+  const int64_t P = swiglu ? 2 * F : F;  // width of pre-activations
+
+  // d_act = d_out Wd ([T,H] x [H,F]), with the activation backward fused.
+  GemmArgs b1{};
+  b1.M = T;
+  b1.N = F;
+  b1.K = H;
+  b1.A = a->d_out;
+  b1.lda = H;
+  b1.B = a->w_down;
+  b1.ldb = F;
+  b1.pre = a->d_pre;
+  b1.aux = a->pre_act;
+  b1.ffn = F;
+  b1.tag = swiglu ? "gemm_dact_swiglu_bwd" : "gemm_dact_gelu_bwd";
+  CHECK_HIP(launch_gemm(dt, true, false, swiglu ? kEpiSwigluBwd : kEpiGeluBwd, b1, s), "d_act GEMM");
+
+  // d_w_down = d_out^T act ([H,T] x [T,F]).
+  GemmArgs b2{};
+  b2.M = H;
+  b2.N = F;
+  b2.K = T;
+  b2.A = a->d_out;
+  b2.lda = H;
+  b2.B = a->act;
+  b2.ldb = F;
+  b2.C = a->d_w_down;
+  b2.ldc = F;
+  b2.tag = "gemm_wgrad_down";
+  CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b2, s), "d_w_down GEMM");
+
+  // d_normed partial = d_pre w_in ([T,P] x [P,H]).
+  GemmArgs b3{};
+  b3.M = T;
+  b3.N = H;
+  b3.K = P;
+  b3.A = a->d_pre;
+  b3.lda = P;
+  b3.B = a->w_in;
+  b3.ldb = H;
+  b3.C = a->d_normed_part;
+  b3.ldc = H;
+  b3.tag = "gemm_dgrad_normed";
+  CHECK_HIP(launch_gemm(dt, true, false, kEpiStoreF32, b3, s), "d_normed GEMM");
+
+  // d_w_in = d_pre^T normed ([P,T] x [T,H]).
+  GemmArgs b4{};
+  b4.M = P;
+  b4.N = H;
+  b4.K = T;
+  b4.A = a->d_pre;
+  b4.lda = P;
+  b4.B = a->normed;
+  b4.ldb = H;
+  b4.C = a->d_w_in;
+  b4.ldc = H;
+  b4.tag = swiglu ? "gemm_wgrad_gate_up" : "gemm_wgrad_fc1";
+  CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b4, s), "d_w_in GEMM");
+
+  if (!swiglu) CHECK_HIP(launch_colsum(dt, a->d_pre, a->d_b_in, a->workspace, T, F, s), "d_b_in column sum");
+  return TP_MLP_OK;
+}
+
+int tp_mlp_sgd_step(const void* param_in, void* param_out, const float* grad, const float* master_in,
+                    float* master_out, int64_t n, int32_t param_dtype, float lr, void* stream) {
+  const char* fn = "tp_mlp_sgd_step";
+  g_err[0] = 0;
+  if (n < 0) return fail(TP_MLP_EINVAL, "%s: n < 0", fn);
+  if (param_dtype != TP_MLP_F32 && param_dtype != TP_MLP_BF16) return fail(TP_MLP_EDTYPE, "%s: unknown dtype", fn);
+  if (master_in && param_dtype != TP_MLP_BF16)
+    return fail(TP_MLP_EDTYPE, "%s: a master copy is only used with bf16 parameters", fn);
+  if (n == 0) return TP_MLP_OK;
+  REQUIRE_PTR(param_in);
+  REQUIRE_PTR(param_out);
+  REQUIRE_PTR(grad);
+  if (master_in) {
+    REQUIRE_PTR(master_in);
+    REQUIRE_PTR(master_out);
+  }
+  CHECK_HIP(launch_sgd(dt_of(param_dtype), param_in, param_out, grad, master_in, master_out, n, lr,
+                       static_cast<hipStream_t>(stream)),
+            "sgd");
+  return TP_MLP_OK;
+}
+
+}  // extern "C"

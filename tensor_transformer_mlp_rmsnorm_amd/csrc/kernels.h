@@ -1,0 +1,84 @@
+// Host-side launchers of the libtpmlp kernels.  Argument checking happens in
+// api.hip before any of these is called; the launchers assume valid shapes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+enum DType { kF32 = 0, kBF16 = 1 };
+
+// Brackets one kernel launch with HIP events on its stream while kernel
+// timing is switched on (tp_mlp_profile_enable); a no-op otherwise.
+class KernelTimer {
+ public:
+  KernelTimer(const char* name, hipStream_t s);
+  ~KernelTimer();
+  KernelTimer(const KernelTimer&) = delete;
+  KernelTimer& operator=(const KernelTimer&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
+  bool active_ = false;
+};
+
+// Epilogues of the MFMA GEMM.
+enum Epi {
+  kEpiStoreF32 = 0,   // C fp32
+  kEpiSwigluFwd = 1,  // pre = [g | u] (T), act = SiLU(g) * u (T); B tile pairs gate/up channels
+  kEpiGeluFwd = 2,    // h = acc + b_in (T), act = gelu(h) (T)
+  kEpiResidual = 3,   // out = acc + x + b_down (T)
+  kEpiSwigluBwd = 4,  // d_pre = [dg | du] from d_act = acc and saved [g | u]
+  kEpiGeluBwd = 5,    // dh = d_act * gelu'(h)
+};
+
+// Operand layouts: A is [M, K] when a_kcontig, else [K, M]; B is [N, K] when
+// b_kcontig, else [K, N].  Leading dimensions are in elements.
+struct GemmArgs {
+  int64_t M, N, K;
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  // epilogue operands (meaning per Epi)
+  void* C;        // kEpiStoreF32: fp32 C [M, ldc]; kEpiResidual: out [M, ldc]
+  int64_t ldc;
+  void* pre;      // SwiGLU/GeLU fwd: pre-activations out; bwd: d_pre out
+  void* act;      // fwd: activation out
+  const void* aux;   // SwiGLU/GeLU bwd: saved pre-activations; residual: x
+  const void* bias;  // GeLU fwd: b_in [N]; residual: b_down [N]
+  int64_t ffn;       // F (column offset of the up half in [T, 2F] tensors)
+  const char* tag;   // kernel name for timing
+};
+
+hipError_t launch_gemm(DType dt, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs& g,
+                       hipStream_t s);
+
+hipError_t launch_rmsnorm_fwd(DType dt, const void* x, const void* w, void* n, float* rstd,
+                              int64_t T, int64_t H, float eps, hipStream_t s);
+
+// RMSNorm backward + residual: dx, and per-block column partials of
+// d_norm_w and d_b_down in `ws` followed by the fixed-order reduction.
+size_t rmsnorm_bwd_workspace(int64_t T, int64_t H);
+hipError_t launch_rmsnorm_bwd(DType dt, const float* dN, const void* x, const void* dY,
+                              const float* rstd, const void* w, void* dx, float* dw, float* db,
+                              void* ws, int64_t T, int64_t H, hipStream_t s);
+
+// Column sums of a [rows, cols] matrix in dtype dt into fp32 out[cols], in a
+// fixed order (two stages through `ws`).
+size_t colsum_workspace(int64_t rows, int64_t cols);
+hipError_t launch_colsum(DType dt, const void* in, float* out, void* ws, int64_t rows, int64_t cols,
+                         hipStream_t s);
+
+hipError_t launch_partial_sum(const float* const* parts, int n_parts, int64_t rows, int64_t cols,
+                              const void* residual, const void* bias, DType in_dt, void* out,
+                              DType out_dt, hipStream_t s);
+
+hipError_t launch_sgd(DType dt, const void* param_in, void* param_out, const float* grad, const float* master_in,
+                      float* master_out, int64_t n, float lr, hipStream_t s);
+
+}  // namespace tpmlp

@@ -1,0 +1,247 @@
+"""One training step of the tensor-parallel MLP sublayer on one GPU.
+
+The S shards of the FFN axis are run one after the other on the same device.
+Each shard's work is exactly one tensor-parallel rank's share; the two
+all-reduces of the method become tp_partial_sum at the same two points
+("Split the contraction" and "Put the other collective in backward",
+"Megatron tensor-parallel MLP", synapticradio.com):
+
+  forward   shard s: tp_mlp_forward -> fp32 partial z_s
+            out = tp_partial_sum(z_0..z_{S-1}) + x + b_down          (forward boundary)
+  backward  shard s: tp_mlp_backward(SHARD, d_out = out) -> dN_s and the shard's weight grads
+            dN  = tp_partial_sum(dN_0..dN_{S-1})                      (backward boundary)
+            tp_mlp_backward(NORM) -> dx, d_norm_w, d_b_down
+  update    tp_mlp_sgd_step on every parameter tensor
+
+Work that every rank repeats on replicated data (the RMSNorm forward, the
+RMSNorm backward, the update of norm_w and b_down) is done once here: its
+result is the same on every rank.  With S = 1 there is nothing to sum: the
+down projection writes x + z + b_down directly and dN_0 is dN.
+
+The ablations of "Remove each collective" are modes of the same driver:
+"missing_forward_reduce" gives each shard its own out_s = x + z_s + b_down
+(its own loss and backward; the backward sum is kept), and
+"missing_backward_reduce" feeds each shard's own dN_s into the RMSNorm
+backward.  Every arithmetic step runs in libtpmlp's kernels; this module only
+allocates device memory (through PyTorch) and sequences the C calls.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, List, Optional
+
+import torch
+
+from . import _lib as L
+
+MODES = ("equivalence", "missing_forward_reduce", "missing_backward_reduce")
+
+
+def _torch_dtype(name: str):
+    return {"bf16": torch.bfloat16, "fp32": torch.float32}[name]
+
+
+class ShardedStep:
+    """Device buffers and the call sequence of one step of a workload.
+
+    ``w`` is a ``synth.Workload`` (tokens, hidden, ffn_full, shards, act,
+    dtype, eps, lr, master, n_run); ``tensors`` the dense CPU tensors of
+    ``synth.draw``.  With ``out_of_place_sgd`` the update writes new
+    parameter buffers and leaves the inputs unchanged, so repeated steps do
+    identical work (benchmarking); otherwise parameters update in place.
+    """
+
+    def __init__(self, w, tensors: Dict[str, torch.Tensor], device="cuda", out_of_place_sgd: bool = False,
+                 stream: Optional[torch.cuda.Stream] = None):
+        self.w = w
+        self.dev = torch.device(device)
+        self.stream = stream
+        self.dt = _torch_dtype(w.dtype)
+        self.cdt = L.BF16 if w.dtype == "bf16" else L.F32
+        self.act = L.ACT_SWIGLU if w.act == "swiglu" else L.ACT_GELU
+        self.swiglu = w.act == "swiglu"
+        T, H, F = w.tokens, w.hidden, w.ffn_local
+        if w.ffn_full % w.shards:
+            raise ValueError("ffn_full must be divisible by shards")
+        self.T, self.H, self.F = T, H, F
+        self.fuse = w.shards == 1
+        self.oop = out_of_place_sgd
+        dev, dt, f32 = self.dev, self.dt, torch.float32
+        up = lambda t: None if t is None else t.to(dev).contiguous()
+        emp = lambda shape, d=dt: torch.empty(shape, dtype=d, device=dev)
+
+        self.x = up(tensors["x"])
+        self.norm_w = up(tensors["norm_w"])
+        self.b_down = up(tensors["b_down"])
+        P = 2 * F if self.swiglu else F
+        self.shards: List[dict] = []
+        for s in range(w.n_run):
+            lo, hi = s * F, (s + 1) * F
+            sh = {}
+            sh["w_in"] = up(tensors["w_in"][:, lo:hi, :] if self.swiglu else tensors["w_in"][lo:hi, :])
+            sh["w_down"] = up(tensors["w_down"][:, lo:hi])
+            sh["b_in"] = None if self.swiglu else up(tensors["b_in"][lo:hi])
+            sh["pre"] = emp((T, P))
+            sh["act"] = emp((T, F))
+            sh["z"] = None if self.fuse else emp((T, H), f32)
+            sh["d_pre"] = emp((T, P))
+            sh["d_w_in"] = emp(sh["w_in"].shape, f32)
+            sh["d_b_in"] = None if self.swiglu else emp((F,), f32)
+            sh["d_w_down"] = emp((H, F), f32)
+            sh["dN_part"] = emp((T, H), f32)
+            self.shards.append(sh)
+        self.normed = emp((T, H))
+        self.rstd = emp((T,), f32)
+        self.out = emp((T, H))
+        self.dN = self.shards[0]["dN_part"] if self.fuse else emp((T, H), f32)
+        self.dx = emp((T, H))
+        self.d_norm_w = emp((H,), f32)
+        self.d_b_down = emp((H,), f32)
+
+        # fp32 master copies of every parameter (exact upcasts of the bf16 values)
+        self.masters = None
+        if w.master:
+            self.masters = {}
+            for name, t in self._param_list():
+                self.masters[name] = t.float().clone()
+        # targets of the update
+        self.new = {}
+        self.new_masters = {}
+        for name, t in self._param_list():
+            self.new[name] = torch.empty_like(t) if self.oop else t
+            if self.masters is not None:
+                self.new_masters[name] = torch.empty_like(self.masters[name]) if self.oop else self.masters[name]
+
+        ws = max(L.tp_mlp_workspace_bytes(self._desc(), L.BWD_NORM),
+                 L.tp_mlp_workspace_bytes(self._desc(), L.BWD_SHARD), 16)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        # per-shard outputs of the ablation modes, allocated on first use
+        self._abl: Dict[str, list] = {}
+
+    # ------------------------------------------------------------ helpers
+    def _desc(self, flags: int = 0) -> L.tp_mlp_desc:
+        w = self.w
+        return L.make_desc(self.T, self.H, self.F, self.act, self.cdt, w.eps, flags)
+
+    def _param_list(self):
+        out = [("norm_w", self.norm_w), ("b_down", self.b_down)]
+        for s, sh in enumerate(self.shards):
+            out.append((f"w_in.{s}", sh["w_in"]))
+            out.append((f"w_down.{s}", sh["w_down"]))
+            if sh["b_in"] is not None:
+                out.append((f"b_in.{s}", sh["b_in"]))
+        return out
+
+    def _grad_of(self, name: str) -> torch.Tensor:
+        if name == "norm_w":
+            return self.d_norm_w
+        if name == "b_down":
+            return self.d_b_down
+        key, s = name.split(".")
+        return self.shards[int(s)]["d_" + key]
+
+    def _abl_bufs(self, name, shape, dtype):
+        if name not in self._abl:
+            self._abl[name] = [torch.empty(shape, dtype=dtype, device=self.dev) for _ in self.shards]
+        return self._abl[name]
+
+    # -------------------------------------------------------------- phases
+    def forward(self, mode: str = "equivalence") -> None:
+        T, H = self.T, self.H
+        st = self.stream
+        for s, sh in enumerate(self.shards):
+            flags = (L.NORMED_READY if s > 0 else 0) | (L.FUSE_EPILOGUE if self.fuse else 0)
+            L.tp_mlp_forward(self._desc(flags), self.x, self.norm_w, sh["w_in"], sh["b_in"], sh["w_down"],
+                             self.normed, self.rstd, sh["pre"], sh["act"], self.out if self.fuse else sh["z"],
+                             self.b_down, stream=st)
+        if self.fuse:
+            return
+        if mode == "missing_forward_reduce":
+            outs = self._abl_bufs("out", (T, H), self.dt)
+            for sh, o in zip(self.shards, outs):
+                L.tp_partial_sum([sh["z"]], T, H, self.x, self.b_down, self.cdt, o, self.cdt, stream=st)
+        else:
+            L.tp_partial_sum([sh["z"] for sh in self.shards], T, H, self.x, self.b_down, self.cdt, self.out,
+                             self.cdt, stream=st)
+
+    def _shard_backward(self, sh, d_out) -> None:
+        L.tp_mlp_backward(self._desc(), L.BWD_SHARD, stream=self.stream, normed=self.normed, pre_act=sh["pre"],
+                          act=sh["act"], w_in=sh["w_in"], w_down=sh["w_down"], d_out=d_out, d_pre=sh["d_pre"],
+                          d_w_in=sh["d_w_in"], d_b_in=sh["d_b_in"], d_w_down=sh["d_w_down"],
+                          d_normed_part=sh["dN_part"], workspace=self.workspace)
+
+    def _norm_backward(self, dN, d_out, dx, d_norm_w, d_b_down) -> None:
+        L.tp_mlp_backward(self._desc(), L.BWD_NORM, stream=self.stream, x=self.x, rstd=self.rstd,
+                          norm_w=self.norm_w, d_out=d_out, d_normed=dN, d_x=dx, d_norm_w=d_norm_w,
+                          d_b_down=d_b_down, workspace=self.workspace)
+
+    def backward(self, mode: str = "equivalence") -> None:
+        T, H = self.T, self.H
+        fwd_abl = mode == "missing_forward_reduce" and not self.fuse
+        outs = self._abl["out"] if fwd_abl else [self.out] * len(self.shards)
+        for sh, o in zip(self.shards, outs):
+            self._shard_backward(sh, o)
+        if not self.fuse and mode != "missing_backward_reduce":
+            L.tp_partial_sum([sh["dN_part"] for sh in self.shards], T, H, None, None, L.F32, self.dN, L.F32,
+                             stream=self.stream)
+        if mode == "equivalence" or self.fuse:
+            self._norm_backward(self.dN, self.out, self.dx, self.d_norm_w, self.d_b_down)
+            return
+        dxs = self._abl_bufs("dx", (T, H), self.dt)
+        dws = self._abl_bufs("d_norm_w", (H,), torch.float32)
+        dbs = self._abl_bufs("d_b_down", (H,), torch.float32)
+        for s, sh in enumerate(self.shards):
+            dN = self.dN if fwd_abl else sh["dN_part"]
+            self._norm_backward(dN, outs[s], dxs[s], dws[s], dbs[s])
+
+    def sgd(self) -> None:
+        lr = self.w.lr
+        for name, t in self._param_list():
+            g = self._grad_of(name)
+            if self.masters is not None:
+                L.tp_mlp_sgd_step(t, self.new[name], g, self.masters[name], self.new_masters[name], t.numel(),
+                                  self.cdt, lr, stream=self.stream)
+            else:
+                L.tp_mlp_sgd_step(t, self.new[name], g, None, None, t.numel(), self.cdt, lr, stream=self.stream)
+
+    def step(self, mode: str = "equivalence", update: bool = True) -> None:
+        self.forward(mode)
+        self.backward(mode)
+        if update and mode == "equivalence":
+            self.sgd()
+
+    # ------------------------------------------------------------- results
+    def results(self, mode: str = "equivalence") -> dict:
+        """CPU copies of the step's outputs, shard slices re-assembled along
+        the FFN axis.  In ablation modes out/dx/d_norm_w/d_b_down are lists
+        over shards."""
+        c = lambda t: t.detach().float().cpu()
+        r = {"normed": c(self.normed), "rstd": c(self.rstd)}
+        cat_in = (lambda ts: torch.cat(ts, dim=1)) if self.swiglu else (lambda ts: torch.cat(ts, dim=0))
+        r["d_w_in"] = cat_in([c(sh["d_w_in"]) for sh in self.shards])
+        r["d_w_down"] = torch.cat([c(sh["d_w_down"]) for sh in self.shards], dim=1)
+        if not self.swiglu:
+            r["d_b_in"] = torch.cat([c(sh["d_b_in"]) for sh in self.shards])
+        r["act"] = torch.cat([c(sh["act"]) for sh in self.shards], dim=1)
+        r["dN_parts"] = [c(sh["dN_part"]) for sh in self.shards]
+        if mode == "equivalence" or self.fuse:
+            r.update(out=c(self.out), dx=c(self.dx), d_norm_w=c(self.d_norm_w), d_b_down=c(self.d_b_down),
+                     dN=c(self.dN))
+        else:
+            r["out"] = [c(o) for o in self._abl["out"]] if mode == "missing_forward_reduce" else c(self.out)
+            r["dx"] = [c(t) for t in self._abl["dx"]]
+            r["d_norm_w"] = [c(t) for t in self._abl["d_norm_w"]]
+            r["d_b_down"] = [c(t) for t in self._abl["d_b_down"]]
+        new = {name: c(self.new[name]) for name, _ in self._param_list()}
+        n = len(self.shards)
+        r["new_norm_w"], r["new_b_down"] = new["norm_w"], new["b_down"]
+        r["new_w_in"] = cat_in([new[f"w_in.{s}"] for s in range(n)])
+        r["new_w_down"] = torch.cat([new[f"w_down.{s}"] for s in range(n)], dim=1)
+        if not self.swiglu:
+            r["new_b_in"] = torch.cat([new[f"b_in.{s}"] for s in range(n)])
+        if self.masters is not None:
+            nm = {name: c(self.new_masters[name]) for name, _ in self._param_list()}
+            r["master_norm_w"], r["master_b_down"] = nm["norm_w"], nm["b_down"]
+            r["master_w_in"] = cat_in([nm[f"w_in.{s}"] for s in range(n)])
+            r["master_w_down"] = torch.cat([nm[f"w_down.{s}"] for s in range(n)], dim=1)
+        return r

@@ -1,0 +1,150 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The shared library loads, exports every function include/tp_mlp.h declares,
+and rejects bad arguments with the documented codes.  Every call here fails
+argument validation (or is a documented no-op) before any HIP call, so the
+dummy pointer values below are never dereferenced or passed to a kernel.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tensor_transformer_mlp_rmsnorm_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_mlp.h")
+
+A = 0x10000  # an aligned dummy address, never dereferenced
+MIS = 0x10008  # misaligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(tp_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail(f"{L.LIB_PATH} not built; run python -m tensor_transformer_mlp_rmsnorm_amd.build")
+    return L.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTED), names
+    raw = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version(lib):
+    assert "gfx950" in L.tp_mlp_version()
+
+
+def _desc(T=16, H=64, F=32, act=L.ACT_SWIGLU, dt=L.BF16, eps=1e-6, flags=0):
+    return L.make_desc(T, H, F, act, dt, eps, flags)
+
+
+def _fwd(desc, **kw):
+    args = dict(x=A, norm_w=A, w_in=A, b_in=None, w_down=A, normed=A, rstd=A, pre_act=A, act=A, out=A, b_down=A)
+    args.update(kw)
+    return lib_call("tp_mlp_forward", ctypes.byref(desc), *[args[k] for k in
+                    ("x", "norm_w", "w_in", "b_in", "w_down", "normed", "rstd", "pre_act", "act", "out", "b_down")],
+                    None)
+
+
+def lib_call(name, *args):
+    return getattr(L.lib(), name)(*args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=60), L.ESHAPE),
+    (dict(H=0), L.ESHAPE),
+    (dict(H=16392), L.ESHAPE),
+    (dict(F=12), L.ESHAPE),
+    (dict(T=-1), L.EINVAL),
+    (dict(dt=7), L.EDTYPE),
+    (dict(act=3), L.EINVAL),
+    (dict(flags=8), L.EINVAL),
+    (dict(eps=-1.0), L.EINVAL),
+    (dict(T=1 << 20, H=4096), L.ESHAPE),  # 2^32 elements in [T, H]
+])
+def test_forward_rejects_bad_descriptor(lib, kw, code):
+    assert _fwd(_desc(**kw)) == code
+    assert L.tp_mlp_last_error() != ""
+
+
+def test_forward_pointer_checks(lib):
+    assert lib.tp_mlp_forward(None, *([A] * 11), None) == L.EINVAL
+    assert _fwd(_desc(), x=None) == L.EINVAL
+    assert _fwd(_desc(), w_in=MIS) == L.EALIGN
+    assert _fwd(_desc(), b_in=A) == L.EINVAL          # SwiGLU takes no fc1 bias
+    assert _fwd(_desc(act=L.ACT_GELU), b_in=None) == L.EINVAL
+    assert _fwd(_desc(flags=L.FUSE_EPILOGUE), b_down=None) == L.EINVAL
+    # T = 0 is a documented no-op: succeeds without touching any buffer
+    assert _fwd(_desc(T=0), x=None, normed=None, out=None) == L.OK
+
+
+def _parts(ptrs):
+    return (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+
+
+def test_partial_sum_checks(lib):
+    f = lib.tp_partial_sum
+    assert f(None, 1, 4, 8, None, None, L.F32, A, L.F32, None) == L.EINVAL
+    assert f(_parts([A]), 0, 4, 8, None, None, L.F32, A, L.F32, None) == L.EINVAL
+    assert f(_parts([A] * 65), 65, 4, 8, None, None, L.F32, A, L.F32, None) == L.EINVAL
+    assert f(_parts([A]), 1, 4, 6, None, None, L.F32, A + 4096, L.F32, None) == L.ESHAPE
+    assert f(_parts([A]), 1, 4, 8, None, None, 5, A + 4096, L.F32, None) == L.EDTYPE
+    assert f(_parts([A]), 1, 4, 8, None, None, L.F32, A, L.F32, None) == L.EINVAL    # out aliases a part
+    assert f(_parts([MIS]), 1, 4, 8, None, None, L.F32, A, L.F32, None) == L.EALIGN
+    assert f(_parts([None]), 1, 4, 8, None, None, L.F32, A, L.F32, None) == L.EINVAL
+    assert f(_parts([A]), 1, 4, 8, MIS, None, L.F32, A + 4096, L.F32, None) == L.EALIGN
+    assert f(_parts([A]), 1, 0, 8, None, None, L.F32, A + 4096, L.F32, None) == L.OK  # empty: no-op
+
+
+def test_backward_checks(lib):
+    d = _desc(T=128, act=L.ACT_GELU)
+    need = L.tp_mlp_workspace_bytes(d, L.BWD_SHARD)
+    assert need > 0
+    assert L.tp_mlp_workspace_bytes(d, L.BWD_NORM) > 0
+    assert L.tp_mlp_workspace_bytes(_desc(T=128), L.BWD_SHARD) == 0
+    a = L.tp_mlp_bwd_args()
+    for name, _ in L.tp_mlp_bwd_args._fields_:
+        if name != "workspace_bytes":
+            setattr(a, name, A)
+    a.workspace_bytes = need - 16
+    assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EWORKSPACE
+    a.workspace_bytes = need
+    assert lib.tp_mlp_backward(ctypes.byref(d), 5, ctypes.byref(a), None) == L.EINVAL
+    assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_SHARD, None, None) == L.EINVAL
+    a.d_w_in = MIS
+    assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EALIGN
+    a.d_w_in = A
+    a.d_b_in = None
+    assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EINVAL
+    # NORM phase without a workspace
+    a.workspace = None
+    assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EWORKSPACE
+    assert "workspace" in L.tp_mlp_last_error()
+
+
+def test_sgd_checks(lib):
+    f = lib.tp_mlp_sgd_step
+    assert f(A, A, A, None, None, -1, L.BF16, 0.1, None) == L.EINVAL
+    assert f(A, A, A, None, None, 8, 9, 0.1, None) == L.EDTYPE
+    assert f(A, A, A, A, A, 8, L.F32, 0.1, None) == L.EDTYPE      # masters only with bf16
+    assert f(A, A, A, A, None, 8, L.BF16, 0.1, None) == L.EINVAL  # master_in without master_out
+    assert f(MIS, A, A, None, None, 8, L.BF16, 0.1, None) == L.EALIGN
+    assert f(None, None, None, None, None, 0, L.BF16, 0.1, None) == L.OK  # n = 0: no-op
+
+
+def test_binding_raises_with_message(lib):
+    with pytest.raises(L.TPMLPError) as ei:
+        L.tp_partial_sum([A], 4, 6, None, None, L.F32, A + 4096, L.F32, stream=0)
+    assert ei.value.code == L.ESHAPE and "multiple of 4" in str(ei.value)

@@ -1,0 +1,262 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small cases are compared element by element on every output of the step;
+they span several 128 x 128 tiles and ragged tails in every dimension.  The
+full-size workloads run in the same configuration bench.py times
+(ShardedStep with out-of-place SGD) and are compared on the whole output and
+on sampled rows, channels and columns that the oracle computes exactly
+(oracle.sampled_step).  Tolerances: tests/tolerance.py.
+"""
+
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.mlp import Params
+from tolerance import check
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tensor_transformer_mlp_rmsnorm_amd import _lib
+    _lib.lib()  # must load: there is no fallback
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def np_params(t) -> Params:
+    c = synth.to_numpy64
+    return Params(c(t["norm_w"]), c(t["w_in"]), c(t["w_down"]), c(t["b_down"]), c(t["b_in"]))
+
+
+def run_gpu(w, t, mode="equivalence", oop=True):
+    from tensor_transformer_mlp_rmsnorm_amd.step import ShardedStep
+    say(f"[gpu] {w.name} T={w.tokens} H={w.hidden} F_full={w.ffn_full} S={w.shards} {w.act} {w.dtype} mode={mode}")
+    st = ShardedStep(w, t, out_of_place_sgd=oop)
+    st.step(mode)
+    torch.cuda.synchronize()
+    return st
+
+
+def compare_full(w, res, d, report):
+    """Every output of an equivalence step against oracle.dense_step."""
+    dt = w.dtype
+    g, npar = d["grads"], d["new_params"]
+    check("out", res["out"], d["out"], dt, rowwise=True, report=report)
+    check("normed", res["normed"], d["n"], dt, rowwise=True, report=report)
+    check("act", res["act"], d["a"], dt, rowwise=True, report=report)
+    check("dN", res["dN"], d["dN"], dt, rowwise=True, report=report)
+    check("dx", res["dx"], d["dx"], dt, rowwise=True, report=report)
+    check("d_norm_w", res["d_norm_w"], g["norm_w"], dt, report=report)
+    check("d_b_down", res["d_b_down"], g["b_down"], dt, report=report)
+    check("d_w_in", res["d_w_in"], g["w_in"], dt, report=report)
+    check("d_w_down", res["d_w_down"], g["w_down"], dt, report=report)
+    check("new_norm_w", res["new_norm_w"], npar.norm_w, dt, report=report)
+    check("new_b_down", res["new_b_down"], npar.b_down, dt, report=report)
+    check("new_w_in", res["new_w_in"], npar.w_in, dt, report=report)
+    check("new_w_down", res["new_w_down"], npar.w_down, dt, report=report)
+    if w.act == "gelu":
+        check("d_b_in", res["d_b_in"], g["b_in"], dt, report=report)
+        check("new_b_in", res["new_b_in"], npar.b_in, dt, report=report)
+    if w.master:
+        check("master_w_in", res["master_w_in"], npar.w_in, dt, report=report)
+        check("master_w_down", res["master_w_down"], npar.w_down, dt, report=report)
+
+
+def run_small(w, perturb=True):
+    t = synth.draw(w, perturb=perturb)
+    st = run_gpu(w, t)
+    res = st.results()
+    prec = np.float64 if w.dtype == "fp32" else np.float32
+    d = oracle.dense_step(synth.to_numpy64(t["x"]), np_params(t), w.act, w.eps, w.lr, dtype=prec)
+    report = {}
+    compare_full(w, res, d, report)
+    say(f"  worst: {max(report.items(), key=lambda kv: kv[1])}")
+    return st, res
+
+
+# ------------------------------------------------------------ the tiny fp32 workload
+
+def test_tiny_fp32_equivalence():
+    """Tiny fp32 block (T=4, H=8, F=16, two shards): every tensor within max-abs 1e-5 of the fp64 oracle."""
+    run_small(synth.workload("tiny_fp32_tp2"), perturb=False)
+
+
+@pytest.mark.parametrize("mode", ["missing_forward_reduce", "missing_backward_reduce"])
+def test_tiny_fp32_ablations_match_oracle(mode):
+    """The GPU path with one boundary sum dropped gives the oracle's ablated
+    results, and differs from the dense step where the page says it does."""
+    w = synth.workload("tiny_fp32_tp2")
+    t = synth.draw(w)
+    st = run_gpu(w, t, mode=mode)
+    res = st.results(mode)
+    x, p = synth.to_numpy64(t["x"]), np_params(t)
+    sh = oracle.sharded_step(x, p, w.act, w.eps, w.lr, w.shards, mode=mode)
+    dense = oracle.dense_step(x, p, w.act, w.eps, w.lr)
+    for s, rk in enumerate(sh["ranks"]):
+        out_s = res["out"][s] if mode == "missing_forward_reduce" else res["out"]
+        check(f"out[{s}]", out_s, rk["out"], "fp32")
+        check(f"dx[{s}]", res["dx"][s], rk["dx"], "fp32")
+        check(f"d_norm_w[{s}]", res["d_norm_w"][s], rk["grads"]["norm_w"], "fp32")
+        check(f"d_b_down[{s}]", res["d_b_down"][s], rk["grads"]["b_down"], "fp32")
+    gap = lambda a, b: float(np.max(np.abs(np.asarray(a, dtype=np.float64) - b)))
+    if mode == "missing_forward_reduce":
+        assert max(gap(o, dense["out"]) for o in res["out"]) > 1e-5
+    else:
+        assert gap(res["out"], dense["out"]) < 1e-5
+        assert max(gap(dx, dense["dx"]) for dx in res["dx"]) > 1e-5
+        assert max(gap(dw, dense["grads"]["norm_w"]) for dw in res["d_norm_w"]) > 1e-5
+        # the local weight gradients are unaffected by the backward ablation
+        check("d_w_in", res["d_w_in"], dense["grads"]["w_in"], "fp32")
+        check("d_w_down", res["d_w_down"], dense["grads"]["w_down"], "fp32")
+
+
+# ------------------------------------------------------------- multi-tile, ragged
+
+SMALL = [
+    # name,                        T,   H,   F_full, S, act,      dtype
+    ("fp32_swiglu_ragged_S2", 257, 136, 144, 2, "swiglu", "fp32"),
+    ("fp32_gelu_ragged_S1", 131, 72, 200, 1, "gelu", "fp32"),
+    ("bf16_swiglu_ragged_S3", 300, 256, 384, 3, "swiglu", "bf16"),
+    ("bf16_swiglu_S1_fused", 200, 128, 136, 1, "swiglu", "bf16"),
+    ("bf16_gelu_ragged_S1", 333, 192, 520, 1, "gelu", "bf16"),
+    ("bf16_gelu_S2", 129, 264, 272, 2, "gelu", "bf16"),
+    ("bf16_swiglu_S8_thin", 65, 64, 128, 8, "swiglu", "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_parity(case):
+    name, T, H, Ff, S, act, dt = case
+    base = synth.Workload(name, tokens=T, hidden=H, ffn_full=Ff, shards=S, act=act, dtype=dt, w_std=0.05,
+                          seed=100 + T)
+    run_small(base)
+
+
+def test_master_weights_small():
+    """fp32 master weights: masters take the update, bf16 copies are their rounding."""
+    w = synth.Workload("bf16_master_small", tokens=96, hidden=64, ffn_full=72, shards=1, act="swiglu",
+                       dtype="bf16", w_std=0.05, seed=5, master=True, outlier_frac=0.05)
+    st, res = run_small(w)
+    assert torch.equal(res["new_w_in"], res["master_w_in"].to(torch.bfloat16).float())
+    assert torch.equal(res["new_norm_w"], res["master_norm_w"].to(torch.bfloat16).float())
+
+
+def test_step_is_deterministic():
+    w = synth.Workload("det", tokens=190, hidden=128, ffn_full=256, shards=2, act="swiglu", dtype="bf16",
+                       w_std=0.05, seed=9)
+    t = synth.draw(w, perturb=True)
+    r1 = run_gpu(w, t).results()
+    r2 = run_gpu(w, t).results()
+    for k in ("out", "dx", "d_w_in", "d_w_down", "d_norm_w", "d_b_down", "new_w_in"):
+        assert torch.equal(r1[k], r2[k]), k
+
+
+def test_empty_tokens():
+    """T = 0: nothing to compute; every gradient is an empty sum (zero) and the update leaves parameters as they were."""
+    w = synth.Workload("empty", tokens=0, hidden=64, ffn_full=64, shards=2, act="swiglu", dtype="bf16",
+                       w_std=0.05, seed=3)
+    t = synth.draw(w, perturb=True)
+    res = run_gpu(w, t).results()
+    for k in ("d_w_in", "d_w_down", "d_norm_w", "d_b_down"):
+        assert torch.count_nonzero(res[k]) == 0, k
+    assert torch.equal(res["new_w_in"], t["w_in"].float())
+    assert torch.equal(res["new_norm_w"], t["norm_w"].float())
+    assert res["out"].shape == (0, 64)
+
+
+def test_single_token_max_hidden():
+    """T = 1 with the largest supported hidden size (16384)."""
+    base = synth.Workload("maxH", tokens=1, hidden=16384, ffn_full=128, shards=2, act="swiglu", dtype="bf16",
+                          w_std=0.01, seed=12)
+    run_small(base)
+
+
+# ---------------------------------------------------------------- full size
+
+def _sample(rng, n, k, must=()):
+    k = min(k, n)
+    s = set(int(v) for v in must if 0 <= v < n)
+    s.update(int(v) for v in rng.choice(n, size=k, replace=False))
+    return np.array(sorted(s), dtype=np.int64)
+
+
+def _gather(st, rows, chans, cols):
+    """Sampled entries of the GPU step, indexed on the device."""
+    F = st.F
+    dev = st.dev
+    ri = torch.as_tensor(rows, device=dev)
+    ci = torch.as_tensor(cols, device=dev)
+    c = lambda t: t.detach().float().cpu()
+    out = {"out": c(st.out), "dx_rows": c(st.dx[ri]), "dN_rows": c(st.dN[ri]),
+           "d_norm_w_cols": c(st.d_norm_w[ci]), "d_b_down": c(st.d_b_down),
+           "new_norm_w_cols": c(st.new["norm_w"][ci]), "new_b_down": c(st.new["b_down"])}
+    act, dwd, dwi, nwd, nwi = [], [], [], [], []
+    for j in chans:
+        s, jl = int(j) // F, int(j) % F
+        sh = st.shards[s]
+        act.append(c(sh["act"][:, jl]))
+        dwd.append(c(sh["d_w_down"][:, jl]))
+        nwd.append(c(st.new[f"w_down.{s}"][:, jl]))
+        if st.swiglu:
+            dwi.append(c(sh["d_w_in"][:, jl, :]))
+            nwi.append(c(st.new[f"w_in.{s}"][:, jl, :]))
+        else:
+            dwi.append(c(sh["d_w_in"][jl, :]))
+            nwi.append(c(st.new[f"w_in.{s}"][jl, :]))
+    out["act_chans"] = torch.stack(act, dim=1)
+    out["d_w_down_chans"] = torch.stack(dwd, dim=1)
+    out["new_w_down_chans"] = torch.stack(nwd, dim=1)
+    out["d_w_in_chans"] = torch.stack(dwi, dim=1 if st.swiglu else 0)
+    out["new_w_in_chans"] = torch.stack(nwi, dim=1 if st.swiglu else 0)
+    if not st.swiglu:
+        out["d_b_in"] = torch.cat([c(sh["d_b_in"]) for sh in st.shards])
+        out["new_b_in"] = torch.cat([c(st.new[f"b_in.{s}"]) for s in range(len(st.shards))])
+    return out
+
+
+FULL = ["gpt2s_gelu_tp1", "llama3_8b_tp8", "llama3_70b_tp8_rank", "llama3_8b_tp1_master"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    """Full workload in the benchmark's configuration: the whole output and
+    sampled rows / FFN channels / hidden columns of everything else."""
+    w = synth.workload(name)
+    t = synth.draw(w)
+    st = run_gpu(w, t, oop=True)
+    rng = np.random.default_rng(w.seed)
+    rows = _sample(rng, w.tokens, 48, must=[0, w.tokens - 1] + t["outlier_rows"][:16].tolist())
+    chans = _sample(rng, w.ffn_full, 48, must=[0, w.ffn_full - 1, w.ffn_local - 1, w.ffn_local])
+    cols = _sample(rng, w.hidden, 48, must=[0, w.hidden - 1])
+    got = _gather(st, rows, chans, cols)
+    del st
+    torch.cuda.empty_cache()
+    t0 = time.time()
+    ref = oracle.sampled_step(synth.to_numpy64(t["x"]).astype(np.float32), np_params(t), w.act, w.eps, w.lr,
+                              rows, chans, cols, dtype=np.float32)
+    say(f"  oracle sampled step: {time.time() - t0:.1f} s")
+    report = {}
+    check("out", got["out"], ref["out"], w.dtype, rowwise=True, report=report)
+    check("dx_rows", got["dx_rows"], ref["dx_rows"], w.dtype, rowwise=True, report=report)
+    check("dN_rows", got["dN_rows"], ref["dN_rows"], w.dtype, rowwise=True, report=report)
+    check("act_chans", got["act_chans"], ref["act_chans"], w.dtype, report=report)
+    for k in ("d_b_down", "d_norm_w_cols", "d_w_down_chans", "d_w_in_chans", "new_norm_w_cols", "new_b_down",
+              "new_w_down_chans", "new_w_in_chans") + (("d_b_in", "new_b_in") if w.act == "gelu" else ()):
+        check(k, got[k], ref[k], w.dtype, report=report)
+    say(f"  worst: {max(report.items(), key=lambda kv: kv[1])}")

@@ -417,3 +417,34 @@ def test_row_sampled_step_equals_full_step(act):
     r = oracle.row_forward_backward(x[rows], p, act, 1e-6)
     for k in ("out", "dx", "dN", "a"):
         np.testing.assert_allclose(r[k], d[k][rows], rtol=1e-13, atol=1e-14, err_msg=k)
+
+
+# ---------------------------------------------------------- full-size sampling
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_sampled_step_equals_dense_step(act):
+    rng = np.random.default_rng(31)
+    x, p = _params(rng, 11, 16, 24, act, 0.3)
+    d = oracle.dense_step(x, p, act, 1e-6, 0.1)
+    rows, chans, cols = [1, 5, 10], [0, 7, 23], [2, 15]
+    s = oracle.sampled_step(x, p, act, 1e-6, 0.1, rows, chans, cols, dtype=np.float64)
+    g, npar = d["grads"], d["new_params"]
+    close = lambda a, b: np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+    close(s["out"], d["out"])
+    close(s["dN_rows"], d["dN"][rows])
+    close(s["dx_rows"], d["dx"][rows])
+    close(s["act_chans"], d["a"][:, chans])
+    close(s["d_b_down"], g["b_down"])
+    close(s["d_w_down_chans"], g["w_down"][:, chans])
+    close(s["d_norm_w_cols"], g["norm_w"][cols])
+    close(s["new_norm_w_cols"], npar.norm_w[cols])
+    close(s["new_b_down"], npar.b_down)
+    close(s["new_w_down_chans"], npar.w_down[:, chans])
+    if act == "swiglu":
+        close(s["d_w_in_chans"], g["w_in"][:, chans, :])
+        close(s["new_w_in_chans"], npar.w_in[:, chans, :])
+    else:
+        close(s["d_w_in_chans"], g["w_in"][chans, :])
+        close(s["d_b_in"], g["b_in"])
+        close(s["new_w_in_chans"], npar.w_in[chans, :])
+        close(s["new_b_in"], npar.b_in)

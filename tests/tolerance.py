@@ -1,0 +1,60 @@
+"""Comparison rules of the parity tests.
+
+fp32 workloads: max |got - ref| <= 1e-5 against the fp64 oracle.
+
+bf16 workloads (bf16 storage, fp32 accumulation): the relative error with a
+floor,  max_i |got_i - ref_i| / max(|ref_i|, rho)  <= 2e-2,  where rho is the
+RMS of the reference over the token row for [T, .] activation tensors and
+over the whole compared tensor for parameters and their gradients.  A bare
+elementwise relative error is meaningless for entries near zero among 10^8
+values; the floor makes the bound relative to the tensor's own scale.  bf16
+rounding of a stored intermediate is 2^-9 ~ 2e-3 relative, so correct
+kernels sit around 1e-3 to 5e-3 and a real fault (a wrong index, a dropped
+term) lands far above 2e-2.
+"""
+
+import numpy as np
+import torch
+
+FP32_ATOL = 1e-5
+BF16_RTOL = 2e-2
+
+
+def _np(a):
+    if isinstance(a, torch.Tensor):
+        return a.detach().double().cpu().numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def max_abs(got, ref) -> float:
+    g, r = _np(got), _np(ref)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    return float(np.max(np.abs(g - r))) if g.size else 0.0
+
+
+def floored_rel(got, ref, rowwise: bool) -> float:
+    g, r = _np(got), _np(ref)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    if g.size == 0:
+        return 0.0
+    if rowwise and r.ndim >= 2:
+        rho = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
+    else:
+        rho = np.sqrt(np.mean(r * r))
+    den = np.maximum(np.abs(r), rho)
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(np.abs(g - r) / den))
+
+
+def check(name, got, ref, dtype: str, rowwise: bool = False, report=None) -> float:
+    if dtype == "fp32":
+        e = max_abs(got, ref)
+        if report is not None:
+            report[name] = e
+        assert e <= FP32_ATOL, f"{name}: max-abs {e:.3e} > {FP32_ATOL}"
+    else:
+        e = floored_rel(got, ref, rowwise)
+        if report is not None:
+            report[name] = e
+        assert e <= BF16_RTOL, f"{name}: floored relative error {e:.3e} > {BF16_RTOL}"
+    return e
