@@ -123,6 +123,8 @@ def main() -> int:
     ap.add_argument("--workload", default="llama3_8b_tp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times), to calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the tensor-parallel shards are "
@@ -140,6 +142,15 @@ def main() -> int:
         print(json.dumps({"error": "no GPU visible"}), flush=True)
         return 1
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_each_way": n * 4, "launches": 3}), flush=True)
+        return 0
     w = synth.workload(args.workload)
     t = synth.draw(w)
     st = ShardedStep(w, t, device="cuda:0", out_of_place_sgd=True)

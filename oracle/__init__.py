@@ -32,5 +32,7 @@ from .mlp import (  # noqa: F401
     inspect_record,
     row_forward_backward,
     MODES,
+    bf16_round,
+    storage_rounding,
 )
 from .sampled import sampled_step  # noqa: F401,E402

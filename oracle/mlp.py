@@ -30,6 +30,16 @@ Readings where the pages are silent (each is listed in the design doc):
   SiLU(v) = v * sigmoid(v); GeLU is the exact erf form;
   loss = sum(out^2) / 2, so d loss / d out = out;
   the optimiser is plain SGD, p <- p - lr * grad on every parameter.
+
+Storage precision.  The bf16 workloads state "bf16 weights and activations
+with fp32 accumulate".  With ``storage="bf16"`` every activation tensor the
+block stores is a bf16 tensor: N, the gate/up (or fc1) pre-activations, the
+activation A, the block output, the pre-activation gradients, and dx are
+each rounded once (to nearest, ties to even) where they are produced, and
+later steps consume the rounded values; contractions, partial sums, row
+statistics and parameter gradients stay exact (the accumulation type).
+Updated bf16 parameters are rounded; fp32 master copies are not.
+``storage="exact"`` (the default) rounds nothing.
 """
 
 from __future__ import annotations
@@ -42,6 +52,41 @@ import numpy as np
 from scipy.special import erf as _erf
 
 MODES = ("equivalence", "missing_forward_reduce", "missing_backward_reduce")
+
+
+def bf16_round(v):
+    """Round to the nearest bfloat16 value, ties to even (8 significant bits,
+    the fp32 exponent range).  Returns the rounded values in v's dtype
+    (float32 stays float32, anything else becomes float64).
+
+    float32 input: on the bit pattern, add 0x7fff plus the lowest kept bit
+    and clear the 16 dropped bits (round-half-even of the dropped part;
+    finite values only, overflow carries into the exponent and gives inf).
+    float64 input: v = m 2^e with 1/2 <= |m| < 1; m 2^8 is rounded to an
+    integer half-to-even and scaled back (no double rounding through fp32)."""
+    v = np.asarray(v)
+    if v.dtype == np.float32:
+        u = v.view(np.uint32).astype(np.uint32, copy=True)
+        u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+        u &= np.uint32(0xFFFF0000)
+        return u.view(np.float32)
+    v = v.astype(np.float64, copy=False)
+    m, e = np.frexp(v)
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+    return np.where(np.abs(r) > 3.3895313892515355e38, np.copysign(np.inf, v), r)
+
+
+def _identity(v):
+    return v
+
+
+def storage_rounding(storage: str):
+    """The rounding applied where the block stores an activation."""
+    if storage == "exact":
+        return _identity
+    if storage == "bf16":
+        return bf16_round
+    raise ValueError(storage)
 
 
 @dataclasses.dataclass
@@ -123,66 +168,74 @@ def rms_norm_bwd(dN, x, r, w):
 
 # ------------------------------------------------------ expansion / contraction
 
-def expansion_fwd(n, p: Params, act: str):
+def expansion_fwd(n, p: Params, act: str, R=_identity):
     """Column-parallel expansion on whatever channels ``p`` holds.
     SwiGLU: g = n Wg^T, u = n Wu^T, a = SiLU(g) * u; returns (pre=(g, u), a).
-    GeLU:   h = n W1^T + b1, a = gelu(h);             returns (pre=(h,), a)."""
+    GeLU:   h = n W1^T + b1, a = gelu(h);             returns (pre=(h,), a).
+    ``R`` is the storage rounding of the pre-activations and of a."""
     if act == "swiglu":
-        g = n @ p.w_in[0].T
-        u = n @ p.w_in[1].T
-        return (g, u), silu(g) * u
+        g = R(n @ p.w_in[0].T)
+        u = R(n @ p.w_in[1].T)
+        return (g, u), R(silu(g) * u)
     if act == "gelu":
-        h = n @ p.w_in.T + p.b_in[None, :]
-        return (h,), gelu(h)
+        h = R(n @ p.w_in.T + p.b_in[None, :])
+        return (h,), R(gelu(h))
     raise ValueError(act)
 
 
-def expansion_bwd(da, n, pre, p: Params, act: str):
+def expansion_bwd(da, n, pre, p: Params, act: str, R=_identity):
     """Backward of expansion_fwd for incoming da.  Returns
-    (d_w_in, d_b_in or None, dN contribution of these channels)."""
+    (d_w_in, d_b_in or None, dN contribution of these channels).
+    ``R`` is the storage rounding of the pre-activation gradients."""
     if act == "swiglu":
         g, u = pre
-        dg = da * u * silu_grad(g)
-        du = da * silu(g)
+        dg = R(da * u * silu_grad(g))
+        du = R(da * silu(g))
         d_w_in = np.stack([dg.T @ n, du.T @ n])
         dN = dg @ p.w_in[0] + du @ p.w_in[1]
         return d_w_in, None, dN
     (h,) = pre
-    dh = da * gelu_grad(h)
+    dh = R(da * gelu_grad(h))
     return dh.T @ n, np.sum(dh, axis=0), dh @ p.w_in
 
 
-def _sgd(p: Params, grads: dict, lr) -> Params:
-    """Plain SGD, p <- p - lr * grad, on every parameter tensor."""
+def _sgd(p: Params, grads: dict, lr, R=_identity) -> Params:
+    """Plain SGD, p <- p - lr * grad, on every parameter tensor; ``R`` is
+    the storage rounding of the updated parameters."""
     new = {}
     for k in ("norm_w", "w_in", "b_in", "w_down", "b_down"):
         v = getattr(p, k)
-        new[k] = None if v is None else v - lr * grads[k]
+        new[k] = None if v is None else R(v - lr * grads[k])
     return Params(new["norm_w"], new["w_in"], new["w_down"], new["b_down"], new["b_in"])
 
 
 # ------------------------------------------------------------------ dense step
 
-def dense_step(x, p: Params, act: str, eps: float, lr: float, dtype=np.float64) -> dict:
+def dense_step(x, p: Params, act: str, eps: float, lr: float, dtype=np.float64, storage: str = "exact") -> dict:
     """One dense training step of the block: forward, loss = sum(out^2)/2,
-    backward with d out = out, SGD.  All arithmetic in ``dtype``."""
+    backward with d out = out, SGD.  All arithmetic in ``dtype``; stored
+    activations rounded per ``storage`` (see the module docstring).
+    ``new_params`` are the updated parameters in storage precision,
+    ``new_masters`` the unrounded updates (fp32 master copies)."""
+    R = storage_rounding(storage)
     x = np.asarray(x, dtype=dtype)
     p = p.astype(dtype)
     n, r = rms_norm_fwd(x, p.norm_w, eps)
-    pre, a = expansion_fwd(n, p, act)
+    n = R(n)
+    pre, a = expansion_fwd(n, p, act, R)
     z = a @ p.w_down.T
-    out = x + z + p.b_down[None, :]
+    out = R(x + z + p.b_down[None, :])
     loss = 0.5 * np.sum(out * out)
     dY = out
     g = {}
     g["b_down"] = np.sum(dY, axis=0)
     g["w_down"] = dY.T @ a
     da = dY @ p.w_down
-    g["w_in"], g["b_in"], dN = expansion_bwd(da, n, pre, p, act)
+    g["w_in"], g["b_in"], dN = expansion_bwd(da, n, pre, p, act, R)
     dxn, g["norm_w"] = rms_norm_bwd(dN, x, r, p.norm_w)
-    dx = dY + dxn
+    dx = R(dY + dxn)
     return dict(x=x, n=n, rstd=r, pre=pre, a=a, z=z, out=out, loss=loss, dY=dY, da=da,
-                dN=dN, dx=dx, grads=g, params=p, new_params=_sgd(p, g, lr))
+                dN=dN, dx=dx, grads=g, params=p, new_params=_sgd(p, g, lr, R), new_masters=_sgd(p, g, lr))
 
 
 # ---------------------------------------------------------------- sharded step
@@ -209,7 +262,7 @@ def _ordered_sum(parts: List[np.ndarray]) -> np.ndarray:
 
 
 def sharded_step(x, p: Params, act: str, eps: float, lr: float, shards: int,
-                 mode: str = "equivalence", dtype=np.float64) -> dict:
+                 mode: str = "equivalence", dtype=np.float64, storage: str = "exact") -> dict:
     """The tensor-parallel decomposition of dense_step over ``shards`` ranks,
     run one rank after the other.  Coded separately from dense_step.
 
@@ -225,24 +278,26 @@ def sharded_step(x, p: Params, act: str, eps: float, lr: float, shards: int,
     Returns per-rank lists (index r) of every local tensor, plus ``partials``."""
     if mode not in MODES:
         raise ValueError(mode)
+    R = storage_rounding(storage)
     x = np.asarray(x, dtype=dtype)
     p = p.astype(dtype)
     ranks = []
     for s in range(shards):
         lp = _shard_params(p, s, shards, act)
         n, r = rms_norm_fwd(x, lp.norm_w, eps)          # replicated input, computed per rank
-        pre, a = expansion_fwd(n, lp, act)               # local channels, no communication
+        n = R(n)
+        pre, a = expansion_fwd(n, lp, act, R)            # local channels, no communication
         z = a @ lp.w_down.T                              # full-width partial output
         ranks.append(dict(params=lp, n=n, rstd=r, pre=pre, a=a, z=z))
 
     # Forward boundary (g): all-reduce of the partials, then residual + bias once.
     if mode == "missing_forward_reduce":
         for rk in ranks:
-            rk["out"] = x + rk["z"] + rk["params"].b_down[None, :]
+            rk["out"] = R(x + rk["z"] + rk["params"].b_down[None, :])
     else:
         zsum = _ordered_sum([rk["z"] for rk in ranks])
         for rk in ranks:
-            rk["out"] = x + zsum + rk["params"].b_down[None, :]
+            rk["out"] = R(x + zsum + rk["params"].b_down[None, :])
 
     # Backward up to the replicated normed input.  g's backward is the identity,
     # so every rank starts from the same d out (= out, from loss sum(out^2)/2).
@@ -251,7 +306,7 @@ def sharded_step(x, p: Params, act: str, eps: float, lr: float, shards: int,
         rk["loss"] = 0.5 * np.sum(dY * dY)
         g = {"b_down": np.sum(dY, axis=0), "w_down": dY.T @ rk["a"]}
         da = dY @ lp.w_down
-        g["w_in"], g["b_in"], rk["dN_partial"] = expansion_bwd(da, rk["n"], rk["pre"], lp, act)
+        g["w_in"], g["b_in"], rk["dN_partial"] = expansion_bwd(da, rk["n"], rk["pre"], lp, act, R)
         rk["da"] = da
         rk["grads"] = g
 
@@ -267,8 +322,8 @@ def sharded_step(x, p: Params, act: str, eps: float, lr: float, shards: int,
     for rk in ranks:
         lp = rk["params"]
         dxn, rk["grads"]["norm_w"] = rms_norm_bwd(rk["dN"], x, rk["rstd"], lp.norm_w)
-        rk["dx"] = rk["out"] + dxn
-        rk["new_params"] = _sgd(lp, rk["grads"], lr)
+        rk["dx"] = R(rk["out"] + dxn)
+        rk["new_params"] = _sgd(lp, rk["grads"], lr, R)
     return dict(ranks=ranks, mode=mode, shards=shards, act=act)
 
 
@@ -359,17 +414,19 @@ def inspect_record(seq: int, batch: int, hidden: int, ffn: int, world: int, rank
 
 # ------------------------------------------------------------ row-sampled step
 
-def row_forward_backward(x_rows, p: Params, act: str, eps: float, dtype=np.float64) -> dict:
+def row_forward_backward(x_rows, p: Params, act: str, eps: float, dtype=np.float64, storage: str = "exact") -> dict:
     """Forward and the activation-gradient part of the backward for a subset of
     token rows.  Every one of these quantities depends only on its own row
     (the block is row-independent and d out = out), so a sample of rows of a
     full-size workload can be checked exactly without the other rows."""
+    R = storage_rounding(storage)
     x = np.asarray(x_rows, dtype=dtype)
     p = p.astype(dtype)
     n, r = rms_norm_fwd(x, p.norm_w, eps)
-    pre, a = expansion_fwd(n, p, act)
-    out = x + a @ p.w_down.T + p.b_down[None, :]
+    n = R(n)
+    pre, a = expansion_fwd(n, p, act, R)
+    out = R(x + a @ p.w_down.T + p.b_down[None, :])
     da = out @ p.w_down
-    _, _, dN = expansion_bwd(da, n, pre, p, act)
+    _, _, dN = expansion_bwd(da, n, pre, p, act, R)
     dxn, _ = rms_norm_bwd(dN, x, r, p.norm_w)
-    return dict(n=n, rstd=r, pre=pre, a=a, out=out, da=da, dN=dN, dx=out + dxn)
+    return dict(n=n, rstd=r, pre=pre, a=a, out=out, da=da, dN=dN, dx=R(out + dxn))

@@ -40,6 +40,16 @@ struct Elem<bf16_t> {
   __device__ __forceinline__ static bf16_t from_f32(float v) { return f32_to_bf16(v); }
 };
 
+// The value a stored element of type T holds (round to T and back).
+template <typename T>
+__device__ __forceinline__ floatx4 stored(floatx4 v) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = bf16_to_f32(f32_to_bf16(v[i]));
+  }
+  return v;
+}
+
 // Load / store 4 consecutive elements as fp32.
 template <typename T>
 __device__ __forceinline__ floatx4 load4(const T* p);

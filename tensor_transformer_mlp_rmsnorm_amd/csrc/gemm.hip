@@ -28,6 +28,8 @@
 //    32 gate rows followed by the same 32 channels' up rows, so a lane holds
 //    g and u of the same (token, channel) and SiLU(g) * u is formed in
 //    registers ("Split the expansion": gate and up channels stay paired).
+//    g and u are stored (bf16) for the backward, and the activation is
+//    formed from those stored values.
 #include "common.h"
 #include "kernels.h"
 
@@ -277,7 +279,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g, int ntm, 
       for (int j = 0; j < 2; ++j) {
         const int64_t ch = (int64_t)tn * kSwigluChannels + wn * 32 + j * 16 + col4;
         if (ch >= F) continue;
-        const floatx4 gv = acc[i][j], uv = acc[i][j + 2];
+        // g and u are stored tensors: the activation is formed from their stored values
+        const floatx4 gv = stored<T>(acc[i][j]), uv = stored<T>(acc[i][j + 2]);
         floatx4 av;
 #pragma unroll
         for (int r = 0; r < 4; ++r) av[r] = gv[r] * sigmoid_f(gv[r]) * uv[r];
@@ -300,7 +303,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g, int ntm, 
           store4<T>(static_cast<T*>(g.C) + m * g.ldc + n, v + xr + bb);
         } else if constexpr (EPI == kEpiGeluFwd) {
           const floatx4 bb = load4<T>(static_cast<const T*>(g.bias) + n);
-          floatx4 h = v + bb, a;
+          const floatx4 h = stored<T>(v + bb);
+          floatx4 a;
 #pragma unroll
           for (int r = 0; r < 4; ++r) a[r] = gelu_f(h[r]);
           store4<T>(static_cast<T*>(g.pre) + m * N + n, h);

@@ -448,3 +448,79 @@ def test_sampled_step_equals_dense_step(act):
         close(s["d_b_in"], g["b_in"])
         close(s["new_w_in_chans"], npar.w_in[chans, :])
         close(s["new_b_in"], npar.b_in)
+
+
+# ------------------------------------------------------------ bf16 storage model
+
+def _torch_bf16(v):
+    return torch.from_numpy(np.asarray(v, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def test_bf16_round_matches_torch_conversion():
+    rng = np.random.default_rng(40)
+    v = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    # exact ties: a bf16 value plus half of its last place, for both parities of that place
+    base = _torch_bf16(rng.standard_normal(1000)).astype(np.float32)
+    ulp = np.ldexp(1.0, np.frexp(base)[1] - 8)
+    ties = (base + 0.5 * ulp).astype(np.float32)
+    for arr in (v, ties, np.array([0.0, -0.0, 1.0, -3.5, 65504.0, 3.3e38], dtype=np.float32)):
+        ref = _torch_bf16(arr)
+        np.testing.assert_array_equal(oracle.bf16_round(arr).astype(np.float64), ref)
+        np.testing.assert_array_equal(oracle.bf16_round(arr.astype(np.float64)), ref)
+    assert oracle.bf16_round(np.float32(1.0) + np.float32(2.0 ** -8)) == 1.0          # tie, even stays
+    assert oracle.bf16_round(np.float32(1.0) + np.float32(3 * 2.0 ** -8)) == 1.0 + 2.0 ** -6  # tie, odd rounds up
+
+
+def _is_bf16(a):
+    a = np.asarray(a, dtype=np.float64)
+    return np.array_equal(oracle.bf16_round(a), a)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_bf16_storage_tensors_are_bf16(act):
+    rng = np.random.default_rng(41)
+    x, p = _params(rng, 9, 16, 24, act, 0.3)
+    x, p = _torch_bf16(x), p.astype(np.float64)
+    for k in p.names():
+        setattr(p, k, _torch_bf16(getattr(p, k)))
+    d = oracle.dense_step(x, p, act, 1e-6, 0.1, storage="bf16")
+    for name in ("n", "a", "out", "dx"):
+        assert _is_bf16(d[name]), name
+    for t in d["pre"]:
+        assert _is_bf16(t)
+    for k in p.names():
+        assert _is_bf16(getattr(d["new_params"], k)), k
+    # masters are not rounded, and round to the stored parameters
+    np.testing.assert_array_equal(oracle.bf16_round(d["new_masters"].w_in), d["new_params"].w_in)
+    e = oracle.dense_step(x, p, act, 1e-6, 0.1)
+    assert not np.array_equal(d["out"], e["out"])
+
+
+def test_bf16_forward_matches_torch_bf16_forward():
+    """The bf16 storage forward against PyTorch's CPU bf16 forward of the
+    page's block (bf16 tensors, fp32 accumulation inside each op)."""
+    rng = np.random.default_rng(42)
+    T, H, Fw = 64, 96, 160
+    x = _torch_bf16(rng.standard_normal((T, H)))
+    p = Params(_torch_bf16(1 + 0.2 * rng.standard_normal(H)), _torch_bf16(rng.standard_normal((2, Fw, H)) * 0.1),
+               _torch_bf16(rng.standard_normal((H, Fw)) * 0.1), _torch_bf16(0.1 * rng.standard_normal(H)))
+    d = oracle.dense_step(x, p, "swiglu", 1e-6, 0.1, storage="bf16")
+    b = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16)
+    with torch.no_grad():
+        n = F.rms_norm(b(x), (H,), b(p.norm_w), eps=1e-6)
+        g, u = F.linear(n, b(p.w_in[0])), F.linear(n, b(p.w_in[1]))
+        hidden = F.silu(g) * u
+        out = b(x) + F.linear(hidden, b(p.w_down), b(p.b_down))
+    one_ulp = lambda a: np.ldexp(1.0, np.frexp(np.abs(a))[1] - 8)
+    # single rounded ops agree to one bf16 place
+    assert np.all(np.abs(n.double().numpy() - d["n"]) <= one_ulp(d["n"]))
+    # with the oracle's N, each projection is one fp32-accumulated dot product rounded once
+    with torch.no_grad():
+        g1 = F.linear(b(d["n"]), b(p.w_in[0])).double().numpy()
+    assert np.all(np.abs(g1 - d["pre"][0]) <= one_ulp(d["pre"][0]))
+    # the whole output: PyTorch rounds more often (SiLU, product, projection,
+    # bias and residual adds each round to bf16); the gap stays inside the
+    # bf16 tolerance
+    rho = np.sqrt(np.mean(d["out"] ** 2))
+    err = np.max(np.abs(out.double().numpy() - d["out"]) / np.maximum(np.abs(d["out"]), rho))
+    assert err < 2e-2

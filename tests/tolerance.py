@@ -1,6 +1,9 @@
 """Comparison rules of the parity tests.
 
-fp32 workloads: max |got - ref| <= 1e-5 against the fp64 oracle.
+fp32 workloads: max |got - ref| <= 1e-5 against the fp64 oracle.  That
+bound is for the unit-scale tiny workload; the larger fp32 test shapes have
+sums of hundreds of O(1) terms, where one fp32 ulp already exceeds 1e-5, so
+there ("fp32-scaled") the bound is 1e-5 * max(1, RMS of the reference tensor).
 
 bf16 workloads (bf16 storage, fp32 accumulation): the relative error with a
 floor,  max_i |got_i - ref_i| / max(|ref_i|, rho)  <= 2e-2,  where rho is the
@@ -52,6 +55,13 @@ def check(name, got, ref, dtype: str, rowwise: bool = False, report=None) -> flo
         if report is not None:
             report[name] = e
         assert e <= FP32_ATOL, f"{name}: max-abs {e:.3e} > {FP32_ATOL}"
+    elif dtype == "fp32-scaled":
+        r = _np(ref)
+        scale = max(1.0, float(np.sqrt(np.mean(r * r)))) if r.size else 1.0
+        e = max_abs(got, ref) / scale
+        if report is not None:
+            report[name] = e
+        assert e <= FP32_ATOL, f"{name}: max-abs / max(1, rms) {e:.3e} > {FP32_ATOL}"
     else:
         e = floored_rel(got, ref, rowwise)
         if report is not None:
