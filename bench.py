@@ -96,11 +96,13 @@ def cpu_baseline(w, t, budget_s: float = 15.0) -> dict:
         oracle.sharded_step(x[:tp], p, w.act, w.eps, w.lr, w.n_run)
         return time.perf_counter() - t0
 
-    probe = min(64, w.tokens)
-    t_probe = run(probe)
-    tp = int(min(w.tokens, max(probe, (budget_s / max(t_probe, 1e-3)) * probe)))
-    tp = max(probe, (tp // 64) * 64)
+    # grow the slice until one run takes at least half the budget (or is the whole batch)
+    tp = min(64, w.tokens)
     secs = run(tp)
+    while secs < 0.5 * budget_s and tp < w.tokens:
+        grow = max(2.0, min(8.0, budget_s / max(secs, 1e-3)))
+        tp = min(w.tokens, max(tp + 64, int(tp * grow) // 64 * 64))
+        secs = run(tp)
     mult = 18 if w.act == "swiglu" else 12
     flops = mult * tp * w.hidden * w.ffn_local * w.n_run
     try:
