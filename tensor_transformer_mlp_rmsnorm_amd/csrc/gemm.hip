@@ -1,4 +1,5 @@
-// MFMA GEMM for the six contractions of the MLP sublayer (gfx950 / CDNA4).
+// MFMA GEMM for the six contractions of the MLP sublayer (gfx950 / CDNA4):
+// the fp32 path (the bf16 path is gemm_bf16.hip).
 //
 //   C[m, n] = sum_k A(m, k) B(k, n)
 //   A(m, k) = A[m * lda + k]  (a_kcontig)  or  A[k * lda + m]
@@ -371,7 +372,7 @@ hipError_t dispatch(bool ak, bool bk, Epi epi, const GemmArgs& g, hipStream_t s)
 }  // namespace
 
 hipError_t launch_gemm(DType dt, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs& g, hipStream_t s) {
-  if (dt == kBF16) return dispatch<bf16_t>(a_kcontig, b_kcontig, epi, g, s);
+  if (dt == kBF16) return launch_gemm_bf16(a_kcontig, b_kcontig, epi, g, s);
   return dispatch<float>(a_kcontig, b_kcontig, epi, g, s);
 }
 

@@ -1,0 +1,311 @@
+// bf16 MFMA GEMM for the six contractions of the MLP sublayer (gfx950 / CDNA4).
+//
+//   C[m, n] = sum_k A(m, k) B(k, n),  A(m,k) = A[m*lda + k] (a_kcontig) or A[k*lda + m],
+//                                     B(k,n) = B[n*ldb + k] (b_kcontig) or B[k*ldb + n].
+//
+// One 512-thread workgroup computes a 256 x 256 output tile:
+//  * 8 waves in a 2 (M) x 4 (N) grid; each wave owns 128 x 64 outputs as 8 x 4
+//    blocks of v_mfma_f32_16x16x32_bf16 (128 fp32 accumulators per lane).  The
+//    LDS bytes read per flop are a quarter of what a 64 x 64 wave tile needs.
+//  * k is staged 64 at a time through two LDS buffers (64 KiB each).  A
+//    K-contiguous operand is stored [row][64 k] (128-byte rows, 16-byte chunks
+//    XOR-swizzled by row); an MN-contiguous operand is stored as it lies in
+//    memory, [k][256 rows] (512-byte rows, chunks XOR-swizzled by k), and its
+//    MFMA fragments are read with the gfx950 LDS transpose read
+//    (ds_read_b64_tr_b16): in each 16-lane group, result lane i element j is the
+//    (i mod 4)-th 16-bit value at the address of lane 4j + i/4, so lanes that
+//    point at 4 consecutive k-rows x 4 column quads receive 4 consecutive k of
+//    one column.  Two such reads give the 8 k-values of an MFMA operand.
+//  * Global loads for the next k-tile are issued before the current tile is
+//    multiplied; one barrier per k-tile.
+//  * B is the MFMA's first operand, so a lane's accumulator holds 4 consecutive
+//    output columns of one row and the epilogues work on 4-wide vectors.
+//  * Tile order: each of the 8 XCDs gets a contiguous range of tile ids
+//    (workgroups are dealt round-robin over XCDs), grouped by 4 tile-rows.
+//  * SwiGLU forward ("Split the expansion", synapticradio.com: gate and up
+//    channels stay paired): a tile covers 128 FFN channels; each wave's 64 B
+//    rows are 32 gate channels followed by the same 32 up channels, so one lane
+//    holds g and u of the same (token, channel).
+#include "common.h"
+#include "kernels.h"
+
+namespace tpmlp {
+namespace {
+
+constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 512;
+constexpr int kSwigluChannels = 128;               // FFN channels per tile in the SwiGLU forward
+constexpr int kTileU4 = 256 * kBK * 2 / 16;        // uint4 per operand tile (32 KiB)
+constexpr int kStageU4 = 2 * kTileU4;              // A + B
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// K-contiguous tile [256 rows][8 chunks of 8 k]: chunk index XOR (row & 7).
+__device__ __forceinline__ int kc_index(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// MN-contiguous tile [64 k][32 chunks of 8 rows]: chunk index XOR f(k), f in
+// {0,2,..,14}: the 4 k-rows of one transpose-read group land in distinct bank
+// quads, and so do the k-rows 8 apart read by the next lane group.
+__device__ __forceinline__ int mn_swz(int k) { return ((k & 3) << 1) ^ (((k >> 3) & 1) << 3); }
+__device__ __forceinline__ int mn_index(int k, int chunk) { return k * 32 + (chunk ^ mn_swz(k)); }
+
+// Physical row of logical tile row r (or -1 outside the operand).
+struct RowMap {
+  int64_t base, limit;
+  bool swiglu;
+  int64_t ffn;
+  __device__ __forceinline__ int64_t operator()(int r) const {
+    if (!swiglu) {
+      const int64_t g = base + r;
+      return g < limit ? g : -1;
+    }
+    const int wave_n = r >> 6, w = r & 63;
+    const int64_t ch = base + wave_n * 32 + (w & 31);
+    return ch < ffn ? (w >> 5) * ffn + ch : -1;
+  }
+};
+
+// Global -> registers: 4 chunks of 16 bytes per thread per operand tile.
+template <bool KC>
+__device__ __forceinline__ void load_tile(uint4 (&reg)[4], const bf16_t* __restrict__ p, int64_t ld, const RowMap& rm,
+                                          int64_t k0, int64_t K, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = tid + kThreads * i;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if constexpr (KC) {
+      const int r = q >> 3, c = q & 7;
+      const int64_t grow = rm(r), gk = k0 + 8 * c;
+      if (grow >= 0 && gk < K) v = *reinterpret_cast<const uint4*>(p + grow * ld + gk);
+    } else {
+      const int kr = q >> 5, c = q & 31;
+      const int64_t gk = k0 + kr, mn = rm.base + 8 * c;
+      if (gk < K && mn < rm.limit) v = *reinterpret_cast<const uint4*>(p + gk * ld + mn);
+    }
+    reg[i] = v;
+  }
+}
+
+template <bool KC>
+__device__ __forceinline__ void store_tile(const uint4 (&reg)[4], uint4* __restrict__ lds, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = tid + kThreads * i;
+    if constexpr (KC) lds[kc_index(q >> 3, q & 7)] = reg[i];
+    else lds[mn_index(q >> 5, q & 31)] = reg[i];
+  }
+}
+
+// MFMA operand fragment: 16 rows starting at `row0`, k = 32*s + 8*(lane/16) .. +7.
+template <bool KC>
+__device__ __forceinline__ uint4 read_frag(const uint4* __restrict__ lds, int row0, int s, int lane) {
+  if constexpr (KC) {
+    return lds[kc_index(row0 + (lane & 15), 4 * s + (lane >> 4))];
+  } else {
+    const int g = lane >> 4, sl = lane & 15;
+    const int mn = row0 + 4 * (sl & 3);
+    const int c = mn >> 3, half = (mn >> 2) & 1;
+    lds_char* base = (lds_char*)(lds);
+    uint2 out[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = 32 * s + 8 * g + 4 * h + (sl >> 2);
+      const int off = mn_index(k, c) * 16 + half * 8;
+      bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + off));
+      out[h] = __builtin_bit_cast(uint2, v);
+    }
+    return make_uint4(out[0].x, out[0].y, out[1].x, out[1].y);
+  }
+}
+
+__device__ __forceinline__ void tile_coords(int pid, int ntm, int ntn, int& tm, int& tn) {
+  const int ntiles = ntm * ntn;
+  const int xcd = pid & 7, local = pid >> 3;
+  const int per = ntiles >> 3, rem = ntiles & 7;
+  const int tile = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  constexpr int kGroup = 4;
+  const int in_group = kGroup * ntn;
+  const int group = tile / in_group;
+  const int first_m = group * kGroup;
+  const int gsize = min(ntm - first_m, kGroup);
+  const int t = tile - group * in_group;
+  tm = first_m + t % gsize;
+  tn = t / gsize;
+}
+
+template <bool AK, bool BKC, int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int ntm, int ntn) {
+  extern __shared__ uint4 smem[];  // 2 stages x (A tile + B tile) = 128 KiB
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 128 x 64 each
+
+  int tm, tn;
+  tile_coords(blockIdx.x, ntm, ntn, tm, tn);
+
+  const bf16_t* __restrict__ A = static_cast<const bf16_t*>(g.A);
+  const bf16_t* __restrict__ B = static_cast<const bf16_t*>(g.B);
+  const int64_t K = g.K;
+  const RowMap ra{(int64_t)tm * kBM, g.M, false, 0};
+  const RowMap rb = (EPI == kEpiSwigluFwd) ? RowMap{(int64_t)tn * kSwigluChannels, g.N, true, g.ffn}
+                                           : RowMap{(int64_t)tn * kBN, g.N, false, 0};
+
+  floatx4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 ra_reg[4], rb_reg[4];
+  const int nk = (int)((K + kBK - 1) / kBK);
+  load_tile<AK>(ra_reg, A, g.lda, ra, 0, K, tid);
+  load_tile<BKC>(rb_reg, B, g.ldb, rb, 0, K, tid);
+  store_tile<AK>(ra_reg, smem, tid);
+  store_tile<BKC>(rb_reg, smem + kTileU4, tid);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int64_t k0 = (int64_t)(kt + 1) * kBK;
+      load_tile<AK>(ra_reg, A, g.lda, ra, k0, K, tid);
+      load_tile<BKC>(rb_reg, B, g.ldb, rb, k0, K, tid);
+    }
+    const uint4* sa = smem + (kt & 1) * kStageU4;
+    const uint4* sb = sa + kTileU4;
+#pragma unroll
+    for (int s = 0; s < kBK / 32; ++s) {
+      uint4 af[8], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) af[i] = read_frag<AK>(sa, wm * 128 + i * 16, s, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = read_frag<BKC>(sb, wn * 64 + j * 16, s, lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[j]),
+                                                              __builtin_bit_cast(bf16x8, af[i]), acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      uint4* dst = smem + ((kt + 1) & 1) * kStageU4;
+      store_tile<AK>(ra_reg, dst, tid);
+      store_tile<BKC>(rb_reg, dst + kTileU4, tid);
+    }
+    __syncthreads();
+  }
+
+  // ------------------------------------------------------------- epilogue
+  const int64_t M = g.M, N = g.N, F = g.ffn;
+  const int col4 = 4 * (lane >> 4), frow = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t m = (int64_t)tm * kBM + wm * 128 + i * 16 + frow;
+    if (m >= M) continue;
+    if constexpr (EPI == kEpiSwigluFwd) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t ch = (int64_t)tn * kSwigluChannels + wn * 32 + j * 16 + col4;
+        if (ch >= F) continue;
+        // g and u are stored tensors: the activation is formed from their stored values
+        const floatx4 gv = stored<bf16_t>(acc[i][j]), uv = stored<bf16_t>(acc[i][j + 2]);
+        floatx4 av;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) av[r] = gv[r] * sigmoid_f(gv[r]) * uv[r];
+        bf16_t* pre = static_cast<bf16_t*>(g.pre) + m * 2 * F;
+        store4<bf16_t>(pre + ch, gv);
+        store4<bf16_t>(pre + F + ch, uv);
+        store4<bf16_t>(static_cast<bf16_t*>(g.act) + m * F + ch, av);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = (int64_t)tn * kBN + wn * 64 + j * 16 + col4;
+        if (n >= N) continue;
+        const floatx4 v = acc[i][j];
+        if constexpr (EPI == kEpiStoreF32) {
+          store4<float>(static_cast<float*>(g.C) + m * g.ldc + n, v);
+        } else if constexpr (EPI == kEpiResidual) {
+          const floatx4 xr = load4<bf16_t>(static_cast<const bf16_t*>(g.aux) + m * g.ldc + n);
+          const floatx4 bb = load4<bf16_t>(static_cast<const bf16_t*>(g.bias) + n);
+          store4<bf16_t>(static_cast<bf16_t*>(g.C) + m * g.ldc + n, v + xr + bb);
+        } else if constexpr (EPI == kEpiGeluFwd) {
+          const floatx4 bb = load4<bf16_t>(static_cast<const bf16_t*>(g.bias) + n);
+          const floatx4 h = stored<bf16_t>(v + bb);
+          floatx4 a;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) a[r] = gelu_f(h[r]);
+          store4<bf16_t>(static_cast<bf16_t*>(g.pre) + m * N + n, h);
+          store4<bf16_t>(static_cast<bf16_t*>(g.act) + m * N + n, a);
+        } else if constexpr (EPI == kEpiSwigluBwd) {
+          const bf16_t* sv = static_cast<const bf16_t*>(g.aux) + m * 2 * F;
+          const floatx4 gv = load4<bf16_t>(sv + n), uv = load4<bf16_t>(sv + F + n);
+          floatx4 dg, du;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sg = sigmoid_f(gv[r]);
+            dg[r] = v[r] * uv[r] * sg * (1.0f + gv[r] * (1.0f - sg));
+            du[r] = v[r] * gv[r] * sg;
+          }
+          bf16_t* dp = static_cast<bf16_t*>(g.pre) + m * 2 * F;
+          store4<bf16_t>(dp + n, dg);
+          store4<bf16_t>(dp + F + n, du);
+        } else if constexpr (EPI == kEpiGeluBwd) {
+          const floatx4 h = load4<bf16_t>(static_cast<const bf16_t*>(g.aux) + m * N + n);
+          floatx4 dh;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dh[r] = v[r] * gelu_grad_f(h[r]);
+          store4<bf16_t>(static_cast<bf16_t*>(g.pre) + m * N + n, dh);
+        }
+      }
+    }
+  }
+}
+
+constexpr size_t kSmemBytes = 2 * kStageU4 * sizeof(uint4);
+
+template <bool AK, bool BKC, int EPI>
+hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
+  const int ntm = (int)((g.M + kBM - 1) / kBM);
+  const int ntn = (EPI == kEpiSwigluFwd) ? (int)((g.ffn + kSwigluChannels - 1) / kSwigluChannels)
+                                         : (int)((g.N + kBN - 1) / kBN);
+  if (ntm == 0 || ntn == 0) return hipSuccess;
+  static bool configured = false;  // raise the dynamic LDS limit once per instantiation
+  if (!configured) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<AK, BKC, EPI>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  KernelTimer timer(g.tag ? g.tag : "gemm", s);
+  hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI>), dim3(ntm * ntn), dim3(kThreads), kSmemBytes, s, g, ntm,
+                     ntn);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(bool ak, bool bk, Epi epi, const GemmArgs& g, hipStream_t s) {
+  if (ak && bk) {
+    switch (epi) {
+      case kEpiStoreF32: return launch_t<true, true, kEpiStoreF32>(g, s);
+      case kEpiSwigluFwd: return launch_t<true, true, kEpiSwigluFwd>(g, s);
+      case kEpiGeluFwd: return launch_t<true, true, kEpiGeluFwd>(g, s);
+      case kEpiResidual: return launch_t<true, true, kEpiResidual>(g, s);
+      default: break;
+    }
+  } else if (ak && !bk) {
+    switch (epi) {
+      case kEpiStoreF32: return launch_t<true, false, kEpiStoreF32>(g, s);
+      case kEpiSwigluBwd: return launch_t<true, false, kEpiSwigluBwd>(g, s);
+      case kEpiGeluBwd: return launch_t<true, false, kEpiGeluBwd>(g, s);
+      default: break;
+    }
+  } else if (!ak && !bk) {
+    if (epi == kEpiStoreF32) return launch_t<false, false, kEpiStoreF32>(g, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tpmlp

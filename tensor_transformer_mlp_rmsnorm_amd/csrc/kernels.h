@@ -57,6 +57,8 @@ struct GemmArgs {
 
 hipError_t launch_gemm(DType dt, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs& g,
                        hipStream_t s);
+// The bf16 kernel (256 x 256 tiles); launch_gemm routes bf16 here.
+hipError_t launch_gemm_bf16(bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs& g, hipStream_t s);
 
 hipError_t launch_rmsnorm_fwd(DType dt, const void* x, const void* w, void* n, float* rstd,
                               int64_t T, int64_t H, float eps, hipStream_t s);
