@@ -26,6 +26,9 @@
  *     enqueue work on it and return; synchronisation is the caller's.
  *   - Shapes: T = tokens (any value >= 0), H = hidden, F = ffn_local.  H and
  *     F must be positive multiples of 8; H <= 16384.  T = 0 is a no-op.
+ *     Every [T,H], [T,2F] and [2F,H] tensor must hold fewer than 2^30
+ *     elements for bf16 (each GEMM operand is addressed through a buffer
+ *     descriptor limited to 2 GiB) and fewer than 2^31 for fp32.
  *   - dtype TP_MLP_F32: every tensor fp32.  dtype TP_MLP_BF16: parameters and
  *     activations bf16 (round to nearest even), accumulation fp32; partial
  *     sums, rstd and every parameter gradient are fp32 in both cases.

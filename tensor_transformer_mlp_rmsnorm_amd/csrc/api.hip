@@ -51,10 +51,12 @@ int check_desc(const tp_mlp_desc* d, const char* fn) {
   if (!(d->eps >= 0.0f)) return fail(TP_MLP_EINVAL, "%s: eps must be >= 0", fn);
   // Element counts stay below 2^31 so per-tensor int arithmetic in the
   // launchers is safe; byte offsets are 64-bit throughout.
-  const int64_t lim = (int64_t)1 << 31;
+  // The bf16 GEMM addresses each operand through a buffer descriptor whose
+  // range check needs the operand below 2 GiB.
+  const int64_t lim = d->dtype == TP_MLP_BF16 ? (int64_t)1 << 30 : (int64_t)1 << 31;
   const int64_t T = d->tokens, H = d->hidden, F = d->ffn_local;
   if (T * H >= lim || T * 2 * F >= lim || 2 * F * H >= lim)
-    return fail(TP_MLP_ESHAPE, "%s: a tensor would hold 2^31 or more elements", fn);
+    return fail(TP_MLP_ESHAPE, "%s: a tensor would hold %lld or more elements", fn, (long long)lim);
   return TP_MLP_OK;
 }
 

@@ -16,8 +16,9 @@
 //    (i mod 4)-th 16-bit value at the address of lane 4j + i/4, so lanes that
 //    point at 4 consecutive k-rows x 4 column quads receive 4 consecutive k of
 //    one column.  Two such reads give the 8 k-values of an MFMA operand.
-//  * Global loads for the next k-tile are issued before the current tile is
-//    multiplied; one barrier per k-tile.
+//  * Global -> LDS with buffer_load_dwordx4 ... lds (no staging registers):
+//    the next k-tile's loads are issued before the current tile is multiplied;
+//    one barrier per k-tile (which also waits for those loads).
 //  * B is the MFMA's first operand, so a lane's accumulator holds 4 consecutive
 //    output columns of one row and the epilogues work on 4-wide vectors.
 //  * Tile order: each of the 8 XCDs gets a contiguous range of tile ids
@@ -65,34 +66,45 @@ struct RowMap {
   }
 };
 
-// Global -> registers: 4 chunks of 16 bytes per thread per operand tile.
-template <bool KC>
-__device__ __forceinline__ void load_tile(uint4 (&reg)[4], const bf16_t* __restrict__ p, int64_t ld, const RowMap& rm,
-                                          int64_t k0, int64_t K, int tid) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = tid + kThreads * i;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if constexpr (KC) {
-      const int r = q >> 3, c = q & 7;
-      const int64_t grow = rm(r), gk = k0 + 8 * c;
-      if (grow >= 0 && gk < K) v = *reinterpret_cast<const uint4*>(p + grow * ld + gk);
-    } else {
-      const int kr = q >> 5, c = q & 31;
-      const int64_t gk = k0 + kr, mn = rm.base + 8 * c;
-      if (gk < K && mn < rm.limit) v = *reinterpret_cast<const uint4*>(p + gk * ld + mn);
-    }
-    reg[i] = v;
-  }
+// Global -> LDS without registers: buffer_load_dwordx4 ... lds writes a
+// wave's 64 x 16 bytes to 1 KiB of LDS at the wave-uniform address in M0, lane
+// j at byte 16 j.  Each wave fills 4 such blocks of each operand tile, and each
+// lane fetches the global chunk that belongs at its LDS slot, so the swizzle is
+// applied on the global side.  Lanes outside the operand (rows past M or N, k
+// past K) use an offset beyond the buffer's size, for which the buffer unit's
+// range check returns zeros: ragged tiles are zero-padded without branches.
+constexpr unsigned kOutOfRange = 0x80000000u;  // every operand is < 2 GiB (checked on the host)
+
+struct Operand {
+  __amdgpu_buffer_rsrc_t rsrc;
+  int64_t ld;
+};
+
+__device__ __forceinline__ Operand make_operand(const void* p, int64_t rows, int64_t ld) {
+  const int64_t bytes = rows * ld * (int64_t)sizeof(bf16_t);
+  return Operand{__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000), ld};
 }
 
 template <bool KC>
-__device__ __forceinline__ void store_tile(const uint4 (&reg)[4], uint4* __restrict__ lds, int tid) {
+__device__ __forceinline__ void issue_tile(const Operand& op, uint4* __restrict__ lds_tile, const RowMap& rm,
+                                           int64_t k0, int64_t K, int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int q = tid + kThreads * i;
-    if constexpr (KC) lds[kc_index(q >> 3, q & 7)] = reg[i];
-    else lds[mn_index(q >> 5, q & 31)] = reg[i];
+    const int b = wave * 4 + i;  // 1 KiB block of the tile
+    unsigned off = kOutOfRange;
+    if constexpr (KC) {
+      const int r = 8 * b + (lane >> 3);
+      const int c = (lane & 7) ^ (r & 7);  // kc_index(r, c) == r * 8 + (lane & 7)
+      const int64_t grow = rm(r), gk = k0 + 8 * c;
+      if (grow >= 0 && gk < K) off = (unsigned)((grow * op.ld + gk) * 2);
+    } else {
+      const int kr = 2 * b + (lane >> 5);
+      const int c = (lane & 31) ^ mn_swz(kr);  // mn_index(kr, c) == kr * 32 + (lane & 31)
+      const int64_t gk = k0 + kr, mn = rm.base + 8 * c;
+      if (gk < K && mn < rm.limit) off = (unsigned)((gk * op.ld + mn) * 2);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (__attribute__((address_space(3))) void*)(lds_tile + b * 64),
+                                             16, off, 0, 0, 0);
   }
 }
 
@@ -157,20 +169,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra_reg[4], rb_reg[4];
+  const Operand opa = make_operand(A, AK ? g.M : K, g.lda);
+  const Operand opb = make_operand(B, BKC ? (EPI == kEpiSwigluFwd ? 2 * g.ffn : g.N) : K, g.ldb);
   const int nk = (int)((K + kBK - 1) / kBK);
-  load_tile<AK>(ra_reg, A, g.lda, ra, 0, K, tid);
-  load_tile<BKC>(rb_reg, B, g.ldb, rb, 0, K, tid);
-  store_tile<AK>(ra_reg, smem, tid);
-  store_tile<BKC>(rb_reg, smem + kTileU4, tid);
-  __syncthreads();
+  issue_tile<AK>(opa, smem, ra, 0, K, wave, lane);
+  issue_tile<BKC>(opb, smem + kTileU4, rb, 0, K, wave, lane);
+  __syncthreads();  // waits for the loads (vmcnt) before the barrier
 
   for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) {
+    if (kt + 1 < nk) {
+      // the other stage was last read in iteration kt - 1, before the barrier that ended it
+      uint4* dst = smem + ((kt + 1) & 1) * kStageU4;
       const int64_t k0 = (int64_t)(kt + 1) * kBK;
-      load_tile<AK>(ra_reg, A, g.lda, ra, k0, K, tid);
-      load_tile<BKC>(rb_reg, B, g.ldb, rb, k0, K, tid);
+      issue_tile<AK>(opa, dst, ra, k0, K, wave, lane);
+      issue_tile<BKC>(opb, dst + kTileU4, rb, k0, K, wave, lane);
     }
     const uint4* sa = smem + (kt & 1) * kStageU4;
     const uint4* sb = sa + kTileU4;
@@ -188,12 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int 
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[j]),
                                                               __builtin_bit_cast(bf16x8, af[i]), acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      uint4* dst = smem + ((kt + 1) & 1) * kStageU4;
-      store_tile<AK>(ra_reg, dst, tid);
-      store_tile<BKC>(rb_reg, dst + kTileU4, tid);
-    }
-    __syncthreads();
+    __syncthreads();  // next stage landed; this stage free
   }
 
   // ------------------------------------------------------------- epilogue

@@ -73,6 +73,7 @@ def lib_call(name, *args):
     (dict(flags=8), L.EINVAL),
     (dict(eps=-1.0), L.EINVAL),
     (dict(T=1 << 20, H=4096), L.ESHAPE),  # 2^32 elements in [T, H]
+    (dict(T=1 << 17, H=8192), L.ESHAPE),  # 2^30 bf16 elements: past the 2 GiB operand limit
 ])
 def test_forward_rejects_bad_descriptor(lib, kw, code):
     assert _fwd(_desc(**kw)) == code
