@@ -161,9 +161,19 @@ int tp_partial_sum(const float* const* parts, int32_t n_parts, int64_t rows, int
 
 size_t tp_mlp_workspace_bytes(const tp_mlp_desc* d, int32_t phase) {
   if (!d || d->tokens < 0 || d->hidden <= 0 || d->ffn_local <= 0) return 0;
-  if (phase == TP_MLP_BWD_NORM) return rmsnorm_bwd_workspace(d->tokens, d->hidden);
-  if (phase == TP_MLP_BWD_SHARD && d->act == TP_MLP_ACT_GELU) return colsum_workspace(d->tokens, d->ffn_local);
-  return 0;
+  const int64_t T = d->tokens, H = d->hidden, F = d->ffn_local;
+  if (phase == TP_MLP_BWD_NORM) return rmsnorm_bwd_workspace(T, H);
+  if (phase != TP_MLP_BWD_SHARD) return 0;
+  size_t need = d->act == TP_MLP_ACT_GELU ? colsum_workspace(T, F) : 0;
+  if (d->dtype == TP_MLP_BF16) {
+    // k-split slices of the two weight-gradient GEMMs (K = T); they run one
+    // after the other and share the workspace
+    const int64_t P = d->act == TP_MLP_ACT_SWIGLU ? 2 * F : F;
+    const size_t w2 = gemm_ksplit_workspace(H, F, T), w4 = gemm_ksplit_workspace(P, H, T);
+    need = need > w2 ? need : w2;
+    need = need > w4 ? need : w4;
+  }
+  return need;
 }
 
 int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* a, void* stream) {
@@ -246,6 +256,8 @@ int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* 
   b2.C = a->d_w_down;
   b2.ldc = F;
   b2.tag = "gemm_wgrad_down";
+  b2.ksplit = gemm_ksplit(b2.M, b2.N, b2.K);
+  b2.ws = static_cast<float*>(a->workspace);
   CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b2, s), "d_w_down GEMM");
 
   // d_normed partial = d_pre w_in ([T,P] x [P,H]).
@@ -274,6 +286,8 @@ int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* 
   b4.C = a->d_w_in;
   b4.ldc = H;
   b4.tag = swiglu ? "gemm_wgrad_gate_up" : "gemm_wgrad_fc1";
+  b4.ksplit = gemm_ksplit(b4.M, b4.N, b4.K);
+  b4.ws = static_cast<float*>(a->workspace);
   CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b4, s), "d_w_in GEMM");
 
   if (!swiglu) CHECK_HIP(launch_colsum(dt, a->d_pre, a->d_b_in, a->workspace, T, F, s), "d_b_in column sum");

@@ -104,7 +104,28 @@ __global__ __launch_bounds__(256) void sgd_kernel(const T* pin, T* pout, const f
   }
 }
 
+__global__ __launch_bounds__(256) void ksplit_reduce_kernel(float* __restrict__ C, const float* __restrict__ ws,
+                                                             int nslices, int64_t M, int64_t N4, int64_t ldc) {
+  const int64_t total = M * N4, stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+    const int64_t m = e / N4, n = 4 * (e - m * N4);
+    const int64_t off = m * ldc + n;
+    floatx4 acc = load4<float>(C + off);
+    for (int s = 0; s < nslices; ++s) acc += load4<float>(ws + (int64_t)s * M * ldc + off);
+    store4<float>(C + off, acc);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_ksplit_reduce(float* C, const float* ws, int nslices, int64_t M, int64_t N, int64_t ldc,
+                                hipStream_t s) {
+  if (M == 0 || N == 0 || nslices == 0) return hipSuccess;
+  KernelTimer timer("ksplit_reduce", s);
+  hipLaunchKernelGGL(ksplit_reduce_kernel, dim3(grid_for(M * N / 4, 256)), dim3(256), 0, s, C, ws, nslices, M, N / 4,
+                     ldc);
+  return hipGetLastError();
+}
 
 hipError_t launch_partial_sum(const float* const* parts, int n_parts, int64_t rows, int64_t cols, const void* residual,
                               const void* bias, DType in_dt, void* out, DType out_dt, hipStream_t s) {

@@ -130,11 +130,16 @@ __device__ __forceinline__ uint4 read_frag(const uint4* __restrict__ lds, int ro
   }
 }
 
-__device__ __forceinline__ void tile_coords(int pid, int ntm, int ntn, int& tm, int& tn) {
-  const int ntiles = ntm * ntn;
+// blockIdx -> (tile_m, tile_n, k slice): each of the 8 XCDs gets a contiguous
+// range of ids (workgroups are dealt round-robin over XCDs); k slices are the
+// slowest index, tiles inside a slice are grouped by 4 tile-rows.
+__device__ __forceinline__ void tile_coords(int pid, int ntm, int ntn, int nks, int& tm, int& tn, int& ks) {
+  const int ntiles = ntm * ntn, total = ntiles * nks;
   const int xcd = pid & 7, local = pid >> 3;
-  const int per = ntiles >> 3, rem = ntiles & 7;
-  const int tile = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  const int per = total >> 3, rem = total & 7;
+  const int lin = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  ks = lin / ntiles;
+  const int tile = lin - ks * ntiles;
   constexpr int kGroup = 4;
   const int in_group = kGroup * ntn;
   const int group = tile / in_group;
@@ -145,6 +150,25 @@ __device__ __forceinline__ void tile_coords(int pid, int ntm, int ntn, int& tm, 
   tn = t / gsize;
 }
 
+template <bool AK, bool BKC>
+__device__ __forceinline__ void mma_half(floatx4 (&acc)[8][4], const uint4 (&af)[8], const uint4 (&bf)[4]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bf[j]),
+                                                          __builtin_bit_cast(bf16x8, af[i]), acc[i][j], 0, 0, 0);
+}
+
+template <bool AK, bool BKC>
+__device__ __forceinline__ void read_half(uint4 (&af)[8], uint4 (&bf)[4], const uint4* stage, int s, int wm, int wn,
+                                          int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) af[i] = read_frag<AK>(stage, wm * 128 + i * 16, s, lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bf[j] = read_frag<BKC>(stage + kTileU4, wn * 64 + j * 16, s, lane);
+}
+
 template <bool AK, bool BKC, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int ntm, int ntn) {
   extern __shared__ uint4 smem[];  // 2 stages x (A tile + B tile) = 128 KiB
@@ -153,12 +177,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int 
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 128 x 64 each
 
-  int tm, tn;
-  tile_coords(blockIdx.x, ntm, ntn, tm, tn);
+  int tm, tn, ks;
+  tile_coords(blockIdx.x, ntm, ntn, g.ksplit, tm, tn, ks);
 
   const bf16_t* __restrict__ A = static_cast<const bf16_t*>(g.A);
   const bf16_t* __restrict__ B = static_cast<const bf16_t*>(g.B);
   const int64_t K = g.K;
+  // this workgroup's k range [kbeg, kend); the slice length is a multiple of kBK
+  const int64_t kper = ((K + (int64_t)g.ksplit * kBK - 1) / ((int64_t)g.ksplit * kBK)) * kBK;
+  const int64_t kbeg = (int64_t)ks * kper;
+  const int64_t kend = min(K, kbeg + kper);
   const RowMap ra{(int64_t)tm * kBM, g.M, false, 0};
   const RowMap rb = (EPI == kEpiSwigluFwd) ? RowMap{(int64_t)tn * kSwigluChannels, g.N, true, g.ffn}
                                            : RowMap{(int64_t)tn * kBN, g.N, false, 0};
@@ -171,34 +199,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int 
 
   const Operand opa = make_operand(A, AK ? g.M : K, g.lda);
   const Operand opb = make_operand(B, BKC ? (EPI == kEpiSwigluFwd ? 2 * g.ffn : g.N) : K, g.ldb);
-  const int nk = (int)((K + kBK - 1) / kBK);
-  issue_tile<AK>(opa, smem, ra, 0, K, wave, lane);
-  issue_tile<BKC>(opb, smem + kTileU4, rb, 0, K, wave, lane);
+  const int nk = kend > kbeg ? (int)((kend - kbeg + kBK - 1) / kBK) : 0;
+  issue_tile<AK>(opa, smem, ra, kbeg, kend, wave, lane);
+  issue_tile<BKC>(opb, smem + kTileU4, rb, kbeg, kend, wave, lane);
   __syncthreads();  // waits for the loads (vmcnt) before the barrier
 
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) {
       // the other stage was last read in iteration kt - 1, before the barrier that ended it
       uint4* dst = smem + ((kt + 1) & 1) * kStageU4;
-      const int64_t k0 = (int64_t)(kt + 1) * kBK;
-      issue_tile<AK>(opa, dst, ra, k0, K, wave, lane);
-      issue_tile<BKC>(opb, dst + kTileU4, rb, k0, K, wave, lane);
+      const int64_t k0 = kbeg + (int64_t)(kt + 1) * kBK;
+      issue_tile<AK>(opa, dst, ra, k0, kend, wave, lane);
+      issue_tile<BKC>(opb, dst + kTileU4, rb, k0, kend, wave, lane);
     }
-    const uint4* sa = smem + (kt & 1) * kStageU4;
-    const uint4* sb = sa + kTileU4;
+    const uint4* st = smem + (kt & 1) * kStageU4;
 #pragma unroll
     for (int s = 0; s < kBK / 32; ++s) {
       uint4 af[8], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) af[i] = read_frag<AK>(sa, wm * 128 + i * 16, s, lane);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = read_frag<BKC>(sb, wn * 64 + j * 16, s, lane);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bfr[j]),
-                                                              __builtin_bit_cast(bf16x8, af[i]), acc[i][j], 0, 0, 0);
+      read_half<AK, BKC>(af, bfr, st, s, wm, wn, lane);
+      mma_half<AK, BKC>(acc, af, bfr);
     }
     __syncthreads();  // next stage landed; this stage free
   }
@@ -232,7 +251,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int 
         if (n >= N) continue;
         const floatx4 v = acc[i][j];
         if constexpr (EPI == kEpiStoreF32) {
-          store4<float>(static_cast<float*>(g.C) + m * g.ldc + n, v);
+          float* c = ks == 0 ? static_cast<float*>(g.C) : g.ws + (int64_t)(ks - 1) * M * g.ldc;
+          store4<float>(c + m * g.ldc + n, v);
         } else if constexpr (EPI == kEpiResidual) {
           const floatx4 xr = load4<bf16_t>(static_cast<const bf16_t*>(g.aux) + m * g.ldc + n);
           const floatx4 bb = load4<bf16_t>(static_cast<const bf16_t*>(g.bias) + n);
@@ -285,10 +305,17 @@ hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  KernelTimer timer(g.tag ? g.tag : "gemm", s);
-  hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI>), dim3(ntm * ntn), dim3(kThreads), kSmemBytes, s, g, ntm,
-                     ntn);
-  return hipGetLastError();
+  GemmArgs ga = g;
+  if (EPI != kEpiStoreF32 || !ga.ws) ga.ksplit = 1;
+  if (ga.ksplit < 1) ga.ksplit = 1;
+  {
+    KernelTimer timer(g.tag ? g.tag : "gemm", s);
+    hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI>), dim3(ntm * ntn * ga.ksplit), dim3(kThreads), kSmemBytes, s,
+                       ga, ntm, ntn);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ga.ksplit == 1) return e;
+  }
+  return launch_ksplit_reduce(static_cast<float*>(ga.C), ga.ws, ga.ksplit - 1, ga.M, ga.N, ga.ldc, s);
 }
 
 }  // namespace

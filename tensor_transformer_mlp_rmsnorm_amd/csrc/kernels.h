@@ -53,7 +53,25 @@ struct GemmArgs {
   const void* bias;  // GeLU fwd: b_in [N]; residual: b_down [N]
   int64_t ffn;       // F (column offset of the up half in [T, 2F] tensors)
   const char* tag;   // kernel name for timing
+  // kEpiStoreF32 only: split the k range over `ksplit` workgroups per tile;
+  // slice 0 writes C, slice s > 0 writes ws + (s - 1) * M * ldc, and a second
+  // kernel adds the slices to C in index order.  ksplit = 1 ignores ws.
+  int ksplit;
+  float* ws;
 };
+
+// Number of k-slices for a bf16 fp32-output GEMM: a function of the shape only
+// (so results are bitwise reproducible): split while the tile count stays
+// under 192 and every slice keeps at least 1024 of k.
+inline int gemm_ksplit(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  int ks = 1;
+  while (ks < 4 && tiles * ks < 192 && K / (2 * ks) >= 1024) ks *= 2;
+  return ks;
+}
+inline size_t gemm_ksplit_workspace(int64_t M, int64_t N, int64_t K) {
+  return (size_t)(gemm_ksplit(M, N, K) - 1) * (size_t)(M * N) * sizeof(float);
+}
 
 hipError_t launch_gemm(DType dt, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs& g,
                        hipStream_t s);
@@ -79,6 +97,11 @@ hipError_t launch_colsum(DType dt, const void* in, float* out, void* ws, int64_t
 hipError_t launch_partial_sum(const float* const* parts, int n_parts, int64_t rows, int64_t cols,
                               const void* residual, const void* bias, DType in_dt, void* out,
                               DType out_dt, hipStream_t s);
+
+// C[m, n] = ((C[m, n] + ws[0][m, n]) + ws[1][m, n]) + ... over `nslices`
+// [M, ldc] fp32 slices (the k-slices of a split GEMM, added in index order).
+hipError_t launch_ksplit_reduce(float* C, const float* ws, int nslices, int64_t M, int64_t N, int64_t ldc,
+                                hipStream_t s);
 
 hipError_t launch_sgd(DType dt, const void* param_in, void* param_out, const float* grad, const float* master_in,
                       float* master_out, int64_t n, float lr, hipStream_t s);

@@ -163,21 +163,36 @@ __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_kernel(
 }  // namespace
 
 // Fixed-order sum over `nparts` partial rows: out[c] = sum_{b=0}^{nparts-1} ws[b][c].
-// Each thread owns one column; its loop runs in index order.
+// A workgroup owns 32 columns; its 8 waves-quarters each sum a contiguous
+// eighth of the rows (in row order) for one column, and the 8 group sums are
+// added in group order.  The order depends only on nparts: deterministic.
+constexpr int kRedCols = 32, kRedGroups = 8;
+
 __global__ __launch_bounds__(256) void reduce_partial_rows_kernel(const float* __restrict__ ws, float* __restrict__ out,
                                                                   int64_t nparts, int64_t cols) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
+  __shared__ float part[kRedGroups][kRedCols];
+  const int tc = threadIdx.x % kRedCols, grp = threadIdx.x / kRedCols;
+  const int64_t c = (int64_t)blockIdx.x * kRedCols + tc;
+  const int64_t per = (nparts + kRedGroups - 1) / kRedGroups;
+  const int64_t b0 = grp * per, b1 = min(nparts, b0 + per);
   float acc = 0.f;
-  for (int64_t b = 0; b < nparts; ++b) acc += ws[b * cols + c];
-  out[c] = acc;
+  if (c < cols)
+    for (int64_t b = b0; b < b1; ++b) acc += ws[b * cols + c];
+  part[grp][tc] = acc;
+  __syncthreads();
+  if (grp == 0 && c < cols) {
+    float s = part[0][tc];
+#pragma unroll
+    for (int g = 1; g < kRedGroups; ++g) s += part[g][tc];
+    out[c] = s;
+  }
 }
 
 hipError_t launch_reduce_partial_rows(const float* ws, float* out, int64_t nparts, int64_t cols, hipStream_t s) {
   if (cols == 0) return hipSuccess;
   KernelTimer timer("column_reduce", s);
-  hipLaunchKernelGGL(reduce_partial_rows_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s, ws, out,
-                     nparts, cols);
+  hipLaunchKernelGGL(reduce_partial_rows_kernel, dim3((unsigned)((cols + kRedCols - 1) / kRedCols)), dim3(256), 0, s,
+                     ws, out, nparts, cols);
   return hipGetLastError();
 }
 
