@@ -78,6 +78,31 @@ def roofline_entry(name, launches, total_ms, w, steps):
     return {"bound": None, "avg_ms": total_ms / launches, "launches": launches}
 
 
+KERNEL_SOURCES = ("tensor_transformer_mlp_rmsnorm_amd/csrc/gemm_bf16.hip", "tensor_transformer_mlp_rmsnorm_amd/csrc/common.h",
+                  "tensor_transformer_mlp_rmsnorm_amd/csrc/kernels.h")
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter record
+    (profiles/traffic_<kernel>_<workload>.json: FETCH_SIZE and WRITE_SIZE
+    scaled by a plain-copy calibration), or None when there is no record or
+    the kernel sources changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    if rec.get("kernel_sources_sha256") != h.hexdigest():
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(w, t, budget_s: float = 15.0) -> dict:
     """The oracle as it stands (fp64 numpy, sharded step) on a token slice of
     the workload, sized to roughly ``budget_s`` of CPU time."""
@@ -180,7 +205,8 @@ def main() -> int:
     dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
     d = kernels[dom]
     roof = {"kernel": dom, "bound": d.get("bound"), "achieved": d.get("achieved"), "peak": d.get("peak"),
-            "unit": d.get("unit"), "frac": d.get("frac"), "traffic": None,
+            "unit": d.get("unit"), "frac": d.get("frac"), "traffic": measured_traffic(dom, w.name),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "per_launch": d.get("per_launch"), "avg_ms": d.get("avg_ms")}
     out = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -201,6 +201,25 @@ size_t tp_mlp_workspace_bytes(const tp_mlp_desc* d, int32_t phase);
 int tp_mlp_sgd_step(const void* param_in, void* param_out, const float* grad, const float* master_in,
                     float* master_out, int64_t n, int32_t param_dtype, float lr, void* stream);
 
+/* One tensor of tp_mlp_sgd_step_multi (fields as in tp_mlp_sgd_step). */
+typedef struct {
+  const void* param_in;
+  void* param_out;
+  const float* grad;
+  const float* master_in;
+  float* master_out;
+  int64_t n;
+} tp_mlp_sgd_tensor;
+
+/*
+ * tp_mlp_sgd_step_multi - tp_mlp_sgd_step on `count` tensors with one kernel
+ * launch.  `list` is a HOST array (read before the call returns).  All
+ * tensors share param_dtype; either every tensor has fp32 masters or none
+ * does.  Each tensor's rules are those of tp_mlp_sgd_step.  count >= 0.
+ */
+int tp_mlp_sgd_step_multi(const tp_mlp_sgd_tensor* list, int32_t count, int32_t param_dtype, float lr,
+                          void* stream);
+
 /*
  * Kernel timing, a measurement aid (off by default).  While enabled, every
  * kernel the library launches is bracketed by two hipEvents recorded on the

@@ -25,7 +25,7 @@ BWD_SHARD, BWD_NORM = 0, 1
 # every symbol include/tp_mlp.h declares
 EXPORTED = ("tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_workspace_bytes",
             "tp_mlp_sgd_step", "tp_mlp_last_error", "tp_mlp_version", "tp_mlp_profile_enable",
-            "tp_mlp_profile_count", "tp_mlp_profile_entry")
+            "tp_mlp_profile_count", "tp_mlp_profile_entry", "tp_mlp_sgd_step_multi")
 
 
 class TPMLPError(RuntimeError):
@@ -41,6 +41,11 @@ class tp_mlp_desc(ctypes.Structure):
 
 
 _vp = ctypes.c_void_p
+
+
+class tp_mlp_sgd_tensor(ctypes.Structure):
+    _fields_ = [("param_in", ctypes.c_void_p), ("param_out", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("master_in", ctypes.c_void_p), ("master_out", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
 class tp_mlp_bwd_args(ctypes.Structure):
@@ -72,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_workspace_bytes.restype = ctypes.c_size_t
         L.tp_mlp_sgd_step.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, _vp]
         L.tp_mlp_sgd_step.restype = ctypes.c_int
+        L.tp_mlp_sgd_step_multi.argtypes = [ctypes.POINTER(tp_mlp_sgd_tensor), ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_float, _vp]
+        L.tp_mlp_sgd_step_multi.restype = ctypes.c_int
         L.tp_mlp_last_error.argtypes = []
         L.tp_mlp_last_error.restype = ctypes.c_char_p
         L.tp_mlp_version.argtypes = []
@@ -151,6 +159,13 @@ def tp_mlp_sgd_step(param_in, param_out, grad, master_in, master_out, n: int, pa
                     stream=None) -> None:
     _check(lib().tp_mlp_sgd_step(_ptr(param_in), _ptr(param_out), _ptr(grad), _ptr(master_in), _ptr(master_out),
                                  n, param_dtype, lr, _stream(stream)))
+
+
+def tp_mlp_sgd_step_multi(tensors: Sequence, param_dtype: int, lr: float, stream=None) -> None:
+    """``tensors``: sequence of (param_in, param_out, grad, master_in, master_out, n)."""
+    arr = (tp_mlp_sgd_tensor * max(1, len(tensors)))(
+        *[tp_mlp_sgd_tensor(_ptr(a), _ptr(b), _ptr(c), _ptr(d), _ptr(e), n) for a, b, c, d, e, n in tensors])
+    _check(lib().tp_mlp_sgd_step_multi(arr, len(tensors), param_dtype, lr, _stream(stream)))
 
 
 def tp_mlp_last_error() -> str:

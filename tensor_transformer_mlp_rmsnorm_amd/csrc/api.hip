@@ -294,26 +294,61 @@ int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* 
   return TP_MLP_OK;
 }
 
-int tp_mlp_sgd_step(const void* param_in, void* param_out, const float* grad, const float* master_in,
-                    float* master_out, int64_t n, int32_t param_dtype, float lr, void* stream) {
-  const char* fn = "tp_mlp_sgd_step";
-  g_err[0] = 0;
-  if (n < 0) return fail(TP_MLP_EINVAL, "%s: n < 0", fn);
-  if (param_dtype != TP_MLP_F32 && param_dtype != TP_MLP_BF16) return fail(TP_MLP_EDTYPE, "%s: unknown dtype", fn);
-  if (master_in && param_dtype != TP_MLP_BF16)
+namespace {
+
+int check_sgd_tensor(const tp_mlp_sgd_tensor& t, int32_t param_dtype, bool master, const char* fn) {
+  if (t.n < 0) return fail(TP_MLP_EINVAL, "%s: n < 0", fn);
+  if ((t.master_in != nullptr) != master)
+    return fail(TP_MLP_EINVAL, "%s: either every tensor has a master copy or none does", fn);
+  if (t.master_in && param_dtype != TP_MLP_BF16)
     return fail(TP_MLP_EDTYPE, "%s: a master copy is only used with bf16 parameters", fn);
-  if (n == 0) return TP_MLP_OK;
+  if (t.n == 0) return TP_MLP_OK;
+  const void* param_in = t.param_in;
+  void* param_out = t.param_out;
+  const float* grad = t.grad;
   REQUIRE_PTR(param_in);
   REQUIRE_PTR(param_out);
   REQUIRE_PTR(grad);
-  if (master_in) {
+  if (t.master_in) {
+    const float* master_in = t.master_in;
+    float* master_out = t.master_out;
     REQUIRE_PTR(master_in);
     REQUIRE_PTR(master_out);
   }
-  CHECK_HIP(launch_sgd(dt_of(param_dtype), param_in, param_out, grad, master_in, master_out, n, lr,
+  return TP_MLP_OK;
+}
+
+int sgd_list(const tp_mlp_sgd_tensor* list, int32_t count, int32_t param_dtype, float lr, void* stream,
+             const char* fn) {
+  if (count < 0) return fail(TP_MLP_EINVAL, "%s: count < 0", fn);
+  if (count > 0 && !list) return fail(TP_MLP_EINVAL, "%s: list is NULL", fn);
+  if (param_dtype != TP_MLP_F32 && param_dtype != TP_MLP_BF16) return fail(TP_MLP_EDTYPE, "%s: unknown dtype", fn);
+  const bool master = count > 0 && list[0].master_in != nullptr;
+  for (int i = 0; i < count; ++i) {
+    const int rc = check_sgd_tensor(list[i], param_dtype, master, fn);
+    if (rc) return rc;
+  }
+  if (count == 0) return TP_MLP_OK;
+  static_assert(sizeof(tp_mlp_sgd_tensor) == sizeof(SgdTensor), "SGD tensor layouts match");
+  CHECK_HIP(launch_sgd(dt_of(param_dtype), reinterpret_cast<const SgdTensor*>(list), count, master, lr,
                        static_cast<hipStream_t>(stream)),
             "sgd");
   return TP_MLP_OK;
+}
+
+}  // namespace
+
+int tp_mlp_sgd_step(const void* param_in, void* param_out, const float* grad, const float* master_in,
+                    float* master_out, int64_t n, int32_t param_dtype, float lr, void* stream) {
+  g_err[0] = 0;
+  const tp_mlp_sgd_tensor t{param_in, param_out, grad, master_in, master_out, n};
+  return sgd_list(&t, 1, param_dtype, lr, stream, "tp_mlp_sgd_step");
+}
+
+int tp_mlp_sgd_step_multi(const tp_mlp_sgd_tensor* list, int32_t count, int32_t param_dtype, float lr,
+                          void* stream) {
+  g_err[0] = 0;
+  return sgd_list(list, count, param_dtype, lr, stream, "tp_mlp_sgd_step_multi");
 }
 
 }  // extern "C"

@@ -15,6 +15,21 @@ struct PartList {
   const float* p[kMaxParts];
 };
 
+constexpr int kSgdMaxTensors = 48;
+struct SgdSeg {
+  const void* pin;
+  void* pout;
+  const float* g;
+  const float* min;
+  float* mout;
+  int64_t n;
+  int64_t block0;  // first workgroup of this tensor
+};
+struct SgdList {
+  SgdSeg seg[kSgdMaxTensors];
+  int count;
+};
+
 // out = ((p0 + p1) + ...) + residual + bias, 4 columns per thread-step.
 // "Split the contraction" (synapticradio.com): the partial down outputs are
 // summed, then the replicated residual and bias are added once.
@@ -46,8 +61,8 @@ hipError_t psum_t(const PartList& pl, int n, int64_t rows, int64_t cols, const v
   const TI* r = static_cast<const TI*>(res);
   const TI* b = static_cast<const TI*>(bias);
   TO* o = static_cast<TO*>(out);
-  const dim3 grid(grid_for(n4, 256)), block(256);
   KernelTimer timer((r || b) ? "partial_sum_residual" : "partial_sum", s);
+  const dim3 grid(grid_for(n4, 256)), block(256);
   if (r && b) hipLaunchKernelGGL((partial_sum_kernel<TI, TO, true, true>), grid, block, 0, s, pl, n, n4, cols4, r, b, o);
   else if (r) hipLaunchKernelGGL((partial_sum_kernel<TI, TO, true, false>), grid, block, 0, s, pl, n, n4, cols4, r, b, o);
   else if (b) hipLaunchKernelGGL((partial_sum_kernel<TI, TO, false, true>), grid, block, 0, s, pl, n, n4, cols4, r, b, o);
@@ -72,35 +87,46 @@ __global__ __launch_bounds__(kColThreads) void colsum_partial_kernel(const T* __
   store4<float>(ws + (int64_t)blockIdx.x * cols + 4 * q, acc);
 }
 
-// SGD: p <- p - lr g ("Reproduce one dense training step": one SGD update).
+// SGD: p <- p - lr g ("Reproduce one dense training step": one SGD update),
+// over a list of parameter tensors in one launch.  Workgroup b belongs to the
+// tensor whose [block0, block0 + blocks) contains b; each thread updates 8
+// consecutive elements (a 16-byte bf16 or 2 x 16-byte fp32 parameter chunk).
 // Out of place when pout != pin (the input is then left unchanged).
+constexpr int kSgdPerThread = 8, kSgdBlock = 256, kSgdPerBlock = kSgdPerThread * kSgdBlock;
+
 template <typename T, bool MASTER>
-__global__ __launch_bounds__(256) void sgd_kernel(const T* pin, T* pout, const float* __restrict__ g,
-                                                  const float* min_, float* mout, int64_t n, float lr) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t n4 = n / 4;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4; e += stride) {
-    const floatx4 gv = load4<float>(g + 4 * e);
-    floatx4 v;
-    if constexpr (MASTER) {
-      v = load4<float>(min_ + 4 * e) - lr * gv;
-      store4<float>(mout + 4 * e, v);
-    } else {
-      v = load4<T>(pin + 4 * e) - lr * gv;
+__global__ __launch_bounds__(kSgdBlock) void sgd_kernel(SgdList L, float lr) {
+  int t = 0;
+  while (t + 1 < L.count && (int64_t)blockIdx.x >= L.seg[t + 1].block0) ++t;
+  const SgdSeg& sg = L.seg[t];
+  const T* pin = static_cast<const T*>(sg.pin);
+  T* pout = static_cast<T*>(sg.pout);
+  const int64_t e0 = ((int64_t)blockIdx.x - sg.block0) * kSgdPerBlock + (int64_t)threadIdx.x * kSgdPerThread;
+  if (e0 + kSgdPerThread <= sg.n) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t e = e0 + 4 * h;
+      const floatx4 gv = load4<float>(sg.g + e);
+      floatx4 v;
+      if constexpr (MASTER) {
+        v = load4<float>(sg.min + e) - lr * gv;
+        store4<float>(sg.mout + e, v);
+      } else {
+        v = load4<T>(pin + e) - lr * gv;
+      }
+      store4<T>(pout + e, v);
     }
-    store4<T>(pout + 4 * e, v);
-  }
-  // tail (n % 4 elements), handled by the first threads of the grid
-  const int64_t t = 4 * n4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < n) {
-    float v;
-    if constexpr (MASTER) {
-      v = min_[t] - lr * g[t];
-      mout[t] = v;
-    } else {
-      v = Elem<T>::to_f32(pin[t]) - lr * g[t];
+  } else {
+    for (int64_t e = e0; e < sg.n; ++e) {
+      float v;
+      if constexpr (MASTER) {
+        v = sg.min[e] - lr * sg.g[e];
+        sg.mout[e] = v;
+      } else {
+        v = Elem<T>::to_f32(pin[e]) - lr * sg.g[e];
+      }
+      pout[e] = Elem<T>::from_f32(v);
     }
-    pout[t] = Elem<T>::from_f32(v);
   }
 }
 
@@ -163,23 +189,34 @@ hipError_t launch_colsum(DType dt, const void* in, float* out, void* ws, int64_t
   return launch_reduce_partial_rows(w, out, nb, cols, s);
 }
 
-hipError_t launch_sgd(DType dt, const void* param_in, void* param_out, const float* grad, const float* master_in,
-                      float* master_out, int64_t n, float lr, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  const dim3 grid(grid_for(n / 4 + 1, 256)), block(256);
+hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, float lr, hipStream_t s) {
   KernelTimer timer("sgd", s);
-  if (dt == kBF16) {
-    const bf16_t* pi = static_cast<const bf16_t*>(param_in);
-    bf16_t* po = static_cast<bf16_t*>(param_out);
-    if (master_in)
-      hipLaunchKernelGGL((sgd_kernel<bf16_t, true>), grid, block, 0, s, pi, po, grad, master_in, master_out, n, lr);
-    else
-      hipLaunchKernelGGL((sgd_kernel<bf16_t, false>), grid, block, 0, s, pi, po, grad, master_in, master_out, n, lr);
-  } else {
-    hipLaunchKernelGGL((sgd_kernel<float, false>), grid, block, 0, s, static_cast<const float*>(param_in),
-                       static_cast<float*>(param_out), grad, master_in, master_out, n, lr);
+  for (int first = 0; first < count; first += kSgdMaxTensors) {
+    SgdList L{};
+    int64_t blocks = 0;
+    for (int i = first; i < count && L.count < kSgdMaxTensors; ++i) {
+      if (list[i].n == 0) continue;
+      SgdSeg& sg = L.seg[L.count++];
+      sg.pin = list[i].param_in;
+      sg.pout = list[i].param_out;
+      sg.g = list[i].grad;
+      sg.min = list[i].master_in;
+      sg.mout = list[i].master_out;
+      sg.n = list[i].n;
+      sg.block0 = blocks;
+      blocks += (sg.n + kSgdPerBlock - 1) / kSgdPerBlock;
+    }
+    if (L.count == 0) continue;
+    if (dt == kBF16) {
+      if (master) hipLaunchKernelGGL((sgd_kernel<bf16_t, true>), dim3((unsigned)blocks), dim3(kSgdBlock), 0, s, L, lr);
+      else hipLaunchKernelGGL((sgd_kernel<bf16_t, false>), dim3((unsigned)blocks), dim3(kSgdBlock), 0, s, L, lr);
+    } else {
+      hipLaunchKernelGGL((sgd_kernel<float, false>), dim3((unsigned)blocks), dim3(kSgdBlock), 0, s, L, lr);
+    }
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace tpmlp

@@ -103,7 +103,16 @@ hipError_t launch_partial_sum(const float* const* parts, int n_parts, int64_t ro
 hipError_t launch_ksplit_reduce(float* C, const float* ws, int nslices, int64_t M, int64_t N, int64_t ldc,
                                 hipStream_t s);
 
-hipError_t launch_sgd(DType dt, const void* param_in, void* param_out, const float* grad, const float* master_in,
-                      float* master_out, int64_t n, float lr, hipStream_t s);
+struct SgdTensor {
+  const void* param_in;
+  void* param_out;
+  const float* grad;
+  const float* master_in;
+  float* master_out;
+  int64_t n;
+};
+// One SGD update of every tensor in `list` (all in dtype dt; all with fp32
+// masters when `master`).
+hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, float lr, hipStream_t s);
 
 }  // namespace tpmlp

@@ -11,7 +11,7 @@ all-reduces of the method become tp_partial_sum at the same two points
   backward  shard s: tp_mlp_backward(SHARD, d_out = out) -> dN_s and the shard's weight grads
             dN  = tp_partial_sum(dN_0..dN_{S-1})                      (backward boundary)
             tp_mlp_backward(NORM) -> dx, d_norm_w, d_b_down
-  update    tp_mlp_sgd_step on every parameter tensor
+  update    tp_mlp_sgd_step_multi over every parameter tensor (one launch)
 
 Work that every rank repeats on replicated data (the RMSNorm forward, the
 RMSNorm backward, the update of norm_w and b_down) is done once here: its
@@ -195,14 +195,15 @@ class ShardedStep:
             self._norm_backward(dN, outs[s], dxs[s], dws[s], dbs[s])
 
     def sgd(self) -> None:
-        lr = self.w.lr
+        """One SGD update of every parameter tensor (one launch)."""
+        lst = []
         for name, t in self._param_list():
             g = self._grad_of(name)
             if self.masters is not None:
-                L.tp_mlp_sgd_step(t, self.new[name], g, self.masters[name], self.new_masters[name], t.numel(),
-                                  self.cdt, lr, stream=self.stream)
+                lst.append((t, self.new[name], g, self.masters[name], self.new_masters[name], t.numel()))
             else:
-                L.tp_mlp_sgd_step(t, self.new[name], g, None, None, t.numel(), self.cdt, lr, stream=self.stream)
+                lst.append((t, self.new[name], g, None, None, t.numel()))
+        L.tp_mlp_sgd_step_multi(lst, self.cdt, self.w.lr, stream=self.stream)
 
     def step(self, mode: str = "equivalence", update: bool = True) -> None:
         self.forward(mode)

@@ -145,6 +145,19 @@ def test_sgd_checks(lib):
     assert f(None, None, None, None, None, 0, L.BF16, 0.1, None) == L.OK  # n = 0: no-op
 
 
+def test_sgd_multi_checks(lib):
+    T = L.tp_mlp_sgd_tensor
+    arr = lambda *ts: (T * max(1, len(ts)))(*ts)
+    f = lib.tp_mlp_sgd_step_multi
+    assert f(None, 0, L.BF16, 0.1, None) == L.OK                              # nothing to do
+    assert f(None, 1, L.BF16, 0.1, None) == L.EINVAL
+    assert f(arr(T(A, A, A, None, None, 8)), -1, L.BF16, 0.1, None) == L.EINVAL
+    assert f(arr(T(A, A, A, None, None, 8), T(A, A, A, A, A, 8)), 2, L.BF16, 0.1, None) == L.EINVAL  # mixed masters
+    assert f(arr(T(A, A, A, None, None, 8), T(A, MIS, A, None, None, 8)), 2, L.BF16, 0.1, None) == L.EALIGN
+    assert f(arr(T(A, A, A, None, None, -3)), 1, L.BF16, 0.1, None) == L.EINVAL
+    assert f(arr(T(None, None, None, None, None, 0)), 1, L.BF16, 0.1, None) == L.OK  # n = 0: no-op
+
+
 def test_binding_raises_with_message(lib):
     with pytest.raises(L.TPMLPError) as ei:
         L.tp_partial_sum([A], 4, 6, None, None, L.F32, A + 4096, L.F32, stream=0)

@@ -266,3 +266,51 @@ def test_full_size_sampled(name):
               "new_w_down_chans", "new_w_in_chans") + (("d_b_in", "new_b_in") if w.act == "gelu" else ()):
         check(k, got[k], ref[k], w.dtype, report=report)
     say(f"  worst: {max(report.items(), key=lambda kv: kv[1])}")
+
+
+# ------------------------------------------------------------------ SGD entry points
+
+@pytest.mark.parametrize("n", [1, 7, 8, 1003, 2048 * 3 + 5])
+def test_sgd_single_tensor_tails(n):
+    """tp_mlp_sgd_step on lengths that exercise the 8-wide path and the scalar
+    tail; in place and out of place; against p - lr g rounded once to bf16."""
+    from tensor_transformer_mlp_rmsnorm_amd import _lib as L
+    g = torch.Generator().manual_seed(n)
+    p = torch.randn(n, generator=g).to(torch.bfloat16)
+    gr = torch.randn(n, generator=g) * 3.0
+    ref = oracle.bf16_round(p.double().numpy() - 0.1 * gr.double().numpy())
+    say(f"[gpu] sgd n={n}")
+    dp, dg = p.cuda(), gr.cuda()
+    out = torch.empty_like(dp)
+    L.tp_mlp_sgd_step(dp, out, dg, None, None, n, L.BF16, 0.1)
+    L.tp_mlp_sgd_step(dp, dp, dg, None, None, n, L.BF16, 0.1)  # in place
+    torch.cuda.synchronize()
+    # fp32 arithmetic then one bf16 rounding: within one bf16 place of the exact
+    # rounding, measured against max(|ref|, RMS) (where p ~ lr g the fp32
+    # difference cancels and only the floor is meaningful)
+    rho = float(np.sqrt(np.mean(ref * ref)))
+    for got in (out, dp):
+        assert np.max(np.abs(got.double().cpu().numpy() - ref) / np.maximum(np.abs(ref), rho)) <= 2.0 ** -8
+
+
+def test_sgd_multi_with_masters():
+    from tensor_transformer_mlp_rmsnorm_amd import _lib as L
+    g = torch.Generator().manual_seed(5)
+    sizes = [13, 4096, 777, 65536 + 3]
+    lst, refs = [], []
+    say("[gpu] sgd multi with masters")
+    keep = []
+    for n in sizes:
+        m = torch.randn(n, generator=g)
+        gr = torch.randn(n, generator=g)
+        dm, dg = m.cuda(), gr.cuda()
+        dp = m.to(torch.bfloat16).cuda()
+        dpo, dmo = torch.empty_like(dp), torch.empty_like(dm)
+        keep += [dm, dg, dp, dpo, dmo]
+        lst.append((dp, dpo, dg, dm, dmo, n))
+        refs.append((m.double().numpy() - 0.1 * gr.double().numpy(), dpo, dmo))
+    L.tp_mlp_sgd_step_multi(lst, L.BF16, 0.1)
+    torch.cuda.synchronize()
+    for mref, dpo, dmo in refs:
+        np.testing.assert_allclose(dmo.double().cpu().numpy(), mref, rtol=1e-6, atol=1e-6)
+        assert torch.equal(dpo.cpu(), dmo.cpu().to(torch.bfloat16))
