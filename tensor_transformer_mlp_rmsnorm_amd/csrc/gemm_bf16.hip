@@ -7,18 +7,31 @@
 //  * 8 waves in a 2 (M) x 4 (N) grid; each wave owns 128 x 64 outputs as 8 x 4
 //    blocks of v_mfma_f32_16x16x32_bf16 (128 fp32 accumulators per lane).  The
 //    LDS bytes read per flop are a quarter of what a 64 x 64 wave tile needs.
-//  * k is staged 64 at a time through two LDS buffers (64 KiB each).  A
-//    K-contiguous operand is stored [row][64 k] (128-byte rows, 16-byte chunks
-//    XOR-swizzled by row); an MN-contiguous operand is stored as it lies in
-//    memory, [k][256 rows] (512-byte rows, chunks XOR-swizzled by k), and its
-//    MFMA fragments are read with the gfx950 LDS transpose read
-//    (ds_read_b64_tr_b16): in each 16-lane group, result lane i element j is the
-//    (i mod 4)-th 16-bit value at the address of lane 4j + i/4, so lanes that
-//    point at 4 consecutive k-rows x 4 column quads receive 4 consecutive k of
-//    one column.  Two such reads give the 8 k-values of an MFMA operand.
-//  * Global -> LDS with buffer_load_dwordx4 ... lds (no staging registers):
-//    the next k-tile's loads are issued before the current tile is multiplied;
-//    one barrier per k-tile (which also waits for those loads).
+//  * k is staged 64 at a time.  A K-contiguous operand is stored [row][64 k]
+//    (128-byte rows, 16-byte chunks XOR-swizzled by row); an MN-contiguous
+//    operand is stored as it lies in memory, [k][256 rows] (512-byte rows,
+//    chunks XOR-swizzled by k), and its MFMA fragments are read with the gfx950
+//    LDS transpose read (ds_read_b64_tr_b16): in each 16-lane group, result lane
+//    i element j is the (i mod 4)-th 16-bit value at the address of lane
+//    4j + i/4, so lanes that point at 4 consecutive k-rows x 4 column quads
+//    receive 4 consecutive k of one column.  Two such reads give the 8 k-values
+//    of an MFMA operand.
+//  * Global -> LDS with buffer_load_dwordx4 ... lds (no staging registers).
+//  * Two schedules:
+//    - both operands K-contiguous (the forward GEMMs): ping-pong.  The wave
+//      groups 0-3 (tile rows 0-127) and 4-7 (rows 128-255), one wave of each on
+//      every SIMD, run one phase apart: while one group reads a k-tile's
+//      fragments from LDS and issues tile loads, the other multiplies the tile
+//      it read before, so the matrix unit of each SIMD has a wave feeding it in
+//      every phase and the multiplying wave never stalls on a memory
+//      instruction.  LDS is a ring of 5 operand slots of 32 KiB: operand tile x
+//      (A of k-tile j is x = 2j, B is 2j+1) sits in slot x mod 5, so a slot is
+//      refilled only after both groups have read it.
+//    - otherwise (a transposed operand): two LDS stages of 64 KiB; all 8 waves
+//      read and multiply each k-tile in step, with the next k-tile's loads issued
+//      first and one barrier per k-tile.  The transpose reads are slower, and
+//      with the phases of a ping-pong the read phase would outlast the multiply
+//      phase; here both share every phase.
 //  * B is the MFMA's first operand, so a lane's accumulator holds 4 consecutive
 //    output columns of one row and the epilogues work on 4-wide vectors.
 //  * Tile order: each of the 8 XCDs gets a contiguous range of tile ids
@@ -36,7 +49,8 @@ namespace {
 constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 512;
 constexpr int kSwigluChannels = 128;               // FFN channels per tile in the SwiGLU forward
 constexpr int kTileU4 = 256 * kBK * 2 / 16;        // uint4 per operand tile (32 KiB)
-constexpr int kStageU4 = 2 * kTileU4;              // A + B
+constexpr int kStageU4 = 2 * kTileU4;              // A + B (two-stage schedule)
+constexpr int kSlots = 5;                          // operand slots (ping-pong schedule)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -108,6 +122,49 @@ __device__ __forceinline__ void issue_tile(const Operand& op, uint4* __restrict_
   }
 }
 
+// Ping-pong loads: a wave's quarter of a K-contiguous operand tile, blocks
+// 8 q .. 8 q + 7 (rows 64 q .. 64 q + 63).  The lane-dependent part of each
+// block's offset is formed once per kernel; the block-dependent part, the same
+// for all lanes, goes in the instruction's SGPR offset.  A block that lies
+// wholly past the operand gets SGPR offset 0, so the sum stays below 2^31 and a
+// lane marked out of range (VGPR offset 0x80000000) stays out of range.
+template <bool SWIGLU>
+struct QuarterLoads {
+  unsigned vbase;     // byte offset of this lane's chunk in block 0
+  int left;           // rows (SwiGLU: channels) from this lane's block-0 row to the operand's end, clamped
+  int k8;             // this lane's k offset inside the tile
+  int64_t first_row;  // block 0's first row (SwiGLU: channel), the same for all lanes
+  int64_t lim;        // rows (SwiGLU: channels) of the operand
+
+  __device__ __forceinline__ QuarterLoads(const Operand& op, const RowMap& rm, int q, int lane) {
+    const int lr = lane >> 3;       // row inside an 8-row block
+    const int c = (lane & 7) ^ lr;  // stored chunk: block rows start at multiples of 8
+    // SwiGLU: logical row 64 q + 8 i + lr is channel base + 32 q + 8 (i & 3) + lr of plane i >> 2
+    first_row = SWIGLU ? rm.base + 32 * q : rm.base + 64 * q;
+    lim = SWIGLU ? rm.ffn : rm.limit;
+    const int64_t d = lim - (first_row + lr);
+    left = d > (1 << 20) ? (1 << 20) : (d < -1 ? -1 : (int)d);
+    vbase = (unsigned)(((first_row + lr) * op.ld + 8 * c) * 2);
+    k8 = 8 * c;
+  }
+
+  __device__ __forceinline__ void issue(const Operand& op, uint4* __restrict__ lds_tile, int q, int64_t k0, int64_t K) {
+    asm volatile("" : "+v"(vbase), "+v"(left), "+v"(k8));  // keep the 8 block offsets from being precomputed
+    uint4* dst = lds_tile + 8 * q * 64;
+    const bool kok = k0 + k8 < K;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int dr = SWIGLU ? 8 * (i & 3) : 8 * i;  // row step of block i within its plane
+      const int64_t plane = SWIGLU ? (i >> 2) * lim : 0;
+      const bool block_in = first_row + dr < lim;  // the same for all lanes
+      const unsigned soff = block_in ? (unsigned)(((plane + dr) * op.ld + k0) * 2) : 0u;
+      const unsigned voff = (kok && dr < left) ? vbase : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (__attribute__((address_space(3))) void*)(dst + i * 64), 16,
+                                               voff, (int)soff, 0, 0);
+    }
+  }
+};
+
 // MFMA operand fragment: 16 rows starting at `row0`, k = 32*s + 8*(lane/16) .. +7.
 template <bool KC>
 __device__ __forceinline__ uint4 read_frag(const uint4* __restrict__ lds, int row0, int s, int lane) {
@@ -169,61 +226,12 @@ __device__ __forceinline__ void read_half(uint4 (&af)[8], uint4 (&bf)[4], const 
   for (int j = 0; j < 4; ++j) bf[j] = read_frag<BKC>(stage + kTileU4, wn * 64 + j * 16, s, lane);
 }
 
-template <bool AK, bool BKC, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int ntm, int ntn) {
-  extern __shared__ uint4 smem[];  // 2 stages x (A tile + B tile) = 128 KiB
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 128 x 64 each
-
-  int tm, tn, ks;
-  tile_coords(blockIdx.x, ntm, ntn, g.ksplit, tm, tn, ks);
-
-  const bf16_t* __restrict__ A = static_cast<const bf16_t*>(g.A);
-  const bf16_t* __restrict__ B = static_cast<const bf16_t*>(g.B);
-  const int64_t K = g.K;
-  // this workgroup's k range [kbeg, kend); the slice length is a multiple of kBK
-  const int64_t kper = ((K + (int64_t)g.ksplit * kBK - 1) / ((int64_t)g.ksplit * kBK)) * kBK;
-  const int64_t kbeg = (int64_t)ks * kper;
-  const int64_t kend = min(K, kbeg + kper);
-  const RowMap ra{(int64_t)tm * kBM, g.M, false, 0};
-  const RowMap rb = (EPI == kEpiSwigluFwd) ? RowMap{(int64_t)tn * kSwigluChannels, g.N, true, g.ffn}
-                                           : RowMap{(int64_t)tn * kBN, g.N, false, 0};
-
-  floatx4 acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  const Operand opa = make_operand(A, AK ? g.M : K, g.lda);
-  const Operand opb = make_operand(B, BKC ? (EPI == kEpiSwigluFwd ? 2 * g.ffn : g.N) : K, g.ldb);
-  const int nk = kend > kbeg ? (int)((kend - kbeg + kBK - 1) / kBK) : 0;
-  issue_tile<AK>(opa, smem, ra, kbeg, kend, wave, lane);
-  issue_tile<BKC>(opb, smem + kTileU4, rb, kbeg, kend, wave, lane);
-  __syncthreads();  // waits for the loads (vmcnt) before the barrier
-
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) {
-      // the other stage was last read in iteration kt - 1, before the barrier that ended it
-      uint4* dst = smem + ((kt + 1) & 1) * kStageU4;
-      const int64_t k0 = kbeg + (int64_t)(kt + 1) * kBK;
-      issue_tile<AK>(opa, dst, ra, k0, kend, wave, lane);
-      issue_tile<BKC>(opb, dst + kTileU4, rb, k0, kend, wave, lane);
-    }
-    const uint4* st = smem + (kt & 1) * kStageU4;
-#pragma unroll
-    for (int s = 0; s < kBK / 32; ++s) {
-      uint4 af[8], bfr[4];
-      read_half<AK, BKC>(af, bfr, st, s, wm, wn, lane);
-      mma_half<AK, BKC>(acc, af, bfr);
-    }
-    __syncthreads();  // next stage landed; this stage free
-  }
-
-  // ------------------------------------------------------------- epilogue
+// Epilogue: acc holds this wave's 128 x 64 outputs; see the Epi enum.
+template <int EPI>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, const floatx4 (&acc)[8][4], int tm, int tn, int ks, int wm,
+                                         int wn, int lane) {
   const int64_t M = g.M, N = g.N, F = g.ffn;
+  asm volatile("" : "+v"(lane));  // addresses are formed here, not kept live through the main loop
   const int col4 = 4 * (lane >> 4), frow = lane & 15;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -290,7 +298,207 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int 
   }
 }
 
+// Ping-pong fragment reads: the 24 ds_read_b128 of one k-tile (A: 8 row blocks,
+// B: 4, each for k 0-31 and 32-63) in one block that also waits for them.  No
+// LDS read is left in flight past it, and the compiler does not add its own
+// wait on the tile loads still in flight (it cannot tell they write other
+// slots).  abase/bbase: this lane's byte address in the first A / B fragment;
+// row block r is 2048 bytes further, and the k 32-63 chunk is at address ^ 64.
+struct Frags {
+  uint4 a[2][8], b[2][4];
+};
+
+__device__ __forceinline__ void read_frags_kc(Frags& f, unsigned abase, unsigned bbase) {
+  asm volatile(
+      "ds_read_b128 %0, %24 offset:0\n"
+      "ds_read_b128 %1, %24 offset:2048\n"
+      "ds_read_b128 %2, %24 offset:4096\n"
+      "ds_read_b128 %3, %24 offset:6144\n"
+      "ds_read_b128 %4, %24 offset:8192\n"
+      "ds_read_b128 %5, %24 offset:10240\n"
+      "ds_read_b128 %6, %24 offset:12288\n"
+      "ds_read_b128 %7, %24 offset:14336\n"
+      "ds_read_b128 %8, %25 offset:0\n"
+      "ds_read_b128 %9, %25 offset:2048\n"
+      "ds_read_b128 %10, %25 offset:4096\n"
+      "ds_read_b128 %11, %25 offset:6144\n"
+      "ds_read_b128 %12, %26 offset:0\n"
+      "ds_read_b128 %13, %26 offset:2048\n"
+      "ds_read_b128 %14, %26 offset:4096\n"
+      "ds_read_b128 %15, %26 offset:6144\n"
+      "ds_read_b128 %16, %26 offset:8192\n"
+      "ds_read_b128 %17, %26 offset:10240\n"
+      "ds_read_b128 %18, %26 offset:12288\n"
+      "ds_read_b128 %19, %26 offset:14336\n"
+      "ds_read_b128 %20, %27 offset:0\n"
+      "ds_read_b128 %21, %27 offset:2048\n"
+      "ds_read_b128 %22, %27 offset:4096\n"
+      "ds_read_b128 %23, %27 offset:6144\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[0][2]), "=&v"(f.a[0][3]), "=&v"(f.a[0][4]), "=&v"(f.a[0][5]),
+        "=&v"(f.a[0][6]), "=&v"(f.a[0][7]), "=&v"(f.b[0][0]), "=&v"(f.b[0][1]), "=&v"(f.b[0][2]), "=&v"(f.b[0][3]),
+        "=&v"(f.a[1][0]), "=&v"(f.a[1][1]), "=&v"(f.a[1][2]), "=&v"(f.a[1][3]), "=&v"(f.a[1][4]), "=&v"(f.a[1][5]),
+        "=&v"(f.a[1][6]), "=&v"(f.a[1][7]), "=&v"(f.b[1][0]), "=&v"(f.b[1][1]), "=&v"(f.b[1][2]), "=&v"(f.b[1][3])
+      : "v"(abase), "v"(bbase), "v"(abase ^ 64u), "v"(bbase ^ 64u)
+      : "memory");
+}
+
+__device__ __forceinline__ void mma_tile(floatx4 (&acc)[8][4], const Frags& f) {
+#pragma unroll
+  for (int s = 0; s < kBK / 32; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.b[s][j]),
+                                                            __builtin_bit_cast(bf16x8, f.a[s][i]), acc[i][j], 0, 0, 0);
+}
+
+// Phase boundary: wait until at most VM of this wave's tile loads are in flight
+// (kNoVm: no wait on them) and its LDS reads are done, then the workgroup
+// barrier.  The scheduling barriers keep the compiler from moving work across.
+constexpr int kNoVm = 63;
+template <int VM>
+__device__ __forceinline__ void phase_end() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x0070);  // vmcnt(VM) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ int slot_u4(int x) { return (x % kSlots) * kTileU4; }
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs g, int ntm, int ntn) {
+  extern __shared__ uint4 smem[];  // 5 operand slots = 160 KiB
+  constexpr bool kSwiglu = EPI == kEpiSwigluFwd;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3, q = wave & 3;
+
+  int tm, tn, ks;
+  tile_coords(blockIdx.x, ntm, ntn, g.ksplit, tm, tn, ks);
+  const int64_t K = g.K;
+  const int64_t kper = ((K + (int64_t)g.ksplit * kBK - 1) / ((int64_t)g.ksplit * kBK)) * kBK;
+  const int64_t kbeg = (int64_t)ks * kper;
+  const int64_t kend = K < kbeg + kper ? K : kbeg + kper;
+  const RowMap ra{(int64_t)tm * kBM, g.M, false, 0};
+  const RowMap rb = kSwiglu ? RowMap{(int64_t)tn * kSwigluChannels, g.N, true, g.ffn}
+                            : RowMap{(int64_t)tn * kBN, g.N, false, 0};
+
+  floatx4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const Operand opa = make_operand(g.A, g.M, g.lda);
+  const Operand opb = make_operand(g.B, kSwiglu ? 2 * g.ffn : g.N, g.ldb);
+  const int nk = kend > kbeg ? (int)((kend - kbeg + kBK - 1) / kBK) : 0;
+  // prologue: every wave loads 4 blocks of each of A_0, B_0, A_1
+  issue_tile<true>(opa, smem + slot_u4(0), ra, kbeg, kend, wave, lane);
+  issue_tile<true>(opb, smem + slot_u4(1), rb, kbeg, kend, wave, lane);
+  if (nk > 1) issue_tile<true>(opa, smem + slot_u4(2), ra, kbeg + kBK, kend, wave, lane);
+  phase_end<0>();
+
+  const unsigned lane_part = (unsigned)((lane & 15) * 128 + (((lane >> 4) ^ (lane & 7)) * 16));
+  const unsigned smem_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+  const unsigned a_lane = smem_addr + lane_part + wm * 128 * 128;  // kc_index(wm*128 + (lane&15), lane>>4) * 16
+  const unsigned b_lane = smem_addr + lane_part + wn * 64 * 128;
+  auto slot_bytes = [](int x) { return (unsigned)(slot_u4(x) * 16); };
+  Frags f;
+  // group A loads B tiles, group B loads A tiles
+  QuarterLoads<kSwiglu> lb(opb, rb, q, lane);
+  QuarterLoads<false> la(opa, ra, q, lane);
+  if (wm == 0) {
+    // phase 2j: read k-tile j, load B of k-tile j+1; phase 2j+1: multiply k-tile j
+    for (int j = 0; j < nk; ++j) {
+      read_frags_kc(f, a_lane + slot_bytes(2 * j), b_lane + slot_bytes(2 * j + 1));
+      if (j + 1 < nk) lb.issue(opb, smem + slot_u4(2 * j + 3), q, kbeg + (int64_t)(j + 1) * kBK, kend);
+      phase_end<kNoVm>();
+      mma_tile(acc, f);
+      phase_end<0>();  // B of k-tile j+1 has landed
+    }
+    if (nk > 0) phase_end<kNoVm>();  // idle in the last phase
+  } else {
+    // phase 2j+1: read k-tile j, load A of k-tile j+2; phase 2j+2: multiply k-tile j
+    if (nk > 0) phase_end<kNoVm>();  // idle in phase 0
+    for (int j = 0; j < nk; ++j) {
+      read_frags_kc(f, a_lane + slot_bytes(2 * j), b_lane + slot_bytes(2 * j + 1));
+      if (j + 2 < nk) {
+        la.issue(opa, smem + slot_u4(2 * j + 4), q, kbeg + (int64_t)(j + 2) * kBK, kend);
+        phase_end<8>();  // A of k-tile j+1 has landed; k-tile j+2's may be in flight
+      } else {
+        phase_end<0>();
+      }
+      mma_tile(acc, f);
+      phase_end<kNoVm>();
+    }
+  }
+  epilogue<EPI>(g, acc, tm, tn, ks, wm, wn, lane);
+}
+
+template <bool AK, bool BKC, int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int ntm, int ntn) {
+  extern __shared__ uint4 smem[];  // 2 stages x (A tile + B tile) = 128 KiB
+  static_assert(!(AK && BKC), "both operands K-contiguous: the ping-pong kernel");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 128 x 64 each
+
+  int tm, tn, ks;
+  tile_coords(blockIdx.x, ntm, ntn, g.ksplit, tm, tn, ks);
+
+  const bf16_t* __restrict__ A = static_cast<const bf16_t*>(g.A);
+  const bf16_t* __restrict__ B = static_cast<const bf16_t*>(g.B);
+  const int64_t K = g.K;
+  // this workgroup's k range [kbeg, kend); the slice length is a multiple of kBK
+  const int64_t kper = ((K + (int64_t)g.ksplit * kBK - 1) / ((int64_t)g.ksplit * kBK)) * kBK;
+  const int64_t kbeg = (int64_t)ks * kper;
+  const int64_t kend = min(K, kbeg + kper);
+  const RowMap ra{(int64_t)tm * kBM, g.M, false, 0};
+  const RowMap rb = (EPI == kEpiSwigluFwd) ? RowMap{(int64_t)tn * kSwigluChannels, g.N, true, g.ffn}
+                                           : RowMap{(int64_t)tn * kBN, g.N, false, 0};
+
+  floatx4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const Operand opa = make_operand(A, AK ? g.M : K, g.lda);
+  const Operand opb = make_operand(B, BKC ? (EPI == kEpiSwigluFwd ? 2 * g.ffn : g.N) : K, g.ldb);
+  const int nk = kend > kbeg ? (int)((kend - kbeg + kBK - 1) / kBK) : 0;
+  issue_tile<AK>(opa, smem, ra, kbeg, kend, wave, lane);
+  issue_tile<BKC>(opb, smem + kTileU4, rb, kbeg, kend, wave, lane);
+  __syncthreads();  // waits for the loads (vmcnt) before the barrier
+
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) {
+      // the other stage was last read in iteration kt - 1, before the barrier that ended it
+      uint4* dst = smem + ((kt + 1) & 1) * kStageU4;
+      const int64_t k0 = kbeg + (int64_t)(kt + 1) * kBK;
+      issue_tile<AK>(opa, dst, ra, k0, kend, wave, lane);
+      issue_tile<BKC>(opb, dst + kTileU4, rb, k0, kend, wave, lane);
+    }
+    const uint4* st = smem + (kt & 1) * kStageU4;
+#pragma unroll
+    for (int s = 0; s < kBK / 32; ++s) {
+      uint4 af[8], bfr[4];
+      read_half<AK, BKC>(af, bfr, st, s, wm, wn, lane);
+      mma_half<AK, BKC>(acc, af, bfr);
+    }
+    __syncthreads();  // next stage landed; this stage free
+  }
+
+  epilogue<EPI>(g, acc, tm, tn, ks, wm, wn, lane);
+}
+
 constexpr size_t kSmemBytes = 2 * kStageU4 * sizeof(uint4);
+constexpr size_t kSmemBytesPingPong = kSlots * kTileU4 * sizeof(uint4);
 
 template <bool AK, bool BKC, int EPI>
 hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
@@ -298,10 +506,14 @@ hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
   const int ntn = (EPI == kEpiSwigluFwd) ? (int)((g.ffn + kSwigluChannels - 1) / kSwigluChannels)
                                          : (int)((g.N + kBN - 1) / kBN);
   if (ntm == 0 || ntn == 0) return hipSuccess;
+  constexpr bool kPingPong = AK && BKC;
+  const void* kernel;
+  if constexpr (kPingPong) kernel = reinterpret_cast<const void*>(&gemm_nt_pingpong_kernel<EPI>);
+  else kernel = reinterpret_cast<const void*>(&gemm_bf16_kernel<AK, BKC, EPI>);
+  constexpr size_t smem = kPingPong ? kSmemBytesPingPong : kSmemBytes;
   static bool configured = false;  // raise the dynamic LDS limit once per instantiation
   if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<AK, BKC, EPI>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytes);
+    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     configured = true;
   }
@@ -310,8 +522,12 @@ hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
   if (ga.ksplit < 1) ga.ksplit = 1;
   {
     KernelTimer timer(g.tag ? g.tag : "gemm", s);
-    hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI>), dim3(ntm * ntn * ga.ksplit), dim3(kThreads), kSmemBytes, s,
-                       ga, ntm, ntn);
+    if constexpr (kPingPong)
+      hipLaunchKernelGGL((gemm_nt_pingpong_kernel<EPI>), dim3(ntm * ntn * ga.ksplit), dim3(kThreads), smem, s, ga, ntm,
+                         ntn);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI>), dim3(ntm * ntn * ga.ksplit), dim3(kThreads), smem, s, ga,
+                         ntm, ntn);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || ga.ksplit == 1) return e;
   }
