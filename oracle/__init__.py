@@ -36,3 +36,14 @@ from .mlp import (  # noqa: F401
     storage_rounding,
 )
 from .sampled import sampled_step  # noqa: F401,E402
+from .optim import (  # noqa: F401,E402
+    ADAM_BETA1,
+    ADAM_BETA2,
+    ADAM_EPS,
+    microbatch_bounds,
+    accumulated_grads,
+    global_grad_norm,
+    clip_coefficient,
+    adamw_update,
+    adamw_step,
+)
