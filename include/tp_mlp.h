@@ -1,6 +1,6 @@
 /*
  * tp_mlp.h - C ABI of one tensor-parallel rank's share of the pre-RMSNorm
- * MLP sublayer (forward, backward, SGD) on an AMD Instinct MI355X (gfx950).
+ * MLP sublayer (forward, backward, SGD or AdamW) on an AMD Instinct MI355X (gfx950).
  *
  * The block is the one rebuilt in "Megatron tensor-parallel MLP"
  * (synapticradio.com), section "Start with the dense block":
@@ -20,7 +20,7 @@
  *
  * Conventions for every call
  *   - All tensor arguments are DEVICE pointers, row-major and contiguous,
- *     16-byte aligned, owned by the caller.  The library allocates no device
+ *     16-byte aligned (rstd: 4-byte aligned), owned by the caller.  The library allocates no device
  *     memory and keeps no device state between calls.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only
  *     enqueue work on it and return; synchronisation is the caller's.
@@ -69,7 +69,14 @@ enum {
   /* Forward: `normed` and `rstd` already hold rms_norm(x) from an earlier call
    * with the same x and norm_w (the replicated input of another shard), so
    * the norm is not recomputed. */
-  TP_MLP_NORMED_READY = 2
+  TP_MLP_NORMED_READY = 2,
+  /* Backward (both phases): add this call's parameter gradients (d_w_in,
+   * d_b_in, d_w_down, d_norm_w, d_b_down) to what those buffers hold instead
+   * of overwriting them: gradient accumulation over the microbatches of a
+   * global batch ("Megatron-LM walkthrough", Part IV, Stage 4: a global batch
+   * is split into microbatches, each run forward and backward, before the
+   * optimiser step).  Activation gradients are always overwritten. */
+  TP_MLP_ACCUMULATE_GRADS = 4
 };
 
 typedef struct {
@@ -79,7 +86,7 @@ typedef struct {
   int32_t act;       /* TP_MLP_ACT_* */
   int32_t dtype;     /* TP_MLP_F32 | TP_MLP_BF16 */
   float eps;         /* RMSNorm epsilon, added to mean(x^2) under the root */
-  int32_t flags;     /* TP_MLP_FUSE_EPILOGUE | TP_MLP_NORMED_READY */
+  int32_t flags;     /* TP_MLP_FUSE_EPILOGUE | TP_MLP_NORMED_READY | TP_MLP_ACCUMULATE_GRADS */
 } tp_mlp_desc;
 
 /*
@@ -179,6 +186,8 @@ typedef struct {
  *   d_x      = d_out + rstd d_normed norm_w - x rstd^3 c        (residual + RMSNorm)
  *   d_norm_w = sum_t d_normed x rstd,   d_b_down = sum_t d_out
  * Column sums are reduced in a fixed order (run-to-run deterministic).
+ * With TP_MLP_ACCUMULATE_GRADS in d->flags, d_w_in, d_b_in, d_w_down,
+ * d_norm_w and d_b_down receive buffer + gradient instead of the gradient.
  * Workspace: at least tp_mlp_workspace_bytes(d, phase) bytes.
  */
 int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* a, void* stream);
@@ -219,6 +228,75 @@ typedef struct {
  */
 int tp_mlp_sgd_step_multi(const tp_mlp_sgd_tensor* list, int32_t count, int32_t param_dtype, float lr,
                           void* stream);
+
+/*
+ * AdamW ("Megatron-LM walkthrough", Part IV, Stage 8: after the gradient norm
+ * is computed and the gradients clipped, AdamW updates the parameters; the
+ * optimiser keeps fp32 moments and fp32 master weights, "Megatron-Core Guide:
+ * 5D Distributed Training Architecture", section 1).  The update is the
+ * published algorithm (Loshchilov & Hutter, decoupled weight decay, with
+ * Adam's bias correction), per element, in fp32:
+ *   g     = grad * s                  (s = *grad_scale, or 1 if grad_scale is NULL)
+ *   m     = beta1 m + (1 - beta1) g
+ *   v     = beta2 v + (1 - beta2) g^2
+ *   theta = theta - lr * ( (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + eps)
+ *                          + weight_decay * theta )
+ * theta is the fp32 master when the tensor has one (then param_out =
+ * round_bf16(theta)), else the parameter itself.
+ */
+typedef struct {
+  float lr;
+  float beta1;         /* in [0, 1) */
+  float beta2;         /* in [0, 1) */
+  float eps;           /* > 0 */
+  float weight_decay;  /* >= 0 */
+  int32_t step;        /* 1 for the first update; the bias corrections use it */
+} tp_mlp_adamw_hparams;
+
+/* One tensor of tp_mlp_adamw_step_multi. */
+typedef struct {
+  const void* param_in;    /* [n] param dtype; read only when there is no master */
+  void* param_out;         /* [n] param dtype (may equal param_in) */
+  const float* grad;       /* [n] fp32 */
+  const float* master_in;  /* [n] fp32 master, or NULL (no master) */
+  float* master_out;       /* [n] fp32 (may equal master_in); NULL iff master_in is */
+  float* m;                /* [n] fp32 first moment, updated in place */
+  float* v;                /* [n] fp32 second moment, updated in place */
+  int64_t n;               /* >= 0 */
+} tp_mlp_adamw_tensor;
+
+/*
+ * tp_mlp_adamw_step_multi - one AdamW update of `count` tensors (one kernel
+ * launch per 32 tensors).  `list` and `hp` are HOST pointers, read before the
+ * call returns.  All tensors share param_dtype; either every tensor has an
+ * fp32 master or none does (masters require param_dtype BF16).  grad_scale is
+ * a DEVICE pointer to one fp32 factor applied to every gradient (for example
+ * the coefficient written by tp_mlp_clip_grad_norm), or NULL.  count >= 0.
+ */
+int tp_mlp_adamw_step_multi(const tp_mlp_adamw_tensor* list, int32_t count, int32_t param_dtype,
+                            const tp_mlp_adamw_hparams* hp, const float* grad_scale, void* stream);
+
+/*
+ * tp_mlp_clip_grad_norm - the global gradient norm and clip coefficient of
+ * Stage 8 ("the gradient norm is computed ... and clipped"):
+ *   norm = sqrt( sum over all tensors and elements of grad^2 )
+ *   coef = min(1, max_norm / (norm + 1e-6))   (coef = 1 when max_norm <= 0)
+ * Squares are summed in fp64 in a fixed order (per 2048-element block, then
+ * the block sums in tensor and block order): run-to-run deterministic.
+ *   grads     HOST array of `count` DEVICE pointers to fp32 gradients
+ *   counts    HOST array of their element counts (each >= 0)
+ *   norm_out  DEVICE fp32 [1] receiving norm, or NULL
+ *   coef_out  DEVICE fp32 [1] receiving coef (pass it as grad_scale to
+ *             tp_mlp_adamw_step_multi; the gradients themselves are unchanged)
+ *   workspace caller-owned DEVICE scratch of at least
+ *             tp_mlp_clip_grad_norm_workspace_bytes(counts, count) bytes
+ */
+int tp_mlp_clip_grad_norm(const float* const* grads, const int64_t* counts, int32_t count, float max_norm,
+                          float* norm_out, float* coef_out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Bytes of workspace tp_mlp_clip_grad_norm needs (counts: HOST array). */
+size_t tp_mlp_clip_grad_norm_workspace_bytes(const int64_t* counts, int32_t count);
 
 /*
  * Kernel timing, a measurement aid (off by default).  While enabled, every

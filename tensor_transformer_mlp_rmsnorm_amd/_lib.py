@@ -19,13 +19,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpmlp.so
 OK, EINVAL, ESHAPE, EDTYPE, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
 ACT_SWIGLU, ACT_GELU = 0, 1
 F32, BF16 = 0, 1
-FUSE_EPILOGUE, NORMED_READY = 1, 2
+FUSE_EPILOGUE, NORMED_READY, ACCUMULATE_GRADS = 1, 2, 4
 BWD_SHARD, BWD_NORM = 0, 1
 
 # every symbol include/tp_mlp.h declares
 EXPORTED = ("tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_workspace_bytes",
             "tp_mlp_sgd_step", "tp_mlp_last_error", "tp_mlp_version", "tp_mlp_profile_enable",
-            "tp_mlp_profile_count", "tp_mlp_profile_entry", "tp_mlp_sgd_step_multi")
+            "tp_mlp_profile_count", "tp_mlp_profile_entry", "tp_mlp_sgd_step_multi", "tp_mlp_adamw_step_multi",
+            "tp_mlp_clip_grad_norm", "tp_mlp_clip_grad_norm_workspace_bytes")
 
 
 class TPMLPError(RuntimeError):
@@ -46,6 +47,17 @@ _vp = ctypes.c_void_p
 class tp_mlp_sgd_tensor(ctypes.Structure):
     _fields_ = [("param_in", ctypes.c_void_p), ("param_out", ctypes.c_void_p), ("grad", ctypes.c_void_p),
                 ("master_in", ctypes.c_void_p), ("master_out", ctypes.c_void_p), ("n", ctypes.c_int64)]
+
+
+class tp_mlp_adamw_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("step", ctypes.c_int32)]
+
+
+class tp_mlp_adamw_tensor(ctypes.Structure):
+    _fields_ = [("param_in", ctypes.c_void_p), ("param_out", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("master_in", ctypes.c_void_p), ("master_out", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
 class tp_mlp_bwd_args(ctypes.Structure):
@@ -80,6 +92,14 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_sgd_step_multi.argtypes = [ctypes.POINTER(tp_mlp_sgd_tensor), ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_float, _vp]
         L.tp_mlp_sgd_step_multi.restype = ctypes.c_int
+        L.tp_mlp_adamw_step_multi.argtypes = [ctypes.POINTER(tp_mlp_adamw_tensor), ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.POINTER(tp_mlp_adamw_hparams), _vp, _vp]
+        L.tp_mlp_adamw_step_multi.restype = ctypes.c_int
+        L.tp_mlp_clip_grad_norm.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(ctypes.c_int64), ctypes.c_int32,
+                                            ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.tp_mlp_clip_grad_norm.restype = ctypes.c_int
+        L.tp_mlp_clip_grad_norm_workspace_bytes.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.c_int32]
+        L.tp_mlp_clip_grad_norm_workspace_bytes.restype = ctypes.c_size_t
         L.tp_mlp_last_error.argtypes = []
         L.tp_mlp_last_error.restype = ctypes.c_char_p
         L.tp_mlp_version.argtypes = []
@@ -166,6 +186,37 @@ def tp_mlp_sgd_step_multi(tensors: Sequence, param_dtype: int, lr: float, stream
     arr = (tp_mlp_sgd_tensor * max(1, len(tensors)))(
         *[tp_mlp_sgd_tensor(_ptr(a), _ptr(b), _ptr(c), _ptr(d), _ptr(e), n) for a, b, c, d, e, n in tensors])
     _check(lib().tp_mlp_sgd_step_multi(arr, len(tensors), param_dtype, lr, _stream(stream)))
+
+
+def make_adamw_hparams(lr: float, step: int, weight_decay: float = 0.0, beta1: float = 0.9, beta2: float = 0.999,
+                       eps: float = 1e-8) -> tp_mlp_adamw_hparams:
+    return tp_mlp_adamw_hparams(lr, beta1, beta2, eps, weight_decay, step)
+
+
+def tp_mlp_adamw_step_multi(tensors: Sequence, param_dtype: int, hp: tp_mlp_adamw_hparams, grad_scale=None,
+                            stream=None) -> None:
+    """``tensors``: sequence of (param_in, param_out, grad, master_in, master_out, m, v, n);
+    ``grad_scale``: a one-element fp32 device tensor (e.g. the clip coefficient) or None."""
+    arr = (tp_mlp_adamw_tensor * max(1, len(tensors)))(
+        *[tp_mlp_adamw_tensor(*[_ptr(t) for t in row[:7]], row[7]) for row in tensors])
+    _check(lib().tp_mlp_adamw_step_multi(arr, len(tensors), param_dtype, ctypes.byref(hp), _ptr(grad_scale),
+                                         _stream(stream)))
+
+
+def tp_mlp_clip_grad_norm_workspace_bytes(counts: Sequence[int]) -> int:
+    arr = (ctypes.c_int64 * max(1, len(counts)))(*counts)
+    return int(lib().tp_mlp_clip_grad_norm_workspace_bytes(arr, len(counts)))
+
+
+def tp_mlp_clip_grad_norm(grads: Sequence, counts: Sequence[int], max_norm: float, norm_out, coef_out, workspace,
+                          workspace_bytes: Optional[int] = None, stream=None) -> None:
+    garr = (_vp * max(1, len(grads)))(*[_ptr(g) for g in grads])
+    carr = (ctypes.c_int64 * max(1, len(counts)))(*counts)
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    _check(lib().tp_mlp_clip_grad_norm(garr, carr, len(grads), max_norm, _ptr(norm_out), _ptr(coef_out),
+                                       _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def tp_mlp_last_error() -> str:

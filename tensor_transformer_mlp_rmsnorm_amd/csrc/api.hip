@@ -1,6 +1,7 @@
 // C ABI of libtpmlp (declared in include/tp_mlp.h): argument checking and the
 // sequence of kernel launches for each call.
 #include <stdarg.h>
+#include <cmath>
 #include <stdio.h>
 
 #include "../../include/tp_mlp.h"
@@ -32,6 +33,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
     if (!aligned16(p)) return fail(TP_MLP_EALIGN, "%s: '%s' is not 16-byte aligned", fn, #p); \
   } while (0)
 
+// rstd is read and written one float at a time: 4-byte alignment suffices
+// (so a row slice of it, a microbatch, is a valid argument).
+#define REQUIRE_PTR4(p)                                                             \
+  do {                                                                              \
+    if (!(p)) return fail(TP_MLP_EINVAL, "%s: argument '%s' is NULL", fn, #p);      \
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return fail(TP_MLP_EALIGN, "%s: '%s' is not 4-byte aligned", fn, #p); \
+  } while (0)
+
 #define CHECK_HIP(expr, where)                  \
   do {                                          \
     const hipError_t e_ = (expr);               \
@@ -47,7 +56,8 @@ int check_desc(const tp_mlp_desc* d, const char* fn) {
     return fail(TP_MLP_ESHAPE, "%s: ffn_local must be a positive multiple of 8", fn);
   if (d->act != TP_MLP_ACT_SWIGLU && d->act != TP_MLP_ACT_GELU) return fail(TP_MLP_EINVAL, "%s: unknown act", fn);
   if (d->dtype != TP_MLP_F32 && d->dtype != TP_MLP_BF16) return fail(TP_MLP_EDTYPE, "%s: unknown dtype", fn);
-  if (d->flags & ~(TP_MLP_FUSE_EPILOGUE | TP_MLP_NORMED_READY)) return fail(TP_MLP_EINVAL, "%s: unknown flags", fn);
+  if (d->flags & ~(TP_MLP_FUSE_EPILOGUE | TP_MLP_NORMED_READY | TP_MLP_ACCUMULATE_GRADS))
+    return fail(TP_MLP_EINVAL, "%s: unknown flags", fn);
   if (!(d->eps >= 0.0f)) return fail(TP_MLP_EINVAL, "%s: eps must be >= 0", fn);
   // Element counts stay below 2^31 so per-tensor int arithmetic in the
   // launchers is safe; byte offsets are 64-bit throughout.
@@ -89,7 +99,7 @@ int tp_mlp_forward(const tp_mlp_desc* d, const void* x, const void* norm_w, cons
   if (T == 0) return TP_MLP_OK;
   REQUIRE_PTR(x);
   REQUIRE_PTR(normed);
-  REQUIRE_PTR(rstd);
+  REQUIRE_PTR4(rstd);
   REQUIRE_PTR(pre_act);
   REQUIRE_PTR(act);
   REQUIRE_PTR(out);
@@ -186,6 +196,7 @@ int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* 
   const int64_t T = d->tokens, H = d->hidden, F = d->ffn_local;
   const bool swiglu = d->act == TP_MLP_ACT_SWIGLU;
   const DType dt = dt_of(d->dtype);
+  const bool accum = (d->flags & TP_MLP_ACCUMULATE_GRADS) != 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t need = tp_mlp_workspace_bytes(d, phase);
   if (need > 0) {
@@ -203,11 +214,11 @@ int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* 
       REQUIRE_PTR(a->d_normed);
       REQUIRE_PTR(a->x);
       REQUIRE_PTR(a->d_out);
-      REQUIRE_PTR(a->rstd);
+      REQUIRE_PTR4(a->rstd);
       REQUIRE_PTR(a->d_x);
     }
     CHECK_HIP(launch_rmsnorm_bwd(dt, a->d_normed, a->x, a->d_out, a->rstd, a->norm_w, a->d_x, a->d_norm_w,
-                                 a->d_b_down, a->workspace, T, H, s),
+                                 a->d_b_down, a->workspace, T, H, accum, s),
               "rmsnorm backward");
     return TP_MLP_OK;
   }
@@ -258,6 +269,7 @@ int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* 
   b2.tag = "gemm_wgrad_down";
   b2.ksplit = gemm_ksplit(b2.M, b2.N, b2.K);
   b2.ws = static_cast<float*>(a->workspace);
+  b2.accum = accum;
   CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b2, s), "d_w_down GEMM");
 
   // d_normed partial = d_pre w_in ([T,P] x [P,H]).
@@ -288,9 +300,11 @@ int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* 
   b4.tag = swiglu ? "gemm_wgrad_gate_up" : "gemm_wgrad_fc1";
   b4.ksplit = gemm_ksplit(b4.M, b4.N, b4.K);
   b4.ws = static_cast<float*>(a->workspace);
+  b4.accum = accum;
   CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b4, s), "d_w_in GEMM");
 
-  if (!swiglu) CHECK_HIP(launch_colsum(dt, a->d_pre, a->d_b_in, a->workspace, T, F, s), "d_b_in column sum");
+  if (!swiglu)
+    CHECK_HIP(launch_colsum(dt, a->d_pre, a->d_b_in, a->workspace, T, F, accum, s), "d_b_in column sum");
   return TP_MLP_OK;
 }
 
@@ -349,6 +363,102 @@ int tp_mlp_sgd_step_multi(const tp_mlp_sgd_tensor* list, int32_t count, int32_t 
                           void* stream) {
   g_err[0] = 0;
   return sgd_list(list, count, param_dtype, lr, stream, "tp_mlp_sgd_step_multi");
+}
+
+int tp_mlp_adamw_step_multi(const tp_mlp_adamw_tensor* list, int32_t count, int32_t param_dtype,
+                            const tp_mlp_adamw_hparams* hp, const float* grad_scale, void* stream) {
+  const char* fn = "tp_mlp_adamw_step_multi";
+  g_err[0] = 0;
+  if (count < 0) return fail(TP_MLP_EINVAL, "%s: count < 0", fn);
+  if (count > 0 && !list) return fail(TP_MLP_EINVAL, "%s: list is NULL", fn);
+  if (!hp) return fail(TP_MLP_EINVAL, "%s: hparams is NULL", fn);
+  if (param_dtype != TP_MLP_F32 && param_dtype != TP_MLP_BF16) return fail(TP_MLP_EDTYPE, "%s: unknown dtype", fn);
+  if (hp->step < 1) return fail(TP_MLP_EINVAL, "%s: step must be >= 1", fn);
+  if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+    return fail(TP_MLP_EINVAL, "%s: betas must lie in [0, 1)", fn);
+  if (!(hp->eps > 0.0f) || !(hp->weight_decay >= 0.0f) || !std::isfinite(hp->lr))
+    return fail(TP_MLP_EINVAL, "%s: eps must be > 0, weight_decay >= 0, lr finite", fn);
+  if (grad_scale && (reinterpret_cast<uintptr_t>(grad_scale) & 3))
+    return fail(TP_MLP_EALIGN, "%s: grad_scale is not 4-byte aligned", fn);
+  const bool master = count > 0 && list[0].master_in != nullptr;
+  for (int i = 0; i < count; ++i) {
+    const tp_mlp_adamw_tensor& t = list[i];
+    if (t.n < 0) return fail(TP_MLP_EINVAL, "%s: n < 0", fn);
+    if ((t.master_in != nullptr) != master)
+      return fail(TP_MLP_EINVAL, "%s: either every tensor has a master copy or none does", fn);
+    if (t.master_in && param_dtype != TP_MLP_BF16)
+      return fail(TP_MLP_EDTYPE, "%s: a master copy is only used with bf16 parameters", fn);
+    if (t.n == 0) continue;
+    void* param_out = t.param_out;
+    const float* grad = t.grad;
+    float* m = t.m;
+    float* v = t.v;
+    REQUIRE_PTR(param_out);
+    REQUIRE_PTR(grad);
+    REQUIRE_PTR(m);
+    REQUIRE_PTR(v);
+    if (master) {
+      float* master_out = t.master_out;
+      REQUIRE_PTR(master_out);
+      if (!aligned16(t.master_in) || !aligned16(master_out))
+        return fail(TP_MLP_EALIGN, "%s: tensor %d master is not 16-byte aligned", fn, i);
+    } else {
+      const void* param_in = t.param_in;
+      REQUIRE_PTR(param_in);
+      if (!aligned16(param_in)) return fail(TP_MLP_EALIGN, "%s: tensor %d param_in is not 16-byte aligned", fn, i);
+    }
+    if (!aligned16(param_out) || !aligned16(grad) || !aligned16(m) || !aligned16(v))
+      return fail(TP_MLP_EALIGN, "%s: tensor %d has a pointer that is not 16-byte aligned", fn, i);
+  }
+  if (count == 0) return TP_MLP_OK;
+  static_assert(sizeof(tp_mlp_adamw_tensor) == sizeof(AdamwTensor), "AdamW tensor layouts match");
+  AdamwConst c;
+  c.lr = hp->lr;
+  c.beta1 = hp->beta1;
+  c.beta2 = hp->beta2;
+  c.eps = hp->eps;
+  c.weight_decay = hp->weight_decay;
+  c.bc1 = (float)(1.0 - std::pow((double)hp->beta1, (double)hp->step));
+  c.bc2 = (float)(1.0 - std::pow((double)hp->beta2, (double)hp->step));
+  CHECK_HIP(launch_adamw(dt_of(param_dtype), reinterpret_cast<const AdamwTensor*>(list), count, master, c, grad_scale,
+                         static_cast<hipStream_t>(stream)),
+            "adamw");
+  return TP_MLP_OK;
+}
+
+size_t tp_mlp_clip_grad_norm_workspace_bytes(const int64_t* counts, int32_t count) {
+  if (count <= 0 || !counts) return 0;
+  for (int i = 0; i < count; ++i)
+    if (counts[i] < 0) return 0;
+  return sumsq_blocks(counts, count) * sizeof(double);
+}
+
+int tp_mlp_clip_grad_norm(const float* const* grads, const int64_t* counts, int32_t count, float max_norm,
+                          float* norm_out, float* coef_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const char* fn = "tp_mlp_clip_grad_norm";
+  g_err[0] = 0;
+  if (count < 0) return fail(TP_MLP_EINVAL, "%s: count < 0", fn);
+  if (count > 0 && (!grads || !counts)) return fail(TP_MLP_EINVAL, "%s: grads or counts is NULL", fn);
+  REQUIRE_PTR(coef_out);
+  if (!std::isfinite(max_norm)) return fail(TP_MLP_EINVAL, "%s: max_norm is not finite", fn);
+  for (int i = 0; i < count; ++i) {
+    if (counts[i] < 0) return fail(TP_MLP_EINVAL, "%s: counts[%d] < 0", fn, i);
+    if (counts[i] == 0) continue;
+    if (!grads[i]) return fail(TP_MLP_EINVAL, "%s: grads[%d] is NULL", fn, i);
+    if (!aligned16(grads[i])) return fail(TP_MLP_EALIGN, "%s: grads[%d] is not 16-byte aligned", fn, i);
+  }
+  const size_t need = tp_mlp_clip_grad_norm_workspace_bytes(counts, count);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(TP_MLP_EWORKSPACE, "%s: workspace of %zu bytes required, %zu given", fn, need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(TP_MLP_EALIGN, "%s: workspace is not 16-byte aligned", fn);
+  }
+  CHECK_HIP(launch_clip_grad_norm(grads, counts, count, max_norm, norm_out, coef_out, static_cast<double*>(workspace),
+                                  static_cast<hipStream_t>(stream)),
+            "gradient norm");
+  return TP_MLP_OK;
 }
 
 }  // extern "C"

@@ -5,8 +5,6 @@
 
 namespace tpmlp {
 
-hipError_t launch_reduce_partial_rows(const float* ws, float* out, int64_t nparts, int64_t cols, hipStream_t s);
-
 namespace {
 
 constexpr int kMaxParts = 64;
@@ -30,26 +28,32 @@ struct SgdList {
   int count;
 };
 
-// out = ((p0 + p1) + ...) + residual + bias, 4 columns per thread-step.
+// out = ((p0 + p1) + ...) + residual + bias, 4 columns per thread.
 // "Split the contraction" (synapticradio.com): the partial down outputs are
-// summed, then the replicated residual and bias are added once.
+// summed, then the replicated residual and bias are added once.  Each partial
+// is read exactly once, so its loads are non-temporal (they do not displace
+// reusable lines from the caches); one 4-column group per thread, no grid-stride
+// loop (the faster form on this memory system).
 template <typename TI, typename TO, bool RES, bool BIAS>
 __global__ __launch_bounds__(256) void partial_sum_kernel(PartList parts, int n_parts, int64_t n4, int64_t cols4,
                                                           const TI* __restrict__ residual, const TI* __restrict__ bias,
                                                           TO* __restrict__ out) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4; e += stride) {
-    floatx4 acc = load4<float>(parts.p[0] + 4 * e);
-    for (int k = 1; k < n_parts; ++k) acc += load4<float>(parts.p[k] + 4 * e);
+    floatx4 acc = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(parts.p[0] + 4 * e));
+    for (int k = 1; k < n_parts; ++k)
+      acc += __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(parts.p[k] + 4 * e));
     if constexpr (RES) acc += load4<TI>(residual + 4 * e);
     if constexpr (BIAS) acc += load4<TI>(bias + 4 * (e % cols4));
     store4<TO>(out + 4 * e, acc);
   }
 }
 
+// One work item per thread up to 2^31 - 1 workgroups; the kernels still loop
+// (grid-stride) so any size is covered.
 inline unsigned grid_for(int64_t n, int64_t per_block) {
   int64_t b = (n + per_block - 1) / per_block;
-  const int64_t cap = 256 * 32;  // 32 workgroups per CU, grid-stride beyond that
+  const int64_t cap = 0x7fffffff;
   if (b > cap) b = cap;
   return (unsigned)(b < 1 ? 1 : b);
 }
@@ -171,7 +175,8 @@ size_t colsum_workspace(int64_t rows, int64_t cols) {
   return (size_t)(nb * cols) * sizeof(float);
 }
 
-hipError_t launch_colsum(DType dt, const void* in, float* out, void* ws, int64_t rows, int64_t cols, hipStream_t s) {
+hipError_t launch_colsum(DType dt, const void* in, float* out, void* ws, int64_t rows, int64_t cols, bool accum,
+                         hipStream_t s) {
   const int64_t nb = (rows + kColRows - 1) / kColRows;
   float* w = static_cast<float*>(ws);
   if (nb > 0) {
@@ -186,7 +191,7 @@ hipError_t launch_colsum(DType dt, const void* in, float* out, void* ws, int64_t
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_reduce_partial_rows(w, out, nb, cols, s);
+  return launch_reduce_partial_rows(w, out, nb, cols, accum, s);
 }
 
 hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, float lr, hipStream_t s) {

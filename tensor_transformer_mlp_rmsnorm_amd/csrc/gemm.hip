@@ -297,7 +297,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g, int ntm, 
         if (n >= N) continue;
         const floatx4 v = acc[i][j];
         if constexpr (EPI == kEpiStoreF32) {
-          store4<float>(static_cast<float*>(g.C) + m * g.ldc + n, v);
+          float* c = static_cast<float*>(g.C) + m * g.ldc + n;
+          store4<float>(c, g.accum ? v + load4<float>(c) : v);
         } else if constexpr (EPI == kEpiResidual) {
           const floatx4 xr = load4<T>(static_cast<const T*>(g.aux) + m * g.ldc + n);
           const floatx4 bb = load4<T>(static_cast<const T*>(g.bias) + n);

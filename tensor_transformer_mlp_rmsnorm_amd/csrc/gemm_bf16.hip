@@ -260,7 +260,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const floatx4 (&acc)
         const floatx4 v = acc[i][j];
         if constexpr (EPI == kEpiStoreF32) {
           float* c = ks == 0 ? static_cast<float*>(g.C) : g.ws + (int64_t)(ks - 1) * M * g.ldc;
-          store4<float>(c + m * g.ldc + n, v);
+          store4<float>(c + m * g.ldc + n, (g.accum && ks == 0) ? v + load4<float>(c + m * g.ldc + n) : v);
         } else if constexpr (EPI == kEpiResidual) {
           const floatx4 xr = load4<bf16_t>(static_cast<const bf16_t*>(g.aux) + m * g.ldc + n);
           const floatx4 bb = load4<bf16_t>(static_cast<const bf16_t*>(g.bias) + n);

@@ -58,6 +58,9 @@ struct GemmArgs {
   // kernel adds the slices to C in index order.  ksplit = 1 ignores ws.
   int ksplit;
   float* ws;
+  // kEpiStoreF32 only: add C's current values to the product (slice 0 reads
+  // and adds them; with a k split the other slices are then added as usual).
+  int accum;
 };
 
 // Number of k-slices for a bf16 fp32-output GEMM: a function of the shape only
@@ -84,15 +87,19 @@ hipError_t launch_rmsnorm_fwd(DType dt, const void* x, const void* w, void* n, f
 // RMSNorm backward + residual: dx, and per-block column partials of
 // d_norm_w and d_b_down in `ws` followed by the fixed-order reduction.
 size_t rmsnorm_bwd_workspace(int64_t T, int64_t H);
+// With `accum`, dw and db receive their current values plus the column sums.
 hipError_t launch_rmsnorm_bwd(DType dt, const float* dN, const void* x, const void* dY,
                               const float* rstd, const void* w, void* dx, float* dw, float* db,
-                              void* ws, int64_t T, int64_t H, hipStream_t s);
+                              void* ws, int64_t T, int64_t H, bool accum, hipStream_t s);
 
 // Column sums of a [rows, cols] matrix in dtype dt into fp32 out[cols], in a
-// fixed order (two stages through `ws`).
+// fixed order (two stages through `ws`); with `accum` added to out's values.
 size_t colsum_workspace(int64_t rows, int64_t cols);
-hipError_t launch_colsum(DType dt, const void* in, float* out, void* ws, int64_t rows, int64_t cols,
+hipError_t launch_colsum(DType dt, const void* in, float* out, void* ws, int64_t rows, int64_t cols, bool accum,
                          hipStream_t s);
+// out[c] = (accum ? out[c] : 0) + sum_{b=0}^{nparts-1} ws[b][c], in a fixed order.
+hipError_t launch_reduce_partial_rows(const float* ws, float* out, int64_t nparts, int64_t cols, bool accum,
+                                      hipStream_t s);
 
 hipError_t launch_partial_sum(const float* const* parts, int n_parts, int64_t rows, int64_t cols,
                               const void* residual, const void* bias, DType in_dt, void* out,
@@ -114,5 +121,30 @@ struct SgdTensor {
 // One SGD update of every tensor in `list` (all in dtype dt; all with fp32
 // masters when `master`).
 hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, float lr, hipStream_t s);
+
+struct AdamwTensor {
+  const void* param_in;
+  void* param_out;
+  const float* grad;
+  const float* master_in;
+  float* master_out;
+  float* m;
+  float* v;
+  int64_t n;
+};
+struct AdamwConst {
+  float lr, beta1, beta2, eps, weight_decay;
+  float bc1, bc2;  // 1 - beta1^step, 1 - beta2^step (formed in double on the host)
+};
+// One AdamW update of every tensor in `list` (dtype dt; fp32 masters when
+// `master`); `scale` is a device pointer to the gradient factor, or null.
+hipError_t launch_adamw(DType dt, const AdamwTensor* list, int count, bool master, const AdamwConst& c,
+                        const float* scale, hipStream_t s);
+
+// Global gradient norm: per-2048-element-block fp64 sums of squares into ws,
+// then one workgroup adds them in order and writes norm and the clip factor.
+size_t sumsq_blocks(const int64_t* counts, int count);
+hipError_t launch_clip_grad_norm(const float* const* grads, const int64_t* counts, int count, float max_norm,
+                                 float* norm_out, float* coef_out, double* ws, hipStream_t s);
 
 }  // namespace tpmlp

@@ -162,14 +162,15 @@ __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_kernel(
 
 }  // namespace
 
-// Fixed-order sum over `nparts` partial rows: out[c] = sum_{b=0}^{nparts-1} ws[b][c].
+// Fixed-order sum over `nparts` partial rows: out[c] = sum_{b=0}^{nparts-1} ws[b][c]
+// (added to out's current value when `accum`).
 // A workgroup owns 32 columns; its 8 waves-quarters each sum a contiguous
 // eighth of the rows (in row order) for one column, and the 8 group sums are
 // added in group order.  The order depends only on nparts: deterministic.
 constexpr int kRedCols = 32, kRedGroups = 8;
 
 __global__ __launch_bounds__(256) void reduce_partial_rows_kernel(const float* __restrict__ ws, float* __restrict__ out,
-                                                                  int64_t nparts, int64_t cols) {
+                                                                  int64_t nparts, int64_t cols, int accum) {
   __shared__ float part[kRedGroups][kRedCols];
   const int tc = threadIdx.x % kRedCols, grp = threadIdx.x / kRedCols;
   const int64_t c = (int64_t)blockIdx.x * kRedCols + tc;
@@ -184,15 +185,16 @@ __global__ __launch_bounds__(256) void reduce_partial_rows_kernel(const float* _
     float s = part[0][tc];
 #pragma unroll
     for (int g = 1; g < kRedGroups; ++g) s += part[g][tc];
-    out[c] = s;
+    out[c] = accum ? out[c] + s : s;
   }
 }
 
-hipError_t launch_reduce_partial_rows(const float* ws, float* out, int64_t nparts, int64_t cols, hipStream_t s) {
+hipError_t launch_reduce_partial_rows(const float* ws, float* out, int64_t nparts, int64_t cols, bool accum,
+                                      hipStream_t s) {
   if (cols == 0) return hipSuccess;
   KernelTimer timer("column_reduce", s);
   hipLaunchKernelGGL(reduce_partial_rows_kernel, dim3((unsigned)((cols + kRedCols - 1) / kRedCols)), dim3(256), 0, s,
-                     ws, out, nparts, cols);
+                     ws, out, nparts, cols, accum ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -211,7 +213,7 @@ size_t rmsnorm_bwd_workspace(int64_t T_, int64_t H) {
 
 template <typename T>
 static hipError_t bwd_t(const float* dN, const void* x, const void* dY, const float* rstd, const void* w, void* dx,
-                        float* dw, float* db, void* ws, int64_t T_, int64_t H, hipStream_t s) {
+                        float* dw, float* db, void* ws, int64_t T_, int64_t H, bool accum, hipStream_t s) {
   const int64_t rpb = bwd_rows_per_block(T_);
   const int64_t nblk = (T_ + rpb - 1) / rpb;
   float* ws_dw = static_cast<float*>(ws);
@@ -237,17 +239,17 @@ static hipError_t bwd_t(const float* dN, const void* x, const void* dY, const fl
     if (e != hipSuccess) return e;
   }
   hipError_t e;
-  e = launch_reduce_partial_rows(ws_dw, dw, nblk, H, s);
+  e = launch_reduce_partial_rows(ws_dw, dw, nblk, H, accum, s);
   if (e != hipSuccess) return e;
-  return launch_reduce_partial_rows(ws_db, db, nblk, H, s);
+  return launch_reduce_partial_rows(ws_db, db, nblk, H, accum, s);
 }
 
 hipError_t launch_rmsnorm_bwd(DType dt, const float* dN, const void* x, const void* dY, const float* rstd,
                               const void* w, void* dx, float* dw, float* db, void* ws, int64_t T_, int64_t H,
-                              hipStream_t s) {
-  // T = 0 still writes the (empty, zero) column sums.
-  if (dt == kBF16) return bwd_t<bf16_t>(dN, x, dY, rstd, w, dx, dw, db, ws, T_, H, s);
-  return bwd_t<float>(dN, x, dY, rstd, w, dx, dw, db, ws, T_, H, s);
+                              bool accum, hipStream_t s) {
+  // T = 0 still writes the (empty, zero) column sums (or leaves accumulated ones as they are).
+  if (dt == kBF16) return bwd_t<bf16_t>(dN, x, dY, rstd, w, dx, dw, db, ws, T_, H, accum, s);
+  return bwd_t<float>(dN, x, dY, rstd, w, dx, dw, db, ws, T_, H, accum, s);
 }
 
 }  // namespace tpmlp

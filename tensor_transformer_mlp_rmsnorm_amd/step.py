@@ -11,7 +11,13 @@ all-reduces of the method become tp_partial_sum at the same two points
   backward  shard s: tp_mlp_backward(SHARD, d_out = out) -> dN_s and the shard's weight grads
             dN  = tp_partial_sum(dN_0..dN_{S-1})                      (backward boundary)
             tp_mlp_backward(NORM) -> dx, d_norm_w, d_b_down
-  update    tp_mlp_sgd_step_multi over every parameter tensor (one launch)
+  update    tp_mlp_sgd_step_multi over every parameter tensor (one launch), or
+            tp_mlp_clip_grad_norm + tp_mlp_adamw_step_multi
+
+A global batch can be run as microbatches ("Megatron-LM walkthrough", Part IV,
+Stage 4): contiguous token slices, each run forward and backward on row views
+of the same buffers, the weight gradients accumulated in fp32
+(TP_MLP_ACCUMULATE_GRADS) before one optimiser step (Stage 8).
 
 Work that every rank repeats on replicated data (the RMSNorm forward, the
 RMSNorm backward, the update of norm_w and b_down) is done once here: its
@@ -39,6 +45,20 @@ MODES = ("equivalence", "missing_forward_reduce", "missing_backward_reduce")
 
 def _torch_dtype(name: str):
     return {"bf16": torch.bfloat16, "fp32": torch.float32}[name]
+
+
+def microbatch_bounds(tokens: int, microbatches: int) -> List[tuple]:
+    """Contiguous token slices [lo, hi): the first tokens % microbatches
+    slices hold one token more than the rest."""
+    if microbatches < 1:
+        raise ValueError("microbatches must be >= 1")
+    base, extra = divmod(tokens, microbatches)
+    out, lo = [], 0
+    for i in range(microbatches):
+        hi = lo + base + (1 if i < extra else 0)
+        out.append((lo, hi))
+        lo = hi
+    return out
 
 
 class ShardedStep:
@@ -115,13 +135,17 @@ class ShardedStep:
         ws = max(L.tp_mlp_workspace_bytes(self._desc(), L.BWD_NORM),
                  L.tp_mlp_workspace_bytes(self._desc(), L.BWD_SHARD), 16)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        # AdamW state, allocated by the first adamw() call
+        self.adam_m: Optional[Dict[str, torch.Tensor]] = None
+        self.adam_v: Optional[Dict[str, torch.Tensor]] = None
+        self.adam_steps = 0
         # per-shard outputs of the ablation modes, allocated on first use
         self._abl: Dict[str, list] = {}
 
     # ------------------------------------------------------------ helpers
-    def _desc(self, flags: int = 0) -> L.tp_mlp_desc:
+    def _desc(self, flags: int = 0, tokens: Optional[int] = None) -> L.tp_mlp_desc:
         w = self.w
-        return L.make_desc(self.T, self.H, self.F, self.act, self.cdt, w.eps, flags)
+        return L.make_desc(self.T if tokens is None else tokens, self.H, self.F, self.act, self.cdt, w.eps, flags)
 
     def _param_list(self):
         out = [("norm_w", self.norm_w), ("b_down", self.b_down)]
@@ -146,15 +170,23 @@ class ShardedStep:
         return self._abl[name]
 
     # -------------------------------------------------------------- phases
-    def forward(self, mode: str = "equivalence") -> None:
-        T, H = self.T, self.H
+    def forward(self, mode: str = "equivalence", rows: Optional[slice] = None) -> None:
+        """Forward of every shard on token rows ``rows`` (default: all)."""
+        r = rows if rows is not None else slice(0, self.T)
+        T, H = r.stop - r.start, self.H
         st = self.stream
         for s, sh in enumerate(self.shards):
             flags = (L.NORMED_READY if s > 0 else 0) | (L.FUSE_EPILOGUE if self.fuse else 0)
-            L.tp_mlp_forward(self._desc(flags), self.x, self.norm_w, sh["w_in"], sh["b_in"], sh["w_down"],
-                             self.normed, self.rstd, sh["pre"], sh["act"], self.out if self.fuse else sh["z"],
-                             self.b_down, stream=st)
+            L.tp_mlp_forward(self._desc(flags, T), self.x[r], self.norm_w, sh["w_in"], sh["b_in"], sh["w_down"],
+                             self.normed[r], self.rstd[r], sh["pre"][r], sh["act"][r],
+                             self.out[r] if self.fuse else sh["z"][r], self.b_down, stream=st)
         if self.fuse:
+            return
+        if rows is not None:
+            if mode != "equivalence":
+                raise ValueError("microbatches run in equivalence mode only")
+            L.tp_partial_sum([sh["z"][r] for sh in self.shards], T, H, self.x[r], self.b_down, self.cdt, self.out[r],
+                             self.cdt, stream=st)
             return
         if mode == "missing_forward_reduce":
             outs = self._abl_bufs("out", (T, H), self.dt)
@@ -164,16 +196,31 @@ class ShardedStep:
             L.tp_partial_sum([sh["z"] for sh in self.shards], T, H, self.x, self.b_down, self.cdt, self.out,
                              self.cdt, stream=st)
 
-    def _shard_backward(self, sh, d_out) -> None:
-        L.tp_mlp_backward(self._desc(), L.BWD_SHARD, stream=self.stream, normed=self.normed, pre_act=sh["pre"],
-                          act=sh["act"], w_in=sh["w_in"], w_down=sh["w_down"], d_out=d_out, d_pre=sh["d_pre"],
-                          d_w_in=sh["d_w_in"], d_b_in=sh["d_b_in"], d_w_down=sh["d_w_down"],
-                          d_normed_part=sh["dN_part"], workspace=self.workspace)
+    def _shard_backward(self, sh, d_out, r: slice = slice(None), flags: int = 0) -> None:
+        T = self.T if r.start is None else r.stop - r.start
+        L.tp_mlp_backward(self._desc(flags, T), L.BWD_SHARD, stream=self.stream, normed=self.normed[r],
+                          pre_act=sh["pre"][r], act=sh["act"][r], w_in=sh["w_in"], w_down=sh["w_down"],
+                          d_out=d_out, d_pre=sh["d_pre"][r], d_w_in=sh["d_w_in"], d_b_in=sh["d_b_in"],
+                          d_w_down=sh["d_w_down"], d_normed_part=sh["dN_part"][r], workspace=self.workspace)
 
-    def _norm_backward(self, dN, d_out, dx, d_norm_w, d_b_down) -> None:
-        L.tp_mlp_backward(self._desc(), L.BWD_NORM, stream=self.stream, x=self.x, rstd=self.rstd,
+    def _norm_backward(self, dN, d_out, dx, d_norm_w, d_b_down, r: slice = slice(None), flags: int = 0) -> None:
+        T = self.T if r.start is None else r.stop - r.start
+        L.tp_mlp_backward(self._desc(flags, T), L.BWD_NORM, stream=self.stream, x=self.x[r], rstd=self.rstd[r],
                           norm_w=self.norm_w, d_out=d_out, d_normed=dN, d_x=dx, d_norm_w=d_norm_w,
                           d_b_down=d_b_down, workspace=self.workspace)
+
+    def backward_rows(self, rows: slice, accumulate: bool) -> None:
+        """Backward of one microbatch (token rows ``rows``, equivalence mode);
+        with ``accumulate`` the weight gradients are added to the buffers."""
+        r, T, H = rows, rows.stop - rows.start, self.H
+        flags = L.ACCUMULATE_GRADS if accumulate else 0
+        for sh in self.shards:
+            self._shard_backward(sh, self.out[r], r, flags)
+        dN = self.dN[r]
+        if not self.fuse:
+            L.tp_partial_sum([sh["dN_part"][r] for sh in self.shards], T, H, None, None, L.F32, dN, L.F32,
+                             stream=self.stream)
+        self._norm_backward(dN, self.out[r], self.dx[r], self.d_norm_w, self.d_b_down, r, flags)
 
     def backward(self, mode: str = "equivalence") -> None:
         T, H = self.T, self.H
@@ -205,11 +252,50 @@ class ShardedStep:
                 lst.append((t, self.new[name], g, None, None, t.numel()))
         L.tp_mlp_sgd_step_multi(lst, self.cdt, self.w.lr, stream=self.stream)
 
-    def step(self, mode: str = "equivalence", update: bool = True) -> None:
-        self.forward(mode)
-        self.backward(mode)
+    def adamw(self, lr: float, weight_decay: float = 0.0, max_norm: float = 0.0, beta1: float = 0.9,
+              beta2: float = 0.999, eps: float = 1e-8) -> None:
+        """Global-norm clip coefficient, then one AdamW update of every
+        parameter tensor (fp32 moments kept on the device; the step count
+        advances by one).  Updates go to the same targets as sgd()."""
+        params = self._param_list()
+        if self.adam_m is None:
+            self.adam_m = {n: torch.zeros(t.shape, dtype=torch.float32, device=self.dev) for n, t in params}
+            self.adam_v = {n: torch.zeros(t.shape, dtype=torch.float32, device=self.dev) for n, t in params}
+            counts = [t.numel() for _, t in params]
+            nbytes = max(L.tp_mlp_clip_grad_norm_workspace_bytes(counts), 16)
+            self._norm_ws = torch.empty(nbytes, dtype=torch.uint8, device=self.dev)
+            self.grad_norm = torch.zeros(1, dtype=torch.float32, device=self.dev)
+            self.clip_coef = torch.ones(1, dtype=torch.float32, device=self.dev)
+        grads = [self._grad_of(n) for n, _ in params]
+        L.tp_mlp_clip_grad_norm(grads, [g.numel() for g in grads], max_norm, self.grad_norm, self.clip_coef,
+                                self._norm_ws, stream=self.stream)
+        self.adam_steps += 1
+        hp = L.make_adamw_hparams(lr, self.adam_steps, weight_decay, beta1, beta2, eps)
+        lst = []
+        for (name, t), g in zip(params, grads):
+            m, v = self.adam_m[name], self.adam_v[name]
+            if self.masters is not None:
+                lst.append((None, self.new[name], g, self.masters[name], self.new_masters[name], m, v, t.numel()))
+            else:
+                lst.append((t, self.new[name], g, None, None, m, v, t.numel()))
+        L.tp_mlp_adamw_step_multi(lst, self.cdt, hp, grad_scale=self.clip_coef, stream=self.stream)
+
+    def step(self, mode: str = "equivalence", update: bool = True, microbatches: int = 1) -> None:
+        """Forward, backward and (``update``) the SGD step.  With
+        ``microbatches`` > 1 the tokens run as that many contiguous slices
+        whose weight gradients accumulate (equivalence mode only)."""
+        if microbatches > 1:
+            if mode != "equivalence":
+                raise ValueError("microbatches run in equivalence mode only")
+            for i, (lo, hi) in enumerate(microbatch_bounds(self.T, microbatches)):
+                self.forward(mode, slice(lo, hi))
+                self.backward_rows(slice(lo, hi), accumulate=i > 0)
+        else:
+            self.forward(mode)
+            self.backward(mode)
         if update and mode == "equivalence":
             self.sgd()
+
 
     # ------------------------------------------------------------- results
     def results(self, mode: str = "equivalence") -> dict:

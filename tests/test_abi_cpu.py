@@ -158,7 +158,70 @@ def test_sgd_multi_checks(lib):
     assert f(arr(T(None, None, None, None, None, 0)), 1, L.BF16, 0.1, None) == L.OK  # n = 0: no-op
 
 
+def test_adamw_checks(lib):
+    T = L.tp_mlp_adamw_tensor
+    arr = lambda *ts: (T * max(1, len(ts)))(*ts)
+    hp = L.make_adamw_hparams(1e-3, 1, weight_decay=0.1)
+    f = lambda a, n, dt=L.BF16, h=hp, scale=None: lib.tp_mlp_adamw_step_multi(a, n, dt, ctypes.byref(h) if h else None,
+                                                                                scale, None)
+    plain = T(A, A, A, None, None, A, A, 8)
+    withm = T(None, A, A, A, A, A, A, 8)
+    assert f(None, 0) == L.OK                                     # nothing to do
+    assert f(None, 1) == L.EINVAL                                 # list missing
+    assert f(arr(plain), -1) == L.EINVAL
+    assert f(arr(plain), 1, h=None) == L.EINVAL                   # hparams missing
+    assert f(arr(plain), 1, dt=7) == L.EDTYPE
+    assert f(arr(withm), 1, dt=L.F32) == L.EDTYPE                 # masters only with bf16
+    assert f(arr(plain, withm), 2) == L.EINVAL                    # mixed masters
+    assert f(arr(T(A, A, None, None, None, A, A, 8)), 1) == L.EINVAL   # no grad
+    assert f(arr(T(A, A, A, None, None, None, A, 8)), 1) == L.EINVAL   # no m
+    assert f(arr(T(None, A, A, A, None, A, A, 8)), 1) == L.EINVAL      # master_out missing
+    assert f(arr(T(A, A, A, None, None, A, MIS, 8)), 1) == L.EALIGN
+    assert f(arr(T(A, A, A, None, None, A, A, -1)), 1) == L.EINVAL
+    assert f(arr(T(None, None, None, None, None, None, None, 0)), 1) == L.OK  # n = 0: no-op
+    assert f(arr(plain), 1, scale=A + 2) == L.EALIGN                   # grad_scale must be 4-byte aligned
+    for bad in (L.make_adamw_hparams(1e-3, 0), L.make_adamw_hparams(1e-3, 1, beta1=1.0),
+                L.make_adamw_hparams(1e-3, 1, beta2=-0.1), L.make_adamw_hparams(1e-3, 1, eps=0.0),
+                L.make_adamw_hparams(1e-3, 1, weight_decay=-1.0), L.make_adamw_hparams(float("inf"), 1)):
+        assert f(arr(plain), 1, h=bad) == L.EINVAL
+
+
+def test_clip_grad_norm_checks(lib):
+    P = ctypes.c_void_p
+    ptrs = lambda *p: (P * max(1, len(p)))(*p)
+    cnts = lambda *c: (ctypes.c_int64 * max(1, len(c)))(*c)
+    ws_bytes = lib.tp_mlp_clip_grad_norm_workspace_bytes
+    # one fp64 partial per started 2048-element block of each tensor
+    assert ws_bytes(cnts(1, 2048, 2049, 0), 4) == 8 * (1 + 1 + 2 + 0)
+    assert ws_bytes(None, 0) == 0 and ws_bytes(cnts(-1), 1) == 0
+    f = lib.tp_mlp_clip_grad_norm
+    assert f(ptrs(A), cnts(8), -1, 1.0, A, A, A, 4096, None) == L.EINVAL
+    assert f(None, None, 1, 1.0, A, A, A, 4096, None) == L.EINVAL
+    assert f(ptrs(A), cnts(8), 1, 1.0, A, None, A, 4096, None) == L.EINVAL       # coef_out missing
+    assert f(ptrs(A), cnts(-8), 1, 1.0, A, A, A, 4096, None) == L.EINVAL
+    assert f(ptrs(None), cnts(8), 1, 1.0, A, A, A, 4096, None) == L.EINVAL
+    assert f(ptrs(MIS), cnts(8), 1, 1.0, A, A, A, 4096, None) == L.EALIGN
+    assert f(ptrs(A), cnts(8), 1, 1.0, A, A, None, 0, None) == L.EWORKSPACE
+    assert f(ptrs(A), cnts(3000), 1, 1.0, A, A, A, 8, None) == L.EWORKSPACE       # needs 16 bytes
+    assert f(ptrs(A), cnts(8), 1, 1.0, A, A, MIS, 4096, None) == L.EALIGN
+    assert f(ptrs(A), cnts(8), 1, float("nan"), A, A, A, 4096, None) == L.EINVAL
+
+
+def test_backward_rejects_unknown_flags(lib):
+    d = L.make_desc(4, 8, 8, L.ACT_SWIGLU, L.F32, 1e-6, flags=8)
+    a = L.tp_mlp_bwd_args()
+    assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EINVAL
+
+
 def test_binding_raises_with_message(lib):
     with pytest.raises(L.TPMLPError) as ei:
         L.tp_partial_sum([A], 4, 6, None, None, L.F32, A + 4096, L.F32, stream=0)
     assert ei.value.code == L.ESHAPE and "multiple of 4" in str(ei.value)
+
+
+def test_step_driver_api():
+    """The step driver (the path bench.py and the GPU tests run) exposes its phases."""
+    from tensor_transformer_mlp_rmsnorm_amd import step
+    for m in ("forward", "backward", "backward_rows", "sgd", "adamw", "step", "results"):
+        assert callable(getattr(step.ShardedStep, m, None)), m
+    assert step.microbatch_bounds(7, 3) == [(0, 3), (3, 5), (5, 7)]
