@@ -47,3 +47,4 @@ from .optim import (  # noqa: F401,E402
     adamw_update,
     adamw_step,
 )
+from .sequence import SP_MODES, sequence_parallel_step, sequence_slices  # noqa: F401,E402
