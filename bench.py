@@ -13,6 +13,13 @@ Prints one JSON line.  `value` is the algorithmic GEMM TFLOP/s of the whole
 step (18 T H F_full flops per step for SwiGLU); per-kernel times come from
 HIP events the library records on its launch stream during the timed steps.
 The CPU oracle is timed on a bounded token slice of the same workload.
+
+After the timed step, `optimizer_path` reports the optimiser side on the same
+workload (unless --no-extras): the global-norm clip plus AdamW over every
+shard's parameters (each kernel against HBM bandwidth), and the step run as 2
+microbatches whose weight gradients accumulate in fp32.  `sequence_parallel`
+times the same step in the sequence-parallel layout (norm, residual and bias
+on each rank's token rows; reduce-scatter and all-gather at the boundaries).
 """
 
 from __future__ import annotations
@@ -59,6 +66,9 @@ def hbm_bytes_per_step(w) -> dict:
         "partial_sum": S * 4 * T * H + 4 * T * H,                        # S fp32 partials in, dN out
         "rmsnorm_bwd": T * H * (4 + 3 * es) + 4 * T + H * es,           # dN, x, dY in, dx out
         "sgd": n_params * per_param,                                     # p (or master), g in; p (+master) out
+        # optimiser path: AdamW reads g, m, v and p (or master) and writes m, v, p (+ master)
+        "adamw": n_params * ((4 + 4 + 4 + 8 + 8 + es) if w.master else (2 * es + 4 + 8 + 8)),
+        "grad_norm": n_params * 4,                                         # every fp32 gradient read once
     }
 
 
@@ -142,6 +152,61 @@ def cpu_baseline(w, t, budget_s: float = 15.0) -> dict:
             "host_cpus": os.cpu_count()}
 
 
+def optimizer_path(st, w, steps: int, warmup: int) -> dict:
+    """The clip + AdamW update (its kernels against HBM bandwidth) and the
+    step run as 2 accumulating microbatches, on the benchmark's step object."""
+    import torch
+    from tensor_transformer_mlp_rmsnorm_amd import _lib as L
+
+    hp = dict(lr=1e-4, weight_decay=0.1, max_norm=1.0)
+    for _ in range(max(1, warmup)):
+        st.adamw(**hp)
+    torch.cuda.synchronize()
+    L.tp_mlp_profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.adamw(**hp)
+    torch.cuda.synchronize()
+    upd_ms = (time.perf_counter() - t0) / steps * 1e3
+    L.tp_mlp_profile_enable(False)
+    prof = L.tp_mlp_profile_entries()
+    res = {"update": "global-norm clip (max_norm 1.0) + AdamW (lr 1e-4, wd 0.1), every shard's parameters",
+           "update_ms": upd_ms,
+           "kernels": {k: roofline_entry(k, n, tot, w, steps) for k, (n, tot) in prof.items()}}
+    for _ in range(max(1, warmup)):
+        st.step(microbatches=2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.step(microbatches=2)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    res["microbatch_step"] = {"microbatches": 2, "tokens_each": w.tokens // 2, "ms_per_step": ms,
+                              "tflops": w.flops_per_step / (ms / 1e3) / 1e12,
+                              "note": "forward + backward per microbatch, fp32 gradient accumulation, one SGD update"}
+    return res
+
+
+def sequence_parallel_timing(w, t, steps: int, warmup: int) -> dict:
+    """The step in the sequence-parallel layout, same inputs and flop count."""
+    import torch
+    from tensor_transformer_mlp_rmsnorm_amd.step import SequenceParallelStep
+
+    sp = SequenceParallelStep(w, t, device="cuda:0", out_of_place_sgd=True)
+    for _ in range(max(1, warmup)):
+        sp.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sp.step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    del sp
+    torch.cuda.empty_cache()
+    return {"ranks": w.shards, "tokens_per_rank_slice": w.tokens // w.shards, "ms_per_step": ms,
+            "tflops": w.flops_per_step / (ms / 1e3) / 1e12}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +215,7 @@ def main() -> int:
     ap.add_argument("--workload", default="llama3_8b_tp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-extras", action="store_true", help="skip the optimiser-path measurements")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -224,6 +290,10 @@ def main() -> int:
         "roofline": roof,
         "kernels": kernels,
     }
+    if not args.no_extras:
+        out["optimizer_path"] = optimizer_path(st, w, args.steps, args.warmup)
+        if w.n_run == w.shards and w.shards > 1:
+            out["sequence_parallel"] = sequence_parallel_timing(w, t, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         del st
         torch.cuda.empty_cache()

@@ -114,6 +114,21 @@ int tp_mlp_forward(const tp_mlp_desc* d, const void* x, const void* norm_w, cons
                    void* pre_act, void* act, void* out, const void* b_down, void* stream);
 
 /*
+ * tp_rmsnorm_forward - the RMSNorm of tp_mlp_forward on its own, for a
+ * sequence-parallel rank's slice of the token rows ("Megatron-LM
+ * walkthrough", Part V, "Deep dive: sequence parallelism": the norm runs on
+ * each rank's slice of the sequence; the slices are then gathered into the
+ * full normed input of the tensor-parallel region, which tp_mlp_forward takes
+ * with TP_MLP_NORMED_READY).
+ *   rstd_t = 1 / sqrt(mean_i x[t,i]^2 + eps),   normed[t,i] = x[t,i] rstd_t w[i]
+ *   x [rows, hidden] dtype; w [hidden] dtype; normed [rows, hidden] dtype;
+ *   rstd [rows] fp32.  hidden: positive multiple of 8, <= 16384; rows >= 0
+ *   (0 is a no-op).  dtype TP_MLP_F32 | TP_MLP_BF16.
+ */
+int tp_rmsnorm_forward(int64_t rows, int64_t hidden, int32_t dtype, float eps, const void* x, const void* w,
+                       void* normed, float* rstd, void* stream);
+
+/*
  * tp_partial_sum - the sum that stands in for the all-reduce at the two
  * tensor-parallel boundaries ("Split the contraction": partial outputs summed,
  * then residual and bias added once; "Put the other collective in backward":

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     TPMLPError,
     tp_mlp_forward,
     tp_partial_sum,
+    tp_rmsnorm_forward,
     tp_mlp_backward,
     tp_mlp_workspace_bytes,
     tp_mlp_sgd_step,
@@ -25,7 +26,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "TPMLPError", "tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_workspace_bytes",
+    "TPMLPError", "tp_mlp_forward", "tp_partial_sum", "tp_rmsnorm_forward", "tp_mlp_backward", "tp_mlp_workspace_bytes",
     "tp_mlp_sgd_step", "tp_mlp_sgd_step_multi", "tp_mlp_adamw_step_multi", "tp_mlp_clip_grad_norm",
     "tp_mlp_clip_grad_norm_workspace_bytes", "make_adamw_hparams", "tp_mlp_last_error", "tp_mlp_version",
     "make_desc",

@@ -26,7 +26,7 @@ BWD_SHARD, BWD_NORM = 0, 1
 EXPORTED = ("tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_workspace_bytes",
             "tp_mlp_sgd_step", "tp_mlp_last_error", "tp_mlp_version", "tp_mlp_profile_enable",
             "tp_mlp_profile_count", "tp_mlp_profile_entry", "tp_mlp_sgd_step_multi", "tp_mlp_adamw_step_multi",
-            "tp_mlp_clip_grad_norm", "tp_mlp_clip_grad_norm_workspace_bytes")
+            "tp_mlp_clip_grad_norm", "tp_mlp_clip_grad_norm_workspace_bytes", "tp_rmsnorm_forward")
 
 
 class TPMLPError(RuntimeError):
@@ -100,6 +100,9 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_clip_grad_norm.restype = ctypes.c_int
         L.tp_mlp_clip_grad_norm_workspace_bytes.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.c_int32]
         L.tp_mlp_clip_grad_norm_workspace_bytes.restype = ctypes.c_size_t
+        L.tp_rmsnorm_forward.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, _vp, _vp,
+                                         _vp, _vp, _vp]
+        L.tp_rmsnorm_forward.restype = ctypes.c_int
         L.tp_mlp_last_error.argtypes = []
         L.tp_mlp_last_error.restype = ctypes.c_char_p
         L.tp_mlp_version.argtypes = []
@@ -144,6 +147,11 @@ def tp_mlp_forward(desc: tp_mlp_desc, x, norm_w, w_in, b_in, w_down, normed, rst
     _check(lib().tp_mlp_forward(ctypes.byref(desc), _ptr(x), _ptr(norm_w), _ptr(w_in), _ptr(b_in), _ptr(w_down),
                                 _ptr(normed), _ptr(rstd), _ptr(pre_act), _ptr(act), _ptr(out), _ptr(b_down),
                                 _stream(stream)))
+
+
+def tp_rmsnorm_forward(rows: int, hidden: int, dtype: int, eps: float, x, w, normed, rstd, stream=None) -> None:
+    _check(lib().tp_rmsnorm_forward(rows, hidden, dtype, eps, _ptr(x), _ptr(w), _ptr(normed), _ptr(rstd),
+                                    _stream(stream)))
 
 
 def tp_partial_sum(parts: Sequence, rows: int, cols: int, residual, bias, in_dtype: int, out, out_dtype: int,

@@ -169,6 +169,25 @@ int tp_partial_sum(const float* const* parts, int32_t n_parts, int64_t rows, int
   return TP_MLP_OK;
 }
 
+int tp_rmsnorm_forward(int64_t rows, int64_t hidden, int32_t dtype, float eps, const void* x, const void* w,
+                       void* normed, float* rstd, void* stream) {
+  const char* fn = "tp_rmsnorm_forward";
+  g_err[0] = 0;
+  if (rows < 0) return fail(TP_MLP_EINVAL, "%s: rows < 0", fn);
+  if (hidden <= 0 || hidden % 8 != 0 || hidden > 16384)
+    return fail(TP_MLP_ESHAPE, "%s: hidden must be a positive multiple of 8, at most 16384", fn);
+  if (dtype != TP_MLP_F32 && dtype != TP_MLP_BF16) return fail(TP_MLP_EDTYPE, "%s: unknown dtype", fn);
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(TP_MLP_EINVAL, "%s: eps must be finite and >= 0", fn);
+  if (rows == 0) return TP_MLP_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(normed);
+  REQUIRE_PTR4(rstd);
+  CHECK_HIP(launch_rmsnorm_fwd(dt_of(dtype), x, w, normed, rstd, rows, hidden, eps, static_cast<hipStream_t>(stream)),
+            "rmsnorm forward");
+  return TP_MLP_OK;
+}
+
 size_t tp_mlp_workspace_bytes(const tp_mlp_desc* d, int32_t phase) {
   if (!d || d->tokens < 0 || d->hidden <= 0 || d->ffn_local <= 0) return 0;
   const int64_t T = d->tokens, H = d->hidden, F = d->ffn_local;

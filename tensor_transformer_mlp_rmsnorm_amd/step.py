@@ -61,6 +61,12 @@ def microbatch_bounds(tokens: int, microbatches: int) -> List[tuple]:
     return out
 
 
+def sequence_slices(tokens: int, ranks: int) -> List[tuple]:
+    """Token rows [lo, hi) of each sequence-parallel rank (the sequence axis
+    is outermost in [T, H], so a rank's slice is a contiguous row block)."""
+    return microbatch_bounds(tokens, ranks)
+
+
 class ShardedStep:
     """Device buffers and the call sequence of one step of a workload.
 
@@ -331,4 +337,94 @@ class ShardedStep:
             r["master_norm_w"], r["master_b_down"] = nm["norm_w"], nm["b_down"]
             r["master_w_in"] = cat_in([nm[f"w_in.{s}"] for s in range(n)])
             r["master_w_down"] = torch.cat([nm[f"w_down.{s}"] for s in range(n)], dim=1)
+        return r
+
+
+class SequenceParallelStep(ShardedStep):
+    """The step in the sequence-parallel layout ("Megatron-LM walkthrough",
+    Part V, "Deep dive: sequence parallelism"; Part IV, Stages 5 and 7).
+
+    Rank r of the S ranks owns FFN channels as in ShardedStep and, outside
+    the tensor-parallel linears, the contiguous token rows slices[r] of the
+    sequence:
+
+      forward   rank r: tp_rmsnorm_forward on its rows -> its rows of N
+                (the all-gather entering the region: every rank's rows land
+                in the one full N buffer the region reads)
+                shard s: tp_mlp_forward(NORMED_READY) on all T rows -> z_s
+                rank r: tp_partial_sum of rows slices[r] of z_0..z_{S-1}
+                + x + b_down -> its rows of out    (the reduce-scatter)
+      backward  shard s: tp_mlp_backward(SHARD) with d_out = out on all rows
+                (the all-gather of dY) -> dN_s
+                rank r: tp_partial_sum of its rows of dN_0..dN_{S-1}
+                (the reduce-scatter), then tp_mlp_backward(NORM) on its rows
+                -> its rows of dx and its own d_norm_w, d_b_down
+                d_norm_w, d_b_down = tp_partial_sum over the ranks (the
+                replicated parameters' gradients summed over the group)
+
+    Mode "missing_norm_grad_reduce" leaves out that last sum: each rank keeps
+    the gradient of its own rows.  Every rank runs, one after the other."""
+
+    MODES = ("equivalence", "missing_norm_grad_reduce")
+
+    def __init__(self, w, tensors, device="cuda", out_of_place_sgd: bool = False, stream=None):
+        super().__init__(w, tensors, device, out_of_place_sgd, stream)
+        if w.n_run != w.shards:
+            raise ValueError("the sequence-parallel step runs every rank")
+        S, H = w.shards, self.H
+        self.slices = sequence_slices(self.T, S)
+        self.rank_d_norm_w = torch.empty((S, H), dtype=torch.float32, device=self.dev)
+        self.rank_d_b_down = torch.empty((S, H), dtype=torch.float32, device=self.dev)
+
+    def forward(self, mode: str = "equivalence", rows=None) -> None:
+        if rows is not None:
+            raise ValueError("the sequence-parallel step takes the whole batch")
+        T, H, st = self.T, self.H, self.stream
+        for lo, hi in self.slices:
+            L.tp_rmsnorm_forward(hi - lo, H, self.cdt, self.w.eps, self.x[lo:hi], self.norm_w, self.normed[lo:hi],
+                                 self.rstd[lo:hi], stream=st)
+        for sh in self.shards:
+            flags = L.NORMED_READY | (L.FUSE_EPILOGUE if self.fuse else 0)
+            L.tp_mlp_forward(self._desc(flags), self.x, self.norm_w, sh["w_in"], sh["b_in"], sh["w_down"], self.normed,
+                             self.rstd, sh["pre"], sh["act"], self.out if self.fuse else sh["z"], self.b_down, stream=st)
+        if self.fuse:
+            return
+        for lo, hi in self.slices:
+            L.tp_partial_sum([sh["z"][lo:hi] for sh in self.shards], hi - lo, H, self.x[lo:hi], self.b_down, self.cdt,
+                             self.out[lo:hi], self.cdt, stream=st)
+
+    def backward(self, mode: str = "equivalence") -> None:
+        if mode not in self.MODES:
+            raise ValueError(mode)
+        H = self.H
+        for sh in self.shards:
+            self._shard_backward(sh, self.out)
+        for r, (lo, hi) in enumerate(self.slices):
+            dN = self.dN[lo:hi]
+            if not self.fuse:
+                L.tp_partial_sum([sh["dN_part"][lo:hi] for sh in self.shards], hi - lo, H, None, None, L.F32, dN, L.F32,
+                                 stream=self.stream)
+            self._norm_backward(dN, self.out[lo:hi], self.dx[lo:hi], self.rank_d_norm_w[r], self.rank_d_b_down[r],
+                                slice(lo, hi))
+        if mode == "equivalence":
+            S = len(self.slices)
+            L.tp_partial_sum([self.rank_d_norm_w[r] for r in range(S)], 1, H, None, None, L.F32, self.d_norm_w, L.F32,
+                             stream=self.stream)
+            L.tp_partial_sum([self.rank_d_b_down[r] for r in range(S)], 1, H, None, None, L.F32, self.d_b_down,
+                             L.F32, stream=self.stream)
+
+    def step(self, mode: str = "equivalence", update: bool = True, microbatches: int = 1) -> None:
+        if microbatches != 1:
+            raise ValueError("the sequence-parallel step takes the whole batch")
+        self.forward(mode)
+        self.backward(mode)
+        if update and mode == "equivalence":
+            self.sgd()
+
+    def results(self, mode: str = "equivalence") -> dict:
+        r = super().results("equivalence")
+        if mode == "missing_norm_grad_reduce":
+            c = lambda t: t.detach().float().cpu()
+            r["d_norm_w"] = [c(t) for t in self.rank_d_norm_w]
+            r["d_b_down"] = [c(t) for t in self.rank_d_b_down]
         return r

@@ -207,6 +207,19 @@ def test_clip_grad_norm_checks(lib):
     assert f(ptrs(A), cnts(8), 1, float("nan"), A, A, A, 4096, None) == L.EINVAL
 
 
+def test_rmsnorm_forward_checks(lib):
+    f = lib.tp_rmsnorm_forward
+    assert f(-1, 64, L.BF16, 1e-6, A, A, A, A, None) == L.EINVAL
+    assert f(4, 60, L.BF16, 1e-6, A, A, A, A, None) == L.ESHAPE
+    assert f(4, 16392, L.BF16, 1e-6, A, A, A, A, None) == L.ESHAPE
+    assert f(4, 64, 5, 1e-6, A, A, A, A, None) == L.EDTYPE
+    assert f(4, 64, L.BF16, float("nan"), A, A, A, A, None) == L.EINVAL
+    assert f(4, 64, L.BF16, 1e-6, None, A, A, A, None) == L.EINVAL
+    assert f(4, 64, L.BF16, 1e-6, A, A, MIS, A, None) == L.EALIGN
+    assert f(4, 64, L.BF16, 1e-6, A, A, A, A + 2, None) == L.EALIGN   # rstd: 4-byte alignment
+    assert f(0, 64, L.BF16, 1e-6, None, None, None, None, None) == L.OK  # no rows: no-op
+
+
 def test_backward_rejects_unknown_flags(lib):
     d = L.make_desc(4, 8, 8, L.ACT_SWIGLU, L.F32, 1e-6, flags=8)
     a = L.tp_mlp_bwd_args()

@@ -1,0 +1,124 @@
+"""Parity of the sequence-parallel step (SequenceParallelStep, through the C
+ABI) with the CPU oracle.  The sequence-parallel step reproduces the dense
+step (pinned in tests/test_oracle_sequence.py), so its outputs are compared
+with oracle.dense_step like the tensor-parallel step's; its ablation, which
+leaves out the sum of the norm-weight and bias gradients over the ranks, is
+compared per rank with oracle.sequence_parallel_step.  The full Llama-3-8B
+TP=8 workload is checked on sampled rows, channels and columns."""
+
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tolerance import check
+from test_gpu_parity import _gather, _sample, compare_full, np_params, storage_of
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tensor_transformer_mlp_rmsnorm_amd import _lib
+    _lib.lib()  # must load: there is no fallback
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def run_sp(w, t, mode="equivalence"):
+    from tensor_transformer_mlp_rmsnorm_amd.step import SequenceParallelStep
+    say(f"[gpu] sequence-parallel {w.name} T={w.tokens} H={w.hidden} F_full={w.ffn_full} S={w.shards} "
+        f"{w.act} {w.dtype} mode={mode}")
+    st = SequenceParallelStep(w, t, out_of_place_sgd=True)
+    st.step(mode)
+    torch.cuda.synchronize()
+    return st
+
+
+SMALL = [
+    # name,                   T,   H,   F_full, S, act,      dtype
+    ("fp32_tiny_S2", 4, 8, 16, 2, "swiglu", "fp32"),
+    ("fp32_swiglu_ragged_S3", 257, 136, 144, 3, "swiglu", "fp32"),
+    ("bf16_swiglu_S4", 300, 256, 384, 4, "swiglu", "bf16"),
+    ("bf16_gelu_ragged_S2", 129, 264, 272, 2, "gelu", "bf16"),
+    ("bf16_swiglu_S1", 200, 128, 136, 1, "swiglu", "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_sequence_parallel_small_parity(case):
+    name, T, H, Ff, S, act, dt = case
+    w = synth.Workload(name, tokens=T, hidden=H, ffn_full=Ff, shards=S, act=act, dtype=dt, w_std=0.05,
+                       seed=300 + T)
+    t = synth.draw(w, perturb=True)
+    res = run_sp(w, t).results()
+    d = oracle.dense_step(synth.to_numpy64(t["x"]), np_params(t), w.act, w.eps, w.lr, storage=storage_of(w))
+    report = {}
+    compare_full(w, res, d, report, strict_fp32=name.startswith("fp32_tiny"))
+    check("rstd", res["rstd"], d["rstd"], "fp32-scaled" if dt == "fp32" else dt, report=report)
+    say(f"  worst: {max(report.items(), key=lambda kv: kv[1])}")
+
+
+def test_missing_norm_grad_reduce_matches_oracle():
+    """Without the sum over ranks each rank holds the norm-weight and bias
+    gradients of its own rows only: equal to the oracle's per-rank values,
+    adding up to the dense gradient, each alone different from it."""
+    w = synth.Workload("sp_ablation", tokens=9, hidden=8, ffn_full=24, shards=3, act="swiglu", dtype="fp32",
+                       w_std=0.5, seed=41)
+    t = synth.draw(w, perturb=True)
+    mode = "missing_norm_grad_reduce"
+    res = run_sp(w, t, mode).results(mode)
+    x, p = synth.to_numpy64(t["x"]), np_params(t)
+    sp = oracle.sequence_parallel_step(x, p, w.act, w.eps, w.lr, w.shards, mode=mode)
+    dense = oracle.dense_step(x, p, w.act, w.eps, w.lr)
+    # gradients of O(10-100) here: the fp32 bound is relative to the tensor's scale (tests/tolerance.py)
+    tol = "fp32-scaled"
+    for r, rk in enumerate(sp["ranks"]):
+        check(f"d_norm_w[{r}]", res["d_norm_w"][r], rk["d_norm_w"], tol)
+        check(f"d_b_down[{r}]", res["d_b_down"][r], rk["d_b_down"], tol)
+        gap = float(np.max(np.abs(res["d_norm_w"][r].double().numpy() - dense["grads"]["norm_w"])))
+        assert gap > 1e-2 * float(np.abs(dense["grads"]["norm_w"]).max()), \
+            f"rank {r}: its own-rows gradient should differ from the group's"
+    check("sum d_norm_w", sum(res["d_norm_w"]), dense["grads"]["norm_w"], tol)
+    check("out", res["out"], dense["out"], tol)
+    check("dx", res["dx"], dense["dx"], tol)
+
+
+def test_sequence_parallel_full_size_sampled():
+    """The Llama-3-8B TP=8 workload in the sequence-parallel layout: the whole
+    output and sampled rows / FFN channels / hidden columns of everything else."""
+    w = synth.workload("llama3_8b_tp8")
+    t = synth.draw(w)
+    st = run_sp(w, t)
+    rng = np.random.default_rng(w.seed + 1)
+    rows = _sample(rng, w.tokens, 48, must=[0, w.tokens - 1] + [lo for lo, _ in st.slices])
+    chans = _sample(rng, w.ffn_full, 48, must=[0, w.ffn_full - 1, w.ffn_local - 1, w.ffn_local])
+    cols = _sample(rng, w.hidden, 48, must=[0, w.hidden - 1])
+    got = _gather(st, rows, chans, cols)
+    del st
+    torch.cuda.empty_cache()
+    t0 = time.time()
+    ref = oracle.sampled_step(synth.to_numpy64(t["x"]).astype(np.float32), np_params(t), w.act, w.eps, w.lr,
+                              rows, chans, cols, dtype=np.float32, storage=storage_of(w))
+    say(f"  oracle sampled step: {time.time() - t0:.1f} s")
+    report = {}
+    check("out", got["out"], ref["out"], w.dtype, rowwise=True, report=report)
+    check("dx_rows", got["dx_rows"], ref["dx_rows"], w.dtype, rowwise=True, report=report)
+    check("dN_rows", got["dN_rows"], ref["dN_rows"], w.dtype, rowwise=True, report=report)
+    check("act_chans", got["act_chans"], ref["act_chans"], w.dtype, report=report)
+    for k in ("d_b_down", "d_norm_w_cols", "d_w_down_chans", "d_w_in_chans", "new_norm_w_cols", "new_b_down",
+              "new_w_down_chans", "new_w_in_chans"):
+        check(k, got[k], ref[k], w.dtype, report=report)
+    say(f"  worst: {max(report.items(), key=lambda kv: kv[1])}")
