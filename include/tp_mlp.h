@@ -296,7 +296,7 @@ int tp_mlp_adamw_step_multi(const tp_mlp_adamw_tensor* list, int32_t count, int3
  * Stage 8 ("the gradient norm is computed ... and clipped"):
  *   norm = sqrt( sum over all tensors and elements of grad^2 )
  *   coef = min(1, max_norm / (norm + 1e-6))   (coef = 1 when max_norm <= 0)
- * Squares are summed in fp64 in a fixed order (per 2048-element block, then
+ * Squares are summed in fp64 in a fixed order (per 16384-element block, then
  * the block sums in tensor and block order): run-to-run deterministic.
  *   grads     HOST array of `count` DEVICE pointers to fp32 gradients
  *   counts    HOST array of their element counts (each >= 0)

@@ -191,8 +191,8 @@ def test_clip_grad_norm_checks(lib):
     ptrs = lambda *p: (P * max(1, len(p)))(*p)
     cnts = lambda *c: (ctypes.c_int64 * max(1, len(c)))(*c)
     ws_bytes = lib.tp_mlp_clip_grad_norm_workspace_bytes
-    # one fp64 partial per started 2048-element block of each tensor
-    assert ws_bytes(cnts(1, 2048, 2049, 0), 4) == 8 * (1 + 1 + 2 + 0)
+    # one fp64 partial per started 16384-element block of each tensor
+    assert ws_bytes(cnts(1, 16384, 16385, 0), 4) == 8 * (1 + 1 + 2 + 0)
     assert ws_bytes(None, 0) == 0 and ws_bytes(cnts(-1), 1) == 0
     f = lib.tp_mlp_clip_grad_norm
     assert f(ptrs(A), cnts(8), -1, 1.0, A, A, A, 4096, None) == L.EINVAL
@@ -202,7 +202,7 @@ def test_clip_grad_norm_checks(lib):
     assert f(ptrs(None), cnts(8), 1, 1.0, A, A, A, 4096, None) == L.EINVAL
     assert f(ptrs(MIS), cnts(8), 1, 1.0, A, A, A, 4096, None) == L.EALIGN
     assert f(ptrs(A), cnts(8), 1, 1.0, A, A, None, 0, None) == L.EWORKSPACE
-    assert f(ptrs(A), cnts(3000), 1, 1.0, A, A, A, 8, None) == L.EWORKSPACE       # needs 16 bytes
+    assert f(ptrs(A), cnts(20000), 1, 1.0, A, A, A, 8, None) == L.EWORKSPACE      # needs 16 bytes
     assert f(ptrs(A), cnts(8), 1, 1.0, A, A, MIS, 4096, None) == L.EALIGN
     assert f(ptrs(A), cnts(8), 1, float("nan"), A, A, A, 4096, None) == L.EINVAL
 
