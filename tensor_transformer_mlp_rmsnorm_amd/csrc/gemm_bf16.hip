@@ -52,6 +52,20 @@ constexpr int kTileU4 = 256 * kBK * 2 / 16;        // uint4 per operand tile (32
 constexpr int kStageU4 = 2 * kTileU4;              // A + B (two-stage schedule)
 constexpr int kSlots = 5;                          // operand slots (ping-pong schedule)
 
+// Output tile shapes of the two-stage kernel: the tile (TM x TN), its wave grid
+// (GM x GN = 8 waves) and each wave's 16 x 16 MFMA blocks (WMB x WNB).  Loads
+// always fill 256-row operand tiles; a 224-wide tile just leaves 32 of them
+// unused.  224 = 7 x 32 makes 1792- and 3584-wide GEMMs exactly 8 and 16 tiles.
+struct Tile256x256 {
+  static constexpr int TM = 256, TN = 256, GN = 4, WMB = 8, WNB = 4;
+};
+struct Tile256x224 {
+  static constexpr int TM = 256, TN = 224, GN = 2, WMB = 4, WNB = 7;
+};
+struct Tile224x256 {
+  static constexpr int TM = 224, TN = 256, GN = 4, WMB = 7, WNB = 4;
+};
+
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -207,40 +221,43 @@ __device__ __forceinline__ void tile_coords(int pid, int ntm, int ntn, int nks, 
   tn = t / gsize;
 }
 
-template <bool AK, bool BKC>
-__device__ __forceinline__ void mma_half(floatx4 (&acc)[8][4], const uint4 (&af)[8], const uint4 (&bf)[4]) {
+template <int WMB, int WNB>
+__device__ __forceinline__ void mma_half(floatx4 (&acc)[WMB][WNB], const uint4 (&af)[WMB], const uint4 (&bf)[WNB]) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < WMB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WNB; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bf[j]),
                                                           __builtin_bit_cast(bf16x8, af[i]), acc[i][j], 0, 0, 0);
 }
 
-template <bool AK, bool BKC>
-__device__ __forceinline__ void read_half(uint4 (&af)[8], uint4 (&bf)[4], const uint4* stage, int s, int wm, int wn,
-                                          int lane) {
+template <bool AK, bool BKC, int WMB, int WNB>
+__device__ __forceinline__ void read_half(uint4 (&af)[WMB], uint4 (&bf)[WNB], const uint4* stage, int s, int wm,
+                                          int wn, int lane) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) af[i] = read_frag<AK>(stage, wm * 128 + i * 16, s, lane);
+  for (int i = 0; i < WMB; ++i) af[i] = read_frag<AK>(stage, wm * WMB * 16 + i * 16, s, lane);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) bf[j] = read_frag<BKC>(stage + kTileU4, wn * 64 + j * 16, s, lane);
+  for (int j = 0; j < WNB; ++j) bf[j] = read_frag<BKC>(stage + kTileU4, wn * WNB * 16 + j * 16, s, lane);
 }
 
-// Epilogue: acc holds this wave's 128 x 64 outputs; see the Epi enum.
-template <int EPI>
-__device__ __forceinline__ void epilogue(const GemmArgs& g, const floatx4 (&acc)[8][4], int tm, int tn, int ks, int wm,
-                                         int wn, int lane) {
+// Epilogue: acc holds this wave's (16 WMB) x (16 WNB) outputs from row m0 and
+// column n0 (SwiGLU forward: 32 channels from ch0, gate blocks then up blocks);
+// see the Epi enum.
+template <int EPI, int WMB, int WNB>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, const floatx4 (&acc)[WMB][WNB], int64_t m0, int64_t n0,
+                                         int64_t ch0, int ks, int lane) {
   const int64_t M = g.M, N = g.N, F = g.ffn;
   asm volatile("" : "+v"(lane));  // addresses are formed here, not kept live through the main loop
   const int col4 = 4 * (lane >> 4), frow = lane & 15;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t m = (int64_t)tm * kBM + wm * 128 + i * 16 + frow;
+  for (int i = 0; i < WMB; ++i) {
+    const int64_t m = m0 + i * 16 + frow;
     if (m >= M) continue;
     if constexpr (EPI == kEpiSwigluFwd) {
+      static_assert(WNB == 4, "SwiGLU pairing: 2 gate blocks then 2 up blocks per wave");
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int64_t ch = (int64_t)tn * kSwigluChannels + wn * 32 + j * 16 + col4;
+        const int64_t ch = ch0 + j * 16 + col4;
         if (ch >= F) continue;
         // g and u are stored tensors: the activation is formed from their stored values
         const floatx4 gv = stored<bf16_t>(acc[i][j]), uv = stored<bf16_t>(acc[i][j + 2]);
@@ -254,8 +271,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const floatx4 (&acc)
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t n = (int64_t)tn * kBN + wn * 64 + j * 16 + col4;
+      for (int j = 0; j < WNB; ++j) {
+        const int64_t n = n0 + j * 16 + col4;
         if (n >= N) continue;
         const floatx4 v = acc[i][j];
         if constexpr (EPI == kEpiStoreF32) {
@@ -437,17 +454,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
       phase_end<kNoVm>();
     }
   }
-  epilogue<EPI>(g, acc, tm, tn, ks, wm, wn, lane);
+  epilogue<EPI, 8, 4>(g, acc, (int64_t)tm * kBM + wm * 128, (int64_t)tn * kBN + wn * 64,
+                      (int64_t)tn * kSwigluChannels + wn * 32, ks, lane);
 }
 
-template <bool AK, bool BKC, int EPI>
+template <bool AK, bool BKC, int EPI, class SH>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int ntm, int ntn) {
   extern __shared__ uint4 smem[];  // 2 stages x (A tile + B tile) = 128 KiB
   static_assert(!(AK && BKC), "both operands K-contiguous: the ping-pong kernel");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 128 x 64 each
+  const int wm = wave / SH::GN, wn = wave % SH::GN;
 
   int tm, tn, ks;
   tile_coords(blockIdx.x, ntm, ntn, g.ksplit, tm, tn, ks);
@@ -459,18 +477,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int 
   const int64_t kper = ((K + (int64_t)g.ksplit * kBK - 1) / ((int64_t)g.ksplit * kBK)) * kBK;
   const int64_t kbeg = (int64_t)ks * kper;
   const int64_t kend = min(K, kbeg + kper);
-  const RowMap ra{(int64_t)tm * kBM, g.M, false, 0};
-  const RowMap rb = (EPI == kEpiSwigluFwd) ? RowMap{(int64_t)tn * kSwigluChannels, g.N, true, g.ffn}
-                                           : RowMap{(int64_t)tn * kBN, g.N, false, 0};
+  static_assert(EPI != kEpiSwigluFwd, "the SwiGLU forward is a K-contiguous (ping-pong) GEMM");
+  const RowMap ra{(int64_t)tm * SH::TM, g.M, false, 0};
+  const RowMap rb{(int64_t)tn * SH::TN, g.N, false, 0};
 
-  floatx4 acc[8][4];
+  floatx4 acc[SH::WMB][SH::WNB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < SH::WMB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < SH::WNB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const Operand opa = make_operand(A, AK ? g.M : K, g.lda);
-  const Operand opb = make_operand(B, BKC ? (EPI == kEpiSwigluFwd ? 2 * g.ffn : g.N) : K, g.ldb);
+  const Operand opb = make_operand(B, BKC ? g.N : K, g.ldb);
   const int nk = kend > kbeg ? (int)((kend - kbeg + kBK - 1) / kBK) : 0;
   issue_tile<AK>(opa, smem, ra, kbeg, kend, wave, lane);
   issue_tile<BKC>(opb, smem + kTileU4, rb, kbeg, kend, wave, lane);
@@ -487,18 +505,55 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs g, int 
     const uint4* st = smem + (kt & 1) * kStageU4;
 #pragma unroll
     for (int s = 0; s < kBK / 32; ++s) {
-      uint4 af[8], bfr[4];
+      uint4 af[SH::WMB], bfr[SH::WNB];
       read_half<AK, BKC>(af, bfr, st, s, wm, wn, lane);
-      mma_half<AK, BKC>(acc, af, bfr);
+      mma_half(acc, af, bfr);
     }
     __syncthreads();  // next stage landed; this stage free
   }
 
-  epilogue<EPI>(g, acc, tm, tn, ks, wm, wn, lane);
+  epilogue<EPI, SH::WMB, SH::WNB>(g, acc, (int64_t)tm * SH::TM + wm * SH::WMB * 16,
+                                  (int64_t)tn * SH::TN + wn * SH::WNB * 16, 0, ks, lane);
 }
 
 constexpr size_t kSmemBytes = 2 * kStageU4 * sizeof(uint4);
 constexpr size_t kSmemBytesPingPong = kSlots * kTileU4 * sizeof(uint4);
+
+// Compute units of the current device (queried once).
+inline int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                                 hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+template <class SH>
+inline int64_t tile_cost(const GemmArgs& g, int ksplit, int cus) {
+  const int64_t tiles = ((g.M + SH::TM - 1) / SH::TM) * ((g.N + SH::TN - 1) / SH::TN) * ksplit;
+  return ((tiles + cus - 1) / cus) * SH::TM * SH::TN;  // rounds of one workgroup per CU x work per tile
+}
+
+template <bool AK, bool BKC, int EPI, class SH>
+hipError_t launch_two_stage(const GemmArgs& ga, hipStream_t s) {
+  const int ntm = (int)((ga.M + SH::TM - 1) / SH::TM), ntn = (int)((ga.N + SH::TN - 1) / SH::TN);
+  auto kernel = gemm_bf16_kernel<AK, BKC, EPI, SH>;
+  static bool configured = false;  // raise the dynamic LDS limit once per instantiation
+  if (!configured) {
+    const hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kSmemBytes);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL(kernel, dim3(ntm * ntn * ga.ksplit), dim3(kThreads), kSmemBytes, s, ga, ntm, ntn);
+  return hipGetLastError();
+}
 
 template <bool AK, bool BKC, int EPI>
 hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
@@ -506,29 +561,34 @@ hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
   const int ntn = (EPI == kEpiSwigluFwd) ? (int)((g.ffn + kSwigluChannels - 1) / kSwigluChannels)
                                          : (int)((g.N + kBN - 1) / kBN);
   if (ntm == 0 || ntn == 0) return hipSuccess;
-  constexpr bool kPingPong = AK && BKC;
-  const void* kernel;
-  if constexpr (kPingPong) kernel = reinterpret_cast<const void*>(&gemm_nt_pingpong_kernel<EPI>);
-  else kernel = reinterpret_cast<const void*>(&gemm_bf16_kernel<AK, BKC, EPI>);
-  constexpr size_t smem = kPingPong ? kSmemBytesPingPong : kSmemBytes;
-  static bool configured = false;  // raise the dynamic LDS limit once per instantiation
-  if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
   GemmArgs ga = g;
   if (EPI != kEpiStoreF32 || !ga.ws) ga.ksplit = 1;
   if (ga.ksplit < 1) ga.ksplit = 1;
   {
     KernelTimer timer(g.tag ? g.tag : "gemm", s);
-    if constexpr (kPingPong)
-      hipLaunchKernelGGL((gemm_nt_pingpong_kernel<EPI>), dim3(ntm * ntn * ga.ksplit), dim3(kThreads), smem, s, ga, ntm,
-                         ntn);
-    else
-      hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, EPI>), dim3(ntm * ntn * ga.ksplit), dim3(kThreads), smem, s, ga,
-                         ntm, ntn);
-    const hipError_t e = hipGetLastError();
+    hipError_t e;
+    if constexpr (AK && BKC) {
+      static bool configured = false;
+      if (!configured) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nt_pingpong_kernel<EPI>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytesPingPong);
+        if (e != hipSuccess) return e;
+        configured = true;
+      }
+      hipLaunchKernelGGL((gemm_nt_pingpong_kernel<EPI>), dim3(ntm * ntn * ga.ksplit), dim3(kThreads),
+                         kSmemBytesPingPong, s, ga, ntm, ntn);
+      e = hipGetLastError();
+    } else {
+      // the tile shape with the least (rounds of one workgroup per CU) x (tile area); a function of the
+      // shape and the CU count only, so results are reproducible on a given device
+      const int cus = device_cus();
+      const int64_t c0 = tile_cost<Tile256x256>(ga, ga.ksplit, cus);
+      const int64_t cn = tile_cost<Tile256x224>(ga, ga.ksplit, cus);
+      const int64_t cm = tile_cost<Tile224x256>(ga, ga.ksplit, cus);
+      if (cn < c0 && cn <= cm) e = launch_two_stage<AK, BKC, EPI, Tile256x224>(ga, s);
+      else if (cm < c0) e = launch_two_stage<AK, BKC, EPI, Tile224x256>(ga, s);
+      else e = launch_two_stage<AK, BKC, EPI, Tile256x256>(ga, s);
+    }
     if (e != hipSuccess || ga.ksplit == 1) return e;
   }
   return launch_ksplit_reduce(static_cast<float*>(ga.C), ga.ws, ga.ksplit - 1, ga.M, ga.N, ga.ldc, s);
