@@ -48,3 +48,11 @@ from .optim import (  # noqa: F401,E402
     adamw_step,
 )
 from .sequence import SP_MODES, sequence_parallel_step, sequence_slices  # noqa: F401,E402
+from .fp8 import (  # noqa: F401,E402
+    E4M3,
+    E5M2,
+    Fp8Meta,
+    fp8_dense_step,
+    fp8_sharded_step,
+    new_metas as fp8_new_metas,
+)
