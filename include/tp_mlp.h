@@ -86,7 +86,8 @@ typedef struct {
   int32_t act;       /* TP_MLP_ACT_* */
   int32_t dtype;     /* TP_MLP_F32 | TP_MLP_BF16 */
   float eps;         /* RMSNorm epsilon, added to mean(x^2) under the root */
-  int32_t flags;     /* TP_MLP_FUSE_EPILOGUE | TP_MLP_NORMED_READY | TP_MLP_ACCUMULATE_GRADS */
+  int32_t flags;     /* TP_MLP_FUSE_EPILOGUE | TP_MLP_NORMED_READY | TP_MLP_ACCUMULATE_GRADS
+                        (| TP_MLP_FP8_SHARED_READY for tp_mlp_backward_fp8) */
 } tp_mlp_desc;
 
 /*
@@ -312,6 +313,132 @@ int tp_mlp_clip_grad_norm(const float* const* grads, const int64_t* counts, int3
 
 /* Bytes of workspace tp_mlp_clip_grad_norm needs (counts: HOST array). */
 size_t tp_mlp_clip_grad_norm_workspace_bytes(const int64_t* counts, int32_t count);
+
+/*
+ * FP8 GEMMs with per-tensor delayed scaling ("Megatron-Core Guide: 5D
+ * Distributed Training Architecture": Transformer Engine runs the matrix
+ * products in FP8 with delayed scaling, feature list item 6).  The pages give
+ * no recipe; this is Transformer Engine's default one:
+ *   - formats (OCP FP8): E4M3 (largest finite 448) for the normed input N,
+ *     the weights and the activation A; E5M2 (largest 57344) for the output
+ *     gradient and the pre-activation gradient;
+ *   - code(x) = round-to-nearest-even(clamp(fp32(x) * s, +-max)), s the
+ *     tensor role's current scale;
+ *   - a GEMM of codes is dequantised by (1/s_a)(1/s_b) in fp32;
+ *   - every cast folds max|x| into its role's running amax; at the end of the
+ *     step tp_mlp_fp8_update_scales pushes it into an amax history of length
+ *     L and sets s = max / max(history) when that is positive and finite
+ *     (else s is kept).  Shards that share a meta share the amax: the amax
+ *     reduction over the tensor-parallel group.
+ * Every GEMM of the step runs on FP8 codes: the forward F2 and F3 on
+ * E4M3 x E4M3, the backward d_act, d_w_down, d_normed and d_w_in on
+ * E5M2 x E4M3; everything between them (norm, activation and its backward,
+ * residual, sums, update) is the bf16 path's.
+ *
+ * Meta: a DEVICE fp32 array of TP_MLP_FP8_META_FLOATS(L) elements:
+ *   [0] scale s   [1] 1/s   [2] running amax   [3] format max   [4..4+L) history, newest first.
+ * Initialise it with tp_mlp_fp8_meta_init; the library updates it from then
+ * on.  A caller may restore a saved meta (a checkpoint) by writing all of
+ * its floats, [1] being the fp32 reciprocal of [0].  1 <= L <= 1024.
+ */
+enum { TP_MLP_FP8_E4M3 = 0, TP_MLP_FP8_E5M2 = 1 };
+#define TP_MLP_FP8_META_FLOATS(L) (4 + (L))
+#define TP_MLP_FP8_MAX_HISTORY 1024
+
+/* s = 1, 1/s = 1, amax = 0, format max, zero history (a kernel on `stream`). */
+int tp_mlp_fp8_meta_init(float* meta, int32_t fmt, int32_t history_len, void* stream);
+
+/*
+ * tp_mlp_fp8_cast - codes of a bf16 matrix x [rows, cols] with meta's scale:
+ * out [rows, cols] and/or out_t [cols, ldt] = the codes transposed (either may
+ * be NULL, not both); max|x| folds into meta's running amax.  cols: a
+ * multiple of 8.  out_t: ldt >= rows and a multiple of 16; its columns rows ..
+ * ldt-1 are written as 0 (the zero padding that lets a transposed operand
+ * have a k extent of ldt).  fmt must be the format meta was initialised with.
+ */
+int tp_mlp_fp8_cast(int64_t rows, int64_t cols, const void* x, int32_t fmt, float* meta, uint8_t* out,
+                    uint8_t* out_t, int64_t ldt, void* stream);
+
+/* End of step: every meta's running amax enters its history (then is zeroed)
+ * and its scale is renewed.  metas: HOST array of count DEVICE pointers
+ * (count <= 16), all with history length history_len. */
+int tp_mlp_fp8_update_scales(float* const* metas, int32_t count, int32_t history_len, void* stream);
+
+/* Metas and code buffers of one shard's FP8 step.  Tp = T rounded up to a
+ * multiple of 16; P = 2F (SwiGLU) or F (GeLU).  Every buffer is DEVICE
+ * memory, 16-byte aligned, owned by the caller; shapes are row-major. */
+typedef struct {
+  int32_t history_len;  /* L of every meta */
+  float* meta_normed;   /* E4M3 */
+  float* meta_w_in;     /* E4M3 */
+  float* meta_act;      /* E4M3 */
+  float* meta_w_down;   /* E4M3 */
+  float* meta_d_out;    /* E5M2 */
+  float* meta_d_pre;    /* E5M2 */
+  /* written by tp_mlp_forward_fp8 (normed_q / normed_t: unless NORMED_READY,
+     then read), read by tp_mlp_backward_fp8 */
+  uint8_t* normed_q;    /* [T, H]  */
+  uint8_t* normed_t;    /* [H, Tp] */
+  uint8_t* w_in_q;      /* [P, H]  */
+  uint8_t* w_in_t;      /* [H, P]  */
+  uint8_t* act_q;       /* [T, F]  */
+  uint8_t* act_t;       /* [F, Tp] */
+  uint8_t* w_down_q;    /* [H, F]  */
+  uint8_t* w_down_t;    /* [F, H]  */
+  /* written by tp_mlp_backward_fp8 (d_out_q / d_out_t: unless
+     TP_MLP_FP8_SHARED_READY, then read) */
+  uint8_t* d_out_q;     /* [T, H]  */
+  uint8_t* d_out_t;     /* [H, Tp] */
+  uint8_t* d_pre_q;     /* [T, P]  */
+  uint8_t* d_pre_t;     /* [P, Tp] */
+} tp_mlp_fp8_args;
+
+/*
+ * tp_mlp_fp8_gemm - the FP8 GEMM on its own:
+ *   C[m, n] (+)= (sum_k dec(A[m, k]) dec(B[n, k])) * scale_inv_a[0] * scale_inv_b[0]
+ *   A [M, lda] codes in fmt_a, B [N, ldb] codes in fmt_b (both K-contiguous;
+ *   K <= lda, K <= ldb, K a multiple of 16, lda and ldb multiples of 16);
+ *   (fmt_a, fmt_b) = (E4M3, E4M3) or (E5M2, E4M3).  scale_inv_a/b: DEVICE
+ *   pointers to one fp32 each (a meta + 1).  C [M, ldc] fp32 (N and ldc
+ *   multiples of 4, ldc >= N); with accumulate != 0 the product is added to
+ *   C.  The k range may be split over workgroups (a function of M, N and K
+ *   only, so the result is run-to-run deterministic); the split needs a
+ *   workspace of tp_mlp_fp8_gemm_workspace_bytes(M, N, K, ldc) bytes (may be 0).
+ * The hardware sums each 128-long block of k with about 12 bits of precision
+ * relative to the block's largest product, then adds the block sums in fp32.
+ */
+int tp_mlp_fp8_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, int32_t fmt_a,
+                    const float* scale_inv_a, const uint8_t* B, int64_t ldb, int32_t fmt_b, const float* scale_inv_b,
+                    float* C, int64_t ldc, int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream);
+size_t tp_mlp_fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t ldc);
+
+/* tp_mlp_desc.flags for tp_mlp_backward_fp8: d_out_q and d_out_t already
+ * hold this step's codes of d_out (an earlier shard's call wrote them). */
+enum { TP_MLP_FP8_SHARED_READY = 8 };
+
+/*
+ * tp_mlp_forward_fp8 - tp_mlp_forward with F2 and F3 on FP8 codes.  Same
+ * arguments and outputs (dtype must be TP_MLP_BF16; H and F multiples of 16),
+ * plus f8: casts N (normed_q, normed_t; skipped with NORMED_READY), w_in
+ * (w_in_q, w_in_t), A (act_q, act_t) and w_down (w_down_q, w_down_t), each
+ * row copy for the forward GEMM and transposed copy for the backward.
+ */
+int tp_mlp_forward_fp8(const tp_mlp_desc* d, const void* x, const void* norm_w, const void* w_in,
+                       const void* b_in, const void* w_down, void* normed, float* rstd, void* pre_act,
+                       void* act, void* out, const void* b_down, const tp_mlp_fp8_args* f8, void* stream);
+
+/*
+ * tp_mlp_backward_fp8 - tp_mlp_backward (phase TP_MLP_BWD_SHARD) with its
+ * four GEMMs on FP8 codes: d_act = d_out Wd on d_out_q and w_down_t;
+ * d_w_down = d_out^T act on d_out_t and act_t; d_normed_part = d_pre w_in on
+ * d_pre_q and w_in_t; d_w_in = d_pre^T normed on d_pre_t and normed_t.  It
+ * casts d_out (unless TP_MLP_FP8_SHARED_READY) and d_pre; the codes of the
+ * forward must be those of the same step.  The other tp_mlp_bwd_args fields,
+ * the workspace (tp_mlp_workspace_bytes) and ACCUMULATE_GRADS are as for
+ * tp_mlp_backward; phase TP_MLP_BWD_NORM is tp_mlp_backward's.
+ */
+int tp_mlp_backward_fp8(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* a,
+                        const tp_mlp_fp8_args* f8, void* stream);
 
 /*
  * Kernel timing, a measurement aid (off by default).  While enabled, every

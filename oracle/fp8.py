@@ -12,9 +12,9 @@ Sources:
   kernels and FP8 supply the last few percent of utilisation.
 
 The pages name the method and nothing more: neither the formats, nor the
-scaling rule, nor which tensors are cast.  The readings taken here (each is
-listed in the design doc) are those of Transformer Engine's default recipe, the
-plainest reading of "FP8 with delayed scaling through Transformer Engine":
+scaling rule, nor which tensors are cast.  The readings taken here are those
+of Transformer Engine's default recipe, the plainest reading of "FP8 with
+delayed scaling through Transformer Engine":
 
 * Formats (OCP FP8): forward tensors (the normed input N, the weights, the
   activation A) in E4M3 -- 4 exponent bits with bias 7, 3 mantissa bits,

@@ -25,7 +25,7 @@ plain reading of the code that survives on them):
   variant (fc1 column-parallel with bias, gelu, fc2 row-parallel with bias,
   skip_bias_add so biases are added after the reduction) and the f/g pair.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   rms_norm(x, w) = x / sqrt(mean_H(x^2) + eps) * w, no mean subtraction, no bias;
   SiLU(v) = v * sigmoid(v); GeLU is the exact erf form;
   loss = sum(out^2) / 2, so d loss / d out = out;

@@ -28,7 +28,7 @@ algorithm: Loshchilov & Hutter, "Decoupled Weight Decay Regularization"
     theta_t = theta_{t-1} - lr * ( (m_t / (1 - b1^t)) / (sqrt(v_t / (1 - b2^t)) + eps)
                                    + wd * theta_{t-1} )
 
-Readings where the pages are silent (each listed in the design doc): b1 = 0.9,
+Readings where the pages are silent: b1 = 0.9,
 b2 = 0.999, eps = 1e-8 unless a caller sets them; the decay acts on every
 parameter tensor; clipping scales every gradient by
 c = min(1, max_norm / (||g||_2 + 1e-6)), ||g||_2 the norm of all gradient

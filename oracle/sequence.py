@@ -22,7 +22,7 @@ Sources:
   row-parallel output is reduce-scattered, the norm runs on the slice, and an
   all-gather rebuilds the full sequence before the next column-parallel linear.
 
-Layout and readings (listed in the design doc): x is [T, H] with the sequence axis
+Layout and readings: x is [T, H] with the sequence axis
 outermost, so a sequence slice is a contiguous block of token rows; rank r
 holds rows [lo_r, hi_r), the first T % S ranks one row more than the rest
 (the pages assume T divisible by S; the ragged split is a harmless

@@ -21,12 +21,21 @@ ACT_SWIGLU, ACT_GELU = 0, 1
 F32, BF16 = 0, 1
 FUSE_EPILOGUE, NORMED_READY, ACCUMULATE_GRADS = 1, 2, 4
 BWD_SHARD, BWD_NORM = 0, 1
+FP8_E4M3, FP8_E5M2 = 0, 1
+FP8_SHARED_READY = 8
+FP8_MAX_HISTORY = 1024
+
+
+def fp8_meta_floats(history_len: int) -> int:
+    return 4 + history_len
 
 # every symbol include/tp_mlp.h declares
 EXPORTED = ("tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_workspace_bytes",
             "tp_mlp_sgd_step", "tp_mlp_last_error", "tp_mlp_version", "tp_mlp_profile_enable",
             "tp_mlp_profile_count", "tp_mlp_profile_entry", "tp_mlp_sgd_step_multi", "tp_mlp_adamw_step_multi",
-            "tp_mlp_clip_grad_norm", "tp_mlp_clip_grad_norm_workspace_bytes", "tp_rmsnorm_forward")
+            "tp_mlp_clip_grad_norm", "tp_mlp_clip_grad_norm_workspace_bytes", "tp_rmsnorm_forward",
+            "tp_mlp_fp8_meta_init", "tp_mlp_fp8_cast", "tp_mlp_fp8_update_scales", "tp_mlp_forward_fp8",
+            "tp_mlp_backward_fp8", "tp_mlp_fp8_gemm", "tp_mlp_fp8_gemm_workspace_bytes")
 
 
 class TPMLPError(RuntimeError):
@@ -66,6 +75,15 @@ class tp_mlp_bwd_args(ctypes.Structure):
                                    "d_norm_w", "d_b_down", "workspace")] + [("workspace_bytes", ctypes.c_size_t)]
 
 
+FP8_META_FIELDS = ("meta_normed", "meta_w_in", "meta_act", "meta_w_down", "meta_d_out", "meta_d_pre")
+FP8_CODE_FIELDS = ("normed_q", "normed_t", "w_in_q", "w_in_t", "act_q", "act_t", "w_down_q", "w_down_t",
+                   "d_out_q", "d_out_t", "d_pre_q", "d_pre_t")
+
+
+class tp_mlp_fp8_args(ctypes.Structure):
+    _fields_ = [("history_len", ctypes.c_int32)] + [(n, _vp) for n in FP8_META_FIELDS + FP8_CODE_FIELDS]
+
+
 _LIB: Optional[ctypes.CDLL] = None
 
 
@@ -103,6 +121,25 @@ def lib() -> ctypes.CDLL:
         L.tp_rmsnorm_forward.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, _vp, _vp,
                                          _vp, _vp, _vp]
         L.tp_rmsnorm_forward.restype = ctypes.c_int
+        L.tp_mlp_fp8_meta_init.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32, _vp]
+        L.tp_mlp_fp8_meta_init.restype = ctypes.c_int
+        L.tp_mlp_fp8_cast.argtypes = [ctypes.c_int64, ctypes.c_int64, _vp, ctypes.c_int32, _vp, _vp, _vp,
+                                      ctypes.c_int64, _vp]
+        L.tp_mlp_fp8_cast.restype = ctypes.c_int
+        L.tp_mlp_fp8_update_scales.argtypes = [ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int32, _vp]
+        L.tp_mlp_fp8_update_scales.restype = ctypes.c_int
+        L.tp_mlp_forward_fp8.argtypes = [ctypes.POINTER(tp_mlp_desc)] + [_vp] * 11 + \
+            [ctypes.POINTER(tp_mlp_fp8_args), _vp]
+        L.tp_mlp_forward_fp8.restype = ctypes.c_int
+        L.tp_mlp_backward_fp8.argtypes = [ctypes.POINTER(tp_mlp_desc), ctypes.c_int32,
+                                          ctypes.POINTER(tp_mlp_bwd_args), ctypes.POINTER(tp_mlp_fp8_args), _vp]
+        L.tp_mlp_backward_fp8.restype = ctypes.c_int
+        L.tp_mlp_fp8_gemm.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp, ctypes.c_int64,
+                                      ctypes.c_int32, _vp, _vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp,
+                                      ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
+        L.tp_mlp_fp8_gemm.restype = ctypes.c_int
+        L.tp_mlp_fp8_gemm_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+        L.tp_mlp_fp8_gemm_workspace_bytes.restype = ctypes.c_size_t
         L.tp_mlp_last_error.argtypes = []
         L.tp_mlp_last_error.restype = ctypes.c_char_p
         L.tp_mlp_version.argtypes = []
@@ -168,6 +205,11 @@ def tp_mlp_workspace_bytes(desc: tp_mlp_desc, phase: int) -> int:
 def tp_mlp_backward(desc: tp_mlp_desc, phase: int, stream=None, **tensors) -> None:
     """``tensors`` are the fields of tp_mlp_bwd_args (torch tensors or None);
     ``workspace`` may be given, ``workspace_bytes`` defaults to its size."""
+    a = _bwd_args(tensors)
+    _check(lib().tp_mlp_backward(ctypes.byref(desc), phase, ctypes.byref(a), _stream(stream)))
+
+
+def _bwd_args(tensors: dict) -> tp_mlp_bwd_args:
     a = tp_mlp_bwd_args()
     for name, _ in tp_mlp_bwd_args._fields_:
         if name == "workspace_bytes":
@@ -180,7 +222,59 @@ def tp_mlp_backward(desc: tp_mlp_desc, phase: int, stream=None, **tensors) -> No
         a.workspace_bytes = tensors.pop("workspace_bytes")
     if tensors:
         raise TypeError(f"unknown backward arguments: {sorted(tensors)}")
-    _check(lib().tp_mlp_backward(ctypes.byref(desc), phase, ctypes.byref(a), _stream(stream)))
+    return a
+
+
+def make_fp8_args(history_len: int, **buffers) -> tp_mlp_fp8_args:
+    """``buffers``: the meta_* and code fields of tp_mlp_fp8_args (tensors or None)."""
+    f = tp_mlp_fp8_args()
+    f.history_len = history_len
+    for name in FP8_META_FIELDS + FP8_CODE_FIELDS:
+        setattr(f, name, _ptr(buffers.pop(name, None)))
+    if buffers:
+        raise TypeError(f"unknown fp8 arguments: {sorted(buffers)}")
+    return f
+
+
+def tp_mlp_fp8_meta_init(meta, fmt: int, history_len: int, stream=None) -> None:
+    _check(lib().tp_mlp_fp8_meta_init(_ptr(meta), fmt, history_len, _stream(stream)))
+
+
+def tp_mlp_fp8_cast(rows: int, cols: int, x, fmt: int, meta, out, out_t=None, ldt: int = 0, stream=None) -> None:
+    _check(lib().tp_mlp_fp8_cast(rows, cols, _ptr(x), fmt, _ptr(meta), _ptr(out), _ptr(out_t), ldt,
+                                 _stream(stream)))
+
+
+def tp_mlp_fp8_update_scales(metas: Sequence, history_len: int, stream=None) -> None:
+    arr = (_vp * max(1, len(metas)))(*[_ptr(m) for m in metas])
+    _check(lib().tp_mlp_fp8_update_scales(arr, len(metas), history_len, _stream(stream)))
+
+
+def tp_mlp_forward_fp8(desc: tp_mlp_desc, x, norm_w, w_in, b_in, w_down, normed, rstd, pre_act, act, out,
+                       b_down, f8: tp_mlp_fp8_args, stream=None) -> None:
+    _check(lib().tp_mlp_forward_fp8(ctypes.byref(desc), _ptr(x), _ptr(norm_w), _ptr(w_in), _ptr(b_in),
+                                    _ptr(w_down), _ptr(normed), _ptr(rstd), _ptr(pre_act), _ptr(act), _ptr(out),
+                                    _ptr(b_down), ctypes.byref(f8), _stream(stream)))
+
+
+def tp_mlp_backward_fp8(desc: tp_mlp_desc, phase: int, f8: tp_mlp_fp8_args, stream=None, **tensors) -> None:
+    """``tensors`` as for tp_mlp_backward."""
+    a = _bwd_args(tensors)
+    _check(lib().tp_mlp_backward_fp8(ctypes.byref(desc), phase, ctypes.byref(a), ctypes.byref(f8),
+                                     _stream(stream)))
+
+
+def tp_mlp_fp8_gemm_workspace_bytes(M: int, N: int, K: int, ldc: int) -> int:
+    return int(lib().tp_mlp_fp8_gemm_workspace_bytes(M, N, K, ldc))
+
+
+def tp_mlp_fp8_gemm(M: int, N: int, K: int, A, lda: int, fmt_a: int, scale_inv_a, B, ldb: int, fmt_b: int,
+                    scale_inv_b, C, ldc: int, accumulate: bool = False, workspace=None, stream=None) -> None:
+    """``scale_inv_a`` / ``scale_inv_b``: one-element fp32 device tensors (or a meta viewed at [1:])."""
+    nbytes = 0 if workspace is None or isinstance(workspace, int) else workspace.numel() * workspace.element_size()
+    _check(lib().tp_mlp_fp8_gemm(M, N, K, _ptr(A), lda, fmt_a, _ptr(scale_inv_a), _ptr(B), ldb, fmt_b,
+                                 _ptr(scale_inv_b), _ptr(C), ldc, 1 if accumulate else 0, _ptr(workspace), nbytes,
+                                 _stream(stream)))
 
 
 def tp_mlp_sgd_step(param_in, param_out, grad, master_in, master_out, n: int, param_dtype: int, lr: float,

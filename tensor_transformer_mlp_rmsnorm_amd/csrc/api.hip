@@ -47,7 +47,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
     if (e_ != hipSuccess) return hip_fail(e_, where); \
   } while (0)
 
-int check_desc(const tp_mlp_desc* d, const char* fn) {
+int check_desc(const tp_mlp_desc* d, const char* fn, int32_t extra_flags = 0) {
   if (!d) return fail(TP_MLP_EINVAL, "%s: descriptor is NULL", fn);
   if (d->tokens < 0) return fail(TP_MLP_EINVAL, "%s: tokens < 0", fn);
   if (d->hidden <= 0 || d->hidden % 8) return fail(TP_MLP_ESHAPE, "%s: hidden must be a positive multiple of 8", fn);
@@ -56,7 +56,7 @@ int check_desc(const tp_mlp_desc* d, const char* fn) {
     return fail(TP_MLP_ESHAPE, "%s: ffn_local must be a positive multiple of 8", fn);
   if (d->act != TP_MLP_ACT_SWIGLU && d->act != TP_MLP_ACT_GELU) return fail(TP_MLP_EINVAL, "%s: unknown act", fn);
   if (d->dtype != TP_MLP_F32 && d->dtype != TP_MLP_BF16) return fail(TP_MLP_EDTYPE, "%s: unknown dtype", fn);
-  if (d->flags & ~(TP_MLP_FUSE_EPILOGUE | TP_MLP_NORMED_READY | TP_MLP_ACCUMULATE_GRADS))
+  if (d->flags & ~(TP_MLP_FUSE_EPILOGUE | TP_MLP_NORMED_READY | TP_MLP_ACCUMULATE_GRADS | extra_flags))
     return fail(TP_MLP_EINVAL, "%s: unknown flags", fn);
   if (!(d->eps >= 0.0f)) return fail(TP_MLP_EINVAL, "%s: eps must be >= 0", fn);
   // Element counts stay below 2^31 so per-tensor int arithmetic in the
@@ -197,10 +197,13 @@ size_t tp_mlp_workspace_bytes(const tp_mlp_desc* d, int32_t phase) {
   if (d->dtype == TP_MLP_BF16) {
     // k-split slices of the two weight-gradient GEMMs (K = T); they run one
     // after the other and share the workspace
+    // (the FP8 backward's k extent is T rounded up to 16)
     const int64_t P = d->act == TP_MLP_ACT_SWIGLU ? 2 * F : F;
-    const size_t w2 = gemm_ksplit_workspace(H, F, T), w4 = gemm_ksplit_workspace(P, H, T);
-    need = need > w2 ? need : w2;
-    need = need > w4 ? need : w4;
+    for (const int64_t K : {T, (T + 15) / 16 * 16}) {
+      const size_t w2 = gemm_ksplit_workspace(H, F, K), w4 = gemm_ksplit_workspace(P, H, K);
+      need = need > w2 ? need : w2;
+      need = need > w4 ? need : w4;
+    }
   }
   return need;
 }
@@ -477,6 +480,328 @@ int tp_mlp_clip_grad_norm(const float* const* grads, const int64_t* counts, int3
   CHECK_HIP(launch_clip_grad_norm(grads, counts, count, max_norm, norm_out, coef_out, static_cast<double*>(workspace),
                                   static_cast<hipStream_t>(stream)),
             "gradient norm");
+  return TP_MLP_OK;
+}
+
+// ------------------------------------------------------------------ FP8
+
+namespace {
+
+int check_meta_args(int32_t history_len, const char* fn) {
+  if (history_len < 1 || history_len > TP_MLP_FP8_MAX_HISTORY)
+    return fail(TP_MLP_EINVAL, "%s: history_len must be in [1, %d]", fn, TP_MLP_FP8_MAX_HISTORY);
+  return TP_MLP_OK;
+}
+
+#define REQUIRE_META(p)                                                            \
+  do {                                                                             \
+    if (!(p)) return fail(TP_MLP_EINVAL, "%s: meta '%s' is NULL", fn, #p);         \
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return fail(TP_MLP_EALIGN, "%s: meta '%s' is not 4-byte aligned", fn, #p); \
+  } while (0)
+
+int check_fp8_desc(const tp_mlp_desc* d, const tp_mlp_fp8_args* f8, const char* fn) {
+  if (d->dtype != TP_MLP_BF16) return fail(TP_MLP_EDTYPE, "%s: the FP8 path takes bf16 tensors", fn);
+  if (d->hidden % 16 || d->ffn_local % 16)
+    return fail(TP_MLP_ESHAPE, "%s: hidden and ffn_local must be multiples of 16 for FP8", fn);
+  if (!f8) return fail(TP_MLP_EINVAL, "%s: fp8 args are NULL", fn);
+  return check_meta_args(f8->history_len, fn);
+}
+
+GemmArgs fp8_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const float* meta_a, const void* B,
+                  int64_t ldb, const float* meta_b, const char* tag) {
+  GemmArgs g{};
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.A = A;
+  g.lda = lda;
+  g.B = B;
+  g.ldb = ldb;
+  g.scale_inv_a = meta_a + 1;
+  g.scale_inv_b = meta_b + 1;
+  g.tag = tag;
+  return g;
+}
+
+}  // namespace
+
+int tp_mlp_fp8_meta_init(float* meta, int32_t fmt, int32_t history_len, void* stream) {
+  const char* fn = "tp_mlp_fp8_meta_init";
+  g_err[0] = 0;
+  if (fmt != TP_MLP_FP8_E4M3 && fmt != TP_MLP_FP8_E5M2) return fail(TP_MLP_EINVAL, "%s: unknown format", fn);
+  int rc = check_meta_args(history_len, fn);
+  if (rc) return rc;
+  REQUIRE_META(meta);
+  CHECK_HIP(launch_fp8_meta_init(meta, fmt, history_len, static_cast<hipStream_t>(stream)), "fp8 meta init");
+  return TP_MLP_OK;
+}
+
+int tp_mlp_fp8_cast(int64_t rows, int64_t cols, const void* x, int32_t fmt, float* meta, uint8_t* out,
+                    uint8_t* out_t, int64_t ldt, void* stream) {
+  const char* fn = "tp_mlp_fp8_cast";
+  g_err[0] = 0;
+  if (fmt != TP_MLP_FP8_E4M3 && fmt != TP_MLP_FP8_E5M2) return fail(TP_MLP_EINVAL, "%s: unknown format", fn);
+  if (rows < 0 || cols < 0) return fail(TP_MLP_EINVAL, "%s: negative size", fn);
+  if (cols % 8) return fail(TP_MLP_ESHAPE, "%s: cols must be a multiple of 8", fn);
+  if (rows * cols >= ((int64_t)1 << 31)) return fail(TP_MLP_ESHAPE, "%s: 2^31 or more elements", fn);
+  if (!out && !out_t) return fail(TP_MLP_EINVAL, "%s: out and out_t are both NULL", fn);
+  if (out_t && (ldt < rows || ldt % 16)) return fail(TP_MLP_ESHAPE, "%s: ldt must be >= rows and a multiple of 16", fn);
+  if (out_t && cols * ldt >= ((int64_t)1 << 31)) return fail(TP_MLP_ESHAPE, "%s: out_t too large", fn);
+  REQUIRE_META(meta);
+  if (cols == 0 || (rows == 0 && (!out_t || ldt == 0))) return TP_MLP_OK;
+  if (rows > 0) REQUIRE_PTR(x);  // rows = 0: only the zero padding of out_t is written
+  if (out) REQUIRE_PTR(out);
+  if (out_t) REQUIRE_PTR(out_t);
+  CHECK_HIP(launch_fp8_cast(fmt, x, rows, cols, out, out_t, ldt, meta, "fp8_cast", static_cast<hipStream_t>(stream)),
+            "fp8 cast");
+  return TP_MLP_OK;
+}
+
+int tp_mlp_fp8_update_scales(float* const* metas, int32_t count, int32_t history_len, void* stream) {
+  const char* fn = "tp_mlp_fp8_update_scales";
+  g_err[0] = 0;
+  if (count < 0 || count > kFp8MaxMetas) return fail(TP_MLP_EINVAL, "%s: count must be in [0, %d]", fn, kFp8MaxMetas);
+  if (count > 0 && !metas) return fail(TP_MLP_EINVAL, "%s: metas is NULL", fn);
+  int rc = check_meta_args(history_len, fn);
+  if (rc) return rc;
+  for (int i = 0; i < count; ++i) {
+    float* m = metas[i];
+    REQUIRE_META(m);
+  }
+  CHECK_HIP(launch_fp8_update(metas, count, history_len, static_cast<hipStream_t>(stream)), "fp8 scale update");
+  return TP_MLP_OK;
+}
+
+size_t tp_mlp_fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t ldc) {
+  if (M <= 0 || N <= 0 || K <= 0 || ldc < N) return 0;
+  return (size_t)(gemm_ksplit(M, N, K) - 1) * (size_t)M * (size_t)ldc * sizeof(float);
+}
+
+int tp_mlp_fp8_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, int32_t fmt_a,
+                    const float* scale_inv_a, const uint8_t* B, int64_t ldb, int32_t fmt_b, const float* scale_inv_b,
+                    float* C, int64_t ldc, int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "tp_mlp_fp8_gemm";
+  g_err[0] = 0;
+  if (M < 0 || N < 0 || K < 0) return fail(TP_MLP_EINVAL, "%s: negative size", fn);
+  if (!((fmt_a == TP_MLP_FP8_E4M3 && fmt_b == TP_MLP_FP8_E4M3) || (fmt_a == TP_MLP_FP8_E5M2 && fmt_b == TP_MLP_FP8_E4M3)))
+    return fail(TP_MLP_EINVAL, "%s: formats must be (E4M3, E4M3) or (E5M2, E4M3)", fn);
+  if (K % 16 || lda % 16 || ldb % 16 || lda < K || ldb < K)
+    return fail(TP_MLP_ESHAPE, "%s: K, lda, ldb must be multiples of 16 with K <= lda, ldb", fn);
+  if (N % 4 || ldc < N || ldc % 4) return fail(TP_MLP_ESHAPE, "%s: N and ldc must be multiples of 4, ldc >= N", fn);
+  if (M * lda >= ((int64_t)1 << 31) || N * ldb >= ((int64_t)1 << 31) || M * ldc >= ((int64_t)1 << 31))
+    return fail(TP_MLP_ESHAPE, "%s: an operand holds 2^31 or more elements", fn);
+  if (M == 0 || N == 0) return TP_MLP_OK;
+  REQUIRE_PTR(C);
+  REQUIRE_META(scale_inv_a);
+  REQUIRE_META(scale_inv_b);
+  if (K > 0) {
+    REQUIRE_PTR(A);
+    REQUIRE_PTR(B);
+  }
+  const size_t need = tp_mlp_fp8_gemm_workspace_bytes(M, N, K, ldc);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(TP_MLP_EWORKSPACE, "%s: workspace of %zu bytes required, %zu given", fn, need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(TP_MLP_EALIGN, "%s: workspace is not 16-byte aligned", fn);
+  }
+  GemmArgs g{};
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.A = A;
+  g.lda = lda;
+  g.B = B;
+  g.ldb = ldb;
+  g.C = C;
+  g.ldc = ldc;
+  g.scale_inv_a = scale_inv_a;
+  g.scale_inv_b = scale_inv_b;
+  g.accum = accumulate != 0;
+  g.ksplit = gemm_ksplit(M, N, K);
+  g.ws = static_cast<float*>(workspace);
+  g.tag = "gemm_fp8";
+  CHECK_HIP(launch_gemm_fp8(fmt_a, fmt_b, kEpiStoreF32, g, static_cast<hipStream_t>(stream)), "fp8 GEMM");
+  return TP_MLP_OK;
+}
+
+int tp_mlp_forward_fp8(const tp_mlp_desc* d, const void* x, const void* norm_w, const void* w_in, const void* b_in,
+                       const void* w_down, void* normed, float* rstd, void* pre_act, void* act, void* out,
+                       const void* b_down, const tp_mlp_fp8_args* f8, void* stream) {
+  const char* fn = "tp_mlp_forward_fp8";
+  g_err[0] = 0;
+  int rc = check_desc(d, fn);
+  if (rc) return rc;
+  rc = check_fp8_desc(d, f8, fn);
+  if (rc) return rc;
+  const int64_t T = d->tokens, H = d->hidden, F = d->ffn_local;
+  const bool swiglu = d->act == TP_MLP_ACT_SWIGLU;
+  const bool fuse = d->flags & TP_MLP_FUSE_EPILOGUE;
+  const bool ready = d->flags & TP_MLP_NORMED_READY;
+  const int64_t P = swiglu ? 2 * F : F, Tp = (T + 15) / 16 * 16;
+  REQUIRE_PTR(norm_w);
+  REQUIRE_PTR(w_in);
+  REQUIRE_PTR(w_down);
+  if (swiglu && b_in) return fail(TP_MLP_EINVAL, "%s: b_in must be NULL for SwiGLU", fn);
+  if (!swiglu) REQUIRE_PTR(b_in);
+  if (fuse) REQUIRE_PTR(b_down);
+  REQUIRE_META(f8->meta_normed);
+  REQUIRE_META(f8->meta_w_in);
+  REQUIRE_META(f8->meta_act);
+  REQUIRE_META(f8->meta_w_down);
+  REQUIRE_PTR(f8->w_in_q);
+  REQUIRE_PTR(f8->w_in_t);
+  REQUIRE_PTR(f8->w_down_q);
+  REQUIRE_PTR(f8->w_down_t);
+  if (T == 0) return TP_MLP_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(normed);
+  REQUIRE_PTR4(rstd);
+  REQUIRE_PTR(pre_act);
+  REQUIRE_PTR(act);
+  REQUIRE_PTR(out);
+  REQUIRE_PTR(f8->normed_q);
+  REQUIRE_PTR(f8->normed_t);
+  REQUIRE_PTR(f8->act_q);
+  REQUIRE_PTR(f8->act_t);
+  if (T * H >= ((int64_t)1 << 30) || H * Tp >= ((int64_t)1 << 30) || F * Tp >= ((int64_t)1 << 30))
+    return fail(TP_MLP_ESHAPE, "%s: a transposed code tensor would hold 2^30 or more elements", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (!ready) {
+    CHECK_HIP(launch_rmsnorm_fwd(kBF16, x, norm_w, normed, rstd, T, H, d->eps, s), "rmsnorm forward");
+    CHECK_HIP(launch_fp8_cast(kFp8E4M3, normed, T, H, f8->normed_q, f8->normed_t, Tp, f8->meta_normed,
+                              "fp8_cast_normed", s),
+              "normed cast");
+  }
+  CHECK_HIP(launch_fp8_cast(kFp8E4M3, w_in, P, H, f8->w_in_q, f8->w_in_t, P, f8->meta_w_in, "fp8_cast_weights", s),
+            "w_in cast");
+
+  GemmArgs g = fp8_gemm(T, P, H, f8->normed_q, H, f8->meta_normed, f8->w_in_q, H, f8->meta_w_in,
+                        swiglu ? "gemm_gate_up_swiglu_fp8" : "gemm_fc1_gelu_fp8");
+  g.pre = pre_act;
+  g.act = act;
+  g.bias = b_in;
+  g.ffn = F;
+  CHECK_HIP(launch_gemm_fp8(kFp8E4M3, kFp8E4M3, swiglu ? kEpiSwigluFwd : kEpiGeluFwd, g, s), "expansion GEMM");
+
+  CHECK_HIP(launch_fp8_cast(kFp8E4M3, act, T, F, f8->act_q, f8->act_t, Tp, f8->meta_act, "fp8_cast_act", s),
+            "act cast");
+  CHECK_HIP(launch_fp8_cast(kFp8E4M3, w_down, H, F, f8->w_down_q, f8->w_down_t, H, f8->meta_w_down,
+                            "fp8_cast_weights", s),
+            "w_down cast");
+  GemmArgs c = fp8_gemm(T, H, F, f8->act_q, F, f8->meta_act, f8->w_down_q, F, f8->meta_w_down,
+                        fuse ? "gemm_down_residual_fp8" : "gemm_down_partial_fp8");
+  c.C = out;
+  c.ldc = H;
+  c.aux = x;
+  c.bias = b_down;
+  c.ffn = F;
+  CHECK_HIP(launch_gemm_fp8(kFp8E4M3, kFp8E4M3, fuse ? kEpiResidual : kEpiStoreF32, c, s), "down GEMM");
+  return TP_MLP_OK;
+}
+
+int tp_mlp_backward_fp8(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* a, const tp_mlp_fp8_args* f8,
+                        void* stream) {
+  const char* fn = "tp_mlp_backward_fp8";
+  g_err[0] = 0;
+  int rc = check_desc(d, fn, TP_MLP_FP8_SHARED_READY);
+  if (rc) return rc;
+  rc = check_fp8_desc(d, f8, fn);
+  if (rc) return rc;
+  if (phase == TP_MLP_BWD_NORM) {
+    tp_mlp_desc dn = *d;
+    dn.flags &= ~TP_MLP_FP8_SHARED_READY;
+    return tp_mlp_backward(&dn, phase, a, stream);
+  }
+  if (phase != TP_MLP_BWD_SHARD) return fail(TP_MLP_EINVAL, "%s: unknown phase", fn);
+  if (!a) return fail(TP_MLP_EINVAL, "%s: args is NULL", fn);
+  const int64_t T = d->tokens, H = d->hidden, F = d->ffn_local;
+  const bool swiglu = d->act == TP_MLP_ACT_SWIGLU;
+  const bool accum = (d->flags & TP_MLP_ACCUMULATE_GRADS) != 0;
+  const bool shared_ready = (d->flags & TP_MLP_FP8_SHARED_READY) != 0;
+  const int64_t P = swiglu ? 2 * F : F, Tp = (T + 15) / 16 * 16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t need = tp_mlp_workspace_bytes(d, phase);
+  if (need > 0) {
+    if (!a->workspace || a->workspace_bytes < need)
+      return fail(TP_MLP_EWORKSPACE, "%s: workspace of %zu bytes required, %zu given", fn, need,
+                  a->workspace ? a->workspace_bytes : (size_t)0);
+    if (!aligned16(a->workspace)) return fail(TP_MLP_EALIGN, "%s: workspace is not 16-byte aligned", fn);
+  }
+  REQUIRE_PTR(a->d_w_in);
+  REQUIRE_PTR(a->d_w_down);
+  if (!swiglu) REQUIRE_PTR(a->d_b_in);
+  if (swiglu && a->d_b_in) return fail(TP_MLP_EINVAL, "%s: d_b_in must be NULL for SwiGLU", fn);
+  REQUIRE_META(f8->meta_normed);
+  REQUIRE_META(f8->meta_w_in);
+  REQUIRE_META(f8->meta_act);
+  REQUIRE_META(f8->meta_w_down);
+  REQUIRE_META(f8->meta_d_out);
+  REQUIRE_META(f8->meta_d_pre);
+  REQUIRE_PTR(f8->w_in_t);
+  REQUIRE_PTR(f8->w_down_t);
+  if (T > 0) {
+    REQUIRE_PTR(a->d_out);
+    REQUIRE_PTR(a->pre_act);
+    REQUIRE_PTR(a->d_pre);
+    REQUIRE_PTR(a->d_normed_part);
+    REQUIRE_PTR(f8->normed_t);
+    REQUIRE_PTR(f8->act_t);
+    REQUIRE_PTR(f8->d_out_q);
+    REQUIRE_PTR(f8->d_out_t);
+    REQUIRE_PTR(f8->d_pre_q);
+    REQUIRE_PTR(f8->d_pre_t);
+    if (T * H >= ((int64_t)1 << 30) || H * Tp >= ((int64_t)1 << 30) || P * Tp >= ((int64_t)1 << 30))
+      return fail(TP_MLP_ESHAPE, "%s: a transposed code tensor would hold 2^30 or more elements", fn);
+  }
+  // T = 0: the casts and the GEMMs with M = T do nothing; the weight-gradient GEMMs (k extent 0)
+  // write zeros, or leave the buffers as they are when accumulating.
+  if (!shared_ready)
+    CHECK_HIP(launch_fp8_cast(kFp8E5M2, a->d_out, T, H, f8->d_out_q, f8->d_out_t, Tp, f8->meta_d_out,
+                              "fp8_cast_d_out", s),
+              "d_out cast");
+
+  // d_act = d_out Wd on d_out_q [T, H] and w_down_t [F, H], the activation backward fused.
+  GemmArgs b1 = fp8_gemm(T, F, H, f8->d_out_q, H, f8->meta_d_out, f8->w_down_t, H, f8->meta_w_down,
+                         swiglu ? "gemm_dact_swiglu_bwd_fp8" : "gemm_dact_gelu_bwd_fp8");
+  b1.pre = a->d_pre;
+  b1.aux = a->pre_act;
+  b1.ffn = F;
+  CHECK_HIP(launch_gemm_fp8(kFp8E5M2, kFp8E4M3, swiglu ? kEpiSwigluBwd : kEpiGeluBwd, b1, s), "d_act GEMM");
+
+  // d_w_down = d_out^T act on d_out_t [H, Tp] and act_t [F, Tp].
+  GemmArgs b2 = fp8_gemm(H, F, Tp, f8->d_out_t, Tp, f8->meta_d_out, f8->act_t, Tp, f8->meta_act, "gemm_wgrad_down_fp8");
+  b2.C = a->d_w_down;
+  b2.ldc = F;
+  b2.ksplit = gemm_ksplit(b2.M, b2.N, b2.K);
+  b2.ws = static_cast<float*>(a->workspace);
+  b2.accum = accum;
+  CHECK_HIP(launch_gemm_fp8(kFp8E5M2, kFp8E4M3, kEpiStoreF32, b2, s), "d_w_down GEMM");
+
+  CHECK_HIP(launch_fp8_cast(kFp8E5M2, a->d_pre, T, P, f8->d_pre_q, f8->d_pre_t, Tp, f8->meta_d_pre,
+                            "fp8_cast_d_pre", s),
+            "d_pre cast");
+
+  // d_normed partial = d_pre w_in on d_pre_q [T, P] and w_in_t [H, P].
+  GemmArgs b3 = fp8_gemm(T, H, P, f8->d_pre_q, P, f8->meta_d_pre, f8->w_in_t, P, f8->meta_w_in,
+                         "gemm_dgrad_normed_fp8");
+  b3.C = a->d_normed_part;
+  b3.ldc = H;
+  CHECK_HIP(launch_gemm_fp8(kFp8E5M2, kFp8E4M3, kEpiStoreF32, b3, s), "d_normed GEMM");
+
+  // d_w_in = d_pre^T normed on d_pre_t [P, Tp] and normed_t [H, Tp].
+  GemmArgs b4 = fp8_gemm(P, H, Tp, f8->d_pre_t, Tp, f8->meta_d_pre, f8->normed_t, Tp, f8->meta_normed,
+                         swiglu ? "gemm_wgrad_gate_up_fp8" : "gemm_wgrad_fc1_fp8");
+  b4.C = a->d_w_in;
+  b4.ldc = H;
+  b4.ksplit = gemm_ksplit(b4.M, b4.N, b4.K);
+  b4.ws = static_cast<float*>(a->workspace);
+  b4.accum = accum;
+  CHECK_HIP(launch_gemm_fp8(kFp8E5M2, kFp8E4M3, kEpiStoreF32, b4, s), "d_w_in GEMM");
+
+  if (!swiglu)
+    CHECK_HIP(launch_colsum(kBF16, a->d_pre, a->d_b_in, a->workspace, T, F, accum, s), "d_b_in column sum");
   return TP_MLP_OK;
 }
 

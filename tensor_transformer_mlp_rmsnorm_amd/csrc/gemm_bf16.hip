@@ -108,14 +108,16 @@ struct Operand {
   int64_t ld;
 };
 
-__device__ __forceinline__ Operand make_operand(const void* p, int64_t rows, int64_t ld) {
-  const int64_t bytes = rows * ld * (int64_t)sizeof(bf16_t);
+__device__ __forceinline__ Operand make_operand(const void* p, int64_t rows, int64_t ld, int elem_bytes = 2) {
+  const int64_t bytes = rows * ld * (int64_t)elem_bytes;
   return Operand{__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000), ld};
 }
 
-template <bool KC>
+template <bool KC, int EB = 2>
 __device__ __forceinline__ void issue_tile(const Operand& op, uint4* __restrict__ lds_tile, const RowMap& rm,
                                            int64_t k0, int64_t K, int wave, int lane) {
+  static_assert(KC || EB == 2, "MN-contiguous tiles hold bf16");
+  constexpr int kChunkElems = 16 / EB;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int b = wave * 4 + i;  // 1 KiB block of the tile
@@ -123,8 +125,8 @@ __device__ __forceinline__ void issue_tile(const Operand& op, uint4* __restrict_
     if constexpr (KC) {
       const int r = 8 * b + (lane >> 3);
       const int c = (lane & 7) ^ (r & 7);  // kc_index(r, c) == r * 8 + (lane & 7)
-      const int64_t grow = rm(r), gk = k0 + 8 * c;
-      if (grow >= 0 && gk < K) off = (unsigned)((grow * op.ld + gk) * 2);
+      const int64_t grow = rm(r), gk = k0 + kChunkElems * c;
+      if (grow >= 0 && gk < K) off = (unsigned)((grow * op.ld + gk) * EB);
     } else {
       const int kr = 2 * b + (lane >> 5);
       const int c = (lane & 31) ^ mn_swz(kr);  // mn_index(kr, c) == kr * 32 + (lane & 31)
@@ -142,7 +144,7 @@ __device__ __forceinline__ void issue_tile(const Operand& op, uint4* __restrict_
 // for all lanes, goes in the instruction's SGPR offset.  A block that lies
 // wholly past the operand gets SGPR offset 0, so the sum stays below 2^31 and a
 // lane marked out of range (VGPR offset 0x80000000) stays out of range.
-template <bool SWIGLU>
+template <bool SWIGLU, int EB = 2>
 struct QuarterLoads {
   unsigned vbase;     // byte offset of this lane's chunk in block 0
   int left;           // rows (SwiGLU: channels) from this lane's block-0 row to the operand's end, clamped
@@ -158,8 +160,8 @@ struct QuarterLoads {
     lim = SWIGLU ? rm.ffn : rm.limit;
     const int64_t d = lim - (first_row + lr);
     left = d > (1 << 20) ? (1 << 20) : (d < -1 ? -1 : (int)d);
-    vbase = (unsigned)(((first_row + lr) * op.ld + 8 * c) * 2);
-    k8 = 8 * c;
+    vbase = (unsigned)(((first_row + lr) * op.ld + (16 / EB) * c) * EB);
+    k8 = (16 / EB) * c;
   }
 
   __device__ __forceinline__ void issue(const Operand& op, uint4* __restrict__ lds_tile, int q, int64_t k0, int64_t K) {
@@ -171,7 +173,7 @@ struct QuarterLoads {
       const int dr = SWIGLU ? 8 * (i & 3) : 8 * i;  // row step of block i within its plane
       const int64_t plane = SWIGLU ? (i >> 2) * lim : 0;
       const bool block_in = first_row + dr < lim;  // the same for all lanes
-      const unsigned soff = block_in ? (unsigned)(((plane + dr) * op.ld + k0) * 2) : 0u;
+      const unsigned soff = block_in ? (unsigned)(((plane + dr) * op.ld + k0) * EB) : 0u;
       const unsigned voff = (kok && dr < left) ? vbase : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (__attribute__((address_space(3))) void*)(dst + i * 64), 16,
                                                voff, (int)soff, 0, 0);
@@ -360,7 +362,21 @@ __device__ __forceinline__ void read_frags_kc(Frags& f, unsigned abase, unsigned
       : "memory");
 }
 
-__device__ __forceinline__ void mma_tile(floatx4 (&acc)[8][4], const Frags& f) {
+// Operand element types of the ping-pong kernel: bf16, or FP8 codes in the
+// OCP formats FA (of A) and FB (of B), with the MFMA's format numbering
+// (0 = E4M3, 1 = E5M2).  A k-tile is 128 bytes of every row in both cases:
+// 64 bf16 or 128 FP8 values.
+struct PpBf16 {
+  static constexpr int kBytes = 2;
+  static constexpr bool kFp8 = false;
+};
+template <int FA, int FB>
+struct PpFp8 {
+  static constexpr int kBytes = 1;
+  static constexpr bool kFp8 = true;
+};
+
+__device__ __forceinline__ void mma_tile(floatx4 (&acc)[8][4], const Frags& f, PpBf16) {
 #pragma unroll
   for (int s = 0; s < kBK / 32; ++s)
 #pragma unroll
@@ -369,6 +385,33 @@ __device__ __forceinline__ void mma_tile(floatx4 (&acc)[8][4], const Frags& f) {
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.b[s][j]),
                                                             __builtin_bit_cast(bf16x8, f.a[s][i]), acc[i][j], 0, 0, 0);
+}
+
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+constexpr int kUnitScales = 0x7f7f7f7f;  // E8M0 block scales of 2^0: the scaled MFMA without scaling
+
+// FP8: one 16 x 16 x 128 MFMA per block and k-tile.  A lane's 32-byte operand
+// is its row's k chunks (lane / 16) and 4 + lane / 16 -- the two 16-byte
+// fragments the bf16 schedule reads for its two k halves.  Any assignment of
+// the 128 k to lane bytes gives the same sums as long as A and B use the same
+// one, and they do.
+template <int FA, int FB>
+__device__ __forceinline__ void mma_tile(floatx4 (&acc)[8][4], const Frags& f, PpFp8<FA, FB>) {
+  intx8 bv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    bv[j] = __builtin_shufflevector(__builtin_bit_cast(intx4, f.b[0][j]), __builtin_bit_cast(intx4, f.b[1][j]), 0, 1,
+                                    2, 3, 4, 5, 6, 7);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const intx8 av = __builtin_shufflevector(__builtin_bit_cast(intx4, f.a[0][i]), __builtin_bit_cast(intx4, f.a[1][i]),
+                                             0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv[j], av, acc[i][j], FB, FA, 0, kUnitScales, 0,
+                                                                   kUnitScales);
+  }
 }
 
 // Phase boundary: wait until at most VM of this wave's tile loads are in flight
@@ -386,10 +429,12 @@ __device__ __forceinline__ void phase_end() {
 
 __device__ __forceinline__ int slot_u4(int x) { return (x % kSlots) * kTileU4; }
 
-template <int EPI>
+template <int EPI, class OP>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs g, int ntm, int ntn) {
   extern __shared__ uint4 smem[];  // 5 operand slots = 160 KiB
   constexpr bool kSwiglu = EPI == kEpiSwigluFwd;
+  constexpr int EB = OP::kBytes;
+  constexpr int kK = 128 / EB;  // k per tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -398,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
   int tm, tn, ks;
   tile_coords(blockIdx.x, ntm, ntn, g.ksplit, tm, tn, ks);
   const int64_t K = g.K;
-  const int64_t kper = ((K + (int64_t)g.ksplit * kBK - 1) / ((int64_t)g.ksplit * kBK)) * kBK;
+  const int64_t kper = ((K + (int64_t)g.ksplit * kK - 1) / ((int64_t)g.ksplit * kK)) * kK;
   const int64_t kbeg = (int64_t)ks * kper;
   const int64_t kend = K < kbeg + kper ? K : kbeg + kper;
   const RowMap ra{(int64_t)tm * kBM, g.M, false, 0};
@@ -411,13 +456,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const Operand opa = make_operand(g.A, g.M, g.lda);
-  const Operand opb = make_operand(g.B, kSwiglu ? 2 * g.ffn : g.N, g.ldb);
-  const int nk = kend > kbeg ? (int)((kend - kbeg + kBK - 1) / kBK) : 0;
+  const Operand opa = make_operand(g.A, g.M, g.lda, EB);
+  const Operand opb = make_operand(g.B, kSwiglu ? 2 * g.ffn : g.N, g.ldb, EB);
+  const int nk = kend > kbeg ? (int)((kend - kbeg + kK - 1) / kK) : 0;
   // prologue: every wave loads 4 blocks of each of A_0, B_0, A_1
-  issue_tile<true>(opa, smem + slot_u4(0), ra, kbeg, kend, wave, lane);
-  issue_tile<true>(opb, smem + slot_u4(1), rb, kbeg, kend, wave, lane);
-  if (nk > 1) issue_tile<true>(opa, smem + slot_u4(2), ra, kbeg + kBK, kend, wave, lane);
+  issue_tile<true, EB>(opa, smem + slot_u4(0), ra, kbeg, kend, wave, lane);
+  issue_tile<true, EB>(opb, smem + slot_u4(1), rb, kbeg, kend, wave, lane);
+  if (nk > 1) issue_tile<true, EB>(opa, smem + slot_u4(2), ra, kbeg + kK, kend, wave, lane);
   phase_end<0>();
 
   const unsigned lane_part = (unsigned)((lane & 15) * 128 + (((lane >> 4) ^ (lane & 7)) * 16));
@@ -427,15 +472,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
   auto slot_bytes = [](int x) { return (unsigned)(slot_u4(x) * 16); };
   Frags f;
   // group A loads B tiles, group B loads A tiles
-  QuarterLoads<kSwiglu> lb(opb, rb, q, lane);
-  QuarterLoads<false> la(opa, ra, q, lane);
+  QuarterLoads<kSwiglu, EB> lb(opb, rb, q, lane);
+  QuarterLoads<false, EB> la(opa, ra, q, lane);
   if (wm == 0) {
     // phase 2j: read k-tile j, load B of k-tile j+1; phase 2j+1: multiply k-tile j
     for (int j = 0; j < nk; ++j) {
       read_frags_kc(f, a_lane + slot_bytes(2 * j), b_lane + slot_bytes(2 * j + 1));
-      if (j + 1 < nk) lb.issue(opb, smem + slot_u4(2 * j + 3), q, kbeg + (int64_t)(j + 1) * kBK, kend);
+      if (j + 1 < nk) lb.issue(opb, smem + slot_u4(2 * j + 3), q, kbeg + (int64_t)(j + 1) * kK, kend);
       phase_end<kNoVm>();
-      mma_tile(acc, f);
+      mma_tile(acc, f, OP{});
       phase_end<0>();  // B of k-tile j+1 has landed
     }
     if (nk > 0) phase_end<kNoVm>();  // idle in the last phase
@@ -445,14 +490,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
     for (int j = 0; j < nk; ++j) {
       read_frags_kc(f, a_lane + slot_bytes(2 * j), b_lane + slot_bytes(2 * j + 1));
       if (j + 2 < nk) {
-        la.issue(opa, smem + slot_u4(2 * j + 4), q, kbeg + (int64_t)(j + 2) * kBK, kend);
+        la.issue(opa, smem + slot_u4(2 * j + 4), q, kbeg + (int64_t)(j + 2) * kK, kend);
         phase_end<8>();  // A of k-tile j+1 has landed; k-tile j+2's may be in flight
       } else {
         phase_end<0>();
       }
-      mma_tile(acc, f);
+      mma_tile(acc, f, OP{});
       phase_end<kNoVm>();
     }
+  }
+  if constexpr (OP::kFp8) {
+    // dequantisation: the product of the operands' inverse scales, read after the main loop
+    const float deq = g.scale_inv_a[0] * g.scale_inv_b[0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] *= deq;
   }
   epilogue<EPI, 8, 4>(g, acc, (int64_t)tm * kBM + wm * 128, (int64_t)tn * kBN + wn * 64,
                       (int64_t)tn * kSwigluChannels + wn * 32, ks, lane);
@@ -555,8 +608,24 @@ hipError_t launch_two_stage(const GemmArgs& ga, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool AK, bool BKC, int EPI>
+template <int EPI, class OP>
+hipError_t launch_pingpong(const GemmArgs& ga, int ntm, int ntn, hipStream_t s) {
+  auto kernel = gemm_nt_pingpong_kernel<EPI, OP>;
+  static bool configured = false;  // raise the dynamic LDS limit once per instantiation
+  if (!configured) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytesPingPong);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL(kernel, dim3(ntm * ntn * ga.ksplit), dim3(kThreads), kSmemBytesPingPong, s, ga, ntm, ntn);
+  return hipGetLastError();
+}
+
+// OP: PpBf16, or PpFp8<FA, FB> (both operands K-contiguous).
+template <bool AK, bool BKC, int EPI, class OP = PpBf16>
 hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
+  static_assert(!OP::kFp8 || (AK && BKC), "FP8 operands are K-contiguous");
   const int ntm = (int)((g.M + kBM - 1) / kBM);
   const int ntn = (EPI == kEpiSwigluFwd) ? (int)((g.ffn + kSwigluChannels - 1) / kSwigluChannels)
                                          : (int)((g.N + kBN - 1) / kBN);
@@ -568,16 +637,7 @@ hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
     KernelTimer timer(g.tag ? g.tag : "gemm", s);
     hipError_t e;
     if constexpr (AK && BKC) {
-      static bool configured = false;
-      if (!configured) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nt_pingpong_kernel<EPI>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmemBytesPingPong);
-        if (e != hipSuccess) return e;
-        configured = true;
-      }
-      hipLaunchKernelGGL((gemm_nt_pingpong_kernel<EPI>), dim3(ntm * ntn * ga.ksplit), dim3(kThreads),
-                         kSmemBytesPingPong, s, ga, ntm, ntn);
-      e = hipGetLastError();
+      e = launch_pingpong<EPI, OP>(ga, ntm, ntn, s);
     } else {
       // the tile shape with the least (rounds of one workgroup per CU) x (tile area); a function of the
       // shape and the CU count only, so results are reproducible on a given device
@@ -614,6 +674,28 @@ hipError_t launch_gemm_bf16(bool ak, bool bk, Epi epi, const GemmArgs& g, hipStr
     }
   } else if (!ak && !bk) {
     if (epi == kEpiStoreF32) return launch_t<false, false, kEpiStoreF32>(g, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_fp8(int fmt_a, int fmt_b, Epi epi, const GemmArgs& g, hipStream_t s) {
+  if (fmt_a == kFp8E4M3 && fmt_b == kFp8E4M3) {
+    using OP = PpFp8<kFp8E4M3, kFp8E4M3>;
+    switch (epi) {
+      case kEpiStoreF32: return launch_t<true, true, kEpiStoreF32, OP>(g, s);
+      case kEpiSwigluFwd: return launch_t<true, true, kEpiSwigluFwd, OP>(g, s);
+      case kEpiGeluFwd: return launch_t<true, true, kEpiGeluFwd, OP>(g, s);
+      case kEpiResidual: return launch_t<true, true, kEpiResidual, OP>(g, s);
+      default: break;
+    }
+  } else if (fmt_a == kFp8E5M2 && fmt_b == kFp8E4M3) {
+    using OP = PpFp8<kFp8E5M2, kFp8E4M3>;
+    switch (epi) {
+      case kEpiStoreF32: return launch_t<true, true, kEpiStoreF32, OP>(g, s);
+      case kEpiSwigluBwd: return launch_t<true, true, kEpiSwigluBwd, OP>(g, s);
+      case kEpiGeluBwd: return launch_t<true, true, kEpiGeluBwd, OP>(g, s);
+      default: break;
+    }
   }
   return hipErrorInvalidValue;
 }

@@ -61,6 +61,10 @@ struct GemmArgs {
   // kEpiStoreF32 only: add C's current values to the product (slice 0 reads
   // and adds them; with a k split the other slices are then added as usual).
   int accum;
+  // FP8 operands: device pointers to the inverse scales of A and B; the
+  // product is multiplied by scale_inv_a[0] * scale_inv_b[0] before the epilogue.
+  const float* scale_inv_a;
+  const float* scale_inv_b;
 };
 
 // Number of k-slices for a bf16 fp32-output GEMM: a function of the shape only
@@ -80,6 +84,25 @@ hipError_t launch_gemm(DType dt, bool a_kcontig, bool b_kcontig, Epi epi, const 
                        hipStream_t s);
 // The bf16 kernel (256 x 256 tiles); launch_gemm routes bf16 here.
 hipError_t launch_gemm_bf16(bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs& g, hipStream_t s);
+
+// FP8 formats (the MFMA's numbering).
+enum Fp8Fmt { kFp8E4M3 = 0, kFp8E5M2 = 1 };
+
+// FP8 GEMM, both operands K-contiguous codes ([M, K] and [N, K], K a multiple
+// of 16): (fmt_a, fmt_b) = (E4M3, E4M3) with the forward epilogues or
+// kEpiStoreF32, (E5M2, E4M3) with the activation-backward epilogues or
+// kEpiStoreF32.  Needs g.scale_inv_a / g.scale_inv_b.
+hipError_t launch_gemm_fp8(int fmt_a, int fmt_b, Epi epi, const GemmArgs& g, hipStream_t s);
+
+// FP8 casts with delayed scaling (meta layout in fp8.hip).  x is bf16
+// [R, C] (C a multiple of 8); out [R, C] and/or out_t [C, ldt] (ldt >= R, a
+// multiple of 16; columns R .. ldt-1 written as zero); either may be null.
+constexpr int kFp8MaxMetas = 16;
+constexpr int kFp8MaxHistory = 1024;
+hipError_t launch_fp8_cast(int fmt, const void* x, int64_t R, int64_t C, uint8_t* out, uint8_t* out_t, int64_t ldt,
+                           float* meta, const char* tag, hipStream_t s);
+hipError_t launch_fp8_update(float* const* metas, int count, int history_len, hipStream_t s);
+hipError_t launch_fp8_meta_init(float* meta, int fmt, int history_len, hipStream_t s);
 
 hipError_t launch_rmsnorm_fwd(DType dt, const void* x, const void* w, void* n, float* rstd,
                               int64_t T, int64_t H, float eps, hipStream_t s);

@@ -428,3 +428,101 @@ class SequenceParallelStep(ShardedStep):
             r["d_norm_w"] = [c(t) for t in self.rank_d_norm_w]
             r["d_b_down"] = [c(t) for t in self.rank_d_b_down]
         return r
+
+
+class Fp8Step(ShardedStep):
+    """The step with every GEMM on FP8 codes and per-tensor delayed scaling
+    (tp_mlp_forward_fp8 / tp_mlp_backward_fp8; Transformer Engine's FP8 with
+    delayed scaling, "Megatron-Core Guide: 5D Distributed Training
+    Architecture", feature list item 6).
+
+    One meta per tensor role is shared by all shards, so each role's amax is
+    the maximum over the tensor-parallel group; tp_mlp_fp8_update_scales
+    renews the scales at the end of every step.  The replicated tensors' codes
+    (N and its transpose, dY and its transpose) are cast once, by shard 0's
+    calls, like the replicated RMSNorm itself.  The norm backward, the sums and
+    the update are those of ShardedStep."""
+
+    ROLES = (("meta_normed", L.FP8_E4M3), ("meta_w_in", L.FP8_E4M3), ("meta_act", L.FP8_E4M3),
+             ("meta_w_down", L.FP8_E4M3), ("meta_d_out", L.FP8_E5M2), ("meta_d_pre", L.FP8_E5M2))
+
+    def __init__(self, w, tensors, device="cuda", out_of_place_sgd: bool = False, stream=None,
+                 history_len: int = 16):
+        if w.dtype != "bf16":
+            raise ValueError("the FP8 step takes bf16 tensors")
+        super().__init__(w, tensors, device, out_of_place_sgd, stream)
+        T, H, F = self.T, self.H, self.F
+        P, Tp = (2 * F if self.swiglu else F), (T + 15) // 16 * 16
+        u8 = lambda shape: torch.empty(shape, dtype=torch.uint8, device=self.dev)
+        self.history_len = history_len
+        self.metas = {}
+        for name, fmt in self.ROLES:
+            m = torch.empty(L.fp8_meta_floats(history_len), dtype=torch.float32, device=self.dev)
+            L.tp_mlp_fp8_meta_init(m, fmt, history_len, stream=self.stream)
+            self.metas[name] = m
+        shared = dict(normed_q=u8((T, H)), normed_t=u8((H, Tp)), d_out_q=u8((T, H)), d_out_t=u8((H, Tp)))
+        self.codes_shared = shared
+        for sh in self.shards:
+            codes = dict(w_in_q=u8((P, H)), w_in_t=u8((H, P)), act_q=u8((T, F)), act_t=u8((F, Tp)),
+                         w_down_q=u8((H, F)), w_down_t=u8((F, H)), d_pre_q=u8((T, P)), d_pre_t=u8((P, Tp)))
+            sh["codes"] = codes
+            sh["f8"] = L.make_fp8_args(history_len, **self.metas, **shared, **codes)
+
+    def forward(self, mode: str = "equivalence", rows=None) -> None:
+        if rows is not None or mode != "equivalence":
+            raise ValueError("the FP8 step runs the whole batch in equivalence mode")
+        T, H, st = self.T, self.H, self.stream
+        for s, sh in enumerate(self.shards):
+            flags = (L.NORMED_READY if s > 0 else 0) | (L.FUSE_EPILOGUE if self.fuse else 0)
+            L.tp_mlp_forward_fp8(self._desc(flags), self.x, self.norm_w, sh["w_in"], sh["b_in"], sh["w_down"],
+                                 self.normed, self.rstd, sh["pre"], sh["act"], self.out if self.fuse else sh["z"],
+                                 self.b_down, sh["f8"], stream=st)
+        if not self.fuse:
+            L.tp_partial_sum([sh["z"] for sh in self.shards], T, H, self.x, self.b_down, self.cdt, self.out,
+                             self.cdt, stream=st)
+
+    def backward(self, mode: str = "equivalence") -> None:
+        if mode != "equivalence":
+            raise ValueError("the FP8 step runs in equivalence mode")
+        T, H = self.T, self.H
+        for s, sh in enumerate(self.shards):
+            flags = L.FP8_SHARED_READY if s > 0 else 0
+            L.tp_mlp_backward_fp8(self._desc(flags), L.BWD_SHARD, sh["f8"], stream=self.stream,
+                                  normed=self.normed, pre_act=sh["pre"], act=sh["act"], w_in=sh["w_in"],
+                                  w_down=sh["w_down"], d_out=self.out, d_pre=sh["d_pre"], d_w_in=sh["d_w_in"],
+                                  d_b_in=sh["d_b_in"], d_w_down=sh["d_w_down"], d_normed_part=sh["dN_part"],
+                                  workspace=self.workspace)
+        if not self.fuse:
+            L.tp_partial_sum([sh["dN_part"] for sh in self.shards], T, H, None, None, L.F32, self.dN, L.F32,
+                             stream=self.stream)
+        self._norm_backward(self.dN, self.out, self.dx, self.d_norm_w, self.d_b_down)
+
+    def update_scales(self) -> None:
+        L.tp_mlp_fp8_update_scales([self.metas[n] for n, _ in self.ROLES], self.history_len, stream=self.stream)
+
+    def step(self, mode: str = "equivalence", update: bool = True, microbatches: int = 1) -> None:
+        if microbatches != 1:
+            raise ValueError("the FP8 step takes the whole batch")
+        self.forward(mode)
+        self.backward(mode)
+        if update:
+            self.sgd()
+        self.update_scales()
+
+    def meta_state(self) -> dict:
+        """{role: (scale, scale_inv, amax, history)} as CPU values."""
+        out = {}
+        for name, _ in self.ROLES:
+            m = self.metas[name].cpu()
+            out[name[5:]] = (float(m[0]), float(m[1]), float(m[2]), m[4:].clone())
+        return out
+
+    def load_meta_state(self, state: dict) -> None:
+        """Restore metas saved by meta_state (or built from another run):
+        {role: (scale, scale_inv, amax, history)}."""
+        for name, _ in self.ROLES:
+            sc, si, am, hist = state[name[5:]]
+            m = self.metas[name]
+            vals = torch.tensor([sc, si, am, float(m[3])] + [float(h) for h in hist], dtype=torch.float32)
+            m.copy_(vals.to(self.dev))
+

@@ -238,3 +238,82 @@ def test_step_driver_api():
     for m in ("forward", "backward", "backward_rows", "sgd", "adamw", "step", "results"):
         assert callable(getattr(step.ShardedStep, m, None)), m
     assert step.microbatch_bounds(7, 3) == [(0, 3), (3, 5), (5, 7)]
+
+
+def _fp8_args(**kw):
+    f = L.tp_mlp_fp8_args()
+    f.history_len = kw.pop("history_len", 4)
+    for n in L.FP8_META_FIELDS + L.FP8_CODE_FIELDS:
+        setattr(f, n, kw.pop(n, A))
+    assert not kw
+    return f
+
+
+def test_fp8_checks(lib):
+    fwd = lambda d, f: lib.tp_mlp_forward_fp8(ctypes.byref(d), A, A, A, None, A, A, A, A, A, A, A,
+                                              ctypes.byref(f) if f is not None else None, None)
+    assert fwd(_desc(dt=L.F32), _fp8_args()) == L.EDTYPE                # bf16 only
+    assert fwd(_desc(H=72), _fp8_args()) == L.ESHAPE                    # H multiple of 16
+    assert fwd(_desc(F=40), _fp8_args()) == L.ESHAPE                    # F multiple of 16
+    assert fwd(_desc(), None) == L.EINVAL
+    assert fwd(_desc(), _fp8_args(history_len=0)) == L.EINVAL
+    assert fwd(_desc(), _fp8_args(history_len=1025)) == L.EINVAL
+    assert fwd(_desc(), _fp8_args(meta_act=None)) == L.EINVAL
+    assert fwd(_desc(), _fp8_args(meta_act=A + 2)) == L.EALIGN
+    assert fwd(_desc(), _fp8_args(act_t=MIS)) == L.EALIGN
+    assert fwd(_desc(flags=8), _fp8_args()) == L.EINVAL                 # SHARED_READY is a backward flag
+    # T = 0 forward: a no-op that needs no activation buffers
+    assert lib.tp_mlp_forward_fp8(ctypes.byref(_desc(T=0)), None, A, A, None, A, None, None, None, None, None, A,
+                                  ctypes.byref(_fp8_args(normed_q=None, normed_t=None, act_q=None, act_t=None)),
+                                  None) == L.OK
+    a = L.tp_mlp_bwd_args()
+    for name, _ in L.tp_mlp_bwd_args._fields_:
+        if name != "workspace_bytes":
+            setattr(a, name, A)
+    a.d_b_in = None
+    a.workspace_bytes = 1 << 30
+    bwd = lambda d, f, phase=L.BWD_SHARD: lib.tp_mlp_backward_fp8(ctypes.byref(d), phase, ctypes.byref(a),
+                                                                  ctypes.byref(f), None)
+    assert bwd(_desc(dt=L.F32), _fp8_args()) == L.EDTYPE
+    assert bwd(_desc(), _fp8_args(), phase=3) == L.EINVAL
+    assert bwd(_desc(flags=16), _fp8_args()) == L.EINVAL
+    assert bwd(_desc(), _fp8_args(d_pre_t=None)) == L.EINVAL
+    assert bwd(_desc(), _fp8_args(meta_d_pre=None)) == L.EINVAL
+    # meta init, cast and update validate before launching
+    assert lib.tp_mlp_fp8_meta_init(A, 2, 4, None) == L.EINVAL
+    assert lib.tp_mlp_fp8_meta_init(A, 0, 0, None) == L.EINVAL
+    assert lib.tp_mlp_fp8_meta_init(None, 0, 4, None) == L.EINVAL
+    cast = lib.tp_mlp_fp8_cast
+    assert cast(4, 12, A, 0, A, A, None, 0, None) == L.ESHAPE           # cols multiple of 8
+    assert cast(4, 16, A, 0, A, None, None, 0, None) == L.EINVAL        # nothing to write
+    assert cast(20, 16, A, 0, A, None, A, 16, None) == L.ESHAPE         # ldt < rows
+    assert cast(4, 16, A, 0, A, None, A, 24, None) == L.ESHAPE          # ldt not a multiple of 16
+    assert cast(4, 16, A, 5, A, A, None, 0, None) == L.EINVAL           # format
+    assert cast(4, 16, A, 0, None, A, None, 0, None) == L.EINVAL        # meta
+    assert cast(4, 16, MIS, 0, A, A, None, 0, None) == L.EALIGN
+    assert cast(0, 16, None, 0, A, A, None, 0, None) == L.OK            # no rows, no padding: no-op
+    P = ctypes.c_void_p
+    upd = lib.tp_mlp_fp8_update_scales
+    assert upd((P * 17)(*([A] * 17)), 17, 4, None) == L.EINVAL          # at most 16 metas
+    assert upd((P * 1)(None), 1, 4, None) == L.EINVAL
+    assert upd((P * 1)(A), 1, 2000, None) == L.EINVAL
+    assert upd(None, 0, 4, None) == L.OK
+    g = lib.tp_mlp_fp8_gemm
+    sinv = A
+    call = lambda M=64, N=64, K=64, lda=64, ldb=64, fa=0, fb=0, ldc=64, ws=None, wsb=0, Ap=A, C=A + 65536: \
+        g(M, N, K, Ap, lda, fa, sinv, A, ldb, fb, sinv, C, ldc, 0, ws, wsb, None)
+    assert call(fa=1, fb=1) == L.EINVAL                                 # (E5M2, E5M2) is not a pair
+    assert call(fa=0, fb=1) == L.EINVAL
+    assert call(K=40, lda=48, ldb=48) == L.ESHAPE                       # K multiple of 16
+    assert call(lda=32) == L.ESHAPE                                     # lda >= K
+    assert call(N=62, ldc=64) == L.ESHAPE                               # N multiple of 4
+    assert call(ldc=60) == L.ESHAPE
+    assert call(M=-1) == L.EINVAL
+    assert call(Ap=MIS) == L.EALIGN
+    assert call(C=None) == L.EINVAL
+    assert call(M=0) == L.OK                                            # empty: no-op
+    need = lib.tp_mlp_fp8_gemm_workspace_bytes(64, 4096, 8192, 4096)
+    assert need == 3 * 64 * 4096 * 4
+    assert call(N=4096, K=8192, lda=8192, ldb=8192, ldc=4096) == L.EWORKSPACE
+    assert call(N=4096, K=8192, lda=8192, ldb=8192, ldc=4096, ws=MIS, wsb=need) == L.EALIGN
+

@@ -19,6 +19,23 @@ term) lands far above 2e-2.
 import numpy as np
 import torch
 
+# FP8 GEMMs.  The matrix unit sums
+# each 128-long block of k with about 12 bits of precision relative to the
+# block's largest product (2^-11.6 worst relative to that product and 2^-12.8
+# relative to the block's sum of |products| were measured); a GEMM of codes
+# given to both sides must then satisfy, per output,
+#     |got - ref| <= FP8_GEMM_REL * (sum_k |a_k b_k|) * dequantisation.
+FP8_GEMM_REL = 2.0 ** -10
+# A whole FP8 step compares tensors that went through casts of computed
+# values: where the GPU's bf16 input to a cast differs by an ulp from the
+# oracle's (the block sums above), a rounding boundary can lie in between and
+# the code differs by a whole FP8 step (12.5% in E4M3, 25% in E5M2).  About
+# 0.1-0.6% of the codes of a step differ this way, so elementwise bounds do
+# not apply; the step is compared by the relative Frobenius error of each
+# tensor, which such flips keep below 1.7e-2 (measured) while a wrong operand,
+# index or scale moves it to O(1).
+FP8_STEP_FROB = 3e-2
+
 FP32_ATOL = 1e-5
 BF16_RTOL = 2e-2
 
@@ -68,3 +85,31 @@ def check(name, got, ref, dtype: str, rowwise: bool = False, report=None) -> flo
             report[name] = e
         assert e <= BF16_RTOL, f"{name}: floored relative error {e:.3e} > {BF16_RTOL}"
     return e
+
+
+def frob_rel(got, ref) -> float:
+    g, r = _np(got), _np(ref)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    n = float(np.linalg.norm(r))
+    return float(np.linalg.norm(g - r)) / n if n > 0 else float(np.linalg.norm(g))
+
+
+def check_fp8_gemm(name, got, ref, abs_products, deq: float, report=None) -> float:
+    """Per-output bound of an FP8 GEMM of identical codes (FP8_GEMM_REL)."""
+    g, r, a = _np(got), _np(ref), _np(abs_products)
+    assert g.shape == r.shape == a.shape, (g.shape, r.shape, a.shape)
+    bound = FP8_GEMM_REL * a * abs(deq) + 1e-30
+    e = float(np.max(np.abs(g - r) / bound)) if g.size else 0.0
+    if report is not None:
+        report[name] = e
+    assert e <= 1.0, f"{name}: error / FP8 GEMM bound {e:.3e} > 1"
+    return e
+
+
+def check_fp8_step(name, got, ref, report=None) -> float:
+    e = frob_rel(got, ref)
+    if report is not None:
+        report[name] = e
+    assert e <= FP8_STEP_FROB, f"{name}: relative Frobenius error {e:.3e} > {FP8_STEP_FROB}"
+    return e
+
