@@ -20,6 +20,8 @@ shard's parameters (each kernel against HBM bandwidth), and the step run as 2
 microbatches whose weight gradients accumulate in fp32.  `sequence_parallel`
 times the same step in the sequence-parallel layout (norm, residual and bias
 on each rank's token rows; reduce-scatter and all-gather at the boundaries).
+`fp8_path` times the step with every GEMM on FP8 codes (delayed scaling),
+its GEMMs against the fp8 MFMA peak and its casts against HBM bandwidth.
 """
 
 from __future__ import annotations
@@ -38,6 +40,7 @@ METRIC = "fwd+bwd TFLOP/s per TP-shard SwiGLU MLP, % of bf16 MFMA peak; tokens/s
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 
 
 def gemm_flops(w) -> dict:
@@ -187,6 +190,64 @@ def optimizer_path(st, w, steps: int, warmup: int) -> dict:
     return res
 
 
+def fp8_cast_bytes(w) -> dict:
+    """Algorithmic HBM bytes of one launch of each FP8 cast kernel (bf16 in,
+    row codes + transposed codes out), by kernel name.  Per shard the
+    weights cast launches twice (w_in, then w_down); their mean is listed."""
+    T, H, F = w.tokens, w.hidden, w.ffn_local
+    P = 2 * F if w.act == "swiglu" else F
+    Tp = (T + 15) // 16 * 16
+    both = lambda r, c, rows_t: r * c * 2 + r * c + c * rows_t
+    return {"fp8_cast_normed": both(T, H, Tp), "fp8_cast_d_out": both(T, H, Tp), "fp8_cast_act": both(T, F, Tp),
+            "fp8_cast_d_pre": both(T, P, Tp), "fp8_cast_weights": (both(P, H, P) + both(H, F, H)) // 2}
+
+
+def fp8_path(w, t, steps: int, warmup: int) -> dict:
+    """The same step with every GEMM on FP8 codes (E4M3 forward, E5M2
+    gradients, per-tensor delayed scaling): its time, and each FP8 GEMM
+    against the fp8 MFMA peak and each cast against HBM bandwidth."""
+    import torch
+    from tensor_transformer_mlp_rmsnorm_amd import _lib as L
+    from tensor_transformer_mlp_rmsnorm_amd.step import Fp8Step
+
+    st = Fp8Step(w, t, device="cuda:0", out_of_place_sgd=True)
+    for _ in range(max(1, warmup)):
+        st.step()
+    torch.cuda.synchronize()
+    L.tp_mlp_profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    L.tp_mlp_profile_enable(False)
+    prof = L.tp_mlp_profile_entries()
+    del st
+    torch.cuda.empty_cache()
+    fl = {k + "_fp8": v for k, v in gemm_flops(w).items()}
+    by = fp8_cast_bytes(w)
+    kernels = {}
+    for k, (n, tot) in prof.items():
+        secs = tot / 1e3
+        if k in fl:
+            ach = fl[k] * n / secs / 1e12
+            kernels[k] = {"bound": "mfma", "achieved": ach, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                          "frac": ach / PEAK_FP8_TFLOPS, "per_launch": fl[k], "avg_ms": tot / n, "launches": n}
+        elif k in by:
+            ach = by[k] * n / secs / 1e9
+            kernels[k] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": ach / PEAK_HBM_GBS, "per_launch": by[k], "avg_ms": tot / n, "launches": n}
+        else:
+            kernels[k] = roofline_entry(k, n, tot, w, steps)
+    gemm_ms = sum(tot for k, (n, tot) in prof.items() if k in fl) / steps
+    return {"recipe": "E4M3 N/weights/activation, E5M2 gradients; delayed scaling, amax history 16, amax shared by "
+                      "the shards", "ms_per_step": ms, "tflops": w.flops_per_step / (ms / 1e3) / 1e12,
+            "gemm_ms_per_step": gemm_ms,
+            "gemm_tflops": w.flops_per_step / (gemm_ms / 1e3) / 1e12 if gemm_ms > 0 else None,
+            "gemm_pct_of_fp8_peak": 100.0 * w.flops_per_step / (gemm_ms / 1e3) / 1e12 / PEAK_FP8_TFLOPS
+            if gemm_ms > 0 else None, "kernels": kernels}
+
+
 def sequence_parallel_timing(w, t, steps: int, warmup: int) -> dict:
     """The step in the sequence-parallel layout, same inputs and flop count."""
     import torch
@@ -215,7 +276,9 @@ def main() -> int:
     ap.add_argument("--workload", default="llama3_8b_tp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--no-extras", action="store_true", help="skip the optimiser-path measurements")
+    ap.add_argument("--no-extras", action="store_true", help="skip the measurements after the timed step")
+    ap.add_argument("--extras", default="optimizer,sp,fp8",
+                    help="comma-separated measurements after the timed step: optimizer, sp, fp8")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -290,12 +353,18 @@ def main() -> int:
         "roofline": roof,
         "kernels": kernels,
     }
-    if not args.no_extras:
+    extras = set() if args.no_extras else {e.strip() for e in args.extras.split(",") if e.strip()}
+    if "optimizer" in extras:
         out["optimizer_path"] = optimizer_path(st, w, args.steps, args.warmup)
-        if w.n_run == w.shards and w.shards > 1:
-            out["sequence_parallel"] = sequence_parallel_timing(w, t, args.steps, args.warmup)
-    if not args.no_cpu_baseline:
+    if "sp" in extras and w.n_run == w.shards and w.shards > 1:
+        out["sequence_parallel"] = sequence_parallel_timing(w, t, args.steps, args.warmup)
+    if "fp8" in extras and w.dtype == "bf16" and w.hidden % 16 == 0 and w.ffn_local % 16 == 0:
         del st
+        torch.cuda.empty_cache()
+        st = None
+        out["fp8_path"] = fp8_path(w, t, args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        st = None
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(w, t, args.cpu_budget)
     else:

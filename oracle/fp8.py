@@ -27,7 +27,7 @@ delayed scaling through Transformer Engine":
 * Per-tensor delayed scaling: a tensor's meta holds its scale s (initially 1),
   the running amax of this step and a history of the last L amaxes (newest
   first).  Every cast during a step uses the current s and folds max|x| into
-  the running amax.  At the end of the step the running amax enters the
+  the running amax (NaN elements have no magnitude and are ignored).  At the end of the step the running amax enters the
   history (the oldest entry drops out), the running amax returns to 0, and
   s becomes fmt_max / max(history) in fp32 when that maximum is positive and
   finite; otherwise s keeps its value (so an all-zero history keeps s = 1).
@@ -147,8 +147,12 @@ class Fp8Meta:
         return np.float32(1.0 / float(self.scale))
 
     def record(self, x) -> None:
-        if np.size(x):
-            self.amax = np.float32(max(float(self.amax), float(np.max(np.abs(np.asarray(x, dtype=np.float32))))))
+        """Fold max|x| into the running amax; NaN elements are ignored (an
+        amax is a maximum of magnitudes, and a NaN has none)."""
+        a = np.abs(np.asarray(x, dtype=np.float32))
+        a = a[~np.isnan(a)]
+        if a.size:
+            self.amax = np.float32(max(float(self.amax), float(np.max(a))))
 
     def update(self) -> None:
         """End of step: the running amax enters the history; a new scale."""
@@ -308,3 +312,90 @@ def product_error_bound(a, b, sa, sb, fa: Fp8Format, fb: Fp8Format) -> np.ndarra
           + np.maximum(0.0, np.abs(b) - fb.max / float(sb)))
     bound = ea @ (np.abs(b) + eb).T + np.abs(a) @ eb.T
     return bound + 2.0 ** -21 * ((np.abs(a) + ea) @ (np.abs(b) + eb).T)
+
+
+def _cast_rows(x, meta: Fp8Meta, chunk: int = 1024) -> np.ndarray:
+    """cast() of a large [rows, cols] matrix, a block of rows at a time (the
+    same codes and amax; bounded temporaries)."""
+    x = np.asarray(x)
+    codes = np.empty(x.shape, dtype=np.uint8)
+    for lo in range(0, x.shape[0], chunk):
+        codes[lo:lo + chunk] = cast(x[lo:lo + chunk], meta)
+    return codes
+
+
+def fp8_sampled_step(x, p: Params, act: str, eps: float, lr: float, metas: Dict[str, Fp8Meta], rows, chans, cols,
+                     dtype=np.float32, storage: str = "bf16") -> dict:
+    """Selected entries of fp8_dense_step at full workload size (metas updated
+    in place).  The whole forward, the output gradient and the pre-activation
+    gradient are computed on the codes; then only sampled token rows (dN, dx),
+    FFN channels (the weight-gradient slices of those channels, the
+    activation) and hidden columns (the norm-weight gradient, which needs a
+    column of dN over all tokens), as oracle.sampled_step does for the bf16
+    step.  Products of decoded codes are summed in `dtype`; tests pin this
+    function to fp8_dense_step entry by entry on small shapes (in float64)."""
+    R = storage_rounding(storage)
+    rows, chans, cols = (np.asarray(v, dtype=np.int64) for v in (rows, chans, cols))
+    x = np.asarray(x, dtype=dtype)
+    p = p.astype(dtype)
+    dec = lambda c, m: decode(c, m.fmt).astype(dtype)
+    deq = lambda ma, mb: dtype(np.float32(ma.scale_inv()) * np.float32(mb.scale_inv()))
+    F = p.w_down.shape[1]
+    n, r = rms_norm_fwd(x, p.norm_w, eps)
+    n = R(n.astype(dtype)).astype(dtype)
+    nq = _cast_rows(n, metas["normed"])
+    wrows = _w_in_rows(p.w_in, act)
+    wq = _cast_rows(wrows, metas["w_in"])
+    Wq = dec(wq, metas["w_in"])                                   # [P, H]
+    h = (dec(nq, metas["normed"]) @ Wq.T) * deq(metas["normed"], metas["w_in"])
+    if act == "swiglu":
+        g, u = R(h[:, :F]).astype(dtype), R(h[:, F:]).astype(dtype)
+        a = R(silu(g) * u).astype(dtype)
+        pre = (g, u)
+    else:
+        hh = R(h + p.b_in[None, :]).astype(dtype)
+        a = R(gelu(hh)).astype(dtype)
+        pre = (hh,)
+    del h
+    aq = _cast_rows(a, metas["act"])
+    wdq = _cast_rows(p.w_down, metas["w_down"])
+    Wd = dec(wdq, metas["w_down"])                                # [H, F]
+    Aq = dec(aq, metas["act"])
+    out = R(x + (Aq @ Wd.T) * deq(metas["act"], metas["w_down"]) + p.b_down[None, :]).astype(dtype)
+    res = {"out": out, "act_chans": a[:, chans]}
+    dY = out
+    res["d_b_down"] = np.sum(dY, axis=0, dtype=np.float64)
+    dyq = _cast_rows(dY, metas["d_out"])
+    DY = dec(dyq, metas["d_out"])
+    da = (DY @ Wd) * deq(metas["d_out"], metas["w_down"])
+    dP = _act_bwd(da, pre, act, lambda v: R(np.asarray(v, dtype=dtype)).astype(dtype))
+    del da, pre
+    if act == "gelu":
+        res["d_b_in"] = np.sum(dP, axis=0, dtype=np.float64)
+    dpq = _cast_rows(dP, metas["d_pre"])
+    DP = dec(dpq, metas["d_pre"])
+    k_in = deq(metas["d_pre"], metas["w_in"])
+    # row-local quantities
+    res["dN_rows"] = (DP[rows] @ Wq) * k_in
+    dxn, _ = rms_norm_bwd(res["dN_rows"], x[rows], r[rows], p.norm_w)
+    res["dx_rows"] = R(dY[rows] + dxn)
+    # channel-sampled weight gradients (SwiGLU: the gate and the up row of each channel)
+    res["d_w_down_chans"] = (DY.T @ Aq[:, chans]) * deq(metas["d_out"], metas["act"])
+    sel = np.concatenate([chans, F + chans]) if act == "swiglu" else chans
+    dwin = (DP[:, sel].T @ dec(nq, metas["normed"])) * deq(metas["d_pre"], metas["normed"])
+    res["d_w_in_chans"] = dwin.reshape(2, len(chans), -1) if act == "swiglu" else dwin
+    # column-sampled norm-weight gradient: dN[:, cols] over all tokens
+    dN_cols = (DP @ Wq[:, cols]) * k_in
+    res["d_norm_w_cols"] = np.sum(dN_cols * x[:, cols] * r[:, None], axis=0)
+    # SGD on the sampled entries
+    res["new_norm_w_cols"] = R(p.norm_w[cols] - lr * res["d_norm_w_cols"])
+    res["new_b_down"] = R(p.b_down - lr * res["d_b_down"])
+    res["new_w_down_chans"] = R(p.w_down[:, chans] - lr * res["d_w_down_chans"])
+    if act == "swiglu":
+        res["new_w_in_chans"] = R(p.w_in[:, chans, :] - lr * res["d_w_in_chans"])
+    else:
+        res["new_w_in_chans"] = R(p.w_in[chans, :] - lr * res["d_w_in_chans"])
+        res["new_b_in"] = R(p.b_in - lr * res["d_b_in"])
+    for m in metas.values():
+        m.update()
+    return res

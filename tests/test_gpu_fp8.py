@@ -432,3 +432,45 @@ def test_fp8_step_small_parity(case):
             assert abs(h[0] - m.history[0]) <= 2e-2 * abs(m.history[0]), (k, h[0], m.history[0])
             assert sc == np.float32(m.fmt.max / float(h.max())), k
             assert si == np.float32(1.0 / sc), k
+
+
+def test_fp8_full_size_sampled():
+    """The Llama-3-8B TP=8 workload in the configuration bench.py times
+    (Fp8Step, out-of-place SGD): a cold step, then a warm step from the
+    oracle's metas after the first, each against oracle.fp8_sampled_step on
+    the whole output and sampled rows / FFN channels / hidden columns, by the
+    step criterion."""
+    import time
+    from tensor_transformer_mlp_rmsnorm_amd.step import Fp8Step
+    from test_gpu_parity import _gather, _sample
+    w = synth.workload("llama3_8b_tp8")
+    t = synth.draw(w)
+    Lh = 16
+    say(f"[gpu] fp8 full size {w.name} T={w.tokens} H={w.hidden} F_full={w.ffn_full} S={w.shards}")
+    st = Fp8Step(w, t, out_of_place_sgd=True, history_len=Lh)
+    rng = np.random.default_rng(w.seed + 7)
+    rows = _sample(rng, w.tokens, 32, must=[0, w.tokens - 1])
+    chans = _sample(rng, w.ffn_full, 32, must=[0, w.ffn_full - 1, w.ffn_local - 1, w.ffn_local])
+    cols = _sample(rng, w.hidden, 32, must=[0, w.hidden - 1])
+    om = fp8.new_metas(Lh)
+    x32, p = synth.to_numpy64(t["x"]).astype(np.float32), np_params(t)
+    for phase in ("cold", "warm"):
+        if phase == "warm":
+            st.load_meta_state(_state_of(om))
+        st.step()
+        torch.cuda.synchronize()
+        got = _gather(st, rows, chans, cols)
+        t0 = time.time()
+        ref = fp8.fp8_sampled_step(x32, p, w.act, w.eps, w.lr, om, rows, chans, cols, dtype=np.float32)
+        say(f"  {phase}: oracle sampled FP8 step {time.time() - t0:.1f} s")
+        report = {}
+        for k in ("out", "dx_rows", "dN_rows", "act_chans", "d_b_down", "d_norm_w_cols", "d_w_down_chans",
+                  "d_w_in_chans", "new_norm_w_cols", "new_b_down", "new_w_down_chans", "new_w_in_chans"):
+            check_fp8_step(k, got[k], ref[k], report=report)
+        say(f"  {phase} worst: {max(report.items(), key=lambda kv: kv[1])}")
+        gs = st.meta_state()
+        for k, m in om.items():
+            h = gs[k][3].numpy()
+            assert abs(h[0] - m.history[0]) <= 2e-2 * abs(m.history[0]), (k, h[0], m.history[0])
+    del st
+    torch.cuda.empty_cache()

@@ -122,11 +122,17 @@ def test_delayed_scaling_rule_worked_sequence():
     z.amax = np.float32(np.inf)
     z.update()
     assert z.scale == np.float32(57344.0 / 4.0)
-    # the amax is that of the values, not of the scaled values
+    # the amax is that of the values, not of the scaled values; NaN elements do not count, inf does
     w = fp8.Fp8Meta.new(E4M3, 1)
     w.scale = np.float32(64.0)
     fp8.cast(np.array([-3.0, 2.0]), w)
     assert w.amax == 3.0
+    w.record(np.array([np.nan, -5.0]))
+    assert w.amax == 5.0
+    w.record(np.array([np.nan]))
+    assert w.amax == 5.0
+    w.record(np.array([-np.inf]))
+    assert w.amax == np.inf
 
 
 @pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3)], ids=["e4m3xe4m3", "e5m2xe4m3"])
@@ -252,3 +258,31 @@ def test_metas_follow_the_step_amaxes_over_steps():
             if step == 0:
                 assert before[k] == 1.0
         p = r["new_params"]
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_sampled_step_is_the_dense_step(act):
+    x, p = _block(12, 40, 32, 24, act)
+    rows, chans, cols = [0, 7, 39], [0, 5, 23], [0, 9, 31]
+    for warm in (False, True):
+        md = _warm_metas(x, p, act) if warm else fp8.new_metas(4)
+        ms = fp8.copy_metas(md)
+        d = fp8.fp8_dense_step(x, p, act, 1e-6, 0.1, md)
+        s = fp8.fp8_sampled_step(x, p, act, 1e-6, 0.1, ms, rows, chans, cols, dtype=np.float64)
+        close = lambda a, b: np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)
+        close(s["out"], d["out"])
+        close(s["act_chans"], d["a"][:, chans])
+        close(s["d_b_down"], d["grads"]["b_down"])
+        close(s["dN_rows"], d["dN"][rows])
+        close(s["dx_rows"], d["dx"][rows])
+        close(s["d_w_down_chans"], d["grads"]["w_down"][:, chans])
+        wi = d["grads"]["w_in"]
+        close(s["d_w_in_chans"], wi[:, chans] if act == "swiglu" else wi[chans])
+        close(s["d_norm_w_cols"], d["grads"]["norm_w"][cols])
+        close(s["new_w_down_chans"], d["new_params"].w_down[:, chans])
+        close(s["new_norm_w_cols"], d["new_params"].norm_w[cols])
+        if act == "gelu":
+            close(s["d_b_in"], d["grads"]["b_in"])
+        for k in md:
+            assert md[k].scale == ms[k].scale
+            np.testing.assert_array_equal(md[k].history, ms[k].history)

@@ -28,13 +28,17 @@ import torch
 FP8_GEMM_REL = 2.0 ** -10
 # A whole FP8 step compares tensors that went through casts of computed
 # values: where the GPU's bf16 input to a cast differs by an ulp from the
-# oracle's (the block sums above), a rounding boundary can lie in between and
-# the code differs by a whole FP8 step (12.5% in E4M3, 25% in E5M2).  About
-# 0.1-0.6% of the codes of a step differ this way, so elementwise bounds do
-# not apply; the step is compared by the relative Frobenius error of each
-# tensor, which such flips keep below 1.7e-2 (measured) while a wrong operand,
-# index or scale moves it to O(1).
-FP8_STEP_FROB = 3e-2
+# oracle's (the block sums above put 1-5% of such inputs an ulp away), a
+# rounding boundary can lie in between and the code differs by a whole FP8
+# step (12.5% of the value in E4M3, 25% in E5M2).  A fraction p of flipped
+# codes gives a GEMM output a relative Frobenius error of about
+# sqrt(p) * 0.25; p <= 1% (0.1-0.6% measured) bounds it by 2.5%, and 2.4% was
+# the worst measured (the row-sampled dx of the Llama-3-8B TP=8 step).
+# Elementwise bounds do not apply to such tensors; each is compared by its
+# relative Frobenius error against twice that estimate, while a wrong operand,
+# index or scale moves it to O(1).  The kernels themselves are held to the
+# strict bounds above on inputs whose codes both sides share.
+FP8_STEP_FROB = 5e-2
 
 FP32_ATOL = 1e-5
 BF16_RTOL = 2e-2
