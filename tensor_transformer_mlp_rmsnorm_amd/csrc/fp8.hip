@@ -22,8 +22,8 @@
 namespace tpmlp {
 namespace {
 
-constexpr int kCastRows = 128, kCastCols = 64, kCastThreads = 256;
-constexpr int kPadT = 16;  // LDS row padding of the transposed tile (bytes)
+constexpr int kCastTile = 128, kCastThreads = 256;
+constexpr int kCastMaxBlocks = 2048;
 
 template <int FMT>
 __device__ __forceinline__ uint32_t cvt_pair(float a, float b) {
@@ -53,49 +53,88 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// One 128 x 64 tile of a bf16 [R, C] matrix: codes to out [R, C] (if ROW) and
-// to out_t [C, ldt] (if TRANS; columns R .. ldt-1 of out_t are written as 0
-// by the tiles of the last tile-row).  Thread t loads rows t/8 + 32 i, chunk t%8.
+// LDS code tile [128 rows][32 dwords]; dword d of row r is stored at d ^ 8 (r >> 6 & 1), so
+// that the column reads below (rows r and r + 64 in one instruction) fall in distinct banks.
+__device__ __forceinline__ int tile_dword(int r, int d) { return r * 32 + (d ^ (((r >> 6) & 1) << 3)); }
+
+// Codes of a bf16 [R, C] matrix, 128 x 128 tiles over a grid-stride loop:
+// out [R, C] (if ROW) and out_t [C, ldt] (if TRANS; the rows R .. ldt-1 of
+// the tiles give zero codes, so out_t's padding columns are written as 0).
+// Load: thread t takes rows t/8 + 32 i (i < 4) and the 16 columns 16 (t%8) ..;
+// transposed store: column t/2, rows 64 (t%2) .. + 63.  One atomic maximum
+// per workgroup folds the amax into meta[2].
 template <int FMT, bool ROW, bool TRANS>
 __global__ __launch_bounds__(kCastThreads) void cast_kernel(const bf16_t* __restrict__ x, int64_t R, int64_t C,
                                                             uint8_t* __restrict__ out, uint8_t* __restrict__ out_t,
-                                                            int64_t ldt, float* __restrict__ meta) {
-  __shared__ __align__(16) uint8_t tile_t[kCastCols][kCastRows + kPadT];  // codes, column-major
+                                                            int64_t ldt, int tiles_c, int tiles, float* __restrict__ meta) {
+  __shared__ uint32_t tile[kCastTile * 32];
+  __shared__ float red[kCastThreads / kWave];
   const int t = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * kCastRows, c0 = (int64_t)blockIdx.x * kCastCols;
   const float s = meta[0], lim = meta[3];
-  const int cc = (t & 7) * 8;
+  const int cq = (t & 7) * 16;  // first of this thread's 16 columns
   float amax = 0.0f;
+  for (int tid = blockIdx.x; tid < tiles; tid += gridDim.x) {
+    const int64_t r0 = (int64_t)(tid / tiles_c) * kCastTile, c0 = (int64_t)(tid % tiles_c) * kCastTile;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rr = (t >> 3) + 32 * i;
-    const int64_t r = r0 + rr, c = c0 + cc;
-    uint2 q = make_uint2(0u, 0u);  // rows past R give zero codes (the transposed padding)
-    if (r < R && c < C) {
-      const uint4 u = *reinterpret_cast<const uint4*>(x + r * C + c);
-      q = cast8<FMT>(u, s, lim, amax);
-      if constexpr (ROW) *reinterpret_cast<uint2*>(out + r * C + c) = q;
+    for (int i = 0; i < 4; ++i) {
+      const int rr = (t >> 3) + 32 * i;
+      const int64_t r = r0 + rr, c = c0 + cq;
+      uint2 q0 = make_uint2(0u, 0u), q1 = make_uint2(0u, 0u);  // past R or C: zero codes
+      if (r < R) {
+        const bf16_t* src = x + r * C + c;
+        if (c < C) q0 = cast8<FMT>(*reinterpret_cast<const uint4*>(src), s, lim, amax);
+        if (c + 8 < C) q1 = cast8<FMT>(*reinterpret_cast<const uint4*>(src + 8), s, lim, amax);
+        if constexpr (ROW) {
+          uint8_t* dst = out + r * C + c;  // 8-byte aligned (C is a multiple of 8); 16 when C is of 16
+          if (c + 8 < C && (C & 15) == 0) {
+            *reinterpret_cast<uint4*>(dst) = make_uint4(q0.x, q0.y, q1.x, q1.y);
+          } else {
+            if (c < C) *reinterpret_cast<uint2*>(dst) = q0;
+            if (c + 8 < C) *reinterpret_cast<uint2*>(dst + 8) = q1;
+          }
+        }
+      }
+      if constexpr (TRANS) {
+        const int d = cq >> 2;  // 4 dwords of codes
+        *reinterpret_cast<uint4*>(&tile[tile_dword(rr, d)]) = make_uint4(q0.x, q0.y, q1.x, q1.y);
+      }
     }
     if constexpr (TRANS) {
-      const uint32_t w[2] = {q.x, q.y};
+      __syncthreads();
+      const int col = t >> 1, seg = (t & 1) * 64;
+      const int64_t c = c0 + col;
+      if (c < C) {
+        const uint8_t* tb = reinterpret_cast<const uint8_t*>(tile);
+        const int dw = col >> 2, byte = col & 3;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tile_t[cc + e][rr] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
-    }
-  }
-  if constexpr (TRANS) {
-    __syncthreads();
-    // thread t: column t/4, rows (t%4)*32 .. +31 of the tile -> out_t row c0 + t/4
-    const int col = t >> 2, seg = (t & 3) * 32;
-    const int64_t c = c0 + col, r = r0 + seg;
-    if (c < C && r < ldt) {
-      const uint4* src = reinterpret_cast<const uint4*>(&tile_t[col][seg]);
-      uint4* dst = reinterpret_cast<uint4*>(out_t + c * ldt + r);
-      dst[0] = src[0];
-      if (r + 16 < ldt) dst[1] = src[1];
+        for (int j = 0; j < 4; ++j) {
+          const int64_t r = r0 + seg + 16 * j;
+          uint32_t w[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const int rr = seg + 16 * j + 4 * k + b;
+              v |= (uint32_t)tb[tile_dword(rr, dw) * 4 + byte] << (8 * b);
+            }
+            w[k] = v;
+          }
+          if (r < ldt) *reinterpret_cast<uint4*>(out_t + c * ldt + r) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+      __syncthreads();  // the tile is rewritten by the next iteration
     }
   }
   amax = wave_max(amax);
-  if ((t & 63) == 0 && amax > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(meta + 2), __float_as_uint(amax));
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  if (t == 0) {
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < kCastThreads / kWave; ++w) m = fmaxf(m, red[w]);
+    if (m > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(meta + 2), __float_as_uint(m));
+  }
 }
 
 // End of step for each meta: history push, amax cleared, new scale.
@@ -160,8 +199,11 @@ template <int FMT, bool ROW, bool TRANS>
 hipError_t launch_cast_t(const bf16_t* x, int64_t R, int64_t C, uint8_t* out, uint8_t* out_t, int64_t ldt,
                          float* meta, hipStream_t s) {
   const int64_t rows = TRANS ? (R > ldt ? R : ldt) : R;  // the transposed padding needs its tile-rows too
-  const dim3 grid((unsigned)((C + kCastCols - 1) / kCastCols), (unsigned)((rows + kCastRows - 1) / kCastRows));
-  hipLaunchKernelGGL((cast_kernel<FMT, ROW, TRANS>), grid, dim3(kCastThreads), 0, s, x, R, C, out, out_t, ldt, meta);
+  const int64_t tc = (C + kCastTile - 1) / kCastTile, tr = (rows + kCastTile - 1) / kCastTile;
+  const int64_t tiles = tc * tr;
+  const int blocks = (int)(tiles < kCastMaxBlocks ? tiles : kCastMaxBlocks);
+  hipLaunchKernelGGL((cast_kernel<FMT, ROW, TRANS>), dim3(blocks), dim3(kCastThreads), 0, s, x, R, C, out, out_t, ldt,
+                     (int)tc, (int)tiles, meta);
   return hipGetLastError();
 }
 
