@@ -56,3 +56,12 @@ from .fp8 import (  # noqa: F401,E402
     fp8_sharded_step,
     new_metas as fp8_new_metas,
 )
+from .attention import (  # noqa: F401,E402
+    ATTN_MODES,
+    AttnParams,
+    AttnShape,
+    attn_dense_step,
+    attn_sharded_step,
+    causal_attention_fwd,
+    causal_attention_bwd,
+)
