@@ -441,6 +441,104 @@ int tp_mlp_backward_fp8(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_ar
                         const tp_mlp_fp8_args* f8, void* stream);
 
 /*
+ * The attention sublayer of one tensor-parallel rank, the same pattern as the
+ * MLP block ("Megatron-LM walkthrough", Part IV, Stages 5-6 and Part V, "Deep
+ * dive: tensor parallelism and the f and g operators": the QKV projection is
+ * column-parallel, so each rank computes Q, K and V of its own heads; attention
+ * runs locally per head; the output projection is row-parallel and its partial
+ * is summed across the ranks; in backward the gradient of the QKV input is
+ * summed).  Ranks own complete grouped-query head groups ("Megatron
+ * tensor-parallel MLP", closing section).  With the pages silent on the
+ * attention itself, it is:
+ *     N   = rms_norm(x, norm_w)                   (as in tp_mlp_forward)
+ *     QKV = N W_qkv^T                             (no bias), columns [Q heads | K heads | V heads]
+ *     o_h = softmax_causal(q_h k_g^T / sqrt(D)) v_g,   g = h / (n_q / n_kv)
+ *     out = x + O W_o^T + b_o                     (b_o once, after the partial sum)
+ * x is [batch, seq, H] flattened to T = batch * seq rows (a sequence's rows
+ * contiguous); causal means key position <= query position within a sequence.
+ * bf16 only (fp32 accumulation).  D (head_dim) is 64 or 128.
+ */
+typedef struct {
+  int64_t batch;     /* sequences */
+  int64_t seq;       /* positions per sequence (T = batch * seq) */
+  int64_t hidden;    /* H: positive multiple of 8, <= 16384 */
+  int32_t n_q;       /* query heads of this rank */
+  int32_t n_kv;      /* key/value heads of this rank; n_q a multiple of it */
+  int32_t head_dim;  /* D: 64 or 128 */
+  int32_t dtype;     /* TP_MLP_BF16 */
+  float eps;         /* RMSNorm epsilon */
+  int32_t flags;     /* TP_MLP_FUSE_EPILOGUE | TP_MLP_NORMED_READY | TP_MLP_ACCUMULATE_GRADS */
+} tp_attn_desc;
+
+/*
+ * tp_attn_forward - one rank's attention forward.  W = (n_q + 2 n_kv) D.
+ *   x [T, H], norm_w [H], w_qkv [W, H] (rows: this rank's Q heads, then K heads,
+ *   then V heads, D rows each), w_o [H, n_q D] (this rank's columns), bf16;
+ *   normed [T, H] bf16 and rstd [T] fp32 out (in, with NORMED_READY);
+ *   qkv [T, W] bf16 out; attn_out [T, n_q D] bf16 out (O); lse [n_q, T] fp32
+ *   out (log of each row's softmax denominator, for the backward);
+ *   out: without FUSE_EPILOGUE [T, H] fp32, this rank's partial O W_o^T; with
+ *   it [T, H] bf16 x + O W_o^T + b_o (b_o [H] bf16, read only then).
+ */
+int tp_attn_forward(const tp_attn_desc* d, const void* x, const void* norm_w, const void* w_qkv, const void* w_o,
+                    void* normed, float* rstd, void* qkv, void* attn_out, float* lse, void* out, const void* b_o,
+                    void* stream);
+
+typedef struct {
+  /* saved from tp_attn_forward */
+  const void* x;           /* [T, H] */
+  const void* normed;      /* [T, H] */
+  const float* rstd;       /* [T] */
+  const void* qkv;         /* [T, W] */
+  const void* attn_out;    /* [T, n_q D] */
+  const float* lse;        /* [n_q, T] */
+  /* parameters */
+  const void* norm_w;      /* [H] */
+  const void* w_qkv;       /* [W, H] */
+  const void* w_o;         /* [H, n_q D] */
+  const void* d_out;       /* [T, H] bf16: gradient of the sublayer output (= out for the loss sum(out^2)/2) */
+  /* SHARD phase outputs */
+  void* d_attn_out;        /* [T, n_q D] bf16: dO = d_out W_o */
+  void* d_qkv;             /* [T, W] bf16 */
+  float* d_w_qkv;          /* [W, H] fp32 */
+  float* d_w_o;            /* [H, n_q D] fp32 */
+  float* d_normed_part;    /* [T, H] fp32: this rank's partial of dL/dN */
+  /* NORM phase */
+  const float* d_normed;   /* [T, H] fp32: summed over ranks */
+  void* d_x;               /* [T, H] bf16 */
+  float* d_norm_w;         /* [H] fp32 */
+  float* d_b_o;            /* [H] fp32 */
+  void* workspace;
+  size_t workspace_bytes;
+} tp_attn_bwd_args;
+
+/*
+ * tp_attn_backward - the backward of tp_attn_forward in the two phases of
+ * tp_mlp_backward.  SHARD: dO = d_out W_o; d_w_o = d_out^T O; the attention
+ * backward (dS = P (dP - rowsum(dO o O)), P recomputed from lse) gives
+ * d_qkv; d_w_qkv = d_qkv^T N; d_normed_part = d_qkv W_qkv.  NORM: RMSNorm's
+ * backward with the residual, d_norm_w and d_b_o = sum_t d_out.
+ * Workspace: tp_attn_workspace_bytes(d, phase).  Deterministic.
+ */
+int tp_attn_backward(const tp_attn_desc* d, int32_t phase, const tp_attn_bwd_args* a, void* stream);
+size_t tp_attn_workspace_bytes(const tp_attn_desc* d, int32_t phase);
+
+/*
+ * tp_attention_forward / tp_attention_backward - the causal grouped-query
+ * attention on its own (the kernels tp_attn_* run between the projections).
+ *   qkv [batch seq, ld] bf16 with the Q, K, V head columns at 0, n_q D and
+ *   (n_q + n_kv) D (ld >= (n_q + 2 n_kv) D, a multiple of 8); o and d_o
+ *   [batch seq, n_q D] bf16; lse [n_q, batch seq] fp32; d_qkv [batch seq, ld]
+ *   bf16 (its first (n_q + 2 n_kv) D columns written); delta: DEVICE fp32
+ *   scratch of n_q batch seq elements.  head_dim 64 or 128.
+ */
+int tp_attention_forward(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv, int32_t head_dim, const void* qkv,
+                         int64_t ld, void* o, float* lse, void* stream);
+int tp_attention_backward(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv, int32_t head_dim, const void* qkv,
+                          int64_t ld, const void* o, const void* d_o, const float* lse, float* delta, void* d_qkv,
+                          void* stream);
+
+/*
  * Kernel timing, a measurement aid (off by default).  While enabled, every
  * kernel the library launches is bracketed by two hipEvents recorded on the
  * launch's own stream; durations are aggregated per kernel name.

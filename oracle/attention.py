@@ -122,13 +122,13 @@ def causal_attention_fwd(q, k, v, group: int):
     lse = np.zeros((b, nq, s), dtype=q.dtype)
     for h in range(nq):
         g = h // group
-        sc = np.einsum("bid,bjd->bij", q[:, h], k[:, g]) * scale
+        sc = (q[:, h] @ k[:, g].transpose(0, 2, 1)) * scale          # [b, s, s]: s_ij = q_i . k_j / sqrt(d)
         sc = np.where(mask[None], sc, -np.inf)
         m = np.max(sc, axis=-1, keepdims=True)
         e = np.exp(sc - m)
         den = np.sum(e, axis=-1, keepdims=True)
         p = e / den
-        o[:, h] = np.einsum("bij,bjd->bid", p, v[:, g])
+        o[:, h] = p @ v[:, g]
         lse[:, h] = (m + np.log(den))[..., 0]
     return o, lse
 
@@ -144,16 +144,16 @@ def causal_attention_bwd(q, k, v, o, do, group: int):
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     for h in range(nq):
         g = h // group
-        sc = np.einsum("bid,bjd->bij", q[:, h], k[:, g]) * scale
+        sc = (q[:, h] @ k[:, g].transpose(0, 2, 1)) * scale
         sc = np.where(mask[None], sc, -np.inf)
         p = np.exp(sc - np.max(sc, axis=-1, keepdims=True))
         p = p / np.sum(p, axis=-1, keepdims=True)
-        dv[:, g] += np.einsum("bij,bid->bjd", p, do[:, h])
-        dp = np.einsum("bid,bjd->bij", do[:, h], v[:, g])
+        dv[:, g] += p.transpose(0, 2, 1) @ do[:, h]
+        dp = do[:, h] @ v[:, g].transpose(0, 2, 1)
         delta = np.sum(do[:, h] * o[:, h], axis=-1, keepdims=True)
         ds = p * (dp - delta)
-        dq[:, h] = np.einsum("bij,bjd->bid", ds, k[:, g]) * scale
-        dk[:, g] += np.einsum("bij,bid->bjd", ds, q[:, h]) * scale
+        dq[:, h] = (ds @ k[:, g]) * scale
+        dk[:, g] += (ds.transpose(0, 2, 1) @ q[:, h]) * scale
     return dq, dk, dv
 
 
@@ -187,7 +187,7 @@ def attn_dense_step(x, p: AttnParams, sh: AttnShape, eps: float, lr: float, dtyp
     dxn, g["norm_w"] = rms_norm_bwd(dN, x, r, p.norm_w)
     dx = R(dY + dxn)
     return dict(x=x, n=n, rstd=r, qkv=qkv, O=O, lse=lse, z=z, out=out, loss=0.5 * float(np.sum(out * out)), dY=dY,
-                dO=dO, dqkv=dqkv, dN=dN, dx=dx, grads=g, params=p, new_params=_sgd(p, g, lr, R))
+                dO=dO, dqkv=dqkv, dN=dN, dx=dx, grads=g, params=p, new_params=_sgd(p, g, lr, R), lr=lr)
 
 
 def shard_heads(sh: AttnShape, r: int, shards: int):

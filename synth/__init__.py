@@ -38,7 +38,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "workload", "draw", "shard_slices", "small_workload"]
+__all__ = ["Workload", "WORKLOADS", "workload", "draw", "shard_slices", "small_workload", "AttnWorkload",
+           "ATTN_WORKLOADS", "attn_workload", "draw_attn"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -171,3 +172,74 @@ def to_numpy64(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
     if t is None:
         return None
     return t.detach().to(torch.float64).cpu().numpy()
+
+
+# ---------------------------------------------------------------- attention
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """The attention sublayer: x [batch, seq, H] flattened to [T, H]; n_q
+    query heads and n_kv key/value heads of width d over S tensor-parallel
+    shards (each shard: complete query/KV groups)."""
+    name: str
+    batch: int
+    seq: int
+    hidden: int
+    n_q: int
+    n_kv: int
+    d: int
+    shards: int
+    w_std: float
+    seed: int
+    lr: float = 0.1
+    eps: float = 1e-6
+    dtype: str = "bf16"
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seq
+
+    @property
+    def flops_per_step(self) -> int:
+        """Algorithmic flops of one step over all shards: the four projections
+        (forward and backward, 6 flops per weight per token) plus causal
+        attention (forward 2 matmuls, backward 4, each over the s(s+1)/2
+        query-key pairs of a sequence)."""
+        T, H, D = self.tokens, self.hidden, self.d
+        W = (self.n_q + 2 * self.n_kv) * D
+        proj = 6 * T * H * (W + self.n_q * D)
+        pairs = self.batch * self.seq * (self.seq + 1) // 2
+        attn = 6 * 2 * pairs * D * self.n_q
+        return proj + attn
+
+
+ATTN_WORKLOADS = {
+    "attn_llama3_8b_tp8": AttnWorkload("attn_llama3_8b_tp8", batch=2, seq=4096, hidden=4096, n_q=32, n_kv=8, d=128,
+                                       shards=8, w_std=0.02, seed=12),
+    "attn_gpt2s_tp1": AttnWorkload("attn_gpt2s_tp1", batch=4, seq=1024, hidden=768, n_q=12, n_kv=12, d=64, shards=1,
+                                   w_std=0.02, seed=11),
+}
+
+
+def attn_workload(name: str) -> AttnWorkload:
+    return ATTN_WORKLOADS[name]
+
+
+def draw_attn(w: AttnWorkload, perturb: bool = False) -> dict:
+    """Dense tensors of an attention workload (CPU torch tensors, storage dtype):
+    x [T, H] ~ N(0,1); w_qkv [(n_q + 2 n_kv) d, H] ~ N(0, std) (rows: Q heads,
+    K heads, V heads); w_o [H, n_q d] ~ N(0, std); norm_w = 1, b_o = 0, then
+    (perturb) norm_w += 0.1 N(0,1), b_o = 0.1 N(0,1).  Drawn in that order."""
+    g = torch.Generator().manual_seed(w.seed)
+    T, H, D = w.tokens, w.hidden, w.d
+    x = torch.randn(T, H, generator=g, dtype=torch.float32)
+    w_qkv = torch.randn((w.n_q + 2 * w.n_kv) * D, H, generator=g, dtype=torch.float32) * w.w_std
+    w_o = torch.randn(H, w.n_q * D, generator=g, dtype=torch.float32) * w.w_std
+    norm_w = torch.ones(H, dtype=torch.float32)
+    b_o = torch.zeros(H, dtype=torch.float32)
+    if perturb:
+        norm_w += 0.1 * torch.randn(H, generator=g, dtype=torch.float32)
+        b_o = 0.1 * torch.randn(H, generator=g, dtype=torch.float32)
+    out = dict(x=x, norm_w=norm_w, w_qkv=w_qkv, w_o=w_o, b_o=b_o)
+    return {k: _round(v, w.dtype) for k, v in out.items()}
+

@@ -35,7 +35,8 @@ EXPORTED = ("tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_works
             "tp_mlp_profile_count", "tp_mlp_profile_entry", "tp_mlp_sgd_step_multi", "tp_mlp_adamw_step_multi",
             "tp_mlp_clip_grad_norm", "tp_mlp_clip_grad_norm_workspace_bytes", "tp_rmsnorm_forward",
             "tp_mlp_fp8_meta_init", "tp_mlp_fp8_cast", "tp_mlp_fp8_update_scales", "tp_mlp_forward_fp8",
-            "tp_mlp_backward_fp8", "tp_mlp_fp8_gemm", "tp_mlp_fp8_gemm_workspace_bytes")
+            "tp_mlp_backward_fp8", "tp_mlp_fp8_gemm", "tp_mlp_fp8_gemm_workspace_bytes", "tp_attn_forward",
+            "tp_attn_backward", "tp_attn_workspace_bytes", "tp_attention_forward", "tp_attention_backward")
 
 
 class TPMLPError(RuntimeError):
@@ -82,6 +83,18 @@ FP8_CODE_FIELDS = ("normed_q", "normed_t", "w_in_q", "w_in_t", "act_q", "act_t",
 
 class tp_mlp_fp8_args(ctypes.Structure):
     _fields_ = [("history_len", ctypes.c_int32)] + [(n, _vp) for n in FP8_META_FIELDS + FP8_CODE_FIELDS]
+
+
+class tp_attn_desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("eps", ctypes.c_float), ("flags", ctypes.c_int32)]
+
+
+class tp_attn_bwd_args(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("x", "normed", "rstd", "qkv", "attn_out", "lse", "norm_w", "w_qkv", "w_o", "d_out",
+                                   "d_attn_out", "d_qkv", "d_w_qkv", "d_w_o", "d_normed_part", "d_normed", "d_x",
+                                   "d_norm_w", "d_b_o", "workspace")] + [("workspace_bytes", ctypes.c_size_t)]
 
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -140,6 +153,19 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_fp8_gemm.restype = ctypes.c_int
         L.tp_mlp_fp8_gemm_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
         L.tp_mlp_fp8_gemm_workspace_bytes.restype = ctypes.c_size_t
+        L.tp_attn_forward.argtypes = [ctypes.POINTER(tp_attn_desc)] + [_vp] * 12
+        L.tp_attn_forward.restype = ctypes.c_int
+        L.tp_attn_backward.argtypes = [ctypes.POINTER(tp_attn_desc), ctypes.c_int32, ctypes.POINTER(tp_attn_bwd_args),
+                                       _vp]
+        L.tp_attn_backward.restype = ctypes.c_int
+        L.tp_attn_workspace_bytes.argtypes = [ctypes.POINTER(tp_attn_desc), ctypes.c_int32]
+        L.tp_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.tp_attention_forward.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, _vp, ctypes.c_int64, _vp, _vp, _vp]
+        L.tp_attention_forward.restype = ctypes.c_int
+        L.tp_attention_backward.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, _vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.tp_attention_backward.restype = ctypes.c_int
         L.tp_mlp_last_error.argtypes = []
         L.tp_mlp_last_error.restype = ctypes.c_char_p
         L.tp_mlp_version.argtypes = []
@@ -275,6 +301,49 @@ def tp_mlp_fp8_gemm(M: int, N: int, K: int, A, lda: int, fmt_a: int, scale_inv_a
     _check(lib().tp_mlp_fp8_gemm(M, N, K, _ptr(A), lda, fmt_a, _ptr(scale_inv_a), _ptr(B), ldb, fmt_b,
                                  _ptr(scale_inv_b), _ptr(C), ldc, 1 if accumulate else 0, _ptr(workspace), nbytes,
                                  _stream(stream)))
+
+
+def make_attn_desc(batch: int, seq: int, hidden: int, n_q: int, n_kv: int, head_dim: int, eps: float,
+                   flags: int = 0, dtype: int = BF16) -> tp_attn_desc:
+    return tp_attn_desc(batch, seq, hidden, n_q, n_kv, head_dim, dtype, eps, flags)
+
+
+def tp_attn_forward(desc: tp_attn_desc, x, norm_w, w_qkv, w_o, normed, rstd, qkv, attn_out, lse, out, b_o=None,
+                    stream=None) -> None:
+    _check(lib().tp_attn_forward(ctypes.byref(desc), _ptr(x), _ptr(norm_w), _ptr(w_qkv), _ptr(w_o), _ptr(normed),
+                                 _ptr(rstd), _ptr(qkv), _ptr(attn_out), _ptr(lse), _ptr(out), _ptr(b_o),
+                                 _stream(stream)))
+
+
+def tp_attn_workspace_bytes(desc: tp_attn_desc, phase: int) -> int:
+    return int(lib().tp_attn_workspace_bytes(ctypes.byref(desc), phase))
+
+
+def tp_attn_backward(desc: tp_attn_desc, phase: int, stream=None, **tensors) -> None:
+    """``tensors``: the fields of tp_attn_bwd_args (torch tensors or None)."""
+    a = tp_attn_bwd_args()
+    for name, _ in tp_attn_bwd_args._fields_:
+        if name == "workspace_bytes":
+            continue
+        v = tensors.pop(name, None)
+        setattr(a, name, _ptr(v))
+        if name == "workspace" and v is not None and not isinstance(v, int):
+            a.workspace_bytes = v.numel() * v.element_size()
+    if tensors:
+        raise TypeError(f"unknown attention backward arguments: {sorted(tensors)}")
+    _check(lib().tp_attn_backward(ctypes.byref(desc), phase, ctypes.byref(a), _stream(stream)))
+
+
+def tp_attention_forward(batch: int, seq: int, n_q: int, n_kv: int, head_dim: int, qkv, ld: int, o, lse,
+                         stream=None) -> None:
+    _check(lib().tp_attention_forward(batch, seq, n_q, n_kv, head_dim, _ptr(qkv), ld, _ptr(o), _ptr(lse),
+                                      _stream(stream)))
+
+
+def tp_attention_backward(batch: int, seq: int, n_q: int, n_kv: int, head_dim: int, qkv, ld: int, o, d_o, lse,
+                          delta, d_qkv, stream=None) -> None:
+    _check(lib().tp_attention_backward(batch, seq, n_q, n_kv, head_dim, _ptr(qkv), ld, _ptr(o), _ptr(d_o), _ptr(lse),
+                                       _ptr(delta), _ptr(d_qkv), _stream(stream)))
 
 
 def tp_mlp_sgd_step(param_in, param_out, grad, master_in, master_out, n: int, param_dtype: int, lr: float,

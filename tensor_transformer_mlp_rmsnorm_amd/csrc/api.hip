@@ -805,4 +805,277 @@ int tp_mlp_backward_fp8(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_ar
   return TP_MLP_OK;
 }
 
+// ------------------------------------------------------------- attention
+
+namespace {
+
+int check_attn_shape(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv, int32_t head_dim, const char* fn) {
+  if (batch < 0 || seq < 0) return fail(TP_MLP_EINVAL, "%s: batch and seq must be >= 0", fn);
+  if (head_dim != 64 && head_dim != 128) return fail(TP_MLP_ESHAPE, "%s: head_dim must be 64 or 128", fn);
+  if (n_q <= 0 || n_kv <= 0 || n_q % n_kv) return fail(TP_MLP_ESHAPE, "%s: n_q must be a positive multiple of n_kv", fn);
+  if (seq > (1 << 24) || batch > (1 << 24)) return fail(TP_MLP_ESHAPE, "%s: batch or seq too large", fn);
+  return TP_MLP_OK;
+}
+
+int check_attn_desc(const tp_attn_desc* d, const char* fn) {
+  if (!d) return fail(TP_MLP_EINVAL, "%s: descriptor is NULL", fn);
+  int rc = check_attn_shape(d->batch, d->seq, d->n_q, d->n_kv, d->head_dim, fn);
+  if (rc) return rc;
+  if (d->hidden <= 0 || d->hidden % 8 || d->hidden > 16384)
+    return fail(TP_MLP_ESHAPE, "%s: hidden must be a positive multiple of 8, <= 16384", fn);
+  if (d->dtype != TP_MLP_BF16) return fail(TP_MLP_EDTYPE, "%s: the attention sublayer takes bf16 tensors", fn);
+  if (d->flags & ~(TP_MLP_FUSE_EPILOGUE | TP_MLP_NORMED_READY | TP_MLP_ACCUMULATE_GRADS))
+    return fail(TP_MLP_EINVAL, "%s: unknown flags", fn);
+  if (!(d->eps >= 0.0f)) return fail(TP_MLP_EINVAL, "%s: eps must be >= 0", fn);
+  const int64_t T = d->batch * d->seq, H = d->hidden;
+  const int64_t W = (int64_t)(d->n_q + 2 * d->n_kv) * d->head_dim, Wo = (int64_t)d->n_q * d->head_dim;
+  const int64_t lim = (int64_t)1 << 30;
+  if (T * H >= lim || T * W >= lim || W * H >= lim || T * Wo >= lim || (int64_t)d->n_q * T >= lim)
+    return fail(TP_MLP_ESHAPE, "%s: a tensor would hold 2^30 or more elements", fn);
+  return TP_MLP_OK;
+}
+
+AttnShapeArgs attn_args(const tp_attn_desc* d) {
+  AttnShapeArgs a;
+  a.batch = d->batch;
+  a.seq = d->seq;
+  a.ld = (int64_t)(d->n_q + 2 * d->n_kv) * d->head_dim;
+  a.n_q = d->n_q;
+  a.n_kv = d->n_kv;
+  a.head_dim = d->head_dim;
+  return a;
+}
+
+// Workspace of the SHARD phase: the k-split slices of the two weight-gradient
+// GEMMs (they run one after the other and share them), then delta [n_q, T].
+size_t attn_ksplit_bytes(const tp_attn_desc* d) {
+  const int64_t T = d->batch * d->seq, H = d->hidden;
+  const int64_t W = (int64_t)(d->n_q + 2 * d->n_kv) * d->head_dim, Wo = (int64_t)d->n_q * d->head_dim;
+  const size_t a = gemm_ksplit_workspace(H, Wo, T), b = gemm_ksplit_workspace(W, H, T);
+  return ((a > b ? a : b) + 255) / 256 * 256;
+}
+
+}  // namespace
+
+size_t tp_attn_workspace_bytes(const tp_attn_desc* d, int32_t phase) {
+  if (!d || d->batch < 0 || d->seq < 0 || d->hidden <= 0 || d->n_q <= 0) return 0;
+  const int64_t T = d->batch * d->seq;
+  if (phase == TP_MLP_BWD_NORM) return rmsnorm_bwd_workspace(T, d->hidden);
+  if (phase != TP_MLP_BWD_SHARD) return 0;
+  return attn_ksplit_bytes(d) + (size_t)d->n_q * (size_t)T * sizeof(float);
+}
+
+int tp_attn_forward(const tp_attn_desc* d, const void* x, const void* norm_w, const void* w_qkv, const void* w_o,
+                    void* normed, float* rstd, void* qkv, void* attn_out, float* lse, void* out, const void* b_o,
+                    void* stream) {
+  const char* fn = "tp_attn_forward";
+  g_err[0] = 0;
+  int rc = check_attn_desc(d, fn);
+  if (rc) return rc;
+  const int64_t T = d->batch * d->seq, H = d->hidden;
+  const int64_t W = (int64_t)(d->n_q + 2 * d->n_kv) * d->head_dim, Wo = (int64_t)d->n_q * d->head_dim;
+  const bool fuse = d->flags & TP_MLP_FUSE_EPILOGUE;
+  REQUIRE_PTR(norm_w);
+  REQUIRE_PTR(w_qkv);
+  REQUIRE_PTR(w_o);
+  if (fuse) REQUIRE_PTR(b_o);
+  if (T == 0) return TP_MLP_OK;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(normed);
+  REQUIRE_PTR4(rstd);
+  REQUIRE_PTR(qkv);
+  REQUIRE_PTR(attn_out);
+  REQUIRE_PTR4(lse);
+  REQUIRE_PTR(out);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!(d->flags & TP_MLP_NORMED_READY))
+    CHECK_HIP(launch_rmsnorm_fwd(kBF16, x, norm_w, normed, rstd, T, H, d->eps, s), "rmsnorm forward");
+  GemmArgs g{};
+  g.M = T;
+  g.N = W;
+  g.K = H;
+  g.A = normed;
+  g.lda = H;
+  g.B = w_qkv;
+  g.ldb = H;
+  g.C = qkv;
+  g.ldc = W;
+  g.tag = "gemm_qkv";
+  CHECK_HIP(launch_gemm_bf16(true, true, kEpiStoreBf16, g, s), "QKV GEMM");
+  const AttnShapeArgs a = attn_args(d);
+  CHECK_HIP(launch_attention_fwd(a, qkv, attn_out, lse, s), "attention");
+  GemmArgs c{};
+  c.M = T;
+  c.N = H;
+  c.K = Wo;
+  c.A = attn_out;
+  c.lda = Wo;
+  c.B = w_o;
+  c.ldb = Wo;
+  c.C = out;
+  c.ldc = H;
+  c.aux = x;
+  c.bias = b_o;
+  c.tag = fuse ? "gemm_out_proj_residual" : "gemm_out_proj_partial";
+  CHECK_HIP(launch_gemm_bf16(true, true, fuse ? kEpiResidual : kEpiStoreF32, c, s), "output projection");
+  return TP_MLP_OK;
+}
+
+int tp_attn_backward(const tp_attn_desc* d, int32_t phase, const tp_attn_bwd_args* a, void* stream) {
+  const char* fn = "tp_attn_backward";
+  g_err[0] = 0;
+  int rc = check_attn_desc(d, fn);
+  if (rc) return rc;
+  if (!a) return fail(TP_MLP_EINVAL, "%s: args is NULL", fn);
+  if (phase != TP_MLP_BWD_SHARD && phase != TP_MLP_BWD_NORM) return fail(TP_MLP_EINVAL, "%s: unknown phase", fn);
+  const int64_t T = d->batch * d->seq, H = d->hidden;
+  const int64_t W = (int64_t)(d->n_q + 2 * d->n_kv) * d->head_dim, Wo = (int64_t)d->n_q * d->head_dim;
+  const bool accum = (d->flags & TP_MLP_ACCUMULATE_GRADS) != 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t need = tp_attn_workspace_bytes(d, phase);
+  if (need > 0) {
+    if (!a->workspace || a->workspace_bytes < need)
+      return fail(TP_MLP_EWORKSPACE, "%s: workspace of %zu bytes required, %zu given", fn, need,
+                  a->workspace ? a->workspace_bytes : (size_t)0);
+    if (!aligned16(a->workspace)) return fail(TP_MLP_EALIGN, "%s: workspace is not 16-byte aligned", fn);
+  }
+  if (phase == TP_MLP_BWD_NORM) {
+    REQUIRE_PTR(a->norm_w);
+    REQUIRE_PTR(a->d_norm_w);
+    REQUIRE_PTR(a->d_b_o);
+    if (T > 0) {
+      REQUIRE_PTR(a->d_normed);
+      REQUIRE_PTR(a->x);
+      REQUIRE_PTR(a->d_out);
+      REQUIRE_PTR4(a->rstd);
+      REQUIRE_PTR(a->d_x);
+    }
+    CHECK_HIP(launch_rmsnorm_bwd(kBF16, a->d_normed, a->x, a->d_out, a->rstd, a->norm_w, a->d_x, a->d_norm_w, a->d_b_o,
+                                 a->workspace, T, H, accum, s),
+              "rmsnorm backward");
+    return TP_MLP_OK;
+  }
+  REQUIRE_PTR(a->w_qkv);
+  REQUIRE_PTR(a->w_o);
+  REQUIRE_PTR(a->d_w_qkv);
+  REQUIRE_PTR(a->d_w_o);
+  if (T > 0) {
+    REQUIRE_PTR(a->normed);
+    REQUIRE_PTR(a->qkv);
+    REQUIRE_PTR(a->attn_out);
+    REQUIRE_PTR4(a->lse);
+    REQUIRE_PTR(a->d_out);
+    REQUIRE_PTR(a->d_attn_out);
+    REQUIRE_PTR(a->d_qkv);
+    REQUIRE_PTR(a->d_normed_part);
+  }
+  float* ksws = static_cast<float*>(a->workspace);
+  float* delta = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + attn_ksplit_bytes(d));
+
+  // dO = d_out W_o ([T, H] x [H, n_q D])
+  GemmArgs b1{};
+  b1.M = T;
+  b1.N = Wo;
+  b1.K = H;
+  b1.A = a->d_out;
+  b1.lda = H;
+  b1.B = a->w_o;
+  b1.ldb = Wo;
+  b1.C = a->d_attn_out;
+  b1.ldc = Wo;
+  b1.tag = "gemm_attn_dgrad_out";
+  CHECK_HIP(launch_gemm_bf16(true, false, kEpiStoreBf16, b1, s), "dO GEMM");
+  // d_w_o = d_out^T O ([H, T] x [T, n_q D])
+  GemmArgs b2{};
+  b2.M = H;
+  b2.N = Wo;
+  b2.K = T;
+  b2.A = a->d_out;
+  b2.lda = H;
+  b2.B = a->attn_out;
+  b2.ldb = Wo;
+  b2.C = a->d_w_o;
+  b2.ldc = Wo;
+  b2.ksplit = gemm_ksplit(b2.M, b2.N, b2.K);
+  b2.ws = ksws;
+  b2.accum = accum;
+  b2.tag = "gemm_attn_wgrad_out";
+  CHECK_HIP(launch_gemm_bf16(false, false, kEpiStoreF32, b2, s), "d_w_o GEMM");
+  CHECK_HIP(launch_attention_bwd(attn_args(d), a->qkv, a->attn_out, a->d_attn_out, a->lse, delta, a->d_qkv, s),
+            "attention backward");
+  // d_normed partial = d_qkv W_qkv ([T, W] x [W, H])
+  GemmArgs b3{};
+  b3.M = T;
+  b3.N = H;
+  b3.K = W;
+  b3.A = a->d_qkv;
+  b3.lda = W;
+  b3.B = a->w_qkv;
+  b3.ldb = H;
+  b3.C = a->d_normed_part;
+  b3.ldc = H;
+  b3.tag = "gemm_attn_dgrad_normed";
+  CHECK_HIP(launch_gemm_bf16(true, false, kEpiStoreF32, b3, s), "d_normed GEMM");
+  // d_w_qkv = d_qkv^T N ([W, T] x [T, H])
+  GemmArgs b4{};
+  b4.M = W;
+  b4.N = H;
+  b4.K = T;
+  b4.A = a->d_qkv;
+  b4.lda = W;
+  b4.B = a->normed;
+  b4.ldb = H;
+  b4.C = a->d_w_qkv;
+  b4.ldc = H;
+  b4.ksplit = gemm_ksplit(b4.M, b4.N, b4.K);
+  b4.ws = ksws;
+  b4.accum = accum;
+  b4.tag = "gemm_attn_wgrad_qkv";
+  CHECK_HIP(launch_gemm_bf16(false, false, kEpiStoreF32, b4, s), "d_w_qkv GEMM");
+  return TP_MLP_OK;
+}
+
+int tp_attention_forward(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv, int32_t head_dim, const void* qkv,
+                         int64_t ld, void* o, float* lse, void* stream) {
+  const char* fn = "tp_attention_forward";
+  g_err[0] = 0;
+  int rc = check_attn_shape(batch, seq, n_q, n_kv, head_dim, fn);
+  if (rc) return rc;
+  if (ld < (int64_t)(n_q + 2 * n_kv) * head_dim || ld % 8) return fail(TP_MLP_ESHAPE, "%s: bad ld", fn);
+  const int64_t T = batch * seq;
+  if (T * ld >= ((int64_t)1 << 31) || T * n_q * head_dim >= ((int64_t)1 << 31))
+    return fail(TP_MLP_ESHAPE, "%s: 2^31 or more elements", fn);
+  if (T == 0) return TP_MLP_OK;
+  REQUIRE_PTR(qkv);
+  REQUIRE_PTR(o);
+  REQUIRE_PTR4(lse);
+  AttnShapeArgs a{batch, seq, ld, n_q, n_kv, head_dim};
+  CHECK_HIP(launch_attention_fwd(a, qkv, o, lse, static_cast<hipStream_t>(stream)), "attention");
+  return TP_MLP_OK;
+}
+
+int tp_attention_backward(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv, int32_t head_dim, const void* qkv,
+                          int64_t ld, const void* o, const void* d_o, const float* lse, float* delta, void* d_qkv,
+                          void* stream) {
+  const char* fn = "tp_attention_backward";
+  g_err[0] = 0;
+  int rc = check_attn_shape(batch, seq, n_q, n_kv, head_dim, fn);
+  if (rc) return rc;
+  if (ld < (int64_t)(n_q + 2 * n_kv) * head_dim || ld % 8) return fail(TP_MLP_ESHAPE, "%s: bad ld", fn);
+  const int64_t T = batch * seq;
+  if (T * ld >= ((int64_t)1 << 31) || T * n_q * head_dim >= ((int64_t)1 << 31))
+    return fail(TP_MLP_ESHAPE, "%s: 2^31 or more elements", fn);
+  if (T == 0) return TP_MLP_OK;
+  REQUIRE_PTR(qkv);
+  REQUIRE_PTR(o);
+  REQUIRE_PTR(d_o);
+  REQUIRE_PTR4(lse);
+  REQUIRE_PTR4(delta);
+  REQUIRE_PTR(d_qkv);
+  AttnShapeArgs a{batch, seq, ld, n_q, n_kv, head_dim};
+  CHECK_HIP(launch_attention_bwd(a, qkv, o, d_o, lse, delta, d_qkv, static_cast<hipStream_t>(stream)),
+            "attention backward");
+  return TP_MLP_OK;
+}
+
 }  // extern "C"

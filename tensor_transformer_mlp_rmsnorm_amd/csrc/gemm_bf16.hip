@@ -280,6 +280,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const floatx4 (&acc)
         if constexpr (EPI == kEpiStoreF32) {
           float* c = ks == 0 ? static_cast<float*>(g.C) : g.ws + (int64_t)(ks - 1) * M * g.ldc;
           store4<float>(c + m * g.ldc + n, (g.accum && ks == 0) ? v + load4<float>(c + m * g.ldc + n) : v);
+        } else if constexpr (EPI == kEpiStoreBf16) {
+          store4<bf16_t>(static_cast<bf16_t*>(g.C) + m * g.ldc + n, v);
         } else if constexpr (EPI == kEpiResidual) {
           const floatx4 xr = load4<bf16_t>(static_cast<const bf16_t*>(g.aux) + m * g.ldc + n);
           const floatx4 bb = load4<bf16_t>(static_cast<const bf16_t*>(g.bias) + n);
@@ -663,11 +665,13 @@ hipError_t launch_gemm_bf16(bool ak, bool bk, Epi epi, const GemmArgs& g, hipStr
       case kEpiSwigluFwd: return launch_t<true, true, kEpiSwigluFwd>(g, s);
       case kEpiGeluFwd: return launch_t<true, true, kEpiGeluFwd>(g, s);
       case kEpiResidual: return launch_t<true, true, kEpiResidual>(g, s);
+      case kEpiStoreBf16: return launch_t<true, true, kEpiStoreBf16>(g, s);
       default: break;
     }
   } else if (ak && !bk) {
     switch (epi) {
       case kEpiStoreF32: return launch_t<true, false, kEpiStoreF32>(g, s);
+      case kEpiStoreBf16: return launch_t<true, false, kEpiStoreBf16>(g, s);
       case kEpiSwigluBwd: return launch_t<true, false, kEpiSwigluBwd>(g, s);
       case kEpiGeluBwd: return launch_t<true, false, kEpiGeluBwd>(g, s);
       default: break;

@@ -34,6 +34,7 @@ enum Epi {
   kEpiResidual = 3,   // out = acc + x + b_down (T)
   kEpiSwigluBwd = 4,  // d_pre = [dg | du] from d_act = acc and saved [g | u]
   kEpiGeluBwd = 5,    // dh = d_act * gelu'(h)
+  kEpiStoreBf16 = 6,  // C bf16 [M, ldc]
 };
 
 // Operand layouts: A is [M, K] when a_kcontig, else [K, M]; B is [N, K] when
@@ -103,6 +104,18 @@ hipError_t launch_fp8_cast(int fmt, const void* x, int64_t R, int64_t C, uint8_t
                            float* meta, const char* tag, hipStream_t s);
 hipError_t launch_fp8_update(float* const* metas, int count, int history_len, hipStream_t s);
 hipError_t launch_fp8_meta_init(float* meta, int fmt, int history_len, hipStream_t s);
+
+// Causal grouped-query attention on a [T, ld] QKV tensor (attention.hip).
+struct AttnShapeArgs {
+  int64_t batch, seq;  // T = batch * seq rows, a sequence's rows contiguous
+  int64_t ld;          // row length of qkv and dqkv (elements)
+  int n_q, n_kv, head_dim;
+};
+// O [T, n_q D] bf16, lse [n_q, T] fp32.
+hipError_t launch_attention_fwd(const AttnShapeArgs& a, const void* qkv, void* O, float* lse, hipStream_t s);
+// dqkv [T, ld] bf16 (every Q, K and V column written); delta: [n_q, T] fp32 scratch.
+hipError_t launch_attention_bwd(const AttnShapeArgs& a, const void* qkv, const void* O, const void* dO,
+                                const float* lse, float* delta, void* dqkv, hipStream_t s);
 
 hipError_t launch_rmsnorm_fwd(DType dt, const void* x, const void* w, void* n, float* rstd,
                               int64_t T, int64_t H, float eps, hipStream_t s);

@@ -526,3 +526,163 @@ class Fp8Step(ShardedStep):
             vals = torch.tensor([sc, si, am, float(m[3])] + [float(h) for h in hist], dtype=torch.float32)
             m.copy_(vals.to(self.dev))
 
+
+
+class AttnStep:
+    """One training step of the tensor-parallel attention sublayer
+    (tp_attn_forward / tp_attn_backward), S shards of complete query/KV head
+    groups run one after the other, with the same two sums as the MLP block:
+
+      forward   shard s: tp_attn_forward -> fp32 partial z_s
+                out = tp_partial_sum(z_0..z_{S-1}) + x + b_o
+      backward  shard s: tp_attn_backward(SHARD, d_out = out) -> dN_s, its weight grads
+                dN = tp_partial_sum(dN_0..dN_{S-1}); tp_attn_backward(NORM) -> dx, d_norm_w, d_b_o
+      update    tp_mlp_sgd_step_multi over every parameter tensor
+
+    Shard r owns query heads [r n_q/S, (r+1) n_q/S) and key/value heads
+    [r n_kv/S, (r+1) n_kv/S): its rows of the fused w_qkv are those Q, K and V
+    heads' rows (in that order) and its columns of w_o those query heads'.
+    Modes as ShardedStep ("missing_forward_reduce", "missing_backward_reduce")."""
+
+    MODES = MODES
+
+    def __init__(self, w, tensors: Dict[str, torch.Tensor], device="cuda", out_of_place_sgd: bool = False,
+                 stream: Optional[torch.cuda.Stream] = None):
+        if w.n_kv % w.shards or w.n_q % w.n_kv:
+            raise ValueError("the shards must own complete query/KV head groups")
+        self.w, self.dev, self.stream = w, torch.device(device), stream
+        self.T, self.H, self.D, S = w.tokens, w.hidden, w.d, w.shards
+        self.nq, self.nkv = w.n_q // S, w.n_kv // S
+        self.fuse = S == 1
+        self.oop = out_of_place_sgd
+        dev, bf, f32 = self.dev, torch.bfloat16, torch.float32
+        T, H, D, nq, nkv = self.T, self.H, self.D, self.nq, self.nkv
+        W, Wo = (nq + 2 * nkv) * D, nq * D
+        emp = lambda shape, d=bf: torch.empty(shape, dtype=d, device=dev)
+        up = lambda t: t.to(dev).contiguous()
+        self.x, self.norm_w, self.b_o = up(tensors["x"]), up(tensors["norm_w"]), up(tensors["b_o"])
+        NQ, NKV = w.n_q, w.n_kv
+        self.shards: List[dict] = []
+        for r in range(S):
+            qlo, kvlo = r * nq, r * nkv
+            rows = torch.cat([torch.arange(qlo * D, (qlo + nq) * D), NQ * D + torch.arange(kvlo * D, (kvlo + nkv) * D),
+                              (NQ + NKV) * D + torch.arange(kvlo * D, (kvlo + nkv) * D)])
+            sh = {"w_qkv": up(tensors["w_qkv"][rows]), "w_o": up(tensors["w_o"][:, qlo * D:(qlo + nq) * D]),
+                  "qkv": emp((T, W)), "attn_out": emp((T, Wo)), "lse": emp((nq, T), f32),
+                  "z": None if self.fuse else emp((T, H), f32), "d_attn_out": emp((T, Wo)), "d_qkv": emp((T, W)),
+                  "d_w_qkv": emp((W, H), f32), "d_w_o": emp((H, Wo), f32), "dN_part": emp((T, H), f32),
+                  "rows": rows}
+            self.shards.append(sh)
+        self.normed, self.rstd, self.out = emp((T, H)), emp((T,), f32), emp((T, H))
+        self.dN = self.shards[0]["dN_part"] if self.fuse else emp((T, H), f32)
+        self.dx, self.d_norm_w, self.d_b_o = emp((T, H)), emp((H,), f32), emp((H,), f32)
+        self.new = {name: (torch.empty_like(t) if self.oop else t) for name, t in self._param_list()}
+        d0 = self._desc()
+        ws = max(L.tp_attn_workspace_bytes(d0, L.BWD_SHARD), L.tp_attn_workspace_bytes(d0, L.BWD_NORM), 16)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self._abl: Dict[str, list] = {}
+
+    def _desc(self, flags: int = 0) -> L.tp_attn_desc:
+        w = self.w
+        return L.make_attn_desc(w.batch, w.seq, self.H, self.nq, self.nkv, self.D, w.eps, flags)
+
+    def _param_list(self):
+        out = [("norm_w", self.norm_w), ("b_o", self.b_o)]
+        for s, sh in enumerate(self.shards):
+            out += [(f"w_qkv.{s}", sh["w_qkv"]), (f"w_o.{s}", sh["w_o"])]
+        return out
+
+    def _grad_of(self, name: str) -> torch.Tensor:
+        if name in ("norm_w", "b_o"):
+            return self.d_norm_w if name == "norm_w" else self.d_b_o
+        key, s = name.split(".")
+        return self.shards[int(s)]["d_" + key]
+
+    def _abl_bufs(self, name, shape, dtype):
+        if name not in self._abl:
+            self._abl[name] = [torch.empty(shape, dtype=dtype, device=self.dev) for _ in self.shards]
+        return self._abl[name]
+
+    def forward(self, mode: str = "equivalence") -> None:
+        T, H, st = self.T, self.H, self.stream
+        for s, sh in enumerate(self.shards):
+            flags = (L.NORMED_READY if s > 0 else 0) | (L.FUSE_EPILOGUE if self.fuse else 0)
+            L.tp_attn_forward(self._desc(flags), self.x, self.norm_w, sh["w_qkv"], sh["w_o"], self.normed, self.rstd,
+                              sh["qkv"], sh["attn_out"], sh["lse"], self.out if self.fuse else sh["z"], self.b_o,
+                              stream=st)
+        if self.fuse:
+            return
+        if mode == "missing_forward_reduce":
+            for sh, o in zip(self.shards, self._abl_bufs("out", (T, H), torch.bfloat16)):
+                L.tp_partial_sum([sh["z"]], T, H, self.x, self.b_o, L.BF16, o, L.BF16, stream=st)
+        else:
+            L.tp_partial_sum([sh["z"] for sh in self.shards], T, H, self.x, self.b_o, L.BF16, self.out, L.BF16,
+                             stream=st)
+
+    def _shard_backward(self, sh, d_out) -> None:
+        L.tp_attn_backward(self._desc(), L.BWD_SHARD, stream=self.stream, normed=self.normed, qkv=sh["qkv"],
+                           attn_out=sh["attn_out"], lse=sh["lse"], w_qkv=sh["w_qkv"], w_o=sh["w_o"], d_out=d_out,
+                           d_attn_out=sh["d_attn_out"], d_qkv=sh["d_qkv"], d_w_qkv=sh["d_w_qkv"], d_w_o=sh["d_w_o"],
+                           d_normed_part=sh["dN_part"], workspace=self.workspace)
+
+    def _norm_backward(self, dN, d_out, dx, d_norm_w, d_b_o) -> None:
+        L.tp_attn_backward(self._desc(), L.BWD_NORM, stream=self.stream, x=self.x, rstd=self.rstd, norm_w=self.norm_w,
+                           d_out=d_out, d_normed=dN, d_x=dx, d_norm_w=d_norm_w, d_b_o=d_b_o, workspace=self.workspace)
+
+    def backward(self, mode: str = "equivalence") -> None:
+        T, H = self.T, self.H
+        fwd_abl = mode == "missing_forward_reduce" and not self.fuse
+        outs = self._abl["out"] if fwd_abl else [self.out] * len(self.shards)
+        for sh, o in zip(self.shards, outs):
+            self._shard_backward(sh, o)
+        if not self.fuse and mode != "missing_backward_reduce":
+            L.tp_partial_sum([sh["dN_part"] for sh in self.shards], T, H, None, None, L.F32, self.dN, L.F32,
+                             stream=self.stream)
+        if mode == "equivalence" or self.fuse:
+            self._norm_backward(self.dN, self.out, self.dx, self.d_norm_w, self.d_b_o)
+            return
+        dxs = self._abl_bufs("dx", (T, H), torch.bfloat16)
+        dws = self._abl_bufs("d_norm_w", (H,), torch.float32)
+        dbs = self._abl_bufs("d_b_o", (H,), torch.float32)
+        for s, sh in enumerate(self.shards):
+            self._norm_backward(self.dN if fwd_abl else sh["dN_part"], outs[s], dxs[s], dws[s], dbs[s])
+
+    def sgd(self) -> None:
+        lst = [(t, self.new[n], self._grad_of(n), None, None, t.numel()) for n, t in self._param_list()]
+        L.tp_mlp_sgd_step_multi(lst, L.BF16, self.w.lr, stream=self.stream)
+
+    def step(self, mode: str = "equivalence", update: bool = True) -> None:
+        if mode not in self.MODES:
+            raise ValueError(mode)
+        self.forward(mode)
+        self.backward(mode)
+        if update and mode == "equivalence":
+            self.sgd()
+
+    def results(self, mode: str = "equivalence") -> dict:
+        """CPU copies (float32) with the shards' slices placed back into the dense w_qkv rows and w_o columns."""
+        c = lambda t: t.detach().float().cpu()
+        w, D = self.w, self.D
+        W_full = (w.n_q + 2 * w.n_kv) * D
+        r = {"normed": c(self.normed), "rstd": c(self.rstd)}
+        dq = torch.zeros(W_full, self.H)
+        do = torch.zeros(self.H, w.n_q * D)
+        nq_ = torch.zeros(W_full, self.H)
+        no_ = torch.zeros(self.H, w.n_q * D)
+        for s, sh in enumerate(self.shards):
+            dq[sh["rows"]] = c(sh["d_w_qkv"])
+            nq_[sh["rows"]] = c(self.new[f"w_qkv.{s}"])
+            cols = slice(s * self.nq * D, (s + 1) * self.nq * D)
+            do[:, cols] = c(sh["d_w_o"])
+            no_[:, cols] = c(self.new[f"w_o.{s}"])
+        r.update(d_w_qkv=dq, d_w_o=do, new_w_qkv=nq_, new_w_o=no_, new_norm_w=c(self.new["norm_w"]),
+                 new_b_o=c(self.new["b_o"]))
+        r["attn_out"] = torch.cat([c(sh["attn_out"]) for sh in self.shards], dim=1)
+        if mode == "equivalence" or self.fuse:
+            r.update(out=c(self.out), dx=c(self.dx), d_norm_w=c(self.d_norm_w), d_b_o=c(self.d_b_o), dN=c(self.dN))
+        else:
+            r["out"] = [c(o) for o in self._abl["out"]] if mode == "missing_forward_reduce" else c(self.out)
+            r["dx"] = [c(t) for t in self._abl["dx"]]
+            r["d_norm_w"] = [c(t) for t in self._abl["d_norm_w"]]
+            r["d_b_o"] = [c(t) for t in self._abl["d_b_o"]]
+        return r

@@ -117,3 +117,26 @@ def check_fp8_step(name, got, ref, report=None) -> float:
     assert e <= FP8_STEP_FROB, f"{name}: relative Frobenius error {e:.3e} > {FP8_STEP_FROB}"
     return e
 
+
+def check_sum_of_stored(name, got, ref, a_terms, b_terms, scale: float = 1.0, report=None) -> float:
+    """The bf16 bound for C = A^T B (times `scale`, e.g. the learning rate of
+    an update) where A is a stored bf16 tensor: besides the floored relative
+    bound, a stored value of A can land one bf16 ulp away from the oracle's
+    where its fp32 value lies within the accumulation error of a rounding
+    midpoint, and a sum dominated by a few large terms then moves by that
+    ulp times the other factor.  The allowance is one such flip of the largest
+    term, bounded separably: 2^-7 max_t |A[t, i]| max_t |B[t, j]| (a bf16 ulp
+    is at most 2^-7 of the value).  a_terms [T, M], b_terms [T, N] are the
+    oracle's A and B."""
+    g, r = _np(got), _np(ref)
+    a, b = np.abs(_np(a_terms)), np.abs(_np(b_terms))
+    assert g.shape == r.shape == (a.shape[1], b.shape[1]), (g.shape, r.shape, a.shape, b.shape)
+    rho = np.sqrt(np.mean(r * r)) if r.size else 0.0
+    allow = 2.0 ** -7 * np.outer(a.max(axis=0), b.max(axis=0)) * abs(scale)
+    bound = BF16_RTOL * np.maximum(np.abs(r), rho) + allow
+    e = float(np.max(np.abs(g - r) / np.where(bound > 0, bound, 1.0))) if g.size else 0.0
+    if report is not None:
+        report[name] = e
+    assert e <= 1.0, f"{name}: error / (bf16 bound + one-ulp flip of the largest term) {e:.3e} > 1"
+    return e
+
