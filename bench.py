@@ -22,6 +22,9 @@ times the same step in the sequence-parallel layout (norm, residual and bias
 on each rank's token rows; reduce-scatter and all-gather at the boundaries).
 `fp8_path` times the step with every GEMM on FP8 codes (delayed scaling),
 its GEMMs against the fp8 MFMA peak and its casts against HBM bandwidth.
+`attention_path` times the tensor-parallel attention sublayer's step on the
+Llama-3-8B TP=8 attention shape (32 query / 8 KV heads of 128, 2 causal
+sequences of 4096), each kernel against the bf16 peak.
 """
 
 from __future__ import annotations
@@ -248,6 +251,61 @@ def fp8_path(w, t, steps: int, warmup: int) -> dict:
             if gemm_ms > 0 else None, "kernels": kernels}
 
 
+def attention_flops(aw) -> dict:
+    """Algorithmic flops of one launch of each attention-sublayer kernel of
+    one shard, by kernel name.  Causal attention touches the
+    s (s + 1) / 2 query-key pairs of each sequence: forward 2 products
+    (S, PV), backward 4 (dP, dS -> dQ, dK, dV); the dK/dV kernel is charged
+    dP, dK and dV, the dQ kernel dQ."""
+    T, H, D, S = aw.tokens, aw.hidden, aw.d, aw.shards
+    nq, nkv = aw.n_q // S, aw.n_kv // S
+    W, Wo = (nq + 2 * nkv) * D, nq * D
+    pd = 2 * (aw.batch * aw.seq * (aw.seq + 1) // 2) * D * nq  # one product over the causal pairs
+    return {"gemm_qkv": 2 * T * H * W, "gemm_out_proj_partial": 2 * T * H * Wo, "gemm_out_proj_residual": 2 * T * H * Wo,
+            "gemm_attn_dgrad_out": 2 * T * H * Wo, "gemm_attn_wgrad_out": 2 * H * Wo * T,
+            "gemm_attn_dgrad_normed": 2 * T * W * H, "gemm_attn_wgrad_qkv": 2 * W * H * T,
+            "attention_fwd": 2 * pd, "attention_bwd_dkdv": 3 * pd, "attention_bwd_dq": pd}
+
+
+def attention_path(steps: int, warmup: int, name: str = "attn_llama3_8b_tp8") -> dict:
+    """The tensor-parallel attention sublayer's step (forward, backward, SGD
+    over all shards in sequence) on the Llama-3-8B TP=8 attention shape: its
+    time and each kernel against its roofline."""
+    import torch
+    import synth
+    from tensor_transformer_mlp_rmsnorm_amd import _lib as L
+    from tensor_transformer_mlp_rmsnorm_amd.step import AttnStep
+
+    aw = synth.attn_workload(name)
+    st = AttnStep(aw, synth.draw_attn(aw), device="cuda:0", out_of_place_sgd=True)
+    for _ in range(max(1, warmup)):
+        st.step()
+    torch.cuda.synchronize()
+    L.tp_mlp_profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    L.tp_mlp_profile_enable(False)
+    prof = L.tp_mlp_profile_entries()
+    del st
+    torch.cuda.empty_cache()
+    fl = attention_flops(aw)
+    kernels = {}
+    for k, (n, tot) in prof.items():
+        if k in fl:
+            ach = fl[k] * n / (tot / 1e3) / 1e12
+            kernels[k] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": ach / PEAK_BF16_TFLOPS, "per_launch": fl[k], "avg_ms": tot / n, "launches": n}
+        else:
+            kernels[k] = {"bound": None, "avg_ms": tot / n, "launches": n}
+    return {"workload": name, "batch": aw.batch, "seq": aw.seq, "hidden": aw.hidden, "n_q": aw.n_q, "n_kv": aw.n_kv,
+            "head_dim": aw.d, "shards": aw.shards, "causal": True, "ms_per_step": ms,
+            "tflops": aw.flops_per_step / (ms / 1e3) / 1e12, "tokens_per_s": aw.tokens / (ms / 1e3),
+            "kernels": kernels}
+
+
 def sequence_parallel_timing(w, t, steps: int, warmup: int) -> dict:
     """The step in the sequence-parallel layout, same inputs and flop count."""
     import torch
@@ -277,8 +335,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-extras", action="store_true", help="skip the measurements after the timed step")
-    ap.add_argument("--extras", default="optimizer,sp,fp8",
-                    help="comma-separated measurements after the timed step: optimizer, sp, fp8")
+    ap.add_argument("--extras", default="optimizer,sp,fp8,attention",
+                    help="comma-separated measurements after the timed step: optimizer, sp, fp8, attention")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -363,6 +421,12 @@ def main() -> int:
         torch.cuda.empty_cache()
         st = None
         out["fp8_path"] = fp8_path(w, t, args.steps, args.warmup)
+    if "attention" in extras:
+        if st is not None:
+            del st
+            torch.cuda.empty_cache()
+            st = None
+        out["attention_path"] = attention_path(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         st = None
         torch.cuda.empty_cache()

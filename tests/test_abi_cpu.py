@@ -317,3 +317,46 @@ def test_fp8_checks(lib):
     assert call(N=4096, K=8192, lda=8192, ldb=8192, ldc=4096) == L.EWORKSPACE
     assert call(N=4096, K=8192, lda=8192, ldb=8192, ldc=4096, ws=MIS, wsb=need) == L.EALIGN
 
+
+
+def test_attention_checks(lib):
+    def desc(**kw):
+        a = dict(batch=2, seq=64, hidden=128, n_q=4, n_kv=2, head_dim=64, eps=1e-6, flags=0, dtype=L.BF16)
+        a.update(kw)
+        return L.make_attn_desc(a["batch"], a["seq"], a["hidden"], a["n_q"], a["n_kv"], a["head_dim"], a["eps"],
+                                a["flags"], a["dtype"])
+
+    fwd = lambda d, **p: lib.tp_attn_forward(ctypes.byref(d), *[p.get(k, A) for k in (
+        "x", "norm_w", "w_qkv", "w_o", "normed", "rstd", "qkv", "attn_out", "lse", "out", "b_o")], None)
+    assert fwd(desc(head_dim=96)) == L.ESHAPE                 # 64 or 128
+    assert fwd(desc(n_q=3, n_kv=2)) == L.ESHAPE               # n_q a multiple of n_kv
+    assert fwd(desc(dtype=L.F32)) == L.EDTYPE                 # bf16 only
+    assert fwd(desc(hidden=100)) == L.ESHAPE
+    assert fwd(desc(flags=8)) == L.EINVAL
+    assert fwd(desc(batch=-1)) == L.EINVAL
+    assert fwd(desc(), w_qkv=None) == L.EINVAL
+    assert fwd(desc(), qkv=MIS) == L.EALIGN
+    assert fwd(desc(), lse=A + 2) == L.EALIGN                 # lse: 4-byte alignment
+    assert fwd(desc(flags=L.FUSE_EPILOGUE), b_o=None) == L.EINVAL
+    assert fwd(desc(seq=0), x=None, qkv=None, out=None) == L.OK   # no tokens: a no-op
+    assert lib.tp_attn_forward(None, *([A] * 11), None) == L.EINVAL
+    d = desc()
+    need = lib.tp_attn_workspace_bytes(ctypes.byref(d), L.BWD_SHARD)
+    assert need >= 4 * 2 * 64 * 4                              # delta [n_q, T] at least
+    a = L.tp_attn_bwd_args()
+    for name, _ in L.tp_attn_bwd_args._fields_:
+        if name != "workspace_bytes":
+            setattr(a, name, A)
+    a.workspace_bytes = need - 16
+    assert lib.tp_attn_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EWORKSPACE
+    a.workspace_bytes = need
+    assert lib.tp_attn_backward(ctypes.byref(d), 7, ctypes.byref(a), None) == L.EINVAL
+    a.d_qkv = MIS
+    assert lib.tp_attn_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EALIGN
+    bare = lib.tp_attention_forward
+    assert bare(1, 8, 2, 1, 64, A, 200, A, A, None) == L.ESHAPE          # ld < (n_q + 2 n_kv) D
+    assert bare(1, 8, 2, 1, 64, A, 260, A, A, None) == L.ESHAPE          # ld not a multiple of 8
+    assert bare(1, 8, 2, 1, 32, A, 256, A, A, None) == L.ESHAPE          # head_dim
+    assert bare(0, 8, 2, 1, 64, None, 256, None, None, None) == L.OK     # empty
+    bb = lib.tp_attention_backward
+    assert bb(1, 8, 2, 1, 64, A, 256, A, A, A, None, A, None) == L.EINVAL   # delta scratch missing
