@@ -529,14 +529,20 @@ size_t tp_attn_workspace_bytes(const tp_attn_desc* d, int32_t phase);
  *   qkv [batch seq, ld] bf16 with the Q, K, V head columns at 0, n_q D and
  *   (n_q + n_kv) D (ld >= (n_q + 2 n_kv) D, a multiple of 8); o and d_o
  *   [batch seq, n_q D] bf16; lse [n_q, batch seq] fp32; d_qkv [batch seq, ld]
- *   bf16 (its first (n_q + 2 n_kv) D columns written); delta: DEVICE fp32
- *   scratch of n_q batch seq elements.  head_dim 64 or 128.
+ *   bf16 (its first (n_q + 2 n_kv) D columns written).  head_dim 64 or 128.
+ *   workspace: DEVICE scratch, 16-byte aligned, of at least
+ *   tp_attention_backward_workspace_bytes(...) bytes (the softmax row terms
+ *   rowsum(dO o O) and, when n_q > n_kv, each query head's fp32 share of dK
+ *   and dV, added in a fixed order); TP_MLP_EWORKSPACE if smaller.
+ *   Deterministic.
  */
 int tp_attention_forward(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv, int32_t head_dim, const void* qkv,
                          int64_t ld, void* o, float* lse, void* stream);
 int tp_attention_backward(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv, int32_t head_dim, const void* qkv,
-                          int64_t ld, const void* o, const void* d_o, const float* lse, float* delta, void* d_qkv,
-                          void* stream);
+                          int64_t ld, const void* o, const void* d_o, const float* lse, void* workspace,
+                          size_t workspace_bytes, void* d_qkv, void* stream);
+size_t tp_attention_backward_workspace_bytes(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv,
+                                             int32_t head_dim);
 
 /*
  * Kernel timing, a measurement aid (off by default).  While enabled, every

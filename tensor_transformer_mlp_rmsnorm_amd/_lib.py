@@ -36,7 +36,8 @@ EXPORTED = ("tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_works
             "tp_mlp_clip_grad_norm", "tp_mlp_clip_grad_norm_workspace_bytes", "tp_rmsnorm_forward",
             "tp_mlp_fp8_meta_init", "tp_mlp_fp8_cast", "tp_mlp_fp8_update_scales", "tp_mlp_forward_fp8",
             "tp_mlp_backward_fp8", "tp_mlp_fp8_gemm", "tp_mlp_fp8_gemm_workspace_bytes", "tp_attn_forward",
-            "tp_attn_backward", "tp_attn_workspace_bytes", "tp_attention_forward", "tp_attention_backward")
+            "tp_attn_backward", "tp_attn_workspace_bytes", "tp_attention_forward", "tp_attention_backward",
+            "tp_attention_backward_workspace_bytes")
 
 
 class TPMLPError(RuntimeError):
@@ -164,8 +165,12 @@ def lib() -> ctypes.CDLL:
                                            ctypes.c_int32, _vp, ctypes.c_int64, _vp, _vp, _vp]
         L.tp_attention_forward.restype = ctypes.c_int
         L.tp_attention_backward.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-                                            ctypes.c_int32, _vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp]
+                                            ctypes.c_int32, _vp, ctypes.c_int64, _vp, _vp, _vp, _vp,
+                                            ctypes.c_size_t, _vp, _vp]
         L.tp_attention_backward.restype = ctypes.c_int
+        L.tp_attention_backward_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                                            ctypes.c_int32, ctypes.c_int32]
+        L.tp_attention_backward_workspace_bytes.restype = ctypes.c_size_t
         L.tp_mlp_last_error.argtypes = []
         L.tp_mlp_last_error.restype = ctypes.c_char_p
         L.tp_mlp_version.argtypes = []
@@ -341,9 +346,13 @@ def tp_attention_forward(batch: int, seq: int, n_q: int, n_kv: int, head_dim: in
 
 
 def tp_attention_backward(batch: int, seq: int, n_q: int, n_kv: int, head_dim: int, qkv, ld: int, o, d_o, lse,
-                          delta, d_qkv, stream=None) -> None:
+                          workspace, workspace_bytes: int, d_qkv, stream=None) -> None:
     _check(lib().tp_attention_backward(batch, seq, n_q, n_kv, head_dim, _ptr(qkv), ld, _ptr(o), _ptr(d_o), _ptr(lse),
-                                       _ptr(delta), _ptr(d_qkv), _stream(stream)))
+                                       _ptr(workspace), workspace_bytes, _ptr(d_qkv), _stream(stream)))
+
+
+def tp_attention_backward_workspace_bytes(batch: int, seq: int, n_q: int, n_kv: int, head_dim: int) -> int:
+    return int(lib().tp_attention_backward_workspace_bytes(batch, seq, n_q, n_kv, head_dim))
 
 
 def tp_mlp_sgd_step(param_in, param_out, grad, master_in, master_out, n: int, param_dtype: int, lr: float,

@@ -847,7 +847,8 @@ AttnShapeArgs attn_args(const tp_attn_desc* d) {
 }
 
 // Workspace of the SHARD phase: the k-split slices of the two weight-gradient
-// GEMMs (they run one after the other and share them), then delta [n_q, T].
+// GEMMs (they run one after the other and share them), then the attention
+// backward's own (delta [n_q, T] and the per-head dK/dV shares).
 size_t attn_ksplit_bytes(const tp_attn_desc* d) {
   const int64_t T = d->batch * d->seq, H = d->hidden;
   const int64_t W = (int64_t)(d->n_q + 2 * d->n_kv) * d->head_dim, Wo = (int64_t)d->n_q * d->head_dim;
@@ -862,7 +863,15 @@ size_t tp_attn_workspace_bytes(const tp_attn_desc* d, int32_t phase) {
   const int64_t T = d->batch * d->seq;
   if (phase == TP_MLP_BWD_NORM) return rmsnorm_bwd_workspace(T, d->hidden);
   if (phase != TP_MLP_BWD_SHARD) return 0;
-  return attn_ksplit_bytes(d) + (size_t)d->n_q * (size_t)T * sizeof(float);
+  (void)T;
+  return attn_ksplit_bytes(d) + attention_bwd_workspace(attn_args(d));
+}
+
+size_t tp_attention_backward_workspace_bytes(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv,
+                                             int32_t head_dim) {
+  if (batch < 0 || seq < 0 || n_q <= 0 || n_kv <= 0 || head_dim <= 0) return 0;
+  AttnShapeArgs a{batch, seq, (int64_t)(n_q + 2 * n_kv) * head_dim, n_q, n_kv, head_dim};
+  return attention_bwd_workspace(a);
 }
 
 int tp_attn_forward(const tp_attn_desc* d, const void* x, const void* norm_w, const void* w_qkv, const void* w_o,
@@ -970,7 +979,7 @@ int tp_attn_backward(const tp_attn_desc* d, int32_t phase, const tp_attn_bwd_arg
     REQUIRE_PTR(a->d_normed_part);
   }
   float* ksws = static_cast<float*>(a->workspace);
-  float* delta = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + attn_ksplit_bytes(d));
+  void* attn_ws = static_cast<char*>(a->workspace) + attn_ksplit_bytes(d);
 
   // dO = d_out W_o ([T, H] x [H, n_q D])
   GemmArgs b1{};
@@ -1001,7 +1010,7 @@ int tp_attn_backward(const tp_attn_desc* d, int32_t phase, const tp_attn_bwd_arg
   b2.accum = accum;
   b2.tag = "gemm_attn_wgrad_out";
   CHECK_HIP(launch_gemm_bf16(false, false, kEpiStoreF32, b2, s), "d_w_o GEMM");
-  CHECK_HIP(launch_attention_bwd(attn_args(d), a->qkv, a->attn_out, a->d_attn_out, a->lse, delta, a->d_qkv, s),
+  CHECK_HIP(launch_attention_bwd(attn_args(d), a->qkv, a->attn_out, a->d_attn_out, a->lse, attn_ws, a->d_qkv, s),
             "attention backward");
   // d_normed partial = d_qkv W_qkv ([T, W] x [W, H])
   GemmArgs b3{};
@@ -1055,8 +1064,8 @@ int tp_attention_forward(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv, 
 }
 
 int tp_attention_backward(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv, int32_t head_dim, const void* qkv,
-                          int64_t ld, const void* o, const void* d_o, const float* lse, float* delta, void* d_qkv,
-                          void* stream) {
+                          int64_t ld, const void* o, const void* d_o, const float* lse, void* workspace,
+                          size_t workspace_bytes, void* d_qkv, void* stream) {
   const char* fn = "tp_attention_backward";
   g_err[0] = 0;
   int rc = check_attn_shape(batch, seq, n_q, n_kv, head_dim, fn);
@@ -1070,10 +1079,14 @@ int tp_attention_backward(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv,
   REQUIRE_PTR(o);
   REQUIRE_PTR(d_o);
   REQUIRE_PTR4(lse);
-  REQUIRE_PTR4(delta);
   REQUIRE_PTR(d_qkv);
   AttnShapeArgs a{batch, seq, ld, n_q, n_kv, head_dim};
-  CHECK_HIP(launch_attention_bwd(a, qkv, o, d_o, lse, delta, d_qkv, static_cast<hipStream_t>(stream)),
+  const size_t need = attention_bwd_workspace(a);
+  if (!workspace || workspace_bytes < need)
+    return fail(TP_MLP_EWORKSPACE, "%s: workspace of %zu bytes required, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(TP_MLP_EALIGN, "%s: workspace is not 16-byte aligned", fn);
+  CHECK_HIP(launch_attention_bwd(a, qkv, o, d_o, lse, workspace, d_qkv, static_cast<hipStream_t>(stream)),
             "attention backward");
   return TP_MLP_OK;
 }

@@ -29,11 +29,12 @@
 // queries; K and V tiles of 64 keys in LDS; online softmax in exp2 with the
 // 1/sqrt(D) scale folded in.  The probabilities P and the score gradients dS
 // enter their products as a bf16 pair (hi + lo, see pack_slots).  Backward
-// (two kernels, no atomics): dK and dV per (key block of 64, KV head, batch),
-// looping over the group's query heads
-// and the query blocks at or after the key block; dQ per (query block, head,
-// batch), looping over key blocks; both recompute P from lse, and use
-// delta = rowsum(dO o O) from a small kernel.
+// (no atomics): dK and dV per (key block of 64, query head, batch) over the
+// query blocks at or after the key block, the shares of a group's query heads
+// then added in a fixed order by a small kernel; dQ per (query block, head,
+// batch) over the key blocks up to it; both recompute P from lse and use
+// delta = rowsum(dO o O) from a small kernel.  Every loop issues the global
+// loads of its next tile before the products of the current one.
 #include "common.h"
 #include "kernels.h"
 
@@ -77,17 +78,29 @@ struct Tile {
     }
     return make_uint4(out[0].x, out[0].y, out[1].x, out[1].y);
   }
-  // Fill rows [0, 64) from global rows r0 .. r0 + 63 (ld elements apart),
-  // columns col0 .. col0 + D - 1; rows at or past `rows` are zero.
-  __device__ __forceinline__ static void load(char* base, const bf16_t* src, int64_t ld, int64_t r0, int64_t rows,
-                                              int64_t col0, int tid) {
+  // A tile's worth of this thread's chunks, staged in registers so the next
+  // tile's global loads overlap the current tile's products.
+  static constexpr int kPer = kAttnBlock * kChunks / kAttnThreads;
+  struct Regs {
+    uint4 v[kPer];
+  };
+  // Global rows r0 .. r0 + 63 (ld elements apart), columns col0 .. col0 + D - 1;
+  // rows at or past `rows` are zero.
+  __device__ __forceinline__ static void fetch(Regs& r, const bf16_t* src, int64_t ld, int64_t r0, int64_t rows,
+                                               int64_t col0, int tid) {
 #pragma unroll
-    for (int i = 0; i < kAttnBlock * kChunks / kAttnThreads; ++i) {
+    for (int i = 0; i < kPer; ++i) {
       const int idx = tid + kAttnThreads * i;
       const int row = idx / kChunks, c = idx % kChunks;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r0 + row < rows) v = *reinterpret_cast<const uint4*>(src + (r0 + row) * ld + col0 + 8 * c);
-      *reinterpret_cast<uint4*>(base + chunk_off(row, c)) = v;
+      r.v[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (r0 + row < rows) r.v[i] = *reinterpret_cast<const uint4*>(src + (r0 + row) * ld + col0 + 8 * c);
+    }
+  }
+  __device__ __forceinline__ static void store(char* base, const Regs& r, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = tid + kAttnThreads * i;
+      *reinterpret_cast<uint4*>(base + chunk_off(idx / kChunks, idx % kChunks)) = r.v[i];
     }
   }
 };
@@ -158,11 +171,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(const bf16_t* __
   float m = -INFINITY, lsum = 0.0f;
   const int64_t kcol = (int64_t)(dm.n_q + kvh) * D, vcol = (int64_t)(dm.n_q + dm.n_kv + kvh) * D;
   const int nkb = qb + 1;  // key blocks 0 .. qb hold every key <= a query of this block
+  const bf16_t* src = qkv + t0 * dm.ld;
+  typename Tile<D>::Regs kr, vr;
+  Tile<D>::fetch(kr, src, dm.ld, 0, dm.seq, kcol, tid);
+  Tile<D>::fetch(vr, src, dm.ld, 0, dm.seq, vcol, tid);
   for (int kb = 0; kb < nkb; ++kb) {
+    __syncthreads();  // the previous tiles are no longer read
+    Tile<D>::store(ktile, kr, tid);
+    Tile<D>::store(vtile, vr, tid);
     __syncthreads();
-    Tile<D>::load(ktile, qkv + t0 * dm.ld, dm.ld, (int64_t)kb * kAttnBlock, dm.seq, kcol, tid);
-    Tile<D>::load(vtile, qkv + t0 * dm.ld, dm.ld, (int64_t)kb * kAttnBlock, dm.seq, vcol, tid);
-    __syncthreads();
+    if (kb + 1 < nkb) {  // the next tiles load while these are multiplied
+      Tile<D>::fetch(kr, src, dm.ld, (int64_t)(kb + 1) * kAttnBlock, dm.seq, kcol, tid);
+      Tile<D>::fetch(vr, src, dm.ld, (int64_t)(kb + 1) * kAttnBlock, dm.seq, vcol, tid);
+    }
     floatx4 s[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -234,21 +255,28 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const bf16_t* __restric
   delta[(int64_t)h * T + t] = acc;
 }
 
-// dK and dV of 64 keys of one KV head: every query head of the group, every
-// query block at or after the key block.  Wave w owns keys 16 w .. 16 w + 15.
+// dK and dV of 64 keys from one query head (one workgroup per key block,
+// query head and sequence; the key blocks with the most query blocks after
+// them are dispatched first): every query block at or after the key block.
+// Wave w owns keys 16 w .. 16 w + 15.  With one query head per KV head the
+// result goes to dqkv; otherwise each head's share goes to
+// part[h % group][t][kv head][2 D] (fp32, dK then dV) and attn_reduce_kernel
+// adds the group's shares in order.
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_dkdv_kernel(const bf16_t* __restrict__ qkv,
                                                                  const bf16_t* __restrict__ dO,
                                                                  const float* __restrict__ lse,
                                                                  const float* __restrict__ delta,
-                                                                 bf16_t* __restrict__ dqkv, AttnDims dm) {
+                                                                 bf16_t* __restrict__ dqkv, float* __restrict__ part,
+                                                                 AttnDims dm) {
   __shared__ __align__(16) char qtile[kAttnBlock * D * 2];
   __shared__ __align__(16) char dotile[kAttnBlock * D * 2];
   __shared__ float lse2_s[kAttnBlock], delta_s[kAttnBlock];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
   const int nkb = (int)((dm.seq + kAttnBlock - 1) / kAttnBlock);
-  int kb, kvh, b;
-  block_coords(nkb, dm.n_kv, (int)dm.batch, kb, kvh, b);
+  const int per = dm.n_q * (int)dm.batch;
+  const int kb = blockIdx.x / per, hq = (blockIdx.x % per) / (int)dm.batch, b = blockIdx.x % (int)dm.batch;
+  const int kvh = hq / dm.group;
   const int64_t t0 = (int64_t)b * dm.seq, T = dm.batch * dm.seq;
   const int key = kb * kAttnBlock + 16 * w + c;  // this lane's key (Y-operand row)
   constexpr int KS = D / 32, EB = D / 16;
@@ -266,59 +294,98 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dkdv_kernel(const bf16_t* _
 #pragma unroll
   for (int i = 0; i < EB; ++i) dk[i] = dv[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int nqb = nkb;
-  for (int hq = kvh * dm.group; hq < (kvh + 1) * dm.group; ++hq) {
-    for (int qb = kb; qb < nqb; ++qb) {
-      __syncthreads();
-      Tile<D>::load(qtile, qkv + t0 * dm.ld, dm.ld, (int64_t)qb * kAttnBlock, dm.seq, (int64_t)hq * D, tid);
-      Tile<D>::load(dotile, dO + t0 * dm.ldo, dm.ldo, (int64_t)qb * kAttnBlock, dm.seq, (int64_t)hq * D, tid);
-      if (tid < kAttnBlock) {
-        const int qq = qb * kAttnBlock + tid;
-        const bool ok = qq < dm.seq;
-        lse2_s[tid] = ok ? lse[(int64_t)hq * T + t0 + qq] * kLog2e : 0.0f;
-        delta_s[tid] = ok ? delta[(int64_t)hq * T + t0 + qq] : 0.0f;
+  const bf16_t* qsrc = qkv + t0 * dm.ld;
+  const bf16_t* dsrc = dO + t0 * dm.ldo;
+  typename Tile<D>::Regs qr, dr;
+  float lr = 0.0f, dl = 0.0f;
+  auto fetch = [&](int qb) {
+    Tile<D>::fetch(qr, qsrc, dm.ld, (int64_t)qb * kAttnBlock, dm.seq, (int64_t)hq * D, tid);
+    Tile<D>::fetch(dr, dsrc, dm.ldo, (int64_t)qb * kAttnBlock, dm.seq, (int64_t)hq * D, tid);
+    if (tid < kAttnBlock) {
+      const int qq = qb * kAttnBlock + tid;
+      const bool ok = qq < dm.seq;
+      lr = ok ? lse[(int64_t)hq * T + t0 + qq] * kLog2e : 0.0f;
+      dl = ok ? delta[(int64_t)hq * T + t0 + qq] : 0.0f;
+    }
+  };
+  fetch(kb);
+  for (int qb = kb; qb < nqb; ++qb) {
+    __syncthreads();
+    Tile<D>::store(qtile, qr, tid);
+    Tile<D>::store(dotile, dr, tid);
+    if (tid < kAttnBlock) {
+      lse2_s[tid] = lr;
+      delta_s[tid] = dl;
+    }
+    __syncthreads();
+    if (qb + 1 < nqb) fetch(qb + 1);
+    // S[q][key] and dP[q][key] for the block's 4 x 16 queries; lane: q = 16 qq + 4 g + r, key = c
+    floatx4 p[4], ds[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      floatx4 sv = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sv = mma(Tile<D>::row8(qtile, 16 * qq + c, 4 * ks + g), kf[ks], sv);
+        dp = mma(Tile<D>::row8(dotile, 16 * qq + c, 4 * ks + g), vf[ks], dp);
       }
-      __syncthreads();
-      // S[q][key] and dP[q][key] for the block's 4 x 16 queries; lane: q = 16 qq + 4 g + r, key = c
-      floatx4 p[4], ds[4];
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s = mma(Tile<D>::row8(qtile, 16 * qq + c, 4 * ks + g), kf[ks], s);
-          dp = mma(Tile<D>::row8(dotile, 16 * qq + c, 4 * ks + g), vf[ks], dp);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ql = 16 * qq + 4 * g + r, qpos = qb * kAttnBlock + ql;
-          const bool ok = key <= qpos && qpos < dm.seq && key < dm.seq;
-          const float pv = ok ? exp2f(s[r] * dm.scale_log2 - lse2_s[ql]) : 0.0f;
-          p[qq][r] = pv;
-          ds[qq][r] = pv * (dp[r] - delta_s[ql]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int ql = 16 * qq + 4 * g + r, qpos = qb * kAttnBlock + ql;
+        const bool ok = key <= qpos && qpos < dm.seq && key < dm.seq;
+        const float pv = ok ? exp2f(sv[r] * dm.scale_log2 - lse2_s[ql]) : 0.0f;
+        p[qq][r] = pv;
+        ds[qq][r] = pv * (dp[r] - delta_s[ql]);
       }
-      // dV^T[e][key] += dO^T P, dK^T[e][key] += Q^T dS (the 1/sqrt(D) is applied at the end)
+    }
+    // dV^T[e][key] += dO^T P, dK^T[e][key] += Q^T dS (the 1/sqrt(D) is applied at the end)
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const SlotPair pf = pack_slots(p[2 * mm], p[2 * mm + 1]);
-        const SlotPair sf = pack_slots(ds[2 * mm], ds[2 * mm + 1]);
+    for (int mm = 0; mm < 2; ++mm) {
+      const SlotPair pf = pack_slots(p[2 * mm], p[2 * mm + 1]);
+      const SlotPair sf = pack_slots(ds[2 * mm], ds[2 * mm + 1]);
 #pragma unroll
-        for (int eb = 0; eb < EB; ++eb) {
-          dv[eb] = mma2(Tile<D>::col8(dotile, mm, 16 * eb, lane), pf, dv[eb]);
-          dk[eb] = mma2(Tile<D>::col8(qtile, mm, 16 * eb, lane), sf, dk[eb]);
-        }
+      for (int eb = 0; eb < EB; ++eb) {
+        dv[eb] = mma2(Tile<D>::col8(dotile, mm, 16 * eb, lane), pf, dv[eb]);
+        dk[eb] = mma2(Tile<D>::col8(qtile, mm, 16 * eb, lane), sf, dk[eb]);
       }
     }
   }
   if (key < dm.seq) {
-    bf16_t* krow = dqkv + (t0 + key) * dm.ld + kcol;
-    bf16_t* vrow = dqkv + (t0 + key) * dm.ld + vcol;
+    if (dm.group == 1) {
+      bf16_t* krow = dqkv + (t0 + key) * dm.ld + kcol;
+      bf16_t* vrow = dqkv + (t0 + key) * dm.ld + vcol;
 #pragma unroll
-    for (int eb = 0; eb < EB; ++eb) {
-      store4<bf16_t>(krow + 16 * eb + 4 * g, dk[eb] * dm.scale);
-      store4<bf16_t>(vrow + 16 * eb + 4 * g, dv[eb]);
+      for (int eb = 0; eb < EB; ++eb) {
+        store4<bf16_t>(krow + 16 * eb + 4 * g, dk[eb] * dm.scale);
+        store4<bf16_t>(vrow + 16 * eb + 4 * g, dv[eb]);
+      }
+    } else {
+      float* row = part + (((int64_t)(hq % dm.group) * T + t0 + key) * dm.n_kv + kvh) * (2 * D);
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb) {
+        store4<float>(row + 16 * eb + 4 * g, dk[eb] * dm.scale);
+        store4<float>(row + D + 16 * eb + 4 * g, dv[eb]);
+      }
     }
   }
+}
+
+// dqkv's K and V columns = the group's shares of part added in order.
+template <int D>
+__global__ __launch_bounds__(256) void attn_reduce_kernel(const float* __restrict__ part, bf16_t* __restrict__ dqkv,
+                                                          AttnDims dm) {
+  const int64_t T = dm.batch * dm.seq;
+  const int64_t n4 = T * dm.n_kv * (2 * D) / 4;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const int64_t e4 = i * 4;  // element of a [T][n_kv][2 D] share
+  const int64_t t = e4 / (dm.n_kv * 2 * D);
+  const int rem = (int)(e4 % (dm.n_kv * 2 * D));
+  const int kvh = rem / (2 * D), e = rem % (2 * D);
+  floatx4 acc = load4<float>(part + e4);
+  for (int j = 1; j < dm.group; ++j) acc += load4<float>(part + (int64_t)j * T * dm.n_kv * 2 * D + e4);
+  const int64_t col = e < D ? (int64_t)(dm.n_q + kvh) * D + e : (int64_t)(dm.n_q + dm.n_kv + kvh) * D + (e - D);
+  store4<bf16_t>(dqkv + t * dm.ld + col, acc);
 }
 
 // dQ of 64 queries of one head: every key block up to the query block.
@@ -353,11 +420,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dq_kernel(const bf16_t* __r
 #pragma unroll
   for (int i = 0; i < EB; ++i) dq[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int64_t kcol = (int64_t)(dm.n_q + kvh) * D, vcol = (int64_t)(dm.n_q + dm.n_kv + kvh) * D;
+  const bf16_t* src = qkv + t0 * dm.ld;
+  typename Tile<D>::Regs kr, vr;
+  Tile<D>::fetch(kr, src, dm.ld, 0, dm.seq, kcol, tid);
+  Tile<D>::fetch(vr, src, dm.ld, 0, dm.seq, vcol, tid);
   for (int kb = 0; kb <= qb; ++kb) {
     __syncthreads();
-    Tile<D>::load(ktile, qkv + t0 * dm.ld, dm.ld, (int64_t)kb * kAttnBlock, dm.seq, kcol, tid);
-    Tile<D>::load(vtile, qkv + t0 * dm.ld, dm.ld, (int64_t)kb * kAttnBlock, dm.seq, vcol, tid);
+    Tile<D>::store(ktile, kr, tid);
+    Tile<D>::store(vtile, vr, tid);
     __syncthreads();
+    if (kb + 1 <= qb) {
+      Tile<D>::fetch(kr, src, dm.ld, (int64_t)(kb + 1) * kAttnBlock, dm.seq, kcol, tid);
+      Tile<D>::fetch(vr, src, dm.ld, (int64_t)(kb + 1) * kAttnBlock, dm.seq, vcol, tid);
+    }
     // S^T[key][q], dP^T[key][q]; lane: key = 16 kk + 4 g + r, q = c
     floatx4 ds[4];
 #pragma unroll
@@ -417,10 +492,12 @@ hipError_t fwd_t(const AttnShapeArgs& a, const void* qkv, void* O, float* lse, h
 
 template <int D>
 hipError_t bwd_t(const AttnShapeArgs& a, const void* qkv, const void* O, const void* dO, const float* lse,
-                 float* delta, void* dqkv, hipStream_t s) {
+                 void* workspace, void* dqkv, hipStream_t s) {
   const AttnDims dm = make_dims(a);
   const int64_t T = a.batch * a.seq;
   const int nb = (int)((a.seq + kAttnBlock - 1) / kAttnBlock);
+  float* delta = static_cast<float*>(workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + attention_delta_bytes(a));
   {
     KernelTimer timer("attention_delta", s);
     const int64_t n = T * a.n_q;
@@ -431,8 +508,16 @@ hipError_t bwd_t(const AttnShapeArgs& a, const void* qkv, const void* O, const v
   }
   {
     KernelTimer timer("attention_bwd_dkdv", s);
-    hipLaunchKernelGGL(attn_dkdv_kernel<D>, dim3(nb * a.n_kv * (int)a.batch), dim3(kAttnThreads), 0, s,
+    hipLaunchKernelGGL(attn_dkdv_kernel<D>, dim3(nb * a.n_q * (int)a.batch), dim3(kAttnThreads), 0, s,
                        static_cast<const bf16_t*>(qkv), static_cast<const bf16_t*>(dO), lse, delta,
+                       static_cast<bf16_t*>(dqkv), part, dm);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (dm.group > 1) {
+    KernelTimer timer("attention_bwd_reduce", s);
+    const int64_t n4 = T * a.n_kv * 2 * D / 4;
+    hipLaunchKernelGGL(attn_reduce_kernel<D>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, part,
                        static_cast<bf16_t*>(dqkv), dm);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -453,11 +538,20 @@ hipError_t launch_attention_fwd(const AttnShapeArgs& a, const void* qkv, void* O
   return hipErrorInvalidValue;
 }
 
+size_t attention_delta_bytes(const AttnShapeArgs& a) {
+  return ((size_t)a.n_q * (size_t)(a.batch * a.seq) * sizeof(float) + 255) / 256 * 256;
+}
+
+size_t attention_bwd_workspace(const AttnShapeArgs& a) {
+  const size_t part = a.n_q == a.n_kv ? 0 : (size_t)a.n_q * (size_t)(a.batch * a.seq) * 2 * a.head_dim * sizeof(float);
+  return attention_delta_bytes(a) + part;
+}
+
 hipError_t launch_attention_bwd(const AttnShapeArgs& a, const void* qkv, const void* O, const void* dO,
-                                const float* lse, float* delta, void* dqkv, hipStream_t s) {
+                                const float* lse, void* workspace, void* dqkv, hipStream_t s) {
   if (a.batch == 0 || a.seq == 0) return hipSuccess;
-  if (a.head_dim == 64) return bwd_t<64>(a, qkv, O, dO, lse, delta, dqkv, s);
-  if (a.head_dim == 128) return bwd_t<128>(a, qkv, O, dO, lse, delta, dqkv, s);
+  if (a.head_dim == 64) return bwd_t<64>(a, qkv, O, dO, lse, workspace, dqkv, s);
+  if (a.head_dim == 128) return bwd_t<128>(a, qkv, O, dO, lse, workspace, dqkv, s);
   return hipErrorInvalidValue;
 }
 

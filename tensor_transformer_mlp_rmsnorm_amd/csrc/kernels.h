@@ -113,9 +113,13 @@ struct AttnShapeArgs {
 };
 // O [T, n_q D] bf16, lse [n_q, T] fp32.
 hipError_t launch_attention_fwd(const AttnShapeArgs& a, const void* qkv, void* O, float* lse, hipStream_t s);
-// dqkv [T, ld] bf16 (every Q, K and V column written); delta: [n_q, T] fp32 scratch.
+// dqkv [T, ld] bf16 (every Q, K and V column written).  workspace (16-byte
+// aligned, attention_bwd_workspace bytes): delta [n_q, T] fp32, padded to 256
+// bytes, then (n_q > n_kv only) the per-head dK/dV shares [group][T][n_kv][2 D] fp32.
+size_t attention_delta_bytes(const AttnShapeArgs& a);
+size_t attention_bwd_workspace(const AttnShapeArgs& a);
 hipError_t launch_attention_bwd(const AttnShapeArgs& a, const void* qkv, const void* O, const void* dO,
-                                const float* lse, float* delta, void* dqkv, hipStream_t s);
+                                const float* lse, void* workspace, void* dqkv, hipStream_t s);
 
 hipError_t launch_rmsnorm_fwd(DType dt, const void* x, const void* w, void* n, float* rstd,
                               int64_t T, int64_t H, float eps, hipStream_t s);

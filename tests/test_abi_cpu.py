@@ -359,4 +359,12 @@ def test_attention_checks(lib):
     assert bare(1, 8, 2, 1, 32, A, 256, A, A, None) == L.ESHAPE          # head_dim
     assert bare(0, 8, 2, 1, 64, None, 256, None, None, None) == L.OK     # empty
     bb = lib.tp_attention_backward
-    assert bb(1, 8, 2, 1, 64, A, 256, A, A, A, None, A, None) == L.EINVAL   # delta scratch missing
+    wsb = lib.tp_attention_backward_workspace_bytes
+    assert wsb(1, 8, 2, 2, 64) >= 2 * 8 * 4                    # delta [n_q, T]
+    assert wsb(1, 8, 2, 1, 64) >= wsb(1, 8, 2, 2, 64) + 2 * 8 * 2 * 64 * 4   # + per-head dK/dV shares
+    assert wsb(1, 8, 0, 1, 64) == 0
+    need_b = wsb(1, 8, 2, 1, 64)
+    assert bb(1, 8, 2, 1, 64, A, 256, A, A, A, None, need_b, A, None) == L.EWORKSPACE   # workspace missing
+    assert bb(1, 8, 2, 1, 64, A, 256, A, A, A, A, need_b - 4, A, None) == L.EWORKSPACE  # too small
+    assert bb(1, 8, 2, 1, 64, A, 256, A, A, A, MIS, need_b, A, None) == L.EALIGN
+    assert bb(0, 8, 2, 1, 64, None, 256, None, None, None, None, 0, None, None) == L.OK  # empty

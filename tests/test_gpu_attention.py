@@ -89,9 +89,10 @@ def test_attention_kernels_match_oracle(case):
     dq, dk, dv = A.causal_attention_bwd(q, k, v, A.split_heads(O_st, nq, sh), A.split_heads(dO, nq, sh), sh.group)
     dqkv_ref = np.concatenate([A.merge_heads(dq, sh), A.merge_heads(dk, sh), A.merge_heads(dv, sh)], axis=1)
     dqkv = torch.full((T, ld), 7.0, dtype=torch.bfloat16, device="cuda")
-    delta = torch.empty(nq * T, dtype=torch.float32, device="cuda")
+    wsb = L.tp_attention_backward_workspace_bytes(b, s, nq, nkv, D)
+    ws = torch.full((wsb,), 0x7f, dtype=torch.uint8, device="cuda")  # garbage: every byte read is written first
     L.tp_attention_backward(b, s, nq, nkv, D, qkv_d, ld, _bf(O_st).cuda(), _bf(dO).cuda(),
-                            torch.from_numpy(lse_flat.astype(np.float32)).cuda(), delta, dqkv)
+                            torch.from_numpy(lse_flat.astype(np.float32)).cuda(), ws, wsb, dqkv)
     torch.cuda.synchronize()
     got = dqkv.cpu()
     check("dQ", got[:, :nq * D], dqkv_ref[:, :nq * D], "bf16", rowwise=True, report=report)
