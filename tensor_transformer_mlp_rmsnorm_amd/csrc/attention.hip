@@ -43,8 +43,14 @@ namespace {
 
 constexpr int kAttnBlock = 64, kAttnThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+// The forward's running maximum is raised (and the partial output rescaled)
+// only when a score exceeds it by more than this many powers of two, so the
+// probabilities formed against it stay below 2^8.
+constexpr float kLazyRescale = 8.0f;
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ floatx4 mma(const uint4& x, const uint4& y, floatx4 acc) {
@@ -52,12 +58,39 @@ __device__ __forceinline__ floatx4 mma(const uint4& x, const uint4& y, floatx4 a
                                                  0, 0, 0);
 }
 
-// A [64][D] bf16 tile in LDS, 16-byte chunks XOR-swizzled by row.
+// 2^x with the hardware instruction: the arguments here are <= 8 (or -inf),
+// and results below 2^-126 are negligible next to the row's largest term.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two fp32 values as bf16 (round to nearest even), the first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{a, b}, bf16x2));
+}
+
+template <typename T>
+struct Flag {
+  static constexpr bool value = T::value;
+};
+struct Masked {
+  static constexpr bool value = true;
+};
+struct Unmasked {
+  static constexpr bool value = false;
+};
+
+// A [64][D] bf16 tile in LDS, 16-byte chunks XOR-swizzled by row with
+// swz(r) = 2 (r mod K/2) + (r / (K/2) mod 2), K = D / 8 chunks per row: the 8
+// rows of a row read (8 lanes, one chunk each) land on 8 distinct chunk
+// positions, and so do the 4 rows x 2 adjacent chunks of a 16-lane transpose
+// read (swz(r) / 2 differs between any 4 consecutive rows).
 template <int D>
 struct Tile {
   static constexpr int kChunks = D / 8;  // 16-byte chunks per row
+  __device__ __forceinline__ static int swz(int row) {
+    return 2 * (row & (kChunks / 2 - 1)) | ((row / (kChunks / 2)) & 1);
+  }
   __device__ __forceinline__ static int chunk_off(int row, int chunk) {
-    return (row * kChunks + (chunk ^ (row & (kChunks - 1)))) * 16;
+    return (row * kChunks + (chunk ^ swz(row))) * 16;
   }
   // Row `row`, elements 8 c .. 8 c + 7.
   __device__ __forceinline__ static uint4 row8(const char* base, int row, int c) {
@@ -84,18 +117,6 @@ struct Tile {
   struct Regs {
     uint4 v[kPer];
   };
-  // Global rows r0 .. r0 + 63 (ld elements apart), columns col0 .. col0 + D - 1;
-  // rows at or past `rows` are zero.
-  __device__ __forceinline__ static void fetch(Regs& r, const bf16_t* src, int64_t ld, int64_t r0, int64_t rows,
-                                               int64_t col0, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = tid + kAttnThreads * i;
-      const int row = idx / kChunks, c = idx % kChunks;
-      r.v[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (r0 + row < rows) r.v[i] = *reinterpret_cast<const uint4*>(src + (r0 + row) * ld + col0 + 8 * c);
-    }
-  }
   __device__ __forceinline__ static void store(char* base, const Regs& r, int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -105,30 +126,84 @@ struct Tile {
   }
 };
 
+// One thread's share of the 64-row tiles of a [rows, ld] bf16 matrix at
+// columns col0 .. col0 + D - 1 (element offsets fit 32 bits: the callers hold
+// fewer than 2^31 elements).
+template <int D>
+struct TileSrc {
+  static constexpr int kPer = Tile<D>::kPer;
+  static constexpr int kRowStep = kAttnThreads / Tile<D>::kChunks;  // rows between a thread's chunks
+  const bf16_t* base;
+  uint32_t ld_tile;  // 64 rows, in elements
+  uint32_t step;     // kRowStep rows, in elements
+  uint32_t off0;     // this thread's first chunk within a tile
+  int row0;
+  __device__ __forceinline__ TileSrc(const bf16_t* p, int64_t ld, int64_t col0, int tid) : base(p + col0) {
+    ld_tile = (uint32_t)(kAttnBlock * ld);
+    step = (uint32_t)(kRowStep * ld);
+    row0 = tid / Tile<D>::kChunks;
+    off0 = (uint32_t)(row0 * ld + 8 * (tid % Tile<D>::kChunks));
+  }
+  // Tile `blk` (rows 64 blk ..); rows at or past `rows` are zero.
+  __device__ __forceinline__ void fetch(typename Tile<D>::Regs& r, int blk, int64_t rows) const {
+    const bf16_t* p = base + (size_t)blk * ld_tile;
+    const int64_t left = rows - (int64_t)blk * kAttnBlock;
+    if (left >= kAttnBlock) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) r.v[i] = *reinterpret_cast<const uint4*>(p + off0 + i * step);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        r.v[i] = row0 + i * kRowStep < left ? *reinterpret_cast<const uint4*>(p + off0 + i * step)
+                                            : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+};
+
 // The lane's 8 k-slot values of one 32-row step m from its two 16-row blocks
-// (block 2m: slots 0-3, block 2m + 1: slots 4-7) as two bf16 operands whose
-// sum carries the fp32 value to 2^-17: hi = bf16(v), lo = bf16(v - hi).  P and
-// dS are the only product operands formed inside the kernels (Q, K, V and dO
-// are bf16 tensors already); two MFMAs on the same other operand keep their
-// products at fp32-like precision, as the oracle's exact probabilities.
+// (block 2m: slots 0-3, block 2m + 1: slots 4-7) as one bf16 operand.
+__device__ __forceinline__ uint4 pack_slots1(const floatx4& b0, const floatx4& b1) {
+  return make_uint4(pack_bf16x2(b0[0], b0[1]), pack_bf16x2(b0[2], b0[3]), pack_bf16x2(b1[0], b1[1]),
+                    pack_bf16x2(b1[2], b1[3]));
+}
+
+// The same as two bf16 operands whose sum carries the fp32 value to 2^-17:
+// hi = bf16(v), lo = bf16(v - hi).  The score gradients dS are multiplied this
+// way: their sum over keys cancels (it is zero up to rounding for every
+// query), so a single bf16 rounding of each term would dominate dQ and dK.
 struct SlotPair {
   uint4 hi, lo;
 };
+__device__ __forceinline__ float lo_half(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi_half(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ SlotPair pack_slots(const floatx4& b0, const floatx4& b1) {
-  float v[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
-    const bf16_t l0 = f32_to_bf16(v[2 * i] - bf16_to_f32(h0)), l1 = f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1));
-    h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    l[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-  }
-  return SlotPair{make_uint4(h[0], h[1], h[2], h[3]), make_uint4(l[0], l[1], l[2], l[3])};
+  const uint4 hi = pack_slots1(b0, b1);
+  const floatx4 r0 = {b0[0] - lo_half(hi.x), b0[1] - hi_half(hi.x), b0[2] - lo_half(hi.y), b0[3] - hi_half(hi.y)};
+  const floatx4 r1 = {b1[0] - lo_half(hi.z), b1[1] - hi_half(hi.z), b1[2] - lo_half(hi.w), b1[3] - hi_half(hi.w)};
+  return SlotPair{hi, pack_slots1(r0, r1)};
 }
 
 __device__ __forceinline__ floatx4 mma2(const uint4& x, const SlotPair& y, floatx4 acc) {
   return mma(x, y.lo, mma(x, y.hi, acc));
+}
+
+// max / sum of the four lanes l, l ^ 16, l ^ 32, l ^ 48 (gfx950 lane swaps:
+// each returns the value and its partner's, one of them the lane's own).
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 struct AttnDims {
@@ -138,20 +213,36 @@ struct AttnDims {
   float scale;                  // 1 / sqrt(D)
 };
 
-// blockIdx -> (block index, head, batch), the block index descending so that
-// the longest causal rows start first.
-__device__ __forceinline__ void block_coords(int nblocks, int heads, int batch, int& blk, int& head, int& b) {
-  const int x = blockIdx.x, per = heads * batch;
-  blk = nblocks - 1 - x / per;
-  head = (x % per) / batch;
-  b = x % batch;
+// Workgroups in order of decreasing work: the first half of the grid takes
+// ranks 0, 1, ... (the heaviest first), the second half ranks n - 1, n - 2, ...
+// (the lightest first).  A grid that fits on the chip at once is placed
+// round-robin over the compute units, so workgroups x and x + n / 2 tend to
+// share one and their causal work adds up to about the same on every unit.
+__device__ __forceinline__ int work_rank(int n) {
+  const int x = blockIdx.x, half = (n + 1) / 2;
+  return x < half ? x : n - 1 - (x - half);
 }
 
+// Rank -> (block index, head, batch) with the block index descending.
+__device__ __forceinline__ void block_coords(int nblocks, int heads, int batch, int& blk, int& head, int& b) {
+  const int per = heads * batch, r = work_rank(nblocks * per);
+  blk = nblocks - 1 - r / per;
+  head = (r % per) / batch;
+  b = r % batch;
+}
+
+// Forward: 64 queries of one head per workgroup, wave w owning queries
+// 16 w .. 16 w + 15; key blocks 0 .. qb, the last one (the diagonal, which
+// also holds any keys past the sequence end) with the causal mask.  K and V
+// tiles are double-buffered in LDS: block kb stores tile kb + 1 (loaded into
+// registers during block kb - 1) into the other buffer, starts the loads of
+// tile kb + 2, multiplies tile kb, and ends with the one barrier per block.
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O,
-                                                                float* __restrict__ lse, AttnDims dm) {
-  __shared__ __align__(16) char ktile[kAttnBlock * D * 2];
-  __shared__ __align__(16) char vtile[kAttnBlock * D * 2];
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(const bf16_t* __restrict__ qkv,
+                                                                   bf16_t* __restrict__ O, float* __restrict__ lse,
+                                                                   AttnDims dm) {
+  __shared__ __align__(16) char ktile[2][kAttnBlock * D * 2];
+  __shared__ __align__(16) char vtile[2][kAttnBlock * D * 2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
   const int nqb = (int)((dm.seq + kAttnBlock - 1) / kAttnBlock);
   int qb, h, b;
@@ -169,61 +260,80 @@ __global__ __launch_bounds__(kAttnThreads) void attn_fwd_kernel(const bf16_t* __
 #pragma unroll
   for (int i = 0; i < EB; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.0f;
-  const int64_t kcol = (int64_t)(dm.n_q + kvh) * D, vcol = (int64_t)(dm.n_q + dm.n_kv + kvh) * D;
-  const int nkb = qb + 1;  // key blocks 0 .. qb hold every key <= a query of this block
   const bf16_t* src = qkv + t0 * dm.ld;
+  const TileSrc<D> ks_src(src, dm.ld, (int64_t)(dm.n_q + kvh) * D, tid);
+  const TileSrc<D> vs_src(src, dm.ld, (int64_t)(dm.n_q + dm.n_kv + kvh) * D, tid);
   typename Tile<D>::Regs kr, vr;
-  Tile<D>::fetch(kr, src, dm.ld, 0, dm.seq, kcol, tid);
-  Tile<D>::fetch(vr, src, dm.ld, 0, dm.seq, vcol, tid);
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();  // the previous tiles are no longer read
-    Tile<D>::store(ktile, kr, tid);
-    Tile<D>::store(vtile, vr, tid);
-    __syncthreads();
-    if (kb + 1 < nkb) {  // the next tiles load while these are multiplied
-      Tile<D>::fetch(kr, src, dm.ld, (int64_t)(kb + 1) * kAttnBlock, dm.seq, kcol, tid);
-      Tile<D>::fetch(vr, src, dm.ld, (int64_t)(kb + 1) * kAttnBlock, dm.seq, vcol, tid);
+  ks_src.fetch(kr, 0, dm.seq);
+  vs_src.fetch(vr, 0, dm.seq);
+  Tile<D>::store(ktile[0], kr, tid);
+  Tile<D>::store(vtile[0], vr, tid);
+  if (qb > 0) {
+    ks_src.fetch(kr, 1, dm.seq);
+    vs_src.fetch(vr, 1, dm.seq);
+  }
+  __syncthreads();
+  auto block = [&](int kb, auto mask) {
+    constexpr bool MASK = Flag<decltype(mask)>::value;
+    const int buf = kb & 1;
+    if (kb < qb) {  // tile kb + 1 into the other buffer, whose last reader was block kb - 1
+      Tile<D>::store(ktile[buf ^ 1], kr, tid);
+      Tile<D>::store(vtile[buf ^ 1], vr, tid);
+      if (kb + 1 < qb) {
+        ks_src.fetch(kr, kb + 2, dm.seq);
+        vs_src.fetch(vr, kb + 2, dm.seq);
+      }
     }
+    const char* kt = ktile[buf];
+    const char* vt = vtile[buf];
+    // S^T[key][q]; lane: key = 16 kk + 4 g + r, q = c
     floatx4 s[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       s[kk] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[kk] = mma(Tile<D>::row8(ktile, 16 * kk + c, 4 * ks + g), qf[ks], s[kk]);
+      for (int ks = 0; ks < KS; ++ks) s[kk] = mma(Tile<D>::row8(kt, 16 * kk + c, 4 * ks + g), qf[ks], s[kk]);
     }
-    float bmax = -INFINITY;
+    if constexpr (MASK) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kb * kAttnBlock + 16 * kk + 4 * g + r;
+          if (!(key <= q && key < dm.seq)) s[kk][r] = -INFINITY;
+        }
+    }
+    float bmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    bmax = fmaxf(bmax, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
+                             fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
+    bmax = max_xor32(max_xor16(bmax)) * dm.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(bmax > m + kLazyRescale)) {  // m = -inf on the first block
+      const float mnew = fmaxf(m, bmax);
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < EB; ++i) acc[i] *= alpha;
+    }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = kb * kAttnBlock + 16 * kk + 4 * g + r;
-        s[kk][r] = (key <= q && key < dm.seq) ? s[kk][r] * dm.scale_log2 : -INFINITY;
-        bmax = fmaxf(bmax, s[kk][r]);
-      }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, kWave));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, kWave));
-    const float mnew = fmaxf(m, bmax);
-    const float alpha = exp2f(m - mnew);  // m = -inf on the first block: alpha = 0
-    m = mnew;
-    lsum *= alpha;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[kk][r] = exp2f(s[kk][r] - mnew);
+        s[kk][r] = fast_exp2(__builtin_fmaf(s[kk][r], dm.scale_log2, -m));
         lsum += s[kk][r];
       }
-#pragma unroll
-    for (int i = 0; i < EB; ++i) acc[i] *= alpha;
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) {
       const SlotPair pf = pack_slots(s[2 * mm], s[2 * mm + 1]);
 #pragma unroll
-      for (int eb = 0; eb < EB; ++eb) acc[eb] = mma2(Tile<D>::col8(vtile, mm, 16 * eb, lane), pf, acc[eb]);
+      for (int eb = 0; eb < EB; ++eb) acc[eb] = mma2(Tile<D>::col8(vt, mm, 16 * eb, lane), pf, acc[eb]);
     }
-  }
-  lsum += __shfl_xor(lsum, 16, kWave);
-  lsum += __shfl_xor(lsum, 32, kWave);
+    __syncthreads();  // tile kb is read; tile kb + 1 is stored
+  };
+  for (int kb = 0; kb < qb; ++kb) block(kb, Unmasked{});
+  block(qb, Masked{});
+  lsum = sum_xor32(sum_xor16(lsum));
   if (q < dm.seq) {
     const float inv = 1.0f / lsum;
     bf16_t* dst = O + (t0 + q) * dm.ldo + (int64_t)h * D;
@@ -257,25 +367,28 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const bf16_t* __restric
 
 // dK and dV of 64 keys from one query head (one workgroup per key block,
 // query head and sequence; the key blocks with the most query blocks after
-// them are dispatched first): every query block at or after the key block.
-// Wave w owns keys 16 w .. 16 w + 15.  With one query head per KV head the
-// result goes to dqkv; otherwise each head's share goes to
+// them are dispatched first): every query block at or after the key block,
+// the first (the diagonal) and the last (which may end past the sequence)
+// with the masks.  Wave w owns keys 16 w .. 16 w + 15.  With one query head
+// per KV head the result goes to dqkv; otherwise each head's share goes to
 // part[h % group][t][kv head][2 D] (fp32, dK then dV) and attn_reduce_kernel
 // adds the group's shares in order.
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_dkdv_kernel(const bf16_t* __restrict__ qkv,
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_dkdv_kernel(const bf16_t* __restrict__ qkv,
                                                                  const bf16_t* __restrict__ dO,
                                                                  const float* __restrict__ lse,
                                                                  const float* __restrict__ delta,
                                                                  bf16_t* __restrict__ dqkv, float* __restrict__ part,
                                                                  AttnDims dm) {
-  __shared__ __align__(16) char qtile[kAttnBlock * D * 2];
-  __shared__ __align__(16) char dotile[kAttnBlock * D * 2];
-  __shared__ float lse2_s[kAttnBlock], delta_s[kAttnBlock];
+  __shared__ __align__(16) char qtile[2][kAttnBlock * D * 2];
+  __shared__ __align__(16) char dotile[2][kAttnBlock * D * 2];
+  __shared__ __align__(16) float lse2_s[2][kAttnBlock];
+  __shared__ __align__(16) float delta_s[2][kAttnBlock];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
   const int nkb = (int)((dm.seq + kAttnBlock - 1) / kAttnBlock);
   const int per = dm.n_q * (int)dm.batch;
-  const int kb = blockIdx.x / per, hq = (blockIdx.x % per) / (int)dm.batch, b = blockIdx.x % (int)dm.batch;
+  const int rank = work_rank(nkb * per);  // key block ascending: the heaviest first
+  const int kb = rank / per, hq = (rank % per) / (int)dm.batch, b = rank % (int)dm.batch;
   const int kvh = hq / dm.group;
   const int64_t t0 = (int64_t)b * dm.seq, T = dm.batch * dm.seq;
   const int key = kb * kAttnBlock + 16 * w + c;  // this lane's key (Y-operand row)
@@ -294,31 +407,44 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dkdv_kernel(const bf16_t* _
 #pragma unroll
   for (int i = 0; i < EB; ++i) dk[i] = dv[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int nqb = nkb;
-  const bf16_t* qsrc = qkv + t0 * dm.ld;
-  const bf16_t* dsrc = dO + t0 * dm.ldo;
+  const TileSrc<D> q_src(qkv + t0 * dm.ld, dm.ld, (int64_t)hq * D, tid);
+  const TileSrc<D> d_src(dO + t0 * dm.ldo, dm.ldo, (int64_t)hq * D, tid);
+  const float* lse_h = lse + (int64_t)hq * T + t0;
+  const float* delta_h = delta + (int64_t)hq * T + t0;
   typename Tile<D>::Regs qr, dr;
   float lr = 0.0f, dl = 0.0f;
   auto fetch = [&](int qb) {
-    Tile<D>::fetch(qr, qsrc, dm.ld, (int64_t)qb * kAttnBlock, dm.seq, (int64_t)hq * D, tid);
-    Tile<D>::fetch(dr, dsrc, dm.ldo, (int64_t)qb * kAttnBlock, dm.seq, (int64_t)hq * D, tid);
+    q_src.fetch(qr, qb, dm.seq);
+    d_src.fetch(dr, qb, dm.seq);
     if (tid < kAttnBlock) {
       const int qq = qb * kAttnBlock + tid;
       const bool ok = qq < dm.seq;
-      lr = ok ? lse[(int64_t)hq * T + t0 + qq] * kLog2e : 0.0f;
-      dl = ok ? delta[(int64_t)hq * T + t0 + qq] : 0.0f;
+      lr = ok ? lse_h[qq] * kLog2e : 0.0f;
+      dl = ok ? delta_h[qq] : 0.0f;
     }
   };
-  fetch(kb);
-  for (int qb = kb; qb < nqb; ++qb) {
-    __syncthreads();
-    Tile<D>::store(qtile, qr, tid);
-    Tile<D>::store(dotile, dr, tid);
+  auto stash = [&](int buf) {
+    Tile<D>::store(qtile[buf], qr, tid);
+    Tile<D>::store(dotile[buf], dr, tid);
     if (tid < kAttnBlock) {
-      lse2_s[tid] = lr;
-      delta_s[tid] = dl;
+      lse2_s[buf][tid] = lr;
+      delta_s[buf][tid] = dl;
     }
-    __syncthreads();
-    if (qb + 1 < nqb) fetch(qb + 1);
+  };
+  // Query blocks kb .. nqb - 1, double-buffered as in the forward.
+  fetch(kb);
+  stash(0);
+  if (kb + 1 < nqb) fetch(kb + 1);
+  __syncthreads();
+  auto block = [&](int qb, auto mask) {
+    constexpr bool MASK = Flag<decltype(mask)>::value;
+    const int buf = (qb - kb) & 1;
+    if (qb + 1 < nqb) {
+      stash(buf ^ 1);
+      if (qb + 2 < nqb) fetch(qb + 2);
+    }
+    const char* qt = qtile[buf];
+    const char* dt = dotile[buf];
     // S[q][key] and dP[q][key] for the block's 4 x 16 queries; lane: q = 16 qq + 4 g + r, key = c
     floatx4 p[4], ds[4];
 #pragma unroll
@@ -326,30 +452,38 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dkdv_kernel(const bf16_t* _
       floatx4 sv = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        sv = mma(Tile<D>::row8(qtile, 16 * qq + c, 4 * ks + g), kf[ks], sv);
-        dp = mma(Tile<D>::row8(dotile, 16 * qq + c, 4 * ks + g), vf[ks], dp);
+        sv = mma(Tile<D>::row8(qt, 16 * qq + c, 4 * ks + g), kf[ks], sv);
+        dp = mma(Tile<D>::row8(dt, 16 * qq + c, 4 * ks + g), vf[ks], dp);
       }
+      const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse2_s[buf][16 * qq + 4 * g]);
+      const floatx4 d4 = *reinterpret_cast<const floatx4*>(&delta_s[buf][16 * qq + 4 * g]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int ql = 16 * qq + 4 * g + r, qpos = qb * kAttnBlock + ql;
-        const bool ok = key <= qpos && qpos < dm.seq && key < dm.seq;
-        const float pv = ok ? exp2f(sv[r] * dm.scale_log2 - lse2_s[ql]) : 0.0f;
+        float pv = fast_exp2(__builtin_fmaf(sv[r], dm.scale_log2, -l4[r]));
+        if constexpr (MASK) {
+          const int qpos = qb * kAttnBlock + 16 * qq + 4 * g + r;
+          if (!(key <= qpos && qpos < dm.seq && key < dm.seq)) pv = 0.0f;
+        }
         p[qq][r] = pv;
-        ds[qq][r] = pv * (dp[r] - delta_s[ql]);
+        ds[qq][r] = pv * (dp[r] - d4[r]);
       }
     }
     // dV^T[e][key] += dO^T P, dK^T[e][key] += Q^T dS (the 1/sqrt(D) is applied at the end)
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) {
-      const SlotPair pf = pack_slots(p[2 * mm], p[2 * mm + 1]);
+      const uint4 pf = pack_slots1(p[2 * mm], p[2 * mm + 1]);
       const SlotPair sf = pack_slots(ds[2 * mm], ds[2 * mm + 1]);
 #pragma unroll
       for (int eb = 0; eb < EB; ++eb) {
-        dv[eb] = mma2(Tile<D>::col8(dotile, mm, 16 * eb, lane), pf, dv[eb]);
-        dk[eb] = mma2(Tile<D>::col8(qtile, mm, 16 * eb, lane), sf, dk[eb]);
+        dv[eb] = mma(Tile<D>::col8(dt, mm, 16 * eb, lane), pf, dv[eb]);
+        dk[eb] = mma2(Tile<D>::col8(qt, mm, 16 * eb, lane), sf, dk[eb]);
       }
     }
-  }
+    __syncthreads();
+  };
+  block(kb, Masked{});
+  for (int qb = kb + 1; qb < nqb - 1; ++qb) block(qb, Unmasked{});
+  if (kb < nqb - 1) block(nqb - 1, Masked{});
   if (key < dm.seq) {
     if (dm.group == 1) {
       bf16_t* krow = dqkv + (t0 + key) * dm.ld + kcol;
@@ -388,15 +522,16 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(const float* __restric
   store4<bf16_t>(dqkv + t * dm.ld + col, acc);
 }
 
-// dQ of 64 queries of one head: every key block up to the query block.
+// dQ of 64 queries of one head: every key block up to the query block, the
+// last (the diagonal) with the masks.
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
                                                                const bf16_t* __restrict__ dO,
                                                                const float* __restrict__ lse,
                                                                const float* __restrict__ delta,
                                                                bf16_t* __restrict__ dqkv, AttnDims dm) {
-  __shared__ __align__(16) char ktile[kAttnBlock * D * 2];
-  __shared__ __align__(16) char vtile[kAttnBlock * D * 2];
+  __shared__ __align__(16) char ktile[2][kAttnBlock * D * 2];
+  __shared__ __align__(16) char vtile[2][kAttnBlock * D * 2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
   const int nqb = (int)((dm.seq + kAttnBlock - 1) / kAttnBlock);
   int qb, h, b;
@@ -419,35 +554,50 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dq_kernel(const bf16_t* __r
   floatx4 dq[EB];
 #pragma unroll
   for (int i = 0; i < EB; ++i) dq[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const int64_t kcol = (int64_t)(dm.n_q + kvh) * D, vcol = (int64_t)(dm.n_q + dm.n_kv + kvh) * D;
   const bf16_t* src = qkv + t0 * dm.ld;
+  const TileSrc<D> ks_src(src, dm.ld, (int64_t)(dm.n_q + kvh) * D, tid);
+  const TileSrc<D> vs_src(src, dm.ld, (int64_t)(dm.n_q + dm.n_kv + kvh) * D, tid);
   typename Tile<D>::Regs kr, vr;
-  Tile<D>::fetch(kr, src, dm.ld, 0, dm.seq, kcol, tid);
-  Tile<D>::fetch(vr, src, dm.ld, 0, dm.seq, vcol, tid);
-  for (int kb = 0; kb <= qb; ++kb) {
-    __syncthreads();
-    Tile<D>::store(ktile, kr, tid);
-    Tile<D>::store(vtile, vr, tid);
-    __syncthreads();
-    if (kb + 1 <= qb) {
-      Tile<D>::fetch(kr, src, dm.ld, (int64_t)(kb + 1) * kAttnBlock, dm.seq, kcol, tid);
-      Tile<D>::fetch(vr, src, dm.ld, (int64_t)(kb + 1) * kAttnBlock, dm.seq, vcol, tid);
+  // Key blocks 0 .. qb, double-buffered as in the forward.
+  ks_src.fetch(kr, 0, dm.seq);
+  vs_src.fetch(vr, 0, dm.seq);
+  Tile<D>::store(ktile[0], kr, tid);
+  Tile<D>::store(vtile[0], vr, tid);
+  if (qb > 0) {
+    ks_src.fetch(kr, 1, dm.seq);
+    vs_src.fetch(vr, 1, dm.seq);
+  }
+  __syncthreads();
+  auto block = [&](int kb, auto mask) {
+    constexpr bool MASK = Flag<decltype(mask)>::value;
+    const int buf = kb & 1;
+    if (kb < qb) {
+      Tile<D>::store(ktile[buf ^ 1], kr, tid);
+      Tile<D>::store(vtile[buf ^ 1], vr, tid);
+      if (kb + 1 < qb) {
+        ks_src.fetch(kr, kb + 2, dm.seq);
+        vs_src.fetch(vr, kb + 2, dm.seq);
+      }
     }
+    const char* kt = ktile[buf];
+    const char* vt = vtile[buf];
     // S^T[key][q], dP^T[key][q]; lane: key = 16 kk + 4 g + r, q = c
     floatx4 ds[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
+      floatx4 sv = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = mma(Tile<D>::row8(ktile, 16 * kk + c, 4 * ks + g), qf[ks], s);
-        dp = mma(Tile<D>::row8(vtile, 16 * kk + c, 4 * ks + g), df[ks], dp);
+        sv = mma(Tile<D>::row8(kt, 16 * kk + c, 4 * ks + g), qf[ks], sv);
+        dp = mma(Tile<D>::row8(vt, 16 * kk + c, 4 * ks + g), df[ks], dp);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = kb * kAttnBlock + 16 * kk + 4 * g + r;
-        const bool ok = key <= q && key < dm.seq && qok;
-        const float pv = ok ? exp2f(s[r] * dm.scale_log2 - lse2) : 0.0f;
+        float pv = fast_exp2(__builtin_fmaf(sv[r], dm.scale_log2, -lse2));
+        if constexpr (MASK) {
+          const int key = kb * kAttnBlock + 16 * kk + 4 * g + r;
+          if (!(key <= q && key < dm.seq && qok)) pv = 0.0f;
+        }
         ds[kk][r] = pv * (dp[r] - dl);
       }
     }
@@ -456,9 +606,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_dq_kernel(const bf16_t* __r
     for (int mm = 0; mm < 2; ++mm) {
       const SlotPair sf = pack_slots(ds[2 * mm], ds[2 * mm + 1]);
 #pragma unroll
-      for (int eb = 0; eb < EB; ++eb) dq[eb] = mma2(Tile<D>::col8(ktile, mm, 16 * eb, lane), sf, dq[eb]);
+      for (int eb = 0; eb < EB; ++eb) dq[eb] = mma2(Tile<D>::col8(kt, mm, 16 * eb, lane), sf, dq[eb]);
     }
-  }
+    __syncthreads();
+  };
+  for (int kb = 0; kb < qb; ++kb) block(kb, Unmasked{});
+  block(qb, Masked{});
   if (qok) {
     bf16_t* dst = dqkv + (t0 + q) * dm.ld + (int64_t)h * D;
 #pragma unroll
