@@ -456,7 +456,8 @@ int tp_mlp_backward_fp8(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_ar
  *     out = x + O W_o^T + b_o                     (b_o once, after the partial sum)
  * x is [batch, seq, H] flattened to T = batch * seq rows (a sequence's rows
  * contiguous); causal means key position <= query position within a sequence.
- * bf16 only (fp32 accumulation).  D (head_dim) is 64 or 128.
+ * bf16 only (fp32 accumulation).  D (head_dim) is 64 or 128; seq * W < 2^30
+ * (W defined below; TP_MLP_ESHAPE otherwise).
  */
 typedef struct {
   int64_t batch;     /* sequences */
@@ -529,7 +530,9 @@ size_t tp_attn_workspace_bytes(const tp_attn_desc* d, int32_t phase);
  *   qkv [batch seq, ld] bf16 with the Q, K, V head columns at 0, n_q D and
  *   (n_q + n_kv) D (ld >= (n_q + 2 n_kv) D, a multiple of 8); o and d_o
  *   [batch seq, n_q D] bf16; lse [n_q, batch seq] fp32; d_qkv [batch seq, ld]
- *   bf16 (its first (n_q + 2 n_kv) D columns written).  head_dim 64 or 128.
+ *   bf16 (its first (n_q + 2 n_kv) D columns written).  head_dim 64 or 128;
+ *   seq * ld < 2^30 (TP_MLP_ESHAPE otherwise: the kernels address one
+ *   sequence's rows with 32-bit byte offsets).
  *   workspace: DEVICE scratch, 16-byte aligned, of at least
  *   tp_attention_backward_workspace_bytes(...) bytes (the softmax row terms
  *   rowsum(dO o O) and, when n_q > n_kv, each query head's fp32 share of dK

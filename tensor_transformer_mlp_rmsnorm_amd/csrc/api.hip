@@ -823,6 +823,8 @@ int check_attn_desc(const tp_attn_desc* d, const char* fn) {
   if (rc) return rc;
   if (d->hidden <= 0 || d->hidden % 8 || d->hidden > 16384)
     return fail(TP_MLP_ESHAPE, "%s: hidden must be a positive multiple of 8, <= 16384", fn);
+  if (d->seq * (int64_t)(d->n_q + 2 * d->n_kv) * d->head_dim >= ((int64_t)1 << 30))
+    return fail(TP_MLP_ESHAPE, "%s: one sequence's QKV rows hold 2^30 or more elements", fn);
   if (d->dtype != TP_MLP_BF16) return fail(TP_MLP_EDTYPE, "%s: the attention sublayer takes bf16 tensors", fn);
   if (d->flags & ~(TP_MLP_FUSE_EPILOGUE | TP_MLP_NORMED_READY | TP_MLP_ACCUMULATE_GRADS))
     return fail(TP_MLP_EINVAL, "%s: unknown flags", fn);
@@ -1051,6 +1053,7 @@ int tp_attention_forward(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv, 
   int rc = check_attn_shape(batch, seq, n_q, n_kv, head_dim, fn);
   if (rc) return rc;
   if (ld < (int64_t)(n_q + 2 * n_kv) * head_dim || ld % 8) return fail(TP_MLP_ESHAPE, "%s: bad ld", fn);
+  if (seq * ld >= ((int64_t)1 << 30)) return fail(TP_MLP_ESHAPE, "%s: one sequence holds 2^30 or more elements", fn);
   const int64_t T = batch * seq;
   if (T * ld >= ((int64_t)1 << 31) || T * n_q * head_dim >= ((int64_t)1 << 31))
     return fail(TP_MLP_ESHAPE, "%s: 2^31 or more elements", fn);
@@ -1071,6 +1074,7 @@ int tp_attention_backward(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv,
   int rc = check_attn_shape(batch, seq, n_q, n_kv, head_dim, fn);
   if (rc) return rc;
   if (ld < (int64_t)(n_q + 2 * n_kv) * head_dim || ld % 8) return fail(TP_MLP_ESHAPE, "%s: bad ld", fn);
+  if (seq * ld >= ((int64_t)1 << 30)) return fail(TP_MLP_ESHAPE, "%s: one sequence holds 2^30 or more elements", fn);
   const int64_t T = batch * seq;
   if (T * ld >= ((int64_t)1 << 31) || T * n_q * head_dim >= ((int64_t)1 << 31))
     return fail(TP_MLP_ESHAPE, "%s: 2^31 or more elements", fn);

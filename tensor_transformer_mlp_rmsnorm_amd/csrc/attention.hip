@@ -160,6 +160,48 @@ struct TileSrc {
   }
 };
 
+// LDS DMA of [64][D] bf16 tiles from the rows of one sequence (a [seq, ld]
+// matrix): buffer_load_dwordx4 ... lds writes a wave's 64 x 16 bytes to 1 KiB
+// of LDS at a wave-uniform address, lane j at byte 16 j, with no registers in
+// between; each lane fetches the global chunk that belongs at its slot under
+// the tile's swizzle.  A 1 KiB block holds kRows = 512 / D rows; wave w of NW
+// fills blocks w, w + NW, ... of a tile, whose rows share one swizzle pattern
+// (NW is a multiple of 4), so a lane's offset inside its blocks is one
+// register.  Lanes whose row is past the sequence get an offset beyond the
+// buffer (the buffer unit returns zeros) and blocks wholly past it a zero SGPR
+// offset, so no offset wraps; the host keeps a sequence below 2^30 elements.
+template <int D, int NW>
+struct TileDma {
+  static constexpr int kChunks = D / 8, kRows = 512 / D, kBlocks = kAttnBlock / kRows, kPerWave = kBlocks / NW;
+  static_assert(kPerWave >= 1 && kBlocks % NW == 0 && NW % 4 == 0, "block split");
+  static constexpr unsigned kOut = 0x80000000u;
+  __amdgpu_buffer_rsrc_t rsrc;
+  int64_t ld, rows;
+  unsigned vlane;  // this lane's byte offset inside one of its blocks
+  int lrow, w;
+  __device__ __forceinline__ TileDma(const bf16_t* seq_base, int64_t ld_, int64_t rows_, int wave, int lane)
+      : ld(ld_), rows(rows_), w(wave) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(seq_base), (short)0, (int)(rows_ * ld_ * 2),
+                                             0x00020000);
+    lrow = lane / kChunks;
+    const int row = kRows * w + lrow;  // a representative row: every block of this wave has the same pattern
+    vlane = (unsigned)((lrow * ld_ + 8 * ((lane % kChunks) ^ Tile<D>::swz(row))) * 2);
+  }
+  // Tile `blk` of the columns col0 .. col0 + D - 1 into the LDS tile at `dst`.
+  __device__ __forceinline__ void issue(char* dst, int blk, int64_t col0) const {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int bb = w + NW * i;
+      const int64_t r0 = (int64_t)blk * kAttnBlock + kRows * bb;
+      const bool in = r0 < rows;
+      const unsigned soff = in ? (unsigned)((r0 * ld + col0) * 2) : 0u;
+      const unsigned voff = r0 + lrow < rows ? vlane : kOut;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + bb * 1024), 16,
+                                               voff, (int)soff, 0, 0);
+    }
+  }
+};
+
 // The lane's 8 k-slot values of one 32-row step m from its two 16-row blocks
 // (block 2m: slots 0-3, block 2m + 1: slots 4-7) as one bf16 operand.
 __device__ __forceinline__ uint4 pack_slots1(const floatx4& b0, const floatx4& b1) {
@@ -223,123 +265,203 @@ __device__ __forceinline__ int work_rank(int n) {
   return x < half ? x : n - 1 - (x - half);
 }
 
-// Rank -> (block index, head, batch) with the block index descending.
+// Rank -> (block index, head, batch) with the block index descending; the
+// rank is blockIdx.x itself (heaviest first, for grids larger than what the
+// chip holds at once, whose later workgroups fill the units that finish
+// first) or work_rank (PAIRED).
+template <bool PAIRED>
 __device__ __forceinline__ void block_coords(int nblocks, int heads, int batch, int& blk, int& head, int& b) {
-  const int per = heads * batch, r = work_rank(nblocks * per);
+  const int per = heads * batch, r = PAIRED ? work_rank(nblocks * per) : (int)blockIdx.x;
   blk = nblocks - 1 - r / per;
   head = (r % per) / batch;
   b = r % batch;
 }
 
-// Forward: 64 queries of one head per workgroup, wave w owning queries
-// 16 w .. 16 w + 15; key blocks 0 .. qb, the last one (the diagonal, which
-// also holds any keys past the sequence end) with the causal mask.  K and V
-// tiles are double-buffered in LDS: block kb stores tile kb + 1 (loaded into
-// registers during block kb - 1) into the other buffer, starts the loads of
-// tile kb + 2, multiplies tile kb, and ends with the one barrier per block.
+constexpr int kSplitWaves = 8, kSplitThreads = kSplitWaves * 64;
+
+// Forward: 64 queries of one head per workgroup of 8 waves, which takes two
+// 64-key tiles per step (tiles 0 .. qb, the last one -- the diagonal, which
+// also holds any keys past the sequence end -- with the causal mask): wave w
+// takes queries 32 (w % 2) .. + 31 and, of tile 2 step + (w / 4), keys
+// 32 (w / 2 % 2) .. + 31.  Each K fragment read from LDS feeds two query
+// blocks and each V fragment four products, and the longest workgroup takes
+// half as many steps as there are tiles.  Each wave keeps its own online
+// softmax over its keys; the four key parts of a query are merged at the end
+// through LDS in a fixed order.  The tiles are double-buffered in LDS and
+// filled by DMA: a step starts the next step's tiles into the other buffer
+// and ends with the one barrier, which also waits for them.
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(const bf16_t* __restrict__ qkv,
-                                                                   bf16_t* __restrict__ O, float* __restrict__ lse,
-                                                                   AttnDims dm) {
-  __shared__ __align__(16) char ktile[2][kAttnBlock * D * 2];
-  __shared__ __align__(16) char vtile[2][kAttnBlock * D * 2];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
+__global__ __launch_bounds__(kSplitThreads, 1) void attn_fwd_kernel(const bf16_t* __restrict__ qkv,
+                                                                    bf16_t* __restrict__ O, float* __restrict__ lse,
+                                                                    AttnDims dm) {
+  constexpr int kTile = kAttnBlock * D * 2, KS = D / 32, EB = D / 16;
+  __shared__ __align__(16) char smem[2][2][2][kTile];  // [buffer][tile of the step][K, V]
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), qh = w & 1, kp = w >> 1, kh = kp & 1, tp = kp >> 1;
   const int nqb = (int)((dm.seq + kAttnBlock - 1) / kAttnBlock);
   int qb, h, b;
-  block_coords(nqb, dm.n_q, (int)dm.batch, qb, h, b);
+  block_coords<false>(nqb, dm.n_q, (int)dm.batch, qb, h, b);
   const int kvh = h / dm.group;
   const int64_t t0 = (int64_t)b * dm.seq;
-  const int q = qb * kAttnBlock + 16 * w + c;  // this lane's query position
-  constexpr int KS = D / 32, EB = D / 16;
-  uint4 qf[KS];
+  const int q0 = qb * kAttnBlock + 32 * qh;  // this wave's first query; lane queries q0 + 16 jq + c
+  uint4 qf[2][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qf[ks] = q < dm.seq ? *reinterpret_cast<const uint4*>(qkv + (t0 + q) * dm.ld + (int64_t)h * D + 32 * ks + 8 * g)
-                        : make_uint4(0u, 0u, 0u, 0u);
-  floatx4 acc[EB];
+  for (int jq = 0; jq < 2; ++jq) {
+    const int q = q0 + 16 * jq + c;
 #pragma unroll
-  for (int i = 0; i < EB; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.0f;
-  const bf16_t* src = qkv + t0 * dm.ld;
-  const TileSrc<D> ks_src(src, dm.ld, (int64_t)(dm.n_q + kvh) * D, tid);
-  const TileSrc<D> vs_src(src, dm.ld, (int64_t)(dm.n_q + dm.n_kv + kvh) * D, tid);
-  typename Tile<D>::Regs kr, vr;
-  ks_src.fetch(kr, 0, dm.seq);
-  vs_src.fetch(vr, 0, dm.seq);
-  Tile<D>::store(ktile[0], kr, tid);
-  Tile<D>::store(vtile[0], vr, tid);
-  if (qb > 0) {
-    ks_src.fetch(kr, 1, dm.seq);
-    vs_src.fetch(vr, 1, dm.seq);
+    for (int ks = 0; ks < KS; ++ks)
+      qf[jq][ks] = q < dm.seq
+                       ? *reinterpret_cast<const uint4*>(qkv + (t0 + q) * dm.ld + (int64_t)h * D + 32 * ks + 8 * g)
+                       : make_uint4(0u, 0u, 0u, 0u);
   }
-  __syncthreads();
-  auto block = [&](int kb, auto mask) {
-    constexpr bool MASK = Flag<decltype(mask)>::value;
-    const int buf = kb & 1;
-    if (kb < qb) {  // tile kb + 1 into the other buffer, whose last reader was block kb - 1
-      Tile<D>::store(ktile[buf ^ 1], kr, tid);
-      Tile<D>::store(vtile[buf ^ 1], vr, tid);
-      if (kb + 1 < qb) {
-        ks_src.fetch(kr, kb + 2, dm.seq);
-        vs_src.fetch(vr, kb + 2, dm.seq);
+  floatx4 acc[2][EB];
+#pragma unroll
+  for (int jq = 0; jq < 2; ++jq)
+#pragma unroll
+    for (int i = 0; i < EB; ++i) acc[jq][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
+  const int64_t kcol = (int64_t)(dm.n_q + kvh) * D, vcol = (int64_t)(dm.n_q + dm.n_kv + kvh) * D;
+  const TileDma<D, kSplitWaves> dma(qkv + t0 * dm.ld, dm.ld, dm.seq, w, lane);
+  const int nsteps = (qb + 2) / 2;
+  auto issue_step = [&](int st, int buf) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      if (2 * st + t <= qb) {
+        dma.issue(smem[buf][t][0], 2 * st + t, kcol);
+        dma.issue(smem[buf][t][1], 2 * st + t, vcol);
       }
-    }
-    const char* kt = ktile[buf];
-    const char* vt = vtile[buf];
-    // S^T[key][q]; lane: key = 16 kk + 4 g + r, q = c
-    floatx4 s[4];
+  };
+  issue_step(0, 0);
+  __syncthreads();
+  auto tile = [&](int kb, const char* kt, const char* vt, auto mask) {
+    constexpr bool MASK = Flag<decltype(mask)>::value;
+    // S^T[key][q]; lane: key = 32 kh + 16 kk + 4 g + r (in the tile), q = q0 + 16 jq + c
+    floatx4 s[2][2];  // [kk][jq]
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      s[kk] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < 2; ++kk) {
+      s[kk][0] = s[kk][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[kk] = mma(Tile<D>::row8(kt, 16 * kk + c, 4 * ks + g), qf[ks], s[kk]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 kf = Tile<D>::row8(kt, 32 * kh + 16 * kk + c, 4 * ks + g);
+        s[kk][0] = mma(kf, qf[0][ks], s[kk][0]);
+        s[kk][1] = mma(kf, qf[1][ks], s[kk][1]);
+      }
     }
     if constexpr (MASK) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int jq = 0; jq < 2; ++jq)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kb * kAttnBlock + 32 * kh + 16 * kk + 4 * g + r, q = q0 + 16 * jq + c;
+            if (!(key <= q && key < dm.seq)) s[kk][jq][r] = -INFINITY;
+          }
+    }
+    float bmax[2];
+#pragma unroll
+    for (int jq = 0; jq < 2; ++jq) {
+      const float v = fmaxf(fmaxf(fmaxf(s[0][jq][0], s[0][jq][1]), fmaxf(s[0][jq][2], s[0][jq][3])),
+                            fmaxf(fmaxf(s[1][jq][0], s[1][jq][1]), fmaxf(s[1][jq][2], s[1][jq][3])));
+      bmax[jq] = max_xor32(max_xor16(v)) * dm.scale_log2;
+    }
+    if (__builtin_amdgcn_ballot_w64(bmax[0] > m[0] + kLazyRescale || bmax[1] > m[1] + kLazyRescale)) {
+#pragma unroll
+      for (int jq = 0; jq < 2; ++jq) {  // m = -inf until a key is seen (a masked tile can leave it so)
+        const float mnew = fmaxf(m[jq], bmax[jq]);
+        const float alpha = m[jq] == -INFINITY ? 0.0f : fast_exp2(m[jq] - mnew);
+        m[jq] = mnew;
+        lsum[jq] *= alpha;
+#pragma unroll
+        for (int i = 0; i < EB; ++i) acc[jq][i] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int jq = 0; jq < 2; ++jq) {
+      const float mref = m[jq] == -INFINITY ? 0.0f : m[jq];  // with m = -inf every score here is -inf
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = kb * kAttnBlock + 16 * kk + 4 * g + r;
-          if (!(key <= q && key < dm.seq)) s[kk][r] = -INFINITY;
+          s[kk][jq][r] = fast_exp2(__builtin_fmaf(s[kk][jq][r], dm.scale_log2, -mref));
+          lsum[jq] += s[kk][jq][r];
         }
     }
-    float bmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    bmax = fmaxf(bmax, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
-                             fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
-    bmax = max_xor32(max_xor16(bmax)) * dm.scale_log2;
-    if (__builtin_amdgcn_ballot_w64(bmax > m + kLazyRescale)) {  // m = -inf on the first block
-      const float mnew = fmaxf(m, bmax);
-      const float alpha = fast_exp2(m - mnew);
-      m = mnew;
-      lsum *= alpha;
+    const SlotPair pf0 = pack_slots(s[0][0], s[1][0]);
+    const SlotPair pf1 = pack_slots(s[0][1], s[1][1]);
 #pragma unroll
-      for (int i = 0; i < EB; ++i) acc[i] *= alpha;
+    for (int eb = 0; eb < EB; ++eb) {
+      const uint4 vf = Tile<D>::col8(vt, kh, 16 * eb, lane);
+      acc[0][eb] = mma2(vf, pf0, acc[0][eb]);
+      acc[1][eb] = mma2(vf, pf1, acc[1][eb]);
     }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[kk][r] = fast_exp2(__builtin_fmaf(s[kk][r], dm.scale_log2, -m));
-        lsum += s[kk][r];
-      }
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      const SlotPair pf = pack_slots(s[2 * mm], s[2 * mm + 1]);
-#pragma unroll
-      for (int eb = 0; eb < EB; ++eb) acc[eb] = mma2(Tile<D>::col8(vt, mm, 16 * eb, lane), pf, acc[eb]);
-    }
-    __syncthreads();  // tile kb is read; tile kb + 1 is stored
   };
-  for (int kb = 0; kb < qb; ++kb) block(kb, Unmasked{});
-  block(qb, Masked{});
-  lsum = sum_xor32(sum_xor16(lsum));
-  if (q < dm.seq) {
-    const float inv = 1.0f / lsum;
-    bf16_t* dst = O + (t0 + q) * dm.ldo + (int64_t)h * D;
+  // Every step but the last holds only tiles before the diagonal.
+  for (int st = 0; st + 1 < nsteps; ++st) {
+    const int buf = st & 1;
+    issue_step(st + 1, buf ^ 1);  // the other buffer's last readers were step st - 1
+    tile(2 * st + tp, smem[buf][tp][0], smem[buf][tp][1], Unmasked{});
+    __syncthreads();  // this step's tiles are read; the next step's have landed
+  }
+  {
+    const int st = nsteps - 1, buf = st & 1, kb = 2 * st + tp;
+    if (kb < qb) tile(kb, smem[buf][tp][0], smem[buf][tp][1], Unmasked{});
+    else if (kb == qb) tile(kb, smem[buf][tp][0], smem[buf][tp][1], Masked{});
+    __syncthreads();
+  }
+  // Merge the four key parts of each query: waves with kp > 0 hand (O, m, l)
+  // to the wave with kp = 0 and the same queries, which adds them in kp order.
+  lsum[0] = sum_xor32(sum_xor16(lsum[0]));
+  lsum[1] = sum_xor32(sum_xor16(lsum[1]));
+  constexpr int kX = (2 * EB * 4 + 4) * 64;  // floats per handed-over state
+  float* xbase = reinterpret_cast<float*>(&smem[0][0][0][0]);
+  if (kp > 0) {
+    float* x = xbase + ((kp - 1) * 2 + qh) * kX;
 #pragma unroll
-    for (int eb = 0; eb < EB; ++eb) store4<bf16_t>(dst + 16 * eb + 4 * g, acc[eb] * inv);
-    if (g == 0) lse[(int64_t)h * dm.batch * dm.seq + t0 + q] = (m + log2f(lsum)) * kLn2;
+    for (int jq = 0; jq < 2; ++jq) {
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb) *reinterpret_cast<floatx4*>(x + ((jq * EB + eb) * 64 + lane) * 4) = acc[jq][eb];
+      x[(2 * EB * 4 + 2 * jq) * 64 + lane] = m[jq];
+      x[(2 * EB * 4 + 2 * jq + 1) * 64 + lane] = lsum[jq];
+    }
+  }
+  __syncthreads();
+  if (kp == 0) {
+#pragma unroll
+    for (int jq = 0; jq < 2; ++jq) {
+      float mp[3], lp[3];
+      float mm = m[jq];
+#pragma unroll
+      for (int p2 = 0; p2 < 3; ++p2) {
+        const float* x = xbase + (p2 * 2 + qh) * kX;
+        mp[p2] = x[(2 * EB * 4 + 2 * jq) * 64 + lane];
+        lp[p2] = x[(2 * EB * 4 + 2 * jq + 1) * 64 + lane];
+        mm = fmaxf(mm, mp[p2]);
+      }
+      const float a0 = m[jq] == -INFINITY ? 0.0f : fast_exp2(m[jq] - mm);
+      float ap[3];
+      float l = lsum[jq] * a0;
+#pragma unroll
+      for (int p2 = 0; p2 < 3; ++p2) {
+        ap[p2] = mp[p2] == -INFINITY ? 0.0f : fast_exp2(mp[p2] - mm);
+        l += lp[p2] * ap[p2];
+      }
+      const int q = q0 + 16 * jq + c;
+      if (q < dm.seq) {
+        const float inv = 1.0f / l;
+        bf16_t* dst = O + (t0 + q) * dm.ldo + (int64_t)h * D;
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb) {
+          floatx4 o = acc[jq][eb] * a0;
+#pragma unroll
+          for (int p2 = 0; p2 < 3; ++p2)
+            o += *reinterpret_cast<const floatx4*>(xbase + (p2 * 2 + qh) * kX + ((jq * EB + eb) * 64 + lane) * 4) *
+                 ap[p2];
+          store4<bf16_t>(dst + 16 * eb + 4 * g, o * inv);
+        }
+        if (g == 0) lse[(int64_t)h * dm.batch * dm.seq + t0 + q] = (mm + log2f(l)) * kLn2;
+      }
+    }
   }
 }
 
@@ -522,100 +644,138 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(const float* __restric
   store4<bf16_t>(dqkv + t * dm.ld + col, acc);
 }
 
-// dQ of 64 queries of one head: every key block up to the query block, the
-// last (the diagonal) with the masks.
+// dQ of 64 queries of one head, split over 8 waves and two key tiles per
+// step as in the forward; the four key parts' dQ are added through LDS at the
+// end, in a fixed order.  Key tiles 0 .. qb, the last (the diagonal) with the
+// masks.
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
-                                                               const bf16_t* __restrict__ dO,
-                                                               const float* __restrict__ lse,
-                                                               const float* __restrict__ delta,
-                                                               bf16_t* __restrict__ dqkv, AttnDims dm) {
-  __shared__ __align__(16) char ktile[2][kAttnBlock * D * 2];
-  __shared__ __align__(16) char vtile[2][kAttnBlock * D * 2];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
+__global__ __launch_bounds__(kSplitThreads, 1) void attn_dq_kernel(const bf16_t* __restrict__ qkv,
+                                                                   const bf16_t* __restrict__ dO,
+                                                                   const float* __restrict__ lse,
+                                                                   const float* __restrict__ delta,
+                                                                   bf16_t* __restrict__ dqkv, AttnDims dm) {
+  constexpr int kTile = kAttnBlock * D * 2, KS = D / 32, EB = D / 16;
+  __shared__ __align__(16) char smem[2][2][2][kTile];  // [buffer][tile of the step][K, V]
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), qh = w & 1, kp = w >> 1, kh = kp & 1, tp = kp >> 1;
   const int nqb = (int)((dm.seq + kAttnBlock - 1) / kAttnBlock);
   int qb, h, b;
-  block_coords(nqb, dm.n_q, (int)dm.batch, qb, h, b);
+  block_coords<false>(nqb, dm.n_q, (int)dm.batch, qb, h, b);
   const int kvh = h / dm.group;
   const int64_t t0 = (int64_t)b * dm.seq, T = dm.batch * dm.seq;
-  const int q = qb * kAttnBlock + 16 * w + c;
-  constexpr int KS = D / 32, EB = D / 16;
-  uint4 qf[KS], df[KS];
-  const bool qok = q < dm.seq;
+  const int q0 = qb * kAttnBlock + 32 * qh;
+  uint4 qf[2][KS], df[2][KS];
+  float lse2[2], dl[2];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = qok ? *reinterpret_cast<const uint4*>(qkv + (t0 + q) * dm.ld + (int64_t)h * D + 32 * ks + 8 * g)
-                 : make_uint4(0u, 0u, 0u, 0u);
-    df[ks] = qok ? *reinterpret_cast<const uint4*>(dO + (t0 + q) * dm.ldo + (int64_t)h * D + 32 * ks + 8 * g)
-                 : make_uint4(0u, 0u, 0u, 0u);
-  }
-  const float lse2 = qok ? lse[(int64_t)h * T + t0 + q] * kLog2e : 0.0f;
-  const float dl = qok ? delta[(int64_t)h * T + t0 + q] : 0.0f;
-  floatx4 dq[EB];
+  for (int jq = 0; jq < 2; ++jq) {
+    const int q = q0 + 16 * jq + c;
+    const bool ok = q < dm.seq;
 #pragma unroll
-  for (int i = 0; i < EB; ++i) dq[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const bf16_t* src = qkv + t0 * dm.ld;
-  const TileSrc<D> ks_src(src, dm.ld, (int64_t)(dm.n_q + kvh) * D, tid);
-  const TileSrc<D> vs_src(src, dm.ld, (int64_t)(dm.n_q + dm.n_kv + kvh) * D, tid);
-  typename Tile<D>::Regs kr, vr;
-  // Key blocks 0 .. qb, double-buffered as in the forward.
-  ks_src.fetch(kr, 0, dm.seq);
-  vs_src.fetch(vr, 0, dm.seq);
-  Tile<D>::store(ktile[0], kr, tid);
-  Tile<D>::store(vtile[0], vr, tid);
-  if (qb > 0) {
-    ks_src.fetch(kr, 1, dm.seq);
-    vs_src.fetch(vr, 1, dm.seq);
-  }
-  __syncthreads();
-  auto block = [&](int kb, auto mask) {
-    constexpr bool MASK = Flag<decltype(mask)>::value;
-    const int buf = kb & 1;
-    if (kb < qb) {
-      Tile<D>::store(ktile[buf ^ 1], kr, tid);
-      Tile<D>::store(vtile[buf ^ 1], vr, tid);
-      if (kb + 1 < qb) {
-        ks_src.fetch(kr, kb + 2, dm.seq);
-        vs_src.fetch(vr, kb + 2, dm.seq);
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[jq][ks] = ok ? *reinterpret_cast<const uint4*>(qkv + (t0 + q) * dm.ld + (int64_t)h * D + 32 * ks + 8 * g)
+                      : make_uint4(0u, 0u, 0u, 0u);
+      df[jq][ks] = ok ? *reinterpret_cast<const uint4*>(dO + (t0 + q) * dm.ldo + (int64_t)h * D + 32 * ks + 8 * g)
+                      : make_uint4(0u, 0u, 0u, 0u);
     }
-    const char* kt = ktile[buf];
-    const char* vt = vtile[buf];
-    // S^T[key][q], dP^T[key][q]; lane: key = 16 kk + 4 g + r, q = c
-    floatx4 ds[4];
+    lse2[jq] = ok ? lse[(int64_t)h * T + t0 + q] * kLog2e : 0.0f;
+    dl[jq] = ok ? delta[(int64_t)h * T + t0 + q] : 0.0f;
+  }
+  floatx4 dq[2][EB];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      floatx4 sv = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int jq = 0; jq < 2; ++jq)
+#pragma unroll
+    for (int i = 0; i < EB; ++i) dq[jq][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int64_t kcol = (int64_t)(dm.n_q + kvh) * D, vcol = (int64_t)(dm.n_q + dm.n_kv + kvh) * D;
+  const TileDma<D, kSplitWaves> dma(qkv + t0 * dm.ld, dm.ld, dm.seq, w, lane);
+  const int nsteps = (qb + 2) / 2;
+  auto issue_step = [&](int st, int buf) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      if (2 * st + t <= qb) {
+        dma.issue(smem[buf][t][0], 2 * st + t, kcol);
+        dma.issue(smem[buf][t][1], 2 * st + t, vcol);
+      }
+  };
+  issue_step(0, 0);
+  __syncthreads();
+  auto tile = [&](int kb, const char* kt, const char* vt, auto mask) {
+    constexpr bool MASK = Flag<decltype(mask)>::value;
+    // S^T[key][q], dP^T[key][q]; lane: key = 32 kh + 16 kk + 4 g + r (in the tile), q = q0 + 16 jq + c
+    floatx4 ds[2][2];  // [kk][jq]
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      floatx4 sv[2], dp[2];
+      sv[0] = sv[1] = dp[0] = dp[1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        sv = mma(Tile<D>::row8(kt, 16 * kk + c, 4 * ks + g), qf[ks], sv);
-        dp = mma(Tile<D>::row8(vt, 16 * kk + c, 4 * ks + g), df[ks], dp);
+        const uint4 kf = Tile<D>::row8(kt, 32 * kh + 16 * kk + c, 4 * ks + g);
+        const uint4 vf = Tile<D>::row8(vt, 32 * kh + 16 * kk + c, 4 * ks + g);
+        sv[0] = mma(kf, qf[0][ks], sv[0]);
+        sv[1] = mma(kf, qf[1][ks], sv[1]);
+        dp[0] = mma(vf, df[0][ks], dp[0]);
+        dp[1] = mma(vf, df[1][ks], dp[1]);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float pv = fast_exp2(__builtin_fmaf(sv[r], dm.scale_log2, -lse2));
-        if constexpr (MASK) {
-          const int key = kb * kAttnBlock + 16 * kk + 4 * g + r;
-          if (!(key <= q && key < dm.seq && qok)) pv = 0.0f;
+      for (int jq = 0; jq < 2; ++jq)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float pv = fast_exp2(__builtin_fmaf(sv[jq][r], dm.scale_log2, -lse2[jq]));
+          if constexpr (MASK) {
+            const int key = kb * kAttnBlock + 32 * kh + 16 * kk + 4 * g + r, q = q0 + 16 * jq + c;
+            if (!(key <= q && key < dm.seq && q < dm.seq)) pv = 0.0f;
+          }
+          ds[kk][jq][r] = pv * (dp[jq][r] - dl[jq]);
         }
-        ds[kk][r] = pv * (dp[r] - dl);
+    }
+    // dQ^T[e][q] += K^T dS^T over this wave's 32 keys
+    const SlotPair sf0 = pack_slots(ds[0][0], ds[1][0]);
+    const SlotPair sf1 = pack_slots(ds[0][1], ds[1][1]);
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) {
+      const uint4 kf = Tile<D>::col8(kt, kh, 16 * eb, lane);
+      dq[0][eb] = mma2(kf, sf0, dq[0][eb]);
+      dq[1][eb] = mma2(kf, sf1, dq[1][eb]);
+    }
+  };
+  for (int st = 0; st + 1 < nsteps; ++st) {
+    const int buf = st & 1;
+    issue_step(st + 1, buf ^ 1);
+    tile(2 * st + tp, smem[buf][tp][0], smem[buf][tp][1], Unmasked{});
+    __syncthreads();
+  }
+  {
+    const int st = nsteps - 1, buf = st & 1, kb = 2 * st + tp;
+    if (kb < qb) tile(kb, smem[buf][tp][0], smem[buf][tp][1], Unmasked{});
+    else if (kb == qb) tile(kb, smem[buf][tp][0], smem[buf][tp][1], Masked{});
+    __syncthreads();
+  }
+  // dQ = the key parts added in kp order, through LDS.
+  constexpr int kX = 2 * EB * 4 * 64;
+  float* xbase = reinterpret_cast<float*>(&smem[0][0][0][0]);
+  if (kp > 0) {
+    float* x = xbase + ((kp - 1) * 2 + qh) * kX;
+#pragma unroll
+    for (int jq = 0; jq < 2; ++jq)
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb) *reinterpret_cast<floatx4*>(x + ((jq * EB + eb) * 64 + lane) * 4) = dq[jq][eb];
+  }
+  __syncthreads();
+  if (kp == 0) {
+#pragma unroll
+    for (int jq = 0; jq < 2; ++jq) {
+      const int q = q0 + 16 * jq + c;
+      if (q < dm.seq) {
+        bf16_t* dst = dqkv + (t0 + q) * dm.ld + (int64_t)h * D;
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb) {
+          floatx4 v = dq[jq][eb];
+#pragma unroll
+          for (int p2 = 0; p2 < 3; ++p2)
+            v += *reinterpret_cast<const floatx4*>(xbase + (p2 * 2 + qh) * kX + ((jq * EB + eb) * 64 + lane) * 4);
+          store4<bf16_t>(dst + 16 * eb + 4 * g, v * dm.scale);
+        }
       }
     }
-    // dQ^T[e][q] += K^T dS^T
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      const SlotPair sf = pack_slots(ds[2 * mm], ds[2 * mm + 1]);
-#pragma unroll
-      for (int eb = 0; eb < EB; ++eb) dq[eb] = mma2(Tile<D>::col8(kt, mm, 16 * eb, lane), sf, dq[eb]);
-    }
-    __syncthreads();
-  };
-  for (int kb = 0; kb < qb; ++kb) block(kb, Unmasked{});
-  block(qb, Masked{});
-  if (qok) {
-    bf16_t* dst = dqkv + (t0 + q) * dm.ld + (int64_t)h * D;
-#pragma unroll
-    for (int eb = 0; eb < EB; ++eb) store4<bf16_t>(dst + 16 * eb + 4 * g, dq[eb] * dm.scale);
   }
 }
 
@@ -638,7 +798,7 @@ hipError_t fwd_t(const AttnShapeArgs& a, const void* qkv, void* O, float* lse, h
   const AttnDims dm = make_dims(a);
   const int nqb = (int)((a.seq + kAttnBlock - 1) / kAttnBlock);
   KernelTimer timer("attention_fwd", s);
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(nqb * a.n_q * (int)a.batch), dim3(kAttnThreads), 0, s,
+  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(nqb * a.n_q * (int)a.batch), dim3(kSplitThreads), 0, s,
                      static_cast<const bf16_t*>(qkv), static_cast<bf16_t*>(O), lse, dm);
   return hipGetLastError();
 }
@@ -676,7 +836,7 @@ hipError_t bwd_t(const AttnShapeArgs& a, const void* qkv, const void* O, const v
     if (e != hipSuccess) return e;
   }
   KernelTimer timer("attention_bwd_dq", s);
-  hipLaunchKernelGGL(attn_dq_kernel<D>, dim3(nb * a.n_q * (int)a.batch), dim3(kAttnThreads), 0, s,
+  hipLaunchKernelGGL(attn_dq_kernel<D>, dim3(nb * a.n_q * (int)a.batch), dim3(kSplitThreads), 0, s,
                      static_cast<const bf16_t*>(qkv), static_cast<const bf16_t*>(dO), lse, delta,
                      static_cast<bf16_t*>(dqkv), dm);
   return hipGetLastError();

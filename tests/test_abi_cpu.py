@@ -332,6 +332,7 @@ def test_attention_checks(lib):
     assert fwd(desc(n_q=3, n_kv=2)) == L.ESHAPE               # n_q a multiple of n_kv
     assert fwd(desc(dtype=L.F32)) == L.EDTYPE                 # bf16 only
     assert fwd(desc(hidden=100)) == L.ESHAPE
+    assert fwd(desc(seq=1 << 22)) == L.ESHAPE                 # one sequence's QKV of 2^30 elements
     assert fwd(desc(flags=8)) == L.EINVAL
     assert fwd(desc(batch=-1)) == L.EINVAL
     assert fwd(desc(), w_qkv=None) == L.EINVAL
@@ -357,6 +358,7 @@ def test_attention_checks(lib):
     assert bare(1, 8, 2, 1, 64, A, 200, A, A, None) == L.ESHAPE          # ld < (n_q + 2 n_kv) D
     assert bare(1, 8, 2, 1, 64, A, 260, A, A, None) == L.ESHAPE          # ld not a multiple of 8
     assert bare(1, 8, 2, 1, 32, A, 256, A, A, None) == L.ESHAPE          # head_dim
+    assert bare(1, 1 << 22, 2, 1, 64, A, 256, A, A, None) == L.ESHAPE    # one sequence of 2^30 elements
     assert bare(0, 8, 2, 1, 64, None, 256, None, None, None) == L.OK     # empty
     bb = lib.tp_attention_backward
     wsb = lib.tp_attention_backward_workspace_bytes
