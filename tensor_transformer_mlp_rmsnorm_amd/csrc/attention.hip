@@ -487,34 +487,36 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const bf16_t* __restric
   delta[(int64_t)h * T + t] = acc;
 }
 
-// dK and dV of 64 keys from one query head (one workgroup per key block,
-// query head and sequence; the key blocks with the most query blocks after
-// them are dispatched first): every query block at or after the key block,
-// the first (the diagonal) and the last (which may end past the sequence)
-// with the masks.  Wave w owns keys 16 w .. 16 w + 15.  With one query head
-// per KV head the result goes to dqkv; otherwise each head's share goes to
+// dK and dV of 64 keys from one query head: one workgroup of 8 waves per key
+// block, query head and sequence (grid order: the key blocks with the most
+// query tiles after them first), over the query tiles kb .. nqb - 1 two per
+// step.  Wave w owns keys 16 (w % 4) .. + 15 and takes the step's tile
+// w / 4; the first and last steps (the diagonal tile and the one that may end
+// past the sequence) apply the masks.  Q and dO tiles, and the tiles' lse and
+// delta, come in by DMA into double-buffered LDS.  At the end the two tile
+// parities' dK and dV are added through LDS.  With one query head per KV head
+// the result goes to dqkv; otherwise each head's share goes to
 // part[h % group][t][kv head][2 D] (fp32, dK then dV) and attn_reduce_kernel
 // adds the group's shares in order.
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_dkdv_kernel(const bf16_t* __restrict__ qkv,
-                                                                 const bf16_t* __restrict__ dO,
-                                                                 const float* __restrict__ lse,
-                                                                 const float* __restrict__ delta,
-                                                                 bf16_t* __restrict__ dqkv, float* __restrict__ part,
-                                                                 AttnDims dm) {
-  __shared__ __align__(16) char qtile[2][kAttnBlock * D * 2];
-  __shared__ __align__(16) char dotile[2][kAttnBlock * D * 2];
-  __shared__ __align__(16) float lse2_s[2][kAttnBlock];
-  __shared__ __align__(16) float delta_s[2][kAttnBlock];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
-  const int nkb = (int)((dm.seq + kAttnBlock - 1) / kAttnBlock);
+__global__ __launch_bounds__(kSplitThreads, 1) void attn_dkdv_kernel(const bf16_t* __restrict__ qkv,
+                                                                     const bf16_t* __restrict__ dO,
+                                                                     const float* __restrict__ lse,
+                                                                     const float* __restrict__ delta,
+                                                                     bf16_t* __restrict__ dqkv,
+                                                                     float* __restrict__ part, AttnDims dm) {
+  constexpr int kTile = kAttnBlock * D * 2, KS = D / 32, EB = D / 16;
+  __shared__ __align__(16) char smem[2][2][2][kTile];  // [buffer][tile of the step][Q, dO]
+  __shared__ __align__(16) float stat[2][2][2][kAttnBlock];  // [buffer][tile][lse, delta]
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), kw = w & 3, tp = w >> 2;
+  const int nqb = (int)((dm.seq + kAttnBlock - 1) / kAttnBlock);
   const int per = dm.n_q * (int)dm.batch;
-  const int rank = work_rank(nkb * per);  // key block ascending: the heaviest first
+  const int rank = blockIdx.x;  // key block ascending: the heaviest first
   const int kb = rank / per, hq = (rank % per) / (int)dm.batch, b = rank % (int)dm.batch;
   const int kvh = hq / dm.group;
   const int64_t t0 = (int64_t)b * dm.seq, T = dm.batch * dm.seq;
-  const int key = kb * kAttnBlock + 16 * w + c;  // this lane's key (Y-operand row)
-  constexpr int KS = D / 32, EB = D / 16;
+  const int key = kb * kAttnBlock + 16 * kw + c;  // this lane's key (Y-operand row)
   const int64_t kcol = (int64_t)(dm.n_q + kvh) * D, vcol = (int64_t)(dm.n_q + dm.n_kv + kvh) * D;
   uint4 kf[KS], vf[KS];
 #pragma unroll
@@ -528,62 +530,53 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_dkdv_kernel(const bf16_t
   floatx4 dk[EB], dv[EB];
 #pragma unroll
   for (int i = 0; i < EB; ++i) dk[i] = dv[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const int nqb = nkb;
-  const TileSrc<D> q_src(qkv + t0 * dm.ld, dm.ld, (int64_t)hq * D, tid);
-  const TileSrc<D> d_src(dO + t0 * dm.ldo, dm.ldo, (int64_t)hq * D, tid);
-  const float* lse_h = lse + (int64_t)hq * T + t0;
-  const float* delta_h = delta + (int64_t)hq * T + t0;
-  typename Tile<D>::Regs qr, dr;
-  float lr = 0.0f, dl = 0.0f;
-  auto fetch = [&](int qb) {
-    q_src.fetch(qr, qb, dm.seq);
-    d_src.fetch(dr, qb, dm.seq);
-    if (tid < kAttnBlock) {
-      const int qq = qb * kAttnBlock + tid;
-      const bool ok = qq < dm.seq;
-      lr = ok ? lse_h[qq] * kLog2e : 0.0f;
-      dl = ok ? delta_h[qq] : 0.0f;
+  const TileDma<D, kSplitWaves> q_dma(qkv + t0 * dm.ld, dm.ld, dm.seq, w, lane);
+  const TileDma<D, kSplitWaves> d_dma(dO + t0 * dm.ldo, dm.ldo, dm.seq, w, lane);
+  // lse and delta of a tile: 64 floats each, one 4-byte DMA per tile and kind
+  // (waves 0-3: tile w / 2 of the step, lse for even w, delta for odd).
+  const float* stat_src = (w & 1) ? delta + (int64_t)hq * T + t0 : lse + (int64_t)hq * T + t0;
+  const __amdgpu_buffer_rsrc_t stat_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(stat_src), (short)0, (int)(dm.seq * 4), 0x00020000);
+  const int ntiles = nqb - kb, nsteps = (ntiles + 1) / 2;
+  auto issue_step = [&](int st, int buf) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int qt = kb + 2 * st + t;
+      if (qt < nqb) {
+        q_dma.issue(smem[buf][t][0], qt, (int64_t)hq * D);
+        d_dma.issue(smem[buf][t][1], qt, (int64_t)hq * D);
+        if (w < 4 && (w >> 1) == t) {
+          const int qq = qt * kAttnBlock + lane;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              stat_rsrc, (__attribute__((address_space(3))) void*)&stat[buf][t][w & 1][0], 4,
+              qq < dm.seq ? (unsigned)(lane * 4) : 0x80000000u, qt * kAttnBlock * 4, 0, 0);
+        }
+      }
     }
   };
-  auto stash = [&](int buf) {
-    Tile<D>::store(qtile[buf], qr, tid);
-    Tile<D>::store(dotile[buf], dr, tid);
-    if (tid < kAttnBlock) {
-      lse2_s[buf][tid] = lr;
-      delta_s[buf][tid] = dl;
-    }
-  };
-  // Query blocks kb .. nqb - 1, double-buffered as in the forward.
-  fetch(kb);
-  stash(0);
-  if (kb + 1 < nqb) fetch(kb + 1);
-  __syncthreads();
-  auto block = [&](int qb, auto mask) {
+  auto tile = [&](int qt, int buf, auto mask) {
     constexpr bool MASK = Flag<decltype(mask)>::value;
-    const int buf = (qb - kb) & 1;
-    if (qb + 1 < nqb) {
-      stash(buf ^ 1);
-      if (qb + 2 < nqb) fetch(qb + 2);
-    }
-    const char* qt = qtile[buf];
-    const char* dt = dotile[buf];
-    // S[q][key] and dP[q][key] for the block's 4 x 16 queries; lane: q = 16 qq + 4 g + r, key = c
+    const char* qtl = smem[buf][tp][0];
+    const char* dtl = smem[buf][tp][1];
+    const float* lse_t = stat[buf][tp][0];
+    const float* del_t = stat[buf][tp][1];
+    // S[q][key] and dP[q][key] for the tile's 4 x 16 queries; lane: q = 16 qq + 4 g + r, key = c
     floatx4 p[4], ds[4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       floatx4 sv = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        sv = mma(Tile<D>::row8(qt, 16 * qq + c, 4 * ks + g), kf[ks], sv);
-        dp = mma(Tile<D>::row8(dt, 16 * qq + c, 4 * ks + g), vf[ks], dp);
+        sv = mma(Tile<D>::row8(qtl, 16 * qq + c, 4 * ks + g), kf[ks], sv);
+        dp = mma(Tile<D>::row8(dtl, 16 * qq + c, 4 * ks + g), vf[ks], dp);
       }
-      const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse2_s[buf][16 * qq + 4 * g]);
-      const floatx4 d4 = *reinterpret_cast<const floatx4*>(&delta_s[buf][16 * qq + 4 * g]);
+      const floatx4 l4 = *reinterpret_cast<const floatx4*>(lse_t + 16 * qq + 4 * g);
+      const floatx4 d4 = *reinterpret_cast<const floatx4*>(del_t + 16 * qq + 4 * g);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float pv = fast_exp2(__builtin_fmaf(sv[r], dm.scale_log2, -l4[r]));
+        float pv = fast_exp2(__builtin_fmaf(sv[r], dm.scale_log2, -l4[r] * kLog2e));
         if constexpr (MASK) {
-          const int qpos = qb * kAttnBlock + 16 * qq + 4 * g + r;
+          const int qpos = qt * kAttnBlock + 16 * qq + 4 * g + r;
           if (!(key <= qpos && qpos < dm.seq && key < dm.seq)) pv = 0.0f;
         }
         p[qq][r] = pv;
@@ -597,16 +590,49 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_dkdv_kernel(const bf16_t
       const SlotPair sf = pack_slots(ds[2 * mm], ds[2 * mm + 1]);
 #pragma unroll
       for (int eb = 0; eb < EB; ++eb) {
-        dv[eb] = mma(Tile<D>::col8(dt, mm, 16 * eb, lane), pf, dv[eb]);
-        dk[eb] = mma2(Tile<D>::col8(qt, mm, 16 * eb, lane), sf, dk[eb]);
+        dv[eb] = mma(Tile<D>::col8(dtl, mm, 16 * eb, lane), pf, dv[eb]);
+        dk[eb] = mma2(Tile<D>::col8(qtl, mm, 16 * eb, lane), sf, dk[eb]);
       }
     }
-    __syncthreads();
   };
-  block(kb, Masked{});
-  for (int qb = kb + 1; qb < nqb - 1; ++qb) block(qb, Unmasked{});
-  if (kb < nqb - 1) block(nqb - 1, Masked{});
-  if (key < dm.seq) {
+  issue_step(0, 0);
+  __syncthreads();
+  // The first step holds the diagonal tile, the last the sequence's last
+  // tile; the steps in between hold neither.
+  {
+    if (nsteps > 1) issue_step(1, 1);
+    const int qt = kb + tp;
+    if (qt < nqb) tile(qt, 0, Masked{});
+    __syncthreads();
+  }
+  for (int st = 1; st + 1 < nsteps; ++st) {
+    const int buf = st & 1;
+    issue_step(st + 1, buf ^ 1);
+    tile(kb + 2 * st + tp, buf, Unmasked{});
+    __syncthreads();
+  }
+  if (nsteps > 1) {
+    const int st = nsteps - 1, qt = kb + 2 * st + tp;
+    if (qt < nqb) tile(qt, st & 1, Masked{});
+    __syncthreads();
+  }
+  // dK, dV = (even tiles) + (odd tiles), through LDS.
+  constexpr int kX = 2 * EB * 4 * 64;
+  float* xbase = reinterpret_cast<float*>(&smem[0][0][0][0]) + kw * kX;
+  if (tp == 1) {
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) {
+      *reinterpret_cast<floatx4*>(xbase + (eb * 64 + lane) * 4) = dk[eb];
+      *reinterpret_cast<floatx4*>(xbase + ((EB + eb) * 64 + lane) * 4) = dv[eb];
+    }
+  }
+  __syncthreads();
+  if (tp == 0 && key < dm.seq) {
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) {
+      dk[eb] += *reinterpret_cast<const floatx4*>(xbase + (eb * 64 + lane) * 4);
+      dv[eb] += *reinterpret_cast<const floatx4*>(xbase + ((EB + eb) * 64 + lane) * 4);
+    }
     if (dm.group == 1) {
       bf16_t* krow = dqkv + (t0 + key) * dm.ld + kcol;
       bf16_t* vrow = dqkv + (t0 + key) * dm.ld + vcol;
@@ -821,7 +847,7 @@ hipError_t bwd_t(const AttnShapeArgs& a, const void* qkv, const void* O, const v
   }
   {
     KernelTimer timer("attention_bwd_dkdv", s);
-    hipLaunchKernelGGL(attn_dkdv_kernel<D>, dim3(nb * a.n_q * (int)a.batch), dim3(kAttnThreads), 0, s,
+    hipLaunchKernelGGL(attn_dkdv_kernel<D>, dim3(nb * a.n_q * (int)a.batch), dim3(kSplitThreads), 0, s,
                        static_cast<const bf16_t*>(qkv), static_cast<const bf16_t*>(dO), lse, delta,
                        static_cast<bf16_t*>(dqkv), part, dm);
     const hipError_t e = hipGetLastError();
