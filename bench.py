@@ -281,12 +281,16 @@ def attention_path(steps: int, warmup: int, name: str = "attn_llama3_8b_tp8") ->
     for _ in range(max(1, warmup)):
         st.step()
     torch.cuda.synchronize()
-    L.tp_mlp_profile_enable(True)
     t0 = time.perf_counter()
     for _ in range(steps):
         st.step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / steps * 1e3
+    # the per-kernel durations from a second run with the library's event timing on
+    L.tp_mlp_profile_enable(True)
+    for _ in range(steps):
+        st.step()
+    torch.cuda.synchronize()
     L.tp_mlp_profile_enable(False)
     prof = L.tp_mlp_profile_entries()
     del st

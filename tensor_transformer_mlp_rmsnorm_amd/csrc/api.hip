@@ -848,14 +848,18 @@ AttnShapeArgs attn_args(const tp_attn_desc* d) {
   return a;
 }
 
-// Workspace of the SHARD phase: the k-split slices of the two weight-gradient
-// GEMMs (they run one after the other and share them), then the attention
-// backward's own (delta [n_q, T] and the per-head dK/dV shares).
+// Workspace of the SHARD phase: the k-split slices of the dO GEMM and of the
+// two weight-gradient GEMMs (they run one after the other and share them),
+// then the attention backward's own (delta [n_q, T] and the per-head dK/dV
+// shares).
 size_t attn_ksplit_bytes(const tp_attn_desc* d) {
   const int64_t T = d->batch * d->seq, H = d->hidden;
   const int64_t W = (int64_t)(d->n_q + 2 * d->n_kv) * d->head_dim, Wo = (int64_t)d->n_q * d->head_dim;
-  const size_t a = gemm_ksplit_workspace(H, Wo, T), b = gemm_ksplit_workspace(W, H, T);
-  return ((a > b ? a : b) + 255) / 256 * 256;
+  size_t m = gemm_ksplit_workspace(H, Wo, T);
+  const size_t b = gemm_ksplit_workspace(W, H, T), c = gemm_ksplit_workspace_bf16(T, Wo, H);  // dW_qkv, dO
+  if (b > m) m = b;
+  if (c > m) m = c;
+  return (m + 255) / 256 * 256;
 }
 
 }  // namespace
@@ -994,6 +998,8 @@ int tp_attn_backward(const tp_attn_desc* d, int32_t phase, const tp_attn_bwd_arg
   b1.ldb = Wo;
   b1.C = a->d_attn_out;
   b1.ldc = Wo;
+  b1.ksplit = gemm_ksplit(b1.M, b1.N, b1.K);
+  b1.ws = ksws;
   b1.tag = "gemm_attn_dgrad_out";
   CHECK_HIP(launch_gemm_bf16(true, false, kEpiStoreBf16, b1, s), "dO GEMM");
   // d_w_o = d_out^T O ([H, T] x [T, n_q D])

@@ -146,7 +146,29 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(float* __restrict__ 
   }
 }
 
+// C (bf16) = the sum of nslices fp32 slices [M, N] (row length N) in index order.
+__global__ __launch_bounds__(256) void ksplit_reduce_bf16_kernel(bf16_t* __restrict__ C, const float* __restrict__ ws,
+                                                                  int nslices, int64_t M, int64_t N4, int64_t ldc) {
+  const int64_t total = M * N4, stride = (int64_t)gridDim.x * blockDim.x, slice = M * N4 * 4;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+    const int64_t m = e / N4, n = 4 * (e - m * N4);
+    const float* src = ws + m * N4 * 4 + n;
+    floatx4 acc = load4<float>(src);
+    for (int s = 1; s < nslices; ++s) acc += load4<float>(src + (int64_t)s * slice);
+    store4<bf16_t>(C + m * ldc + n, acc);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_ksplit_reduce_bf16(void* C, const float* ws, int nslices, int64_t M, int64_t N, int64_t ldc,
+                                     hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  KernelTimer timer("ksplit_reduce_bf16", s);
+  hipLaunchKernelGGL(ksplit_reduce_bf16_kernel, dim3(grid_for(M * N / 4, 256)), dim3(256), 0, s,
+                     static_cast<bf16_t*>(C), ws, nslices, M, N / 4, ldc);
+  return hipGetLastError();
+}
 
 hipError_t launch_ksplit_reduce(float* C, const float* ws, int nslices, int64_t M, int64_t N, int64_t ldc,
                                 hipStream_t s) {

@@ -624,35 +624,51 @@ hipError_t launch_pingpong(const GemmArgs& ga, int ntm, int ntn, hipStream_t s) 
   return hipGetLastError();
 }
 
-// OP: PpBf16, or PpFp8<FA, FB> (both operands K-contiguous).
+// The GEMM's workgroups alone (no k-split reduction).  OP: PpBf16, or
+// PpFp8<FA, FB> (both operands K-contiguous).
+template <bool AK, bool BKC, int EPI, class OP = PpBf16>
+hipError_t launch_tiles(const GemmArgs& ga, int ntm, int ntn, hipStream_t s) {
+  static_assert(!OP::kFp8 || (AK && BKC), "FP8 operands are K-contiguous");
+  KernelTimer timer(ga.tag ? ga.tag : "gemm", s);
+  if constexpr (AK && BKC) {
+    return launch_pingpong<EPI, OP>(ga, ntm, ntn, s);
+  } else {
+    // the tile shape with the least (rounds of one workgroup per CU) x (tile area); a function of the
+    // shape and the CU count only, so results are reproducible on a given device
+    const int cus = device_cus();
+    const int64_t c0 = tile_cost<Tile256x256>(ga, ga.ksplit, cus);
+    const int64_t cn = tile_cost<Tile256x224>(ga, ga.ksplit, cus);
+    const int64_t cm = tile_cost<Tile224x256>(ga, ga.ksplit, cus);
+    if (cn < c0 && cn <= cm) return launch_two_stage<AK, BKC, EPI, Tile256x224>(ga, s);
+    if (cm < c0) return launch_two_stage<AK, BKC, EPI, Tile224x256>(ga, s);
+    return launch_two_stage<AK, BKC, EPI, Tile256x256>(ga, s);
+  }
+}
+
 template <bool AK, bool BKC, int EPI, class OP = PpBf16>
 hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
-  static_assert(!OP::kFp8 || (AK && BKC), "FP8 operands are K-contiguous");
   const int ntm = (int)((g.M + kBM - 1) / kBM);
   const int ntn = (EPI == kEpiSwigluFwd) ? (int)((g.ffn + kSwigluChannels - 1) / kSwigluChannels)
                                          : (int)((g.N + kBN - 1) / kBN);
   if (ntm == 0 || ntn == 0) return hipSuccess;
   GemmArgs ga = g;
+  if constexpr (EPI == kEpiStoreBf16 && !OP::kFp8) {
+    if (ga.ws && ga.ksplit > 1 && ga.N % 4 == 0) {
+      // every slice in fp32 in the workspace, then their sum as bf16
+      GemmArgs gf = ga;
+      gf.C = ga.ws;
+      gf.ldc = ga.N;
+      gf.ws = ga.ws + ga.M * ga.N;
+      gf.accum = 0;
+      const hipError_t e = launch_tiles<AK, BKC, kEpiStoreF32, OP>(gf, ntm, ntn, s);
+      if (e != hipSuccess) return e;
+      return launch_ksplit_reduce_bf16(ga.C, ga.ws, ga.ksplit, ga.M, ga.N, ga.ldc, s);
+    }
+  }
   if (EPI != kEpiStoreF32 || !ga.ws) ga.ksplit = 1;
   if (ga.ksplit < 1) ga.ksplit = 1;
-  {
-    KernelTimer timer(g.tag ? g.tag : "gemm", s);
-    hipError_t e;
-    if constexpr (AK && BKC) {
-      e = launch_pingpong<EPI, OP>(ga, ntm, ntn, s);
-    } else {
-      // the tile shape with the least (rounds of one workgroup per CU) x (tile area); a function of the
-      // shape and the CU count only, so results are reproducible on a given device
-      const int cus = device_cus();
-      const int64_t c0 = tile_cost<Tile256x256>(ga, ga.ksplit, cus);
-      const int64_t cn = tile_cost<Tile256x224>(ga, ga.ksplit, cus);
-      const int64_t cm = tile_cost<Tile224x256>(ga, ga.ksplit, cus);
-      if (cn < c0 && cn <= cm) e = launch_two_stage<AK, BKC, EPI, Tile256x224>(ga, s);
-      else if (cm < c0) e = launch_two_stage<AK, BKC, EPI, Tile224x256>(ga, s);
-      else e = launch_two_stage<AK, BKC, EPI, Tile256x256>(ga, s);
-    }
-    if (e != hipSuccess || ga.ksplit == 1) return e;
-  }
+  const hipError_t e = launch_tiles<AK, BKC, EPI, OP>(ga, ntm, ntn, s);
+  if (e != hipSuccess || ga.ksplit == 1) return e;
   return launch_ksplit_reduce(static_cast<float*>(ga.C), ga.ws, ga.ksplit - 1, ga.M, ga.N, ga.ldc, s);
 }
 

@@ -54,9 +54,11 @@ struct GemmArgs {
   const void* bias;  // GeLU fwd: b_in [N]; residual: b_down [N]
   int64_t ffn;       // F (column offset of the up half in [T, 2F] tensors)
   const char* tag;   // kernel name for timing
-  // kEpiStoreF32 only: split the k range over `ksplit` workgroups per tile;
+  // kEpiStoreF32: split the k range over `ksplit` workgroups per tile;
   // slice 0 writes C, slice s > 0 writes ws + (s - 1) * M * ldc, and a second
-  // kernel adds the slices to C in index order.  ksplit = 1 ignores ws.
+  // kernel adds the slices to C in index order.  kEpiStoreBf16: every slice s
+  // writes fp32 to ws + s * M * N (row length N) and the second kernel writes
+  // their sum, in index order, to C as bf16.  ksplit = 1 ignores ws.
   int ksplit;
   float* ws;
   // kEpiStoreF32 only: add C's current values to the product (slice 0 reads
@@ -79,6 +81,11 @@ inline int gemm_ksplit(int64_t M, int64_t N, int64_t K) {
 }
 inline size_t gemm_ksplit_workspace(int64_t M, int64_t N, int64_t K) {
   return (size_t)(gemm_ksplit(M, N, K) - 1) * (size_t)(M * N) * sizeof(float);
+}
+// The same for a bf16-output GEMM (every slice in the workspace).
+inline size_t gemm_ksplit_workspace_bf16(int64_t M, int64_t N, int64_t K) {
+  const int ks = gemm_ksplit(M, N, K);
+  return ks > 1 ? (size_t)ks * (size_t)(M * N) * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm(DType dt, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs& g,
@@ -147,6 +154,8 @@ hipError_t launch_partial_sum(const float* const* parts, int n_parts, int64_t ro
 
 // C[m, n] = ((C[m, n] + ws[0][m, n]) + ws[1][m, n]) + ... over `nslices`
 // [M, ldc] fp32 slices (the k-slices of a split GEMM, added in index order).
+hipError_t launch_ksplit_reduce_bf16(void* C, const float* ws, int nslices, int64_t M, int64_t N, int64_t ldc,
+                                     hipStream_t s);
 hipError_t launch_ksplit_reduce(float* C, const float* ws, int nslices, int64_t M, int64_t N, int64_t ldc,
                                 hipStream_t s);
 
