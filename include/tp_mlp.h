@@ -557,10 +557,14 @@ size_t tp_attention_backward_workspace_bytes(int64_t batch, int64_t seq, int32_t
  *   number of distinct kernel names (or a negative error code);
  *   tp_mlp_profile_entry(i, ...) returns entry i: name (valid until the next
  *   enable(1) or count call), number of launches and total milliseconds.
+ *   tp_mlp_profile_only(name) restricts recording to the kernels of that
+ *   name (the names tp_mlp_profile_entry reports); NULL records every kernel
+ *   again.  The name is copied.
  * Event recording adds a few microseconds per launch; leave it off outside
- * measurements.
+ * measurements, or restrict it to the kernel being measured.
  */
 int tp_mlp_profile_enable(int32_t on);
+int tp_mlp_profile_only(const char* name);
 int32_t tp_mlp_profile_count(void);
 int tp_mlp_profile_entry(int32_t i, const char** name, int64_t* launches, double* total_ms);
 

@@ -37,7 +37,7 @@ EXPORTED = ("tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_works
             "tp_mlp_fp8_meta_init", "tp_mlp_fp8_cast", "tp_mlp_fp8_update_scales", "tp_mlp_forward_fp8",
             "tp_mlp_backward_fp8", "tp_mlp_fp8_gemm", "tp_mlp_fp8_gemm_workspace_bytes", "tp_attn_forward",
             "tp_attn_backward", "tp_attn_workspace_bytes", "tp_attention_forward", "tp_attention_backward",
-            "tp_attention_backward_workspace_bytes")
+            "tp_attention_backward_workspace_bytes", "tp_mlp_profile_only")
 
 
 class TPMLPError(RuntimeError):
@@ -177,6 +177,8 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_version.restype = ctypes.c_char_p
         L.tp_mlp_profile_enable.argtypes = [ctypes.c_int32]
         L.tp_mlp_profile_enable.restype = ctypes.c_int
+        L.tp_mlp_profile_only.argtypes = [ctypes.c_char_p]
+        L.tp_mlp_profile_only.restype = ctypes.c_int
         L.tp_mlp_profile_count.argtypes = []
         L.tp_mlp_profile_count.restype = ctypes.c_int32
         L.tp_mlp_profile_entry.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_char_p),
@@ -409,6 +411,11 @@ def tp_mlp_version() -> str:
 
 def tp_mlp_profile_enable(on: bool) -> None:
     _check(lib().tp_mlp_profile_enable(1 if on else 0))
+
+
+def tp_mlp_profile_only(name) -> None:
+    """Record only the kernels named ``name`` (None: every kernel)."""
+    _check(lib().tp_mlp_profile_only(name.encode() if name is not None else None))
 
 
 def tp_mlp_profile_entries() -> dict:

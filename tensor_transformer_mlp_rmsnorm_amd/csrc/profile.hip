@@ -1,6 +1,9 @@
 // Per-kernel timing with HIP events, for measurement.  Off by default; when
-// on, every kernel launch of the library is bracketed by two events recorded
-// on the launch's own stream, and durations are aggregated by kernel name.
+// on, every kernel launch of the library (or every launch of one kernel name)
+// is bracketed by two events recorded on the launch's own stream, and
+// durations are aggregated by kernel name.
+#include <string.h>
+
 #include <map>
 #include <mutex>
 #include <string>
@@ -20,6 +23,8 @@ struct Record {
 struct Profiler {
   std::mutex mu;
   bool on = false;
+  bool filtered = false;  // record only the kernels named `only`
+  std::string only;
   std::vector<Record> records;
   std::vector<hipEvent_t> pool;
   struct Agg {
@@ -59,7 +64,7 @@ Profiler& prof() {
 KernelTimer::KernelTimer(const char* name, hipStream_t s) : name_(name), stream_(s) {
   Profiler& p = prof();
   std::lock_guard<std::mutex> g(p.mu);
-  if (!p.on) return;
+  if (!p.on || (p.filtered && strcmp(name, p.only.c_str()) != 0)) return;
   start_ = p.take();
   stop_ = p.take();
   if (start_ && stop_ && hipEventRecord(start_, s) == hipSuccess) {
@@ -91,6 +96,14 @@ int tp_mlp_profile_enable(int32_t on) {
     p.agg_valid = false;
   }
   p.on = on != 0;
+  return TP_MLP_OK;
+}
+
+int tp_mlp_profile_only(const char* name) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.filtered = name != nullptr;
+  p.only = name ? name : "";
   return TP_MLP_OK;
 }
 
