@@ -107,18 +107,31 @@ __global__ __launch_bounds__(kSgdBlock) void sgd_kernel(SgdList L, float lr) {
   T* pout = static_cast<T*>(sg.pout);
   const int64_t e0 = ((int64_t)blockIdx.x - sg.block0) * kSgdPerBlock + (int64_t)threadIdx.x * kSgdPerThread;
   if (e0 + kSgdPerThread <= sg.n) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t e = e0 + 4 * h;
-      const floatx4 gv = load4<float>(sg.g + e);
-      floatx4 v;
-      if constexpr (MASTER) {
-        v = load4<float>(sg.min + e) - lr * gv;
-        store4<float>(sg.mout + e, v);
-      } else {
-        v = load4<T>(pin + e) - lr * gv;
-      }
-      store4<T>(pout + e, v);
+    // 16-byte accesses throughout (every pointer is 16-byte aligned); the
+    // gradient is read once, with the non-temporal hint
+    const floatx4 g0 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(sg.g + e0));
+    const floatx4 g1 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(sg.g + e0 + 4));
+    floatx4 v0, v1;
+    if constexpr (MASTER) {
+      v0 = load4<float>(sg.min + e0) - lr * g0;
+      v1 = load4<float>(sg.min + e0 + 4) - lr * g1;
+      store4<float>(sg.mout + e0, v0);
+      store4<float>(sg.mout + e0 + 4, v1);
+    } else if constexpr (sizeof(T) == 2) {
+      float f[8];
+      Chunk<bf16_t>::unpack(*reinterpret_cast<const uint4*>(pin + e0), f);
+      v0 = floatx4{f[0], f[1], f[2], f[3]} - lr * g0;
+      v1 = floatx4{f[4], f[5], f[6], f[7]} - lr * g1;
+    } else {
+      v0 = load4<T>(pin + e0) - lr * g0;
+      v1 = load4<T>(pin + e0 + 4) - lr * g1;
+    }
+    if constexpr (sizeof(T) == 2) {
+      const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      *reinterpret_cast<uint4*>(pout + e0) = Chunk<bf16_t>::pack(f);
+    } else {
+      store4<T>(pout + e0, v0);
+      store4<T>(pout + e0 + 4, v1);
     }
   } else {
     for (int64_t e = e0; e < sg.n; ++e) {

@@ -8,7 +8,8 @@
 //   dx_ti = dY_ti + rstd_t dN_ti w_i - x_ti rstd_t^3 c_t
 //   dw_i  = sum_t dN_ti x_ti rstd_t,   db_i = sum_t dY_ti
 // Both are HBM-bound.  The forward reads each row once (one wavefront per
-// row, the row held in registers) and writes N and rstd.  The backward
+// row, the row held in registers, the next row loading meanwhile) and writes
+// N and rstd.  The backward
 // streams dN (fp32), x and dY once, writes dx, and reduces the two column
 // sums deterministically: each workgroup owns a fixed range of rows and
 // fixed columns per thread, writes one partial row, and a second kernel sums
@@ -19,44 +20,91 @@
 namespace tpmlp {
 namespace {
 
-constexpr int kFwdRowsPerBlock = 4;  // one wave per row
+// 16 bytes read with the non-temporal hint (data read once: it need not stay
+// in the caches).
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// Loads are issued unconditionally from a clamped index and the values of
+// lanes past the row end zeroed afterwards, so no load sits in a branch (the
+// compiler would wait for each one before leaving it).
+__device__ __forceinline__ int clampi(int i, int n) { return i < n ? i : n - 1; }
+__device__ __forceinline__ uint4 masked16(uint4 v, bool ok) { return ok ? v : make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ floatx4 masked4(floatx4 v, bool ok) { return ok ? v : floatx4{0.f, 0.f, 0.f, 0.f}; }
 
-template <typename T, int NC>
+// Forward: one wave per row, 4 waves per workgroup, each wave taking rows
+// w, w + 4, w + 8, w + 12 of the workgroup's 16; the norm weight is read once
+// per wave and the next row is loaded while the current one is reduced.
+constexpr int kFwdWaves = 4, kFwdRowsPerWave = 4, kFwdRowsPerBlock = kFwdWaves * kFwdRowsPerWave;
+
+// FULL: the row is exactly NC chunks per lane (no lane past its end), so no
+// access needs a guard.
+template <typename T, int NC, bool FULL>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ x, const T* __restrict__ w,
                                                           T* __restrict__ n, float* __restrict__ rstd,
                                                           int64_t rows, int H, float eps) {
   constexpr int E = Elem<T>::kPerChunk;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kFwdRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  // Rows of up to 4096 bf16 (2048 fp32) keep the weight and the next row in
+  // registers too (two row buffers used in turn, so no register copy waits
+  // for a load); wider rows reload the weight and load one row at a time.
+  constexpr bool kPf = NC <= 8;
+  constexpr int NB = kPf ? 2 : 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row0 = (int64_t)blockIdx.x * kFwdRowsPerBlock + wave;
+  if (row0 >= rows) return;
   const int nch = H / E;
-  const T* xr = x + row * H;
-  uint4 v[NC];
-  float ss = 0.f;
+  uint4 wv[kPf ? NC : 1], v[NB][NC];
+  auto load_row = [&](int64_t row, uint4* dst) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int idx = lane + 64 * c;
-    v[c] = make_uint4(0, 0, 0, 0);
-    if (idx < nch) v[c] = *reinterpret_cast<const uint4*>(xr + (int64_t)idx * E);
-    float f[E];
-    Chunk<T>::unpack(v[c], f);
+    for (int c = 0; c < NC; ++c) {
+      const int idx = lane + 64 * c;
+      dst[c] = FULL ? load_nt16(x + row * H + (int64_t)idx * E)
+                    : masked16(load_nt16(x + row * H + (int64_t)clampi(idx, nch) * E), idx < nch);
+    }
+  };
+  load_row(row0, v[0]);
+  if constexpr (kPf) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) ss += f[e] * f[e];
+    for (int c = 0; c < NC; ++c) {
+      const int idx = lane + 64 * c;
+      wv[c] = FULL ? *reinterpret_cast<const uint4*>(w + (int64_t)idx * E)
+                   : masked16(*reinterpret_cast<const uint4*>(w + (int64_t)clampi(idx, nch) * E), idx < nch);
+    }
   }
-  ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)H + eps);
-  if (lane == 0) rstd[row] = r;
-  T* nr = n + row * H;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int idx = lane + 64 * c;
-    if (idx >= nch) continue;
-    float f[E], wf[E];
-    Chunk<T>::unpack(v[c], f);
-    Chunk<T>::unpack(*reinterpret_cast<const uint4*>(w + (int64_t)idx * E), wf);
+  for (int i = 0; i < kFwdRowsPerWave; ++i) {
+    const int64_t row = row0 + (int64_t)kFwdWaves * i;
+    if (row >= rows) break;
+    const int64_t next = row + kFwdWaves;
+    uint4* cur = v[kPf ? (i & 1) : 0];
+    if (kPf && i + 1 < kFwdRowsPerWave && next < rows) load_row(next, v[(i + 1) & (NB - 1)]);
+    float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) f[e] = f[e] * r * wf[e];
-    *reinterpret_cast<uint4*>(nr + (int64_t)idx * E) = Chunk<T>::pack(f);
+    for (int c = 0; c < NC; ++c) {
+      float f[E];
+      Chunk<T>::unpack(cur[c], f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) ss += f[e] * f[e];
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)H + eps);
+    if (lane == 0) rstd[row] = r;
+    T* nr = n + row * H;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int idx = lane + 64 * c;
+      if (!FULL && idx >= nch) continue;
+      float f[E], wf[E];
+      Chunk<T>::unpack(cur[c], f);
+      if constexpr (kPf) Chunk<T>::unpack(wv[c], wf);
+      else Chunk<T>::unpack(*reinterpret_cast<const uint4*>(w + (int64_t)idx * E), wf);
+#pragma unroll
+      for (int e = 0; e < E; ++e) f[e] = f[e] * r * wf[e];
+      *reinterpret_cast<uint4*>(nr + (int64_t)idx * E) = Chunk<T>::pack(f);
+    }
+    if (!kPf && i + 1 < kFwdRowsPerWave && next < rows) load_row(next, v[0]);
   }
 }
 
@@ -71,14 +119,26 @@ hipError_t fwd_t(const void* x, const void* w, void* n, float* rstd, int64_t T_,
   const T* wp = static_cast<const T*>(w);
   T* np_ = static_cast<T*>(n);
   KernelTimer timer("rmsnorm_fwd", s);
-#define TPMLP_FWD(NC) \
-  hipLaunchKernelGGL((rmsnorm_fwd_kernel<T, NC>), grid, dim3(256), 0, s, xp, wp, np_, rstd, T_, (int)H, eps)
-  if (per_lane <= 1) TPMLP_FWD(1);
-  else if (per_lane <= 2) TPMLP_FWD(2);
-  else if (per_lane <= 4) TPMLP_FWD(4);
-  else if (per_lane <= 8) TPMLP_FWD(8);
-  else if (per_lane <= 16) TPMLP_FWD(16);
-  else TPMLP_FWD(32);
+#define TPMLP_FWD(NC)                                                                                      \
+  if (nch == 64 * (NC))                                                                                      \
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<T, NC, true>), grid, dim3(256), 0, s, xp, wp, np_, rstd, T_, (int)H, \
+                       eps);                                                                                 \
+  else                                                                                                       \
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<T, NC, false>), grid, dim3(256), 0, s, xp, wp, np_, rstd, T_,      \
+                       (int)H, eps)
+  if (per_lane <= 1) {
+    TPMLP_FWD(1);
+  } else if (per_lane <= 2) {
+    TPMLP_FWD(2);
+  } else if (per_lane <= 4) {
+    TPMLP_FWD(4);
+  } else if (per_lane <= 8) {
+    TPMLP_FWD(8);
+  } else if (per_lane <= 16) {
+    TPMLP_FWD(16);
+  } else {
+    TPMLP_FWD(32);
+  }
 #undef TPMLP_FWD
   return hipGetLastError();
 }
@@ -95,12 +155,13 @@ __host__ __device__ inline int64_t bwd_rows_per_block(int64_t T_) {
   return r < 8 ? 8 : r;
 }
 
-template <typename T, int UPT>
+// FULL: every thread's UPT units lie inside the row (no guards needed).
+template <typename T, int UPT, bool FULL>
 __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_kernel(
     const float* __restrict__ dN, const T* __restrict__ x, const T* __restrict__ dY,
     const float* __restrict__ rstd, const T* __restrict__ w, T* __restrict__ dx, float* __restrict__ ws_dw,
     float* __restrict__ ws_db, int64_t rows, int H, int64_t rows_per_block) {
-  __shared__ float red[2][kBwdThreads / 64];
+  __shared__ float red[2][2][kBwdThreads / 64];  // [slot][row of the pair][wave]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nunits = H / 4;  // 4 columns per unit
   const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
@@ -109,46 +170,66 @@ __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_kernel(
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
     const int q = tid + kBwdThreads * u;
-    wv[u] = (q < nunits) ? load4<T>(w + 4 * q) : floatx4{0.f, 0.f, 0.f, 0.f};
+    wv[u] = FULL ? load4<T>(w + 4 * q) : masked4(load4<T>(w + 4 * clampi(q, nunits)), q < nunits);
     dwa[u] = floatx4{0.f, 0.f, 0.f, 0.f};
     dba[u] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   const float invH = 1.0f / (float)H;
-  for (int64_t t = r0; t < r1; ++t) {
-    const float r = rstd[t];
-    floatx4 dn[UPT], xv[UPT], dy[UPT];
-    float part = 0.f;
+  // Rows go two at a time (one at a time for wide rows): both rows' loads
+  // are issued together, the two row sums share one barrier (which waits
+  // only for LDS), then both dx rows are written.
+  constexpr int NR = UPT <= 4 ? 2 : 1;
+  for (int64_t t = r0; t < r1; t += NR) {
+    floatx4 dn[NR][UPT], xv[NR][UPT], dy[NR][UPT];
+    float r[NR], part[NR];
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int q = tid + kBwdThreads * u;
-      if (q < nunits) {
-        const int64_t off = t * H + 4 * q;
-        dn[u] = load4<float>(dN + off);
-        xv[u] = load4<T>(x + off);
-        dy[u] = load4<T>(dY + off);
-      } else {
-        dn[u] = xv[u] = dy[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < NR; ++k) {
+      const int64_t tk = t + k < r1 ? t + k : t;  // a missing second row repeats the first (not written)
+      r[k] = rstd[tk];
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int q = tid + kBwdThreads * u;
+        const bool ok = FULL || q < nunits;
+        const int64_t off = tk * H + 4 * (FULL ? q : clampi(q, nunits));
+        dn[k][u] = masked4(__builtin_nontemporal_load(reinterpret_cast<const floatx4*>(dN + off)), ok);
+        xv[k][u] = masked4(load4<T>(x + off), ok);
+        dy[k][u] = masked4(load4<T>(dY + off), ok);
       }
-      const floatx4 p = dn[u] * wv[u] * xv[u];
-      part += (p[0] + p[1]) + (p[2] + p[3]);
     }
-    part = wave_sum(part);
-    const int slot = (int)(t & 1);
-    if (lane == 0) red[slot][wave] = part;
-    __syncthreads();
-    float c = 0.f;
+    __builtin_amdgcn_sched_barrier(0);  // every load of the pair is issued before any use
 #pragma unroll
-    for (int i = 0; i < kBwdThreads / 64; ++i) c += red[slot][i];
-    c *= invH;
-    const float r3c = r * r * r * c;
+    for (int k = 0; k < NR; ++k) {
+      float pk = 0.f;
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int q = tid + kBwdThreads * u;
-      if (q >= nunits) continue;
-      const floatx4 d = dy[u] + r * dn[u] * wv[u] - xv[u] * r3c;
-      store4<T>(dx + t * H + 4 * q, d);
-      dwa[u] += dn[u] * xv[u] * r;
-      dba[u] += dy[u];
+      for (int u = 0; u < UPT; ++u) {
+        const floatx4 p = dn[k][u] * wv[u] * xv[k][u];
+        pk += (p[0] + p[1]) + (p[2] + p[3]);
+      }
+      part[k] = wave_sum(pk);
+    }
+    const int slot = (int)(((t - r0) / NR) & 1);
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < NR; ++k) red[slot][k][wave] = part[k];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      if (t + k >= r1) break;
+      float c = 0.f;
+#pragma unroll
+      for (int i = 0; i < kBwdThreads / 64; ++i) c += red[slot][k][i];
+      c *= invH;
+      const float r3c = r[k] * r[k] * r[k] * c;
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int q = tid + kBwdThreads * u;
+        if (!FULL && q >= nunits) continue;
+        const floatx4 d = dy[k][u] + r[k] * dn[k][u] * wv[u] - xv[k][u] * r3c;
+        store4<T>(dx + (t + k) * H + 4 * q, d);
+        dwa[u] += dn[k][u] * xv[k][u] * r[k];
+        dba[u] += dy[k][u];
+      }
     }
   }
 #pragma unroll
@@ -226,14 +307,24 @@ static hipError_t bwd_t(const float* dN, const void* x, const void* dY, const fl
   T* dxp = static_cast<T*>(dx);
   if (nblk > 0) {
     KernelTimer timer("rmsnorm_bwd", s);
-#define TPMLP_BWD(U)                                                                                           \
-  hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, U>), dim3((unsigned)nblk), dim3(kBwdThreads), 0, s, dN, xp, dyp, rstd, \
-                     wp, dxp, ws_dw, ws_db, T_, (int)H, rpb)
-  if (upt <= 1) TPMLP_BWD(1);
-  else if (upt <= 2) TPMLP_BWD(2);
-  else if (upt <= 4) TPMLP_BWD(4);
-  else if (upt <= 8) TPMLP_BWD(8);
-  else TPMLP_BWD(16);
+#define TPMLP_BWD(U)                                                                                          \
+  if (units == (int64_t)kBwdThreads * (U))                                                                      \
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, U, true>), dim3((unsigned)nblk), dim3(kBwdThreads), 0, s, dN, xp, \
+                       dyp, rstd, wp, dxp, ws_dw, ws_db, T_, (int)H, rpb);                                     \
+  else                                                                                                          \
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, U, false>), dim3((unsigned)nblk), dim3(kBwdThreads), 0, s, dN, xp, \
+                       dyp, rstd, wp, dxp, ws_dw, ws_db, T_, (int)H, rpb)
+    if (upt <= 1) {
+      TPMLP_BWD(1);
+    } else if (upt <= 2) {
+      TPMLP_BWD(2);
+    } else if (upt <= 4) {
+      TPMLP_BWD(4);
+    } else if (upt <= 8) {
+      TPMLP_BWD(8);
+    } else {
+      TPMLP_BWD(16);
+    }
 #undef TPMLP_BWD
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
