@@ -480,10 +480,17 @@ typedef struct {
  *   out (log of each row's softmax denominator, for the backward);
  *   out: without FUSE_EPILOGUE [T, H] fp32, this rank's partial O W_o^T; with
  *   it [T, H] bf16 x + O W_o^T + b_o (b_o [H] bf16, read only then).
+ *   workspace: NULL, or DEVICE scratch (16-byte aligned) of at least
+ *   tp_attn_forward_workspace_bytes(d) bytes (TP_MLP_EWORKSPACE if smaller):
+ *   with it the QKV product, whose W columns give few output tiles, splits
+ *   its k range over more workgroups (fp32 slices added in a fixed order);
+ *   without it the product runs unsplit.  The result bits do not depend on
+ *   workspace's address, only on whether one is given.
  */
 int tp_attn_forward(const tp_attn_desc* d, const void* x, const void* norm_w, const void* w_qkv, const void* w_o,
                     void* normed, float* rstd, void* qkv, void* attn_out, float* lse, void* out, const void* b_o,
-                    void* stream);
+                    void* workspace, size_t workspace_bytes, void* stream);
+size_t tp_attn_forward_workspace_bytes(const tp_attn_desc* d);
 
 typedef struct {
   /* saved from tp_attn_forward */

@@ -37,7 +37,7 @@ EXPORTED = ("tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_works
             "tp_mlp_fp8_meta_init", "tp_mlp_fp8_cast", "tp_mlp_fp8_update_scales", "tp_mlp_forward_fp8",
             "tp_mlp_backward_fp8", "tp_mlp_fp8_gemm", "tp_mlp_fp8_gemm_workspace_bytes", "tp_attn_forward",
             "tp_attn_backward", "tp_attn_workspace_bytes", "tp_attention_forward", "tp_attention_backward",
-            "tp_attention_backward_workspace_bytes", "tp_mlp_profile_only")
+            "tp_attention_backward_workspace_bytes", "tp_mlp_profile_only", "tp_attn_forward_workspace_bytes")
 
 
 class TPMLPError(RuntimeError):
@@ -154,7 +154,9 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_fp8_gemm.restype = ctypes.c_int
         L.tp_mlp_fp8_gemm_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
         L.tp_mlp_fp8_gemm_workspace_bytes.restype = ctypes.c_size_t
-        L.tp_attn_forward.argtypes = [ctypes.POINTER(tp_attn_desc)] + [_vp] * 12
+        L.tp_attn_forward.argtypes = [ctypes.POINTER(tp_attn_desc)] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+        L.tp_attn_forward_workspace_bytes.argtypes = [ctypes.POINTER(tp_attn_desc)]
+        L.tp_attn_forward_workspace_bytes.restype = ctypes.c_size_t
         L.tp_attn_forward.restype = ctypes.c_int
         L.tp_attn_backward.argtypes = [ctypes.POINTER(tp_attn_desc), ctypes.c_int32, ctypes.POINTER(tp_attn_bwd_args),
                                        _vp]
@@ -316,10 +318,14 @@ def make_attn_desc(batch: int, seq: int, hidden: int, n_q: int, n_kv: int, head_
 
 
 def tp_attn_forward(desc: tp_attn_desc, x, norm_w, w_qkv, w_o, normed, rstd, qkv, attn_out, lse, out, b_o=None,
-                    stream=None) -> None:
+                    workspace=None, workspace_bytes: int = 0, stream=None) -> None:
     _check(lib().tp_attn_forward(ctypes.byref(desc), _ptr(x), _ptr(norm_w), _ptr(w_qkv), _ptr(w_o), _ptr(normed),
                                  _ptr(rstd), _ptr(qkv), _ptr(attn_out), _ptr(lse), _ptr(out), _ptr(b_o),
-                                 _stream(stream)))
+                                 _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def tp_attn_forward_workspace_bytes(desc: tp_attn_desc) -> int:
+    return int(lib().tp_attn_forward_workspace_bytes(ctypes.byref(desc)))
 
 
 def tp_attn_workspace_bytes(desc: tp_attn_desc, phase: int) -> int:

@@ -880,9 +880,15 @@ size_t tp_attention_backward_workspace_bytes(int64_t batch, int64_t seq, int32_t
   return attention_bwd_workspace(a);
 }
 
+size_t tp_attn_forward_workspace_bytes(const tp_attn_desc* d) {
+  if (!d || d->batch < 0 || d->seq < 0 || d->hidden <= 0 || d->n_q <= 0 || d->n_kv <= 0 || d->head_dim <= 0) return 0;
+  const int64_t T = d->batch * d->seq, W = (int64_t)(d->n_q + 2 * d->n_kv) * d->head_dim;
+  return gemm_ksplit_workspace_bf16(T, W, d->hidden);
+}
+
 int tp_attn_forward(const tp_attn_desc* d, const void* x, const void* norm_w, const void* w_qkv, const void* w_o,
                     void* normed, float* rstd, void* qkv, void* attn_out, float* lse, void* out, const void* b_o,
-                    void* stream) {
+                    void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "tp_attn_forward";
   g_err[0] = 0;
   int rc = check_attn_desc(d, fn);
@@ -894,6 +900,12 @@ int tp_attn_forward(const tp_attn_desc* d, const void* x, const void* norm_w, co
   REQUIRE_PTR(w_qkv);
   REQUIRE_PTR(w_o);
   if (fuse) REQUIRE_PTR(b_o);
+  const size_t need = tp_attn_forward_workspace_bytes(d);
+  if (workspace) {
+    if (workspace_bytes < need)
+      return fail(TP_MLP_EWORKSPACE, "%s: workspace of %zu bytes required, %zu given", fn, need, workspace_bytes);
+    if (!aligned16(workspace)) return fail(TP_MLP_EALIGN, "%s: workspace is not 16-byte aligned", fn);
+  }
   if (T == 0) return TP_MLP_OK;
   REQUIRE_PTR(x);
   REQUIRE_PTR(normed);
@@ -915,6 +927,10 @@ int tp_attn_forward(const tp_attn_desc* d, const void* x, const void* norm_w, co
   g.ldb = H;
   g.C = qkv;
   g.ldc = W;
+  if (workspace && need > 0) {  // k split over workgroups: the QKV product alone has few output tiles
+    g.ksplit = gemm_ksplit(T, W, H);
+    g.ws = static_cast<float*>(workspace);
+  }
   g.tag = "gemm_qkv";
   CHECK_HIP(launch_gemm_bf16(true, true, kEpiStoreBf16, g, s), "QKV GEMM");
   const AttnShapeArgs a = attn_args(d);

@@ -578,7 +578,8 @@ class AttnStep:
         self.dx, self.d_norm_w, self.d_b_o = emp((T, H)), emp((H,), f32), emp((H,), f32)
         self.new = {name: (torch.empty_like(t) if self.oop else t) for name, t in self._param_list()}
         d0 = self._desc()
-        ws = max(L.tp_attn_workspace_bytes(d0, L.BWD_SHARD), L.tp_attn_workspace_bytes(d0, L.BWD_NORM), 16)
+        ws = max(L.tp_attn_workspace_bytes(d0, L.BWD_SHARD), L.tp_attn_workspace_bytes(d0, L.BWD_NORM),
+                 L.tp_attn_forward_workspace_bytes(d0), 16)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
         self._abl: Dict[str, list] = {}
 
@@ -609,7 +610,7 @@ class AttnStep:
             flags = (L.NORMED_READY if s > 0 else 0) | (L.FUSE_EPILOGUE if self.fuse else 0)
             L.tp_attn_forward(self._desc(flags), self.x, self.norm_w, sh["w_qkv"], sh["w_o"], self.normed, self.rstd,
                               sh["qkv"], sh["attn_out"], sh["lse"], self.out if self.fuse else sh["z"], self.b_o,
-                              stream=st)
+                              workspace=self.workspace, workspace_bytes=self.workspace.numel(), stream=st)
         if self.fuse:
             return
         if mode == "missing_forward_reduce":

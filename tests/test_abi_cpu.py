@@ -327,7 +327,8 @@ def test_attention_checks(lib):
                                 a["flags"], a["dtype"])
 
     fwd = lambda d, **p: lib.tp_attn_forward(ctypes.byref(d), *[p.get(k, A) for k in (
-        "x", "norm_w", "w_qkv", "w_o", "normed", "rstd", "qkv", "attn_out", "lse", "out", "b_o")], None)
+        "x", "norm_w", "w_qkv", "w_o", "normed", "rstd", "qkv", "attn_out", "lse", "out", "b_o")],
+        p.get("ws", None), p.get("ws_bytes", 0), None)
     assert fwd(desc(head_dim=96)) == L.ESHAPE                 # 64 or 128
     assert fwd(desc(n_q=3, n_kv=2)) == L.ESHAPE               # n_q a multiple of n_kv
     assert fwd(desc(dtype=L.F32)) == L.EDTYPE                 # bf16 only
@@ -340,7 +341,14 @@ def test_attention_checks(lib):
     assert fwd(desc(), lse=A + 2) == L.EALIGN                 # lse: 4-byte alignment
     assert fwd(desc(flags=L.FUSE_EPILOGUE), b_o=None) == L.EINVAL
     assert fwd(desc(seq=0), x=None, qkv=None, out=None) == L.OK   # no tokens: a no-op
-    assert lib.tp_attn_forward(None, *([A] * 11), None) == L.EINVAL
+    assert lib.tp_attn_forward(None, *([A] * 11), None, 0, None) == L.EINVAL
+    fneed = lib.tp_attn_forward_workspace_bytes(ctypes.byref(desc(batch=1, seq=8192, hidden=4096, n_q=4, n_kv=1,
+                                                                  head_dim=128)))
+    assert fneed >= 2 * 8192 * 768 * 4                         # the QKV product's k slices (fp32)
+    big = desc(batch=1, seq=8192, hidden=4096, n_q=4, n_kv=1, head_dim=128)
+    assert fwd(big, ws=A, ws_bytes=fneed - 16) == L.EWORKSPACE
+    assert fwd(big, ws=MIS, ws_bytes=fneed) == L.EALIGN
+    assert lib.tp_attn_forward_workspace_bytes(ctypes.byref(desc())) == 0   # K = 128: no split
     d = desc()
     need = lib.tp_attn_workspace_bytes(ctypes.byref(d), L.BWD_SHARD)
     assert need >= 4 * 2 * 64 * 4                              # delta [n_q, T] at least
