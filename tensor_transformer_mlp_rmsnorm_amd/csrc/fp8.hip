@@ -57,12 +57,26 @@ __device__ __forceinline__ float wave_max(float v) {
 // that the column reads below (rows r and r + 64 in one instruction) fall in distinct banks.
 __device__ __forceinline__ int tile_dword(int r, int d) { return r * 32 + (d ^ (((r >> 6) & 1) << 3)); }
 
+// The 4 x 4 byte transpose of the dwords a, b, c, e (byte k of each): out[k]
+// holds byte k of a, b, c, e in that order.
+__device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t e, uint32_t (&out)[4]) {
+  const uint32_t ab01 = __builtin_amdgcn_perm(b, a, 0x05010400u), ab23 = __builtin_amdgcn_perm(b, a, 0x07030602u);
+  const uint32_t ce01 = __builtin_amdgcn_perm(e, c, 0x05010400u), ce23 = __builtin_amdgcn_perm(e, c, 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(ce01, ab01, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(ce01, ab01, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(ce23, ab23, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(ce23, ab23, 0x07060302u);
+}
+
 // Codes of a bf16 [R, C] matrix, 128 x 128 tiles over a grid-stride loop:
 // out [R, C] (if ROW) and out_t [C, ldt] (if TRANS; the rows R .. ldt-1 of
 // the tiles give zero codes, so out_t's padding columns are written as 0).
 // Load: thread t takes rows t/8 + 32 i (i < 4) and the 16 columns 16 (t%8) ..;
-// transposed store: column t/2, rows 64 (t%2) .. + 63.  One atomic maximum
-// per workgroup folds the amax into meta[2].
+// a tile wholly inside the matrix issues its 8 loads before any use (edge
+// tiles load under guards).  Transposed store: thread t reads the code dwords
+// of columns 4 (t%32) .. + 3 in rows 16 (t/32) .. + 15 from LDS, transposes
+// them in registers (byte permutes) and writes 16 bytes to each of the four
+// columns.  One atomic maximum per workgroup folds the amax into meta[2].
 template <int FMT, bool ROW, bool TRANS>
 __global__ __launch_bounds__(kCastThreads) void cast_kernel(const bf16_t* __restrict__ x, int64_t R, int64_t C,
                                                             uint8_t* __restrict__ out, uint8_t* __restrict__ out_t,
@@ -75,52 +89,65 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(const bf16_t* __rest
   float amax = 0.0f;
   for (int tid = blockIdx.x; tid < tiles; tid += gridDim.x) {
     const int64_t r0 = (int64_t)(tid / tiles_c) * kCastTile, c0 = (int64_t)(tid % tiles_c) * kCastTile;
+    const bool full = r0 + kCastTile <= R && c0 + kCastTile <= C;  // the same for the whole workgroup
+    uint2 q[4][2];
+    if (full) {
+      uint4 v[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16_t* src = x + (r0 + (t >> 3) + 32 * i) * C + c0 + cq;
+        v[i][0] = *reinterpret_cast<const uint4*>(src);
+        v[i][1] = *reinterpret_cast<const uint4*>(src + 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        q[i][0] = cast8<FMT>(v[i][0], s, lim, amax);
+        q[i][1] = cast8<FMT>(v[i][1], s, lim, amax);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = r0 + (t >> 3) + 32 * i, c = c0 + cq;
+        q[i][0] = q[i][1] = make_uint2(0u, 0u);  // past R or C: zero codes
+        if (r < R) {
+          const bf16_t* src = x + r * C + c;
+          if (c < C) q[i][0] = cast8<FMT>(*reinterpret_cast<const uint4*>(src), s, lim, amax);
+          if (c + 8 < C) q[i][1] = cast8<FMT>(*reinterpret_cast<const uint4*>(src + 8), s, lim, amax);
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = (t >> 3) + 32 * i;
       const int64_t r = r0 + rr, c = c0 + cq;
-      uint2 q0 = make_uint2(0u, 0u), q1 = make_uint2(0u, 0u);  // past R or C: zero codes
-      if (r < R) {
-        const bf16_t* src = x + r * C + c;
-        if (c < C) q0 = cast8<FMT>(*reinterpret_cast<const uint4*>(src), s, lim, amax);
-        if (c + 8 < C) q1 = cast8<FMT>(*reinterpret_cast<const uint4*>(src + 8), s, lim, amax);
-        if constexpr (ROW) {
-          uint8_t* dst = out + r * C + c;  // 8-byte aligned (C is a multiple of 8); 16 when C is of 16
-          if (c + 8 < C && (C & 15) == 0) {
-            *reinterpret_cast<uint4*>(dst) = make_uint4(q0.x, q0.y, q1.x, q1.y);
-          } else {
-            if (c < C) *reinterpret_cast<uint2*>(dst) = q0;
-            if (c + 8 < C) *reinterpret_cast<uint2*>(dst + 8) = q1;
-          }
+      if constexpr (ROW) {
+        uint8_t* dst = out + r * C + c;  // 8-byte aligned (C is a multiple of 8); 16 when C is of 16
+        if (full && (C & 15) == 0) {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(q[i][0].x, q[i][0].y, q[i][1].x, q[i][1].y);
+        } else if (r < R) {
+          if (c < C) *reinterpret_cast<uint2*>(dst) = q[i][0];
+          if (c + 8 < C) *reinterpret_cast<uint2*>(dst + 8) = q[i][1];
         }
       }
-      if constexpr (TRANS) {
-        const int d = cq >> 2;  // 4 dwords of codes
-        *reinterpret_cast<uint4*>(&tile[tile_dword(rr, d)]) = make_uint4(q0.x, q0.y, q1.x, q1.y);
-      }
+      if constexpr (TRANS)
+        *reinterpret_cast<uint4*>(&tile[tile_dword(rr, cq >> 2)]) =
+            make_uint4(q[i][0].x, q[i][0].y, q[i][1].x, q[i][1].y);
     }
     if constexpr (TRANS) {
       __syncthreads();
-      const int col = t >> 1, seg = (t & 1) * 64;
-      const int64_t c = c0 + col;
-      if (c < C) {
-        const uint8_t* tb = reinterpret_cast<const uint8_t*>(tile);
-        const int dw = col >> 2, byte = col & 3;
+      const int dw = t & 31, rb = t >> 5;
+      uint32_t d[16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t r = r0 + seg + 16 * j;
-          uint32_t w[4];
+      for (int j = 0; j < 16; ++j) d[j] = tile[tile_dword(16 * rb + j, dw)];
+      uint32_t o[4][4];  // [row quad m][column k]
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            uint32_t v = 0;
+      for (int m = 0; m < 4; ++m) transpose4x4(d[4 * m], d[4 * m + 1], d[4 * m + 2], d[4 * m + 3], o[m]);
+      const int64_t r = r0 + 16 * rb;
+      if (r < ldt) {  // ldt and r are multiples of 16: the whole 16 bytes lie inside the row
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const int rr = seg + 16 * j + 4 * k + b;
-              v |= (uint32_t)tb[tile_dword(rr, dw) * 4 + byte] << (8 * b);
-            }
-            w[k] = v;
-          }
-          if (r < ldt) *reinterpret_cast<uint4*>(out_t + c * ldt + r) = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int k = 0; k < 4; ++k) {
+          const int64_t c = c0 + 4 * dw + k;
+          if (c < C) *reinterpret_cast<uint4*>(out_t + c * ldt + r) = make_uint4(o[0][k], o[1][k], o[2][k], o[3][k]);
         }
       }
       __syncthreads();  // the tile is rewritten by the next iteration
