@@ -25,23 +25,24 @@
 // j is the (i mod 4)-th 16-bit value at the address of lane 4 j + i / 4.  The
 // backward kernels use the same device for Q^T, dO^T and K^T.
 //
-// Forward: one workgroup per (query block of 64, head, batch), 4 waves of 16
-// queries; K and V tiles of 64 keys in LDS; online softmax in exp2 with the
-// 1/sqrt(D) scale folded in.  The probabilities P and the score gradients dS
+// Forward: one workgroup of 8 waves per (query block of 64, head, batch),
+// two 64-key tiles per step, each wave 32 queries x 32 keys of a tile; online
+// softmax in exp2 with the 1/sqrt(D) scale folded in, the key parts of a
+// query merged at the end.  The score gradients dS (and the forward's P)
 // enter their products as a bf16 pair (hi + lo, see pack_slots).  Backward
 // (no atomics): dK and dV per (key block of 64, query head, batch) over the
 // query blocks at or after the key block, the shares of a group's query heads
 // then added in a fixed order by a small kernel; dQ per (query block, head,
 // batch) over the key blocks up to it; both recompute P from lse and use
-// delta = rowsum(dO o O) from a small kernel.  Every loop issues the global
-// loads of its next tile before the products of the current one.
+// delta = rowsum(dO o O) from a small kernel.  Tiles reach LDS by DMA into
+// two buffers used in turn.
 #include "common.h"
 #include "kernels.h"
 
 namespace tpmlp {
 namespace {
 
-constexpr int kAttnBlock = 64, kAttnThreads = 256;
+constexpr int kAttnBlock = 64;
 constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
 // The forward's running maximum is raised (and the partial output rescaled)
 // only when a score exceeds it by more than this many powers of two, so the
@@ -110,53 +111,6 @@ struct Tile {
       out[h] = __builtin_bit_cast(uint2, v);
     }
     return make_uint4(out[0].x, out[0].y, out[1].x, out[1].y);
-  }
-  // A tile's worth of this thread's chunks, staged in registers so the next
-  // tile's global loads overlap the current tile's products.
-  static constexpr int kPer = kAttnBlock * kChunks / kAttnThreads;
-  struct Regs {
-    uint4 v[kPer];
-  };
-  __device__ __forceinline__ static void store(char* base, const Regs& r, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = tid + kAttnThreads * i;
-      *reinterpret_cast<uint4*>(base + chunk_off(idx / kChunks, idx % kChunks)) = r.v[i];
-    }
-  }
-};
-
-// One thread's share of the 64-row tiles of a [rows, ld] bf16 matrix at
-// columns col0 .. col0 + D - 1 (element offsets fit 32 bits: the callers hold
-// fewer than 2^31 elements).
-template <int D>
-struct TileSrc {
-  static constexpr int kPer = Tile<D>::kPer;
-  static constexpr int kRowStep = kAttnThreads / Tile<D>::kChunks;  // rows between a thread's chunks
-  const bf16_t* base;
-  uint32_t ld_tile;  // 64 rows, in elements
-  uint32_t step;     // kRowStep rows, in elements
-  uint32_t off0;     // this thread's first chunk within a tile
-  int row0;
-  __device__ __forceinline__ TileSrc(const bf16_t* p, int64_t ld, int64_t col0, int tid) : base(p + col0) {
-    ld_tile = (uint32_t)(kAttnBlock * ld);
-    step = (uint32_t)(kRowStep * ld);
-    row0 = tid / Tile<D>::kChunks;
-    off0 = (uint32_t)(row0 * ld + 8 * (tid % Tile<D>::kChunks));
-  }
-  // Tile `blk` (rows 64 blk ..); rows at or past `rows` are zero.
-  __device__ __forceinline__ void fetch(typename Tile<D>::Regs& r, int blk, int64_t rows) const {
-    const bf16_t* p = base + (size_t)blk * ld_tile;
-    const int64_t left = rows - (int64_t)blk * kAttnBlock;
-    if (left >= kAttnBlock) {
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) r.v[i] = *reinterpret_cast<const uint4*>(p + off0 + i * step);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        r.v[i] = row0 + i * kRowStep < left ? *reinterpret_cast<const uint4*>(p + off0 + i * step)
-                                            : make_uint4(0u, 0u, 0u, 0u);
-    }
   }
 };
 
@@ -255,23 +209,11 @@ struct AttnDims {
   float scale;                  // 1 / sqrt(D)
 };
 
-// Workgroups in order of decreasing work: the first half of the grid takes
-// ranks 0, 1, ... (the heaviest first), the second half ranks n - 1, n - 2, ...
-// (the lightest first).  A grid that fits on the chip at once is placed
-// round-robin over the compute units, so workgroups x and x + n / 2 tend to
-// share one and their causal work adds up to about the same on every unit.
-__device__ __forceinline__ int work_rank(int n) {
-  const int x = blockIdx.x, half = (n + 1) / 2;
-  return x < half ? x : n - 1 - (x - half);
-}
-
-// Rank -> (block index, head, batch) with the block index descending; the
-// rank is blockIdx.x itself (heaviest first, for grids larger than what the
-// chip holds at once, whose later workgroups fill the units that finish
-// first) or work_rank (PAIRED).
-template <bool PAIRED>
+// blockIdx -> (block index, head, batch), the block index descending: the
+// workgroups with the most work start first, and those the chip cannot hold
+// at once fill the units that finish first.
 __device__ __forceinline__ void block_coords(int nblocks, int heads, int batch, int& blk, int& head, int& b) {
-  const int per = heads * batch, r = PAIRED ? work_rank(nblocks * per) : (int)blockIdx.x;
+  const int per = heads * batch, r = (int)blockIdx.x;
   blk = nblocks - 1 - r / per;
   head = (r % per) / batch;
   b = r % batch;
@@ -300,7 +242,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void attn_fwd_kernel(const bf16_t
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), qh = w & 1, kp = w >> 1, kh = kp & 1, tp = kp >> 1;
   const int nqb = (int)((dm.seq + kAttnBlock - 1) / kAttnBlock);
   int qb, h, b;
-  block_coords<false>(nqb, dm.n_q, (int)dm.batch, qb, h, b);
+  block_coords(nqb, dm.n_q, (int)dm.batch, qb, h, b);
   const int kvh = h / dm.group;
   const int64_t t0 = (int64_t)b * dm.seq;
   const int q0 = qb * kAttnBlock + 32 * qh;  // this wave's first query; lane queries q0 + 16 jq + c
@@ -686,7 +628,7 @@ __global__ __launch_bounds__(kSplitThreads, 1) void attn_dq_kernel(const bf16_t*
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), qh = w & 1, kp = w >> 1, kh = kp & 1, tp = kp >> 1;
   const int nqb = (int)((dm.seq + kAttnBlock - 1) / kAttnBlock);
   int qb, h, b;
-  block_coords<false>(nqb, dm.n_q, (int)dm.batch, qb, h, b);
+  block_coords(nqb, dm.n_q, (int)dm.batch, qb, h, b);
   const int kvh = h / dm.group;
   const int64_t t0 = (int64_t)b * dm.seq, T = dm.batch * dm.seq;
   const int q0 = qb * kAttnBlock + 32 * qh;
