@@ -87,7 +87,15 @@ __global__ __launch_bounds__(kColThreads) void colsum_partial_kernel(const T* __
   const int64_t r0 = (int64_t)blockIdx.x * kColRows;
   const int64_t r1 = min(rows, r0 + kColRows);
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t t = r0; t < r1; ++t) acc += load4<T>(in + t * cols + 4 * q);
+  int64_t t = r0;
+  for (; t + 8 <= r1; t += 8) {  // eight loads in flight; the additions stay in row order
+    floatx4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = load4<T>(in + (t + k) * cols + 4 * q);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += v[k];
+  }
+  for (; t < r1; ++t) acc += load4<T>(in + t * cols + 4 * q);
   store4<float>(ws + (int64_t)blockIdx.x * cols + 4 * q, acc);
 }
 

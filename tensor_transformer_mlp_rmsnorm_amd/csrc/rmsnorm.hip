@@ -258,8 +258,18 @@ __global__ __launch_bounds__(256) void reduce_partial_rows_kernel(const float* _
   const int64_t per = (nparts + kRedGroups - 1) / kRedGroups;
   const int64_t b0 = grp * per, b1 = min(nparts, b0 + per);
   float acc = 0.f;
-  if (c < cols)
-    for (int64_t b = b0; b < b1; ++b) acc += ws[b * cols + c];
+  if (c < cols) {
+    // eight loads in flight at a time; the additions stay in row order
+    int64_t b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = ws[(b + k) * cols + c];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += v[k];
+    }
+    for (; b < b1; ++b) acc += ws[b * cols + c];
+  }
   part[grp][tc] = acc;
   __syncthreads();
   if (grp == 0 && c < cols) {
