@@ -184,12 +184,14 @@ def test_attention_ablations_match_oracle(mode):
         assert gap > 5e-2 * float(np.abs(dense["dx"]).max()), (s, gap)
 
 
-def test_attention_full_size():
+@pytest.mark.parametrize("name", ["attn_llama3_8b_tp8", "attn_gpt2s_tp1"])
+def test_attention_full_size(name):
     """The Llama-3-8B TP=8 attention layer (32 query heads, 8 KV heads of 128,
-    2 sequences of 4096) in the benchmark's configuration, every output
-    against the oracle's dense step in fp32."""
+    2 sequences of 4096) in the benchmark's configuration, and the GPT-2-small
+    layer (12 heads of 64, 4 sequences of 1024, one shard: the fused output
+    epilogue), every output against the oracle's dense step in fp32."""
     from tensor_transformer_mlp_rmsnorm_amd.step import AttnStep
-    w = synth.attn_workload("attn_llama3_8b_tp8")
+    w = synth.attn_workload(name)
     t = synth.draw_attn(w)
     say(f"[gpu] attention full size {w.name}")
     st = AttnStep(w, t, out_of_place_sgd=True)
