@@ -11,9 +11,9 @@ RMS of the reference over the token row for [T, .] activation tensors and
 over the whole compared tensor for parameters and their gradients.  A bare
 elementwise relative error is meaningless for entries near zero among 10^8
 values; the floor makes the bound relative to the tensor's own scale.  bf16
-rounding of a stored intermediate is 2^-9 ~ 2e-3 relative, so correct
-kernels sit around 1e-3 to 5e-3 and a real fault (a wrong index, a dropped
-term) lands far above 2e-2.
+rounding of a stored intermediate is 2^-9 ~ 2e-3 relative, so on the narrow
+test shapes correct kernels sit around 1e-3 to 5e-3 and a real fault (a wrong
+index, a dropped term) lands far above 2e-2.  Wide shapes: NATURAL_FACTOR.
 """
 
 import numpy as np
@@ -42,6 +42,17 @@ FP8_STEP_FROB = 5e-2
 
 FP32_ATOL = 1e-5
 BF16_RTOL = 2e-2
+# Wide bf16 shapes (thousands of tokens x thousands of hidden columns): a
+# stored bf16 intermediate that lies within an fp32 rounding of a bf16
+# rounding boundary is rounded one way by an fp32 implementation and the other
+# way by the fp64 oracle; SiLU's slope amplifies such a flip (for g << 0 the
+# log-derivative of silu(g) is about 1 + |g|) and it travels through the
+# following GEMM.  Among 10^7 - 10^8 entries the worst floored error of a
+# correct fp32 implementation then reaches 1.5 - 2e-2 (measured with the oracle
+# itself in fp32 arithmetic against fp64: dN 1.9e-2 and dx 1.9e-2 at 8000 x
+# 4000).  Such cases are bounded by max(BF16_RTOL, NATURAL_FACTOR x that
+# fp32-oracle error on the same input), computed per tensor by the test.
+NATURAL_FACTOR = 1.5
 
 
 def _np(a):
@@ -70,7 +81,12 @@ def floored_rel(got, ref, rowwise: bool) -> float:
     return float(np.max(np.abs(g - r) / den))
 
 
-def check(name, got, ref, dtype: str, rowwise: bool = False, report=None) -> float:
+def natural_bound(ref64, ref32, rowwise: bool = False) -> float:
+    """Bound for a bf16 tensor from the oracle's own fp32-arithmetic error."""
+    return max(BF16_RTOL, NATURAL_FACTOR * floored_rel(ref32, ref64, rowwise))
+
+
+def check(name, got, ref, dtype: str, rowwise: bool = False, report=None, tol=None) -> float:
     if dtype == "fp32":
         e = max_abs(got, ref)
         if report is not None:
@@ -85,9 +101,10 @@ def check(name, got, ref, dtype: str, rowwise: bool = False, report=None) -> flo
         assert e <= FP32_ATOL, f"{name}: max-abs / max(1, rms) {e:.3e} > {FP32_ATOL}"
     else:
         e = floored_rel(got, ref, rowwise)
+        bound = BF16_RTOL if tol is None else tol
         if report is not None:
             report[name] = e
-        assert e <= BF16_RTOL, f"{name}: floored relative error {e:.3e} > {BF16_RTOL}"
+        assert e <= bound, f"{name}: floored relative error {e:.3e} > {bound:.3e}"
     return e
 
 
