@@ -94,12 +94,12 @@ struct Tile {
     return (row * kChunks + (chunk ^ swz(row))) * 16;
   }
   // Row `row`, elements 8 c .. 8 c + 7.
-  __device__ __forceinline__ static uint4 row8(const char* base, int row, int c) {
+  __device__ __forceinline__ static uint4 row8(const char* __restrict__ base, int row, int c) {
     return *reinterpret_cast<const uint4*>(base + chunk_off(row, c));
   }
   // Column fragment for this lane (X or Y operand row e0 + l % 16) at the 8
   // rows 32 m + 16 h + 4 (l / 16) + j, h < 2, j < 4: two transpose reads.
-  __device__ __forceinline__ static uint4 col8(const char* base, int m, int e0, int lane) {
+  __device__ __forceinline__ static uint4 col8(const char* __restrict__ base, int m, int e0, int lane) {
     const int g = lane >> 4, a = lane & 15;
     uint2 out[2];
 #pragma unroll
@@ -113,6 +113,15 @@ struct Tile {
     return make_uint4(out[0].x, out[0].y, out[1].x, out[1].y);
   }
 };
+
+// Four floats from LDS.  Like the tile reads above, the pointer is restrict:
+// the reads of a step touch only the buffer the previous step's DMA filled,
+// never the one the current step's DMA is writing (the barrier that ends a
+// step waits for that DMA), and saying so keeps the compiler from waiting for
+// the in-flight DMA before every read.
+__device__ __forceinline__ floatx4 lds_load4(const float* __restrict__ p) {
+  return *reinterpret_cast<const floatx4*>(p);
+}
 
 // LDS DMA of [64][D] bf16 tiles from the rows of one sequence (a [seq, ld]
 // matrix): buffer_load_dwordx4 ... lds writes a wave's 64 x 16 bytes to 1 KiB
@@ -448,8 +457,16 @@ __global__ __launch_bounds__(kSplitThreads, 1) void attn_dkdv_kernel(const bf16_
                                                                      bf16_t* __restrict__ dqkv,
                                                                      float* __restrict__ part, AttnDims dm) {
   constexpr int kTile = kAttnBlock * D * 2, KS = D / 32, EB = D / 16;
-  __shared__ __align__(16) char smem[2][2][2][kTile];  // [buffer][tile of the step][Q, dO]
-  __shared__ __align__(16) float stat[2][2][2][kAttnBlock];  // [buffer][tile][lse, delta]
+  // One LDS object for the tiles and the statistics: with the reads' restrict
+  // pointers the compiler can then tell that a step's reads do not touch what
+  // the DMA in flight writes (with two objects it waits for that DMA first).
+  struct Lds {
+    char tiles[2][2][2][kTile];        // [buffer][tile of the step][Q, dO]
+    float stat[2][2][2][kAttnBlock];   // [buffer][tile][lse, delta]
+  };
+  __shared__ __align__(16) Lds lds;
+  auto& smem = lds.tiles;
+  auto& stat = lds.stat;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), kw = w & 3, tp = w >> 2;
   const int nqb = (int)((dm.seq + kAttnBlock - 1) / kAttnBlock);
@@ -512,8 +529,8 @@ __global__ __launch_bounds__(kSplitThreads, 1) void attn_dkdv_kernel(const bf16_
         sv = mma(Tile<D>::row8(qtl, 16 * qq + c, 4 * ks + g), kf[ks], sv);
         dp = mma(Tile<D>::row8(dtl, 16 * qq + c, 4 * ks + g), vf[ks], dp);
       }
-      const floatx4 l4 = *reinterpret_cast<const floatx4*>(lse_t + 16 * qq + 4 * g);
-      const floatx4 d4 = *reinterpret_cast<const floatx4*>(del_t + 16 * qq + 4 * g);
+      const floatx4 l4 = lds_load4(lse_t + 16 * qq + 4 * g);
+      const floatx4 d4 = lds_load4(del_t + 16 * qq + 4 * g);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float pv = fast_exp2(__builtin_fmaf(sv[r], dm.scale_log2, -l4[r] * kLog2e));
