@@ -79,16 +79,30 @@ struct Unmasked {
   static constexpr bool value = false;
 };
 
-// A [64][D] bf16 tile in LDS, 16-byte chunks XOR-swizzled by row with
-// swz(r) = 2 (r mod K/2) + (r / (K/2) mod 2), K = D / 8 chunks per row: the 8
-// rows of a row read (8 lanes, one chunk each) land on 8 distinct chunk
-// positions, and so do the 4 rows x 2 adjacent chunks of a 16-lane transpose
-// read (swz(r) / 2 differs between any 4 consecutive rows).
-template <int D>
+// A [64][D] bf16 tile in LDS, 16-byte chunks XOR-swizzled by row.  The LDS
+// serves a 16-byte read (ds_read_b128) in four passes of the lanes
+// p, p + 4, ..., p + 60, and a transpose read (ds_read_b64_tr_b16) in two
+// passes of 32 lanes; a pass is conflict-free when its lanes hit distinct
+// bank groups (16 bytes, or 8 bytes for the transpose read) of the 256-byte
+// bank row (measured with rocprofv3's SQ_LDS_BANK_CONFLICT on isolated reads).
+// The row reads here take 16 rows x chunks 4 ks .. 4 ks + 3 (lane: row l % 16,
+// chunk l / 16), the transpose reads 8 rows x 2 adjacent chunks per pass.
+//  * swz(r) = 2 (r mod K/2) + (r / (K/2) mod 2), K = D / 8 chunks per row:
+//    conflict-free transpose reads, 2-way conflicts in the row reads of D = 128.
+//  * CF (D = 128 only): swz(r) = 4 ((r mod 4) ^ (r / 4 mod 4)) + 2 (r / 4 mod 2)
+//    gives rows r, r + 4, r + 8, r + 12 distinct chunk quads and any 8 rows
+//    from a multiple of 8 distinct chunk pairs: both reads conflict-free, for
+//    about 12 more address instructions per step, which pays only in the dK/dV
+//    kernel (the most LDS reads per MFMA).
+// For D = 64 (128-byte rows, two to a bank row) the row reads of a pass share
+// one half of the bank row whatever the swizzle.
+template <int D, bool CF = false>
 struct Tile {
+  static_assert(!CF || D == 128, "the conflict-free layout is for 16 chunks per row");
   static constexpr int kChunks = D / 8;  // 16-byte chunks per row
   __device__ __forceinline__ static int swz(int row) {
-    return 2 * (row & (kChunks / 2 - 1)) | ((row / (kChunks / 2)) & 1);
+    if constexpr (CF) return (((row & 3) ^ ((row >> 2) & 3)) << 2) | (((row >> 2) & 1) << 1);
+    else return 2 * (row & (kChunks / 2 - 1)) | ((row / (kChunks / 2)) & 1);
   }
   __device__ __forceinline__ static int chunk_off(int row, int chunk) {
     return (row * kChunks + (chunk ^ swz(row))) * 16;
@@ -133,7 +147,7 @@ __device__ __forceinline__ floatx4 lds_load4(const float* __restrict__ p) {
 // register.  Lanes whose row is past the sequence get an offset beyond the
 // buffer (the buffer unit returns zeros) and blocks wholly past it a zero SGPR
 // offset, so no offset wraps; the host keeps a sequence below 2^30 elements.
-template <int D, int NW>
+template <int D, int NW, bool CF = false>
 struct TileDma {
   static constexpr int kChunks = D / 8, kRows = 512 / D, kBlocks = kAttnBlock / kRows, kPerWave = kBlocks / NW;
   static_assert(kPerWave >= 1 && kBlocks % NW == 0 && NW % 4 == 0, "block split");
@@ -148,7 +162,7 @@ struct TileDma {
                                              0x00020000);
     lrow = lane / kChunks;
     const int row = kRows * w + lrow;  // a representative row: every block of this wave has the same pattern
-    vlane = (unsigned)((lrow * ld_ + 8 * ((lane % kChunks) ^ Tile<D>::swz(row))) * 2);
+    vlane = (unsigned)((lrow * ld_ + 8 * ((lane % kChunks) ^ Tile<D, CF>::swz(row))) * 2);
   }
   // Tile `blk` of the columns col0 .. col0 + D - 1 into the LDS tile at `dst`.
   __device__ __forceinline__ void issue(char* dst, int blk, int64_t col0) const {
@@ -457,6 +471,8 @@ __global__ __launch_bounds__(kSplitThreads, 1) void attn_dkdv_kernel(const bf16_
                                                                      bf16_t* __restrict__ dqkv,
                                                                      float* __restrict__ part, AttnDims dm) {
   constexpr int kTile = kAttnBlock * D * 2, KS = D / 32, EB = D / 16;
+  constexpr bool kCF = D == 128;  // conflict-free tile layout (see Tile)
+  using TL = Tile<D, kCF>;
   // One LDS object for the tiles and the statistics: with the reads' restrict
   // pointers the compiler can then tell that a step's reads do not touch what
   // the DMA in flight writes (with two objects it waits for that DMA first).
@@ -489,8 +505,8 @@ __global__ __launch_bounds__(kSplitThreads, 1) void attn_dkdv_kernel(const bf16_
   floatx4 dk[EB], dv[EB];
 #pragma unroll
   for (int i = 0; i < EB; ++i) dk[i] = dv[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const TileDma<D, kSplitWaves> q_dma(qkv + t0 * dm.ld, dm.ld, dm.seq, w, lane);
-  const TileDma<D, kSplitWaves> d_dma(dO + t0 * dm.ldo, dm.ldo, dm.seq, w, lane);
+  const TileDma<D, kSplitWaves, kCF> q_dma(qkv + t0 * dm.ld, dm.ld, dm.seq, w, lane);
+  const TileDma<D, kSplitWaves, kCF> d_dma(dO + t0 * dm.ldo, dm.ldo, dm.seq, w, lane);
   // lse and delta of a tile: 64 floats each, one 4-byte DMA per tile and kind
   // (waves 0-3: tile w / 2 of the step, lse for even w, delta for odd).
   const float* stat_src = (w & 1) ? delta + (int64_t)hq * T + t0 : lse + (int64_t)hq * T + t0;
@@ -526,8 +542,8 @@ __global__ __launch_bounds__(kSplitThreads, 1) void attn_dkdv_kernel(const bf16_
       floatx4 sv = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        sv = mma(Tile<D>::row8(qtl, 16 * qq + c, 4 * ks + g), kf[ks], sv);
-        dp = mma(Tile<D>::row8(dtl, 16 * qq + c, 4 * ks + g), vf[ks], dp);
+        sv = mma(TL::row8(qtl, 16 * qq + c, 4 * ks + g), kf[ks], sv);
+        dp = mma(TL::row8(dtl, 16 * qq + c, 4 * ks + g), vf[ks], dp);
       }
       const floatx4 l4 = lds_load4(lse_t + 16 * qq + 4 * g);
       const floatx4 d4 = lds_load4(del_t + 16 * qq + 4 * g);
@@ -549,8 +565,8 @@ __global__ __launch_bounds__(kSplitThreads, 1) void attn_dkdv_kernel(const bf16_
       const SlotPair sf = pack_slots(ds[2 * mm], ds[2 * mm + 1]);
 #pragma unroll
       for (int eb = 0; eb < EB; ++eb) {
-        dv[eb] = mma(Tile<D>::col8(dtl, mm, 16 * eb, lane), pf, dv[eb]);
-        dk[eb] = mma2(Tile<D>::col8(qtl, mm, 16 * eb, lane), sf, dk[eb]);
+        dv[eb] = mma(TL::col8(dtl, mm, 16 * eb, lane), pf, dv[eb]);
+        dk[eb] = mma2(TL::col8(qtl, mm, 16 * eb, lane), sf, dk[eb]);
       }
     }
   };
