@@ -393,11 +393,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const floatx4 (&acc)
 // wait on the tile loads still in flight (it cannot tell they write other
 // slots).  abase/bbase: this lane's byte address in the first A / B fragment;
 // row block r is 2048 bytes further, and the k 32-63 chunk is at address ^ 64.
+template <int WMB, int WNB>
 struct Frags {
-  uint4 a[2][8], b[2][4];
+  uint4 a[2][WMB], b[2][WNB];
 };
 
-__device__ __forceinline__ void read_frags_kc(Frags& f, unsigned abase, unsigned bbase) {
+__device__ __forceinline__ void read_frags_kc(Frags<8, 4>& f, unsigned abase, unsigned bbase) {
   asm volatile(
       "ds_read_b128 %0, %24 offset:0\n"
       "ds_read_b128 %1, %24 offset:2048\n"
@@ -432,6 +433,55 @@ __device__ __forceinline__ void read_frags_kc(Frags& f, unsigned abase, unsigned
       : "memory");
 }
 
+// The same for a 64 x 112 wave tile (A: 4 row blocks, B: 7): 22 reads.
+__device__ __forceinline__ void read_frags_kc(Frags<4, 7>& f, unsigned abase, unsigned bbase) {
+  asm volatile(
+      "ds_read_b128 %0, %22 offset:0\n"
+      "ds_read_b128 %1, %22 offset:2048\n"
+      "ds_read_b128 %2, %22 offset:4096\n"
+      "ds_read_b128 %3, %22 offset:6144\n"
+      "ds_read_b128 %4, %23 offset:0\n"
+      "ds_read_b128 %5, %23 offset:2048\n"
+      "ds_read_b128 %6, %23 offset:4096\n"
+      "ds_read_b128 %7, %23 offset:6144\n"
+      "ds_read_b128 %8, %23 offset:8192\n"
+      "ds_read_b128 %9, %23 offset:10240\n"
+      "ds_read_b128 %10, %23 offset:12288\n"
+      "ds_read_b128 %11, %24 offset:0\n"
+      "ds_read_b128 %12, %24 offset:2048\n"
+      "ds_read_b128 %13, %24 offset:4096\n"
+      "ds_read_b128 %14, %24 offset:6144\n"
+      "ds_read_b128 %15, %25 offset:0\n"
+      "ds_read_b128 %16, %25 offset:2048\n"
+      "ds_read_b128 %17, %25 offset:4096\n"
+      "ds_read_b128 %18, %25 offset:6144\n"
+      "ds_read_b128 %19, %25 offset:8192\n"
+      "ds_read_b128 %20, %25 offset:10240\n"
+      "ds_read_b128 %21, %25 offset:12288\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[0][2]), "=&v"(f.a[0][3]), "=&v"(f.b[0][0]), "=&v"(f.b[0][1]),
+        "=&v"(f.b[0][2]), "=&v"(f.b[0][3]), "=&v"(f.b[0][4]), "=&v"(f.b[0][5]), "=&v"(f.b[0][6]), "=&v"(f.a[1][0]),
+        "=&v"(f.a[1][1]), "=&v"(f.a[1][2]), "=&v"(f.a[1][3]), "=&v"(f.b[1][0]), "=&v"(f.b[1][1]), "=&v"(f.b[1][2]),
+        "=&v"(f.b[1][3]), "=&v"(f.b[1][4]), "=&v"(f.b[1][5]), "=&v"(f.b[1][6])
+      : "v"(abase), "v"(bbase), "v"(abase ^ 64u), "v"(bbase ^ 64u)
+      : "memory");
+}
+
+// Wave tiles of the ping-pong kernel: the two groups (waves 0-3 and 4-7) own
+// tile rows 0-127 and 128-255; inside a group a wave owns 128 x 64 (PpTile256,
+// 256-wide tiles) or 64 x 112 (PpTile224: 2 x 2 waves over 128 x 224, for N
+// that 224 divides into fewer rounds of the CUs).
+struct PpTile256 {
+  static constexpr int TN = 256, WMB = 8, WNB = 4;
+  __device__ __forceinline__ static int row0(int wave) { return (wave >> 2) * 128; }
+  __device__ __forceinline__ static int col0(int wave) { return (wave & 3) * 64; }
+};
+struct PpTile224 {
+  static constexpr int TN = 224, WMB = 4, WNB = 7;
+  __device__ __forceinline__ static int row0(int wave) { return (wave >> 2) * 128 + ((wave >> 1) & 1) * 64; }
+  __device__ __forceinline__ static int col0(int wave) { return (wave & 1) * 112; }
+};
+
 // Operand element types of the ping-pong kernel: bf16, or FP8 codes in the
 // OCP formats FA (of A) and FB (of B), with the MFMA's format numbering
 // (0 = E4M3, 1 = E5M2).  A k-tile is 128 bytes of every row in both cases:
@@ -446,13 +496,14 @@ struct PpFp8 {
   static constexpr bool kFp8 = true;
 };
 
-__device__ __forceinline__ void mma_tile(floatx4 (&acc)[8][4], const Frags& f, PpBf16) {
+template <int WMB, int WNB>
+__device__ __forceinline__ void mma_tile(floatx4 (&acc)[WMB][WNB], const Frags<WMB, WNB>& f, PpBf16) {
 #pragma unroll
   for (int s = 0; s < kBK / 32; ++s)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < WMB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < WNB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.b[s][j]),
                                                             __builtin_bit_cast(bf16x8, f.a[s][i]), acc[i][j], 0, 0, 0);
 }
@@ -466,19 +517,19 @@ constexpr int kUnitScales = 0x7f7f7f7f;  // E8M0 block scales of 2^0: the scaled
 // fragments the bf16 schedule reads for its two k halves.  Any assignment of
 // the 128 k to lane bytes gives the same sums as long as A and B use the same
 // one, and they do.
-template <int FA, int FB>
-__device__ __forceinline__ void mma_tile(floatx4 (&acc)[8][4], const Frags& f, PpFp8<FA, FB>) {
-  intx8 bv[4];
+template <int FA, int FB, int WMB, int WNB>
+__device__ __forceinline__ void mma_tile(floatx4 (&acc)[WMB][WNB], const Frags<WMB, WNB>& f, PpFp8<FA, FB>) {
+  intx8 bv[WNB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < WNB; ++j)
     bv[j] = __builtin_shufflevector(__builtin_bit_cast(intx4, f.b[0][j]), __builtin_bit_cast(intx4, f.b[1][j]), 0, 1,
                                     2, 3, 4, 5, 6, 7);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < WMB; ++i) {
     const intx8 av = __builtin_shufflevector(__builtin_bit_cast(intx4, f.a[0][i]), __builtin_bit_cast(intx4, f.a[1][i]),
                                              0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WNB; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv[j], av, acc[i][j], FB, FA, 0, kUnitScales, 0,
                                                                    kUnitScales);
   }
@@ -499,10 +550,12 @@ __device__ __forceinline__ void phase_end() {
 
 __device__ __forceinline__ int slot_u4(int x) { return (x % kSlots) * kTileU4; }
 
-template <int EPI, class OP>
+template <int EPI, class OP, class PT = PpTile256>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs g, int ntm, int ntn) {
   extern __shared__ uint4 smem[];  // 5 operand slots = 160 KiB
   constexpr bool kSwiglu = EPI == kEpiSwigluFwd;
+  static_assert(!kSwiglu || PT::TN == 256, "the SwiGLU pairing uses 256-row B tiles of 128 channels");
+  constexpr int WMB = PT::WMB, WNB = PT::WNB;
   constexpr int EB = OP::kBytes;
   constexpr int kK = 128 / EB;  // k per tile
 
@@ -518,13 +571,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
   const int64_t kend = K < kbeg + kper ? K : kbeg + kper;
   const RowMap ra{(int64_t)tm * kBM, g.M, false, 0};
   const RowMap rb = kSwiglu ? RowMap{(int64_t)tn * kSwigluChannels, g.N, true, g.ffn}
-                            : RowMap{(int64_t)tn * kBN, g.N, false, 0};
+                            : RowMap{(int64_t)tn * PT::TN, g.N, false, 0};
 
-  floatx4 acc[8][4];
+  floatx4 acc[WMB][WNB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < WMB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WNB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const Operand opa = make_operand(g.A, g.M, g.lda, EB);
   const Operand opb = make_operand(g.B, kSwiglu ? 2 * g.ffn : g.N, g.ldb, EB);
@@ -537,10 +590,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
 
   const unsigned lane_part = (unsigned)((lane & 15) * 128 + (((lane >> 4) ^ (lane & 7)) * 16));
   const unsigned smem_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
-  const unsigned a_lane = smem_addr + lane_part + wm * 128 * 128;  // kc_index(wm*128 + (lane&15), lane>>4) * 16
-  const unsigned b_lane = smem_addr + lane_part + wn * 64 * 128;
+  // kc_index(row0 + (lane & 15), lane >> 4) * 16: rows are 128 bytes
+  const unsigned a_lane = smem_addr + lane_part + PT::row0(wave) * 128;
+  const unsigned b_lane = smem_addr + lane_part + PT::col0(wave) * 128;
   auto slot_bytes = [](int x) { return (unsigned)(slot_u4(x) * 16); };
-  Frags f;
+  Frags<WMB, WNB> f;
   // group A loads B tiles, group B loads A tiles
   QuarterLoads<kSwiglu, EB> lb(opb, rb, q, lane);
   QuarterLoads<false, EB> la(opa, ra, q, lane);
@@ -573,12 +627,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
     // dequantisation: the product of the operands' inverse scales, read after the main loop
     const float deq = g.scale_inv_a[0] * g.scale_inv_b[0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < WMB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] *= deq;
+      for (int j = 0; j < WNB; ++j) acc[i][j] *= deq;
   }
-  epilogue<EPI, 8, 4>(g, acc, (int64_t)tm * kBM + wm * 128, (int64_t)tn * kBN + wn * 64,
-                      (int64_t)tn * kSwigluChannels + wn * 32, ks, lane);
+  epilogue<EPI, WMB, WNB>(g, acc, (int64_t)tm * kBM + PT::row0(wave), (int64_t)tn * PT::TN + PT::col0(wave),
+                          (int64_t)tn * kSwigluChannels + wn * 32, ks, lane);
 }
 
 template <bool AK, bool BKC, int EPI, class SH>
@@ -679,9 +733,9 @@ hipError_t launch_two_stage(const GemmArgs& ga, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI, class OP>
+template <int EPI, class OP, class PT = PpTile256>
 hipError_t launch_pingpong(const GemmArgs& ga, int ntm, int ntn, hipStream_t s) {
-  auto kernel = gemm_nt_pingpong_kernel<EPI, OP>;
+  auto kernel = gemm_nt_pingpong_kernel<EPI, OP, PT>;
   static bool configured = false;  // raise the dynamic LDS limit once per instantiation
   if (!configured) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -700,6 +754,14 @@ hipError_t launch_tiles(const GemmArgs& ga, int ntm, int ntn, hipStream_t s) {
   static_assert(!OP::kFp8 || (AK && BKC), "FP8 operands are K-contiguous");
   KernelTimer timer(ga.tag ? ga.tag : "gemm", s);
   if constexpr (AK && BKC) {
+    if constexpr (EPI != kEpiSwigluFwd) {
+      // 224-wide tiles when (rounds of one workgroup per CU) x (tile width) is smaller, as for the
+      // two-stage kernel's tile choice
+      const int64_t cus = device_cus(), ntn224 = (ga.N + 223) / 224;
+      const int64_t r256 = ((int64_t)ntm * ntn * ga.ksplit + cus - 1) / cus;
+      const int64_t r224 = ((int64_t)ntm * ntn224 * ga.ksplit + cus - 1) / cus;
+      if (r224 * 224 < r256 * 256) return launch_pingpong<EPI, OP, PpTile224>(ga, ntm, (int)ntn224, s);
+    }
     return launch_pingpong<EPI, OP>(ga, ntm, ntn, s);
   } else {
     // the tile shape with the least (rounds of one workgroup per CU) x (tile area); a function of the
