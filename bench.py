@@ -98,23 +98,35 @@ KERNEL_SOURCES = ("tensor_transformer_mlp_rmsnorm_amd/csrc/gemm_bf16.hip", "tens
                   "tensor_transformer_mlp_rmsnorm_amd/csrc/kernels.h")
 
 
+def kernel_sources_fingerprint() -> str:
+    """sha256 of the GEMM sources' code: every line with its // comment and
+    trailing blanks removed, empty lines skipped (the sources hold no // inside
+    string literals).  A traffic record stays valid across comment edits and
+    not across code edits."""
+    import hashlib
+    import re
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel)) as f:
+            for line in f:
+                code = re.sub(r"//.*$", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed counter record
     (profiles/traffic_<kernel>_<workload>.json: FETCH_SIZE and WRITE_SIZE
     scaled by a plain-copy calibration), or None when there is no record or
-    the kernel sources changed since the counters were taken."""
-    import hashlib
-
+    the kernel code changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    if rec.get("kernel_sources_sha256") != h.hexdigest():
+    if rec.get("kernel_sources_sha256") != kernel_sources_fingerprint():
         return None
     return float(rec["traffic_bytes_per_launch"])
 

@@ -3,7 +3,8 @@
 //   C[m, n] = sum_k A(m, k) B(k, n),  A(m,k) = A[m*lda + k] (a_kcontig) or A[k*lda + m],
 //                                     B(k,n) = B[n*ldb + k] (b_kcontig) or B[k*ldb + n].
 //
-// One 512-thread workgroup computes a 256 x 256 output tile:
+// One 512-thread workgroup computes a 256 x 256 output tile (variants: 224-wide
+// tiles where they fill the CUs better, and a 16-wave form, both below):
 //  * 8 waves in a 2 (M) x 4 (N) grid; each wave owns 128 x 64 outputs as 8 x 4
 //    blocks of v_mfma_f32_16x16x32_bf16 (128 fp32 accumulators per lane).  The
 //    LDS bytes read per flop are a quarter of what a 64 x 64 wave tile needs.
@@ -26,7 +27,9 @@
 //      every phase and the multiplying wave never stalls on a memory
 //      instruction.  LDS is a ring of 5 operand slots of 32 KiB: operand tile x
 //      (A of k-tile j is x = 2j, B is 2j+1) sits in slot x mod 5, so a slot is
-//      refilled only after both groups have read it.
+//      refilled only after both groups have read it.  A 256 x 224 tile (2 x 2
+//      waves of 64 x 112 per group) serves N that 224 divides into fewer rounds
+//      of the CUs, except for the SwiGLU forward.
 //    - otherwise (a transposed operand): two LDS stages of 64 KiB; all waves
 //      read and multiply each k-tile in step, with the next k-tile's loads issued
 //      first and one barrier per k-tile.  The transpose reads are slower, and
