@@ -178,7 +178,9 @@ typedef struct {
   void* d_x;              /* [T, H] dtype */
   float* d_norm_w;        /* [H] fp32 */
   float* d_b_down;        /* [H] fp32 */
-  /* scratch for deterministic column reductions, caller-owned */
+  /* scratch, caller-owned: k-split slices and column partials of the
+     deterministic reductions; in bf16 also Wd transposed ([F, H]) for the
+     d_act GEMM */
   void* workspace;
   size_t workspace_bytes;
 } tp_mlp_bwd_args;

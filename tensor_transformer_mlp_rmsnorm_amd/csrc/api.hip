@@ -198,7 +198,10 @@ size_t tp_mlp_workspace_bytes(const tp_mlp_desc* d, int32_t phase) {
     // k-split slices of the two weight-gradient GEMMs (K = T); they run one
     // after the other and share the workspace
     // (the FP8 backward's k extent is T rounded up to 16)
+    // The bf16 d_act GEMM reads Wd transposed ([F, H]) from the workspace
+    // before either of them runs.
     const int64_t P = d->act == TP_MLP_ACT_SWIGLU ? 2 * F : F;
+    if (T > 0) need = need > (size_t)(F * H * 2) ? need : (size_t)(F * H * 2);
     for (const int64_t K : {T, (T + 15) / 16 * 16}) {
       const size_t w2 = gemm_ksplit_workspace(H, F, K), w4 = gemm_ksplit_workspace(P, H, K);
       need = need > w2 ? need : w2;
@@ -262,7 +265,9 @@ int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* 
   }
   const int64_t P = swiglu ? 2 * F : F;  // width of pre-activations
 
-  // d_act = d_out Wd ([T,H] x [H,F]), with the activation backward fused.
+  // d_act = d_out Wd ([T,H] x [H,F]), with the activation backward fused.  In
+  // bf16 both operands are made K-contiguous (Wd^T [F, H] in the workspace) for
+  // the ping-pong GEMM: the transpose moves 4 F H bytes, the GEMM gains more.
   GemmArgs b1{};
   b1.M = T;
   b1.N = F;
@@ -275,7 +280,15 @@ int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* 
   b1.aux = a->pre_act;
   b1.ffn = F;
   b1.tag = swiglu ? "gemm_dact_swiglu_bwd" : "gemm_dact_gelu_bwd";
-  CHECK_HIP(launch_gemm(dt, true, false, swiglu ? kEpiSwigluBwd : kEpiGeluBwd, b1, s), "d_act GEMM");
+  const Epi act_bwd = swiglu ? kEpiSwigluBwd : kEpiGeluBwd;
+  if (dt == kBF16 && T > 0) {
+    CHECK_HIP(launch_transpose_bf16(a->w_down, a->workspace, H, F, s), "Wd transpose");
+    b1.B = a->workspace;
+    b1.ldb = H;
+    CHECK_HIP(launch_gemm(dt, true, true, act_bwd, b1, s), "d_act GEMM");
+  } else {
+    CHECK_HIP(launch_gemm(dt, true, false, act_bwd, b1, s), "d_act GEMM");
+  }
 
   // d_w_down = d_out^T act ([H,T] x [T,F]).
   GemmArgs b2{};

@@ -180,6 +180,39 @@ __global__ __launch_bounds__(256) void ksplit_reduce_bf16_kernel(bf16_t* __restr
   }
 }
 
+// out[c, r] = in[r, c] for a row-major [R, C] bf16 matrix (R, C multiples of
+// 8) through 64 x 64 LDS tiles, 16-byte loads along C and 16-byte stores
+// along R.  With a row pitch of 33 dwords the 8 rows that one store gathers
+// (of one column) sit on distinct banks across a wave.
+constexpr int kTrTile = 64, kTrPitch = 66;  // bf16 elements per LDS row
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ in, bf16_t* __restrict__ out,
+                                                              int64_t R, int64_t C, int tiles_c) {
+  __shared__ uint32_t tile[kTrTile * kTrPitch / 2];
+  const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * kTrTile, c0 = (int64_t)(blockIdx.x % tiles_c) * kTrTile;
+  for (int i = threadIdx.x; i < kTrTile * 8; i += 256) {
+    const int row = i >> 3, ch = i & 7;  // input row r0 + row, columns c0 + 8 ch .. + 7
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + row < R && c0 + ch * 8 < C) v = *reinterpret_cast<const uint4*>(in + (r0 + row) * C + c0 + ch * 8);
+    uint32_t* d = tile + row * (kTrPitch / 2) + ch * 4;
+    d[0] = v.x;
+    d[1] = v.y;
+    d[2] = v.z;
+    d[3] = v.w;
+  }
+  __syncthreads();
+  const bf16_t* t16 = reinterpret_cast<const bf16_t*>(tile);
+  for (int i = threadIdx.x; i < kTrTile * 8; i += 256) {
+    const int oc = i >> 3, ch = i & 7;  // output row c0 + oc, columns r0 + 8 ch .. + 7
+    if (c0 + oc >= C || r0 + ch * 8 >= R) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)t16[(8 * ch + 2 * j) * kTrPitch + oc] |
+             ((uint32_t)t16[(8 * ch + 2 * j + 1) * kTrPitch + oc] << 16);
+    *reinterpret_cast<uint4*>(out + (c0 + oc) * R + r0 + ch * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_ksplit_reduce_bf16(void* C, const float* ws, int nslices, int64_t M, int64_t N, int64_t ldc,
@@ -265,6 +298,16 @@ hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, f
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+hipError_t launch_transpose_bf16(const void* in, void* out, int64_t R, int64_t C, hipStream_t s) {
+  if (R == 0 || C == 0) return hipSuccess;
+  if (R % 8 || C % 8) return hipErrorInvalidValue;
+  KernelTimer timer("transpose_bf16", s);
+  const int64_t tr = (R + kTrTile - 1) / kTrTile, tc = (C + kTrTile - 1) / kTrTile;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(tr * tc)), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(in), static_cast<bf16_t*>(out), R, C, (int)tc);
+  return hipGetLastError();
 }
 
 }  // namespace tpmlp

@@ -818,6 +818,8 @@ hipError_t launch_gemm_bf16(bool ak, bool bk, Epi epi, const GemmArgs& g, hipStr
       case kEpiGeluFwd: return launch_t<true, true, kEpiGeluFwd>(g, s);
       case kEpiResidual: return launch_t<true, true, kEpiResidual>(g, s);
       case kEpiStoreBf16: return launch_t<true, true, kEpiStoreBf16>(g, s);
+      case kEpiSwigluBwd: return launch_t<true, true, kEpiSwigluBwd>(g, s);
+      case kEpiGeluBwd: return launch_t<true, true, kEpiGeluBwd>(g, s);
       default: break;
     }
   } else if (ak && !bk) {

@@ -159,6 +159,9 @@ hipError_t launch_ksplit_reduce_bf16(void* C, const float* ws, int nslices, int6
 hipError_t launch_ksplit_reduce(float* C, const float* ws, int nslices, int64_t M, int64_t N, int64_t ldc,
                                 hipStream_t s);
 
+// out [C, R] = in [R, C]^T, bf16, row-major; R and C multiples of 8.
+hipError_t launch_transpose_bf16(const void* in, void* out, int64_t R, int64_t C, hipStream_t s);
+
 struct SgdTensor {
   const void* param_in;
   void* param_out;

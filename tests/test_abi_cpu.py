@@ -114,7 +114,10 @@ def test_backward_checks(lib):
     need = L.tp_mlp_workspace_bytes(d, L.BWD_SHARD)
     assert need > 0
     assert L.tp_mlp_workspace_bytes(d, L.BWD_NORM) > 0
-    assert L.tp_mlp_workspace_bytes(_desc(T=128), L.BWD_SHARD) == 0
+    assert L.tp_mlp_workspace_bytes(_desc(T=128, dt=L.F32), L.BWD_SHARD) == 0
+    # bf16: the transposed down weight [F, H] for the d_act GEMM
+    assert L.tp_mlp_workspace_bytes(_desc(T=128), L.BWD_SHARD) >= 32 * 64 * 2
+    assert L.tp_mlp_workspace_bytes(_desc(T=0), L.BWD_SHARD) == 0
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
         if name != "workspace_bytes":
