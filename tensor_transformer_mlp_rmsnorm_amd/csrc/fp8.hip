@@ -23,7 +23,7 @@ namespace tpmlp {
 namespace {
 
 constexpr int kCastTile = 128, kCastThreads = 256;
-constexpr int kCastMaxBlocks = 2048;
+constexpr int kCastBlocks = 512;  // workgroups a cast aims for (two per CU)
 
 template <int FMT>
 __device__ __forceinline__ uint32_t cvt_pair(float a, float b) {
@@ -72,8 +72,10 @@ __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c,
 // out [R, C] (if ROW) and out_t [C, ldt] (if TRANS; the rows R .. ldt-1 of
 // the tiles give zero codes, so out_t's padding columns are written as 0).
 // Load: thread t takes rows t/8 + 32 i (i < 4) and the 16 columns 16 (t%8) ..;
-// a tile wholly inside the matrix issues its 8 loads before any use (edge
-// tiles load under guards).  Transposed store: thread t reads the code dwords
+// a tile wholly inside the matrix is loaded one iteration ahead, its 8 loads
+// in flight while the previous tile's codes are stored, so that each
+// workgroup's reads and writes overlap (edge tiles load under guards, when
+// they are cast).  Transposed store: thread t reads the code dwords
 // of columns 4 (t%32) .. + 3 in rows 16 (t/32) .. + 15 from LDS, transposes
 // them in registers (byte permutes) and writes 16 bytes to each of the four
 // columns.  One atomic maximum per workgroup folds the amax into meta[2].
@@ -87,18 +89,26 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(const bf16_t* __rest
   const float s = meta[0], lim = meta[3];
   const int cq = (t & 7) * 16;  // first of this thread's 16 columns
   float amax = 0.0f;
+  // whether tile id lies wholly inside the matrix (the same for the whole workgroup)
+  auto full_tile = [&](int id) {
+    return (int64_t)(id / tiles_c + 1) * kCastTile <= R && (int64_t)(id % tiles_c + 1) * kCastTile <= C;
+  };
+  uint4 v[4][2];  // the raw chunks of the next full tile
+  auto load_tile = [&](int id) {
+    const int64_t r0 = (int64_t)(id / tiles_c) * kCastTile, c0 = (int64_t)(id % tiles_c) * kCastTile;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16_t* src = x + (r0 + (t >> 3) + 32 * i) * C + c0 + cq;
+      v[i][0] = *reinterpret_cast<const uint4*>(src);
+      v[i][1] = *reinterpret_cast<const uint4*>(src + 8);
+    }
+  };
+  if ((int)blockIdx.x < tiles && full_tile(blockIdx.x)) load_tile(blockIdx.x);
   for (int tid = blockIdx.x; tid < tiles; tid += gridDim.x) {
     const int64_t r0 = (int64_t)(tid / tiles_c) * kCastTile, c0 = (int64_t)(tid % tiles_c) * kCastTile;
-    const bool full = r0 + kCastTile <= R && c0 + kCastTile <= C;  // the same for the whole workgroup
+    const bool full = full_tile(tid);
     uint2 q[4][2];
     if (full) {
-      uint4 v[4][2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16_t* src = x + (r0 + (t >> 3) + 32 * i) * C + c0 + cq;
-        v[i][0] = *reinterpret_cast<const uint4*>(src);
-        v[i][1] = *reinterpret_cast<const uint4*>(src + 8);
-      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         q[i][0] = cast8<FMT>(v[i][0], s, lim, amax);
@@ -116,6 +126,8 @@ __global__ __launch_bounds__(kCastThreads) void cast_kernel(const bf16_t* __rest
         }
       }
     }
+    const int next = tid + (int)gridDim.x;
+    if (next < tiles && full_tile(next)) load_tile(next);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = (t >> 3) + 32 * i;
@@ -228,7 +240,8 @@ hipError_t launch_cast_t(const bf16_t* x, int64_t R, int64_t C, uint8_t* out, ui
   const int64_t rows = TRANS ? (R > ldt ? R : ldt) : R;  // the transposed padding needs its tile-rows too
   const int64_t tc = (C + kCastTile - 1) / kCastTile, tr = (rows + kCastTile - 1) / kCastTile;
   const int64_t tiles = tc * tr;
-  const int blocks = (int)(tiles < kCastMaxBlocks ? tiles : kCastMaxBlocks);
+  const int64_t per_block = (tiles + kCastBlocks - 1) / kCastBlocks;  // tiles per workgroup, evened out
+  const int blocks = (int)((tiles + per_block - 1) / per_block);
   hipLaunchKernelGGL((cast_kernel<FMT, ROW, TRANS>), dim3(blocks), dim3(kCastThreads), 0, s, x, R, C, out, out_t, ldt,
                      (int)tc, (int)tiles, meta);
   return hipGetLastError();
