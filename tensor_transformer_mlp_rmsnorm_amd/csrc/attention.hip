@@ -430,26 +430,32 @@ __global__ __launch_bounds__(kSplitThreads, 1) void attn_fwd_kernel(const bf16_t
   }
 }
 
-// delta[h][t] = sum_e dO[t][h D + e] O[t][h D + e]
+// delta[h][t] = sum_e dO[t][h D + e] O[t][h D + e].  D / 8 consecutive lanes
+// share a row (16 bytes of O and of dO each, so a row is read as one
+// contiguous segment) and add their partial sums with lane shuffles in a
+// fixed order.
 template <int D>
 __global__ __launch_bounds__(256) void attn_delta_kernel(const bf16_t* __restrict__ O, const bf16_t* __restrict__ dO,
                                                           float* __restrict__ delta, int64_t T, int n_q, int64_t ldo) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T * n_q) return;
-  const int h = (int)(i / T);
-  const int64_t t = i % T;
-  const bf16_t* o = O + t * ldo + (int64_t)h * D;
-  const bf16_t* d = dO + t * ldo + (int64_t)h * D;
+  constexpr int L = D / 8;  // lanes per row; divides the wave, so a row's lanes sit in one wave
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = gid / L;  // (head, token) pair, token fastest
+  const int c = (int)(gid % L);
+  const bool ok = i < T * n_q;
+  const int h = ok ? (int)(i / T) : 0;
+  const int64_t t = ok ? i % T : 0;
   float acc = 0.0f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
+  if (ok) {
+    const int64_t off = t * ldo + (int64_t)h * D + 8 * c;
     float a[8], e[8];
-    Chunk<bf16_t>::unpack(*reinterpret_cast<const uint4*>(o + 8 * c), a);
-    Chunk<bf16_t>::unpack(*reinterpret_cast<const uint4*>(d + 8 * c), e);
+    Chunk<bf16_t>::unpack(*reinterpret_cast<const uint4*>(O + off), a);
+    Chunk<bf16_t>::unpack(*reinterpret_cast<const uint4*>(dO + off), e);
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc += a[k] * e[k];
   }
-  delta[(int64_t)h * T + t] = acc;
+#pragma unroll
+  for (int m = L / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, kWave);
+  if (ok && c == 0) delta[(int64_t)h * T + t] = acc;
 }
 
 // dK and dV of 64 keys from one query head: one workgroup of 8 waves per key
@@ -814,7 +820,7 @@ hipError_t bwd_t(const AttnShapeArgs& a, const void* qkv, const void* O, const v
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + attention_delta_bytes(a));
   {
     KernelTimer timer("attention_delta", s);
-    const int64_t n = T * a.n_q;
+    const int64_t n = T * a.n_q * (D / 8);  // threads: D / 8 per (head, token)
     hipLaunchKernelGGL(attn_delta_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        static_cast<const bf16_t*>(O), static_cast<const bf16_t*>(dO), delta, T, a.n_q, dm.ldo);
     const hipError_t e = hipGetLastError();
