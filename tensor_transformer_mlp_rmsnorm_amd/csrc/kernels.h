@@ -71,12 +71,12 @@ struct GemmArgs {
 };
 
 // Number of k-slices for a bf16 fp32-output GEMM: a function of the shape only
-// (so results are bitwise reproducible): split while the tile count stays
-// under 192 and every slice keeps at least 1024 of k.
+// (so results are bitwise reproducible): split (up to 8 ways) while the tile
+// count stays under 192 and every slice keeps at least 1024 of k.
 inline int gemm_ksplit(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   int ks = 1;
-  while (ks < 4 && tiles * ks < 192 && K / (2 * ks) >= 1024) ks *= 2;
+  while (ks < 8 && tiles * ks < 192 && K / (2 * ks) >= 1024) ks *= 2;
   return ks;
 }
 inline size_t gemm_ksplit_workspace(int64_t M, int64_t N, int64_t K) {

@@ -316,7 +316,7 @@ def test_fp8_checks(lib):
     assert call(C=None) == L.EINVAL
     assert call(M=0) == L.OK                                            # empty: no-op
     need = lib.tp_mlp_fp8_gemm_workspace_bytes(64, 4096, 8192, 4096)
-    assert need == 3 * 64 * 4096 * 4
+    assert need == 7 * 64 * 4096 * 4        # 16 tiles of 256 x 256, K = 8192: 8 k-slices, 7 in the workspace
     assert call(N=4096, K=8192, lda=8192, ldb=8192, ldc=4096) == L.EWORKSPACE
     assert call(N=4096, K=8192, lda=8192, ldb=8192, ldc=4096, ws=MIS, wsb=need) == L.EALIGN
 
