@@ -71,12 +71,14 @@ struct GemmArgs {
 };
 
 // Number of k-slices for a bf16 fp32-output GEMM: a function of the shape only
-// (so results are bitwise reproducible): split (up to 8 ways) while the tile
-// count stays under 192 and every slice keeps at least 1024 of k.
+// (so results are bitwise reproducible).  Shapes with fewer than 192 tiles of
+// 256 x 256 take the most slices (at most 8) that keep all workgroups in one
+// round of 256 CUs and every slice at least 1024 of k.
 inline int gemm_ksplit(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles >= 192) return 1;
   int ks = 1;
-  while (ks < 8 && tiles * ks < 192 && K / (2 * ks) >= 1024) ks *= 2;
+  while (ks < 8 && tiles * (ks + 1) <= 256 && K / (ks + 1) >= 1024) ++ks;
   return ks;
 }
 inline size_t gemm_ksplit_workspace(int64_t M, int64_t N, int64_t K) {
