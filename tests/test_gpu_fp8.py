@@ -188,7 +188,7 @@ GEMMS = [
     # M,   N,    K,    lda,  ldb, ldc,  fmt_a, accumulate
     (300, 200, 272, 272, 272, 200, 0, False),
     (257, 520, 1040, 1056, 1040, 528, 1, True),
-    (64, 4096, 8192, 8192, 8192, 4100, 1, False),   # k split over 4 workgroups
+    (64, 4096, 8192, 8192, 8192, 4100, 1, False),   # k split over 8 workgroups
     (1, 16, 16, 16, 16, 16, 0, False),
     (129, 260, 304, 304, 320, 260, 1, True),        # k extent of a padded transpose
     (520, 264, 8192, 8192, 8192, 264, 0, True),     # k split, accumulating
