@@ -21,6 +21,8 @@ from .mlp import (  # noqa: F401
     Params,
     rms_norm_fwd,
     rms_norm_bwd,
+    activation_fwd,
+    activation_bwd,
     sigmoid,
     silu,
     silu_grad,

@@ -168,35 +168,60 @@ def rms_norm_bwd(dN, x, r, w):
 
 # ------------------------------------------------------ expansion / contraction
 
+def activation_fwd(pre, act: str, R=_identity):
+    """The activation applied locally to a shard's pre-activations ("Split the
+    expansion": no communication).  SwiGLU: pre = (g, u), a = SiLU(g) * u;
+    GeLU: pre = (h,), a = gelu(h).  ``R`` is the storage rounding of a."""
+    if act == "swiglu":
+        g, u = pre
+        return R(silu(g) * u)
+    if act == "gelu":
+        (h,) = pre
+        return R(gelu(h))
+    raise ValueError(act)
+
+
+def activation_bwd(da, pre, act: str, R=_identity):
+    """Backward of activation_fwd for incoming da = dL/da.  SwiGLU:
+    dg = da * u * SiLU'(g), du = da * SiLU(g); GeLU: dh = da * gelu'(h).
+    Returns the tuple of pre-activation gradients, each rounded by ``R``
+    (they are stored tensors: the pre-activation gradients)."""
+    if act == "swiglu":
+        g, u = pre
+        return R(da * u * silu_grad(g)), R(da * silu(g))
+    if act == "gelu":
+        (h,) = pre
+        return (R(da * gelu_grad(h)),)
+    raise ValueError(act)
+
+
 def expansion_fwd(n, p: Params, act: str, R=_identity):
     """Column-parallel expansion on whatever channels ``p`` holds.
     SwiGLU: g = n Wg^T, u = n Wu^T, a = SiLU(g) * u; returns (pre=(g, u), a).
     GeLU:   h = n W1^T + b1, a = gelu(h);             returns (pre=(h,), a).
     ``R`` is the storage rounding of the pre-activations and of a."""
     if act == "swiglu":
-        g = R(n @ p.w_in[0].T)
-        u = R(n @ p.w_in[1].T)
-        return (g, u), R(silu(g) * u)
-    if act == "gelu":
-        h = R(n @ p.w_in.T + p.b_in[None, :])
-        return (h,), R(gelu(h))
-    raise ValueError(act)
+        pre = (R(n @ p.w_in[0].T), R(n @ p.w_in[1].T))
+    elif act == "gelu":
+        pre = (R(n @ p.w_in.T + p.b_in[None, :]),)
+    else:
+        raise ValueError(act)
+    return pre, activation_fwd(pre, act, R)
 
 
-def expansion_bwd(da, n, pre, p: Params, act: str, R=_identity):
+def expansion_bwd(da, n, pre, p: Params, act: str, R=_identity, with_d_pre: bool = False):
     """Backward of expansion_fwd for incoming da.  Returns
-    (d_w_in, d_b_in or None, dN contribution of these channels).
+    (d_w_in, d_b_in or None, dN contribution of these channels), and with
+    ``with_d_pre`` also the pre-activation gradients (dg, du) or (dh,).
     ``R`` is the storage rounding of the pre-activation gradients."""
+    d_pre = activation_bwd(da, pre, act, R)
     if act == "swiglu":
-        g, u = pre
-        dg = R(da * u * silu_grad(g))
-        du = R(da * silu(g))
-        d_w_in = np.stack([dg.T @ n, du.T @ n])
-        dN = dg @ p.w_in[0] + du @ p.w_in[1]
-        return d_w_in, None, dN
-    (h,) = pre
-    dh = R(da * gelu_grad(h))
-    return dh.T @ n, np.sum(dh, axis=0), dh @ p.w_in
+        dg, du = d_pre
+        res = (np.stack([dg.T @ n, du.T @ n]), None, dg @ p.w_in[0] + du @ p.w_in[1])
+    else:
+        (dh,) = d_pre
+        res = (dh.T @ n, np.sum(dh, axis=0), dh @ p.w_in)
+    return res + (d_pre,) if with_d_pre else res
 
 
 def _sgd(p: Params, grads: dict, lr, R=_identity) -> Params:
@@ -231,11 +256,11 @@ def dense_step(x, p: Params, act: str, eps: float, lr: float, dtype=np.float64, 
     g["b_down"] = np.sum(dY, axis=0)
     g["w_down"] = dY.T @ a
     da = dY @ p.w_down
-    g["w_in"], g["b_in"], dN = expansion_bwd(da, n, pre, p, act, R)
+    g["w_in"], g["b_in"], dN, d_pre = expansion_bwd(da, n, pre, p, act, R, with_d_pre=True)
     dxn, g["norm_w"] = rms_norm_bwd(dN, x, r, p.norm_w)
     dx = R(dY + dxn)
     return dict(x=x, n=n, rstd=r, pre=pre, a=a, z=z, out=out, loss=loss, dY=dY, da=da,
-                dN=dN, dx=dx, grads=g, params=p, new_params=_sgd(p, g, lr, R), new_masters=_sgd(p, g, lr))
+                d_pre=d_pre, dN=dN, dx=dx, grads=g, params=p, new_params=_sgd(p, g, lr, R), new_masters=_sgd(p, g, lr))
 
 
 # ---------------------------------------------------------------- sharded step
