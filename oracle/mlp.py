@@ -331,7 +331,8 @@ def sharded_step(x, p: Params, act: str, eps: float, lr: float, shards: int,
         rk["loss"] = 0.5 * np.sum(dY * dY)
         g = {"b_down": np.sum(dY, axis=0), "w_down": dY.T @ rk["a"]}
         da = dY @ lp.w_down
-        g["w_in"], g["b_in"], rk["dN_partial"] = expansion_bwd(da, rk["n"], rk["pre"], lp, act, R)
+        g["w_in"], g["b_in"], rk["dN_partial"], rk["d_pre"] = expansion_bwd(da, rk["n"], rk["pre"], lp, act, R,
+                                                                          with_d_pre=True)
         rk["da"] = da
         rk["grads"] = g
 

@@ -272,10 +272,13 @@ hipError_t launch_colsum(DType dt, const void* in, float* out, void* ws, int64_t
 
 hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, float lr, hipStream_t s) {
   KernelTimer timer("sgd", s);
+  // each launch takes the next kSgdMaxTensors entries of the list (empty
+  // tensors among them are skipped), so every tensor is updated exactly once
   for (int first = 0; first < count; first += kSgdMaxTensors) {
     SgdList L{};
     int64_t blocks = 0;
-    for (int i = first; i < count && L.count < kSgdMaxTensors; ++i) {
+    const int last = count < first + kSgdMaxTensors ? count : first + kSgdMaxTensors;
+    for (int i = first; i < last; ++i) {
       if (list[i].n == 0) continue;
       SgdSeg& sg = L.seg[L.count++];
       sg.pin = list[i].param_in;

@@ -108,6 +108,40 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ 
   }
 }
 
+// Rows wider than 32 chunks per lane (fp32 rows over 8192 columns): one wave
+// per row in two passes over the row (sum of squares, then the scaled
+// store), re-reading x instead of holding the row in registers.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_loop_kernel(const T* __restrict__ x, const T* __restrict__ w,
+                                                               T* __restrict__ n, float* __restrict__ rstd,
+                                                               int64_t rows, int H, float eps) {
+  constexpr int E = Elem<T>::kPerChunk;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  const int nch = H / E;
+  const T* xr = x + row * H;
+  float ss = 0.f;
+  for (int c = lane; c < nch; c += 64) {
+    float f[E];
+    Chunk<T>::unpack(*reinterpret_cast<const uint4*>(xr + (int64_t)c * E), f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) ss += f[e] * f[e];
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  if (lane == 0) rstd[row] = r;
+  T* nr = n + row * H;
+  for (int c = lane; c < nch; c += 64) {
+    float f[E], wf[E];
+    Chunk<T>::unpack(*reinterpret_cast<const uint4*>(xr + (int64_t)c * E), f);
+    Chunk<T>::unpack(*reinterpret_cast<const uint4*>(w + (int64_t)c * E), wf);
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] = f[e] * r * wf[e];
+    *reinterpret_cast<uint4*>(nr + (int64_t)c * E) = Chunk<T>::pack(f);
+  }
+}
+
 template <typename T>
 hipError_t fwd_t(const void* x, const void* w, void* n, float* rstd, int64_t T_, int64_t H, float eps,
                  hipStream_t s) {
@@ -136,8 +170,11 @@ hipError_t fwd_t(const void* x, const void* w, void* n, float* rstd, int64_t T_,
     TPMLP_FWD(8);
   } else if (per_lane <= 16) {
     TPMLP_FWD(16);
-  } else {
+  } else if (per_lane <= 32) {
     TPMLP_FWD(32);
+  } else {
+    hipLaunchKernelGGL(rmsnorm_fwd_loop_kernel<T>, dim3((unsigned)((T_ + 3) / 4)), dim3(256), 0, s, xp, wp, np_, rstd,
+                       T_, (int)H, eps);
   }
 #undef TPMLP_FWD
   return hipGetLastError();

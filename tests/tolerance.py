@@ -13,7 +13,10 @@ elementwise relative error is meaningless for entries near zero among 10^8
 values; the floor makes the bound relative to the tensor's own scale.  bf16
 rounding of a stored intermediate is 2^-9 ~ 2e-3 relative, so on the narrow
 test shapes correct kernels sit around 1e-3 to 5e-3 and a real fault (a wrong
-index, a dropped term) lands far above 2e-2.  Wide shapes: NATURAL_FACTOR.
+index, a dropped term) lands far above 2e-2.  Wide shapes (10^7 - 10^8
+entries), where upstream rounding flips leave a correct implementation no
+margin end to end on the activation, dN and dx, hold those three tensors to
+the same bound stage by stage (tests/stagewise.py); the bound is never raised.
 """
 
 import numpy as np
@@ -42,17 +45,6 @@ FP8_STEP_FROB = 5e-2
 
 FP32_ATOL = 1e-5
 BF16_RTOL = 2e-2
-# Wide bf16 shapes (thousands of tokens x thousands of hidden columns): a
-# stored bf16 intermediate that lies within an fp32 rounding of a bf16
-# rounding boundary is rounded one way by an fp32 implementation and the other
-# way by the fp64 oracle; SiLU's slope amplifies such a flip (for g << 0 the
-# log-derivative of silu(g) is about 1 + |g|) and it travels through the
-# following GEMM.  Among 10^7 - 10^8 entries the worst floored error of a
-# correct fp32 implementation then reaches 1.5 - 2e-2 (measured with the oracle
-# itself in fp32 arithmetic against fp64: dN 1.9e-2 and dx 1.9e-2 at 8000 x
-# 4000).  Such cases are bounded by max(BF16_RTOL, NATURAL_FACTOR x that
-# fp32-oracle error on the same input), computed per tensor by the test.
-NATURAL_FACTOR = 1.5
 
 
 def _np(a):
@@ -79,11 +71,6 @@ def floored_rel(got, ref, rowwise: bool) -> float:
     den = np.maximum(np.abs(r), rho)
     den = np.where(den > 0, den, 1.0)
     return float(np.max(np.abs(g - r) / den))
-
-
-def natural_bound(ref64, ref32, rowwise: bool = False) -> float:
-    """Bound for a bf16 tensor from the oracle's own fp32-arithmetic error."""
-    return max(BF16_RTOL, NATURAL_FACTOR * floored_rel(ref32, ref64, rowwise))
 
 
 def check(name, got, ref, dtype: str, rowwise: bool = False, report=None, tol=None) -> float:
