@@ -11,11 +11,17 @@ host, and then:
   (tests/stagewise.py), within the bf16 bound 2e-2 (floored relative).
 * test_end_to_end: every tensor of the step against the fp64 oracle's whole
   dense step (storage model: each stored activation rounded to bf16 once),
-  element by element within 2e-2, except the activation, dN and dx: those
-  three sit, for any correct fp32-accumulating implementation, up to 1.9e-2
-  from the fp64 oracle end to end at these sizes (rounding flips of upstream
-  stored values amplified by SiLU's slope; measured with the oracle itself
-  run in fp32 arithmetic), so they are held to 2e-2 stage-wise and their
+  element by element within 2e-2, except the activation, the pre-activation
+  gradients, dN and dx.  For those, any correct fp32-accumulating
+  implementation sits up to 1.9e-2 (act, dN, dx) and 5.5e-2 (pre-activation
+  gradients) from the fp64 oracle end to end at these sizes, measured with
+  the oracle itself run in fp32 arithmetic: a stored bf16 pre-activation g or
+  u whose exact value lies next to a rounding midpoint is rounded one way in
+  fp32 and the other in fp64; the flip moves a by up to 2^-8 |g u|, that
+  channel's column of W_d spreads it over the row of z and of out (flipping
+  many of the row's stored outputs), and since d out = out it returns through
+  W_d^T into the same channel's d_act with gain |W_d[:, j]|^2 (about 1.6 at
+  these shapes).  Those four are held to 2e-2 stage by stage, and their
   end-to-end error is printed.  The full-width workload (34.6 TFLOP and
   ~470 M-element activation tensors per dense oracle step) is compared end to
   end on sampled rows, channels and columns that the oracle computes exactly
@@ -39,7 +45,6 @@ pytestmark = pytest.mark.gpu
 
 FULL = ["gpt2s_gelu_tp1", "llama3_8b_tp8", "llama3_70b_tp8_rank", "llama3_8b_tp1_master"]
 DENSE_END_TO_END = {"gpt2s_gelu_tp1", "llama3_8b_tp8", "llama3_70b_tp8_rank"}
-STAGEWISE_ONLY = ("act", "dN", "dx")
 
 
 def say(*a):
@@ -119,7 +124,6 @@ def test_end_to_end(full):
     cmp("out", h["out"], d["out"], True)
     for s, sh in enumerate(h["shards"]):
         cmp(f"pre[{s}]", sh["pre"], _pre_of_shards(w, d["pre"], s), True)
-        cmp(f"d_pre[{s}]", sh["d_pre"], _pre_of_shards(w, d["d_pre"], s), True)
     cmp("d_w_in", _cat_shards(h, "d_w_in", 1 if swiglu else 0), g["w_in"], False)
     cmp("d_w_down", _cat_shards(h, "d_w_down", 1), g["w_down"], False)
     cmp("d_norm_w", h["d_norm_w"], g["norm_w"], False)
@@ -135,6 +139,8 @@ def test_end_to_end(full):
         cmp("new_b_in", torch.cat([new[f"b_in.{s}"].float() for s in range(n)]), npar.b_in, False)
     # held stage-wise (test_stage); printed here
     printed["act"] = floored_rel(_cat_shards(h, "act", 1), d["a"], True)
+    printed["d_pre"] = max(floored_rel(sh["d_pre"], _pre_of_shards(w, d["d_pre"], s), True)
+                           for s, sh in enumerate(h["shards"]))
     printed["dN"] = floored_rel(h["dN"], d["dN"], True)
     printed["dx"] = floored_rel(h["dx"], d["dx"], True)
     say(f"  {w.name} end-to-end: " + ", ".join(f"{k} {v:.2e}" for k, v in report.items())

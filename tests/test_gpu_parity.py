@@ -319,8 +319,9 @@ def test_sgd_multi_more_than_one_launch_with_empty_tensors_in_place():
             continue
         got = dp.double().cpu().numpy()
         rho = float(np.sqrt(np.mean(ref * ref)))
-        # one step: within one bf16 place of the exact rounding (two steps would be ~lr |g| away)
-        assert np.max(np.abs(got - ref) / np.maximum(np.abs(ref), rho)) <= 2.0 ** -8
+        # one step: within one bf16 place (2^-7 of the value at most) of the exact rounding; a second
+        # step would move the value by lr |g|, about 0.1 of its size
+        assert np.max(np.abs(got - ref) / np.maximum(np.abs(ref), rho)) <= 2.0 ** -7
 
 
 @pytest.mark.parametrize("H", [8200, 12288, 16384])
