@@ -214,6 +214,26 @@ int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* 
 size_t tp_mlp_workspace_bytes(const tp_mlp_desc* d, int32_t phase);
 
 /*
+ * tp_mlp_backward_noalloc - tp_mlp_backward for callers that cannot allocate
+ * device memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation): the same phases, arguments, checks,
+ * kernels and results, but a->workspace and a->workspace_bytes are ignored.
+ * The scratch is instead a device array of TP_MLP_NOALLOC_SCRATCH_BYTES that
+ * the library itself holds, one per GPU it runs on, for the life of the
+ * process; the first call on a device looks up that device's copy (the
+ * device current at the call).  The call allocates nothing.
+ *   Returns TP_MLP_EWORKSPACE, before any work is enqueued, when
+ *   tp_mlp_workspace_bytes(d, phase) exceeds TP_MLP_NOALLOC_SCRATCH_BYTES.
+ *   Every call on one GPU shares that GPU's scratch: calls whose work may
+ *   overlap on one device (other streams, other threads) race; order them
+ *   on one stream or synchronise them.  The scratch holds no state from one
+ *   call to the next that a later call relies on (every element a call reads
+ *   was written by that call).
+ */
+#define TP_MLP_NOALLOC_SCRATCH_BYTES (128u << 20)
+int tp_mlp_backward_noalloc(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* a, void* stream);
+
+/*
  * tp_mlp_sgd_step - one plain SGD update, p <- p - lr * g (the page's one SGD
  * update of every parameter, "Reproduce one dense training step").
  *   param_in  [n] in param_dtype, param_out [n] in param_dtype (may equal

@@ -37,7 +37,8 @@ EXPORTED = ("tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_works
             "tp_mlp_fp8_meta_init", "tp_mlp_fp8_cast", "tp_mlp_fp8_update_scales", "tp_mlp_forward_fp8",
             "tp_mlp_backward_fp8", "tp_mlp_fp8_gemm", "tp_mlp_fp8_gemm_workspace_bytes", "tp_attn_forward",
             "tp_attn_backward", "tp_attn_workspace_bytes", "tp_attention_forward", "tp_attention_backward",
-            "tp_attention_backward_workspace_bytes", "tp_mlp_profile_only", "tp_attn_forward_workspace_bytes")
+            "tp_attention_backward_workspace_bytes", "tp_mlp_profile_only", "tp_attn_forward_workspace_bytes",
+            "tp_mlp_backward_noalloc")
 
 
 class TPMLPError(RuntimeError):
@@ -117,6 +118,9 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_backward.argtypes = [ctypes.POINTER(tp_mlp_desc), ctypes.c_int32, ctypes.POINTER(tp_mlp_bwd_args),
                                       _vp]
         L.tp_mlp_backward.restype = ctypes.c_int
+        L.tp_mlp_backward_noalloc.argtypes = [ctypes.POINTER(tp_mlp_desc), ctypes.c_int32,
+                                              ctypes.POINTER(tp_mlp_bwd_args), _vp]
+        L.tp_mlp_backward_noalloc.restype = ctypes.c_int
         L.tp_mlp_workspace_bytes.argtypes = [ctypes.POINTER(tp_mlp_desc), ctypes.c_int32]
         L.tp_mlp_workspace_bytes.restype = ctypes.c_size_t
         L.tp_mlp_sgd_step.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, _vp]
@@ -242,6 +246,18 @@ def tp_mlp_backward(desc: tp_mlp_desc, phase: int, stream=None, **tensors) -> No
     ``workspace`` may be given, ``workspace_bytes`` defaults to its size."""
     a = _bwd_args(tensors)
     _check(lib().tp_mlp_backward(ctypes.byref(desc), phase, ctypes.byref(a), _stream(stream)))
+
+
+def tp_mlp_backward_noalloc(desc: tp_mlp_desc, phase: int, stream=None, **tensors) -> None:
+    """tp_mlp_backward with the library's own scratch: ``workspace`` is not
+    taken (the C call ignores it)."""
+    if "workspace" in tensors or "workspace_bytes" in tensors:
+        raise TypeError("tp_mlp_backward_noalloc takes no workspace")
+    a = _bwd_args(tensors)
+    _check(lib().tp_mlp_backward_noalloc(ctypes.byref(desc), phase, ctypes.byref(a), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 def _bwd_args(tensors: dict) -> tp_mlp_bwd_args:

@@ -2,6 +2,7 @@
 // sequence of kernel launches for each call.
 #include <stdarg.h>
 #include <cmath>
+#include <mutex>
 #include <stdio.h>
 
 #include "../../include/tp_mlp.h"
@@ -211,13 +212,11 @@ size_t tp_mlp_workspace_bytes(const tp_mlp_desc* d, int32_t phase) {
   return need;
 }
 
-int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* a, void* stream) {
-  const char* fn = "tp_mlp_backward";
-  g_err[0] = 0;
-  int rc = check_desc(d, fn);
-  if (rc) return rc;
-  if (!a) return fail(TP_MLP_EINVAL, "%s: args is NULL", fn);
-  if (phase != TP_MLP_BWD_SHARD && phase != TP_MLP_BWD_NORM) return fail(TP_MLP_EINVAL, "%s: unknown phase", fn);
+namespace {
+
+// The backward of both phases after the descriptor, the phase and the args
+// pointer have been checked; a->workspace is the scratch its kernels use.
+int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* a, void* stream, const char* fn) {
   const int64_t T = d->tokens, H = d->hidden, F = d->ffn_local;
   const bool swiglu = d->act == TP_MLP_ACT_SWIGLU;
   const DType dt = dt_of(d->dtype);
@@ -341,6 +340,67 @@ int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* 
   if (!swiglu)
     CHECK_HIP(launch_colsum(dt, a->d_pre, a->d_b_in, a->workspace, T, F, accum, s), "d_b_in column sum");
   return TP_MLP_OK;
+}
+
+int check_bwd_call(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* a, const char* fn) {
+  const int rc = check_desc(d, fn);
+  if (rc) return rc;
+  if (!a) return fail(TP_MLP_EINVAL, "%s: args is NULL", fn);
+  if (phase != TP_MLP_BWD_SHARD && phase != TP_MLP_BWD_NORM) return fail(TP_MLP_EINVAL, "%s: unknown phase", fn);
+  return TP_MLP_OK;
+}
+
+// Scratch of tp_mlp_backward_noalloc: a device array of the library's own,
+// one per GPU (each device's copy lives at its own address for as long as
+// the process runs).  Host code never passes the array's name to a kernel:
+// the name is a host-side stand-in; the device address is taken once per
+// device with hipGetSymbolAddress, with that device current, and kept.
+static __device__ __align__(256) unsigned char scratch[TP_MLP_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(const char* fn, void** out) {
+  int dev = -1;
+  CHECK_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TP_MLP_EINVAL, "%s: device index %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    CHECK_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(TP_MLP_EHIP, "%s: no device address for the scratch array", fn);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TP_MLP_OK;
+}
+
+}  // namespace
+
+int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* a, void* stream) {
+  const char* fn = "tp_mlp_backward";
+  g_err[0] = 0;
+  const int rc = check_bwd_call(d, phase, a, fn);
+  if (rc) return rc;
+  return backward_checked(d, phase, a, stream, fn);
+}
+
+int tp_mlp_backward_noalloc(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* a, void* stream) {
+  const char* fn = "tp_mlp_backward_noalloc";
+  g_err[0] = 0;
+  int rc = check_bwd_call(d, phase, a, fn);
+  if (rc) return rc;
+  const size_t need = tp_mlp_workspace_bytes(d, phase);
+  if (need > (size_t)TP_MLP_NOALLOC_SCRATCH_BYTES)
+    return fail(TP_MLP_EWORKSPACE, "%s: this call needs %zu bytes of scratch, more than the %zu the library holds",
+                fn, need, (size_t)TP_MLP_NOALLOC_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  rc = scratch_of_current_device(fn, &ptr);
+  if (rc) return rc;
+  tp_mlp_bwd_args b = *a;  // the caller's tensors with the library's scratch
+  b.workspace = ptr;
+  b.workspace_bytes = (size_t)TP_MLP_NOALLOC_SCRATCH_BYTES;
+  return backward_checked(d, phase, &b, stream, fn);
 }
 
 namespace {
