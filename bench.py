@@ -14,7 +14,10 @@ step (18 T H F_full flops per step for SwiGLU); per-kernel times come from
 HIP events the library records on its launch stream during the timed steps.
 The CPU oracle is timed on a bounded token slice of the same workload.
 
-After the timed step, `optimizer_path` reports the optimiser side on the same
+After the timed step, `other_workloads` times the other bf16 workloads the
+same way (GPT-2-small GeLU tp=1, one Llama-3-70B TP=8 rank, Llama-3-8B full
+width with fp32 masters), each with its dominant kernel's roofline, and
+`optimizer_path` reports the optimiser side on the same
 workload (unless --no-extras): the global-norm clip plus AdamW over every
 shard's parameters (each kernel against HBM bandwidth), and the step run as 2
 microbatches whose weight gradients accumulate in fp32.  `sequence_parallel`
@@ -44,6 +47,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+# the bf16 workloads timed besides the main one (the tiny fp32 one is correctness only)
+OTHER_WORKLOADS = ("gpt2s_gelu_tp1", "llama3_70b_tp8_rank", "llama3_8b_tp1_master")
 
 
 def gemm_flops(w) -> dict:
@@ -167,7 +172,7 @@ def cpu_baseline(w, t, budget_s: float = 15.0) -> dict:
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"oracle.sharded_step (fp64 numpy) on the first {tp} of {w.tokens} tokens, all "
                       f"{w.n_run} shards, full H and F; {secs:.2f} s; tokens/s {tp / secs:.1f}",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def optimizer_path(st, w, steps: int, warmup: int) -> dict:
@@ -349,6 +354,62 @@ def sequence_parallel_timing(w, t, steps: int, warmup: int) -> dict:
             "tflops": w.flops_per_step / (ms / 1e3) / 1e12}
 
 
+def workload_timing(name: str, steps: int, warmup: int) -> dict:
+    """One more workload's step, timed as the main one is (inputs resident,
+    SGD out of place, no events in the timed steps), with every kernel's
+    duration from a second run and the dominant kernel against its roofline."""
+    import torch
+
+    import synth
+    from tensor_transformer_mlp_rmsnorm_amd import _lib as L
+    from tensor_transformer_mlp_rmsnorm_amd.step import ShardedStep
+
+    w = synth.workload(name)
+    st = ShardedStep(w, synth.draw(w), device="cuda:0", out_of_place_sgd=True)
+    for _ in range(max(1, warmup)):
+        st.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    L.tp_mlp_profile_enable(True)
+    for _ in range(steps):
+        st.step()
+    torch.cuda.synchronize()
+    L.tp_mlp_profile_enable(False)
+    prof = L.tp_mlp_profile_entries()
+    del st
+    torch.cuda.empty_cache()
+    kernels = {k: roofline_entry(k, n, tot, w, steps) for k, (n, tot) in prof.items()}
+    dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
+    gemm_ms = sum(tot for k, (n, tot) in prof.items() if k in gemm_flops(w)) / steps
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    tflops = w.flops_per_step / (ms / 1e3) / 1e12
+    d = kernels[dom]
+    return {"workload": name, "tokens": w.tokens, "hidden": w.hidden, "ffn_full": w.ffn_full, "shards": w.shards,
+            "shards_run": w.n_run, "act": w.act, "master": w.master, "ms_per_step": ms, "tflops": tflops,
+            "pct_of_bf16_peak": 100.0 * tflops / peak, "tokens_per_s": w.tokens / (ms / 1e3),
+            "gemm_ms_per_step": gemm_ms,
+            "gemm_tflops": w.flops_per_step / (gemm_ms / 1e3) / 1e12 if gemm_ms > 0 else None,
+            "roofline": {"kernel": dom, "bound": d.get("bound"), "achieved": d.get("achieved"), "peak": d.get("peak"),
+                         "unit": d.get("unit"), "frac": d.get("frac"), "per_launch": d.get("per_launch"),
+                         "avg_ms": d.get("avg_ms")},
+            "kernels": kernels}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,8 +419,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-extras", action="store_true", help="skip the measurements after the timed step")
-    ap.add_argument("--extras", default="optimizer,sp,fp8,attention",
-                    help="comma-separated measurements after the timed step: optimizer, sp, fp8, attention")
+    ap.add_argument("--extras", default="configs,optimizer,sp,fp8,attention",
+                    help="comma-separated measurements after the timed step: configs (the other bf16 workloads: "
+                         "GPT-2-small GeLU, one Llama-3-70B TP=8 rank, Llama-3-8B full width with fp32 masters), "
+                         "optimizer, sp, fp8, attention")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -448,6 +511,11 @@ def main() -> int:
         "kernels": kernels,
     }
     extras = set() if args.no_extras else {e.strip() for e in args.extras.split(",") if e.strip()}
+    if "configs" in extras:
+        out["other_workloads"] = {}
+        for name in OTHER_WORKLOADS:
+            if name != w.name:
+                out["other_workloads"][name] = workload_timing(name, args.steps, args.warmup)
     if "optimizer" in extras:
         out["optimizer_path"] = optimizer_path(st, w, args.steps, args.warmup)
     if "sp" in extras and w.n_run == w.shards and w.shards > 1:

@@ -71,12 +71,6 @@ struct Tile256x224 {
 struct Tile224x256 {
   static constexpr int TM = 224, TN = 256, NW = 8, GN = 4, WMB = 7, WNB = 4;
 };
-// 16 waves of 64 x 64: a third more LDS bytes per flop than 128 x 64, but four
-// waves per SIMD instead of two to overlap the transpose reads of an
-// MN-contiguous B with the multiplies of the other waves.
-struct Tile256x256W16 {
-  static constexpr int TM = 256, TN = 256, NW = 16, GN = 4, WMB = 4, WNB = 4;
-};
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -294,17 +288,29 @@ __device__ __forceinline__ void epilogue_act_bwd(const GemmArgs& g, const floatx
     r[3] = __uint_as_float(u.y & 0xffff0000u);
     return r;
   };
-  load_block(0, buf[0]);
+  // When the wave's whole tile of saved values fits in the registers the main
+  // loop has freed (56 loads of 8 bytes: the 64 x 112 wave tile with g and u),
+  // every load is issued before the first is used, so the tile's reads are in
+  // flight together; otherwise one 16-row block ahead.
+  constexpr bool kAllAhead = WMB * WNB * NL <= 56;
+  uint2 all[kAllAhead ? WMB : 1][WNB][NL];
+  if constexpr (kAllAhead) {
+#pragma unroll
+    for (int i = 0; i < WMB; ++i) load_block(i, all[i]);
+  } else {
+    load_block(0, buf[0]);
+  }
 #pragma unroll
   for (int i = 0; i < WMB; ++i) {
-    if (i + 1 < WMB) load_block(i + 1, buf[(i + 1) & 1]);
+    if (!kAllAhead && i + 1 < WMB) load_block(i + 1, buf[(i + 1) & 1]);
+    const uint2 (&cur)[WNB][NL] = kAllAhead ? all[kAllAhead ? i : 0] : buf[i & 1];
     const int64_t m = m0 + i * 16 + frow;
 #pragma unroll
     for (int j = 0; j < WNB; ++j) {
       const int64_t n = n0 + j * 16 + col4;
       const floatx4 v = acc[i][j];
       if constexpr (kSwiglu) {
-        const floatx4 gv = unpack(buf[i & 1][j][0]), uv = unpack(buf[i & 1][j][NL - 1]);
+        const floatx4 gv = unpack(cur[j][0]), uv = unpack(cur[j][NL - 1]);
         floatx4 dg, du;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -317,7 +323,7 @@ __device__ __forceinline__ void epilogue_act_bwd(const GemmArgs& g, const floatx
           store4<bf16_t>(out + m * ld + second + n, du);
         }
       } else {
-        const floatx4 h = unpack(buf[i & 1][j][0]);
+        const floatx4 h = unpack(cur[j][0]);
         floatx4 dh;
 #pragma unroll
         for (int r = 0; r < 4; ++r) dh[r] = v[r] * gelu_grad_f(h[r]);
@@ -697,6 +703,82 @@ __global__ __launch_bounds__(SH::NW * 64, 1) void gemm_bf16_kernel(GemmArgs g, i
                                   (int64_t)tn * SH::TN + wn * SH::WNB * 16, 0, ks, lane);
 }
 
+// The two-stage schedule with the fragment reads one k-half ahead: each wave
+// holds two fragment sets; the reads of k-half h + 1 are issued before the
+// MFMAs of k-half h, so their LDS latency runs under those MFMAs instead of
+// stalling both waves of a SIMD at the start of every k-tile.  Per k-tile:
+//   reads  set1 <- (tile j, k 32-63)          MFMAs on set0 (tile j, k 0-31)
+//   wait for this wave's reads and its loads of tile j+1; barrier (tile j+1
+//   published, every wave done with tile j's stage)
+//   loads of tile j+2 into tile j's stage
+//   reads  set0 <- (tile j+1, k 0-31)         MFMAs on set1 (tile j, k 32-63)
+// Every fragment read of a k-half is issued before the first MFMA that
+// follows it (left to itself the compiler sinks the reads below most of the
+// MFMAs, and they are then still in flight at the barrier).
+__device__ __forceinline__ void pipe_order() { __builtin_amdgcn_sched_barrier(0); }
+
+template <bool AK, bool BKC, int EPI, class SH>
+__global__ __launch_bounds__(SH::NW * 64, 1) void gemm_bf16_pipe_kernel(GemmArgs g, int ntm, int ntn) {
+  extern __shared__ uint4 smem[];  // 2 stages x (A tile + B tile) = 128 KiB
+  static_assert(!(AK && BKC), "both operands K-contiguous: the ping-pong kernel");
+  static_assert(EPI != kEpiSwigluFwd, "the SwiGLU forward is a K-contiguous (ping-pong) GEMM");
+  static_assert(SH::NW / SH::GN * SH::WMB * 16 == SH::TM && SH::GN * SH::WNB * 16 == SH::TN, "waves cover the tile");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / SH::GN, wn = wave % SH::GN;
+
+  int tm, tn, ks;
+  tile_coords(blockIdx.x, ntm, ntn, g.ksplit, tm, tn, ks);
+  const bf16_t* __restrict__ A = static_cast<const bf16_t*>(g.A);
+  const bf16_t* __restrict__ B = static_cast<const bf16_t*>(g.B);
+  const int64_t K = g.K;
+  const int64_t kper = ((K + (int64_t)g.ksplit * kBK - 1) / ((int64_t)g.ksplit * kBK)) * kBK;
+  const int64_t kbeg = (int64_t)ks * kper;
+  const int64_t kend = min(K, kbeg + kper);
+  const RowMap ra{(int64_t)tm * SH::TM, g.M, false, 0};
+  const RowMap rb{(int64_t)tn * SH::TN, g.N, false, 0};
+
+  floatx4 acc[SH::WMB][SH::WNB];
+#pragma unroll
+  for (int i = 0; i < SH::WMB; ++i)
+#pragma unroll
+    for (int j = 0; j < SH::WNB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const Operand opa = make_operand(A, AK ? g.M : K, g.lda);
+  const Operand opb = make_operand(B, BKC ? g.N : K, g.ldb);
+  const int nk = kend > kbeg ? (int)((kend - kbeg + kBK - 1) / kBK) : 0;
+  issue_tile<AK, 2, SH::NW>(opa, smem, ra, kbeg, kend, wave, lane);
+  issue_tile<BKC, 2, SH::NW>(opb, smem + kTileU4, rb, kbeg, kend, wave, lane);
+  __syncthreads();  // tile 0 landed
+  if (nk > 1) {
+    issue_tile<AK, 2, SH::NW>(opa, smem + kStageU4, ra, kbeg + kBK, kend, wave, lane);
+    issue_tile<BKC, 2, SH::NW>(opb, smem + kStageU4 + kTileU4, rb, kbeg + kBK, kend, wave, lane);
+  }
+  uint4 a0[SH::WMB], b0[SH::WNB], a1[SH::WMB], b1[SH::WNB];
+  read_half<AK, BKC>(a0, b0, smem, 0, wm, wn, lane);
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint4* st = smem + (kt & 1) * kStageU4;
+    read_half<AK, BKC>(a1, b1, st, 1, wm, wn, lane);
+    pipe_order();
+    mma_half(acc, a0, b0);
+    __syncthreads();  // this wave's reads and its loads of tile kt+1 done; every wave past tile kt's stage
+    if (kt + 2 < nk) {
+      uint4* dst = smem + (kt & 1) * kStageU4;
+      const int64_t k0 = kbeg + (int64_t)(kt + 2) * kBK;
+      issue_tile<AK, 2, SH::NW>(opa, dst, ra, k0, kend, wave, lane);
+      issue_tile<BKC, 2, SH::NW>(opb, dst + kTileU4, rb, k0, kend, wave, lane);
+    }
+    // the next tile's first half (the stage after the last tile holds whatever it held; unused)
+    read_half<AK, BKC>(a0, b0, smem + ((kt + 1) & 1) * kStageU4, 0, wm, wn, lane);
+    pipe_order();
+    mma_half(acc, a1, b1);
+  }
+
+  epilogue<EPI, SH::WMB, SH::WNB>(g, acc, (int64_t)tm * SH::TM + wm * SH::WMB * 16,
+                                  (int64_t)tn * SH::TN + wn * SH::WNB * 16, 0, ks, lane);
+}
+
 constexpr size_t kSmemBytes = 2 * kStageU4 * sizeof(uint4);
 constexpr size_t kSmemBytesPingPong = kSlots * kTileU4 * sizeof(uint4);
 
@@ -720,10 +802,24 @@ inline int64_t tile_cost(const GemmArgs& g, int ksplit, int cus) {
   return ((tiles + cus - 1) / cus) * SH::TM * SH::TN;  // rounds of one workgroup per CU x work per tile
 }
 
+// Which two-stage main loop a tile shape runs: the pipelined one where it was
+// measured faster -- the 224 x 256 tile (the gate/up weight gradient: 240 ->
+// 224 us) and the NN 256 x 256 tile (the input gradient: 237 -> 214 us against
+// the 16-wave tile) -- and the plain one for the 256 x 224 and the TN 256 x 256
+// tiles, where reading a whole k-half ahead measured slower.
+template <bool AK, bool BKC, class SH>
+constexpr bool pipelined_loop() {
+  if constexpr (SH::NW != 8) return false;
+  else if constexpr (SH::TM == 224 && SH::TN == 256) return true;
+  else return SH::TM == 256 && SH::TN == 256 && AK && !BKC;
+}
+
 template <bool AK, bool BKC, int EPI, class SH>
 hipError_t launch_two_stage(const GemmArgs& ga, hipStream_t s) {
   const int ntm = (int)((ga.M + SH::TM - 1) / SH::TM), ntn = (int)((ga.N + SH::TN - 1) / SH::TN);
-  auto kernel = gemm_bf16_kernel<AK, BKC, EPI, SH>;
+  void (*kernel)(GemmArgs, int, int);
+  if constexpr (pipelined_loop<AK, BKC, SH>()) kernel = gemm_bf16_pipe_kernel<AK, BKC, EPI, SH>;
+  else kernel = gemm_bf16_kernel<AK, BKC, EPI, SH>;
   static bool configured = false;  // raise the dynamic LDS limit once per instantiation
   if (!configured) {
     const hipError_t e =
@@ -776,7 +872,6 @@ hipError_t launch_tiles(const GemmArgs& ga, int ntm, int ntn, hipStream_t s) {
     if (cn < c0 && cn <= cm) return launch_two_stage<AK, BKC, EPI, Tile256x224>(ga, s);
     if (cm < c0) return launch_two_stage<AK, BKC, EPI, Tile224x256>(ga, s);
     // A K-contiguous, B MN-contiguous, fp32 out: 16 waves measured faster (dgrad 8192 x 4096 x 3584)
-    if constexpr (AK && !BKC && EPI == kEpiStoreF32) return launch_two_stage<AK, BKC, EPI, Tile256x256W16>(ga, s);
     return launch_two_stage<AK, BKC, EPI, Tile256x256>(ga, s);
   }
 }
