@@ -75,7 +75,8 @@ def hbm_bytes_per_step(w) -> dict:
         "rmsnorm_fwd": T * H * 2 * es + 4 * T + H * es,                 # x in, N out, rstd out, w in
         "partial_sum_residual": S * 4 * T * H + 2 * es * T * H + H * es,  # S fp32 partials + x in, out
         "partial_sum": S * 4 * T * H + 4 * T * H,                        # S fp32 partials in, dN out
-        "rmsnorm_bwd": T * H * (4 + 3 * es) + 4 * T + H * es,           # dN, x, dY in, dx out
+        # the S fp32 partials of dN (summed as they are read), x, dY in, dx out
+        "rmsnorm_bwd": T * H * (4 * S + 3 * es) + 4 * T + H * es,
         "sgd": n_params * per_param,                                     # p (or master), g in; p (+master) out
         # optimiser path: AdamW reads g, m, v and p (or master) and writes m, v, p (+ master)
         "adamw": n_params * ((4 + 4 + 4 + 8 + 8 + es) if w.master else (2 * es + 4 + 8 + 8)),

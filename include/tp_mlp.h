@@ -183,6 +183,15 @@ typedef struct {
      d_act GEMM */
   void* workspace;
   size_t workspace_bytes;
+  /* NORM phase, instead of d_normed: the shards' partials of dL/dN
+     (d_normed_part of each SHARD call), summed by the RMSNorm backward as it
+     reads them -- in index order with fp32 additions, the sum tp_partial_sum
+     forms, so the results are the same bits -- rather than summed into
+     d_normed first and read back.  A HOST array of n_d_normed_parts DEVICE
+     pointers, each [T, H] fp32, 1 <= n_d_normed_parts <= 64.
+     n_d_normed_parts = 0 (as in zero-initialised args): d_normed is read. */
+  const float* const* d_normed_parts;
+  int32_t n_d_normed_parts;
 } tp_mlp_bwd_args;
 
 /*
@@ -199,7 +208,8 @@ typedef struct {
  *   d_b_in       = sum_t dh                (GeLU only)
  *   d_normed_part= d_pre w_in              (fp32 partial, summed by tp_partial_sum)
  *   This phase reads normed, pre_act, act, w_in, w_down and d_out.
- * phase TP_MLP_BWD_NORM (once, after the sum):
+ * phase TP_MLP_BWD_NORM (once, after the sum, or with the sum streamed in
+ * through d_normed_parts):
  *   c_t      = (1/H) sum_i d_normed[t,i] norm_w[i] x[t,i]
  *   d_x      = d_out + rstd d_normed norm_w - x rstd^3 c        (residual + RMSNorm)
  *   d_norm_w = sum_t d_normed x rstd,   d_b_down = sum_t d_out

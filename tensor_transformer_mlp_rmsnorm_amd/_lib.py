@@ -75,7 +75,8 @@ class tp_mlp_adamw_tensor(ctypes.Structure):
 class tp_mlp_bwd_args(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("x", "normed", "rstd", "pre_act", "act", "norm_w", "w_in", "w_down", "d_out",
                                    "d_pre", "d_w_in", "d_b_in", "d_w_down", "d_normed_part", "d_normed", "d_x",
-                                   "d_norm_w", "d_b_down", "workspace")] + [("workspace_bytes", ctypes.c_size_t)]
+                                   "d_norm_w", "d_b_down", "workspace")] + [("workspace_bytes", ctypes.c_size_t)] + \
+        [("d_normed_parts", ctypes.POINTER(_vp)), ("n_d_normed_parts", ctypes.c_int32)]
 
 
 FP8_META_FIELDS = ("meta_normed", "meta_w_in", "meta_act", "meta_w_down", "meta_d_out", "meta_d_pre")
@@ -261,9 +262,17 @@ NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 def _bwd_args(tensors: dict) -> tp_mlp_bwd_args:
+    """``d_normed_parts`` may be a sequence of tensors (the NORM phase then
+    sums them); the pointer array stays alive with the returned struct."""
     a = tp_mlp_bwd_args()
+    parts = tensors.pop("d_normed_parts", None)
+    if parts:
+        arr = (_vp * len(parts))(*[_ptr(p) for p in parts])
+        a._parts_keepalive = arr
+        a.d_normed_parts = ctypes.cast(arr, ctypes.POINTER(_vp))
+        a.n_d_normed_parts = len(parts)
     for name, _ in tp_mlp_bwd_args._fields_:
-        if name == "workspace_bytes":
+        if name in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts"):
             continue
         v = tensors.pop(name, None)
         setattr(a, name, _ptr(v))

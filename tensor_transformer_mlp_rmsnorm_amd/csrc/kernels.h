@@ -134,10 +134,13 @@ hipError_t launch_rmsnorm_fwd(DType dt, const void* x, const void* w, void* n, f
                               int64_t T, int64_t H, float eps, hipStream_t s);
 
 // RMSNorm backward + residual: dx, and per-block column partials of
-// d_norm_w and d_b_down in `ws` followed by the fixed-order reduction.
+// d_norm_w and d_b_down in `ws` followed by the fixed-order reduction.  The
+// gradient of N is the sum, in index order, of the n_parts (1 .. 64) [T, H]
+// fp32 arrays dN_parts (a host array of device pointers).
+constexpr int kMaxNormParts = 64;
 size_t rmsnorm_bwd_workspace(int64_t T, int64_t H);
 // With `accum`, dw and db receive their current values plus the column sums.
-hipError_t launch_rmsnorm_bwd(DType dt, const float* dN, const void* x, const void* dY,
+hipError_t launch_rmsnorm_bwd(DType dt, const float* const* dN_parts, int n_parts, const void* x, const void* dY,
                               const float* rstd, const void* w, void* dx, float* dw, float* db,
                               void* ws, int64_t T, int64_t H, bool accum, hipStream_t s);
 

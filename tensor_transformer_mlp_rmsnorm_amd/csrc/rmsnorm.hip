@@ -3,7 +3,8 @@
 // Forward  ("Start with the dense block", synapticradio.com: N = rms_norm(x, norm_weight)):
 //   rstd_t = 1 / sqrt(mean_i x_ti^2 + eps),   N_ti = x_ti rstd_t w_i
 // Backward ("Put the other collective in backward": the summed dN goes
-// through RMSNorm's backward and into the residual input):
+// through RMSNorm's backward and into the residual input; the sum of the
+// shards' partials can be formed here, as the rows are read):
 //   c_t   = (1/H) sum_i dN_ti w_i x_ti
 //   dx_ti = dY_ti + rstd_t dN_ti w_i - x_ti rstd_t^3 c_t
 //   dw_i  = sum_t dN_ti x_ti rstd_t,   db_i = sum_t dY_ti
@@ -11,9 +12,9 @@
 // row, the row held in registers, the next row loading meanwhile) and writes
 // N and rstd.  The backward
 // streams dN (fp32), x and dY once, writes dx, and reduces the two column
-// sums deterministically: each workgroup owns a fixed range of rows and
-// fixed columns per thread, writes one partial row, and a second kernel sums
-// the partial rows in index order.
+// sums deterministically: each workgroup owns a fixed set of rows (every
+// G-th row, G workgroups) and fixed columns per thread, writes one partial
+// row, and a second kernel sums the partial rows in index order.
 #include "common.h"
 #include "kernels.h"
 
@@ -108,9 +109,9 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ 
   }
 }
 
-// Rows wider than 32 chunks per lane (fp32 rows over 8192 columns): one wave
-// per row in two passes over the row (sum of squares, then the scaled
-// store), re-reading x instead of holding the row in registers.
+// Rows wider than 16 chunks per lane (bf16 rows over 8192 columns, fp32 over
+// 4096; held in registers they would spill): one wave per row in two passes
+// over the row (sum of squares, then the scaled store), re-reading x.
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_loop_kernel(const T* __restrict__ x, const T* __restrict__ w,
                                                                T* __restrict__ n, float* __restrict__ rstd,
@@ -170,8 +171,6 @@ hipError_t fwd_t(const void* x, const void* w, void* n, float* rstd, int64_t T_,
     TPMLP_FWD(8);
   } else if (per_lane <= 16) {
     TPMLP_FWD(16);
-  } else if (per_lane <= 32) {
-    TPMLP_FWD(32);
   } else {
     hipLaunchKernelGGL(rmsnorm_fwd_loop_kernel<T>, dim3((unsigned)((T_ + 3) / 4)), dim3(256), 0, s, xp, wp, np_, rstd,
                        T_, (int)H, eps);
@@ -192,17 +191,74 @@ __host__ __device__ inline int64_t bwd_rows_per_block(int64_t T_) {
   return r < 8 ? 8 : r;
 }
 
+// The gradient of N as shard partials summed inside the backward ("Put the
+// other collective in backward": the shards' partials are summed before
+// RMSNorm's backward; here the sum is streamed into it instead of written out
+// and read back): dN = ((p[0] + p[1]) + p[2]) + ..., fp32, in index order --
+// the order of the partial-sum kernel, so both forms give the same bits.
+struct NormParts {
+  const float* p[kMaxNormParts];
+  int n;
+};
+
+// The dN units of one row: NP > 0 parts known at compile time (every part's
+// loads issued before the first addition), NP = 0 any count (one part's loads
+// at a time).
+template <int NP, int UPT, bool FULL>
+__device__ __forceinline__ void load_dn(const NormParts& parts, int64_t row, int H, int tid, int nunits,
+                                        floatx4 (&dn)[UPT]) {
+  if constexpr (NP > 0) {
+    floatx4 v[NP][UPT];
+#pragma unroll
+    for (int k = 0; k < NP; ++k)
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int q = tid + kBwdThreads * u;
+        const int64_t off = row * H + 4 * (FULL ? q : clampi(q, nunits));
+        v[k][u] = masked4(__builtin_nontemporal_load(reinterpret_cast<const floatx4*>(parts.p[k] + off)),
+                          FULL || q < nunits);
+      }
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      floatx4 acc = v[0][u];
+#pragma unroll
+      for (int k = 1; k < NP; ++k) acc += v[k][u];
+      dn[u] = acc;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int q = tid + kBwdThreads * u;
+      const int64_t off = row * H + 4 * (FULL ? q : clampi(q, nunits));
+      dn[u] = masked4(__builtin_nontemporal_load(reinterpret_cast<const floatx4*>(parts.p[0] + off)), FULL || q < nunits);
+    }
+    for (int k = 1; k < parts.n; ++k) {
+      floatx4 v[UPT];
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int q = tid + kBwdThreads * u;
+        const int64_t off = row * H + 4 * (FULL ? q : clampi(q, nunits));
+        v[u] = masked4(__builtin_nontemporal_load(reinterpret_cast<const floatx4*>(parts.p[k] + off)), FULL || q < nunits);
+      }
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) dn[u] += v[u];
+    }
+  }
+}
+
 // FULL: every thread's UPT units lie inside the row (no guards needed).
-template <typename T, int UPT, bool FULL>
+template <typename T, int UPT, bool FULL, int NP>
 __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_kernel(
-    const float* __restrict__ dN, const T* __restrict__ x, const T* __restrict__ dY,
+    const NormParts parts, const T* __restrict__ x, const T* __restrict__ dY,
     const float* __restrict__ rstd, const T* __restrict__ w, T* __restrict__ dx, float* __restrict__ ws_dw,
     float* __restrict__ ws_db, int64_t rows, int H, int64_t rows_per_block) {
   __shared__ float red[2][2][kBwdThreads / 64];  // [slot][row of the pair][wave]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nunits = H / 4;  // 4 columns per unit
-  const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
-  const int64_t r1 = min(rows, r0 + rows_per_block);
+  // Workgroup b takes rows b, b + G, b + 2G, ... (G workgroups): at any time
+  // the workgroups work on neighbouring rows, so the GPU sweeps each tensor
+  // front to back (a fixed assignment, so the column sums' order is fixed).
+  const int64_t G = gridDim.x;
   floatx4 wv[UPT], dwa[UPT], dba[UPT];
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
@@ -212,26 +268,27 @@ __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_kernel(
     dba[u] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   const float invH = 1.0f / (float)H;
-  // Rows go two at a time (one at a time for wide rows): both rows' loads
-  // are issued together, the two row sums share one barrier (which waits
-  // only for LDS), then both dx rows are written.
-  constexpr int NR = UPT <= 4 ? 2 : 1;
-  for (int64_t t = r0; t < r1; t += NR) {
+  // Rows go two at a time (one at a time for wide rows and for summed
+  // partials): both rows' loads are issued together, the two row sums share
+  // one barrier (which waits only for LDS), then both dx rows are written.
+  constexpr int NR = (UPT <= 4 && NP == 1) ? 2 : 1;
+  int64_t it = 0;
+  for (int64_t t = blockIdx.x; t < rows; t += NR * G, ++it) {
     floatx4 dn[NR][UPT], xv[NR][UPT], dy[NR][UPT];
     float r[NR], part[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-      const int64_t tk = t + k < r1 ? t + k : t;  // a missing second row repeats the first (not written)
+      const int64_t tk = t + k * G < rows ? t + k * G : t;  // a missing second row repeats the first (not written)
       r[k] = rstd[tk];
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
         const int q = tid + kBwdThreads * u;
         const bool ok = FULL || q < nunits;
         const int64_t off = tk * H + 4 * (FULL ? q : clampi(q, nunits));
-        dn[k][u] = masked4(__builtin_nontemporal_load(reinterpret_cast<const floatx4*>(dN + off)), ok);
         xv[k][u] = masked4(load4<T>(x + off), ok);
         dy[k][u] = masked4(load4<T>(dY + off), ok);
       }
+      load_dn<NP, UPT, FULL>(parts, tk, H, tid, nunits, dn[k]);
     }
     __builtin_amdgcn_sched_barrier(0);  // every load of the pair is issued before any use
 #pragma unroll
@@ -244,7 +301,7 @@ __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_kernel(
       }
       part[k] = wave_sum(pk);
     }
-    const int slot = (int)(((t - r0) / NR) & 1);
+    const int slot = (int)(it & 1);
     if (lane == 0) {
 #pragma unroll
       for (int k = 0; k < NR; ++k) red[slot][k][wave] = part[k];
@@ -252,7 +309,7 @@ __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_kernel(
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-      if (t + k >= r1) break;
+      if (t + k * G >= rows) break;
       float c = 0.f;
 #pragma unroll
       for (int i = 0; i < kBwdThreads / 64; ++i) c += red[slot][k][i];
@@ -263,10 +320,99 @@ __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_kernel(
         const int q = tid + kBwdThreads * u;
         if (!FULL && q >= nunits) continue;
         const floatx4 d = dy[k][u] + r[k] * dn[k][u] * wv[u] - xv[k][u] * r3c;
-        store4<T>(dx + (t + k) * H + 4 * q, d);
+        store4<T>(dx + (t + k * G) * H + 4 * q, d);
         dwa[u] += dn[k][u] * xv[k][u] * r[k];
         dba[u] += dy[k][u];
       }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int q = tid + kBwdThreads * u;
+    if (q >= nunits) continue;
+    store4<float>(ws_dw + (int64_t)blockIdx.x * H + 4 * q, dwa[u]);
+    store4<float>(ws_db + (int64_t)blockIdx.x * H + 4 * q, dba[u]);
+  }
+}
+
+// The backward with NP > 1 shard partials, software-pipelined over its rows:
+// the loads of row t + 1 (NP partials, x, dY) are issued before row t's sum,
+// barrier, dx stores and column accumulation, so the next row's reads are in
+// flight while the current one is finished.  Partials are summed (in index
+// order) as soon as they land, so a row in flight holds NP x UPT vectors and
+// a finished one UPT.
+template <typename T, int UPT, bool FULL, int NP>
+__global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_parts_kernel(
+    const NormParts parts, const T* __restrict__ x, const T* __restrict__ dY, const float* __restrict__ rstd,
+    const T* __restrict__ w, T* __restrict__ dx, float* __restrict__ ws_dw, float* __restrict__ ws_db, int64_t rows,
+    int H, int64_t rows_per_block) {
+  static_assert(NP > 1, "the single-partial backward is rmsnorm_bwd_kernel");
+  __shared__ float red[2][kBwdThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nunits = H / 4;
+  const int64_t G = gridDim.x;  // rows b, b + G, ... as in rmsnorm_bwd_kernel
+  floatx4 wv[UPT], dwa[UPT], dba[UPT];
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int q = tid + kBwdThreads * u;
+    wv[u] = FULL ? load4<T>(w + 4 * q) : masked4(load4<T>(w + 4 * clampi(q, nunits)), q < nunits);
+    dwa[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+    dba[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float invH = 1.0f / (float)H;
+  floatx4 pv[NP][UPT], xn[UPT], dyn[UPT];
+  auto issue = [&](int64_t t) {  // row t's loads (t < rows)
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int q = tid + kBwdThreads * u;
+      const bool ok = FULL || q < nunits;
+      const int64_t off = t * H + 4 * (FULL ? q : clampi(q, nunits));
+#pragma unroll
+      for (int k = 0; k < NP; ++k)
+        pv[k][u] = masked4(__builtin_nontemporal_load(reinterpret_cast<const floatx4*>(parts.p[k] + off)), ok);
+      xn[u] = masked4(load4<T>(x + off), ok);
+      dyn[u] = masked4(load4<T>(dY + off), ok);
+    }
+  };
+  if (blockIdx.x < rows) issue(blockIdx.x);  // (no rows: the partial column sums are zero)
+  int64_t it = 0;
+  for (int64_t t = blockIdx.x; t < rows; t += G, ++it) {
+    floatx4 dn[UPT], xv[UPT], dy[UPT];
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      floatx4 acc = pv[0][u];
+#pragma unroll
+      for (int k = 1; k < NP; ++k) acc += pv[k][u];
+      dn[u] = acc;
+      xv[u] = xn[u];
+      dy[u] = dyn[u];
+    }
+    const float r = rstd[t];
+    if (t + G < rows) issue(t + G);
+    __builtin_amdgcn_sched_barrier(0);  // the next row's loads are issued before this row's work
+    float pk = 0.f;
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const floatx4 p = dn[u] * wv[u] * xv[u];
+      pk += (p[0] + p[1]) + (p[2] + p[3]);
+    }
+    pk = wave_sum(pk);
+    const int slot = (int)(it & 1);
+    if (lane == 0) red[slot][wave] = pk;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    float c = 0.f;
+#pragma unroll
+    for (int i = 0; i < kBwdThreads / 64; ++i) c += red[slot][i];
+    c *= invH;
+    const float r3c = r * r * r * c;
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int q = tid + kBwdThreads * u;
+      if (!FULL && q >= nunits) continue;
+      const floatx4 d = dy[u] + r * dn[u] * wv[u] - xv[u] * r3c;
+      store4<T>(dx + t * H + 4 * q, d);
+      dwa[u] += dn[u] * xv[u] * r;
+      dba[u] += dy[u];
     }
   }
 #pragma unroll
@@ -339,9 +485,30 @@ size_t rmsnorm_bwd_workspace(int64_t T_, int64_t H) {
   return (size_t)(2 * nblk * H) * sizeof(float);
 }
 
+template <typename T, int UPT, bool FULL>
+static void launch_bwd_np(const NormParts& parts, dim3 grid, hipStream_t s, const T* xp, const T* dyp, const float* rstd,
+                          const T* wp, T* dxp, float* ws_dw, float* ws_db, int64_t T_, int H, int64_t rpb) {
+  // every part's loads in flight together for the usual shard counts while they fit in registers
+  if (parts.n == 1)
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, UPT, FULL, 1>), grid, dim3(kBwdThreads), 0, s, parts, xp, dyp, rstd, wp,
+                       dxp, ws_dw, ws_db, T_, H, rpb);
+  else if (parts.n == 2 && UPT <= 8)
+    hipLaunchKernelGGL((rmsnorm_bwd_parts_kernel<T, (UPT <= 8 ? UPT : 1), FULL, 2>), grid, dim3(kBwdThreads), 0, s,
+                       parts, xp, dyp, rstd, wp, dxp, ws_dw, ws_db, T_, H, rpb);
+  else if (parts.n == 4 && UPT <= 4)
+    hipLaunchKernelGGL((rmsnorm_bwd_parts_kernel<T, (UPT <= 4 ? UPT : 1), FULL, 4>), grid, dim3(kBwdThreads), 0, s,
+                       parts, xp, dyp, rstd, wp, dxp, ws_dw, ws_db, T_, H, rpb);
+  else if (parts.n == 8 && UPT <= 4)
+    hipLaunchKernelGGL((rmsnorm_bwd_parts_kernel<T, (UPT <= 4 ? UPT : 1), FULL, 8>), grid, dim3(kBwdThreads), 0, s,
+                       parts, xp, dyp, rstd, wp, dxp, ws_dw, ws_db, T_, H, rpb);
+  else
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, UPT, FULL, 0>), grid, dim3(kBwdThreads), 0, s, parts, xp, dyp, rstd, wp,
+                       dxp, ws_dw, ws_db, T_, H, rpb);
+}
+
 template <typename T>
-static hipError_t bwd_t(const float* dN, const void* x, const void* dY, const float* rstd, const void* w, void* dx,
-                        float* dw, float* db, void* ws, int64_t T_, int64_t H, bool accum, hipStream_t s) {
+static hipError_t bwd_t(const NormParts& parts, const void* x, const void* dY, const float* rstd, const void* w,
+                        void* dx, float* dw, float* db, void* ws, int64_t T_, int64_t H, bool accum, hipStream_t s) {
   const int64_t rpb = bwd_rows_per_block(T_);
   const int64_t nblk = (T_ + rpb - 1) / rpb;
   float* ws_dw = static_cast<float*>(ws);
@@ -356,11 +523,9 @@ static hipError_t bwd_t(const float* dN, const void* x, const void* dY, const fl
     KernelTimer timer("rmsnorm_bwd", s);
 #define TPMLP_BWD(U)                                                                                          \
   if (units == (int64_t)kBwdThreads * (U))                                                                      \
-    hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, U, true>), dim3((unsigned)nblk), dim3(kBwdThreads), 0, s, dN, xp, \
-                       dyp, rstd, wp, dxp, ws_dw, ws_db, T_, (int)H, rpb);                                     \
+    launch_bwd_np<T, U, true>(parts, dim3((unsigned)nblk), s, xp, dyp, rstd, wp, dxp, ws_dw, ws_db, T_, (int)H, rpb); \
   else                                                                                                          \
-    hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, U, false>), dim3((unsigned)nblk), dim3(kBwdThreads), 0, s, dN, xp, \
-                       dyp, rstd, wp, dxp, ws_dw, ws_db, T_, (int)H, rpb)
+    launch_bwd_np<T, U, false>(parts, dim3((unsigned)nblk), s, xp, dyp, rstd, wp, dxp, ws_dw, ws_db, T_, (int)H, rpb)
     if (upt <= 1) {
       TPMLP_BWD(1);
     } else if (upt <= 2) {
@@ -382,12 +547,16 @@ static hipError_t bwd_t(const float* dN, const void* x, const void* dY, const fl
   return launch_reduce_partial_rows(ws_db, db, nblk, H, accum, s);
 }
 
-hipError_t launch_rmsnorm_bwd(DType dt, const float* dN, const void* x, const void* dY, const float* rstd,
-                              const void* w, void* dx, float* dw, float* db, void* ws, int64_t T_, int64_t H,
-                              bool accum, hipStream_t s) {
+hipError_t launch_rmsnorm_bwd(DType dt, const float* const* dN_parts, int n_parts, const void* x, const void* dY,
+                              const float* rstd, const void* w, void* dx, float* dw, float* db, void* ws, int64_t T_,
+                              int64_t H, bool accum, hipStream_t s) {
+  if (n_parts < 1 || n_parts > kMaxNormParts) return hipErrorInvalidValue;
+  NormParts parts{};
+  for (int k = 0; k < n_parts; ++k) parts.p[k] = dN_parts[k];
+  parts.n = n_parts;
   // T = 0 still writes the (empty, zero) column sums (or leaves accumulated ones as they are).
-  if (dt == kBF16) return bwd_t<bf16_t>(dN, x, dY, rstd, w, dx, dw, db, ws, T_, H, accum, s);
-  return bwd_t<float>(dN, x, dY, rstd, w, dx, dw, db, ws, T_, H, accum, s);
+  if (dt == kBF16) return bwd_t<bf16_t>(parts, x, dY, rstd, w, dx, dw, db, ws, T_, H, accum, s);
+  return bwd_t<float>(parts, x, dY, rstd, w, dx, dw, db, ws, T_, H, accum, s);
 }
 
 }  // namespace tpmlp

@@ -9,8 +9,8 @@ all-reduces of the method become tp_partial_sum at the same two points
   forward   shard s: tp_mlp_forward -> fp32 partial z_s
             out = tp_partial_sum(z_0..z_{S-1}) + x + b_down          (forward boundary)
   backward  shard s: tp_mlp_backward(SHARD, d_out = out) -> dN_s and the shard's weight grads
-            dN  = tp_partial_sum(dN_0..dN_{S-1})                      (backward boundary)
-            tp_mlp_backward(NORM) -> dx, d_norm_w, d_b_down
+            tp_mlp_backward(NORM, d_normed_parts = dN_0..dN_{S-1})   (backward boundary: the sum
+            of the partials formed inside the RMSNorm backward) -> dx, d_norm_w, d_b_down
   update    tp_mlp_sgd_step_multi over every parameter tensor (one launch), or
             tp_mlp_clip_grad_norm + tp_mlp_adamw_step_multi
 
@@ -147,6 +147,8 @@ class ShardedStep:
         self.adam_steps = 0
         # per-shard outputs of the ablation modes, allocated on first use
         self._abl: Dict[str, list] = {}
+        # the last backward summed dN inside the RMSNorm backward (dN's buffer not written)
+        self._dN_streamed = False
 
     # ------------------------------------------------------------ helpers
     def _desc(self, flags: int = 0, tokens: Optional[int] = None) -> L.tp_mlp_desc:
@@ -209,11 +211,24 @@ class ShardedStep:
                           d_out=d_out, d_pre=sh["d_pre"][r], d_w_in=sh["d_w_in"], d_b_in=sh["d_b_in"],
                           d_w_down=sh["d_w_down"], d_normed_part=sh["dN_part"][r], workspace=self.workspace)
 
-    def _norm_backward(self, dN, d_out, dx, d_norm_w, d_b_down, r: slice = slice(None), flags: int = 0) -> None:
+    def _norm_backward(self, dN, d_out, dx, d_norm_w, d_b_down, r: slice = slice(None), flags: int = 0,
+                       parts=None) -> None:
+        """The NORM phase on the summed dN, or with ``parts`` (the shards'
+        partials of dN) summed by the RMSNorm backward as it reads them."""
         T = self.T if r.start is None else r.stop - r.start
+        kw = dict(d_normed_parts=parts) if parts else dict(d_normed=dN)
         L.tp_mlp_backward(self._desc(flags, T), L.BWD_NORM, stream=self.stream, x=self.x[r], rstd=self.rstd[r],
-                          norm_w=self.norm_w, d_out=d_out, d_normed=dN, d_x=dx, d_norm_w=d_norm_w,
-                          d_b_down=d_b_down, workspace=self.workspace)
+                          norm_w=self.norm_w, d_out=d_out, d_x=dx, d_norm_w=d_norm_w, d_b_down=d_b_down,
+                          workspace=self.workspace, **kw)
+
+    def materialize_dN(self) -> None:
+        """Write the summed dN into its buffer when the step streamed the
+        shards' partials into the RMSNorm backward instead (tp_partial_sum:
+        the same sum, in the same order, so the same bits the backward used)."""
+        if self._dN_streamed and not self.fuse:
+            L.tp_partial_sum([sh["dN_part"] for sh in self.shards], self.T, self.H, None, None, L.F32, self.dN, L.F32,
+                             stream=self.stream)
+        self._dN_streamed = False
 
     def backward_rows(self, rows: slice, accumulate: bool) -> None:
         """Backward of one microbatch (token rows ``rows``, equivalence mode);
@@ -222,11 +237,10 @@ class ShardedStep:
         flags = L.ACCUMULATE_GRADS if accumulate else 0
         for sh in self.shards:
             self._shard_backward(sh, self.out[r], r, flags)
-        dN = self.dN[r]
-        if not self.fuse:
-            L.tp_partial_sum([sh["dN_part"][r] for sh in self.shards], T, H, None, None, L.F32, dN, L.F32,
-                             stream=self.stream)
-        self._norm_backward(dN, self.out[r], self.dx[r], self.d_norm_w, self.d_b_down, r, flags)
+        # the backward boundary: the shards' partials summed inside the RMSNorm backward
+        parts = None if self.fuse else [sh["dN_part"][r] for sh in self.shards]
+        self._norm_backward(self.dN[r], self.out[r], self.dx[r], self.d_norm_w, self.d_b_down, r, flags, parts=parts)
+        self._dN_streamed = not self.fuse
 
     def backward(self, mode: str = "equivalence") -> None:
         T, H = self.T, self.H
@@ -234,12 +248,15 @@ class ShardedStep:
         outs = self._abl["out"] if fwd_abl else [self.out] * len(self.shards)
         for sh, o in zip(self.shards, outs):
             self._shard_backward(sh, o)
-        if not self.fuse and mode != "missing_backward_reduce":
+        if mode == "equivalence" or self.fuse:
+            # the backward boundary: the shards' partials summed inside the RMSNorm backward
+            parts = None if self.fuse else [sh["dN_part"] for sh in self.shards]
+            self._norm_backward(self.dN, self.out, self.dx, self.d_norm_w, self.d_b_down, parts=parts)
+            self._dN_streamed = not self.fuse
+            return
+        if mode != "missing_backward_reduce":
             L.tp_partial_sum([sh["dN_part"] for sh in self.shards], T, H, None, None, L.F32, self.dN, L.F32,
                              stream=self.stream)
-        if mode == "equivalence" or self.fuse:
-            self._norm_backward(self.dN, self.out, self.dx, self.d_norm_w, self.d_b_down)
-            return
         dxs = self._abl_bufs("dx", (T, H), self.dt)
         dws = self._abl_bufs("d_norm_w", (H,), torch.float32)
         dbs = self._abl_bufs("d_b_down", (H,), torch.float32)
@@ -308,6 +325,7 @@ class ShardedStep:
         """CPU copies of the step's outputs, shard slices re-assembled along
         the FFN axis.  In ablation modes out/dx/d_norm_w/d_b_down are lists
         over shards."""
+        self.materialize_dN()
         c = lambda t: t.detach().float().cpu()
         r = {"normed": c(self.normed), "rstd": c(self.rstd)}
         cat_in = (lambda ts: torch.cat(ts, dim=1)) if self.swiglu else (lambda ts: torch.cat(ts, dim=0))
@@ -356,9 +374,10 @@ class SequenceParallelStep(ShardedStep):
                 + x + b_down -> its rows of out    (the reduce-scatter)
       backward  shard s: tp_mlp_backward(SHARD) with d_out = out on all rows
                 (the all-gather of dY) -> dN_s
-                rank r: tp_partial_sum of its rows of dN_0..dN_{S-1}
-                (the reduce-scatter), then tp_mlp_backward(NORM) on its rows
-                -> its rows of dx and its own d_norm_w, d_b_down
+                rank r: tp_mlp_backward(NORM) on its rows with its rows of
+                dN_0..dN_{S-1} as d_normed_parts (the reduce-scatter, summed
+                inside the RMSNorm backward) -> its rows of dx and its own
+                d_norm_w, d_b_down
                 d_norm_w, d_b_down = tp_partial_sum over the ranks (the
                 replicated parameters' gradients summed over the group)
 
@@ -400,12 +419,11 @@ class SequenceParallelStep(ShardedStep):
         for sh in self.shards:
             self._shard_backward(sh, self.out)
         for r, (lo, hi) in enumerate(self.slices):
-            dN = self.dN[lo:hi]
-            if not self.fuse:
-                L.tp_partial_sum([sh["dN_part"][lo:hi] for sh in self.shards], hi - lo, H, None, None, L.F32, dN, L.F32,
-                                 stream=self.stream)
-            self._norm_backward(dN, self.out[lo:hi], self.dx[lo:hi], self.rank_d_norm_w[r], self.rank_d_b_down[r],
-                                slice(lo, hi))
+            # the reduce-scatter of dN: each rank's rows of the partials, summed inside its RMSNorm backward
+            parts = None if self.fuse else [sh["dN_part"][lo:hi] for sh in self.shards]
+            self._norm_backward(self.dN[lo:hi], self.out[lo:hi], self.dx[lo:hi], self.rank_d_norm_w[r],
+                                self.rank_d_b_down[r], slice(lo, hi), parts=parts)
+        self._dN_streamed = not self.fuse
         if mode == "equivalence":
             S = len(self.slices)
             L.tp_partial_sum([self.rank_d_norm_w[r] for r in range(S)], 1, H, None, None, L.F32, self.d_norm_w, L.F32,
@@ -492,10 +510,10 @@ class Fp8Step(ShardedStep):
                                   w_down=sh["w_down"], d_out=self.out, d_pre=sh["d_pre"], d_w_in=sh["d_w_in"],
                                   d_b_in=sh["d_b_in"], d_w_down=sh["d_w_down"], d_normed_part=sh["dN_part"],
                                   workspace=self.workspace)
-        if not self.fuse:
-            L.tp_partial_sum([sh["dN_part"] for sh in self.shards], T, H, None, None, L.F32, self.dN, L.F32,
-                             stream=self.stream)
-        self._norm_backward(self.dN, self.out, self.dx, self.d_norm_w, self.d_b_down)
+        # the backward boundary: the shards' partials summed inside the RMSNorm backward
+        parts = None if self.fuse else [sh["dN_part"] for sh in self.shards]
+        self._norm_backward(self.dN, self.out, self.dx, self.d_norm_w, self.d_b_down, parts=parts)
+        self._dN_streamed = not self.fuse
 
     def update_scales(self) -> None:
         L.tp_mlp_fp8_update_scales([self.metas[n] for n, _ in self.ROLES], self.history_len, stream=self.stream)

@@ -46,6 +46,7 @@ ROWS = 4096  # token rows per block
 
 def collect(st) -> dict:
     """Host copies of every tensor a ShardedStep stored (bf16 stays bf16)."""
+    st.materialize_dN()
     c = lambda t: None if t is None else t.detach().cpu()
     h = {"normed": c(st.normed), "rstd": c(st.rstd), "out": c(st.out), "dN": c(st.dN), "dx": c(st.dx),
          "d_norm_w": c(st.d_norm_w), "d_b_down": c(st.d_b_down), "shards": [],

@@ -120,7 +120,7 @@ def test_backward_checks(lib):
     assert L.tp_mlp_workspace_bytes(_desc(T=0), L.BWD_SHARD) == 0
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name != "workspace_bytes":
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts"):
             setattr(a, name, A)
     a.workspace_bytes = need - 16
     assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EWORKSPACE
@@ -271,7 +271,7 @@ def test_fp8_checks(lib):
                                   None) == L.OK
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name != "workspace_bytes":
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts"):
             setattr(a, name, A)
     a.d_b_in = None
     a.workspace_bytes = 1 << 30
@@ -357,7 +357,7 @@ def test_attention_checks(lib):
     assert need >= 4 * 2 * 64 * 4                              # delta [n_q, T] at least
     a = L.tp_attn_bwd_args()
     for name, _ in L.tp_attn_bwd_args._fields_:
-        if name != "workspace_bytes":
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts"):
             setattr(a, name, A)
     a.workspace_bytes = need - 16
     assert lib.tp_attn_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EWORKSPACE
@@ -381,3 +381,28 @@ def test_attention_checks(lib):
     assert bb(1, 8, 2, 1, 64, A, 256, A, A, A, A, need_b - 4, A, None) == L.EWORKSPACE  # too small
     assert bb(1, 8, 2, 1, 64, A, 256, A, A, A, MIS, need_b, A, None) == L.EALIGN
     assert bb(0, 8, 2, 1, 64, None, 256, None, None, None, None, 0, None, None) == L.OK  # empty
+
+
+def test_backward_norm_parts_checks(lib):
+    """The NORM phase's streamed partials: count in [0, 64], a non-NULL
+    array when the count is positive, every part non-NULL and aligned; all
+    checked before any launch."""
+    d = _desc(T=128)
+    a = L.tp_mlp_bwd_args()
+    for name, _ in L.tp_mlp_bwd_args._fields_:
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts"):
+            setattr(a, name, A)
+    a.workspace_bytes = L.tp_mlp_workspace_bytes(d, L.BWD_NORM)
+    a.n_d_normed_parts = 65
+    assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EINVAL
+    a.n_d_normed_parts = -1
+    assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EINVAL
+    a.n_d_normed_parts = 2
+    assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EINVAL  # NULL array
+    arr = (ctypes.c_void_p * 2)(A, None)
+    a.d_normed_parts = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EINVAL
+    assert b"part" in lib.tp_mlp_last_error()
+    arr2 = (ctypes.c_void_p * 2)(A, MIS)
+    a.d_normed_parts = ctypes.cast(arr2, ctypes.POINTER(ctypes.c_void_p))
+    assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EALIGN

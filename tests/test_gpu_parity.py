@@ -217,6 +217,7 @@ def _sample(rng, n, k, must=()):
 
 def _gather(st, rows, chans, cols):
     """Sampled entries of the GPU step, indexed on the device."""
+    st.materialize_dN()
     F = st.F
     dev = st.dev
     ri = torch.as_tensor(rows, device=dev)
@@ -374,3 +375,45 @@ def test_ksplit_gemms_stagewise(case):
     for stage in STAGES:
         run_stage(stage, w, t, h, report)
     say(f"  worst stage-wise: {max(report.items(), key=lambda kv: kv[1])}")
+
+
+NORM_PARTS = [(1, 264), (2, 4096), (3, 136), (4, 4096), (5, 1032), (8, 4096), (8, 8192), (16, 520)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("n_parts,H", NORM_PARTS, ids=[f"{n}x{h}" for n, h in NORM_PARTS])
+def test_norm_backward_streamed_parts_bitwise(dt, n_parts, H):
+    """The NORM phase given the shards' partials of dN (summed inside the
+    RMSNorm backward) against tp_partial_sum followed by the NORM phase on
+    the summed dN: the same bits in dx, d_norm_w and d_b_down."""
+    from tensor_transformer_mlp_rmsnorm_amd import _lib as L
+    T = 150
+    tdt, cdt = (torch.bfloat16, L.BF16) if dt == "bf16" else (torch.float32, L.F32)
+    g = torch.Generator().manual_seed(n_parts * 1000 + H)
+    say(f"[gpu] NORM phase with {n_parts} streamed parts, H={H}, {dt}")
+    dev = "cuda:0"
+    x = torch.randn(T, H, generator=g).to(tdt).to(dev)
+    dy = torch.randn(T, H, generator=g).to(tdt).to(dev)
+    w = (1 + 0.1 * torch.randn(H, generator=g)).to(tdt).to(dev)
+    rstd = (0.5 + torch.rand(T, generator=g)).to(dev)
+    parts = [torch.randn(T, H, generator=g).to(dev) for _ in range(n_parts)]
+    desc = L.make_desc(T, H, 8, L.ACT_SWIGLU, cdt, 1e-6, 0)
+    ws = torch.empty(max(L.tp_mlp_workspace_bytes(desc, L.BWD_NORM), 16), dtype=torch.uint8, device=dev)
+    outs = []
+    for streamed in (False, True):
+        dx = torch.full_like(x, float("nan"))
+        dw = torch.full((H,), float("nan"), device=dev)
+        db = torch.full((H,), float("nan"), device=dev)
+        if streamed:
+            kw = dict(d_normed_parts=parts)
+        else:
+            dn = torch.empty(T, H, device=dev)
+            L.tp_partial_sum(parts, T, H, None, None, L.F32, dn, L.F32)
+            kw = dict(d_normed=dn)
+        L.tp_mlp_backward(desc, L.BWD_NORM, x=x, rstd=rstd, norm_w=w, d_out=dy, d_x=dx, d_norm_w=dw, d_b_down=db,
+                          workspace=ws, **kw)
+        outs.append((dx, dw, db))
+    torch.cuda.synchronize()
+    for a, b, name in zip(outs[0], outs[1], ("dx", "d_norm_w", "d_b_down")):
+        assert not torch.isnan(b).any(), name
+        assert torch.equal(a, b), name
