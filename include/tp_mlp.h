@@ -192,6 +192,11 @@ typedef struct {
      n_d_normed_parts = 0 (as in zero-initialised args): d_normed is read. */
   const float* const* d_normed_parts;
   int32_t n_d_normed_parts;
+  /* SHARD phase, optional (bf16): w_down transposed, [F, H], as
+     tp_mlp_transpose_bf16 or the SGD's transposed copy write it.  Given, the
+     d_act GEMM reads it; NULL, the phase transposes w_down into the
+     workspace first.  It must hold the transpose of this w_down. */
+  const void* w_down_t;
 } tp_mlp_bwd_args;
 
 /*
@@ -258,7 +263,13 @@ int tp_mlp_backward_noalloc(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bw
 int tp_mlp_sgd_step(const void* param_in, void* param_out, const float* grad, const float* master_in,
                     float* master_out, int64_t n, int32_t param_dtype, float lr, void* stream);
 
-/* One tensor of tp_mlp_sgd_step_multi (fields as in tp_mlp_sgd_step). */
+/* One tensor of tp_mlp_sgd_step_multi (fields as in tp_mlp_sgd_step).
+ * Optionally (bf16 parameters only) the updated values are also written
+ * transposed: param_out_t != NULL receives the parameter seen as [t_rows,
+ * t_cols] row-major (t_rows * t_cols == n, both multiples of 8) transposed,
+ * [t_cols, t_rows], in the same bits as param_out.  This keeps the
+ * transposed down weight that tp_mlp_backward can take (w_down_t) in step
+ * with w_down [H, F]: t_rows = H, t_cols = F.  Zero-initialised: no copy. */
 typedef struct {
   const void* param_in;
   void* param_out;
@@ -266,11 +277,22 @@ typedef struct {
   const float* master_in;
   float* master_out;
   int64_t n;
+  void* param_out_t;
+  int64_t t_rows;
+  int64_t t_cols;
 } tp_mlp_sgd_tensor;
 
 /*
+ * tp_mlp_transpose_bf16 - out [cols, rows] = in [rows, cols] transposed, bf16,
+ * row-major (a layout helper: the transposed down weight w_down_t of
+ * tp_mlp_backward).  rows, cols >= 0 and multiples of 8; in and out DEVICE
+ * pointers, 16-byte aligned, not overlapping.
+ */
+int tp_mlp_transpose_bf16(const void* in, void* out, int64_t rows, int64_t cols, void* stream);
+
+/*
  * tp_mlp_sgd_step_multi - tp_mlp_sgd_step on `count` tensors with one kernel
- * launch.  `list` is a HOST array (read before the call returns).  All
+ * launch (and one more for the tensors with a transposed copy).  `list` is a HOST array (read before the call returns).  All
  * tensors share param_dtype; either every tensor has fp32 masters or none
  * does.  Each tensor's rules are those of tp_mlp_sgd_step.  count >= 0.
  */

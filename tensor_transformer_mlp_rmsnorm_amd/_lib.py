@@ -38,7 +38,7 @@ EXPORTED = ("tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_works
             "tp_mlp_backward_fp8", "tp_mlp_fp8_gemm", "tp_mlp_fp8_gemm_workspace_bytes", "tp_attn_forward",
             "tp_attn_backward", "tp_attn_workspace_bytes", "tp_attention_forward", "tp_attention_backward",
             "tp_attention_backward_workspace_bytes", "tp_mlp_profile_only", "tp_attn_forward_workspace_bytes",
-            "tp_mlp_backward_noalloc")
+            "tp_mlp_backward_noalloc", "tp_mlp_transpose_bf16")
 
 
 class TPMLPError(RuntimeError):
@@ -58,7 +58,8 @@ _vp = ctypes.c_void_p
 
 class tp_mlp_sgd_tensor(ctypes.Structure):
     _fields_ = [("param_in", ctypes.c_void_p), ("param_out", ctypes.c_void_p), ("grad", ctypes.c_void_p),
-                ("master_in", ctypes.c_void_p), ("master_out", ctypes.c_void_p), ("n", ctypes.c_int64)]
+                ("master_in", ctypes.c_void_p), ("master_out", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("param_out_t", ctypes.c_void_p), ("t_rows", ctypes.c_int64), ("t_cols", ctypes.c_int64)]
 
 
 class tp_mlp_adamw_hparams(ctypes.Structure):
@@ -76,7 +77,7 @@ class tp_mlp_bwd_args(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("x", "normed", "rstd", "pre_act", "act", "norm_w", "w_in", "w_down", "d_out",
                                    "d_pre", "d_w_in", "d_b_in", "d_w_down", "d_normed_part", "d_normed", "d_x",
                                    "d_norm_w", "d_b_down", "workspace")] + [("workspace_bytes", ctypes.c_size_t)] + \
-        [("d_normed_parts", ctypes.POINTER(_vp)), ("n_d_normed_parts", ctypes.c_int32)]
+        [("d_normed_parts", ctypes.POINTER(_vp)), ("n_d_normed_parts", ctypes.c_int32), ("w_down_t", _vp)]
 
 
 FP8_META_FIELDS = ("meta_normed", "meta_w_in", "meta_act", "meta_w_down", "meta_d_out", "meta_d_pre")
@@ -124,6 +125,8 @@ def lib() -> ctypes.CDLL:
         L.tp_mlp_backward_noalloc.restype = ctypes.c_int
         L.tp_mlp_workspace_bytes.argtypes = [ctypes.POINTER(tp_mlp_desc), ctypes.c_int32]
         L.tp_mlp_workspace_bytes.restype = ctypes.c_size_t
+        L.tp_mlp_transpose_bf16.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp]
+        L.tp_mlp_transpose_bf16.restype = ctypes.c_int
         L.tp_mlp_sgd_step.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, _vp]
         L.tp_mlp_sgd_step.restype = ctypes.c_int
         L.tp_mlp_sgd_step_multi.argtypes = [ctypes.POINTER(tp_mlp_sgd_tensor), ctypes.c_int32, ctypes.c_int32,
@@ -395,10 +398,18 @@ def tp_mlp_sgd_step(param_in, param_out, grad, master_in, master_out, n: int, pa
 
 
 def tp_mlp_sgd_step_multi(tensors: Sequence, param_dtype: int, lr: float, stream=None) -> None:
-    """``tensors``: sequence of (param_in, param_out, grad, master_in, master_out, n)."""
-    arr = (tp_mlp_sgd_tensor * max(1, len(tensors)))(
-        *[tp_mlp_sgd_tensor(_ptr(a), _ptr(b), _ptr(c), _ptr(d), _ptr(e), n) for a, b, c, d, e, n in tensors])
+    """``tensors``: sequence of (param_in, param_out, grad, master_in, master_out, n), or of
+    (..., n, param_out_t, t_rows, t_cols) for a tensor that also gets its transposed copy."""
+    def one(t):
+        a, b, c, d, e, n = t[:6]
+        pt, rows, cols = t[6:] if len(t) > 6 else (None, 0, 0)
+        return tp_mlp_sgd_tensor(_ptr(a), _ptr(b), _ptr(c), _ptr(d), _ptr(e), n, _ptr(pt), rows, cols)
+    arr = (tp_mlp_sgd_tensor * max(1, len(tensors)))(*[one(t) for t in tensors])
     _check(lib().tp_mlp_sgd_step_multi(arr, len(tensors), param_dtype, lr, _stream(stream)))
+
+
+def tp_mlp_transpose_bf16(x, out, rows: int, cols: int, stream=None) -> None:
+    _check(lib().tp_mlp_transpose_bf16(_ptr(x), _ptr(out), rows, cols, _stream(stream)))
 
 
 def make_adamw_hparams(lr: float, step: int, weight_decay: float = 0.0, beta1: float = 0.9, beta2: float = 0.999,

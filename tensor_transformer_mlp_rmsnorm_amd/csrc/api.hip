@@ -263,6 +263,10 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
   // SHARD phase
   REQUIRE_PTR(a->w_in);
   REQUIRE_PTR(a->w_down);
+  if (a->w_down_t) {
+    if (!aligned16(a->w_down_t)) return fail(TP_MLP_EALIGN, "%s: 'w_down_t' is not 16-byte aligned", fn);
+    if (dt != kBF16) return fail(TP_MLP_EDTYPE, "%s: w_down_t is taken for bf16 only", fn);
+  }
   REQUIRE_PTR(a->d_w_in);
   REQUIRE_PTR(a->d_w_down);
   if (!swiglu) REQUIRE_PTR(a->d_b_in);
@@ -294,8 +298,12 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
   b1.tag = swiglu ? "gemm_dact_swiglu_bwd" : "gemm_dact_gelu_bwd";
   const Epi act_bwd = swiglu ? kEpiSwigluBwd : kEpiGeluBwd;
   if (dt == kBF16 && T > 0) {
-    CHECK_HIP(launch_transpose_bf16(a->w_down, a->workspace, H, F, s), "Wd transpose");
-    b1.B = a->workspace;
+    if (a->w_down_t) {
+      b1.B = a->w_down_t;  // the caller's transposed copy
+    } else {
+      CHECK_HIP(launch_transpose_bf16(a->w_down, a->workspace, H, F, s), "Wd transpose");
+      b1.B = a->workspace;
+    }
     b1.ldb = H;
     CHECK_HIP(launch_gemm(dt, true, true, act_bwd, b1, s), "d_act GEMM");
   } else {
@@ -437,6 +445,13 @@ int check_sgd_tensor(const tp_mlp_sgd_tensor& t, int32_t param_dtype, bool maste
     REQUIRE_PTR(master_in);
     REQUIRE_PTR(master_out);
   }
+  if (t.param_out_t) {
+    void* param_out_t = t.param_out_t;
+    REQUIRE_PTR(param_out_t);
+    if (param_dtype != TP_MLP_BF16) return fail(TP_MLP_EDTYPE, "%s: a transposed copy is written for bf16 only", fn);
+    if (t.t_rows <= 0 || t.t_cols <= 0 || t.t_rows % 8 || t.t_cols % 8 || t.t_rows * t.t_cols != t.n)
+      return fail(TP_MLP_ESHAPE, "%s: t_rows x t_cols must equal n, both positive multiples of 8", fn);
+  }
   return TP_MLP_OK;
 }
 
@@ -460,10 +475,23 @@ int sgd_list(const tp_mlp_sgd_tensor* list, int32_t count, int32_t param_dtype, 
 
 }  // namespace
 
+int tp_mlp_transpose_bf16(const void* in, void* out, int64_t rows, int64_t cols, void* stream) {
+  const char* fn = "tp_mlp_transpose_bf16";
+  g_err[0] = 0;
+  if (rows < 0 || cols < 0 || rows % 8 || cols % 8)
+    return fail(TP_MLP_ESHAPE, "%s: rows and cols must be non-negative multiples of 8", fn);
+  if (rows == 0 || cols == 0) return TP_MLP_OK;
+  REQUIRE_PTR(in);
+  REQUIRE_PTR(out);
+  if (rows * cols >= ((int64_t)1 << 31)) return fail(TP_MLP_ESHAPE, "%s: 2^31 or more elements", fn);
+  CHECK_HIP(launch_transpose_bf16(in, out, rows, cols, static_cast<hipStream_t>(stream)), "transpose");
+  return TP_MLP_OK;
+}
+
 int tp_mlp_sgd_step(const void* param_in, void* param_out, const float* grad, const float* master_in,
                     float* master_out, int64_t n, int32_t param_dtype, float lr, void* stream) {
   g_err[0] = 0;
-  const tp_mlp_sgd_tensor t{param_in, param_out, grad, master_in, master_out, n};
+  const tp_mlp_sgd_tensor t{param_in, param_out, grad, master_in, master_out, n, nullptr, 0, 0};
   return sgd_list(&t, 1, param_dtype, lr, stream, "tp_mlp_sgd_step");
 }
 

@@ -106,6 +106,32 @@ __global__ __launch_bounds__(kColThreads) void colsum_partial_kernel(const T* __
 // Out of place when pout != pin (the input is then left unchanged).
 constexpr int kSgdPerThread = 8, kSgdBlock = 256, kSgdPerBlock = kSgdPerThread * kSgdBlock;
 
+// The update of 8 consecutive elements from e (16-byte accesses throughout:
+// every pointer is 16-byte aligned; the gradient is read once, with the
+// non-temporal hint): v = p - lr g, or with masters m' = m - lr g (written)
+// and v = m'.  Shared by the flat and the transposing kernels, so both give
+// the same bits.
+template <typename T, bool MASTER>
+__device__ __forceinline__ void sgd8(const T* pin, const float* g, const float* min, float* mout, int64_t e, float lr,
+                                     floatx4& v0, floatx4& v1) {
+  const floatx4 g0 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(g + e));
+  const floatx4 g1 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(g + e + 4));
+  if constexpr (MASTER) {
+    v0 = load4<float>(min + e) - lr * g0;
+    v1 = load4<float>(min + e + 4) - lr * g1;
+    store4<float>(mout + e, v0);
+    store4<float>(mout + e + 4, v1);
+  } else if constexpr (sizeof(T) == 2) {
+    float f[8];
+    Chunk<bf16_t>::unpack(*reinterpret_cast<const uint4*>(pin + e), f);
+    v0 = floatx4{f[0], f[1], f[2], f[3]} - lr * g0;
+    v1 = floatx4{f[4], f[5], f[6], f[7]} - lr * g1;
+  } else {
+    v0 = load4<T>(pin + e) - lr * g0;
+    v1 = load4<T>(pin + e + 4) - lr * g1;
+  }
+}
+
 template <typename T, bool MASTER>
 __global__ __launch_bounds__(kSgdBlock) void sgd_kernel(SgdList L, float lr) {
   int t = 0;
@@ -115,25 +141,8 @@ __global__ __launch_bounds__(kSgdBlock) void sgd_kernel(SgdList L, float lr) {
   T* pout = static_cast<T*>(sg.pout);
   const int64_t e0 = ((int64_t)blockIdx.x - sg.block0) * kSgdPerBlock + (int64_t)threadIdx.x * kSgdPerThread;
   if (e0 + kSgdPerThread <= sg.n) {
-    // 16-byte accesses throughout (every pointer is 16-byte aligned); the
-    // gradient is read once, with the non-temporal hint
-    const floatx4 g0 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(sg.g + e0));
-    const floatx4 g1 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(sg.g + e0 + 4));
     floatx4 v0, v1;
-    if constexpr (MASTER) {
-      v0 = load4<float>(sg.min + e0) - lr * g0;
-      v1 = load4<float>(sg.min + e0 + 4) - lr * g1;
-      store4<float>(sg.mout + e0, v0);
-      store4<float>(sg.mout + e0 + 4, v1);
-    } else if constexpr (sizeof(T) == 2) {
-      float f[8];
-      Chunk<bf16_t>::unpack(*reinterpret_cast<const uint4*>(pin + e0), f);
-      v0 = floatx4{f[0], f[1], f[2], f[3]} - lr * g0;
-      v1 = floatx4{f[4], f[5], f[6], f[7]} - lr * g1;
-    } else {
-      v0 = load4<T>(pin + e0) - lr * g0;
-      v1 = load4<T>(pin + e0 + 4) - lr * g1;
-    }
+    sgd8<T, MASTER>(pin, sg.g, sg.min, sg.mout, e0, lr, v0, v1);
     if constexpr (sizeof(T) == 2) {
       const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       *reinterpret_cast<uint4*>(pout + e0) = Chunk<bf16_t>::pack(f);
@@ -151,6 +160,67 @@ __global__ __launch_bounds__(kSgdBlock) void sgd_kernel(SgdList L, float lr) {
         v = Elem<T>::to_f32(pin[e]) - lr * sg.g[e];
       }
       pout[e] = Elem<T>::from_f32(v);
+    }
+  }
+}
+
+// SGD of bf16 tensors that also receive their updated values transposed:
+// the parameter seen as [rows, cols] (row-major) is updated in 64 x 64 tiles;
+// each tile's new values are written row-major to pout and, through an LDS
+// tile, as [cols, rows] to pout_t (the layout another contraction reads with
+// its k contiguous).  The update itself is sgd8, as in sgd_kernel.
+constexpr int kSgdTMaxTensors = 16, kSgdTTile = 64;
+struct SgdTSeg {
+  const void* pin;
+  void* pout;
+  void* pout_t;
+  const float* g;
+  const float* min;
+  float* mout;
+  int64_t rows, cols, tiles_c;
+  int64_t block0;
+};
+struct SgdTList {
+  SgdTSeg seg[kSgdTMaxTensors];
+  int count;
+};
+
+template <bool MASTER>
+__global__ __launch_bounds__(256) void sgd_t_kernel(SgdTList L, float lr) {
+  __shared__ bf16_t tile[kSgdTTile][kSgdTTile + 2];
+  int t = 0;
+  while (t + 1 < L.count && (int64_t)blockIdx.x >= L.seg[t + 1].block0) ++t;
+  const SgdTSeg& sg = L.seg[t];
+  const int64_t b = (int64_t)blockIdx.x - sg.block0;
+  const int64_t r0 = (b / sg.tiles_c) * kSgdTTile, c0 = (b % sg.tiles_c) * kSgdTTile;
+  const bf16_t* pin = static_cast<const bf16_t*>(sg.pin);
+  bf16_t* pout = static_cast<bf16_t*>(sg.pout);
+  // 64 rows x 8 chunks of 8 columns, two chunks per thread (rows and cols are multiples of 8)
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int ch = threadIdx.x + 256 * pass, row = ch >> 3, col8 = (ch & 7) * 8;
+    const int64_t gr = r0 + row, gc = c0 + col8;
+    if (gr < sg.rows && gc < sg.cols) {
+      const int64_t e = gr * sg.cols + gc;
+      floatx4 v0, v1;
+      sgd8<bf16_t, MASTER>(pin, sg.g, sg.min, sg.mout, e, lr, v0, v1);
+      const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      *reinterpret_cast<uint4*>(pout + e) = Chunk<bf16_t>::pack(f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tile[row][col8 + i] = f32_to_bf16(f[i]);
+    }
+  }
+  __syncthreads();
+  bf16_t* pt = static_cast<bf16_t*>(sg.pout_t);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int ch = threadIdx.x + 256 * pass, col = ch >> 3, row8 = (ch & 7) * 8;
+    const int64_t gc = c0 + col, gr = r0 + row8;
+    if (gc < sg.cols && gr < sg.rows) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = (uint32_t)tile[row8 + 2 * i][col] | ((uint32_t)tile[row8 + 2 * i + 1][col] << 16);
+      *reinterpret_cast<uint4*>(pt + gc * sg.rows + gr) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
@@ -273,13 +343,14 @@ hipError_t launch_colsum(DType dt, const void* in, float* out, void* ws, int64_t
 hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, float lr, hipStream_t s) {
   KernelTimer timer("sgd", s);
   // each launch takes the next kSgdMaxTensors entries of the list (empty
-  // tensors among them are skipped), so every tensor is updated exactly once
+  // tensors and those with a transposed copy among them are skipped), so
+  // every tensor is updated exactly once
   for (int first = 0; first < count; first += kSgdMaxTensors) {
     SgdList L{};
     int64_t blocks = 0;
     const int last = count < first + kSgdMaxTensors ? count : first + kSgdMaxTensors;
     for (int i = first; i < last; ++i) {
-      if (list[i].n == 0) continue;
+      if (list[i].n == 0 || list[i].param_out_t) continue;
       SgdSeg& sg = L.seg[L.count++];
       sg.pin = list[i].param_in;
       sg.pout = list[i].param_out;
@@ -297,6 +368,33 @@ hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, f
     } else {
       hipLaunchKernelGGL((sgd_kernel<float, false>), dim3((unsigned)blocks), dim3(kSgdBlock), 0, s, L, lr);
     }
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  // the tensors with a transposed copy (bf16)
+  for (int first = 0; first < count; first += kSgdTMaxTensors) {
+    SgdTList L{};
+    int64_t blocks = 0;
+    const int last = count < first + kSgdTMaxTensors ? count : first + kSgdTMaxTensors;
+    for (int i = first; i < last; ++i) {
+      if (list[i].n == 0 || !list[i].param_out_t) continue;
+      if (dt != kBF16) return hipErrorInvalidValue;
+      SgdTSeg& sg = L.seg[L.count++];
+      sg.pin = list[i].param_in;
+      sg.pout = list[i].param_out;
+      sg.pout_t = list[i].param_out_t;
+      sg.g = list[i].grad;
+      sg.min = list[i].master_in;
+      sg.mout = list[i].master_out;
+      sg.rows = list[i].t_rows;
+      sg.cols = list[i].t_cols;
+      sg.tiles_c = (sg.cols + kSgdTTile - 1) / kSgdTTile;
+      sg.block0 = blocks;
+      blocks += ((sg.rows + kSgdTTile - 1) / kSgdTTile) * sg.tiles_c;
+    }
+    if (L.count == 0) continue;
+    if (master) hipLaunchKernelGGL((sgd_t_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, L, lr);
+    else hipLaunchKernelGGL((sgd_t_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, L, lr);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -174,6 +174,10 @@ struct SgdTensor {
   const float* master_in;
   float* master_out;
   int64_t n;
+  // optional (bf16): the updated values of the [t_rows, t_cols] parameter
+  // also written transposed, [t_cols, t_rows], to param_out_t
+  void* param_out_t;
+  int64_t t_rows, t_cols;
 };
 // One SGD update of every tensor in `list` (all in dtype dt; all with fp32
 // masters when `master`).

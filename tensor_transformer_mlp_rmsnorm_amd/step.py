@@ -115,6 +115,12 @@ class ShardedStep:
             sh["d_b_in"] = None if self.swiglu else emp((F,), f32)
             sh["d_w_down"] = emp((H, F), f32)
             sh["dN_part"] = emp((T, H), f32)
+            # bf16: the down weight transposed, [F, H], read by the d_act GEMM; formed
+            # once here and then written by every SGD update beside w_down
+            sh["w_down_t"] = None
+            if self.cdt == L.BF16:
+                sh["w_down_t"] = emp((F, H))
+                L.tp_mlp_transpose_bf16(sh["w_down"], sh["w_down_t"], H, F, stream=stream)
             self.shards.append(sh)
         self.normed = emp((T, H))
         self.rstd = emp((T,), f32)
@@ -133,6 +139,10 @@ class ShardedStep:
         # targets of the update
         self.new = {}
         self.new_masters = {}
+        self.new_t = {}  # targets of the transposed copies (bf16 down weights)
+        for s, sh in enumerate(self.shards):
+            if sh["w_down_t"] is not None:
+                self.new_t[f"w_down.{s}"] = torch.empty_like(sh["w_down_t"]) if self.oop else sh["w_down_t"]
         for name, t in self._param_list():
             self.new[name] = torch.empty_like(t) if self.oop else t
             if self.masters is not None:
@@ -209,7 +219,8 @@ class ShardedStep:
         L.tp_mlp_backward(self._desc(flags, T), L.BWD_SHARD, stream=self.stream, normed=self.normed[r],
                           pre_act=sh["pre"][r], act=sh["act"][r], w_in=sh["w_in"], w_down=sh["w_down"],
                           d_out=d_out, d_pre=sh["d_pre"][r], d_w_in=sh["d_w_in"], d_b_in=sh["d_b_in"],
-                          d_w_down=sh["d_w_down"], d_normed_part=sh["dN_part"][r], workspace=self.workspace)
+                          d_w_down=sh["d_w_down"], d_normed_part=sh["dN_part"][r], w_down_t=sh["w_down_t"],
+                          workspace=self.workspace)
 
     def _norm_backward(self, dN, d_out, dx, d_norm_w, d_b_down, r: slice = slice(None), flags: int = 0,
                        parts=None) -> None:
@@ -270,9 +281,12 @@ class ShardedStep:
         for name, t in self._param_list():
             g = self._grad_of(name)
             if self.masters is not None:
-                lst.append((t, self.new[name], g, self.masters[name], self.new_masters[name], t.numel()))
+                e = (t, self.new[name], g, self.masters[name], self.new_masters[name], t.numel())
             else:
-                lst.append((t, self.new[name], g, None, None, t.numel()))
+                e = (t, self.new[name], g, None, None, t.numel())
+            if name in self.new_t:  # the down weight's transposed copy, written with it
+                e = e + (self.new_t[name], self.H, self.F)
+            lst.append(e)
         L.tp_mlp_sgd_step_multi(lst, self.cdt, self.w.lr, stream=self.stream)
 
     def adamw(self, lr: float, weight_decay: float = 0.0, max_norm: float = 0.0, beta1: float = 0.9,
@@ -302,6 +316,8 @@ class ShardedStep:
             else:
                 lst.append((t, self.new[name], g, None, None, m, v, t.numel()))
         L.tp_mlp_adamw_step_multi(lst, self.cdt, hp, grad_scale=self.clip_coef, stream=self.stream)
+        for name, tt in self.new_t.items():  # the down weights' transposed copies follow the update
+            L.tp_mlp_transpose_bf16(self.new[name], tt, self.H, self.F, stream=self.stream)
 
     def step(self, mode: str = "equivalence", update: bool = True, microbatches: int = 1) -> None:
         """Forward, backward and (``update``) the SGD step.  With

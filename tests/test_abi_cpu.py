@@ -120,7 +120,7 @@ def test_backward_checks(lib):
     assert L.tp_mlp_workspace_bytes(_desc(T=0), L.BWD_SHARD) == 0
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t"):
             setattr(a, name, A)
     a.workspace_bytes = need - 16
     assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EWORKSPACE
@@ -271,7 +271,7 @@ def test_fp8_checks(lib):
                                   None) == L.OK
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t"):
             setattr(a, name, A)
     a.d_b_in = None
     a.workspace_bytes = 1 << 30
@@ -357,7 +357,7 @@ def test_attention_checks(lib):
     assert need >= 4 * 2 * 64 * 4                              # delta [n_q, T] at least
     a = L.tp_attn_bwd_args()
     for name, _ in L.tp_attn_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t"):
             setattr(a, name, A)
     a.workspace_bytes = need - 16
     assert lib.tp_attn_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EWORKSPACE
@@ -390,7 +390,7 @@ def test_backward_norm_parts_checks(lib):
     d = _desc(T=128)
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t"):
             setattr(a, name, A)
     a.workspace_bytes = L.tp_mlp_workspace_bytes(d, L.BWD_NORM)
     a.n_d_normed_parts = 65
@@ -406,3 +406,21 @@ def test_backward_norm_parts_checks(lib):
     arr2 = (ctypes.c_void_p * 2)(A, MIS)
     a.d_normed_parts = ctypes.cast(arr2, ctypes.POINTER(ctypes.c_void_p))
     assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EALIGN
+
+
+def test_sgd_transposed_copy_checks(lib):
+    """The SGD tensor's transposed copy: bf16 only, t_rows x t_cols == n with
+    both multiples of 8, an aligned pointer; and tp_mlp_transpose_bf16's
+    shape checks; all before any launch."""
+    t = L.tp_mlp_sgd_tensor(A, A, A, None, None, 64 * 32, A, 64, 32)
+    assert lib.tp_mlp_sgd_step_multi(ctypes.byref(t), 1, L.F32, ctypes.c_float(0.1), None) == L.EDTYPE
+    t.t_rows = 60
+    t.t_cols = 32
+    assert lib.tp_mlp_sgd_step_multi(ctypes.byref(t), 1, L.BF16, ctypes.c_float(0.1), None) == L.ESHAPE
+    t.t_rows, t.t_cols = 64, 16  # product != n
+    assert lib.tp_mlp_sgd_step_multi(ctypes.byref(t), 1, L.BF16, ctypes.c_float(0.1), None) == L.ESHAPE
+    t.t_cols, t.param_out_t = 32, MIS
+    assert lib.tp_mlp_sgd_step_multi(ctypes.byref(t), 1, L.BF16, ctypes.c_float(0.1), None) == L.EALIGN
+    assert lib.tp_mlp_transpose_bf16(A, A, 12, 16, None) == L.ESHAPE
+    assert lib.tp_mlp_transpose_bf16(A, MIS, 16, 16, None) == L.EALIGN
+    assert lib.tp_mlp_transpose_bf16(None, None, 0, 16, None) == L.OK

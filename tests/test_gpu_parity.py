@@ -417,3 +417,71 @@ def test_norm_backward_streamed_parts_bitwise(dt, n_parts, H):
     for a, b, name in zip(outs[0], outs[1], ("dx", "d_norm_w", "d_b_down")):
         assert not torch.isnan(b).any(), name
         assert torch.equal(a, b), name
+
+
+SGD_T = [(136, 264), (64, 8), (520, 72), (4096, 1792)]
+
+
+@pytest.mark.parametrize("masters", [False, True])
+@pytest.mark.parametrize("rows,cols", SGD_T, ids=[f"{r}x{c}" for r, c in SGD_T])
+def test_sgd_transposed_copy(rows, cols, masters):
+    """An SGD tensor that also receives its updated values transposed: the
+    row-major result equals the plain update bit for bit, and the copy is its
+    exact transpose (tiles of 64 with ragged edges; bf16, with and without
+    fp32 masters); tensors without a copy in the same list are unaffected."""
+    from tensor_transformer_mlp_rmsnorm_amd import _lib as L
+    g = torch.Generator().manual_seed(rows * 7 + cols)
+    n = rows * cols
+    say(f"[gpu] sgd with transposed copy {rows}x{cols} masters={masters}")
+    p = torch.randn(n, generator=g).to(torch.bfloat16).cuda()
+    gr = torch.randn(n, generator=g).cuda()
+    m = p.float().clone() if masters else None
+    other_p = torch.randn(777, generator=g).to(torch.bfloat16).cuda()
+    other_g = torch.randn(777, generator=g).cuda()
+    other_m = other_p.float().clone() if masters else None
+    outs = []
+    for with_t in (False, True):
+        po, oo = torch.empty_like(p), torch.empty_like(other_p)
+        mo = torch.empty_like(m) if masters else None
+        omo = torch.empty_like(other_m) if masters else None
+        pt = torch.full((cols, rows), float("nan"), dtype=torch.bfloat16, device="cuda") if with_t else None
+        e = (p, po, gr, m, mo, n) + ((pt, rows, cols) if with_t else ())
+        L.tp_mlp_sgd_step_multi([(other_p, oo, other_g, other_m, omo, 777), e], L.BF16, 0.1)
+        outs.append((po, oo, mo, pt))
+    torch.cuda.synchronize()
+    (po0, oo0, mo0, _), (po1, oo1, mo1, pt1) = outs
+    assert torch.equal(po0, po1) and torch.equal(oo0, oo1)
+    if masters:
+        assert torch.equal(mo0, mo1)
+    assert torch.equal(pt1, po1.view(rows, cols).t().contiguous())
+
+
+def test_backward_with_transposed_down_weight_bitwise():
+    """The SHARD phase given w_down_t gives the bits of the phase that
+    transposes w_down itself; after in-place SGD steps the step driver's copy
+    is still the transpose of the updated weight."""
+    from tensor_transformer_mlp_rmsnorm_amd import _lib as L
+    from tensor_transformer_mlp_rmsnorm_amd.step import ShardedStep
+    w = synth.Workload("wdt", tokens=300, hidden=256, ffn_full=384, shards=2, act="swiglu", dtype="bf16",
+                       w_std=0.05, seed=31)
+    t = synth.draw(w, perturb=True)
+    say("[gpu] backward with and without the transposed down weight")
+    st = ShardedStep(w, t)
+    st.forward()
+    sh = st.shards[1]
+    res = []
+    for wdt in (None, sh["w_down_t"]):
+        o = {k: torch.full_like(sh[k], float("nan")) for k in ("d_pre", "d_w_in", "d_w_down", "dN_part")}
+        L.tp_mlp_backward(st._desc(), L.BWD_SHARD, normed=st.normed, pre_act=sh["pre"], act=sh["act"],
+                          w_in=sh["w_in"], w_down=sh["w_down"], d_out=st.out, d_pre=o["d_pre"], d_w_in=o["d_w_in"],
+                          d_w_down=o["d_w_down"], d_normed_part=o["dN_part"], w_down_t=wdt, workspace=st.workspace)
+        res.append(o)
+    torch.cuda.synchronize()
+    for k in res[0]:
+        assert torch.equal(res[0][k], res[1][k]), k
+    st.backward()
+    st.sgd()  # in place: w_down and its transposed copy
+    st.step()
+    torch.cuda.synchronize()
+    for shd in st.shards:
+        assert torch.equal(shd["w_down_t"], shd["w_down"].t().contiguous())
