@@ -3,8 +3,8 @@
 //   C[m, n] = sum_k A(m, k) B(k, n),  A(m,k) = A[m*lda + k] (a_kcontig) or A[k*lda + m],
 //                                     B(k,n) = B[n*ldb + k] (b_kcontig) or B[k*ldb + n].
 //
-// One 512-thread workgroup computes a 256 x 256 output tile (variants: 224-wide
-// tiles where they fill the CUs better, and a 16-wave form, both below):
+// One 512-thread workgroup computes a 256 x 256 output tile (variant: 224-wide
+// tiles where they fill the CUs better, below):
 //  * 8 waves in a 2 (M) x 4 (N) grid; each wave owns 128 x 64 outputs as 8 x 4
 //    blocks of v_mfma_f32_16x16x32_bf16 (128 fp32 accumulators per lane).  The
 //    LDS bytes read per flop are a quarter of what a 64 x 64 wave tile needs.
@@ -34,9 +34,11 @@
 //      read and multiply each k-tile in step, with the next k-tile's loads issued
 //      first and one barrier per k-tile.  The transpose reads are slower, and
 //      with the phases of a ping-pong the read phase would outlast the multiply
-//      phase; here both share every phase.  For A K-contiguous, B MN-contiguous
-//      and fp32 output the 256 x 256 tile runs as 16 waves of 64 x 64 (four per
-//      SIMD), which hides the transpose reads better than 8 waves of 128 x 64.
+//      phase; here both share every phase.  On the 224 x 256 tile and on the
+//      256 x 256 tile with A K-contiguous and B MN-contiguous the loop is
+//      pipelined by half a k-tile: a wave reads the fragments of the next
+//      k-half before it multiplies the current one, so its LDS reads are in
+//      flight under its own MFMAs.
 //  * B is the MFMA's first operand, so a lane's accumulator holds 4 consecutive
 //    output columns of one row and the epilogues work on 4-wide vectors.
 //  * Tile order: each of the 8 XCDs gets a contiguous range of tile ids
@@ -804,8 +806,8 @@ inline int64_t tile_cost(const GemmArgs& g, int ksplit, int cus) {
 
 // Which two-stage main loop a tile shape runs: the pipelined one where it was
 // measured faster -- the 224 x 256 tile (the gate/up weight gradient: 240 ->
-// 224 us) and the NN 256 x 256 tile (the input gradient: 237 -> 214 us against
-// the 16-wave tile) -- and the plain one for the 256 x 224 and the TN 256 x 256
+// 224 us) and the NN 256 x 256 tile (the input gradient: 237 -> 214 us) --
+// and the plain one for the 256 x 224 and the TN 256 x 256
 // tiles, where reading a whole k-half ahead measured slower.
 template <bool AK, bool BKC, class SH>
 constexpr bool pipelined_loop() {
@@ -871,7 +873,6 @@ hipError_t launch_tiles(const GemmArgs& ga, int ntm, int ntn, hipStream_t s) {
     const int64_t cm = tile_cost<Tile224x256>(ga, ga.ksplit, cus);
     if (cn < c0 && cn <= cm) return launch_two_stage<AK, BKC, EPI, Tile256x224>(ga, s);
     if (cm < c0) return launch_two_stage<AK, BKC, EPI, Tile224x256>(ga, s);
-    // A K-contiguous, B MN-contiguous, fp32 out: 16 waves measured faster (dgrad 8192 x 4096 x 3584)
     return launch_two_stage<AK, BKC, EPI, Tile256x256>(ga, s);
   }
 }

@@ -26,6 +26,15 @@ host, and then:
   ~470 M-element activation tensors per dense oracle step) is compared end to
   end on sampled rows, channels and columns that the oracle computes exactly
   (oracle.sampled_step), in fp32 accumulation.
+* test_against_exact_storage: every tensor of the dense workloads against
+  the fp64 oracle with no storage rounding at all (storage="exact").  The
+  bound 2e-2 is asserted for each tensor on which the bf16 storage model
+  itself stays within 1.5e-2 of exact; on the others bf16 storage alone
+  (one rounding of each stored activation, every contraction exact) already
+  moves the result past or near 2e-2 -- at Llama-3-8B TP=8: out 2.1e-2,
+  act 5.1e-2, dN 2.4e-2, dx 3.7e-2, the weight gradients 2.9-3.9e-2,
+  the pre-activation gradients 0.11 -- so there the GPU is held to at most
+  twice the storage model's own distance from exact, and both are printed.
 """
 
 import sys
@@ -99,6 +108,23 @@ def _pre_of_shards(w, pre_tuple, s):
     return np.concatenate([p[:, lo:hi] for p in pre_tuple], axis=1)
 
 
+_DENSE = {}
+
+
+def _dense(w, t, storage):
+    """The fp64 oracle's dense step of workload w, kept for the tests of the
+    same workload (one workload's steps at a time)."""
+    key = (w.name, storage)
+    if key not in _DENSE:
+        for k in [k for k in _DENSE if k[0] != w.name]:
+            del _DENSE[k]
+        t0 = time.time()
+        _DENSE[key] = oracle.dense_step(synth.to_numpy64(t["x"]), _np_params(t), w.act, w.eps, w.lr,
+                                        storage=storage)
+        say(f"  oracle dense step (fp64, {storage} storage): {time.time() - t0:.1f} s")
+    return _DENSE[key]
+
+
 def test_end_to_end(full):
     w, t, h = full
     report, printed = {}, {}
@@ -108,8 +134,7 @@ def test_end_to_end(full):
         say(f"  {w.name} end-to-end (sampled): " + ", ".join(f"{k} {v:.2e}" for k, v in report.items())
             + f"  ({time.time() - t0:.1f} s)")
         return
-    d = oracle.dense_step(synth.to_numpy64(t["x"]), _np_params(t), w.act, w.eps, w.lr, storage="bf16")
-    say(f"  oracle dense step (fp64): {time.time() - t0:.1f} s")
+    d = _dense(w, t, "bf16")
     g, npar = d["grads"], d["new_params"]
     swiglu = w.act == "swiglu"
     fails = []
@@ -146,6 +171,69 @@ def test_end_to_end(full):
     say(f"  {w.name} end-to-end: " + ", ".join(f"{k} {v:.2e}" for k, v in report.items())
         + "; stage-wise only: " + ", ".join(f"{k} {v:.2e}" for k, v in printed.items())
         + f"  ({time.time() - t0:.1f} s)")
+    assert not fails, "; ".join(fails)
+
+
+def _step_tensors(w, h):
+    """(name, GPU tensor, field of an oracle dense step, rowwise) for every
+    tensor the step stores or updates; per-shard pre-activations and their
+    gradients are listed per shard."""
+    swiglu = w.act == "swiglu"
+    n = len(h["shards"])
+    new = h["new"]
+    items = [("normed", h["normed"], lambda d: d["n"], True),
+             ("out", h["out"], lambda d: d["out"], True),
+             ("act", _cat_shards(h, "act", 1), lambda d: d["a"], True),
+             ("dN", h["dN"], lambda d: d["dN"], True),
+             ("dx", h["dx"], lambda d: d["dx"], True),
+             ("d_w_in", _cat_shards(h, "d_w_in", 1 if swiglu else 0), lambda d: d["grads"]["w_in"], False),
+             ("d_w_down", _cat_shards(h, "d_w_down", 1), lambda d: d["grads"]["w_down"], False),
+             ("d_norm_w", h["d_norm_w"], lambda d: d["grads"]["norm_w"], False),
+             ("d_b_down", h["d_b_down"], lambda d: d["grads"]["b_down"], False),
+             ("new_norm_w", new["norm_w"], lambda d: d["new_params"].norm_w, False),
+             ("new_b_down", new["b_down"], lambda d: d["new_params"].b_down, False),
+             ("new_w_in", torch.cat([new[f"w_in.{s}"].float() for s in range(n)], dim=1 if swiglu else 0),
+              lambda d: d["new_params"].w_in, False),
+             ("new_w_down", torch.cat([new[f"w_down.{s}"].float() for s in range(n)], dim=1),
+              lambda d: d["new_params"].w_down, False)]
+    if not swiglu:
+        items += [("d_b_in", _cat_shards(h, "d_b_in", 0), lambda d: d["grads"]["b_in"], False),
+                  ("new_b_in", torch.cat([new[f"b_in.{s}"].float() for s in range(n)]),
+                   lambda d: d["new_params"].b_in, False)]
+    for s, sh in enumerate(h["shards"]):
+        items.append((f"pre[{s}]", sh["pre"], lambda d, s=s: _pre_of_shards(w, d["pre"], s), True))
+        items.append((f"d_pre[{s}]", sh["d_pre"], lambda d, s=s: _pre_of_shards(w, d["d_pre"], s), True))
+    return items
+
+
+EXACT_ASSERTED_BELOW = 1.5e-2  # storage model's own distance from exact under which 2e-2 is asserted
+
+
+def test_against_exact_storage(full):
+    """The GPU step against the fp64 oracle with no bf16 storage rounding."""
+    w, t, h = full
+    if w.name not in DENSE_END_TO_END:
+        pytest.skip("the full-width workload's dense oracle step does not fit the test's time")
+    t0 = time.time()
+    dm, de = _dense(w, t, "bf16"), _dense(w, t, "exact")
+    held, storage_bound = [], []
+    fails = []
+    for name, got, field, rowwise in _step_tensors(w, h):
+        ref = field(de)
+        e_gpu = floored_rel(got, ref, rowwise)
+        e_model = floored_rel(field(dm), ref, rowwise)
+        if e_model <= EXACT_ASSERTED_BELOW:
+            held.append((name, e_gpu, e_model))
+            if not e_gpu <= 2e-2:
+                fails.append(f"{name}: {e_gpu:.3e} from exact > 2e-2 (storage model {e_model:.3e})")
+        else:
+            storage_bound.append((name, e_gpu, e_model))
+            if not e_gpu <= 2.0 * e_model:
+                fails.append(f"{name}: {e_gpu:.3e} from exact > twice the storage model's {e_model:.3e}")
+    fmt = lambda lst: ", ".join(f"{k} {a:.2e} (model {b:.2e})" for k, a, b in lst)
+    say(f"  {w.name} against exact storage, held to 2e-2: {fmt(held)}")
+    say(f"  {w.name} against exact storage, bf16 storage alone {EXACT_ASSERTED_BELOW:.1e}+: {fmt(storage_bound)}"
+        f"  ({time.time() - t0:.1f} s)")
     assert not fails, "; ".join(fails)
 
 
