@@ -212,6 +212,8 @@ size_t tp_mlp_workspace_bytes(const tp_mlp_desc* d, int32_t phase) {
   return need;
 }
 
+}  // extern "C"
+
 namespace {
 
 // The backward of both phases after the descriptor, the phase and the args
@@ -398,6 +400,8 @@ int scratch_of_current_device(const char* fn, void** out) {
 
 }  // namespace
 
+extern "C" {
+
 int tp_mlp_backward(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args* a, void* stream) {
   const char* fn = "tp_mlp_backward";
   g_err[0] = 0;
@@ -423,6 +427,8 @@ int tp_mlp_backward_noalloc(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bw
   b.workspace_bytes = (size_t)TP_MLP_NOALLOC_SCRATCH_BYTES;
   return backward_checked(d, phase, &b, stream, fn);
 }
+
+}  // extern "C"
 
 namespace {
 
@@ -474,6 +480,8 @@ int sgd_list(const tp_mlp_sgd_tensor* list, int32_t count, int32_t param_dtype, 
 }
 
 }  // namespace
+
+extern "C" {
 
 int tp_mlp_transpose_bf16(const void* in, void* out, int64_t rows, int64_t cols, void* stream) {
   const char* fn = "tp_mlp_transpose_bf16";
@@ -599,6 +607,8 @@ int tp_mlp_clip_grad_norm(const float* const* grads, const int64_t* counts, int3
 
 // ------------------------------------------------------------------ FP8
 
+}  // extern "C"
+
 namespace {
 
 int check_meta_args(int32_t history_len, const char* fn) {
@@ -638,6 +648,8 @@ GemmArgs fp8_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, c
 }
 
 }  // namespace
+
+extern "C" {
 
 int tp_mlp_fp8_meta_init(float* meta, int32_t fmt, int32_t history_len, void* stream) {
   const char* fn = "tp_mlp_fp8_meta_init";
@@ -921,6 +933,8 @@ int tp_mlp_backward_fp8(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_ar
 
 // ------------------------------------------------------------- attention
 
+}  // extern "C"
+
 namespace {
 
 int check_attn_shape(int64_t batch, int64_t seq, int32_t n_q, int32_t n_kv, int32_t head_dim, const char* fn) {
@@ -977,6 +991,8 @@ size_t attn_ksplit_bytes(const tp_attn_desc* d) {
 }
 
 }  // namespace
+
+extern "C" {
 
 size_t tp_attn_workspace_bytes(const tp_attn_desc* d, int32_t phase) {
   if (!d || d->batch < 0 || d->seq < 0 || d->hidden <= 0 || d->n_q <= 0) return 0;

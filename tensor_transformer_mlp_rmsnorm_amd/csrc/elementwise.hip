@@ -342,14 +342,12 @@ hipError_t launch_colsum(DType dt, const void* in, float* out, void* ws, int64_t
 
 hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, float lr, hipStream_t s) {
   KernelTimer timer("sgd", s);
-  // each launch takes the next kSgdMaxTensors entries of the list (empty
-  // tensors and those with a transposed copy among them are skipped), so
-  // every tensor is updated exactly once
-  for (int first = 0; first < count; first += kSgdMaxTensors) {
+  // Each launch takes the next (up to) kSgdMaxTensors non-empty tensors of the
+  // list that have no transposed copy, so every tensor is updated exactly once.
+  for (int i = 0; i < count;) {
     SgdList L{};
     int64_t blocks = 0;
-    const int last = count < first + kSgdMaxTensors ? count : first + kSgdMaxTensors;
-    for (int i = first; i < last; ++i) {
+    for (; i < count && L.count < kSgdMaxTensors; ++i) {
       if (list[i].n == 0 || list[i].param_out_t) continue;
       SgdSeg& sg = L.seg[L.count++];
       sg.pin = list[i].param_in;
@@ -361,7 +359,7 @@ hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, f
       sg.block0 = blocks;
       blocks += (sg.n + kSgdPerBlock - 1) / kSgdPerBlock;
     }
-    if (L.count == 0) continue;
+    if (L.count == 0) break;
     if (dt == kBF16) {
       if (master) hipLaunchKernelGGL((sgd_kernel<bf16_t, true>), dim3((unsigned)blocks), dim3(kSgdBlock), 0, s, L, lr);
       else hipLaunchKernelGGL((sgd_kernel<bf16_t, false>), dim3((unsigned)blocks), dim3(kSgdBlock), 0, s, L, lr);
@@ -371,12 +369,11 @@ hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, f
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  // the tensors with a transposed copy (bf16)
-  for (int first = 0; first < count; first += kSgdTMaxTensors) {
+  // Then the tensors with a transposed copy (bf16), up to kSgdTMaxTensors per launch.
+  for (int i = 0; i < count;) {
     SgdTList L{};
     int64_t blocks = 0;
-    const int last = count < first + kSgdTMaxTensors ? count : first + kSgdTMaxTensors;
-    for (int i = first; i < last; ++i) {
+    for (; i < count && L.count < kSgdTMaxTensors; ++i) {
       if (list[i].n == 0 || !list[i].param_out_t) continue;
       if (dt != kBF16) return hipErrorInvalidValue;
       SgdTSeg& sg = L.seg[L.count++];
@@ -392,7 +389,7 @@ hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, f
       sg.block0 = blocks;
       blocks += ((sg.rows + kSgdTTile - 1) / kSgdTTile) * sg.tiles_c;
     }
-    if (L.count == 0) continue;
+    if (L.count == 0) break;
     if (master) hipLaunchKernelGGL((sgd_t_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, L, lr);
     else hipLaunchKernelGGL((sgd_t_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, L, lr);
     const hipError_t err = hipGetLastError();

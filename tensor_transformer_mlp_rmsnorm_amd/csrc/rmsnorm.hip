@@ -35,6 +35,25 @@ __device__ __forceinline__ int clampi(int i, int n) { return i < n ? i : n - 1; 
 __device__ __forceinline__ uint4 masked16(uint4 v, bool ok) { return ok ? v : make_uint4(0, 0, 0, 0); }
 __device__ __forceinline__ floatx4 masked4(floatx4 v, bool ok) { return ok ? v : floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// Four consecutive elements as they come from memory, and their fp32 values.
+template <typename T>
+struct RawVec;
+template <>
+struct RawVec<float> {
+  using type = floatx4;
+  static __device__ __forceinline__ type load(const float* p) { return *reinterpret_cast<const floatx4*>(p); }
+  static __device__ __forceinline__ floatx4 value(type v) { return v; }
+};
+template <>
+struct RawVec<bf16_t> {
+  using type = uint2;
+  static __device__ __forceinline__ type load(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+  static __device__ __forceinline__ floatx4 value(type u) {
+    return floatx4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                   __uint_as_float(u.y & 0xffff0000u)};
+  }
+};
+
 // Forward: one wave per row, 4 waves per workgroup, each wave taking rows
 // w, w + 4, w + 8, w + 12 of the workgroup's 16; the norm weight is read once
 // per wave and the next row is loaded while the current one is reduced.
@@ -336,11 +355,14 @@ __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_kernel(
 }
 
 // The backward with NP > 1 shard partials, software-pipelined over its rows:
-// the loads of row t + 1 (NP partials, x, dY) are issued before row t's sum,
-// barrier, dx stores and column accumulation, so the next row's reads are in
-// flight while the current one is finished.  Partials are summed (in index
-// order) as soon as they land, so a row in flight holds NP x UPT vectors and
-// a finished one UPT.
+// the loads of row t + G (NP partials, x, dY) are issued before row t's
+// reduction, barrier, dx stores and column accumulation, so the next row's
+// reads are in flight while the current one is finished.  The issue sits in
+// the loop body with no branch around it (the last row is finished after the
+// loop): the compiler waits for every load issued inside a branch before
+// leaving it, which would take the overlap away.  Partials are summed in index
+// order as soon as they land.  The running column sums of dw and db live in
+// LDS; each thread reads and writes only its own slots, in row order.
 template <typename T, int UPT, bool FULL, int NP>
 __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_parts_kernel(
     const NormParts parts, const T* __restrict__ x, const T* __restrict__ dY, const float* __restrict__ rstd,
@@ -348,48 +370,60 @@ __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_parts_kernel(
     int H, int64_t rows_per_block) {
   static_assert(NP > 1, "the single-partial backward is rmsnorm_bwd_kernel");
   __shared__ float red[2][kBwdThreads / 64];
+  __shared__ floatx4 col_dw[UPT][kBwdThreads], col_db[UPT][kBwdThreads];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nunits = H / 4;
   const int64_t G = gridDim.x;  // rows b, b + G, ... as in rmsnorm_bwd_kernel
-  floatx4 wv[UPT], dwa[UPT], dba[UPT];
+  floatx4 wv[UPT];
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
     const int q = tid + kBwdThreads * u;
     wv[u] = FULL ? load4<T>(w + 4 * q) : masked4(load4<T>(w + 4 * clampi(q, nunits)), q < nunits);
-    dwa[u] = floatx4{0.f, 0.f, 0.f, 0.f};
-    dba[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+    col_dw[u][tid] = floatx4{0.f, 0.f, 0.f, 0.f};
+    col_db[u][tid] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   const float invH = 1.0f / (float)H;
-  floatx4 pv[NP][UPT], xn[UPT], dyn[UPT];
-  auto issue = [&](int64_t t) {  // row t's loads (t < rows)
+  // The row in flight, as loaded: the loop carries these registers unchanged
+  // until the row is taken (a conversion or mask at the load would make the
+  // compiler wait for the load where it sits).
+  using Raw = typename RawVec<T>::type;
+  floatx4 pv[NP][UPT];
+  Raw xn[UPT], dyn[UPT];
+  // Row t's loads.  The row's base is uniform over the workgroup and a lane's
+  // column offset is one 32-bit value shared by every tensor it reads.
+  auto issue = [&](int64_t t) {
+    const int64_t ro = t * H;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int q = tid + kBwdThreads * u;
-      const bool ok = FULL || q < nunits;
-      const int64_t off = t * H + 4 * (FULL ? q : clampi(q, nunits));
+      const uint32_t c = 4u * (uint32_t)(FULL ? q : clampi(q, nunits));
 #pragma unroll
       for (int k = 0; k < NP; ++k)
-        pv[k][u] = masked4(__builtin_nontemporal_load(reinterpret_cast<const floatx4*>(parts.p[k] + off)), ok);
-      xn[u] = masked4(load4<T>(x + off), ok);
-      dyn[u] = masked4(load4<T>(dY + off), ok);
+        pv[k][u] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>((parts.p[k] + ro) + c));
+      xn[u] = RawVec<T>::load((x + ro) + c);
+      dyn[u] = RawVec<T>::load((dY + ro) + c);
     }
   };
-  if (blockIdx.x < rows) issue(blockIdx.x);  // (no rows: the partial column sums are zero)
-  int64_t it = 0;
-  for (int64_t t = blockIdx.x; t < rows; t += G, ++it) {
-    floatx4 dn[UPT], xv[UPT], dy[UPT];
+  // dN of the row in flight, in index order, with its x and dY (units past the
+  // row's end read a clamped address and are zeroed here).
+  auto take = [&](floatx4 (&dn)[UPT], floatx4 (&xv)[UPT], floatx4 (&dy)[UPT]) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
+      const bool ok = FULL || tid + kBwdThreads * u < nunits;
       floatx4 acc = pv[0][u];
 #pragma unroll
       for (int k = 1; k < NP; ++k) acc += pv[k][u];
-      dn[u] = acc;
-      xv[u] = xn[u];
-      dy[u] = dyn[u];
+      dn[u] = masked4(acc, ok);
+      xv[u] = masked4(RawVec<T>::value(xn[u]), ok);
+      dy[u] = masked4(RawVec<T>::value(dyn[u]), ok);
+      // the converted values exist here, so the loaded registers are free for the next row
+      // (otherwise the conversion sinks to its use and the loop carries copies of the loads)
+      asm volatile("" : "+v"(dn[u]), "+v"(xv[u]), "+v"(dy[u]));
     }
-    const float r = rstd[t];
-    if (t + G < rows) issue(t + G);
-    __builtin_amdgcn_sched_barrier(0);  // the next row's loads are issued before this row's work
+  };
+  // Row t's reduction, dx and column sums.
+  auto finish = [&](int64_t t, int slot, float r, const floatx4 (&dn)[UPT], const floatx4 (&xv)[UPT],
+                    const floatx4 (&dy)[UPT]) {
     float pk = 0.f;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
@@ -397,7 +431,6 @@ __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_parts_kernel(
       pk += (p[0] + p[1]) + (p[2] + p[3]);
     }
     pk = wave_sum(pk);
-    const int slot = (int)(it & 1);
     if (lane == 0) red[slot][wave] = pk;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     float c = 0.f;
@@ -410,17 +443,33 @@ __global__ __launch_bounds__(kBwdThreads) void rmsnorm_bwd_parts_kernel(
       const int q = tid + kBwdThreads * u;
       if (!FULL && q >= nunits) continue;
       const floatx4 d = dy[u] + r * dn[u] * wv[u] - xv[u] * r3c;
-      store4<T>(dx + t * H + 4 * q, d);
-      dwa[u] += dn[u] * xv[u] * r;
-      dba[u] += dy[u];
+      store4<T>((dx + t * H) + 4u * (uint32_t)q, d);
+      col_dw[u][tid] += dn[u] * xv[u] * r;
+      col_db[u][tid] += dy[u];
     }
+  };
+  int64_t t = blockIdx.x, it = 0;
+  if (t < rows) {  // (no rows: the partial column sums are zero)
+    issue(t);
+    for (; t + G < rows; t += G, ++it) {
+      floatx4 dn[UPT], xv[UPT], dy[UPT];
+      take(dn, xv, dy);
+      const float r = rstd[t];
+      __builtin_amdgcn_sched_barrier(0);  // this row's partials are summed before their registers take the next row
+      issue(t + G);
+      __builtin_amdgcn_sched_barrier(0);  // the next row's loads are issued before this row's work
+      finish(t, (int)(it & 1), r, dn, xv, dy);
+    }
+    floatx4 dn[UPT], xv[UPT], dy[UPT];
+    take(dn, xv, dy);
+    finish(t, (int)(it & 1), rstd[t], dn, xv, dy);
   }
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
     const int q = tid + kBwdThreads * u;
     if (q >= nunits) continue;
-    store4<float>(ws_dw + (int64_t)blockIdx.x * H + 4 * q, dwa[u]);
-    store4<float>(ws_db + (int64_t)blockIdx.x * H + 4 * q, dba[u]);
+    store4<float>(ws_dw + (int64_t)blockIdx.x * H + 4 * q, col_dw[u][tid]);
+    store4<float>(ws_db + (int64_t)blockIdx.x * H + 4 * q, col_db[u][tid]);
   }
 }
 

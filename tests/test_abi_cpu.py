@@ -42,6 +42,21 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(raw, n), n
 
 
+def test_no_other_c_symbols_are_exported(lib):
+    """Every exported symbol with C linkage (an unmangled name) is one the
+    header declares: internal helpers stay internal."""
+    import shutil
+    import subprocess
+
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    c_names = {f[2] for f in (line.split() for line in out.splitlines())
+               if len(f) == 3 and f[1] == "T" and not f[2].startswith("_Z")}
+    assert c_names == set(declared_functions()), sorted(c_names ^ set(declared_functions()))
+
+
 def test_version(lib):
     assert "gfx950" in L.tp_mlp_version()
 
