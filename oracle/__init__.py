@@ -18,52 +18,36 @@ page's printed error magnitudes and ablation signatures).  None is unpinned.
 """
 
 from .mlp import (  # noqa: F401
+    MODES,
     Params,
-    rms_norm_fwd,
-    rms_norm_bwd,
-    activation_fwd,
     activation_bwd,
+    activation_fwd,
+    bf16_round,
+    dense_step,
+    fixture_record,
+    gelu,
+    gelu_grad,
+    inspect_record,
+    rms_norm_bwd,
+    rms_norm_fwd,
+    row_forward_backward,
+    sharded_step,
     sigmoid,
     silu,
     silu_grad,
-    gelu,
-    gelu_grad,
-    dense_step,
-    sharded_step,
-    fixture_record,
-    inspect_record,
-    row_forward_backward,
-    MODES,
-    bf16_round,
     storage_rounding,
 )
 from .sampled import sampled_step  # noqa: F401,E402
 from .optim import (  # noqa: F401,E402
     ADAM_BETA1,
     ADAM_BETA2,
-    ADAM_EPS,
-    microbatch_bounds,
     accumulated_grads,
-    global_grad_norm,
-    clip_coefficient,
-    adamw_update,
     adamw_step,
+    adamw_update,
+    clip_coefficient,
+    global_grad_norm,
+    microbatch_bounds,
 )
-from .sequence import SP_MODES, sequence_parallel_step, sequence_slices  # noqa: F401,E402
-from .fp8 import (  # noqa: F401,E402
-    E4M3,
-    E5M2,
-    Fp8Meta,
-    fp8_dense_step,
-    fp8_sharded_step,
-    new_metas as fp8_new_metas,
-)
-from .attention import (  # noqa: F401,E402
-    ATTN_MODES,
-    AttnParams,
-    AttnShape,
-    attn_dense_step,
-    attn_sharded_step,
-    causal_attention_fwd,
-    causal_attention_bwd,
-)
+from .sequence import sequence_parallel_step  # noqa: F401,E402
+from .fp8 import fp8_dense_step  # noqa: F401,E402
+from .attention import attn_dense_step, attn_sharded_step  # noqa: F401,E402

@@ -208,6 +208,9 @@ size_t tp_mlp_workspace_bytes(const tp_mlp_desc* d, int32_t phase) {
       need = need > w2 ? need : w2;
       need = need > w4 ? need : w4;
     }
+    // and of the input-gradient GEMM (K = P) when it has few tiles
+    const size_t w3 = gemm_ksplit_workspace(T, H, P);
+    need = need > w3 ? need : w3;
   }
   return need;
 }
@@ -341,6 +344,8 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
   b3.C = a->d_normed_part;
   b3.ldc = H;
   b3.tag = "gemm_dgrad_normed";
+  b3.ksplit = gemm_ksplit(b3.M, b3.N, b3.K);
+  b3.ws = static_cast<float*>(a->workspace);
   CHECK_HIP(launch_gemm(dt, true, false, kEpiStoreF32, b3, s), "d_normed GEMM");
 
   // d_w_in = d_pre^T normed ([P,T] x [T,H]).
@@ -914,6 +919,8 @@ int tp_mlp_backward_fp8(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_ar
                          "gemm_dgrad_normed_fp8");
   b3.C = a->d_normed_part;
   b3.ldc = H;
+  b3.ksplit = gemm_ksplit(b3.M, b3.N, b3.K);
+  b3.ws = static_cast<float*>(a->workspace);
   CHECK_HIP(launch_gemm_fp8(kFp8E5M2, kFp8E4M3, kEpiStoreF32, b3, s), "d_normed GEMM");
 
   // d_w_in = d_pre^T normed on d_pre_t [P, Tp] and normed_t [H, Tp].
