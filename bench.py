@@ -71,14 +71,15 @@ def hbm_bytes_per_step(w) -> dict:
     es = 2 if w.dtype == "bf16" else 4
     n_params = H + H + S * (2 * F * H + H * F + (F if w.act == "gelu" else 0))
     per_param = (4 + 4 + 4 + es) if w.master else (es + 4 + es)
-    n_wd_t = S * H * F if w.dtype == "bf16" else 0  # the down weights' transposed copies, written with the update
+    P = 2 * F if w.act == "swiglu" else F
+    n_t = S * (H * F + P * H) if w.dtype == "bf16" else 0  # the weights' transposed copies, written with the update
     return {
         "rmsnorm_fwd": T * H * 2 * es + 4 * T + H * es,                 # x in, N out, rstd out, w in
         "partial_sum_residual": S * 4 * T * H + 2 * es * T * H + H * es,  # S fp32 partials + x in, out
         "partial_sum": S * 4 * T * H + 4 * T * H,                        # S fp32 partials in, dN out
         # the S fp32 partials of dN (summed as they are read), x, dY in, dx out
         "rmsnorm_bwd": T * H * (4 * S + 3 * es) + 4 * T + H * es,
-        "sgd": n_params * per_param + n_wd_t * es,                       # p (or master), g in; p (+master), W_d^T out
+        "sgd": n_params * per_param + n_t * es,                          # p (or master), g in; p (+master), W^T out
         # optimiser path: AdamW reads g, m, v and p (or master) and writes m, v, p (+ master)
         "adamw": n_params * ((4 + 4 + 4 + 8 + 8 + es) if w.master else (2 * es + 4 + 8 + 8)),
         "grad_norm": n_params * 4,                                         # every fp32 gradient read once

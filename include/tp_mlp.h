@@ -197,6 +197,12 @@ typedef struct {
      d_act GEMM reads it; NULL, the phase transposes w_down into the
      workspace first.  It must hold the transpose of this w_down. */
   const void* w_down_t;
+  /* SHARD phase, optional (bf16): w_in transposed, [H, 2F] | [H, F] (w_in read
+     as a [2F, H] | [F, H] matrix), as tp_mlp_transpose_bf16 or the SGD's
+     transposed copy write it.  Given, the d_normed GEMM reads both operands
+     K-contiguous; NULL, it reads w_in as it lies.  It must hold the transpose
+     of this w_in. */
+  const void* w_in_t;
 } tp_mlp_bwd_args;
 
 /*

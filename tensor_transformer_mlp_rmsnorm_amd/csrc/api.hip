@@ -272,6 +272,10 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
     if (!aligned16(a->w_down_t)) return fail(TP_MLP_EALIGN, "%s: 'w_down_t' is not 16-byte aligned", fn);
     if (dt != kBF16) return fail(TP_MLP_EDTYPE, "%s: w_down_t is taken for bf16 only", fn);
   }
+  if (a->w_in_t) {
+    if (!aligned16(a->w_in_t)) return fail(TP_MLP_EALIGN, "%s: 'w_in_t' is not 16-byte aligned", fn);
+    if (dt != kBF16) return fail(TP_MLP_EDTYPE, "%s: w_in_t is taken for bf16 only", fn);
+  }
   REQUIRE_PTR(a->d_w_in);
   REQUIRE_PTR(a->d_w_down);
   if (!swiglu) REQUIRE_PTR(a->d_b_in);
@@ -346,7 +350,13 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
   b3.tag = "gemm_dgrad_normed";
   b3.ksplit = gemm_ksplit(b3.M, b3.N, b3.K);
   b3.ws = static_cast<float*>(a->workspace);
-  CHECK_HIP(launch_gemm(dt, true, false, kEpiStoreF32, b3, s), "d_normed GEMM");
+  if (dt == kBF16 && a->w_in_t) {
+    b3.B = a->w_in_t;  // the caller's transposed copy: both operands K-contiguous
+    b3.ldb = P;
+    CHECK_HIP(launch_gemm(dt, true, true, kEpiStoreF32, b3, s), "d_normed GEMM");
+  } else {
+    CHECK_HIP(launch_gemm(dt, true, false, kEpiStoreF32, b3, s), "d_normed GEMM");
+  }
 
   // d_w_in = d_pre^T normed ([P,T] x [T,H]).
   GemmArgs b4{};

@@ -187,7 +187,13 @@ struct SgdTList {
 
 template <bool MASTER>
 __global__ __launch_bounds__(256) void sgd_t_kernel(SgdTList L, float lr) {
-  __shared__ bf16_t tile[kSgdTTile][kSgdTTile + 2];
+  // A 64 x 64 tile: each thread updates two chunks of 8 consecutive elements of a row (16-byte
+  // accesses, the flat kernel's arithmetic), stores them row-major and, as one 16-byte write, into
+  // an LDS tile whose rows are padded to 144 bytes; then each thread reads 8 rows x 2 adjacent
+  // columns back with 4-byte reads and stores the two 8-element column chunks of the transposed
+  // copy.  Eight consecutive lanes take the 8 row groups of one column pair, so each wave writes
+  // whole 128-byte column segments.
+  __shared__ __align__(16) bf16_t tile[kSgdTTile][kSgdTTile + 8];
   int t = 0;
   while (t + 1 < L.count && (int64_t)blockIdx.x >= L.seg[t + 1].block0) ++t;
   const SgdTSeg& sg = L.seg[t];
@@ -205,23 +211,27 @@ __global__ __launch_bounds__(256) void sgd_t_kernel(SgdTList L, float lr) {
       floatx4 v0, v1;
       sgd8<bf16_t, MASTER>(pin, sg.g, sg.min, sg.mout, e, lr, v0, v1);
       const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      *reinterpret_cast<uint4*>(pout + e) = Chunk<bf16_t>::pack(f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) tile[row][col8 + i] = f32_to_bf16(f[i]);
+      const uint4 u = Chunk<bf16_t>::pack(f);
+      *reinterpret_cast<uint4*>(pout + e) = u;
+      *reinterpret_cast<uint4*>(&tile[row][col8]) = u;
     }
   }
   __syncthreads();
   bf16_t* pt = static_cast<bf16_t*>(sg.pout_t);
+  const int c = 2 * (threadIdx.x >> 3), rr = 8 * (threadIdx.x & 7);
+  const int64_t gc = c0 + c, gr = r0 + rr;
+  if (gc < sg.cols && gr < sg.rows) {  // (cols and rows are multiples of 8: the pair and the 8 rows are whole)
+    uint32_t w[8];
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int ch = threadIdx.x + 256 * pass, col = ch >> 3, row8 = (ch & 7) * 8;
-    const int64_t gc = c0 + col, gr = r0 + row8;
-    if (gc < sg.cols && gr < sg.rows) {
-      uint32_t w[4];
+    for (int i = 0; i < 8; ++i) w[i] = *reinterpret_cast<const uint32_t*>(&tile[rr + i][c]);
+    uint32_t lo[4], hi[4];  // column c (low halves) and column c + 1 (high halves), rows rr .. rr + 7
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (uint32_t)tile[row8 + 2 * i][col] | ((uint32_t)tile[row8 + 2 * i + 1][col] << 16);
-      *reinterpret_cast<uint4*>(pt + gc * sg.rows + gr) = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = (w[2 * i] & 0xffffu) | (w[2 * i + 1] << 16);
+      hi[i] = (w[2 * i] >> 16) | (w[2 * i + 1] & 0xffff0000u);
     }
+    *reinterpret_cast<uint4*>(pt + gc * sg.rows + gr) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4*>(pt + (gc + 1) * sg.rows + gr) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
   }
 }
 

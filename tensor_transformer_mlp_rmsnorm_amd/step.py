@@ -11,8 +11,10 @@ all-reduces of the method become tp_partial_sum at the same two points
   backward  shard s: tp_mlp_backward(SHARD, d_out = out) -> dN_s and the shard's weight grads
             tp_mlp_backward(NORM, d_normed_parts = dN_0..dN_{S-1})   (backward boundary: the sum
             of the partials formed inside the RMSNorm backward) -> dx, d_norm_w, d_b_down
-  update    tp_mlp_sgd_step_multi over every parameter tensor (one launch), or
-            tp_mlp_clip_grad_norm + tp_mlp_adamw_step_multi
+  update    tp_mlp_sgd_step_multi over every parameter tensor, writing the bf16 weight
+            matrices' transposed copies beside them (the backward's d_act and d_normed
+            GEMMs read those, so both run with K-contiguous operands), or
+            tp_mlp_clip_grad_norm + tp_mlp_adamw_step_multi (copies re-formed after it)
 
 A global batch can be run as microbatches ("Megatron-LM walkthrough", Part IV,
 Stage 4): contiguous token slices, each run forward and backward on row views
@@ -115,12 +117,15 @@ class ShardedStep:
             sh["d_b_in"] = None if self.swiglu else emp((F,), f32)
             sh["d_w_down"] = emp((H, F), f32)
             sh["dN_part"] = emp((T, H), f32)
-            # bf16: the down weight transposed, [F, H], read by the d_act GEMM; formed
-            # once here and then written by every SGD update beside w_down
-            sh["w_down_t"] = None
+            # bf16: each weight matrix is also kept transposed -- w_down as [F, H] for the
+            # d_act GEMM, w_in as [H, P] for the d_normed GEMM -- formed once here and then
+            # written by every SGD update beside the weight
+            sh["w_down_t"] = sh["w_in_t"] = None
             if self.cdt == L.BF16:
                 sh["w_down_t"] = emp((F, H))
                 L.tp_mlp_transpose_bf16(sh["w_down"], sh["w_down_t"], H, F, stream=stream)
+                sh["w_in_t"] = emp((H, P))
+                L.tp_mlp_transpose_bf16(sh["w_in"], sh["w_in_t"], P, H, stream=stream)
             self.shards.append(sh)
         self.normed = emp((T, H))
         self.rstd = emp((T,), f32)
@@ -139,10 +144,13 @@ class ShardedStep:
         # targets of the update
         self.new = {}
         self.new_masters = {}
-        self.new_t = {}  # targets of the transposed copies (bf16 down weights)
+        # the transposed copies written with the update: name -> (target, rows, cols of the weight)
+        self.new_t = {}
         for s, sh in enumerate(self.shards):
-            if sh["w_down_t"] is not None:
-                self.new_t[f"w_down.{s}"] = torch.empty_like(sh["w_down_t"]) if self.oop else sh["w_down_t"]
+            for key, rows, cols in (("w_down", H, F), ("w_in", P, H)):
+                tt = sh[key + "_t"]
+                if tt is not None:
+                    self.new_t[f"{key}.{s}"] = (torch.empty_like(tt) if self.oop else tt, rows, cols)
         for name, t in self._param_list():
             self.new[name] = torch.empty_like(t) if self.oop else t
             if self.masters is not None:
@@ -220,7 +228,7 @@ class ShardedStep:
                           pre_act=sh["pre"][r], act=sh["act"][r], w_in=sh["w_in"], w_down=sh["w_down"],
                           d_out=d_out, d_pre=sh["d_pre"][r], d_w_in=sh["d_w_in"], d_b_in=sh["d_b_in"],
                           d_w_down=sh["d_w_down"], d_normed_part=sh["dN_part"][r], w_down_t=sh["w_down_t"],
-                          workspace=self.workspace)
+                          w_in_t=sh["w_in_t"], workspace=self.workspace)
 
     def _norm_backward(self, dN, d_out, dx, d_norm_w, d_b_down, r: slice = slice(None), flags: int = 0,
                        parts=None) -> None:
@@ -284,8 +292,8 @@ class ShardedStep:
                 e = (t, self.new[name], g, self.masters[name], self.new_masters[name], t.numel())
             else:
                 e = (t, self.new[name], g, None, None, t.numel())
-            if name in self.new_t:  # the down weight's transposed copy, written with it
-                e = e + (self.new_t[name], self.H, self.F)
+            if name in self.new_t:  # the weight's transposed copy, written with it
+                e = e + self.new_t[name]
             lst.append(e)
         L.tp_mlp_sgd_step_multi(lst, self.cdt, self.w.lr, stream=self.stream)
 
@@ -316,8 +324,8 @@ class ShardedStep:
             else:
                 lst.append((t, self.new[name], g, None, None, m, v, t.numel()))
         L.tp_mlp_adamw_step_multi(lst, self.cdt, hp, grad_scale=self.clip_coef, stream=self.stream)
-        for name, tt in self.new_t.items():  # the down weights' transposed copies follow the update
-            L.tp_mlp_transpose_bf16(self.new[name], tt, self.H, self.F, stream=self.stream)
+        for name, (tt, rows, cols) in self.new_t.items():  # the transposed copies follow the update
+            L.tp_mlp_transpose_bf16(self.new[name], tt, rows, cols, stream=self.stream)
 
     def step(self, mode: str = "equivalence", update: bool = True, microbatches: int = 1) -> None:
         """Forward, backward and (``update``) the SGD step.  With

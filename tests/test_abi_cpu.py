@@ -135,7 +135,7 @@ def test_backward_checks(lib):
     assert L.tp_mlp_workspace_bytes(_desc(T=0), L.BWD_SHARD) == 0
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t"):
             setattr(a, name, A)
     a.workspace_bytes = need - 16
     assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EWORKSPACE
@@ -286,7 +286,7 @@ def test_fp8_checks(lib):
                                   None) == L.OK
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t"):
             setattr(a, name, A)
     a.d_b_in = None
     a.workspace_bytes = 1 << 30
@@ -372,7 +372,7 @@ def test_attention_checks(lib):
     assert need >= 4 * 2 * 64 * 4                              # delta [n_q, T] at least
     a = L.tp_attn_bwd_args()
     for name, _ in L.tp_attn_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t"):
             setattr(a, name, A)
     a.workspace_bytes = need - 16
     assert lib.tp_attn_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EWORKSPACE
@@ -405,7 +405,7 @@ def test_backward_norm_parts_checks(lib):
     d = _desc(T=128)
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t"):
             setattr(a, name, A)
     a.workspace_bytes = L.tp_mlp_workspace_bytes(d, L.BWD_NORM)
     a.n_d_normed_parts = 65

@@ -456,32 +456,45 @@ def test_sgd_transposed_copy(rows, cols, masters):
     assert torch.equal(pt1, po1.view(rows, cols).t().contiguous())
 
 
-def test_backward_with_transposed_down_weight_bitwise():
+def test_backward_with_transposed_weights():
     """The SHARD phase given w_down_t gives the bits of the phase that
-    transposes w_down itself; after in-place SGD steps the step driver's copy
-    is still the transpose of the updated weight."""
+    transposes w_down itself.  Given w_in_t, the d_normed GEMM reads both
+    operands K-contiguous (another kernel, another order of the fp32 sums
+    within each k-step): dN_s agrees to fp32 rounding, every other output bit
+    for bit.  After in-place SGD steps the step driver's copies are still the
+    transposes of the updated weights."""
     from tensor_transformer_mlp_rmsnorm_amd import _lib as L
     from tensor_transformer_mlp_rmsnorm_amd.step import ShardedStep
     w = synth.Workload("wdt", tokens=300, hidden=256, ffn_full=384, shards=2, act="swiglu", dtype="bf16",
                        w_std=0.05, seed=31)
     t = synth.draw(w, perturb=True)
-    say("[gpu] backward with and without the transposed down weight")
+    say("[gpu] backward with and without the transposed weights")
     st = ShardedStep(w, t)
     st.forward()
     sh = st.shards[1]
     res = []
-    for wdt in (None, sh["w_down_t"]):
+    for wdt, wit in ((None, None), (sh["w_down_t"], None), (sh["w_down_t"], sh["w_in_t"])):
         o = {k: torch.full_like(sh[k], float("nan")) for k in ("d_pre", "d_w_in", "d_w_down", "dN_part")}
         L.tp_mlp_backward(st._desc(), L.BWD_SHARD, normed=st.normed, pre_act=sh["pre"], act=sh["act"],
                           w_in=sh["w_in"], w_down=sh["w_down"], d_out=st.out, d_pre=o["d_pre"], d_w_in=o["d_w_in"],
-                          d_w_down=o["d_w_down"], d_normed_part=o["dN_part"], w_down_t=wdt, workspace=st.workspace)
+                          d_w_down=o["d_w_down"], d_normed_part=o["dN_part"], w_down_t=wdt, w_in_t=wit,
+                          workspace=st.workspace)
         res.append(o)
     torch.cuda.synchronize()
     for k in res[0]:
         assert torch.equal(res[0][k], res[1][k]), k
+    for k in ("d_pre", "d_w_in", "d_w_down"):
+        assert torch.equal(res[1][k], res[2][k]), k
+    a, b = res[1]["dN_part"], res[2]["dN_part"]
+    assert not torch.isnan(b).any()
+    diff = (a - b).abs().max().item()
+    scale = a.abs().max().item()
+    say(f"  dN_s with w_in_t: max |diff| {diff:.3e} (max |dN_s| {scale:.3e}); bitwise: {torch.equal(a, b)}")
+    assert diff <= 2.0 ** -20 * scale
     st.backward()
-    st.sgd()  # in place: w_down and its transposed copy
+    st.sgd()  # in place: the weights and their transposed copies
     st.step()
     torch.cuda.synchronize()
     for shd in st.shards:
         assert torch.equal(shd["w_down_t"], shd["w_down"].t().contiguous())
+        assert torch.equal(shd["w_in_t"], shd["w_in"].reshape(-1, w.hidden).t().contiguous())
