@@ -458,10 +458,10 @@ def test_sgd_transposed_copy(rows, cols, masters):
 
 def test_backward_with_transposed_weights():
     """The SHARD phase given w_down_t gives the bits of the phase that
-    transposes w_down itself.  Given w_in_t, the d_normed GEMM reads both
-    operands K-contiguous (another kernel, another order of the fp32 sums
-    within each k-step): dN_s agrees to fp32 rounding, every other output bit
-    for bit.  After in-place SGD steps the step driver's copies are still the
+    transposes w_down itself, and given w_in_t (the d_normed GEMM then reads
+    both operands K-contiguous, on the ping-pong kernel) the bits of the phase
+    that reads w_in as it lies: each output sees the same sequence of MFMAs.
+    After in-place SGD steps the step driver's copies are still the
     transposes of the updated weights."""
     from tensor_transformer_mlp_rmsnorm_amd import _lib as L
     from tensor_transformer_mlp_rmsnorm_amd.step import ShardedStep
@@ -483,14 +483,8 @@ def test_backward_with_transposed_weights():
     torch.cuda.synchronize()
     for k in res[0]:
         assert torch.equal(res[0][k], res[1][k]), k
-    for k in ("d_pre", "d_w_in", "d_w_down"):
+    for k in res[1]:
         assert torch.equal(res[1][k], res[2][k]), k
-    a, b = res[1]["dN_part"], res[2]["dN_part"]
-    assert not torch.isnan(b).any()
-    diff = (a - b).abs().max().item()
-    scale = a.abs().max().item()
-    say(f"  dN_s with w_in_t: max |diff| {diff:.3e} (max |dN_s| {scale:.3e}); bitwise: {torch.equal(a, b)}")
-    assert diff <= 2.0 ** -20 * scale
     st.backward()
     st.sgd()  # in place: the weights and their transposed copies
     st.step()
