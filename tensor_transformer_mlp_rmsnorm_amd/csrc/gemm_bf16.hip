@@ -86,19 +86,24 @@ __device__ __forceinline__ int kc_index(int row, int chunk) { return row * 8 + (
 __device__ __forceinline__ int mn_swz(int k) { return ((k & 3) << 1) ^ (((k >> 3) & 1) << 3); }
 __device__ __forceinline__ int mn_index(int k, int chunk) { return k * 32 + (chunk ^ mn_swz(k)); }
 
-// Physical row of logical tile row r (or -1 outside the operand).
+// Physical row of logical tile row r (or -1 outside the operand).  SwiGLU B
+// tiles: each wave's 2 x chans rows are chans gate channels followed by the
+// same chans up channels (32 per wave in 256-row tiles, 56 in 224-row ones;
+// rows past the tile's `rows` are not loaded).
 struct RowMap {
   int64_t base, limit;
   bool swiglu;
   int64_t ffn;
+  int chans = 32, rows = 256;
   __device__ __forceinline__ int64_t operator()(int r) const {
     if (!swiglu) {
       const int64_t g = base + r;
       return g < limit ? g : -1;
     }
-    const int wave_n = r >> 6, w = r & 63;
-    const int64_t ch = base + wave_n * 32 + (w & 31);
-    return ch < ffn ? (w >> 5) * ffn + ch : -1;
+    if (r >= rows) return -1;
+    const int wave_n = r / (2 * chans), w = r - wave_n * 2 * chans;
+    const int64_t ch = base + wave_n * chans + (w < chans ? w : w - chans);
+    return ch < ffn ? (w < chans ? 0 : ffn) + ch : -1;
   }
 };
 
@@ -154,8 +159,11 @@ __device__ __forceinline__ void issue_tile(const Operand& op, uint4* __restrict_
 // for all lanes, goes in the instruction's SGPR offset.  A block that lies
 // wholly past the operand gets SGPR offset 0, so the sum stays below 2^31 and a
 // lane marked out of range (VGPR offset 0x80000000) stays out of range.
-template <bool SWIGLU, int EB = 2>
+// SwiGLU B tiles (CH channels per wave, RowMap's layout): every 8-row block is
+// 8 consecutive channels of one plane.
+template <bool SWIGLU, int EB = 2, int CH = 32>
 struct QuarterLoads {
+  static_assert(CH == 32 || CH == 56, "SwiGLU tiles of 4 x 32 or 2 x 56 channels");
   unsigned vbase;     // byte offset of this lane's chunk in block 0
   int left;           // rows (SwiGLU: channels) from this lane's block-0 row to the operand's end, clamped
   int k8;             // this lane's k offset inside the tile
@@ -165,8 +173,9 @@ struct QuarterLoads {
   __device__ __forceinline__ QuarterLoads(const Operand& op, const RowMap& rm, int q, int lane) {
     const int lr = lane >> 3;       // row inside an 8-row block
     const int c = (lane & 7) ^ lr;  // stored chunk: block rows start at multiples of 8
-    // SwiGLU: logical row 64 q + 8 i + lr is channel base + 32 q + 8 (i & 3) + lr of plane i >> 2
-    first_row = SWIGLU ? rm.base + 32 * q : rm.base + 64 * q;
+    // SwiGLU, 32 channels per wave: logical row 64 q + 8 i + lr is channel base + 32 q + 8 (i & 3) + lr
+    // of plane i >> 2; 56 per wave: channels are counted from the tile's base (see issue)
+    first_row = SWIGLU ? (CH == 32 ? rm.base + 32 * q : rm.base) : rm.base + 64 * q;
     lim = SWIGLU ? rm.ffn : rm.limit;
     const int64_t d = lim - (first_row + lr);
     left = d > (1 << 20) ? (1 << 20) : (d < -1 ? -1 : (int)d);
@@ -180,11 +189,21 @@ struct QuarterLoads {
     const bool kok = k0 + k8 < K;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int dr = SWIGLU ? 8 * (i & 3) : 8 * i;  // row step of block i within its plane
-      const int64_t plane = SWIGLU ? (i >> 2) * lim : 0;
-      const bool block_in = first_row + dr < lim;  // the same for all lanes
+      int dr;             // row (SwiGLU: channel) step of block i within its plane
+      int64_t plane = 0;  // SwiGLU: the plane's first row
+      bool used = true;   // 224-row tiles: blocks 28-31 are loaded as zeros (the load count stays fixed)
+      if constexpr (SWIGLU && CH == 56) {
+        const int b = 8 * q + i, wb = b % 14;  // block b: wave b / 14, plane wb / 7
+        dr = 56 * (b / 14) + 8 * (wb % 7);
+        plane = (wb / 7) * lim;
+        used = b < 28;
+      } else {
+        dr = SWIGLU ? 8 * (i & 3) : 8 * i;
+        plane = SWIGLU ? (i >> 2) * lim : 0;
+      }
+      const bool block_in = used && first_row + dr < lim;  // the same for all lanes
       const unsigned soff = block_in ? (unsigned)(((plane + dr) * op.ld + k0) * EB) : 0u;
-      const unsigned voff = (kok && dr < left) ? vbase : kOutOfRange;
+      const unsigned voff = (kok && used && dr < left) ? vbase : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (__attribute__((address_space(3))) void*)(dst + i * 64), 16,
                                                voff, (int)soff, 0, 0);
     }
@@ -338,6 +357,59 @@ __device__ __forceinline__ void epilogue_act_bwd(const GemmArgs& g, const floatx
 // Epilogue: acc holds this wave's (16 WMB) x (16 WNB) outputs from row m0 and
 // column n0 (SwiGLU forward: 32 channels from ch0, gate blocks then up blocks);
 // see the Epi enum.
+// SwiGLU forward on a 224-row B tile: a wave's 7 blocks of 16 B rows are 56
+// gate channels (blocks 0-2 and lane groups 0-1 of block 3) followed by the
+// same 56 up channels (lane groups 2-3 of block 3 and blocks 4-6).  Lane group
+// G of gate block j holds channels 16 j + 4 G .. + 3; their up values sit in
+// lane group G + 2 of block j + 3 (G < 2) or G - 2 of block j + 4 (G >= 2), 32
+// lanes away in the same row.  v_permlane32_swap of blocks j + 3 and j + 4
+// (the first operand's lanes 32-63 take the second's lanes 0-31 and the second's
+// lanes 0-31 take the first's lanes 32-63) brings both halves beside the gate
+// values.  Every lane runs the exchanges; only the stores are guarded.
+template <int WMB>
+__device__ __forceinline__ void epilogue_swiglu224(const GemmArgs& g, const floatx4 (&acc)[WMB][7], int64_t m0,
+                                                   int64_t ch0, int lane) {
+  const int64_t M = g.M, F = g.ffn;
+  const int G = lane >> 4, frow = lane & 15;
+  const bool lo = lane < 32;
+  auto swap = [](float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+#pragma unroll
+  for (int i = 0; i < WMB; ++i) {
+    const int64_t m = m0 + i * 16 + frow;
+    const bool mok = m < M;
+    // g and u are stored tensors: the activation is formed from their stored values
+    floatx4 sv[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) sv[j] = stored<bf16_t>(acc[i][j]);
+    bf16_t* pre = static_cast<bf16_t*>(g.pre) + m * 2 * F;
+    bf16_t* act = static_cast<bf16_t*>(g.act) + m * F;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      const int r = 16 * j + 4 * G;  // the wave's B row of this lane's first value
+      const int64_t ch = ch0 + (r < 56 ? r : r - 56);
+      if (mok && ch < F) store4<bf16_t>(pre + (r < 56 ? 0 : F) + ch, sv[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      floatx4 uv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // block 3's gate half (lanes 0-31) takes block 6's upper half
+        const float2 t = j < 3 ? swap(sv[j + 3][e], sv[j + 4][e]) : swap(sv[6][e], sv[6][e]);
+        uv[e] = lo ? t.y : t.x;
+      }
+      floatx4 av;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) av[e] = sv[j][e] * sigmoid_f(sv[j][e]) * uv[e];
+      const int64_t ch = ch0 + 16 * j + 4 * G;
+      if (mok && ch < F && (j < 3 || lo)) store4<bf16_t>(act + ch, av);
+    }
+  }
+}
+
 template <int EPI, int WMB, int WNB>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, const floatx4 (&acc)[WMB][WNB], int64_t m0, int64_t n0,
                                          int64_t ch0, int ks, int lane) {
@@ -345,6 +417,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const floatx4 (&acc)
     epilogue_act_bwd<EPI, WMB, WNB>(g, acc, m0, n0, lane);
     return;
   }
+  if constexpr (EPI == kEpiSwigluFwd && WNB == 7) {
+    epilogue_swiglu224<WMB>(g, acc, m0, ch0, lane);
+  } else {
   const int64_t M = g.M, N = g.N, F = g.ffn;
   asm volatile("" : "+v"(lane));  // addresses are formed here, not kept live through the main loop
   const int col4 = 4 * (lane >> 4), frow = lane & 15;
@@ -394,6 +469,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const floatx4 (&acc)
         }
       }
     }
+  }
   }
 }
 
@@ -565,14 +641,15 @@ template <int EPI, class OP, class PT = PpTile256>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs g, int ntm, int ntn) {
   extern __shared__ uint4 smem[];  // 5 operand slots = 160 KiB
   constexpr bool kSwiglu = EPI == kEpiSwigluFwd;
-  static_assert(!kSwiglu || PT::TN == 256, "the SwiGLU pairing uses 256-row B tiles of 128 channels");
+  // SwiGLU: channels per wave and per tile (256-row B tiles: 4 waves of 32; 224-row: 2 waves of 56)
+  constexpr int kWaveChans = PT::TN == 256 ? 32 : 56, kTileChans = PT::TN == 256 ? 128 : 112;
   constexpr int WMB = PT::WMB, WNB = PT::WNB;
   constexpr int EB = OP::kBytes;
   constexpr int kK = 128 / EB;  // k per tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3, q = wave & 3;
+  const int wm = wave >> 2, q = wave & 3;
 
   int tm, tn, ks;
   tile_coords(blockIdx.x, ntm, ntn, g.ksplit, tm, tn, ks);
@@ -581,7 +658,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
   const int64_t kbeg = (int64_t)ks * kper;
   const int64_t kend = K < kbeg + kper ? K : kbeg + kper;
   const RowMap ra{(int64_t)tm * kBM, g.M, false, 0};
-  const RowMap rb = kSwiglu ? RowMap{(int64_t)tn * kSwigluChannels, g.N, true, g.ffn}
+  const RowMap rb = kSwiglu ? RowMap{(int64_t)tn * kTileChans, g.N, true, g.ffn, kWaveChans, PT::TN}
                             : RowMap{(int64_t)tn * PT::TN, g.N, false, 0};
 
   floatx4 acc[WMB][WNB];
@@ -607,7 +684,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
   auto slot_bytes = [](int x) { return (unsigned)(slot_u4(x) * 16); };
   Frags<WMB, WNB> f;
   // group A loads B tiles, group B loads A tiles
-  QuarterLoads<kSwiglu, EB> lb(opb, rb, q, lane);
+  QuarterLoads<kSwiglu, EB, kWaveChans> lb(opb, rb, q, lane);
   QuarterLoads<false, EB> la(opa, ra, q, lane);
   if (wm == 0) {
     // phase 2j: read k-tile j, load B of k-tile j+1; phase 2j+1: multiply k-tile j
@@ -643,7 +720,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
       for (int j = 0; j < WNB; ++j) acc[i][j] *= deq;
   }
   epilogue<EPI, WMB, WNB>(g, acc, (int64_t)tm * kBM + PT::row0(wave), (int64_t)tn * PT::TN + PT::col0(wave),
-                          (int64_t)tn * kSwigluChannels + wn * 32, ks, lane);
+                          (int64_t)tn * kTileChans + (PT::col0(wave) / (2 * kWaveChans)) * kWaveChans, ks, lane);
 }
 
 template <bool AK, bool BKC, int EPI, class SH>
@@ -855,14 +932,13 @@ hipError_t launch_tiles(const GemmArgs& ga, int ntm, int ntn, hipStream_t s) {
   static_assert(!OP::kFp8 || (AK && BKC), "FP8 operands are K-contiguous");
   KernelTimer timer(ga.tag ? ga.tag : "gemm", s);
   if constexpr (AK && BKC) {
-    if constexpr (EPI != kEpiSwigluFwd) {
-      // 224-wide tiles when (rounds of one workgroup per CU) x (tile width) is smaller, as for the
-      // two-stage kernel's tile choice
-      const int64_t cus = device_cus(), ntn224 = (ga.N + 223) / 224;
-      const int64_t r256 = ((int64_t)ntm * ntn * ga.ksplit + cus - 1) / cus;
-      const int64_t r224 = ((int64_t)ntm * ntn224 * ga.ksplit + cus - 1) / cus;
-      if (r224 * 224 < r256 * 256) return launch_pingpong<EPI, OP, PpTile224>(ga, ntm, (int)ntn224, s);
-    }
+    // 224-wide tiles when (rounds of one workgroup per CU) x (tile width) is smaller, as for the
+    // two-stage kernel's tile choice (SwiGLU: 112 channels per tile instead of 128)
+    const int64_t cus = device_cus();
+    const int64_t ntn224 = EPI == kEpiSwigluFwd ? (ga.ffn + 111) / 112 : (ga.N + 223) / 224;
+    const int64_t r256 = ((int64_t)ntm * ntn * ga.ksplit + cus - 1) / cus;
+    const int64_t r224 = ((int64_t)ntm * ntn224 * ga.ksplit + cus - 1) / cus;
+    if (r224 * 224 < r256 * 256) return launch_pingpong<EPI, OP, PpTile224>(ga, ntm, (int)ntn224, s);
     return launch_pingpong<EPI, OP>(ga, ntm, ntn, s);
   } else {
     // the tile shape with the least (rounds of one workgroup per CU) x (tile area); a function of the
