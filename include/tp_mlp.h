@@ -115,6 +115,25 @@ int tp_mlp_forward(const tp_mlp_desc* d, const void* x, const void* norm_w, cons
                    void* pre_act, void* act, void* out, const void* b_down, void* stream);
 
 /*
+ * tp_mlp_forward_ws - tp_mlp_forward with a caller-owned workspace, which
+ * lets the down projection split its k range (F) over several workgroups per
+ * output tile when the GEMM has few tiles (bf16; a function of the shape
+ * only, so results are run-to-run identical): the slices are summed in index
+ * order in fp32, and with TP_MLP_FUSE_EPILOGUE the residual and bias are then
+ * added by tp_partial_sum's kernel (out = x + z + b_down).  The results equal
+ * tp_mlp_forward's up to the order of the fp32 additions.
+ *   workspace        device, 16-byte aligned, >= tp_mlp_forward_workspace_bytes(d)
+ *                    bytes (NULL allowed when that is 0)
+ * Errors: as tp_mlp_forward, and TP_MLP_EWORKSPACE when the workspace is
+ * smaller than needed (checked before any launch).
+ */
+size_t tp_mlp_forward_workspace_bytes(const tp_mlp_desc* d);
+int tp_mlp_forward_ws(const tp_mlp_desc* d, const void* x, const void* norm_w, const void* w_in,
+                      const void* b_in, const void* w_down, void* normed, float* rstd,
+                      void* pre_act, void* act, void* out, const void* b_down,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * tp_rmsnorm_forward - the RMSNorm of tp_mlp_forward on its own, for a
  * sequence-parallel rank's slice of the token rows ("Megatron-LM
  * walkthrough", Part V, "Deep dive: sequence parallelism": the norm runs on

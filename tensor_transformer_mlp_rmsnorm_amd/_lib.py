@@ -38,7 +38,7 @@ EXPORTED = ("tp_mlp_forward", "tp_partial_sum", "tp_mlp_backward", "tp_mlp_works
             "tp_mlp_backward_fp8", "tp_mlp_fp8_gemm", "tp_mlp_fp8_gemm_workspace_bytes", "tp_attn_forward",
             "tp_attn_backward", "tp_attn_workspace_bytes", "tp_attention_forward", "tp_attention_backward",
             "tp_attention_backward_workspace_bytes", "tp_mlp_profile_only", "tp_attn_forward_workspace_bytes",
-            "tp_mlp_backward_noalloc", "tp_mlp_transpose_bf16")
+            "tp_mlp_backward_noalloc", "tp_mlp_transpose_bf16", "tp_mlp_forward_ws", "tp_mlp_forward_workspace_bytes")
 
 
 class TPMLPError(RuntimeError):
@@ -114,6 +114,9 @@ def lib() -> ctypes.CDLL:
                                "`python -m tensor_transformer_mlp_rmsnorm_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         L.tp_mlp_forward.argtypes = [ctypes.POINTER(tp_mlp_desc)] + [_vp] * 12
+        L.tp_mlp_forward_ws.argtypes = [ctypes.POINTER(tp_mlp_desc)] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+        L.tp_mlp_forward_workspace_bytes.argtypes = [ctypes.POINTER(tp_mlp_desc)]
+        L.tp_mlp_forward_workspace_bytes.restype = ctypes.c_size_t
         L.tp_mlp_forward.restype = ctypes.c_int
         L.tp_partial_sum.argtypes = [ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, _vp, _vp,
                                      ctypes.c_int32, _vp, ctypes.c_int32, _vp]
@@ -228,6 +231,19 @@ def tp_mlp_forward(desc: tp_mlp_desc, x, norm_w, w_in, b_in, w_down, normed, rst
     _check(lib().tp_mlp_forward(ctypes.byref(desc), _ptr(x), _ptr(norm_w), _ptr(w_in), _ptr(b_in), _ptr(w_down),
                                 _ptr(normed), _ptr(rstd), _ptr(pre_act), _ptr(act), _ptr(out), _ptr(b_down),
                                 _stream(stream)))
+
+
+def tp_mlp_forward_ws(desc: tp_mlp_desc, x, norm_w, w_in, b_in, w_down, normed, rstd, pre_act, act, out,
+                      b_down=None, workspace=None, workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().tp_mlp_forward_ws(ctypes.byref(desc), _ptr(x), _ptr(norm_w), _ptr(w_in), _ptr(b_in), _ptr(w_down),
+                                   _ptr(normed), _ptr(rstd), _ptr(pre_act), _ptr(act), _ptr(out), _ptr(b_down),
+                                   _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def tp_mlp_forward_workspace_bytes(desc: tp_mlp_desc) -> int:
+    return int(lib().tp_mlp_forward_workspace_bytes(ctypes.byref(desc)))
 
 
 def tp_rmsnorm_forward(rows: int, hidden: int, dtype: int, eps: float, x, w, normed, rstd, stream=None) -> None:

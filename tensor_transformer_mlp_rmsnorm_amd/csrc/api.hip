@@ -81,10 +81,30 @@ const char* tp_mlp_last_error(void) { return g_err; }
 
 const char* tp_mlp_version(void) { return "libtpmlp 0.1 gfx950"; }
 
-int tp_mlp_forward(const tp_mlp_desc* d, const void* x, const void* norm_w, const void* w_in, const void* b_in,
-                   const void* w_down, void* normed, float* rstd, void* pre_act, void* act, void* out,
-                   const void* b_down, void* stream) {
-  const char* fn = "tp_mlp_forward";
+}  // extern "C"
+
+namespace {
+
+// k slices of the down projection (bf16, through the forward's workspace)
+int forward_ksplit(const tp_mlp_desc* d) {
+  if (d->dtype != TP_MLP_BF16 || d->tokens <= 0) return 1;
+  return gemm_ksplit(d->tokens, d->hidden, d->ffn_local);
+}
+
+size_t forward_ws_bytes(const tp_mlp_desc* d) {
+  const int ks = forward_ksplit(d);
+  if (ks <= 1) return 0;
+  const size_t th = (size_t)d->tokens * (size_t)d->hidden * sizeof(float);
+  // fused: z then the ks - 1 further slices; partial: the further slices (slice 0 writes out)
+  return (d->flags & TP_MLP_FUSE_EPILOGUE) ? (size_t)ks * th : (size_t)(ks - 1) * th;
+}
+
+// with_ws: tp_mlp_forward_ws (the down projection may split k through the workspace); otherwise
+// tp_mlp_forward, which never splits
+int forward_checked(const tp_mlp_desc* d, const void* x, const void* norm_w, const void* w_in, const void* b_in,
+                    const void* w_down, void* normed, float* rstd, void* pre_act, void* act, void* out,
+                    const void* b_down, bool with_ws, void* workspace, size_t workspace_bytes, void* stream,
+                    const char* fn) {
   g_err[0] = 0;
   int rc = check_desc(d, fn);
   if (rc) return rc;
@@ -106,6 +126,14 @@ int tp_mlp_forward(const tp_mlp_desc* d, const void* x, const void* norm_w, cons
   REQUIRE_PTR(out);
   const DType dt = dt_of(d->dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // the down projection's k split (tp_mlp_forward_ws only)
+  const int ks = with_ws ? forward_ksplit(d) : 1;
+  if (ks > 1) {
+    if (!workspace || workspace_bytes < forward_ws_bytes(d))
+      return fail(TP_MLP_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace ? workspace_bytes : 0,
+                  forward_ws_bytes(d));
+    REQUIRE_PTR(workspace);
+  }
 
   if (!(d->flags & TP_MLP_NORMED_READY))
     CHECK_HIP(launch_rmsnorm_fwd(dt, x, norm_w, normed, rstd, T, H, d->eps, s), "rmsnorm forward");
@@ -141,8 +169,47 @@ int tp_mlp_forward(const tp_mlp_desc* d, const void* x, const void* norm_w, cons
   c.bias = b_down;
   c.ffn = F;
   c.tag = fuse ? "gemm_down_residual" : "gemm_down_partial";
+  if (ks > 1) {
+    // k split: the slices go to the workspace and are added in index order
+    c.ksplit = ks;
+    if (fuse) {
+      float* z = static_cast<float*>(workspace);
+      c.C = z;
+      c.ws = z + T * H;
+      CHECK_HIP(launch_gemm(dt, true, true, kEpiStoreF32, c, s), "down GEMM");
+      const float* parts[1] = {z};
+      CHECK_HIP(launch_partial_sum(parts, 1, T, H, x, b_down, dt, out, dt, s), "residual and bias");
+    } else {
+      c.ws = static_cast<float*>(workspace);
+      CHECK_HIP(launch_gemm(dt, true, true, kEpiStoreF32, c, s), "down GEMM");
+    }
+    return TP_MLP_OK;
+  }
   CHECK_HIP(launch_gemm(dt, true, true, fuse ? kEpiResidual : kEpiStoreF32, c, s), "down GEMM");
   return TP_MLP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_mlp_forward(const tp_mlp_desc* d, const void* x, const void* norm_w, const void* w_in, const void* b_in,
+                   const void* w_down, void* normed, float* rstd, void* pre_act, void* act, void* out,
+                   const void* b_down, void* stream) {
+  return forward_checked(d, x, norm_w, w_in, b_in, w_down, normed, rstd, pre_act, act, out, b_down, false, nullptr, 0,
+                         stream, "tp_mlp_forward");
+}
+
+size_t tp_mlp_forward_workspace_bytes(const tp_mlp_desc* d) {
+  if (!d || d->tokens < 0 || d->hidden <= 0 || d->ffn_local <= 0) return 0;
+  return forward_ws_bytes(d);
+}
+
+int tp_mlp_forward_ws(const tp_mlp_desc* d, const void* x, const void* norm_w, const void* w_in, const void* b_in,
+                      const void* w_down, void* normed, float* rstd, void* pre_act, void* act, void* out,
+                      const void* b_down, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_checked(d, x, norm_w, w_in, b_in, w_down, normed, rstd, pre_act, act, out, b_down, true, workspace,
+                         workspace_bytes, stream, "tp_mlp_forward_ws");
 }
 
 int tp_partial_sum(const float* const* parts, int32_t n_parts, int64_t rows, int64_t cols, const void* residual,

@@ -6,7 +6,8 @@ all-reduces of the method become tp_partial_sum at the same two points
 ("Split the contraction" and "Put the other collective in backward",
 "Megatron tensor-parallel MLP", synapticradio.com):
 
-  forward   shard s: tp_mlp_forward -> fp32 partial z_s
+  forward   shard s: tp_mlp_forward_ws -> fp32 partial z_s (the down GEMM splits k through the
+            step's workspace where it has few tiles)
             out = tp_partial_sum(z_0..z_{S-1}) + x + b_down          (forward boundary)
   backward  shard s: tp_mlp_backward(SHARD, d_out = out) -> dN_s and the shard's weight grads
             tp_mlp_backward(NORM, d_normed_parts = dN_0..dN_{S-1})   (backward boundary: the sum
@@ -156,8 +157,10 @@ class ShardedStep:
             if self.masters is not None:
                 self.new_masters[name] = torch.empty_like(self.masters[name]) if self.oop else self.masters[name]
 
+        # one workspace for the forward's k-split slices and the backward's scratch (never in use together)
         ws = max(L.tp_mlp_workspace_bytes(self._desc(), L.BWD_NORM),
-                 L.tp_mlp_workspace_bytes(self._desc(), L.BWD_SHARD), 16)
+                 L.tp_mlp_workspace_bytes(self._desc(), L.BWD_SHARD),
+                 L.tp_mlp_forward_workspace_bytes(self._desc(L.FUSE_EPILOGUE if self.fuse else 0)), 16)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
         # AdamW state, allocated by the first adamw() call
         self.adam_m: Optional[Dict[str, torch.Tensor]] = None
@@ -203,9 +206,10 @@ class ShardedStep:
         st = self.stream
         for s, sh in enumerate(self.shards):
             flags = (L.NORMED_READY if s > 0 else 0) | (L.FUSE_EPILOGUE if self.fuse else 0)
-            L.tp_mlp_forward(self._desc(flags, T), self.x[r], self.norm_w, sh["w_in"], sh["b_in"], sh["w_down"],
-                             self.normed[r], self.rstd[r], sh["pre"][r], sh["act"][r],
-                             self.out[r] if self.fuse else sh["z"][r], self.b_down, stream=st)
+            L.tp_mlp_forward_ws(self._desc(flags, T), self.x[r], self.norm_w, sh["w_in"], sh["b_in"], sh["w_down"],
+                                self.normed[r], self.rstd[r], sh["pre"][r], sh["act"][r],
+                                self.out[r] if self.fuse else sh["z"][r], self.b_down, workspace=self.workspace,
+                                stream=st)
         if self.fuse:
             return
         if rows is not None:
@@ -428,8 +432,9 @@ class SequenceParallelStep(ShardedStep):
                                  self.rstd[lo:hi], stream=st)
         for sh in self.shards:
             flags = L.NORMED_READY | (L.FUSE_EPILOGUE if self.fuse else 0)
-            L.tp_mlp_forward(self._desc(flags), self.x, self.norm_w, sh["w_in"], sh["b_in"], sh["w_down"], self.normed,
-                             self.rstd, sh["pre"], sh["act"], self.out if self.fuse else sh["z"], self.b_down, stream=st)
+            L.tp_mlp_forward_ws(self._desc(flags), self.x, self.norm_w, sh["w_in"], sh["b_in"], sh["w_down"],
+                                self.normed, self.rstd, sh["pre"], sh["act"], self.out if self.fuse else sh["z"],
+                                self.b_down, workspace=self.workspace, stream=st)
         if self.fuse:
             return
         for lo, hi in self.slices:

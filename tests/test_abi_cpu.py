@@ -95,6 +95,28 @@ def test_forward_rejects_bad_descriptor(lib, kw, code):
     assert L.tp_mlp_last_error() != ""
 
 
+def test_forward_workspace_bytes(lib):
+    """The down projection splits k through the forward's workspace only when
+    it has few tiles (bf16): the GPT-2-small shape does, the Llama shapes and
+    fp32 do not; fused, z and the further slices; partial, the further slices."""
+    kb = lambda **kw: L.tp_mlp_forward_workspace_bytes(_desc(**kw))
+    T, H, F = 4096, 768, 3072  # 48 tiles of 256 x 256, k 3072: 3 slices
+    assert kb(T=T, H=H, F=F, act=L.ACT_GELU, flags=L.FUSE_EPILOGUE) == 3 * T * H * 4
+    assert kb(T=T, H=H, F=F, act=L.ACT_GELU) == 2 * T * H * 4
+    assert kb(T=T, H=H, F=F, act=L.ACT_GELU, dt=L.F32) == 0
+    assert kb(T=8192, H=4096, F=1792) == 0
+    assert kb(T=0, H=H, F=F) == 0
+
+
+def test_forward_ws_rejects_small_workspace(lib):
+    d = _desc(T=4096, H=768, F=3072, act=L.ACT_GELU, flags=L.FUSE_EPILOGUE)
+    need = L.tp_mlp_forward_workspace_bytes(d)
+    args = (A, A, A, A, A, A, A, A, A, A, A)  # x .. b_down (b_in given: GeLU)
+    assert lib.tp_mlp_forward_ws(ctypes.byref(d), *args, A, need - 16, None) == L.EWORKSPACE
+    assert "workspace" in L.tp_mlp_last_error()
+    assert lib.tp_mlp_forward_ws(ctypes.byref(d), *args, None, 0, None) == L.EWORKSPACE
+
+
 def test_forward_pointer_checks(lib):
     assert lib.tp_mlp_forward(None, *([A] * 11), None) == L.EINVAL
     assert _fwd(_desc(), x=None) == L.EINVAL

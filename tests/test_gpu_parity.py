@@ -344,29 +344,33 @@ def test_rmsnorm_forward_fp32_wide_rows(H):
     check("rstd", rstd.cpu(), rr, "fp32")
 
 
-# Weight-gradient and input-gradient GEMMs that split k over 2, 3, 4, 5 and 7
-# workgroups per tile (a function of the shape: tiles of 256 x 256 and k), with
-# a k that does not divide into whole 64-wide steps per slice, checked stage by
-# stage over every element (one step with S = 1, and one run as 2 microbatches
-# whose weight gradients accumulate into the split GEMMs' outputs).
+# Weight-gradient, input-gradient and down-projection GEMMs that split k over
+# 2, 3, 4, 5 and 7 workgroups per tile (a function of the shape: tiles of
+# 256 x 256 and k), with a k that does not divide into whole 64-wide steps per
+# slice, checked stage by stage over every element (steps with S = 1, where the
+# forward's slices are summed and the residual added after them, one with
+# S = 2, where they form the fp32 partial, and one run as 2 microbatches whose
+# weight gradients accumulate into the split GEMMs' outputs).
 KSPLIT = [
-    # name, T, H, F, microbatches   (slices: d_w_down, d_w_in, dN)
-    ("ks5_2_2", 8192, 768, 4096, 1),
-    ("ks5_2_3_ragged_k", 7000, 768, 4096, 1),
-    ("ks7_3_2", 7300, 768, 3072, 1),
-    ("ks3_1_5", 4000, 768, 6144, 1),
-    ("ks7_4_2_accumulate", 8000, 1024, 2048, 2),
+    # name, T, H, F_full, microbatches, shards   (slices: d_w_down, d_w_in, dN; the down GEMM of the forward splits
+    # too where it has few tiles -- fused with the residual for one shard, into the fp32 partial for two)
+    ("ks5_2_2", 8192, 768, 4096, 1, 1),
+    ("ks5_2_3_ragged_k", 7000, 768, 4096, 1, 1),
+    ("ks7_3_2", 7300, 768, 3072, 1, 1),
+    ("ks3_1_5", 4000, 768, 6144, 1, 1),
+    ("ks7_4_2_accumulate", 8000, 1024, 2048, 2, 1),
+    ("ks4_2_5_fwd4_two_shards", 4096, 768, 8192, 1, 2),
 ]
 
 
 @pytest.mark.parametrize("case", KSPLIT, ids=[c[0] for c in KSPLIT])
 def test_ksplit_gemms_stagewise(case):
     from tensor_transformer_mlp_rmsnorm_amd.step import ShardedStep
-    name, T, H, F, mb = case
-    w = synth.Workload(name, tokens=T, hidden=H, ffn_full=F, shards=1, act="swiglu", dtype="bf16", w_std=0.03,
+    name, T, H, F, mb, S = case
+    w = synth.Workload(name, tokens=T, hidden=H, ffn_full=F, shards=S, act="swiglu", dtype="bf16", w_std=0.03,
                        seed=T + F)
     t = synth.draw(w, perturb=True)
-    say(f"[gpu] k-split {name} T={T} H={H} F={F} microbatches={mb}")
+    say(f"[gpu] k-split {name} T={T} H={H} F={F} S={S} microbatches={mb}")
     st = ShardedStep(w, t, out_of_place_sgd=True)
     st.step(microbatches=mb)
     torch.cuda.synchronize()
