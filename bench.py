@@ -294,6 +294,21 @@ def attention_flops(aw) -> dict:
             "attention_fwd": 2 * pd, "attention_bwd_dkdv": 3 * pd, "attention_bwd_dq": pd}
 
 
+def attention_hbm_bytes(aw) -> dict:
+    """Algorithmic HBM bytes per step of the attention step's bandwidth-bound
+    kernels (bf16 storage): the RMSNorm forward and backward, the two boundary
+    sums and the SGD over every shard's parameters, by kernel name."""
+    T, H, S = aw.tokens, aw.hidden, aw.shards
+    w_qkv = (aw.n_q + 2 * aw.n_kv) * aw.d * H  # all shards' rows of the fused projection
+    w_o = H * aw.n_q * aw.d
+    n_params = 2 * H + w_qkv + w_o
+    return {"rmsnorm_fwd": T * H * 2 * 2 + 4 * T + 2 * H,
+            "partial_sum_residual": S * 4 * T * H + 2 * 2 * T * H + 2 * H,
+            "partial_sum": S * 4 * T * H + 4 * T * H,
+            "rmsnorm_bwd": T * H * (4 + 3 * 2) + 4 * T + 2 * H,
+            "sgd": n_params * (2 + 4 + 2)}
+
+
 def attention_path(steps: int, warmup: int, name: str = "attn_llama3_8b_tp8") -> dict:
     """The tensor-parallel attention sublayer's step (forward, backward, SGD
     over all shards in sequence) on the Llama-3-8B TP=8 attention shape: its
@@ -322,13 +337,17 @@ def attention_path(steps: int, warmup: int, name: str = "attn_llama3_8b_tp8") ->
     prof = L.tp_mlp_profile_entries()
     del st
     torch.cuda.empty_cache()
-    fl = attention_flops(aw)
+    fl, by = attention_flops(aw), attention_hbm_bytes(aw)
     kernels = {}
     for k, (n, tot) in prof.items():
         if k in fl:
             ach = fl[k] * n / (tot / 1e3) / 1e12
             kernels[k] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                           "frac": ach / PEAK_BF16_TFLOPS, "per_launch": fl[k], "avg_ms": tot / n, "launches": n}
+        elif k in by:  # one launch per step
+            ach = by[k] * n / (tot / 1e3) / 1e9
+            kernels[k] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": ach / PEAK_HBM_GBS, "per_launch": by[k], "avg_ms": tot / n, "launches": n}
         else:
             kernels[k] = {"bound": None, "avg_ms": tot / n, "launches": n}
     return {"workload": name, "batch": aw.batch, "seq": aw.seq, "hidden": aw.hidden, "n_q": aw.n_q, "n_kv": aw.n_kv,
