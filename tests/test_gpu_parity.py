@@ -151,8 +151,8 @@ SMALL = [
     ("bf16_gelu_ragged_S1", 333, 192, 520, 1, "gelu", "bf16"),
     ("bf16_gelu_S2", 129, 264, 272, 2, "gelu", "bf16"),
     ("bf16_swiglu_S8_thin", 65, 64, 128, 8, "swiglu", "bf16"),
-    # more than one round of tiles per CU: the input-gradient GEMM takes the 16-wave 256 x 256 tile,
-    # ragged in M, N and K; a wide shape: act, dN and dx held stage-wise
+    # more than one round of tiles per CU, ragged in M, N and K (H = 4000); a wide shape: act, dN and dx
+    # held stage-wise
     ("bf16_swiglu_wide_ragged_S1", 8000, 4000, 136, 1, "swiglu", "bf16"),
 ]
 WIDE = {"bf16_swiglu_wide_ragged_S1"}
