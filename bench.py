@@ -35,6 +35,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -505,6 +506,15 @@ def main() -> int:
     prof_dom = L.tp_mlp_profile_entries()
 
     ms = elapsed / args.steps * 1e3
+    # Per-step times from a separate pass with an event pair around each step: their median and
+    # minimum, beside the mean over the K steps timed as one block above (which is `ms_per_step`).
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in pairs:
+        a.record()
+        st.step()
+        b.record()
+    torch.cuda.synchronize()
+    per_step = [a.elapsed_time(b) for a, b in pairs]
     flops = w.flops_per_step
     tflops = flops / (ms / 1e3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -524,6 +534,7 @@ def main() -> int:
                    "ffn_full": w.ffn_full, "ffn_local": w.ffn_local, "shards": w.shards, "shards_run": w.n_run,
                    "act": w.act, "parallelism": f"tp{w.shards} emulated: shards in sequence on one GPU"},
         "pct_of_bf16_peak": 100.0 * tflops / peak,
+        "step_ms_median": statistics.median(per_step), "step_ms_min": min(per_step),
         "tokens_per_s": w.tokens / (ms / 1e3),
         "shard_tokens_per_s": w.tokens / (ms / 1e3 / w.n_run),
         "flops_per_step": flops,
