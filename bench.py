@@ -297,8 +297,10 @@ def attention_flops(aw) -> dict:
 
 def attention_hbm_bytes(aw) -> dict:
     """Algorithmic HBM bytes per step of the attention step's bandwidth-bound
-    kernels (bf16 storage): the RMSNorm forward and backward, the two boundary
-    sums and the SGD over every shard's parameters, by kernel name."""
+    kernels (bf16 storage): the RMSNorm forward, the forward boundary sum, the
+    RMSNorm backward with the backward boundary streamed into it (a separate
+    dN sum only in the ablation modes) and the SGD over every shard's
+    parameters, by kernel name."""
     T, H, S = aw.tokens, aw.hidden, aw.shards
     w_qkv = (aw.n_q + 2 * aw.n_kv) * aw.d * H  # all shards' rows of the fused projection
     w_o = H * aw.n_q * aw.d
@@ -306,7 +308,8 @@ def attention_hbm_bytes(aw) -> dict:
     return {"rmsnorm_fwd": T * H * 2 * 2 + 4 * T + 2 * H,
             "partial_sum_residual": S * 4 * T * H + 2 * 2 * T * H + 2 * H,
             "partial_sum": S * 4 * T * H + 4 * T * H,
-            "rmsnorm_bwd": T * H * (4 + 3 * 2) + 4 * T + 2 * H,
+            # the S fp32 partials of dN (summed as they are read), x, dY in, dx out
+            "rmsnorm_bwd": T * H * (4 * S + 3 * 2) + 4 * T + 2 * H,
             "sgd": n_params * (2 + 4 + 2)}
 
 

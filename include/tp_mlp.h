@@ -597,6 +597,15 @@ typedef struct {
   float* d_b_o;            /* [H] fp32 */
   void* workspace;
   size_t workspace_bytes;
+  /* NORM phase, instead of d_normed: the shards' partials of dL/dN
+     (d_normed_part of each SHARD call), summed by the RMSNorm backward as it
+     reads them -- in index order with fp32 additions, the sum tp_partial_sum
+     forms, so the results are the same bits.  A HOST array of
+     n_d_normed_parts DEVICE pointers, each [T, H] fp32,
+     1 <= n_d_normed_parts <= 64.  n_d_normed_parts = 0 (as in
+     zero-initialised args): d_normed is read. */
+  const float* const* d_normed_parts;
+  int32_t n_d_normed_parts;
 } tp_attn_bwd_args;
 
 /*
@@ -604,7 +613,8 @@ typedef struct {
  * tp_mlp_backward.  SHARD: dO = d_out W_o; d_w_o = d_out^T O; the attention
  * backward (dS = P (dP - rowsum(dO o O)), P recomputed from lse) gives
  * d_qkv; d_w_qkv = d_qkv^T N; d_normed_part = d_qkv W_qkv.  NORM: RMSNorm's
- * backward with the residual, d_norm_w and d_b_o = sum_t d_out.
+ * backward with the residual, d_norm_w and d_b_o = sum_t d_out, on dN given
+ * summed (d_normed) or as the shards' partials (d_normed_parts).
  * Workspace: tp_attn_workspace_bytes(d, phase).  Deterministic.
  */
 int tp_attn_backward(const tp_attn_desc* d, int32_t phase, const tp_attn_bwd_args* a, void* stream);

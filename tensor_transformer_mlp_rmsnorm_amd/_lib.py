@@ -99,7 +99,8 @@ class tp_attn_desc(ctypes.Structure):
 class tp_attn_bwd_args(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("x", "normed", "rstd", "qkv", "attn_out", "lse", "norm_w", "w_qkv", "w_o", "d_out",
                                    "d_attn_out", "d_qkv", "d_w_qkv", "d_w_o", "d_normed_part", "d_normed", "d_x",
-                                   "d_norm_w", "d_b_o", "workspace")] + [("workspace_bytes", ctypes.c_size_t)]
+                                   "d_norm_w", "d_b_o", "workspace")] + [("workspace_bytes", ctypes.c_size_t)] + \
+        [("d_normed_parts", ctypes.POINTER(_vp)), ("n_d_normed_parts", ctypes.c_int32)]
 
 
 _LIB: Optional[ctypes.CDLL] = None
@@ -378,10 +379,17 @@ def tp_attn_workspace_bytes(desc: tp_attn_desc, phase: int) -> int:
 
 
 def tp_attn_backward(desc: tp_attn_desc, phase: int, stream=None, **tensors) -> None:
-    """``tensors``: the fields of tp_attn_bwd_args (torch tensors or None)."""
+    """``tensors``: the fields of tp_attn_bwd_args (torch tensors or None);
+    ``d_normed_parts`` may be a sequence of tensors (the NORM phase then sums them)."""
     a = tp_attn_bwd_args()
+    parts = tensors.pop("d_normed_parts", None)
+    if parts:
+        arr = (_vp * len(parts))(*[_ptr(p) for p in parts])
+        a._parts_keepalive = arr
+        a.d_normed_parts = ctypes.cast(arr, ctypes.POINTER(_vp))
+        a.n_d_normed_parts = len(parts)
     for name, _ in tp_attn_bwd_args._fields_:
-        if name == "workspace_bytes":
+        if name in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts"):
             continue
         v = tensors.pop(name, None)
         setattr(a, name, _ptr(v))

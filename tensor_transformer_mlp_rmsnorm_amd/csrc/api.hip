@@ -1188,16 +1188,28 @@ int tp_attn_backward(const tp_attn_desc* d, int32_t phase, const tp_attn_bwd_arg
     REQUIRE_PTR(a->norm_w);
     REQUIRE_PTR(a->d_norm_w);
     REQUIRE_PTR(a->d_b_o);
+    const int np = a->n_d_normed_parts;
+    if (np < 0 || np > kMaxNormParts)
+      return fail(TP_MLP_EINVAL, "%s: n_d_normed_parts must be in [0, %d]", fn, kMaxNormParts);
+    if (np > 0 && !a->d_normed_parts) return fail(TP_MLP_EINVAL, "%s: d_normed_parts is NULL", fn);
+    const float* dn_one[1] = {a->d_normed};
+    const float* const* parts = np > 0 ? a->d_normed_parts : dn_one;
     if (T > 0) {
-      REQUIRE_PTR(a->d_normed);
+      if (np > 0) {
+        for (int k = 0; k < np; ++k) {
+          const float* part = parts[k];
+          REQUIRE_PTR(part);
+        }
+      } else {
+        REQUIRE_PTR(a->d_normed);
+      }
       REQUIRE_PTR(a->x);
       REQUIRE_PTR(a->d_out);
       REQUIRE_PTR4(a->rstd);
       REQUIRE_PTR(a->d_x);
     }
-    const float* const dn_one[1] = {a->d_normed};
-    CHECK_HIP(launch_rmsnorm_bwd(kBF16, dn_one, 1, a->x, a->d_out, a->rstd, a->norm_w, a->d_x, a->d_norm_w, a->d_b_o,
-                                 a->workspace, T, H, accum, s),
+    CHECK_HIP(launch_rmsnorm_bwd(kBF16, parts, np > 0 ? np : 1, a->x, a->d_out, a->rstd, a->norm_w, a->d_x,
+                                 a->d_norm_w, a->d_b_o, a->workspace, T, H, accum, s),
               "rmsnorm backward");
     return TP_MLP_OK;
   }

@@ -583,7 +583,8 @@ class AttnStep:
       forward   shard s: tp_attn_forward -> fp32 partial z_s
                 out = tp_partial_sum(z_0..z_{S-1}) + x + b_o
       backward  shard s: tp_attn_backward(SHARD, d_out = out) -> dN_s, its weight grads
-                dN = tp_partial_sum(dN_0..dN_{S-1}); tp_attn_backward(NORM) -> dx, d_norm_w, d_b_o
+                tp_attn_backward(NORM, d_normed_parts = dN_0..dN_{S-1}) -> dx, d_norm_w, d_b_o
+                (the backward boundary: the partials summed as the RMSNorm backward reads them)
       update    tp_mlp_sgd_step_multi over every parameter tensor
 
     Shard r owns query heads [r n_q/S, (r+1) n_q/S) and key/value heads
@@ -622,6 +623,8 @@ class AttnStep:
             self.shards.append(sh)
         self.normed, self.rstd, self.out = emp((T, H)), emp((T,), f32), emp((T, H))
         self.dN = self.shards[0]["dN_part"] if self.fuse else emp((T, H), f32)
+        # the last backward summed dN inside the RMSNorm backward (dN's buffer not written)
+        self._dN_streamed = False
         self.dx, self.d_norm_w, self.d_b_o = emp((T, H)), emp((H,), f32), emp((H,), f32)
         self.new = {name: (torch.empty_like(t) if self.oop else t) for name, t in self._param_list()}
         d0 = self._desc()
@@ -673,9 +676,21 @@ class AttnStep:
                            d_attn_out=sh["d_attn_out"], d_qkv=sh["d_qkv"], d_w_qkv=sh["d_w_qkv"], d_w_o=sh["d_w_o"],
                            d_normed_part=sh["dN_part"], workspace=self.workspace)
 
-    def _norm_backward(self, dN, d_out, dx, d_norm_w, d_b_o) -> None:
+    def _norm_backward(self, dN, d_out, dx, d_norm_w, d_b_o, parts=None) -> None:
+        """The NORM phase on the summed dN, or with ``parts`` (the shards'
+        partials of dN) summed by the RMSNorm backward as it reads them."""
+        kw = dict(d_normed_parts=parts) if parts else dict(d_normed=dN)
         L.tp_attn_backward(self._desc(), L.BWD_NORM, stream=self.stream, x=self.x, rstd=self.rstd, norm_w=self.norm_w,
-                           d_out=d_out, d_normed=dN, d_x=dx, d_norm_w=d_norm_w, d_b_o=d_b_o, workspace=self.workspace)
+                           d_out=d_out, d_x=dx, d_norm_w=d_norm_w, d_b_o=d_b_o, workspace=self.workspace, **kw)
+
+    def materialize_dN(self) -> None:
+        """Write the summed dN into its buffer when the step streamed the
+        shards' partials into the RMSNorm backward instead (tp_partial_sum:
+        the same sum, in the same order, so the same bits the backward used)."""
+        if self._dN_streamed:
+            L.tp_partial_sum([sh["dN_part"] for sh in self.shards], self.T, self.H, None, None, L.F32, self.dN, L.F32,
+                             stream=self.stream)
+        self._dN_streamed = False
 
     def backward(self, mode: str = "equivalence") -> None:
         T, H = self.T, self.H
@@ -683,12 +698,15 @@ class AttnStep:
         outs = self._abl["out"] if fwd_abl else [self.out] * len(self.shards)
         for sh, o in zip(self.shards, outs):
             self._shard_backward(sh, o)
-        if not self.fuse and mode != "missing_backward_reduce":
+        if mode == "equivalence" or self.fuse:
+            # the backward boundary: the shards' partials summed inside the RMSNorm backward
+            parts = None if self.fuse else [sh["dN_part"] for sh in self.shards]
+            self._norm_backward(self.dN, self.out, self.dx, self.d_norm_w, self.d_b_o, parts=parts)
+            self._dN_streamed = not self.fuse
+            return
+        if mode != "missing_backward_reduce":
             L.tp_partial_sum([sh["dN_part"] for sh in self.shards], T, H, None, None, L.F32, self.dN, L.F32,
                              stream=self.stream)
-        if mode == "equivalence" or self.fuse:
-            self._norm_backward(self.dN, self.out, self.dx, self.d_norm_w, self.d_b_o)
-            return
         dxs = self._abl_bufs("dx", (T, H), torch.bfloat16)
         dws = self._abl_bufs("d_norm_w", (H,), torch.float32)
         dbs = self._abl_bufs("d_b_o", (H,), torch.float32)
@@ -709,6 +727,7 @@ class AttnStep:
 
     def results(self, mode: str = "equivalence") -> dict:
         """CPU copies (float32) with the shards' slices placed back into the dense w_qkv rows and w_o columns."""
+        self.materialize_dN()
         c = lambda t: t.detach().float().cpu()
         w, D = self.w, self.D
         W_full = (w.n_q + 2 * w.n_kv) * D

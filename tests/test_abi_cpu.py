@@ -445,6 +445,31 @@ def test_backward_norm_parts_checks(lib):
     assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EALIGN
 
 
+def test_attn_backward_norm_parts_checks(lib):
+    """The attention NORM phase's streamed partials are checked as the MLP's:
+    count in [0, 64], a non-NULL array when the count is positive, every part
+    non-NULL and aligned; all before any launch."""
+    d = L.make_attn_desc(2, 64, 256, 4, 2, 64, 1e-6)
+    a = L.tp_attn_bwd_args()
+    for name, _ in L.tp_attn_bwd_args._fields_:
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts"):
+            setattr(a, name, A)
+    a.workspace_bytes = lib.tp_attn_workspace_bytes(ctypes.byref(d), L.BWD_NORM)
+    a.n_d_normed_parts = 65
+    assert lib.tp_attn_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EINVAL
+    a.n_d_normed_parts = -1
+    assert lib.tp_attn_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EINVAL
+    a.n_d_normed_parts = 2
+    assert lib.tp_attn_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EINVAL  # NULL array
+    arr = (ctypes.c_void_p * 2)(A, None)
+    a.d_normed_parts = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    assert lib.tp_attn_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EINVAL
+    assert b"part" in lib.tp_mlp_last_error()
+    arr2 = (ctypes.c_void_p * 2)(A, MIS)
+    a.d_normed_parts = ctypes.cast(arr2, ctypes.POINTER(ctypes.c_void_p))
+    assert lib.tp_attn_backward(ctypes.byref(d), L.BWD_NORM, ctypes.byref(a), None) == L.EALIGN
+
+
 def test_sgd_transposed_copy_checks(lib):
     """The SGD tensor's transposed copy: bf16 only, t_rows x t_cols == n with
     both multiples of 8, an aligned pointer; and tp_mlp_transpose_bf16's
