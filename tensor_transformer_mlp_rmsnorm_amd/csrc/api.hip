@@ -403,7 +403,29 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
   b2.accum = accum;
   CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b2, s), "d_w_down GEMM");
 
-  // d_normed partial = d_pre w_in ([T,P] x [P,H]).
+  // d_w_in = d_pre^T normed ([P,T] x [T,H]).
+  GemmArgs b4{};
+  b4.M = P;
+  b4.N = H;
+  b4.K = T;
+  b4.A = a->d_pre;
+  b4.lda = P;
+  b4.B = a->normed;
+  b4.ldb = H;
+  b4.C = a->d_w_in;
+  b4.ldc = H;
+  b4.tag = swiglu ? "gemm_wgrad_gate_up" : "gemm_wgrad_fc1";
+  b4.ksplit = gemm_ksplit(b4.M, b4.N, b4.K);
+  b4.ws = static_cast<float*>(a->workspace);
+  b4.accum = accum;
+  CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b4, s), "d_w_in GEMM");
+
+  if (!swiglu)
+    CHECK_HIP(launch_colsum(dt, a->d_pre, a->d_b_in, a->workspace, T, F, accum, s), "d_b_in column sum");
+
+  // d_normed partial = d_pre w_in ([T,P] x [P,H]), last: the norm backward
+  // that follows the last shard reads this partial while it is still in the
+  // memory-side cache, instead of evicting a weight gradient written after it.
   GemmArgs b3{};
   b3.M = T;
   b3.N = H;
@@ -424,26 +446,6 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
   } else {
     CHECK_HIP(launch_gemm(dt, true, false, kEpiStoreF32, b3, s), "d_normed GEMM");
   }
-
-  // d_w_in = d_pre^T normed ([P,T] x [T,H]).
-  GemmArgs b4{};
-  b4.M = P;
-  b4.N = H;
-  b4.K = T;
-  b4.A = a->d_pre;
-  b4.lda = P;
-  b4.B = a->normed;
-  b4.ldb = H;
-  b4.C = a->d_w_in;
-  b4.ldc = H;
-  b4.tag = swiglu ? "gemm_wgrad_gate_up" : "gemm_wgrad_fc1";
-  b4.ksplit = gemm_ksplit(b4.M, b4.N, b4.K);
-  b4.ws = static_cast<float*>(a->workspace);
-  b4.accum = accum;
-  CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b4, s), "d_w_in GEMM");
-
-  if (!swiglu)
-    CHECK_HIP(launch_colsum(dt, a->d_pre, a->d_b_in, a->workspace, T, F, accum, s), "d_b_in column sum");
   return TP_MLP_OK;
 }
 
@@ -991,15 +993,6 @@ int tp_mlp_backward_fp8(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_ar
                             "fp8_cast_d_pre", s),
             "d_pre cast");
 
-  // d_normed partial = d_pre w_in on d_pre_q [T, P] and w_in_t [H, P].
-  GemmArgs b3 = fp8_gemm(T, H, P, f8->d_pre_q, P, f8->meta_d_pre, f8->w_in_t, P, f8->meta_w_in,
-                         "gemm_dgrad_normed_fp8");
-  b3.C = a->d_normed_part;
-  b3.ldc = H;
-  b3.ksplit = gemm_ksplit(b3.M, b3.N, b3.K);
-  b3.ws = static_cast<float*>(a->workspace);
-  CHECK_HIP(launch_gemm_fp8(kFp8E5M2, kFp8E4M3, kEpiStoreF32, b3, s), "d_normed GEMM");
-
   // d_w_in = d_pre^T normed on d_pre_t [P, Tp] and normed_t [H, Tp].
   GemmArgs b4 = fp8_gemm(P, H, Tp, f8->d_pre_t, Tp, f8->meta_d_pre, f8->normed_t, Tp, f8->meta_normed,
                          swiglu ? "gemm_wgrad_gate_up_fp8" : "gemm_wgrad_fc1_fp8");
@@ -1012,6 +1005,16 @@ int tp_mlp_backward_fp8(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_ar
 
   if (!swiglu)
     CHECK_HIP(launch_colsum(kBF16, a->d_pre, a->d_b_in, a->workspace, T, F, accum, s), "d_b_in column sum");
+
+  // d_normed partial = d_pre w_in on d_pre_q [T, P] and w_in_t [H, P]; last, as in
+  // the bf16 backward (the norm backward then reads it from the memory-side cache).
+  GemmArgs b3 = fp8_gemm(T, H, P, f8->d_pre_q, P, f8->meta_d_pre, f8->w_in_t, P, f8->meta_w_in,
+                         "gemm_dgrad_normed_fp8");
+  b3.C = a->d_normed_part;
+  b3.ldc = H;
+  b3.ksplit = gemm_ksplit(b3.M, b3.N, b3.K);
+  b3.ws = static_cast<float*>(a->workspace);
+  CHECK_HIP(launch_gemm_fp8(kFp8E5M2, kFp8E4M3, kEpiStoreF32, b3, s), "d_normed GEMM");
   return TP_MLP_OK;
 }
 
@@ -1263,19 +1266,6 @@ int tp_attn_backward(const tp_attn_desc* d, int32_t phase, const tp_attn_bwd_arg
   CHECK_HIP(launch_gemm_bf16(false, false, kEpiStoreF32, b2, s), "d_w_o GEMM");
   CHECK_HIP(launch_attention_bwd(attn_args(d), a->qkv, a->attn_out, a->d_attn_out, a->lse, attn_ws, a->d_qkv, s),
             "attention backward");
-  // d_normed partial = d_qkv W_qkv ([T, W] x [W, H])
-  GemmArgs b3{};
-  b3.M = T;
-  b3.N = H;
-  b3.K = W;
-  b3.A = a->d_qkv;
-  b3.lda = W;
-  b3.B = a->w_qkv;
-  b3.ldb = H;
-  b3.C = a->d_normed_part;
-  b3.ldc = H;
-  b3.tag = "gemm_attn_dgrad_normed";
-  CHECK_HIP(launch_gemm_bf16(true, false, kEpiStoreF32, b3, s), "d_normed GEMM");
   // d_w_qkv = d_qkv^T N ([W, T] x [T, H])
   GemmArgs b4{};
   b4.M = W;
@@ -1292,6 +1282,19 @@ int tp_attn_backward(const tp_attn_desc* d, int32_t phase, const tp_attn_bwd_arg
   b4.accum = accum;
   b4.tag = "gemm_attn_wgrad_qkv";
   CHECK_HIP(launch_gemm_bf16(false, false, kEpiStoreF32, b4, s), "d_w_qkv GEMM");
+  // d_normed partial = d_qkv W_qkv ([T, W] x [W, H]); last, as in the MLP backward
+  GemmArgs b3{};
+  b3.M = T;
+  b3.N = H;
+  b3.K = W;
+  b3.A = a->d_qkv;
+  b3.lda = W;
+  b3.B = a->w_qkv;
+  b3.ldb = H;
+  b3.C = a->d_normed_part;
+  b3.ldc = H;
+  b3.tag = "gemm_attn_dgrad_normed";
+  CHECK_HIP(launch_gemm_bf16(true, false, kEpiStoreF32, b3, s), "d_normed GEMM");
   return TP_MLP_OK;
 }
 
