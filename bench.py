@@ -53,16 +53,42 @@ OTHER_WORKLOADS = ("gpt2s_gelu_tp1", "llama3_70b_tp8_rank", "llama3_8b_tp1_maste
 
 
 def gemm_flops(w) -> dict:
-    """Algorithmic flops of one launch of each GEMM, by kernel name."""
+    """Algorithmic flops of one launch of each GEMM, by kernel name (a
+    weight-gradient GEMM that applies the SGD update as it forms the gradient
+    is named with the suffix _sgd)."""
     T, H, F = w.tokens, w.hidden, w.ffn_local
     if w.act == "swiglu":
-        return {"gemm_gate_up_swiglu": 2 * T * 2 * F * H, "gemm_down_partial": 2 * T * H * F,
-                "gemm_down_residual": 2 * T * H * F, "gemm_dact_swiglu_bwd": 2 * T * F * H,
-                "gemm_wgrad_down": 2 * H * F * T, "gemm_dgrad_normed": 2 * T * H * 2 * F,
-                "gemm_wgrad_gate_up": 2 * 2 * F * H * T}
-    return {"gemm_fc1_gelu": 2 * T * F * H, "gemm_down_partial": 2 * T * H * F, "gemm_down_residual": 2 * T * H * F,
-            "gemm_dact_gelu_bwd": 2 * T * F * H, "gemm_wgrad_down": 2 * H * F * T,
-            "gemm_dgrad_normed": 2 * T * H * F, "gemm_wgrad_fc1": 2 * F * H * T}
+        fl = {"gemm_gate_up_swiglu": 2 * T * 2 * F * H, "gemm_down_partial": 2 * T * H * F,
+              "gemm_down_residual": 2 * T * H * F, "gemm_dact_swiglu_bwd": 2 * T * F * H,
+              "gemm_wgrad_down": 2 * H * F * T, "gemm_dgrad_normed": 2 * T * H * 2 * F,
+              "gemm_wgrad_gate_up": 2 * 2 * F * H * T}
+    else:
+        fl = {"gemm_fc1_gelu": 2 * T * F * H, "gemm_down_partial": 2 * T * H * F,
+              "gemm_down_residual": 2 * T * H * F, "gemm_dact_gelu_bwd": 2 * T * F * H,
+              "gemm_wgrad_down": 2 * H * F * T, "gemm_dgrad_normed": 2 * T * H * F, "gemm_wgrad_fc1": 2 * F * H * T}
+    for k in ("gemm_wgrad_down", "gemm_wgrad_gate_up", "gemm_wgrad_fc1"):
+        if k in fl:
+            fl[k + "_sgd"] = fl[k]
+    return fl
+
+
+def gemm_ksplit(M: int, N: int, K: int) -> int:
+    """The library's k-slice count of a bf16 fp32-output GEMM (a function of
+    the shape: fewer than 192 tiles of 256 x 256 take the most slices, at most
+    8, that keep one round of 256 CUs and 1024 of k per slice)."""
+    tiles = -(-M // 256) * -(-N // 256)
+    if tiles >= 192:
+        return 1
+    ks = 1
+    while ks < 8 and tiles * (ks + 1) <= 256 and K // (ks + 1) >= 1024:
+        ks += 1
+    return ks
+
+
+def fused_update(w) -> bool:
+    """Whether the step takes the weight matrices' SGD update inside their
+    weight-gradient GEMMs (tp_mlp_fused_sgd; the bf16 steps here do)."""
+    return w.dtype == "bf16"
 
 
 def hbm_bytes_per_step(w) -> dict:
@@ -70,17 +96,31 @@ def hbm_bytes_per_step(w) -> dict:
     (compulsory reads + writes of its operands), by kernel name."""
     T, H, F, S = w.tokens, w.hidden, w.ffn_local, w.n_run
     es = 2 if w.dtype == "bf16" else 4
-    n_params = H + H + S * (2 * F * H + H * F + (F if w.act == "gelu" else 0))
-    per_param = (4 + 4 + 4 + es) if w.master else (es + 4 + es)
     P = 2 * F if w.act == "swiglu" else F
-    n_t = S * (H * F + P * H) if w.dtype == "bf16" else 0  # the weights' transposed copies, written with the update
+    n_w = S * (P * H + H * F)  # the weight matrices' elements
+    n_params = H + H + n_w + S * (F if w.act == "gelu" else 0)
+    per_param = (4 + 4 + 4 + es) if w.master else (es + 4 + es)
+    n_t = n_w if w.dtype == "bf16" else 0  # the weights' transposed copies, written with the update
+    fused = fused_update(w)
+    # with the update fused, the separate SGD takes the vectors only; a weight-gradient GEMM with k
+    # slices leaves them to sgd_ksplit, which reads the slices and the weight (or master) and writes the
+    # weight, its transposed copy (and the master)
+    sgd_bytes = (n_params - n_w) * per_param if fused else n_params * per_param + n_t * es
+    upd = (4 + 4 + es) if w.master else (es + es)
+    ksplit_bytes = 0
+    if fused:
+        for M, N in ((H, F), (P, H)):
+            ks = gemm_ksplit(M, N, T)
+            if ks > 1:
+                ksplit_bytes += S * M * N * (ks * 4 + upd + es)
     return {
+        "sgd_ksplit": ksplit_bytes,
         "rmsnorm_fwd": T * H * 2 * es + 4 * T + H * es,                 # x in, N out, rstd out, w in
         "partial_sum_residual": S * 4 * T * H + 2 * es * T * H + H * es,  # S fp32 partials + x in, out
         "partial_sum": S * 4 * T * H + 4 * T * H,                        # S fp32 partials in, dN out
         # the S fp32 partials of dN (summed as they are read), x, dY in, dx out
         "rmsnorm_bwd": T * H * (4 * S + 3 * es) + 4 * T + H * es,
-        "sgd": n_params * per_param + n_t * es,                          # p (or master), g in; p (+master), W^T out
+        "sgd": sgd_bytes,                                                # p (or master), g in; p (+master), W^T out
         # optimiser path: AdamW reads g, m, v and p (or master) and writes m, v, p (+ master)
         "adamw": n_params * ((4 + 4 + 4 + 8 + 8 + es) if w.master else (2 * es + 4 + 8 + 8)),
         "grad_norm": n_params * 4,                                         # every fp32 gradient read once
@@ -186,6 +226,7 @@ def optimizer_path(st, w, steps: int, warmup: int) -> dict:
     from tensor_transformer_mlp_rmsnorm_amd import _lib as L
 
     hp = dict(lr=1e-4, weight_decay=0.1, max_norm=1.0)
+    st.step(update=False)  # the gradients AdamW reads (a step with the update fused does not write them)
     for _ in range(max(1, warmup)):
         st.adamw(**hp)
     torch.cuda.synchronize()
@@ -391,7 +432,7 @@ def workload_timing(name: str, steps: int, warmup: int) -> dict:
     from tensor_transformer_mlp_rmsnorm_amd.step import ShardedStep
 
     w = synth.workload(name)
-    st = ShardedStep(w, synth.draw(w), device="cuda:0", out_of_place_sgd=True)
+    st = ShardedStep(w, synth.draw(w), device="cuda:0", out_of_place_sgd=True, fused_sgd=fused_update(w))
     for _ in range(max(1, warmup)):
         st.step()
     torch.cuda.synchronize()
@@ -479,7 +520,7 @@ def main() -> int:
         return 0
     w = synth.workload(args.workload)
     t = synth.draw(w)
-    st = ShardedStep(w, t, device="cuda:0", out_of_place_sgd=True)
+    st = ShardedStep(w, t, device="cuda:0", out_of_place_sgd=True, fused_sgd=fused_update(w))
     for _ in range(args.warmup):
         st.step()
     torch.cuda.synchronize()

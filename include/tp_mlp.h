@@ -172,6 +172,40 @@ int tp_partial_sum(const float* const* parts, int32_t n_parts, int64_t rows, int
 /* Backward phases (see tp_mlp_backward). */
 enum { TP_MLP_BWD_SHARD = 0, TP_MLP_BWD_NORM = 1 };
 
+/*
+ * The SGD update of a shard's two weight matrices taken inside the SHARD
+ * phase ("Reproduce one dense training step": one SGD update of every
+ * parameter; in a tensor-parallel rank the sharded weights' gradients need no
+ * reduction, so the update can follow their weight-gradient GEMMs at once).
+ * bf16 only.  Each GEMM's fp32 product dW is applied where it is formed and
+ * never written:
+ *   master == NULL:  W_out = round_bf16(W - lr dW)           (fp32 arithmetic)
+ *   master != NULL:  M_out = M - lr dW (fp32),  W_out = round_bf16(M_out)
+ * the bits tp_mlp_sgd_step_multi gives from the gradient the unfused phase
+ * would have written.  W_t_out (optional) receives the same values transposed
+ * (w_in: [H, 2F] | [H, F]; w_down: [F, H]), the copies tp_mlp_backward takes
+ * as w_in_t / w_down_t.
+ *   w_in_out       [2,F,H] | [F,H] bf16; may equal w_in (in place)
+ *   w_in_t_out     NULL or [H, 2F] | [H, F] bf16; may equal w_in_t
+ *   w_in_master    NULL or [2F|F, H] fp32, read; w_in_master_out then
+ *                  required, may equal it
+ *   w_down_*       the same for w_down [H, F] (transposed copy [F, H])
+ * Outputs must not partially overlap any tensor the phase reads.  When
+ * w_in_out equals w_in or w_in_t_out equals w_in_t, the phase forms its
+ * d_normed partial (which reads w_in) before it updates w_in.
+ */
+typedef struct {
+  float lr;
+  void* w_in_out;
+  void* w_in_t_out;
+  const float* w_in_master;
+  float* w_in_master_out;
+  void* w_down_out;
+  void* w_down_t_out;
+  const float* w_down_master;
+  float* w_down_master_out;
+} tp_mlp_fused_sgd;
+
 typedef struct {
   /* saved from tp_mlp_forward */
   const void* x;          /* [T, H]  dtype */
@@ -222,6 +256,12 @@ typedef struct {
      K-contiguous; NULL, it reads w_in as it lies.  It must hold the transpose
      of this w_in. */
   const void* w_in_t;
+  /* SHARD phase, optional (bf16): the SGD update of w_in and w_down taken in
+     their weight-gradient GEMMs (see tp_mlp_fused_sgd).  Given, d_w_in and
+     d_w_down are not written (they may be NULL) and TP_MLP_ACCUMULATE_GRADS
+     is an error; GeLU's d_b_in is still written.  NULL: the gradients are
+     written and the update is the caller's (tp_mlp_sgd_step_multi). */
+  const tp_mlp_fused_sgd* fused_sgd;
 } tp_mlp_bwd_args;
 
 /*
@@ -237,7 +277,9 @@ typedef struct {
  *   d_w_in       = d_pre^T normed          (fp32, [2F, H] rows gate then up | [F, H])
  *   d_b_in       = sum_t dh                (GeLU only)
  *   d_normed_part= d_pre w_in              (fp32 partial, summed by tp_partial_sum)
- *   This phase reads normed, pre_act, act, w_in, w_down and d_out.
+ *   This phase reads normed, pre_act, act, w_in, w_down and d_out.  With
+ *   a->fused_sgd, d_w_down and d_w_in are applied to the weights as they are
+ *   formed instead of being written.
  * phase TP_MLP_BWD_NORM (once, after the sum, or with the sum streamed in
  * through d_normed_parts):
  *   c_t      = (1/H) sum_i d_normed[t,i] norm_w[i] x[t,i]

@@ -73,12 +73,18 @@ class tp_mlp_adamw_tensor(ctypes.Structure):
                 ("v", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
+class tp_mlp_fused_sgd(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float)] + [(n, _vp) for n in (
+        "w_in_out", "w_in_t_out", "w_in_master", "w_in_master_out",
+        "w_down_out", "w_down_t_out", "w_down_master", "w_down_master_out")]
+
+
 class tp_mlp_bwd_args(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("x", "normed", "rstd", "pre_act", "act", "norm_w", "w_in", "w_down", "d_out",
                                    "d_pre", "d_w_in", "d_b_in", "d_w_down", "d_normed_part", "d_normed", "d_x",
                                    "d_norm_w", "d_b_down", "workspace")] + [("workspace_bytes", ctypes.c_size_t)] + \
         [("d_normed_parts", ctypes.POINTER(_vp)), ("n_d_normed_parts", ctypes.c_int32), ("w_down_t", _vp),
-         ("w_in_t", _vp)]
+         ("w_in_t", _vp), ("fused_sgd", ctypes.POINTER(tp_mlp_fused_sgd))]
 
 
 FP8_META_FIELDS = ("meta_normed", "meta_w_in", "meta_act", "meta_w_down", "meta_d_out", "meta_d_pre")
@@ -286,6 +292,19 @@ def _bwd_args(tensors: dict) -> tp_mlp_bwd_args:
     """``d_normed_parts`` may be a sequence of tensors (the NORM phase then
     sums them); the pointer array stays alive with the returned struct."""
     a = tp_mlp_bwd_args()
+    fused = tensors.pop("fused_sgd", None)
+    if fused:
+        f = tp_mlp_fused_sgd()
+        for name, _ in tp_mlp_fused_sgd._fields_:
+            if name == "lr":
+                f.lr = float(fused["lr"])
+            else:
+                setattr(f, name, _ptr(fused.get(name)))
+        unknown = set(fused) - {n for n, _ in tp_mlp_fused_sgd._fields_}
+        if unknown:
+            raise TypeError(f"unknown fused_sgd fields: {sorted(unknown)}")
+        a._fused_keepalive = f
+        a.fused_sgd = ctypes.pointer(f)
     parts = tensors.pop("d_normed_parts", None)
     if parts:
         arr = (_vp * len(parts))(*[_ptr(p) for p in parts])
@@ -293,7 +312,7 @@ def _bwd_args(tensors: dict) -> tp_mlp_bwd_args:
         a.d_normed_parts = ctypes.cast(arr, ctypes.POINTER(_vp))
         a.n_d_normed_parts = len(parts)
     for name, _ in tp_mlp_bwd_args._fields_:
-        if name in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts"):
+        if name in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "fused_sgd"):
             continue
         v = tensors.pop(name, None)
         setattr(a, name, _ptr(v))
@@ -389,7 +408,7 @@ def tp_attn_backward(desc: tp_attn_desc, phase: int, stream=None, **tensors) -> 
         a.d_normed_parts = ctypes.cast(arr, ctypes.POINTER(_vp))
         a.n_d_normed_parts = len(parts)
     for name, _ in tp_attn_bwd_args._fields_:
-        if name in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts"):
+        if name in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "fused_sgd"):
             continue
         v = tensors.pop(name, None)
         setattr(a, name, _ptr(v))

@@ -270,8 +270,9 @@ size_t tp_mlp_workspace_bytes(const tp_mlp_desc* d, int32_t phase) {
     // before either of them runs.
     const int64_t P = d->act == TP_MLP_ACT_SWIGLU ? 2 * F : F;
     if (T > 0) need = need > (size_t)(F * H * 2) ? need : (size_t)(F * H * 2);
+    // (with the update fused, tp_mlp_fused_sgd, every slice goes to the workspace)
     for (const int64_t K : {T, (T + 15) / 16 * 16}) {
-      const size_t w2 = gemm_ksplit_workspace(H, F, K), w4 = gemm_ksplit_workspace(P, H, K);
+      const size_t w2 = gemm_ksplit_workspace_sgd(H, F, K), w4 = gemm_ksplit_workspace_sgd(P, H, K);
       need = need > w2 ? need : w2;
       need = need > w4 ? need : w4;
     }
@@ -343,8 +344,29 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
     if (!aligned16(a->w_in_t)) return fail(TP_MLP_EALIGN, "%s: 'w_in_t' is not 16-byte aligned", fn);
     if (dt != kBF16) return fail(TP_MLP_EDTYPE, "%s: w_in_t is taken for bf16 only", fn);
   }
-  REQUIRE_PTR(a->d_w_in);
-  REQUIRE_PTR(a->d_w_down);
+  const tp_mlp_fused_sgd* fu = a->fused_sgd;
+  if (fu) {
+    if (dt != kBF16) return fail(TP_MLP_EDTYPE, "%s: fused_sgd is taken for bf16 only", fn);
+    if (accum) return fail(TP_MLP_EINVAL, "%s: fused_sgd with TP_MLP_ACCUMULATE_GRADS", fn);
+    if (!std::isfinite(fu->lr)) return fail(TP_MLP_EINVAL, "%s: fused_sgd->lr is not finite", fn);
+    REQUIRE_PTR(fu->w_in_out);
+    REQUIRE_PTR(fu->w_down_out);
+    if (fu->w_in_t_out && !aligned16(fu->w_in_t_out))
+      return fail(TP_MLP_EALIGN, "%s: 'fused_sgd->w_in_t_out' is not 16-byte aligned", fn);
+    if (fu->w_down_t_out && !aligned16(fu->w_down_t_out))
+      return fail(TP_MLP_EALIGN, "%s: 'fused_sgd->w_down_t_out' is not 16-byte aligned", fn);
+    if (fu->w_in_master) {
+      REQUIRE_PTR(fu->w_in_master);
+      REQUIRE_PTR(fu->w_in_master_out);
+    }
+    if (fu->w_down_master) {
+      REQUIRE_PTR(fu->w_down_master);
+      REQUIRE_PTR(fu->w_down_master_out);
+    }
+  } else {
+    REQUIRE_PTR(a->d_w_in);
+    REQUIRE_PTR(a->d_w_down);
+  }
   if (!swiglu) REQUIRE_PTR(a->d_b_in);
   if (swiglu && a->d_b_in) return fail(TP_MLP_EINVAL, "%s: d_b_in must be NULL for SwiGLU", fn);
   if (T > 0) {
@@ -386,7 +408,8 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
     CHECK_HIP(launch_gemm(dt, true, false, act_bwd, b1, s), "d_act GEMM");
   }
 
-  // d_w_down = d_out^T act ([H,T] x [T,F]).
+  // d_w_down = d_out^T act ([H,T] x [T,F]); with the update fused, applied to
+  // w_down as it is formed (d_act above has already read w_down / w_down_t).
   GemmArgs b2{};
   b2.M = H;
   b2.N = F;
@@ -397,13 +420,18 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
   b2.ldb = F;
   b2.C = a->d_w_down;
   b2.ldc = F;
-  b2.tag = "gemm_wgrad_down";
+  b2.tag = fu ? "gemm_wgrad_down_sgd" : "gemm_wgrad_down";
   b2.ksplit = gemm_ksplit(b2.M, b2.N, b2.K);
   b2.ws = static_cast<float*>(a->workspace);
   b2.accum = accum;
-  CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b2, s), "d_w_down GEMM");
+  if (fu) {
+    b2.sgd = SgdEpi{a->w_down, fu->w_down_out, fu->w_down_t_out, fu->w_down_master, fu->w_down_master_out, fu->lr};
+    CHECK_HIP(launch_gemm(dt, false, false, kEpiSgd, b2, s), "d_w_down GEMM + SGD");
+  } else {
+    CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b2, s), "d_w_down GEMM");
+  }
 
-  // d_w_in = d_pre^T normed ([P,T] x [T,H]).
+  // d_w_in = d_pre^T normed ([P,T] x [T,H]), or with the update fused, w_in's update.
   GemmArgs b4{};
   b4.M = P;
   b4.N = H;
@@ -414,11 +442,26 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
   b4.ldb = H;
   b4.C = a->d_w_in;
   b4.ldc = H;
-  b4.tag = swiglu ? "gemm_wgrad_gate_up" : "gemm_wgrad_fc1";
+  b4.tag = fu ? (swiglu ? "gemm_wgrad_gate_up_sgd" : "gemm_wgrad_fc1_sgd")
+              : (swiglu ? "gemm_wgrad_gate_up" : "gemm_wgrad_fc1");
   b4.ksplit = gemm_ksplit(b4.M, b4.N, b4.K);
   b4.ws = static_cast<float*>(a->workspace);
   b4.accum = accum;
-  CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b4, s), "d_w_in GEMM");
+  if (fu) b4.sgd = SgdEpi{a->w_in, fu->w_in_out, fu->w_in_t_out, fu->w_in_master, fu->w_in_master_out, fu->lr};
+  auto run_b4 = [&]() -> int {
+    if (fu) {
+      CHECK_HIP(launch_gemm(dt, false, false, kEpiSgd, b4, s), "d_w_in GEMM + SGD");
+    } else {
+      CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b4, s), "d_w_in GEMM");
+    }
+    return TP_MLP_OK;
+  };
+  // An in-place update of w_in must wait for the d_normed GEMM below, which reads it.
+  const bool b4_after_b3 = fu && (fu->w_in_out == a->w_in || (a->w_in_t && fu->w_in_t_out == a->w_in_t));
+  if (!b4_after_b3) {
+    const int rc = run_b4();
+    if (rc) return rc;
+  }
 
   if (!swiglu)
     CHECK_HIP(launch_colsum(dt, a->d_pre, a->d_b_in, a->workspace, T, F, accum, s), "d_b_in column sum");
@@ -446,6 +489,7 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
   } else {
     CHECK_HIP(launch_gemm(dt, true, false, kEpiStoreF32, b3, s), "d_normed GEMM");
   }
+  if (b4_after_b3) return run_b4();
   return TP_MLP_OK;
 }
 
@@ -939,6 +983,7 @@ int tp_mlp_backward_fp8(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_ar
                   a->workspace ? a->workspace_bytes : (size_t)0);
     if (!aligned16(a->workspace)) return fail(TP_MLP_EALIGN, "%s: workspace is not 16-byte aligned", fn);
   }
+  if (a->fused_sgd) return fail(TP_MLP_EINVAL, "%s: fused_sgd is not taken by the FP8 backward", fn);
   REQUIRE_PTR(a->d_w_in);
   REQUIRE_PTR(a->d_w_down);
   if (!swiglu) REQUIRE_PTR(a->d_b_in);

@@ -125,6 +125,18 @@ __device__ __forceinline__ uint4 Chunk<bf16_t>::pack(const float (&f)[8]) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// ------------------------------------------------------------------- SGD
+
+// One SGD update, p - lr g, as a single fused multiply-add (every kernel that
+// applies the update goes through these, so all give the same bits).
+__device__ __forceinline__ float sgd_value(float p, float g, float lr) { return __builtin_fmaf(-lr, g, p); }
+__device__ __forceinline__ floatx4 sgd_value4(floatx4 p, floatx4 g, float lr) {
+  floatx4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = sgd_value(p[i], g[i], lr);
+  return r;
+}
+
 // ------------------------------------------------------------ wave reductions
 
 __device__ __forceinline__ float wave_sum(float v) {

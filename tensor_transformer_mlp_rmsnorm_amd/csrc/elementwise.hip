@@ -111,25 +111,49 @@ constexpr int kSgdPerThread = 8, kSgdBlock = 256, kSgdPerBlock = kSgdPerThread *
 // non-temporal hint): v = p - lr g, or with masters m' = m - lr g (written)
 // and v = m'.  Shared by the flat and the transposing kernels, so both give
 // the same bits.
+// The old values of the 8 elements from e: the fp32 masters, or the parameter.
+template <typename T, bool MASTER>
+__device__ __forceinline__ void sgd8_old(const T* pin, const float* min, int64_t e, floatx4& p0, floatx4& p1) {
+  if constexpr (MASTER) {
+    p0 = load4<float>(min + e);
+    p1 = load4<float>(min + e + 4);
+  } else if constexpr (sizeof(T) == 2) {
+    float f[8];
+    Chunk<bf16_t>::unpack(*reinterpret_cast<const uint4*>(pin + e), f);
+    p0 = floatx4{f[0], f[1], f[2], f[3]};
+    p1 = floatx4{f[4], f[5], f[6], f[7]};
+  } else {
+    p0 = load4<T>(pin + e);
+    p1 = load4<T>(pin + e + 4);
+  }
+}
+
+// The updated values v = p - lr g (with masters also stored as the new masters).
+template <bool MASTER>
+__device__ __forceinline__ void sgd8_new(floatx4 p0, floatx4 p1, floatx4 g0, floatx4 g1, float* mout, int64_t e,
+                                         float lr, floatx4& v0, floatx4& v1) {
+  v0 = sgd_value4(p0, g0, lr);
+  v1 = sgd_value4(p1, g1, lr);
+  if constexpr (MASTER) {
+    store4<float>(mout + e, v0);
+    store4<float>(mout + e + 4, v1);
+  }
+}
+
+template <typename T, bool MASTER>
+__device__ __forceinline__ void sgd8_apply(const T* pin, floatx4 g0, floatx4 g1, const float* min, float* mout,
+                                           int64_t e, float lr, floatx4& v0, floatx4& v1) {
+  floatx4 p0, p1;
+  sgd8_old<T, MASTER>(pin, min, e, p0, p1);
+  sgd8_new<MASTER>(p0, p1, g0, g1, mout, e, lr, v0, v1);
+}
+
 template <typename T, bool MASTER>
 __device__ __forceinline__ void sgd8(const T* pin, const float* g, const float* min, float* mout, int64_t e, float lr,
                                      floatx4& v0, floatx4& v1) {
   const floatx4 g0 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(g + e));
   const floatx4 g1 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(g + e + 4));
-  if constexpr (MASTER) {
-    v0 = load4<float>(min + e) - lr * g0;
-    v1 = load4<float>(min + e + 4) - lr * g1;
-    store4<float>(mout + e, v0);
-    store4<float>(mout + e + 4, v1);
-  } else if constexpr (sizeof(T) == 2) {
-    float f[8];
-    Chunk<bf16_t>::unpack(*reinterpret_cast<const uint4*>(pin + e), f);
-    v0 = floatx4{f[0], f[1], f[2], f[3]} - lr * g0;
-    v1 = floatx4{f[4], f[5], f[6], f[7]} - lr * g1;
-  } else {
-    v0 = load4<T>(pin + e) - lr * g0;
-    v1 = load4<T>(pin + e + 4) - lr * g1;
-  }
+  sgd8_apply<T, MASTER>(pin, g0, g1, min, mout, e, lr, v0, v1);
 }
 
 template <typename T, bool MASTER>
@@ -154,10 +178,10 @@ __global__ __launch_bounds__(kSgdBlock) void sgd_kernel(SgdList L, float lr) {
     for (int64_t e = e0; e < sg.n; ++e) {
       float v;
       if constexpr (MASTER) {
-        v = sg.min[e] - lr * sg.g[e];
+        v = sgd_value(sg.min[e], sg.g[e], lr);
         sg.mout[e] = v;
       } else {
-        v = Elem<T>::to_f32(pin[e]) - lr * sg.g[e];
+        v = sgd_value(Elem<T>::to_f32(pin[e]), sg.g[e], lr);
       }
       pout[e] = Elem<T>::from_f32(v);
     }
@@ -185,42 +209,54 @@ struct SgdTList {
   int count;
 };
 
-template <bool MASTER>
-__global__ __launch_bounds__(256) void sgd_t_kernel(SgdTList L, float lr) {
-  // A 64 x 64 tile: each thread updates two chunks of 8 consecutive elements of a row (16-byte
-  // accesses, the flat kernel's arithmetic), stores them row-major and, as one 16-byte write, into
-  // an LDS tile whose rows are padded to 144 bytes; then each thread reads 8 rows x 2 adjacent
-  // columns back with 4-byte reads and stores the two 8-element column chunks of the transposed
-  // copy.  Eight consecutive lanes take the 8 row groups of one column pair, so each wave writes
-  // whole 128-byte column segments.
+// One 64 x 64 tile of the transposing update: each thread updates two chunks
+// of 8 consecutive elements of a row (16-byte accesses, the flat kernel's
+// arithmetic), stores them row-major and, as one 16-byte write, into an LDS
+// tile whose rows are padded to 144 bytes; then each thread reads 8 rows x 2
+// adjacent columns back with 4-byte reads and stores the two 8-element column
+// chunks of the transposed copy.  Eight consecutive lanes take the 8 row
+// groups of one column pair, so each wave writes whole 128-byte column
+// segments.  grad8(e, g0, g1) yields the gradient of elements e .. e + 7; pt
+// may be null (no transposed copy).
+template <bool MASTER, class G>
+__device__ __forceinline__ void sgd_t_tile(const bf16_t* pin, bf16_t* pout, bf16_t* pt, const float* min, float* mout,
+                                           int64_t rows, int64_t cols, int64_t r0, int64_t c0, float lr,
+                                           const G& grad8) {
   __shared__ __align__(16) bf16_t tile[kSgdTTile][kSgdTTile + 8];
-  int t = 0;
-  while (t + 1 < L.count && (int64_t)blockIdx.x >= L.seg[t + 1].block0) ++t;
-  const SgdTSeg& sg = L.seg[t];
-  const int64_t b = (int64_t)blockIdx.x - sg.block0;
-  const int64_t r0 = (b / sg.tiles_c) * kSgdTTile, c0 = (b % sg.tiles_c) * kSgdTTile;
-  const bf16_t* pin = static_cast<const bf16_t*>(sg.pin);
-  bf16_t* pout = static_cast<bf16_t*>(sg.pout);
-  // 64 rows x 8 chunks of 8 columns, two chunks per thread (rows and cols are multiples of 8)
+  // 64 rows x 8 chunks of 8 columns, two chunks per thread (rows and cols are multiples of 8).  Both
+  // chunks' loads are issued before any store (a store could alias a later load as far as the
+  // compiler knows, so interleaving them would leave one chunk's loads in flight at a time).
+  floatx4 g[2][2], p[2][2];
+  bool ok[2];
+  int64_t e[2];
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int ch = threadIdx.x + 256 * pass, row = ch >> 3, col8 = (ch & 7) * 8;
     const int64_t gr = r0 + row, gc = c0 + col8;
-    if (gr < sg.rows && gc < sg.cols) {
-      const int64_t e = gr * sg.cols + gc;
+    ok[pass] = gr < rows && gc < cols;
+    e[pass] = gr * cols + gc;
+    if (ok[pass]) {
+      grad8(e[pass], g[pass][0], g[pass][1]);
+      sgd8_old<bf16_t, MASTER>(pin, min, e[pass], p[pass][0], p[pass][1]);
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int ch = threadIdx.x + 256 * pass, row = ch >> 3, col8 = (ch & 7) * 8;
+    if (ok[pass]) {
       floatx4 v0, v1;
-      sgd8<bf16_t, MASTER>(pin, sg.g, sg.min, sg.mout, e, lr, v0, v1);
+      sgd8_new<MASTER>(p[pass][0], p[pass][1], g[pass][0], g[pass][1], mout, e[pass], lr, v0, v1);
       const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       const uint4 u = Chunk<bf16_t>::pack(f);
-      *reinterpret_cast<uint4*>(pout + e) = u;
+      *reinterpret_cast<uint4*>(pout + e[pass]) = u;
       *reinterpret_cast<uint4*>(&tile[row][col8]) = u;
     }
   }
+  if (!pt) return;  // (uniform over the workgroup)
   __syncthreads();
-  bf16_t* pt = static_cast<bf16_t*>(sg.pout_t);
   const int c = 2 * (threadIdx.x >> 3), rr = 8 * (threadIdx.x & 7);
   const int64_t gc = c0 + c, gr = r0 + rr;
-  if (gc < sg.cols && gr < sg.rows) {  // (cols and rows are multiples of 8: the pair and the 8 rows are whole)
+  if (gc < cols && gr < rows) {  // (cols and rows are multiples of 8: the pair and the 8 rows are whole)
     uint32_t w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = *reinterpret_cast<const uint32_t*>(&tile[rr + i][c]);
@@ -230,9 +266,47 @@ __global__ __launch_bounds__(256) void sgd_t_kernel(SgdTList L, float lr) {
       lo[i] = (w[2 * i] & 0xffffu) | (w[2 * i + 1] << 16);
       hi[i] = (w[2 * i] >> 16) | (w[2 * i + 1] & 0xffff0000u);
     }
-    *reinterpret_cast<uint4*>(pt + gc * sg.rows + gr) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    *reinterpret_cast<uint4*>(pt + (gc + 1) * sg.rows + gr) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4*>(pt + gc * rows + gr) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4*>(pt + (gc + 1) * rows + gr) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
   }
+}
+
+template <bool MASTER>
+__global__ __launch_bounds__(256) void sgd_t_kernel(SgdTList L, float lr) {
+  int t = 0;
+  while (t + 1 < L.count && (int64_t)blockIdx.x >= L.seg[t + 1].block0) ++t;
+  const SgdTSeg& sg = L.seg[t];
+  const int64_t b = (int64_t)blockIdx.x - sg.block0;
+  const int64_t r0 = (b / sg.tiles_c) * kSgdTTile, c0 = (b % sg.tiles_c) * kSgdTTile;
+  const float* grad = sg.g;
+  sgd_t_tile<MASTER>(static_cast<const bf16_t*>(sg.pin), static_cast<bf16_t*>(sg.pout),
+                     static_cast<bf16_t*>(sg.pout_t), sg.min, sg.mout, sg.rows, sg.cols, r0, c0, lr,
+                     [grad](int64_t e, floatx4& g0, floatx4& g1) {
+                       g0 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(grad + e));
+                       g1 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(grad + e + 4));
+                     });
+}
+
+// The update of one weight whose gradient is the sum of a split GEMM's
+// k-slices, ((s0 + s1) + s2) + ..., the order of ksplit_reduce_kernel, so the
+// gradient has the bits the unfused path stores (and then reads back).
+template <bool MASTER>
+__global__ __launch_bounds__(256) void sgd_ksplit_kernel(SgdEpi u, const float* __restrict__ ws, int nslices,
+                                                         int64_t rows, int64_t cols, int64_t tiles_c) {
+  const int64_t b = blockIdx.x;
+  const int64_t r0 = (b / tiles_c) * kSgdTTile, c0 = (b % tiles_c) * kSgdTTile;
+  const int64_t slice = rows * cols;
+  sgd_t_tile<MASTER>(static_cast<const bf16_t*>(u.w_in), static_cast<bf16_t*>(u.w_out),
+                     static_cast<bf16_t*>(u.w_out_t), u.m_in, u.m_out, rows, cols, r0, c0, u.lr,
+                     [ws, nslices, slice](int64_t e, floatx4& g0, floatx4& g1) {
+                       g0 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(ws + e));
+                       g1 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(ws + e + 4));
+                       for (int k = 1; k < nslices; ++k) {
+                         const float* p = ws + (int64_t)k * slice + e;
+                         g0 += __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+                         g1 += __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p + 4));
+                       }
+                     });
 }
 
 __global__ __launch_bounds__(256) void ksplit_reduce_kernel(float* __restrict__ C, const float* __restrict__ ws,
@@ -406,6 +480,18 @@ hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, f
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+hipError_t launch_sgd_ksplit(const SgdEpi& u, const float* ws, int nslices, int64_t M, int64_t N, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (M % 8 || N % 8 || nslices < 1) return hipErrorInvalidValue;
+  KernelTimer timer("sgd_ksplit", s);
+  const int64_t tr = (M + kSgdTTile - 1) / kSgdTTile, tc = (N + kSgdTTile - 1) / kSgdTTile;
+  if (u.m_in)
+    hipLaunchKernelGGL(sgd_ksplit_kernel<true>, dim3((unsigned)(tr * tc)), dim3(256), 0, s, u, ws, nslices, M, N, tc);
+  else
+    hipLaunchKernelGGL(sgd_ksplit_kernel<false>, dim3((unsigned)(tr * tc)), dim3(256), 0, s, u, ws, nslices, M, N, tc);
+  return hipGetLastError();
 }
 
 hipError_t launch_transpose_bf16(const void* in, void* out, int64_t R, int64_t C, hipStream_t s) {

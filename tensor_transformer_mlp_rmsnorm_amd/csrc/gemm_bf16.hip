@@ -474,6 +474,83 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const floatx4 (&acc)
 }
 
 
+// kEpiSgd (two-stage kernels): the product is the gradient dW of a bf16 weight
+// W [M, N] and the SGD step is taken here, so dW never goes to memory.  Each
+// lane updates its 4 consecutive columns of a row exactly as the SGD kernels
+// do (sgd_value: one fma, then the round to bf16) and stores them row-major.
+// For the transposed copy W_t [N, M] the tile goes through LDS as [TN][TM + 8]
+// bf16 (the main loop's stages are free by then): lanes of neighbouring rows
+// swap halves so that each writes whole dwords (two rows of one column), the
+// 16-byte row pad puts the 8 column rows of one store in distinct banks, and
+// every thread then writes 16-byte chunks of the transposed rows.
+template <class SH>
+constexpr size_t sgd_stage_bytes() {
+  return (size_t)SH::TN * (SH::TM + 8) * sizeof(bf16_t);
+}
+
+template <class SH, bool MASTER>
+__device__ __forceinline__ void epilogue_sgd(const GemmArgs& g, const floatx4 (&acc)[SH::WMB][SH::WNB],
+                                             int64_t tile_m0, int64_t tile_n0, int wm, int wn, int lane,
+                                             uint4* smem) {
+  constexpr int kPitch = SH::TM + 8;  // bf16 per LDS row (one transposed row: a column of W)
+  const int64_t M = g.M, N = g.N;
+  const SgdEpi& u = g.sgd;
+  const float lr = u.lr;
+  const bf16_t* __restrict__ w_in = static_cast<const bf16_t*>(u.w_in);
+  bf16_t* __restrict__ w_out = static_cast<bf16_t*>(u.w_out);
+  bf16_t* const w_out_t = static_cast<bf16_t*>(u.w_out_t);
+  bf16_t* const lds = reinterpret_cast<bf16_t*>(smem);
+  const int frow = lane & 15, col4 = 4 * (lane >> 4);
+  const bool odd = lane & 1;
+  __syncthreads();  // every wave is past its last read of the main loop's stages
+#pragma unroll
+  for (int i = 0; i < SH::WMB; ++i) {
+    const int lm = wm * SH::WMB * 16 + i * 16 + frow;  // row of W within the tile
+    const int64_t m = tile_m0 + lm;
+    floatx4 p[SH::WNB];
+#pragma unroll
+    for (int j = 0; j < SH::WNB; ++j) {  // the old values of the row's blocks, loaded together
+      const int64_t n = tile_n0 + wn * SH::WNB * 16 + j * 16 + col4;
+      const bool ok = m < M && n < N;  // (N is a multiple of 4: the lane's 4 columns are whole)
+      if constexpr (MASTER) p[j] = ok ? load4<float>(u.m_in + m * N + n) : floatx4{0.f, 0.f, 0.f, 0.f};
+      else p[j] = ok ? load4<bf16_t>(w_in + m * N + n) : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < SH::WNB; ++j) {
+      const int ln = wn * SH::WNB * 16 + j * 16 + col4;  // column of W within the tile
+      const int64_t n = tile_n0 + ln;
+      const bool ok = m < M && n < N;
+      const floatx4 v = sgd_value4(p[j], acc[i][j], lr);
+      if (ok) {
+        if constexpr (MASTER) store4<float>(u.m_out + m * N + n, v);
+        store4<bf16_t>(w_out + m * N + n, v);
+      }
+      if (w_out_t) {
+        const uint32_t b0 = f32_to_bf16(v[0]), b1 = f32_to_bf16(v[1]), b2 = f32_to_bf16(v[2]),
+                       b3 = f32_to_bf16(v[3]);
+        // even lanes (row lm) keep columns 0, 1 and take the odd neighbour's (row lm + 1); odd lanes
+        // keep columns 2, 3 and take the even neighbour's (row lm - 1)
+        const uint32_t send = odd ? (b0 | (b1 << 16)) : (b2 | (b3 << 16));
+        const uint32_t recv = (uint32_t)__shfl_xor((int)send, 1, kWave);
+        const int c0 = odd ? 2 : 0, r0 = odd ? lm - 1 : lm;
+        const uint32_t lo = odd ? (recv & 0xffffu) | (b2 << 16) : b0 | (recv << 16);
+        const uint32_t hi = odd ? (recv >> 16) | (b3 << 16) : b1 | (recv & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(lds + (ln + c0) * kPitch + r0) = lo;
+        *reinterpret_cast<uint32_t*>(lds + (ln + c0 + 1) * kPitch + r0) = hi;
+      }
+    }
+  }
+  if (!w_out_t) return;  // (uniform)
+  __syncthreads();
+  constexpr int kChunks = SH::TM / 8;  // 16-byte chunks per transposed row
+  for (int c = threadIdx.x; c < SH::TN * kChunks; c += SH::NW * 64) {
+    const int ln = c / kChunks, lc = (c - ln * kChunks) * 8;
+    const int64_t n = tile_n0 + ln, m = tile_m0 + lc;
+    if (n < N && m < M)  // (M is a multiple of 8: a chunk is wholly inside or outside)
+      *reinterpret_cast<uint4*>(w_out_t + n * M + m) = *reinterpret_cast<const uint4*>(lds + ln * kPitch + lc);
+  }
+}
+
 // Ping-pong fragment reads: the 24 ds_read_b128 of one k-tile (A: 8 row blocks,
 // B: 4, each for k 0-31 and 32-63) in one block that also waits for them.  No
 // LDS read is left in flight past it, and the compiler does not add its own
@@ -778,8 +855,13 @@ __global__ __launch_bounds__(SH::NW * 64, 1) void gemm_bf16_kernel(GemmArgs g, i
     __syncthreads();  // next stage landed; this stage free
   }
 
-  epilogue<EPI, SH::WMB, SH::WNB>(g, acc, (int64_t)tm * SH::TM + wm * SH::WMB * 16,
-                                  (int64_t)tn * SH::TN + wn * SH::WNB * 16, 0, ks, lane);
+  if constexpr (EPI == kEpiSgd) {
+    if (g.sgd.m_in) epilogue_sgd<SH, true>(g, acc, (int64_t)tm * SH::TM, (int64_t)tn * SH::TN, wm, wn, lane, smem);
+    else epilogue_sgd<SH, false>(g, acc, (int64_t)tm * SH::TM, (int64_t)tn * SH::TN, wm, wn, lane, smem);
+  } else {
+    epilogue<EPI, SH::WMB, SH::WNB>(g, acc, (int64_t)tm * SH::TM + wm * SH::WMB * 16,
+                                    (int64_t)tn * SH::TN + wn * SH::WNB * 16, 0, ks, lane);
+  }
 }
 
 // The two-stage schedule with the fragment reads one k-half ahead: each wave
@@ -854,8 +936,13 @@ __global__ __launch_bounds__(SH::NW * 64, 1) void gemm_bf16_pipe_kernel(GemmArgs
     mma_half(acc, a1, b1);
   }
 
-  epilogue<EPI, SH::WMB, SH::WNB>(g, acc, (int64_t)tm * SH::TM + wm * SH::WMB * 16,
-                                  (int64_t)tn * SH::TN + wn * SH::WNB * 16, 0, ks, lane);
+  if constexpr (EPI == kEpiSgd) {
+    if (g.sgd.m_in) epilogue_sgd<SH, true>(g, acc, (int64_t)tm * SH::TM, (int64_t)tn * SH::TN, wm, wn, lane, smem);
+    else epilogue_sgd<SH, false>(g, acc, (int64_t)tm * SH::TM, (int64_t)tn * SH::TN, wm, wn, lane, smem);
+  } else {
+    epilogue<EPI, SH::WMB, SH::WNB>(g, acc, (int64_t)tm * SH::TM + wm * SH::WMB * 16,
+                                    (int64_t)tn * SH::TN + wn * SH::WNB * 16, 0, ks, lane);
+  }
 }
 
 constexpr size_t kSmemBytes = 2 * kStageU4 * sizeof(uint4);
@@ -899,15 +986,18 @@ hipError_t launch_two_stage(const GemmArgs& ga, hipStream_t s) {
   void (*kernel)(GemmArgs, int, int);
   if constexpr (pipelined_loop<AK, BKC, SH>()) kernel = gemm_bf16_pipe_kernel<AK, BKC, EPI, SH>;
   else kernel = gemm_bf16_kernel<AK, BKC, EPI, SH>;
+  // the SGD epilogue stages the transposed tile in LDS: [TN][TM + 8] bf16 (132 KiB for 256 x 256)
+  constexpr size_t smem = EPI == kEpiSgd && sgd_stage_bytes<SH>() > kSmemBytes ? sgd_stage_bytes<SH>() : kSmemBytes;
+  static_assert(smem <= 160 * 1024, "LDS of one CU");
   static bool configured = false;  // raise the dynamic LDS limit once per instantiation
   if (!configured) {
     const hipError_t e =
         hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)kSmemBytes);
+                            (int)smem);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(kernel, dim3(ntm * ntn * ga.ksplit), dim3(SH::NW * 64), kSmemBytes, s, ga, ntm, ntn);
+  hipLaunchKernelGGL(kernel, dim3(ntm * ntn * ga.ksplit), dim3(SH::NW * 64), smem, s, ga, ntm, ntn);
   return hipGetLastError();
 }
 
@@ -973,7 +1063,21 @@ hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
       return launch_ksplit_reduce_bf16(ga.C, ga.ws, ga.ksplit, ga.M, ga.N, ga.ldc, s);
     }
   }
-  if (EPI != kEpiStoreF32 || !ga.ws) ga.ksplit = 1;
+  if constexpr (EPI == kEpiSgd) {
+    if (ga.ws && ga.ksplit > 1) {
+      // every slice in fp32 in the workspace, then their sum in index order and the update
+      GemmArgs gf = ga;
+      gf.C = ga.ws;
+      gf.ldc = ga.N;
+      gf.ws = ga.ws + ga.M * ga.N;
+      gf.accum = 0;
+      const hipError_t e = launch_tiles<AK, BKC, kEpiStoreF32, OP>(gf, ntm, ntn, s);
+      if (e != hipSuccess) return e;
+      return launch_sgd_ksplit(ga.sgd, ga.ws, ga.ksplit, ga.M, ga.N, s);
+    }
+  }
+  if ((EPI != kEpiStoreF32 && EPI != kEpiSgd) || !ga.ws) ga.ksplit = 1;
+  if (EPI == kEpiSgd) ga.ksplit = 1;
   if (ga.ksplit < 1) ga.ksplit = 1;
   const hipError_t e = launch_tiles<AK, BKC, EPI, OP>(ga, ntm, ntn, s);
   if (e != hipSuccess || ga.ksplit == 1) return e;
@@ -1004,6 +1108,7 @@ hipError_t launch_gemm_bf16(bool ak, bool bk, Epi epi, const GemmArgs& g, hipStr
     }
   } else if (!ak && !bk) {
     if (epi == kEpiStoreF32) return launch_t<false, false, kEpiStoreF32>(g, s);
+    if (epi == kEpiSgd) return launch_t<false, false, kEpiSgd>(g, s);
   }
   return hipErrorInvalidValue;
 }

@@ -35,6 +35,20 @@ enum Epi {
   kEpiSwigluBwd = 4,  // d_pre = [dg | du] from d_act = acc and saved [g | u]
   kEpiGeluBwd = 5,    // dh = d_act * gelu'(h)
   kEpiStoreBf16 = 6,  // C bf16 [M, ldc]
+  kEpiSgd = 7,        // the product is the gradient of a bf16 weight [M, N]: SGD update applied (GemmArgs.sgd)
+};
+
+// kEpiSgd: where the update of a weight W [M, N] (bf16, row-major) goes.  The
+// product C = dW is never stored; W_out = round(W_in - lr C), or with fp32
+// masters M_out = M_in - lr C and W_out = round(M_out); W_out_t (optional)
+// receives the same values transposed, [N, M].  Outputs may equal inputs.
+struct SgdEpi {
+  const void* w_in;
+  void* w_out;
+  void* w_out_t;
+  const float* m_in;
+  float* m_out;
+  float lr;
 };
 
 // Operand layouts: A is [M, K] when a_kcontig, else [K, M]; B is [N, K] when
@@ -68,6 +82,9 @@ struct GemmArgs {
   // product is multiplied by scale_inv_a[0] * scale_inv_b[0] before the epilogue.
   const float* scale_inv_a;
   const float* scale_inv_b;
+  // kEpiSgd only (with a k split, every slice goes to ws and a second kernel
+  // sums them in index order and applies the update)
+  SgdEpi sgd;
 };
 
 // Number of k-slices for a bf16 fp32-output GEMM: a function of the shape only
@@ -83,6 +100,12 @@ inline int gemm_ksplit(int64_t M, int64_t N, int64_t K) {
 }
 inline size_t gemm_ksplit_workspace(int64_t M, int64_t N, int64_t K) {
   return (size_t)(gemm_ksplit(M, N, K) - 1) * (size_t)(M * N) * sizeof(float);
+}
+// The same for a weight-gradient GEMM with the SGD update applied (kEpiSgd:
+// every slice in the workspace).
+inline size_t gemm_ksplit_workspace_sgd(int64_t M, int64_t N, int64_t K) {
+  const int ks = gemm_ksplit(M, N, K);
+  return ks > 1 ? (size_t)ks * (size_t)(M * N) * sizeof(float) : 0;
 }
 // The same for a bf16-output GEMM (every slice in the workspace).
 inline size_t gemm_ksplit_workspace_bf16(int64_t M, int64_t N, int64_t K) {
@@ -182,6 +205,10 @@ struct SgdTensor {
 // One SGD update of every tensor in `list` (all in dtype dt; all with fp32
 // masters when `master`).
 hipError_t launch_sgd(DType dt, const SgdTensor* list, int count, bool master, float lr, hipStream_t s);
+// The SGD update of one bf16 weight [M, N] whose gradient is the sum, in
+// index order, of `nslices` [M, N] fp32 slices at ws (a split GEMM's
+// k-slices), with the optional transposed copy: the arithmetic of launch_sgd.
+hipError_t launch_sgd_ksplit(const SgdEpi& u, const float* ws, int nslices, int64_t M, int64_t N, hipStream_t s);
 
 struct AdamwTensor {
   const void* param_in;

@@ -78,10 +78,19 @@ class ShardedStep:
     ``synth.draw``.  With ``out_of_place_sgd`` the update writes new
     parameter buffers and leaves the inputs unchanged, so repeated steps do
     identical work (benchmarking); otherwise parameters update in place.
+    With ``fused_sgd`` (bf16) a step's SGD update of every shard's w_in and
+    w_down is taken inside the SHARD backward, in their weight-gradient GEMMs
+    (tp_mlp_fused_sgd): those gradients are then never written, and the
+    separate update covers the remaining parameters.  The new parameters are
+    the same bits as without it.
     """
 
     def __init__(self, w, tensors: Dict[str, torch.Tensor], device="cuda", out_of_place_sgd: bool = False,
-                 stream: Optional[torch.cuda.Stream] = None):
+                 stream: Optional[torch.cuda.Stream] = None, fused_sgd: bool = False):
+        if fused_sgd and w.dtype != "bf16":
+            raise ValueError("the fused update is bf16 only")
+        self.fused_sgd = fused_sgd
+        self._fused_names: set = set()
         self.w = w
         self.dev = torch.device(device)
         self.stream = stream
@@ -226,13 +235,28 @@ class ShardedStep:
             L.tp_partial_sum([sh["z"] for sh in self.shards], T, H, self.x, self.b_down, self.cdt, self.out,
                              self.cdt, stream=st)
 
-    def _shard_backward(self, sh, d_out, r: slice = slice(None), flags: int = 0) -> None:
+    def _fused_update(self, s: int) -> dict:
+        """The tp_mlp_fused_sgd fields of shard s: its w_in and w_down updated
+        into the same targets (and transposed copies, masters) as sgd()."""
+        f = {"lr": self.w.lr}
+        for key in ("w_in", "w_down"):
+            name = f"{key}.{s}"
+            f[key + "_out"] = self.new[name]
+            f[key + "_t_out"] = self.new_t[name][0] if name in self.new_t else None
+            if self.masters is not None:
+                f[key + "_master"] = self.masters[name]
+                f[key + "_master_out"] = self.new_masters[name]
+            self._fused_names.add(name)
+        return f
+
+    def _shard_backward(self, sh, d_out, r: slice = slice(None), flags: int = 0, fused: Optional[dict] = None) -> None:
         T = self.T if r.start is None else r.stop - r.start
+        grads = {} if fused else dict(d_w_in=sh["d_w_in"], d_w_down=sh["d_w_down"])
         L.tp_mlp_backward(self._desc(flags, T), L.BWD_SHARD, stream=self.stream, normed=self.normed[r],
                           pre_act=sh["pre"][r], act=sh["act"][r], w_in=sh["w_in"], w_down=sh["w_down"],
-                          d_out=d_out, d_pre=sh["d_pre"][r], d_w_in=sh["d_w_in"], d_b_in=sh["d_b_in"],
-                          d_w_down=sh["d_w_down"], d_normed_part=sh["dN_part"][r], w_down_t=sh["w_down_t"],
-                          w_in_t=sh["w_in_t"], workspace=self.workspace)
+                          d_out=d_out, d_pre=sh["d_pre"][r], d_b_in=sh["d_b_in"],
+                          d_normed_part=sh["dN_part"][r], w_down_t=sh["w_down_t"],
+                          w_in_t=sh["w_in_t"], workspace=self.workspace, fused_sgd=fused, **grads)
 
     def _norm_backward(self, dN, d_out, dx, d_norm_w, d_b_down, r: slice = slice(None), flags: int = 0,
                        parts=None) -> None:
@@ -258,6 +282,7 @@ class ShardedStep:
         with ``accumulate`` the weight gradients are added to the buffers."""
         r, T, H = rows, rows.stop - rows.start, self.H
         flags = L.ACCUMULATE_GRADS if accumulate else 0
+        self._fused_names = set()
         for sh in self.shards:
             self._shard_backward(sh, self.out[r], r, flags)
         # the backward boundary: the shards' partials summed inside the RMSNorm backward
@@ -265,12 +290,19 @@ class ShardedStep:
         self._norm_backward(self.dN[r], self.out[r], self.dx[r], self.d_norm_w, self.d_b_down, r, flags, parts=parts)
         self._dN_streamed = not self.fuse
 
-    def backward(self, mode: str = "equivalence") -> None:
+    def backward(self, mode: str = "equivalence", fused_update: bool = False) -> None:
+        """The backward of every shard, then the NORM phase.  With
+        ``fused_update`` (equivalence mode, ``fused_sgd`` steps) the shards'
+        w_in and w_down are updated inside the SHARD phase and their
+        gradients are not written; sgd() then updates the rest."""
         T, H = self.T, self.H
         fwd_abl = mode == "missing_forward_reduce" and not self.fuse
         outs = self._abl["out"] if fwd_abl else [self.out] * len(self.shards)
-        for sh, o in zip(self.shards, outs):
-            self._shard_backward(sh, o)
+        if fused_update and mode != "equivalence":
+            raise ValueError("the fused update runs in equivalence mode only")
+        self._fused_names = set()
+        for s, (sh, o) in enumerate(zip(self.shards, outs)):
+            self._shard_backward(sh, o, fused=self._fused_update(s) if fused_update else None)
         if mode == "equivalence" or self.fuse:
             # the backward boundary: the shards' partials summed inside the RMSNorm backward
             parts = None if self.fuse else [sh["dN_part"] for sh in self.shards]
@@ -288,9 +320,12 @@ class ShardedStep:
             self._norm_backward(dN, outs[s], dxs[s], dws[s], dbs[s])
 
     def sgd(self) -> None:
-        """One SGD update of every parameter tensor (one launch)."""
+        """One SGD update of every parameter tensor (one launch), except
+        those the last backward already updated (fused_update)."""
         lst = []
         for name, t in self._param_list():
+            if name in self._fused_names:
+                continue
             g = self._grad_of(name)
             if self.masters is not None:
                 e = (t, self.new[name], g, self.masters[name], self.new_masters[name], t.numel())
@@ -343,7 +378,7 @@ class ShardedStep:
                 self.backward_rows(slice(lo, hi), accumulate=i > 0)
         else:
             self.forward(mode)
-            self.backward(mode)
+            self.backward(mode, fused_update=self.fused_sgd and update and mode == "equivalence")
         if update and mode == "equivalence":
             self.sgd()
 
@@ -357,8 +392,11 @@ class ShardedStep:
         c = lambda t: t.detach().float().cpu()
         r = {"normed": c(self.normed), "rstd": c(self.rstd)}
         cat_in = (lambda ts: torch.cat(ts, dim=1)) if self.swiglu else (lambda ts: torch.cat(ts, dim=0))
-        r["d_w_in"] = cat_in([c(sh["d_w_in"]) for sh in self.shards])
-        r["d_w_down"] = torch.cat([c(sh["d_w_down"]) for sh in self.shards], dim=1)
+        if self._fused_names:  # the last backward applied these gradients without writing them
+            r["d_w_in"] = r["d_w_down"] = None
+        else:
+            r["d_w_in"] = cat_in([c(sh["d_w_in"]) for sh in self.shards])
+            r["d_w_down"] = torch.cat([c(sh["d_w_down"]) for sh in self.shards], dim=1)
         if not self.swiglu:
             r["d_b_in"] = torch.cat([c(sh["d_b_in"]) for sh in self.shards])
         r["act"] = torch.cat([c(sh["act"]) for sh in self.shards], dim=1)

@@ -157,7 +157,7 @@ def test_backward_checks(lib):
     assert L.tp_mlp_workspace_bytes(_desc(T=0), L.BWD_SHARD) == 0
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd"):
             setattr(a, name, A)
     a.workspace_bytes = need - 16
     assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EWORKSPACE
@@ -308,7 +308,7 @@ def test_fp8_checks(lib):
                                   None) == L.OK
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd"):
             setattr(a, name, A)
     a.d_b_in = None
     a.workspace_bytes = 1 << 30
@@ -394,7 +394,7 @@ def test_attention_checks(lib):
     assert need >= 4 * 2 * 64 * 4                              # delta [n_q, T] at least
     a = L.tp_attn_bwd_args()
     for name, _ in L.tp_attn_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd"):
             setattr(a, name, A)
     a.workspace_bytes = need - 16
     assert lib.tp_attn_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EWORKSPACE
@@ -420,6 +420,50 @@ def test_attention_checks(lib):
     assert bb(0, 8, 2, 1, 64, None, 256, None, None, None, None, 0, None, None) == L.OK  # empty
 
 
+def test_backward_fused_sgd_checks(lib):
+    """The SHARD phase with the update fused (tp_mlp_fused_sgd): bf16 only,
+    not with accumulated gradients, targets present and aligned, a master's
+    output given with it, and the gradients then optional; the FP8 backward
+    refuses it.  All checked before any launch."""
+    d = _desc(T=128)
+    a = L.tp_mlp_bwd_args()
+    for name, _ in L.tp_mlp_bwd_args._fields_:
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd",
+                        "d_b_in"):
+            setattr(a, name, A)
+    a.workspace_bytes = L.tp_mlp_workspace_bytes(d, L.BWD_SHARD)
+    f = L.tp_mlp_fused_sgd(lr=0.1, w_in_out=A, w_down_out=A)
+    a.fused_sgd = ctypes.pointer(f)
+    call = lambda desc=d: lib.tp_mlp_backward(ctypes.byref(desc), L.BWD_SHARD, ctypes.byref(a), None)
+    assert call(_desc(T=128, dt=L.F32)) == L.EDTYPE
+    assert call(_desc(T=128, flags=L.ACCUMULATE_GRADS)) == L.EINVAL
+    f.lr = float("nan")
+    assert call() == L.EINVAL
+    f.lr = 0.1
+    f.w_in_out = None
+    assert call() == L.EINVAL
+    f.w_in_out = MIS
+    assert call() == L.EALIGN
+    f.w_in_out = A
+    f.w_down_t_out = MIS
+    assert call() == L.EALIGN
+    f.w_down_t_out = A
+    f.w_in_master = A
+    assert call() == L.EINVAL  # no w_in_master_out
+    assert "w_in_master_out" in L.tp_mlp_last_error()
+    f.w_in_master = None
+    # the gradients are not written: NULL is accepted (checked up to the missing d_pre)
+    a.d_w_in = a.d_w_down = None
+    a.d_pre = None
+    assert call() == L.EINVAL
+    assert "d_pre" in L.tp_mlp_last_error()
+    a.d_pre = A
+    a.workspace_bytes = 1 << 30
+    fp8 = L.make_fp8_args(1, **{n: A for n in L.FP8_META_FIELDS + L.FP8_CODE_FIELDS})
+    assert lib.tp_mlp_backward_fp8(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), ctypes.byref(fp8), None) == L.EINVAL
+    assert "fused_sgd" in L.tp_mlp_last_error()
+
+
 def test_backward_norm_parts_checks(lib):
     """The NORM phase's streamed partials: count in [0, 64], a non-NULL
     array when the count is positive, every part non-NULL and aligned; all
@@ -427,7 +471,7 @@ def test_backward_norm_parts_checks(lib):
     d = _desc(T=128)
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd"):
             setattr(a, name, A)
     a.workspace_bytes = L.tp_mlp_workspace_bytes(d, L.BWD_NORM)
     a.n_d_normed_parts = 65

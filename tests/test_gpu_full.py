@@ -2,9 +2,14 @@
 
 Each full workload (GPT-2-small GeLU tp=1, Llama-3-8B TP=8 with all 8
 shards, one Llama-3-70B TP=8 rank, Llama-3-8B full width with fp32 masters)
-runs once on the GPU exactly as bench.py times it (ShardedStep, new
-parameters written out of place); every tensor it stores is copied to the
-host, and then:
+runs once on the GPU as bench.py times it (ShardedStep, new parameters
+written out of place) but with the weight gradients written; every tensor it
+stores is copied to the host, and then:
+
+* test_fused_update_bitwise: the step exactly as bench.py times it, with the
+  weight matrices' SGD update taken inside their weight-gradient GEMMs
+  (gradients never written), gives the same bits in every parameter,
+  transposed copy, master, out, dx and norm/bias gradient.
 
 * test_stage: every kernel's output, element by element over the whole
   tensor, against the fp64 oracle stage fed the GPU's own stored inputs
@@ -76,9 +81,35 @@ def full(request):
     st.step()
     torch.cuda.synchronize()
     h = collect(st)
-    del st
+    # the benchmark's step takes the weight matrices' update inside their weight-gradient GEMMs: its
+    # new parameters (transposed copies, masters) must be the bits of the step above
+    fu = ShardedStep(w, t, device="cuda:0", out_of_place_sgd=True, fused_sgd=True)
+    fu.step()
+    torch.cuda.synchronize()
+    bits = lambda x: x.view(torch.int16 if x.element_size() == 2 else torch.int32)
+    diff = lambda a, b: int((bits(a) != bits(b)).sum())
+    mism = {}
+    for name, _ in st._param_list():
+        mism["new " + name] = diff(fu.new[name], st.new[name])
+        if w.master:
+            mism["master " + name] = diff(fu.new_masters[name], st.new_masters[name])
+    for key, (tt, _, _) in st.new_t.items():
+        mism["transposed " + key] = diff(fu.new_t[key][0], tt)
+    for attr in ("out", "dx", "d_norm_w", "d_b_down"):
+        mism[attr] = diff(getattr(fu, attr), getattr(st, attr))
+    h["fused_mismatch"] = mism
+    del st, fu
     torch.cuda.empty_cache()
     yield w, t, h
+
+
+def test_fused_update_bitwise(full):
+    """The step as the benchmark times it (update fused into the weight-gradient
+    GEMMs) writes the same bits as the step whose every tensor is checked here."""
+    w, _, h = full
+    bad = {k: v for k, v in h["fused_mismatch"].items() if v}
+    say(f"  {w.name}: fused vs unfused, {len(h['fused_mismatch'])} tensors compared, differing: {bad}")
+    assert not bad
 
 
 @pytest.mark.parametrize("stage", STAGES)
