@@ -113,7 +113,11 @@ def hbm_bytes_per_step(w) -> dict:
             ks = gemm_ksplit(M, N, T)
             if ks > 1:
                 ksplit_bytes += S * M * N * (ks * 4 + upd + es)
+    # with the update fused and the w_in gradient GEMM on K-contiguous operands (no masters, T a multiple
+    # of 8, k not split), N is transposed once per step
+    nt = fused and not w.master and T % 8 == 0 and gemm_ksplit(P, H, T) == 1
     return {
+        "transpose_bf16": 2 * T * H * es if nt else 0,
         "sgd_ksplit": ksplit_bytes,
         "rmsnorm_fwd": T * H * 2 * es + 4 * T + H * es,                 # x in, N out, rstd out, w in
         "partial_sum_residual": S * 4 * T * H + 2 * es * T * H + H * es,  # S fp32 partials + x in, out

@@ -262,6 +262,19 @@ typedef struct {
      is an error; GeLU's d_b_in is still written.  NULL: the gradients are
      written and the update is the caller's (tp_mlp_sgd_step_multi). */
   const tp_mlp_fused_sgd* fused_sgd;
+  /* SHARD phase, optional (bf16, T a multiple of 8): the activations of the
+     w_in weight-gradient GEMM in the layout that makes its k (the tokens)
+     contiguous in both operands.
+       d_pre_t   [2F | F, T] written: the transpose of d_pre (written with it;
+                 needs w_down_t).
+       normed_t  [H, T] read: the transpose of normed (tp_mlp_transpose_bf16).
+     When both are given with fused_sgd (no w_in masters), w_in_t and a
+     w_in weight-gradient GEMM whose k is not split, that GEMM forms dW_in^T
+     = normed_t d_pre_t^T and the update writes w_in_t_out from it directly
+     and w_in_out transposed: the same values.  Otherwise they change nothing
+     but the extra write of d_pre_t. */
+  const void* normed_t;
+  void* d_pre_t;
 } tp_mlp_bwd_args;
 
 /*

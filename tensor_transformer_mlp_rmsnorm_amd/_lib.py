@@ -84,7 +84,7 @@ class tp_mlp_bwd_args(ctypes.Structure):
                                    "d_pre", "d_w_in", "d_b_in", "d_w_down", "d_normed_part", "d_normed", "d_x",
                                    "d_norm_w", "d_b_down", "workspace")] + [("workspace_bytes", ctypes.c_size_t)] + \
         [("d_normed_parts", ctypes.POINTER(_vp)), ("n_d_normed_parts", ctypes.c_int32), ("w_down_t", _vp),
-         ("w_in_t", _vp), ("fused_sgd", ctypes.POINTER(tp_mlp_fused_sgd))]
+         ("w_in_t", _vp), ("fused_sgd", ctypes.POINTER(tp_mlp_fused_sgd)), ("normed_t", _vp), ("d_pre_t", _vp)]
 
 
 FP8_META_FIELDS = ("meta_normed", "meta_w_in", "meta_act", "meta_w_down", "meta_d_out", "meta_d_pre")

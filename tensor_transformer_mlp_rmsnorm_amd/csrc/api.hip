@@ -378,6 +378,19 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
     REQUIRE_PTR(a->d_normed_part);
   }
   const int64_t P = swiglu ? 2 * F : F;  // width of pre-activations
+  if (a->d_pre_t || a->normed_t) {
+    if (dt != kBF16) return fail(TP_MLP_EDTYPE, "%s: d_pre_t / normed_t are taken for bf16 only", fn);
+    if (T % 8 != 0) return fail(TP_MLP_ESHAPE, "%s: d_pre_t / normed_t need T a multiple of 8", fn);
+    if (a->d_pre_t && !aligned16(a->d_pre_t)) return fail(TP_MLP_EALIGN, "%s: 'd_pre_t' is not 16-byte aligned", fn);
+    if (a->normed_t && !aligned16(a->normed_t))
+      return fail(TP_MLP_EALIGN, "%s: 'normed_t' is not 16-byte aligned", fn);
+    if (a->d_pre_t && !a->w_down_t) return fail(TP_MLP_EINVAL, "%s: d_pre_t needs w_down_t", fn);
+  }
+  // The w_in weight-gradient GEMM on K-contiguous operands (dW_in^T = normed_t d_pre_t^T): with the
+  // update fused, no w_in masters (they are laid out as w_in), the old values read from w_in_t, and k
+  // not split.
+  const bool b4_nt = fu && !fu->w_in_master && a->w_in_t && a->normed_t && a->d_pre_t && T > 0 &&
+                     gemm_ksplit(P, H, T) == 1;
 
   // d_act = d_out Wd ([T,H] x [H,F]), with the activation backward fused.  In
   // bf16 both operands are made K-contiguous (Wd^T [F, H] in the workspace) for
@@ -403,7 +416,10 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
       b1.B = a->workspace;
     }
     b1.ldb = H;
-    CHECK_HIP(launch_gemm(dt, true, true, act_bwd, b1, s), "d_act GEMM");
+    b1.pre_t = a->d_pre_t;  // the transposed copy of d_pre as well, when asked for
+    b1.ld_t = T;
+    const Epi e1 = a->d_pre_t ? (swiglu ? kEpiSwigluBwdT : kEpiGeluBwdT) : act_bwd;
+    CHECK_HIP(launch_gemm(dt, true, true, e1, b1, s), "d_act GEMM");
   } else {
     CHECK_HIP(launch_gemm(dt, true, false, act_bwd, b1, s), "d_act GEMM");
   }
@@ -425,7 +441,8 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
   b2.ws = static_cast<float*>(a->workspace);
   b2.accum = accum;
   if (fu) {
-    b2.sgd = SgdEpi{a->w_down, fu->w_down_out, fu->w_down_t_out, fu->w_down_master, fu->w_down_master_out, fu->lr};
+    b2.sgd = SgdEpi{a->w_down, a->w_down_t, fu->w_down_out, fu->w_down_t_out, fu->w_down_master,
+                    fu->w_down_master_out, fu->lr};
     CHECK_HIP(launch_gemm(dt, false, false, kEpiSgd, b2, s), "d_w_down GEMM + SGD");
   } else {
     CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b2, s), "d_w_down GEMM");
@@ -447,9 +464,21 @@ int backward_checked(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_args*
   b4.ksplit = gemm_ksplit(b4.M, b4.N, b4.K);
   b4.ws = static_cast<float*>(a->workspace);
   b4.accum = accum;
-  if (fu) b4.sgd = SgdEpi{a->w_in, fu->w_in_out, fu->w_in_t_out, fu->w_in_master, fu->w_in_master_out, fu->lr};
+  if (fu)
+    b4.sgd = SgdEpi{a->w_in, a->w_in_t, fu->w_in_out, fu->w_in_t_out, fu->w_in_master, fu->w_in_master_out, fu->lr};
+  if (b4_nt) {  // dW_in^T [H, P] = normed_t [H, T] x d_pre_t [P, T]^T
+    b4.M = H;
+    b4.N = P;
+    b4.A = a->normed_t;
+    b4.lda = T;
+    b4.B = a->d_pre_t;
+    b4.ldb = T;
+    b4.ksplit = 1;
+  }
   auto run_b4 = [&]() -> int {
-    if (fu) {
+    if (b4_nt) {
+      CHECK_HIP(launch_gemm(dt, true, true, kEpiSgdT, b4, s), "d_w_in^T GEMM + SGD");
+    } else if (fu) {
       CHECK_HIP(launch_gemm(dt, false, false, kEpiSgd, b4, s), "d_w_in GEMM + SGD");
     } else {
       CHECK_HIP(launch_gemm(dt, false, false, kEpiStoreF32, b4, s), "d_w_in GEMM");

@@ -338,32 +338,44 @@ __global__ __launch_bounds__(256) void ksplit_reduce_bf16_kernel(bf16_t* __restr
 // 8) through 64 x 64 LDS tiles, 16-byte loads along C and 16-byte stores
 // along R.  With a row pitch of 33 dwords the 8 rows that one store gathers
 // (of one column) sit on distinct banks across a wave.
-constexpr int kTrTile = 64, kTrPitch = 66;  // bf16 elements per LDS row
+constexpr int kTrTile = 64;
+// out [C, R] = in [R, C]^T in 64 x 64 tiles: each thread loads two 16-byte row
+// chunks into an LDS tile whose rows are padded to 144 bytes, then reads 8
+// rows x 2 adjacent columns back with 4-byte reads and stores the two
+// 8-element column chunks (eight consecutive lanes cover one column pair, so
+// each wave writes whole 128-byte segments): the transposed store of
+// sgd_t_tile.  R and C are multiples of 8.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* __restrict__ in, bf16_t* __restrict__ out,
                                                               int64_t R, int64_t C, int tiles_c) {
-  __shared__ uint32_t tile[kTrTile * kTrPitch / 2];
+  __shared__ __align__(16) bf16_t tile[kTrTile][kTrTile + 8];
   const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * kTrTile, c0 = (int64_t)(blockIdx.x % tiles_c) * kTrTile;
-  for (int i = threadIdx.x; i < kTrTile * 8; i += 256) {
-    const int row = i >> 3, ch = i & 7;  // input row r0 + row, columns c0 + 8 ch .. + 7
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + row < R && c0 + ch * 8 < C) v = *reinterpret_cast<const uint4*>(in + (r0 + row) * C + c0 + ch * 8);
-    uint32_t* d = tile + row * (kTrPitch / 2) + ch * 4;
-    d[0] = v.x;
-    d[1] = v.y;
-    d[2] = v.z;
-    d[3] = v.w;
+  uint4 v[2];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {  // both loads issued before either LDS store
+    const int ch = threadIdx.x + 256 * pass, row = ch >> 3, col8 = (ch & 7) * 8;
+    v[pass] = (r0 + row < R && c0 + col8 < C) ? *reinterpret_cast<const uint4*>(in + (r0 + row) * C + c0 + col8)
+                                              : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int ch = threadIdx.x + 256 * pass, row = ch >> 3, col8 = (ch & 7) * 8;
+    *reinterpret_cast<uint4*>(&tile[row][col8]) = v[pass];
   }
   __syncthreads();
-  const bf16_t* t16 = reinterpret_cast<const bf16_t*>(tile);
-  for (int i = threadIdx.x; i < kTrTile * 8; i += 256) {
-    const int oc = i >> 3, ch = i & 7;  // output row c0 + oc, columns r0 + 8 ch .. + 7
-    if (c0 + oc >= C || r0 + ch * 8 >= R) continue;
-    uint32_t w[4];
+  const int c = 2 * (threadIdx.x >> 3), rr = 8 * (threadIdx.x & 7);
+  const int64_t gc = c0 + c, gr = r0 + rr;
+  if (gc < C && gr < R) {
+    uint32_t w[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = (uint32_t)t16[(8 * ch + 2 * j) * kTrPitch + oc] |
-             ((uint32_t)t16[(8 * ch + 2 * j + 1) * kTrPitch + oc] << 16);
-    *reinterpret_cast<uint4*>(out + (c0 + oc) * R + r0 + ch * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int i = 0; i < 8; ++i) w[i] = *reinterpret_cast<const uint32_t*>(&tile[rr + i][c]);
+    uint32_t lo[4], hi[4];  // column c (low halves) and column c + 1 (high halves), rows rr .. rr + 7
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = (w[2 * i] & 0xffffu) | (w[2 * i + 1] << 16);
+      hi[i] = (w[2 * i] >> 16) | (w[2 * i + 1] & 0xffff0000u);
+    }
+    *reinterpret_cast<uint4*>(out + gc * R + gr) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4*>(out + (gc + 1) * R + gr) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
   }
 }
 

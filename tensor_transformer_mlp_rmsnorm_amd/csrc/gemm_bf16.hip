@@ -75,6 +75,12 @@ struct Tile224x256 {
 };
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// 4 values rounded to bf16 as store4<bf16_t> stores them.
+__device__ __forceinline__ uint2 pack_bf16x4(floatx4 v) {
+  return make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                    (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+}
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 
@@ -278,9 +284,11 @@ __device__ __forceinline__ void read_half(uint4 (&af)[WMB], uint4 (&bf)[WNB], co
 // unconditionally (addresses clamped into the tensor; lanes outside it discard
 // what they read), so a wave waits for memory about once per block instead of
 // once per load; only the stores are guarded.
-template <int EPI, int WMB, int WNB>
+// With STASH, the stored bf16 bits of each block's dg and du (or dh) are also
+// left in stash[i][j][0 | 1] for the transposed copy.
+template <int EPI, int WMB, int WNB, bool STASH = false>
 __device__ __forceinline__ void epilogue_act_bwd(const GemmArgs& g, const floatx4 (&acc)[WMB][WNB], int64_t m0,
-                                                 int64_t n0, int lane) {
+                                                 int64_t n0, int lane, uint2 (*stash)[WNB][2] = nullptr) {
   static_assert(EPI == kEpiSwigluBwd || EPI == kEpiGeluBwd, "activation backward epilogues only");
   constexpr bool kSwiglu = EPI == kEpiSwigluBwd;
   constexpr int NL = kSwiglu ? 2 : 1;  // saved tensors per output: g and u, or h
@@ -343,12 +351,17 @@ __device__ __forceinline__ void epilogue_act_bwd(const GemmArgs& g, const floatx
           store4<bf16_t>(out + m * ld + n, dg);
           store4<bf16_t>(out + m * ld + second + n, du);
         }
+        if constexpr (STASH) {
+          stash[i][j][0] = pack_bf16x4(dg);
+          stash[i][j][1] = pack_bf16x4(du);
+        }
       } else {
         const floatx4 h = unpack(cur[j][0]);
         floatx4 dh;
 #pragma unroll
         for (int r = 0; r < 4; ++r) dh[r] = v[r] * gelu_grad_f(h[r]);
         if (m < M && n < N) store4<bf16_t>(out + m * ld + n, dh);
+        if constexpr (STASH) stash[i][j][0] = pack_bf16x4(dh);
       }
     }
   }
@@ -474,81 +487,99 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const floatx4 (&acc)
 }
 
 
-// kEpiSgd (two-stage kernels): the product is the gradient dW of a bf16 weight
-// W [M, N] and the SGD step is taken here, so dW never goes to memory.  Each
-// lane updates its 4 consecutive columns of a row exactly as the SGD kernels
-// do (sgd_value: one fma, then the round to bf16) and stores them row-major.
-// For the transposed copy W_t [N, M] the tile goes through LDS as [TN][TM + 8]
-// bf16 (the main loop's stages are free by then): lanes of neighbouring rows
-// swap halves so that each writes whole dwords (two rows of one column), the
-// 16-byte row pad puts the 8 column rows of one store in distinct banks, and
-// every thread then writes 16-byte chunks of the transposed rows.
-template <class SH>
-constexpr size_t sgd_stage_bytes() {
-  return (size_t)SH::TN * (SH::TM + 8) * sizeof(bf16_t);
+// Transposed stores of an output tile through LDS (the main loop's LDS is
+// free by then).  A lane holds 4 consecutive columns ln .. ln + 3 of one tile
+// row lm; the tile is staged as [columns][TM + 8] bf16 (a column of the tile
+// becomes a row): lanes of neighbouring rows (lane ^ 1) swap halves so that
+// each writes whole dwords holding two rows of one column, and the 16-byte row
+// pad puts the 8 rows one dword store touches in distinct banks.  Then every
+// thread writes 16-byte chunks of the staged rows.
+template <int kPitch>
+__device__ __forceinline__ void stage_t4(bf16_t* lds, int lm, int ln, uint2 bits, bool odd) {
+  const uint32_t b0 = bits.x & 0xffffu, b1 = bits.x >> 16, b2 = bits.y & 0xffffu, b3 = bits.y >> 16;
+  // even lanes (row lm) keep columns 0, 1 and take the odd neighbour's (row lm + 1); odd lanes keep
+  // columns 2, 3 and take the even neighbour's (row lm - 1)
+  const uint32_t send = odd ? (b0 | (b1 << 16)) : (b2 | (b3 << 16));
+  const uint32_t recv = (uint32_t)__shfl_xor((int)send, 1, kWave);
+  const int c0 = odd ? 2 : 0, r0 = odd ? lm - 1 : lm;
+  const uint32_t lo = odd ? (recv & 0xffffu) | (b2 << 16) : b0 | (recv << 16);
+  const uint32_t hi = odd ? (recv >> 16) | (b3 << 16) : b1 | (recv & 0xffff0000u);
+  *reinterpret_cast<uint32_t*>(lds + (ln + c0) * kPitch + r0) = lo;
+  *reinterpret_cast<uint32_t*>(lds + (ln + c0 + 1) * kPitch + r0) = hi;
 }
 
-template <class SH, bool MASTER>
-__device__ __forceinline__ void epilogue_sgd(const GemmArgs& g, const floatx4 (&acc)[SH::WMB][SH::WNB],
-                                             int64_t tile_m0, int64_t tile_n0, int wm, int wn, int lane,
-                                             uint4* smem) {
-  constexpr int kPitch = SH::TM + 8;  // bf16 per LDS row (one transposed row: a column of W)
+// The staged tile's rows c < TN (tile columns n0 + c < N) to dst[(n0 + c) * ld + m0 + r], r < TM
+// (m0 + r < M; M a multiple of 8, so a 16-byte chunk is wholly inside or outside).
+template <int TM, int TN, int NTHREADS>
+__device__ __forceinline__ void store_t_tile(const bf16_t* lds, bf16_t* dst, int64_t ld, int64_t m0, int64_t n0,
+                                             int64_t M, int64_t N) {
+  constexpr int kPitch = TM + 8, kChunks = TM / 8;
+  for (int c = threadIdx.x; c < TN * kChunks; c += NTHREADS) {
+    const int ln = c / kChunks, lc = (c - ln * kChunks) * 8;
+    const int64_t n = n0 + ln, m = m0 + lc;
+    if (n < N && m < M)
+      *reinterpret_cast<uint4*>(dst + n * ld + m) = *reinterpret_cast<const uint4*>(lds + ln * kPitch + lc);
+  }
+}
+
+template <int TM, int TN>
+constexpr size_t t_stage_bytes() {
+  return (size_t)TN * (TM + 8) * sizeof(bf16_t);
+}
+
+// kEpiSgd / kEpiSgdT: the product is the gradient of a bf16 weight and the SGD
+// step is taken here, so the gradient never goes to memory.  Each lane updates
+// its 4 consecutive columns of a row exactly as the SGD kernels do (sgd_value:
+// one fma, then the round to bf16) and stores them in the product's layout;
+// the transposed layout goes through LDS (stage_t4, store_t_tile).
+//   kEpiSgd:  the product is dW, W [M, N]: old values from w_in (or the
+//             masters m_in), W to w_out directly, W^T [N, M] to w_out_t.
+//   kEpiSgdT: the product is dW^T, W [N, M]: old values from w_in_t (W^T, in
+//             the product's layout), W^T to w_out_t directly, W to w_out.
+// The tile is TM x TN from (tile_m0, tile_n0), the wave's blocks from (wr0,
+// wc0) within it; NTHREADS threads per workgroup.
+template <int TM, int TN, int WMB, int WNB, int NTHREADS, bool MASTER, bool ROLE_T>
+__device__ __forceinline__ void epilogue_sgd(const GemmArgs& g, const floatx4 (&acc)[WMB][WNB], int64_t tile_m0,
+                                             int64_t tile_n0, int wr0, int wc0, int lane, uint4* smem) {
+  static_assert(!(MASTER && ROLE_T), "the transposed-role update keeps no masters");
+  constexpr int kPitch = TM + 8;  // bf16 per LDS row (one column of the tile)
   const int64_t M = g.M, N = g.N;
   const SgdEpi& u = g.sgd;
   const float lr = u.lr;
-  const bf16_t* __restrict__ w_in = static_cast<const bf16_t*>(u.w_in);
-  bf16_t* __restrict__ w_out = static_cast<bf16_t*>(u.w_out);
-  bf16_t* const w_out_t = static_cast<bf16_t*>(u.w_out_t);
+  const bf16_t* __restrict__ src = static_cast<const bf16_t*>(ROLE_T ? u.w_in_t : u.w_in);
+  bf16_t* const direct = static_cast<bf16_t*>(ROLE_T ? u.w_out_t : u.w_out);
+  bf16_t* const trans = static_cast<bf16_t*>(ROLE_T ? u.w_out : u.w_out_t);
   bf16_t* const lds = reinterpret_cast<bf16_t*>(smem);
   const int frow = lane & 15, col4 = 4 * (lane >> 4);
   const bool odd = lane & 1;
-  __syncthreads();  // every wave is past its last read of the main loop's stages
+  __syncthreads();  // every wave is past its last read of the main loop's LDS
 #pragma unroll
-  for (int i = 0; i < SH::WMB; ++i) {
-    const int lm = wm * SH::WMB * 16 + i * 16 + frow;  // row of W within the tile
+  for (int i = 0; i < WMB; ++i) {
+    const int lm = wr0 + i * 16 + frow;  // row of the product within the tile
     const int64_t m = tile_m0 + lm;
-    floatx4 p[SH::WNB];
+    floatx4 p[WNB];
 #pragma unroll
-    for (int j = 0; j < SH::WNB; ++j) {  // the old values of the row's blocks, loaded together
-      const int64_t n = tile_n0 + wn * SH::WNB * 16 + j * 16 + col4;
+    for (int j = 0; j < WNB; ++j) {  // the old values of the row's blocks, loaded together
+      const int64_t n = tile_n0 + wc0 + j * 16 + col4;
       const bool ok = m < M && n < N;  // (N is a multiple of 4: the lane's 4 columns are whole)
       if constexpr (MASTER) p[j] = ok ? load4<float>(u.m_in + m * N + n) : floatx4{0.f, 0.f, 0.f, 0.f};
-      else p[j] = ok ? load4<bf16_t>(w_in + m * N + n) : floatx4{0.f, 0.f, 0.f, 0.f};
+      else p[j] = ok ? load4<bf16_t>(src + m * N + n) : floatx4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int j = 0; j < SH::WNB; ++j) {
-      const int ln = wn * SH::WNB * 16 + j * 16 + col4;  // column of W within the tile
+    for (int j = 0; j < WNB; ++j) {
+      const int ln = wc0 + j * 16 + col4;  // column of the product within the tile
       const int64_t n = tile_n0 + ln;
-      const bool ok = m < M && n < N;
       const floatx4 v = sgd_value4(p[j], acc[i][j], lr);
-      if (ok) {
+      if (m < M && n < N) {
         if constexpr (MASTER) store4<float>(u.m_out + m * N + n, v);
-        store4<bf16_t>(w_out + m * N + n, v);
+        if (direct) store4<bf16_t>(direct + m * N + n, v);
       }
-      if (w_out_t) {
-        const uint32_t b0 = f32_to_bf16(v[0]), b1 = f32_to_bf16(v[1]), b2 = f32_to_bf16(v[2]),
-                       b3 = f32_to_bf16(v[3]);
-        // even lanes (row lm) keep columns 0, 1 and take the odd neighbour's (row lm + 1); odd lanes
-        // keep columns 2, 3 and take the even neighbour's (row lm - 1)
-        const uint32_t send = odd ? (b0 | (b1 << 16)) : (b2 | (b3 << 16));
-        const uint32_t recv = (uint32_t)__shfl_xor((int)send, 1, kWave);
-        const int c0 = odd ? 2 : 0, r0 = odd ? lm - 1 : lm;
-        const uint32_t lo = odd ? (recv & 0xffffu) | (b2 << 16) : b0 | (recv << 16);
-        const uint32_t hi = odd ? (recv >> 16) | (b3 << 16) : b1 | (recv & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(lds + (ln + c0) * kPitch + r0) = lo;
-        *reinterpret_cast<uint32_t*>(lds + (ln + c0 + 1) * kPitch + r0) = hi;
-      }
+      if (trans) stage_t4<kPitch>(lds, lm, ln, pack_bf16x4(v), odd);
     }
   }
-  if (!w_out_t) return;  // (uniform)
+  if (!trans) return;  // (uniform)
   __syncthreads();
-  constexpr int kChunks = SH::TM / 8;  // 16-byte chunks per transposed row
-  for (int c = threadIdx.x; c < SH::TN * kChunks; c += SH::NW * 64) {
-    const int ln = c / kChunks, lc = (c - ln * kChunks) * 8;
-    const int64_t n = tile_n0 + ln, m = tile_m0 + lc;
-    if (n < N && m < M)  // (M is a multiple of 8: a chunk is wholly inside or outside)
-      *reinterpret_cast<uint4*>(w_out_t + n * M + m) = *reinterpret_cast<const uint4*>(lds + ln * kPitch + lc);
-  }
+  store_t_tile<TM, TN, NTHREADS>(lds, trans, M, tile_m0, tile_n0, M, N);
 }
 
 // Ping-pong fragment reads: the 24 ds_read_b128 of one k-tile (A: 8 row blocks,
@@ -796,8 +827,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
 #pragma unroll
       for (int j = 0; j < WNB; ++j) acc[i][j] *= deq;
   }
-  epilogue<EPI, WMB, WNB>(g, acc, (int64_t)tm * kBM + PT::row0(wave), (int64_t)tn * PT::TN + PT::col0(wave),
-                          (int64_t)tn * kTileChans + (PT::col0(wave) / (2 * kWaveChans)) * kWaveChans, ks, lane);
+  const int64_t tile_m0 = (int64_t)tm * kBM, tile_n0 = (int64_t)tn * PT::TN;
+  if constexpr (EPI == kEpiSgdT) {
+    epilogue_sgd<kBM, PT::TN, WMB, WNB, kThreads, false, true>(g, acc, tile_m0, tile_n0, PT::row0(wave),
+                                                               PT::col0(wave), lane, smem);
+  } else if constexpr (EPI == kEpiSwigluBwdT || EPI == kEpiGeluBwdT) {
+    // the activation backward, then d_pre transposed (gate rows, then up rows) through LDS
+    constexpr int kBase = EPI == kEpiSwigluBwdT ? kEpiSwigluBwd : kEpiGeluBwd;
+    constexpr int NL = EPI == kEpiSwigluBwdT ? 2 : 1;
+    uint2 stash[WMB][WNB][2];
+    epilogue_act_bwd<kBase, WMB, WNB, true>(g, acc, tile_m0 + PT::row0(wave), tile_n0 + PT::col0(wave), lane, stash);
+    constexpr int kPitch = kBM + 8;
+    bf16_t* const lds = reinterpret_cast<bf16_t*>(smem);
+    const int frow = lane & 15, col4 = 4 * (lane >> 4);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      __syncthreads();  // the LDS is free: the main loop (l = 0) or the previous half's stores are done
+#pragma unroll
+      for (int i = 0; i < WMB; ++i)
+#pragma unroll
+        for (int j = 0; j < WNB; ++j)
+          stage_t4<kPitch>(lds, PT::row0(wave) + i * 16 + frow, PT::col0(wave) + j * 16 + col4, stash[i][j][l],
+                           lane & 1);
+      __syncthreads();
+      store_t_tile<kBM, PT::TN, kThreads>(lds, static_cast<bf16_t*>(g.pre_t) + (int64_t)l * g.ffn * g.ld_t, g.ld_t,
+                                          tile_m0, tile_n0, g.M, g.N);
+    }
+  } else {
+    epilogue<EPI, WMB, WNB>(g, acc, tile_m0 + PT::row0(wave), tile_n0 + PT::col0(wave),
+                            (int64_t)tn * kTileChans + (PT::col0(wave) / (2 * kWaveChans)) * kWaveChans, ks, lane);
+  }
 }
 
 template <bool AK, bool BKC, int EPI, class SH>
@@ -856,8 +915,14 @@ __global__ __launch_bounds__(SH::NW * 64, 1) void gemm_bf16_kernel(GemmArgs g, i
   }
 
   if constexpr (EPI == kEpiSgd) {
-    if (g.sgd.m_in) epilogue_sgd<SH, true>(g, acc, (int64_t)tm * SH::TM, (int64_t)tn * SH::TN, wm, wn, lane, smem);
-    else epilogue_sgd<SH, false>(g, acc, (int64_t)tm * SH::TM, (int64_t)tn * SH::TN, wm, wn, lane, smem);
+    constexpr int NT = SH::NW * 64;
+    const int wr0 = wm * SH::WMB * 16, wc0 = wn * SH::WNB * 16;
+    if (g.sgd.m_in)
+      epilogue_sgd<SH::TM, SH::TN, SH::WMB, SH::WNB, NT, true, false>(g, acc, (int64_t)tm * SH::TM,
+                                                                      (int64_t)tn * SH::TN, wr0, wc0, lane, smem);
+    else
+      epilogue_sgd<SH::TM, SH::TN, SH::WMB, SH::WNB, NT, false, false>(g, acc, (int64_t)tm * SH::TM,
+                                                                       (int64_t)tn * SH::TN, wr0, wc0, lane, smem);
   } else {
     epilogue<EPI, SH::WMB, SH::WNB>(g, acc, (int64_t)tm * SH::TM + wm * SH::WMB * 16,
                                     (int64_t)tn * SH::TN + wn * SH::WNB * 16, 0, ks, lane);
@@ -937,8 +1002,14 @@ __global__ __launch_bounds__(SH::NW * 64, 1) void gemm_bf16_pipe_kernel(GemmArgs
   }
 
   if constexpr (EPI == kEpiSgd) {
-    if (g.sgd.m_in) epilogue_sgd<SH, true>(g, acc, (int64_t)tm * SH::TM, (int64_t)tn * SH::TN, wm, wn, lane, smem);
-    else epilogue_sgd<SH, false>(g, acc, (int64_t)tm * SH::TM, (int64_t)tn * SH::TN, wm, wn, lane, smem);
+    constexpr int NT = SH::NW * 64;
+    const int wr0 = wm * SH::WMB * 16, wc0 = wn * SH::WNB * 16;
+    if (g.sgd.m_in)
+      epilogue_sgd<SH::TM, SH::TN, SH::WMB, SH::WNB, NT, true, false>(g, acc, (int64_t)tm * SH::TM,
+                                                                      (int64_t)tn * SH::TN, wr0, wc0, lane, smem);
+    else
+      epilogue_sgd<SH::TM, SH::TN, SH::WMB, SH::WNB, NT, false, false>(g, acc, (int64_t)tm * SH::TM,
+                                                                       (int64_t)tn * SH::TN, wr0, wc0, lane, smem);
   } else {
     epilogue<EPI, SH::WMB, SH::WNB>(g, acc, (int64_t)tm * SH::TM + wm * SH::WMB * 16,
                                     (int64_t)tn * SH::TN + wn * SH::WNB * 16, 0, ks, lane);
@@ -987,7 +1058,8 @@ hipError_t launch_two_stage(const GemmArgs& ga, hipStream_t s) {
   if constexpr (pipelined_loop<AK, BKC, SH>()) kernel = gemm_bf16_pipe_kernel<AK, BKC, EPI, SH>;
   else kernel = gemm_bf16_kernel<AK, BKC, EPI, SH>;
   // the SGD epilogue stages the transposed tile in LDS: [TN][TM + 8] bf16 (132 KiB for 256 x 256)
-  constexpr size_t smem = EPI == kEpiSgd && sgd_stage_bytes<SH>() > kSmemBytes ? sgd_stage_bytes<SH>() : kSmemBytes;
+  constexpr size_t stage = t_stage_bytes<SH::TM, SH::TN>();
+  constexpr size_t smem = EPI == kEpiSgd && stage > kSmemBytes ? stage : kSmemBytes;
   static_assert(smem <= 160 * 1024, "LDS of one CU");
   static bool configured = false;  // raise the dynamic LDS limit once per instantiation
   if (!configured) {
@@ -1096,6 +1168,9 @@ hipError_t launch_gemm_bf16(bool ak, bool bk, Epi epi, const GemmArgs& g, hipStr
       case kEpiStoreBf16: return launch_t<true, true, kEpiStoreBf16>(g, s);
       case kEpiSwigluBwd: return launch_t<true, true, kEpiSwigluBwd>(g, s);
       case kEpiGeluBwd: return launch_t<true, true, kEpiGeluBwd>(g, s);
+      case kEpiSwigluBwdT: return launch_t<true, true, kEpiSwigluBwdT>(g, s);
+      case kEpiGeluBwdT: return launch_t<true, true, kEpiGeluBwdT>(g, s);
+      case kEpiSgdT: return launch_t<true, true, kEpiSgdT>(g, s);
       default: break;
     }
   } else if (ak && !bk) {

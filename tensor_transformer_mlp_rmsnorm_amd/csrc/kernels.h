@@ -36,14 +36,21 @@ enum Epi {
   kEpiGeluBwd = 5,    // dh = d_act * gelu'(h)
   kEpiStoreBf16 = 6,  // C bf16 [M, ldc]
   kEpiSgd = 7,        // the product is the gradient of a bf16 weight [M, N]: SGD update applied (GemmArgs.sgd)
+  kEpiSgdT = 8,       // the product is the gradient of W^T for a bf16 weight W [N, M]: the same update
+  kEpiSwigluBwdT = 9, // kEpiSwigluBwd, and d_pre also written transposed to pre_t
+  kEpiGeluBwdT = 10,  // kEpiGeluBwd, and d_pre also written transposed to pre_t
 };
 
 // kEpiSgd: where the update of a weight W [M, N] (bf16, row-major) goes.  The
 // product C = dW is never stored; W_out = round(W_in - lr C), or with fp32
 // masters M_out = M_in - lr C and W_out = round(M_out); W_out_t (optional)
 // receives the same values transposed, [N, M].  Outputs may equal inputs.
+// kEpiSgdT: the product is dW^T [M, N] of a weight W [N, M]; the old values
+// are read from w_in_t (W^T), W^T goes to w_out_t and W to w_out (either may
+// be null); no masters.
 struct SgdEpi {
   const void* w_in;
+  const void* w_in_t;
   void* w_out;
   void* w_out_t;
   const float* m_in;
@@ -85,6 +92,10 @@ struct GemmArgs {
   // kEpiSgd only (with a k split, every slice goes to ws and a second kernel
   // sums them in index order and applies the update)
   SgdEpi sgd;
+  // kEpiSwigluBwdT / kEpiGeluBwdT: d_pre transposed, [2F | F rows][ld_t] (M a
+  // multiple of 8); the up half's rows follow the gate half's
+  void* pre_t;
+  int64_t ld_t;
 };
 
 // Number of k-slices for a bf16 fp32-output GEMM: a function of the shape only

@@ -57,7 +57,7 @@ struct RawVec<bf16_t> {
 // Forward: one wave per row, 4 waves per workgroup, each wave taking rows
 // w, w + 4, w + 8, w + 12 of the workgroup's 16; the norm weight is read once
 // per wave and the next row is loaded while the current one is reduced.
-constexpr int kFwdWaves = 4, kFwdRowsPerWave = 4, kFwdRowsPerBlock = kFwdWaves * kFwdRowsPerWave;
+constexpr int kFwdWaves = 4, kFwdRowsPerWave = 1, kFwdRowsPerBlock = kFwdWaves * kFwdRowsPerWave;
 
 // FULL: the row is exactly NC chunks per lane (no lane past its end), so no
 // access needs a guard.

@@ -50,6 +50,19 @@ def _torch_dtype(name: str):
     return {"bf16": torch.bfloat16, "fp32": torch.float32}[name]
 
 
+def _wgrad_ksplit(M: int, N: int, K: int) -> int:
+    """The k-slice count the library gives a bf16 weight-gradient GEMM of this
+    shape (a function of the shape: fewer than 192 tiles of 256 x 256 take the
+    most slices, at most 8, that keep one round of 256 CUs and 1024 of k each)."""
+    tiles = -(-M // 256) * -(-N // 256)
+    if tiles >= 192:
+        return 1
+    ks = 1
+    while ks < 8 and tiles * (ks + 1) <= 256 and K // (ks + 1) >= 1024:
+        ks += 1
+    return ks
+
+
 def microbatch_bounds(tokens: int, microbatches: int) -> List[tuple]:
     """Contiguous token slices [lo, hi): the first tokens % microbatches
     slices hold one token more than the rest."""
@@ -139,6 +152,13 @@ class ShardedStep:
             self.shards.append(sh)
         self.normed = emp((T, H))
         self.rstd = emp((T,), f32)
+        # The fused update's w_in weight-gradient GEMM on K-contiguous operands: N and d_pre transposed
+        # ([H, T] once per step, [P, T] per shard in one shared buffer), when the library takes that path
+        # (no masters, T a multiple of 8, a k range the GEMM does not split).
+        self.normed_t = self.d_pre_t = None
+        if fused_sgd and not w.master and T % 8 == 0 and T > 0 and _wgrad_ksplit(P, H, T) == 1:
+            self.normed_t = emp((H, T))
+            self.d_pre_t = emp((P, T))
         self.out = emp((T, H))
         self.dN = self.shards[0]["dN_part"] if self.fuse else emp((T, H), f32)
         self.dx = emp((T, H))
@@ -252,6 +272,8 @@ class ShardedStep:
     def _shard_backward(self, sh, d_out, r: slice = slice(None), flags: int = 0, fused: Optional[dict] = None) -> None:
         T = self.T if r.start is None else r.stop - r.start
         grads = {} if fused else dict(d_w_in=sh["d_w_in"], d_w_down=sh["d_w_down"])
+        if fused and self.d_pre_t is not None:
+            grads.update(normed_t=self.normed_t, d_pre_t=self.d_pre_t)
         L.tp_mlp_backward(self._desc(flags, T), L.BWD_SHARD, stream=self.stream, normed=self.normed[r],
                           pre_act=sh["pre"][r], act=sh["act"][r], w_in=sh["w_in"], w_down=sh["w_down"],
                           d_out=d_out, d_pre=sh["d_pre"][r], d_b_in=sh["d_b_in"],
@@ -301,6 +323,8 @@ class ShardedStep:
         if fused_update and mode != "equivalence":
             raise ValueError("the fused update runs in equivalence mode only")
         self._fused_names = set()
+        if fused_update and self.normed_t is not None:
+            L.tp_mlp_transpose_bf16(self.normed, self.normed_t, T, H, stream=self.stream)
         for s, (sh, o) in enumerate(zip(self.shards, outs)):
             self._shard_backward(sh, o, fused=self._fused_update(s) if fused_update else None)
         if mode == "equivalence" or self.fuse:

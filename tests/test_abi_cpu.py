@@ -157,7 +157,8 @@ def test_backward_checks(lib):
     assert L.tp_mlp_workspace_bytes(_desc(T=0), L.BWD_SHARD) == 0
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd",
+                        "normed_t", "d_pre_t"):
             setattr(a, name, A)
     a.workspace_bytes = need - 16
     assert lib.tp_mlp_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EWORKSPACE
@@ -308,7 +309,8 @@ def test_fp8_checks(lib):
                                   None) == L.OK
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd",
+                        "normed_t", "d_pre_t"):
             setattr(a, name, A)
     a.d_b_in = None
     a.workspace_bytes = 1 << 30
@@ -394,7 +396,8 @@ def test_attention_checks(lib):
     assert need >= 4 * 2 * 64 * 4                              # delta [n_q, T] at least
     a = L.tp_attn_bwd_args()
     for name, _ in L.tp_attn_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd",
+                        "normed_t", "d_pre_t"):
             setattr(a, name, A)
     a.workspace_bytes = need - 16
     assert lib.tp_attn_backward(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), None) == L.EWORKSPACE
@@ -429,7 +432,7 @@ def test_backward_fused_sgd_checks(lib):
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
         if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd",
-                        "d_b_in"):
+                        "d_b_in", "normed_t", "d_pre_t"):
             setattr(a, name, A)
     a.workspace_bytes = L.tp_mlp_workspace_bytes(d, L.BWD_SHARD)
     f = L.tp_mlp_fused_sgd(lr=0.1, w_in_out=A, w_down_out=A)
@@ -458,6 +461,18 @@ def test_backward_fused_sgd_checks(lib):
     assert call() == L.EINVAL
     assert "d_pre" in L.tp_mlp_last_error()
     a.d_pre = A
+    # the transposed activations: bf16, T a multiple of 8, aligned, d_pre_t only with w_down_t
+    a.d_pre_t = A
+    assert call() == L.EINVAL and "w_down_t" in L.tp_mlp_last_error()
+    a.w_down_t = A
+    a.d_pre_t = MIS
+    assert call() == L.EALIGN
+    a.d_pre_t = A
+    a.normed_t = MIS
+    assert call() == L.EALIGN
+    a.normed_t = A
+    assert call(_desc(T=124)) == L.ESHAPE
+    a.d_pre_t = a.normed_t = a.w_down_t = None
     a.workspace_bytes = 1 << 30
     fp8 = L.make_fp8_args(1, **{n: A for n in L.FP8_META_FIELDS + L.FP8_CODE_FIELDS})
     assert lib.tp_mlp_backward_fp8(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), ctypes.byref(fp8), None) == L.EINVAL
@@ -471,7 +486,8 @@ def test_backward_norm_parts_checks(lib):
     d = _desc(T=128)
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
-        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd"):
+        if name not in ("workspace_bytes", "d_normed_parts", "n_d_normed_parts", "w_down_t", "w_in_t", "fused_sgd",
+                        "normed_t", "d_pre_t"):
             setattr(a, name, A)
     a.workspace_bytes = L.tp_mlp_workspace_bytes(d, L.BWD_NORM)
     a.n_d_normed_parts = 65

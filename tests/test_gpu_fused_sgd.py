@@ -8,8 +8,9 @@ same update arithmetic and the same rounding.  So the fused step is compared
 with the unfused one bit for bit, on every tensor both write, for shapes
 that cover one and several output tiles with ragged edges in both weight
 dimensions, no k split and k splits of 2 and 4 slices (few tiles, long T),
-SwiGLU and GeLU, fp32 masters, in-place and out-of-place updates; one case
-also goes through the C ABI with no transposed copy.  The unfused step is
+SwiGLU and GeLU, fp32 masters, in-place and out-of-place updates, and the
+path that forms the w_in update from N and d_pre transposed (dW_in^T, both
+operands K-contiguous); cases also go through the C ABI directly.  The unfused step is
 held to the oracle in test_gpu_parity.py; here one case is also compared
 with the fp64 oracle directly.
 """
@@ -63,6 +64,9 @@ CASES = [
     ("gelu_S1_master_inplace", 1000, 520, 600, 1, "gelu", True, False),
     ("gelu_S2_ksplit", 3000, 136, 2 * 264, 2, "gelu", False, False),
     ("swiglu_S2_inplace", 700, 264, 2 * 232, 2, "swiglu", False, False),
+    # T a multiple of 8, no masters, no k split: the w_in gradient GEMM on N^T and d_pre^T (dW_in^T)
+    ("swiglu_S2_nt_inplace", 704, 264, 2 * 232, 2, "swiglu", False, False),
+    ("gelu_S2_nt", 1000, 264, 2 * 264, 2, "gelu", False, True),
 ]
 
 
@@ -99,6 +103,10 @@ def test_fused_update_equals_unfused_bitwise(case):
             assert_same_bits(f"d_b_in.{s}", a["d_b_in"], b["d_b_in"])
     res = got.results()
     assert res["d_w_in"] is None and res["d_w_down"] is None  # applied, never written
+    nt = T % 8 == 0 and not master and name not in ("swiglu_S2_ksplit2", "gelu_S2_ksplit")
+    assert (got.d_pre_t is not None) == nt, name
+    if nt:  # the last shard's d_pre, transposed by the d_act GEMM's epilogue
+        assert_same_bits("d_pre_t", got.d_pre_t, got.shards[-1]["d_pre"].t().contiguous())
 
 
 def test_fused_update_against_oracle():
@@ -152,3 +160,65 @@ def test_fused_update_without_transposed_copies_abi(ksplit):
     assert_same_bits("w_down", wd1, wd0)
     assert_same_bits("d_pre", d_pre1, d_pre0)
     assert_same_bits("d_normed_part", dn1, dn0)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_transposed_activation_path_abi(act):
+    """Through the C ABI: d_pre_t is the exact transpose of d_pre, and the
+    w_in update formed from normed_t and d_pre_t (dW_in^T, both operands
+    K-contiguous) writes the bits of the unfused phase + tp_mlp_sgd_step_multi,
+    with the transposed target or without it."""
+    from tensor_transformer_mlp_rmsnorm_amd import _lib as L
+    T, H, F = 520, 264, 136  # ragged tiles in both weight dimensions, one k range
+    sw = act == "swiglu"
+    P = 2 * F if sw else F
+    dev = "cuda:0"
+    g = torch.Generator().manual_seed(4)
+    r = lambda *s, std=1.0: (torch.randn(*s, generator=g) * std).to(torch.bfloat16).to(dev)
+    normed, d_out = r(T, H), r(T, H)
+    pre, act_t = r(T, P), r(T, F)
+    w_in, w_down = r(P, H, std=0.05), r(H, F, std=0.05)
+    b_in = None if sw else r(F, std=0.05)
+    w_in_t, w_down_t = w_in.t().contiguous(), w_down.t().contiguous()
+    normed_t = normed.t().contiguous()
+    desc = L.make_desc(T, H, F, L.ACT_SWIGLU if sw else L.ACT_GELU, L.BF16, 1e-6, 0)
+    ws = torch.empty(L.tp_mlp_workspace_bytes(desc, L.BWD_SHARD), dtype=torch.uint8, device=dev)
+    f32 = lambda *s: torch.empty(*s, dtype=torch.float32, device=dev)
+    bf = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device=dev)
+    common = dict(normed=normed, pre_act=pre, act=act_t, w_in=w_in, w_down=w_down, d_out=d_out, workspace=ws,
+                  w_in_t=w_in_t, w_down_t=w_down_t)
+    d_pre0, dn0, gi, gd = bf(T, P), f32(T, H), f32(P, H), f32(H, F)
+    dbi = None if sw else f32(F)
+    L.tp_mlp_backward(desc, L.BWD_SHARD, d_pre=d_pre0, d_normed_part=dn0, d_w_in=gi, d_w_down=gd, d_b_in=dbi,
+                      **common)
+    wi0, wit0 = bf(P, H), bf(H, P)
+    L.tp_mlp_sgd_step_multi([(w_in, wi0, gi, None, None, w_in.numel(), wit0, P, H)], L.BF16, 0.1)
+    for targets in ("both", "plain_only"):
+        d_pre1, dn1, wi1, wit1, wd1, dpt = bf(T, P), f32(T, H), bf(P, H), bf(H, P), bf(H, F), bf(P, T)
+        fu = dict(lr=0.1, w_down_out=wd1, w_in_out=wi1)
+        if targets == "both":
+            fu["w_in_t_out"] = wit1
+        L.tp_mlp_backward(desc, L.BWD_SHARD, d_pre=d_pre1, d_normed_part=dn1, d_b_in=None if sw else f32(F),
+                          normed_t=normed_t, d_pre_t=dpt, fused_sgd=fu, **common)
+        torch.cuda.synchronize()
+        assert_same_bits("d_pre", d_pre1, d_pre0)
+        assert_same_bits("d_pre_t", dpt, d_pre0.t().contiguous())
+        assert_same_bits("d_normed_part", dn1, dn0)
+        assert_same_bits("w_in " + targets, wi1, wi0)
+        if targets != "plain_only":
+            assert_same_bits("w_in_t " + targets, wit1, wit0)
+
+
+@pytest.mark.parametrize("shape", [(8, 8), (72, 136), (520, 264), (4096, 1792), (8192, 4096)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_transpose_bf16_exact(shape):
+    """tp_mlp_transpose_bf16 (the step's N^T, the weights' first transposed copies): every element moved bit for
+    bit, ragged 64 x 64 tiles included."""
+    from tensor_transformer_mlp_rmsnorm_amd import _lib as L
+    R, C = shape
+    g = torch.Generator().manual_seed(R + C)
+    x = torch.randn(R, C, generator=g).to(torch.bfloat16).to("cuda:0")
+    out = torch.full((C, R), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    L.tp_mlp_transpose_bf16(x, out, R, C)
+    torch.cuda.synchronize()
+    assert_same_bits("transpose", out, x.t().contiguous())
