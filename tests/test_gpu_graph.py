@@ -40,10 +40,18 @@ CASES = [
     # one shard: the fused residual epilogue, the GeLU path and its bias gradient
     ("graph_gelu_bf16_s1", dict(tokens=260, hidden=192, ffn_full=320, shards=1, act="gelu", dtype="bf16")),
     ("graph_swiglu_fp32_s2", dict(tokens=64, hidden=64, ffn_full=128, shards=2, act="swiglu", dtype="fp32")),
+    # the benchmark's form of the step: the weight matrices' update fused into their gradient GEMMs, the gate/up
+    # weight gradient on N^T and d_pre^T (T a multiple of 8, one k range), and with k split (the slices' update)
+    ("graph_swiglu_bf16_s2_fused", dict(tokens=304, hidden=264, ffn_full=560, shards=2, act="swiglu", dtype="bf16",
+                                        fused=True)),
+    ("graph_swiglu_bf16_s2_fused_ksplit", dict(tokens=2504, hidden=264, ffn_full=560, shards=2, act="swiglu",
+                                               dtype="bf16", fused=True)),
 ]
 
 
 def _equal(a, b) -> bool:
+    if a is None or b is None:
+        return a is None and b is None
     if isinstance(a, list):
         return len(a) == len(b) and all(_equal(x, y) for x, y in zip(a, b))
     return torch.equal(a, b)
@@ -53,11 +61,13 @@ def _equal(a, b) -> bool:
 def test_graph_replays_equal_eager_steps(name, kw):
     from tensor_transformer_mlp_rmsnorm_amd.step import ShardedStep
 
+    kw = dict(kw)
+    fused = kw.pop("fused", False)
     w = synth.Workload(name, w_std=0.05, seed=31, **kw)
     t = synth.draw(w)
-    say(f"[gpu] {name}: T={w.tokens} H={w.hidden} F_full={w.ffn_full} S={w.shards} {w.act} {w.dtype}")
-    st = ShardedStep(w, t, out_of_place_sgd=True)
-    ref = ShardedStep(w, t, out_of_place_sgd=True)
+    say(f"[gpu] {name}: T={w.tokens} H={w.hidden} F_full={w.ffn_full} S={w.shards} {w.act} {w.dtype} fused={fused}")
+    st = ShardedStep(w, t, out_of_place_sgd=True, fused_sgd=fused)
+    ref = ShardedStep(w, t, out_of_place_sgd=True, fused_sgd=fused)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
