@@ -282,7 +282,7 @@ def fp8_path(w, t, steps: int, warmup: int) -> dict:
     from tensor_transformer_mlp_rmsnorm_amd import _lib as L
     from tensor_transformer_mlp_rmsnorm_amd.step import Fp8Step
 
-    st = Fp8Step(w, t, device="cuda:0", out_of_place_sgd=True)
+    st = Fp8Step(w, t, device="cuda:0", out_of_place_sgd=True, fused_sgd=True)
     for _ in range(max(1, warmup)):
         st.step()
     torch.cuda.synchronize()

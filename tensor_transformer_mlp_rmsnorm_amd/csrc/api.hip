@@ -1012,9 +1012,32 @@ int tp_mlp_backward_fp8(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_ar
                   a->workspace ? a->workspace_bytes : (size_t)0);
     if (!aligned16(a->workspace)) return fail(TP_MLP_EALIGN, "%s: workspace is not 16-byte aligned", fn);
   }
-  if (a->fused_sgd) return fail(TP_MLP_EINVAL, "%s: fused_sgd is not taken by the FP8 backward", fn);
-  REQUIRE_PTR(a->d_w_in);
-  REQUIRE_PTR(a->d_w_down);
+  const tp_mlp_fused_sgd* fu = a->fused_sgd;
+  if (fu) {
+    if (accum) return fail(TP_MLP_EINVAL, "%s: fused_sgd with TP_MLP_ACCUMULATE_GRADS", fn);
+    if (!std::isfinite(fu->lr)) return fail(TP_MLP_EINVAL, "%s: fused_sgd->lr is not finite", fn);
+    REQUIRE_PTR(fu->w_in_out);
+    REQUIRE_PTR(fu->w_down_out);
+    if (fu->w_in_t_out && !aligned16(fu->w_in_t_out))
+      return fail(TP_MLP_EALIGN, "%s: 'fused_sgd->w_in_t_out' is not 16-byte aligned", fn);
+    if (fu->w_down_t_out && !aligned16(fu->w_down_t_out))
+      return fail(TP_MLP_EALIGN, "%s: 'fused_sgd->w_down_t_out' is not 16-byte aligned", fn);
+    if (fu->w_in_master) {
+      REQUIRE_PTR(fu->w_in_master);
+      REQUIRE_PTR(fu->w_in_master_out);
+    } else {
+      REQUIRE_PTR(a->w_in);  // the old values
+    }
+    if (fu->w_down_master) {
+      REQUIRE_PTR(fu->w_down_master);
+      REQUIRE_PTR(fu->w_down_master_out);
+    } else {
+      REQUIRE_PTR(a->w_down);
+    }
+  } else {
+    REQUIRE_PTR(a->d_w_in);
+    REQUIRE_PTR(a->d_w_down);
+  }
   if (!swiglu) REQUIRE_PTR(a->d_b_in);
   if (swiglu && a->d_b_in) return fail(TP_MLP_EINVAL, "%s: d_b_in must be NULL for SwiGLU", fn);
   REQUIRE_META(f8->meta_normed);
@@ -1061,7 +1084,14 @@ int tp_mlp_backward_fp8(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_ar
   b2.ksplit = gemm_ksplit(b2.M, b2.N, b2.K);
   b2.ws = static_cast<float*>(a->workspace);
   b2.accum = accum;
-  CHECK_HIP(launch_gemm_fp8(kFp8E5M2, kFp8E4M3, kEpiStoreF32, b2, s), "d_w_down GEMM");
+  // With the update fused it is applied here (the FP8 GEMMs read the weights' codes, cast before the
+  // step, so an in-place update of the bf16 weights needs no ordering).
+  if (fu) {
+    b2.tag = "gemm_wgrad_down_sgd_fp8";
+    b2.sgd = SgdEpi{a->w_down, nullptr, fu->w_down_out, fu->w_down_t_out, fu->w_down_master, fu->w_down_master_out,
+                    fu->lr};
+  }
+  CHECK_HIP(launch_gemm_fp8(kFp8E5M2, kFp8E4M3, fu ? kEpiSgd : kEpiStoreF32, b2, s), "d_w_down GEMM");
 
   CHECK_HIP(launch_fp8_cast(kFp8E5M2, a->d_pre, T, P, f8->d_pre_q, f8->d_pre_t, Tp, f8->meta_d_pre,
                             "fp8_cast_d_pre", s),
@@ -1075,7 +1105,11 @@ int tp_mlp_backward_fp8(const tp_mlp_desc* d, int32_t phase, const tp_mlp_bwd_ar
   b4.ksplit = gemm_ksplit(b4.M, b4.N, b4.K);
   b4.ws = static_cast<float*>(a->workspace);
   b4.accum = accum;
-  CHECK_HIP(launch_gemm_fp8(kFp8E5M2, kFp8E4M3, kEpiStoreF32, b4, s), "d_w_in GEMM");
+  if (fu) {
+    b4.tag = swiglu ? "gemm_wgrad_gate_up_sgd_fp8" : "gemm_wgrad_fc1_sgd_fp8";
+    b4.sgd = SgdEpi{a->w_in, nullptr, fu->w_in_out, fu->w_in_t_out, fu->w_in_master, fu->w_in_master_out, fu->lr};
+  }
+  CHECK_HIP(launch_gemm_fp8(kFp8E5M2, kFp8E4M3, fu ? kEpiSgd : kEpiStoreF32, b4, s), "d_w_in GEMM");
 
   if (!swiglu)
     CHECK_HIP(launch_colsum(kBF16, a->d_pre, a->d_b_in, a->workspace, T, F, accum, s), "d_b_in column sum");

@@ -831,6 +831,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
   if constexpr (EPI == kEpiSgdT) {
     epilogue_sgd<kBM, PT::TN, WMB, WNB, kThreads, false, true>(g, acc, tile_m0, tile_n0, PT::row0(wave),
                                                                PT::col0(wave), lane, smem);
+  } else if constexpr (EPI == kEpiSgd) {  // (the FP8 weight gradients)
+    if (g.sgd.m_in)
+      epilogue_sgd<kBM, PT::TN, WMB, WNB, kThreads, true, false>(g, acc, tile_m0, tile_n0, PT::row0(wave),
+                                                                 PT::col0(wave), lane, smem);
+    else
+      epilogue_sgd<kBM, PT::TN, WMB, WNB, kThreads, false, false>(g, acc, tile_m0, tile_n0, PT::row0(wave),
+                                                                  PT::col0(wave), lane, smem);
   } else if constexpr (EPI == kEpiSwigluBwdT || EPI == kEpiGeluBwdT) {
     // the activation backward, then d_pre transposed (gate rows, then up rows) through LDS
     constexpr int kBase = EPI == kEpiSwigluBwdT ? kEpiSwigluBwd : kEpiGeluBwd;
@@ -1202,6 +1209,7 @@ hipError_t launch_gemm_fp8(int fmt_a, int fmt_b, Epi epi, const GemmArgs& g, hip
     using OP = PpFp8<kFp8E5M2, kFp8E4M3>;
     switch (epi) {
       case kEpiStoreF32: return launch_t<true, true, kEpiStoreF32, OP>(g, s);
+      case kEpiSgd: return launch_t<true, true, kEpiSgd, OP>(g, s);
       case kEpiSwigluBwd: return launch_t<true, true, kEpiSwigluBwd, OP>(g, s);
       case kEpiGeluBwd: return launch_t<true, true, kEpiGeluBwd, OP>(g, s);
       default: break;

@@ -255,14 +255,15 @@ class ShardedStep:
             L.tp_partial_sum([sh["z"] for sh in self.shards], T, H, self.x, self.b_down, self.cdt, self.out,
                              self.cdt, stream=st)
 
-    def _fused_update(self, s: int) -> dict:
+    def _fused_update(self, s: int, transposed: bool = True) -> dict:
         """The tp_mlp_fused_sgd fields of shard s: its w_in and w_down updated
-        into the same targets (and transposed copies, masters) as sgd()."""
+        into the same targets (and transposed copies, masters) as sgd();
+        without ``transposed`` the transposed copies are not written."""
         f = {"lr": self.w.lr}
         for key in ("w_in", "w_down"):
             name = f"{key}.{s}"
             f[key + "_out"] = self.new[name]
-            f[key + "_t_out"] = self.new_t[name][0] if name in self.new_t else None
+            f[key + "_t_out"] = self.new_t[name][0] if (transposed and name in self.new_t) else None
             if self.masters is not None:
                 f[key + "_master"] = self.masters[name]
                 f[key + "_master_out"] = self.new_masters[name]
@@ -556,10 +557,11 @@ class Fp8Step(ShardedStep):
              ("meta_w_down", L.FP8_E4M3), ("meta_d_out", L.FP8_E5M2), ("meta_d_pre", L.FP8_E5M2))
 
     def __init__(self, w, tensors, device="cuda", out_of_place_sgd: bool = False, stream=None,
-                 history_len: int = 16):
+                 history_len: int = 16, fused_sgd: bool = False):
         if w.dtype != "bf16":
             raise ValueError("the FP8 step takes bf16 tensors")
-        super().__init__(w, tensors, device, out_of_place_sgd, stream)
+        super().__init__(w, tensors, device, out_of_place_sgd, stream, fused_sgd=fused_sgd)
+        self.normed_t = self.d_pre_t = None  # the FP8 GEMMs read codes (their transposes come with the casts)
         T, H, F = self.T, self.H, self.F
         P, Tp = (2 * F if self.swiglu else F), (T + 15) // 16 * 16
         u8 = lambda shape: torch.empty(shape, dtype=torch.uint8, device=self.dev)
@@ -590,17 +592,23 @@ class Fp8Step(ShardedStep):
             L.tp_partial_sum([sh["z"] for sh in self.shards], T, H, self.x, self.b_down, self.cdt, self.out,
                              self.cdt, stream=st)
 
-    def backward(self, mode: str = "equivalence") -> None:
+    def backward(self, mode: str = "equivalence", fused_update: bool = False) -> None:
+        """With ``fused_update`` the weight matrices' SGD update is taken in
+        their FP8 weight-gradient GEMMs (their bf16 transposed copies, which
+        the FP8 GEMMs do not read, are not written)."""
         if mode != "equivalence":
             raise ValueError("the FP8 step runs in equivalence mode")
         T, H = self.T, self.H
+        self._fused_names = set()
         for s, sh in enumerate(self.shards):
             flags = L.FP8_SHARED_READY if s > 0 else 0
+            grads = dict(fused_sgd=self._fused_update(s, transposed=False)) if fused_update else \
+                dict(d_w_in=sh["d_w_in"], d_w_down=sh["d_w_down"])
             L.tp_mlp_backward_fp8(self._desc(flags), L.BWD_SHARD, sh["f8"], stream=self.stream,
                                   normed=self.normed, pre_act=sh["pre"], act=sh["act"], w_in=sh["w_in"],
-                                  w_down=sh["w_down"], d_out=self.out, d_pre=sh["d_pre"], d_w_in=sh["d_w_in"],
-                                  d_b_in=sh["d_b_in"], d_w_down=sh["d_w_down"], d_normed_part=sh["dN_part"],
-                                  workspace=self.workspace)
+                                  w_down=sh["w_down"], d_out=self.out, d_pre=sh["d_pre"],
+                                  d_b_in=sh["d_b_in"], d_normed_part=sh["dN_part"],
+                                  workspace=self.workspace, **grads)
         # the backward boundary: the shards' partials summed inside the RMSNorm backward
         parts = None if self.fuse else [sh["dN_part"] for sh in self.shards]
         self._norm_backward(self.dN, self.out, self.dx, self.d_norm_w, self.d_b_down, parts=parts)
@@ -613,7 +621,7 @@ class Fp8Step(ShardedStep):
         if microbatches != 1:
             raise ValueError("the FP8 step takes the whole batch")
         self.forward(mode)
-        self.backward(mode)
+        self.backward(mode, fused_update=self.fused_sgd and update)
         if update:
             self.sgd()
         self.update_scales()

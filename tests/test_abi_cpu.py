@@ -426,8 +426,8 @@ def test_attention_checks(lib):
 def test_backward_fused_sgd_checks(lib):
     """The SHARD phase with the update fused (tp_mlp_fused_sgd): bf16 only,
     not with accumulated gradients, targets present and aligned, a master's
-    output given with it, and the gradients then optional; the FP8 backward
-    refuses it.  All checked before any launch."""
+    output given with it, and the gradients then optional; the same checks in
+    the FP8 backward.  All checked before any launch."""
     d = _desc(T=128)
     a = L.tp_mlp_bwd_args()
     for name, _ in L.tp_mlp_bwd_args._fields_:
@@ -475,8 +475,14 @@ def test_backward_fused_sgd_checks(lib):
     a.d_pre_t = a.normed_t = a.w_down_t = None
     a.workspace_bytes = 1 << 30
     fp8 = L.make_fp8_args(1, **{n: A for n in L.FP8_META_FIELDS + L.FP8_CODE_FIELDS})
+    # the FP8 backward takes the fused update too: with no master it reads the old w_in, which must be given
+    a.w_in = None
     assert lib.tp_mlp_backward_fp8(ctypes.byref(d), L.BWD_SHARD, ctypes.byref(a), ctypes.byref(fp8), None) == L.EINVAL
-    assert "fused_sgd" in L.tp_mlp_last_error()
+    assert "w_in" in L.tp_mlp_last_error()
+    a.w_in = A
+    d_acc = _desc(T=128, flags=L.ACCUMULATE_GRADS)
+    assert lib.tp_mlp_backward_fp8(ctypes.byref(d_acc), L.BWD_SHARD, ctypes.byref(a), ctypes.byref(fp8),
+                                   None) == L.EINVAL
 
 
 def test_backward_norm_parts_checks(lib):

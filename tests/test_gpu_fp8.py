@@ -474,3 +474,45 @@ def test_fp8_full_size_sampled():
             assert abs(h[0] - m.history[0]) <= 2e-2 * abs(m.history[0]), (k, h[0], m.history[0])
     del st
     torch.cuda.empty_cache()
+
+
+FUSED = [
+    ("swiglu_S2_ragged", 200, 144, 2 * 144, 2, "swiglu"),
+    ("gelu_S1_ksplit", 2500, 272, 272, 1, "gelu"),
+    ("llama3_8b_tp8", None, None, None, None, None),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[c[0] for c in FUSED])
+def test_fp8_fused_update_equals_unfused_bitwise(case):
+    """The FP8 step with the weight matrices' update taken in their FP8
+    weight-gradient GEMMs (as bench.py times it) against the FP8 step that
+    writes the gradients and runs the SGD kernels: the same fp32 gradients,
+    the same update, so the new parameters and every other output are the same
+    bits, over two steps (cold, then warm metas)."""
+    from tensor_transformer_mlp_rmsnorm_amd.step import Fp8Step
+    name, T, H, Ff, S, act = case
+    if T is None:
+        w = synth.workload(name)
+    else:
+        w = synth.Workload("fp8_fused_" + name, tokens=T, hidden=H, ffn_full=Ff, shards=S, act=act, dtype="bf16",
+                           w_std=0.05, seed=700 + T)
+    t = synth.draw(w, perturb=T is not None)
+    say(f"[gpu] fp8 fused update {name} T={w.tokens} H={w.hidden} F_full={w.ffn_full} S={w.shards} {w.act}")
+    ref = Fp8Step(w, t, out_of_place_sgd=False, history_len=8)
+    got = Fp8Step(w, t, out_of_place_sgd=False, history_len=8, fused_sgd=True)
+    bits = lambda x: x.view(torch.int16 if x.element_size() == 2 else torch.int32)
+    for step in range(2):
+        ref.step()
+        got.step()
+        torch.cuda.synchronize()
+        for pname, _ in ref._param_list():
+            diff = int((bits(got.new[pname]) != bits(ref.new[pname])).sum())
+            assert diff == 0, (step, pname, diff)
+        for attr in ("out", "dx", "d_norm_w", "d_b_down"):
+            assert torch.equal(bits(getattr(got, attr)), bits(getattr(ref, attr))), (step, attr)
+        for k in ("meta_w_in", "meta_d_pre", "meta_act"):
+            assert torch.equal(got.metas[k], ref.metas[k]), (step, k)
+    say(f"  two steps, {len(ref._param_list())} parameters: same bits")
+    del ref, got
+    torch.cuda.empty_cache()
