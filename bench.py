@@ -410,7 +410,7 @@ def sequence_parallel_timing(w, t, steps: int, warmup: int) -> dict:
     import torch
     from tensor_transformer_mlp_rmsnorm_amd.step import SequenceParallelStep
 
-    sp = SequenceParallelStep(w, t, device="cuda:0", out_of_place_sgd=True)
+    sp = SequenceParallelStep(w, t, device="cuda:0", out_of_place_sgd=True, fused_sgd=fused_update(w))
     for _ in range(max(1, warmup)):
         sp.step()
     torch.cuda.synchronize()

@@ -477,8 +477,9 @@ class SequenceParallelStep(ShardedStep):
 
     MODES = ("equivalence", "missing_norm_grad_reduce")
 
-    def __init__(self, w, tensors, device="cuda", out_of_place_sgd: bool = False, stream=None):
-        super().__init__(w, tensors, device, out_of_place_sgd, stream)
+    def __init__(self, w, tensors, device="cuda", out_of_place_sgd: bool = False, stream=None,
+                 fused_sgd: bool = False):
+        super().__init__(w, tensors, device, out_of_place_sgd, stream, fused_sgd=fused_sgd)
         if w.n_run != w.shards:
             raise ValueError("the sequence-parallel step runs every rank")
         S, H = w.shards, self.H
@@ -504,12 +505,15 @@ class SequenceParallelStep(ShardedStep):
             L.tp_partial_sum([sh["z"][lo:hi] for sh in self.shards], hi - lo, H, self.x[lo:hi], self.b_down, self.cdt,
                              self.out[lo:hi], self.cdt, stream=st)
 
-    def backward(self, mode: str = "equivalence") -> None:
+    def backward(self, mode: str = "equivalence", fused_update: bool = False) -> None:
         if mode not in self.MODES:
             raise ValueError(mode)
-        H = self.H
-        for sh in self.shards:
-            self._shard_backward(sh, self.out)
+        T, H = self.T, self.H
+        self._fused_names = set()
+        if fused_update and self.normed_t is not None:
+            L.tp_mlp_transpose_bf16(self.normed, self.normed_t, T, H, stream=self.stream)
+        for s, sh in enumerate(self.shards):
+            self._shard_backward(sh, self.out, fused=self._fused_update(s) if fused_update else None)
         for r, (lo, hi) in enumerate(self.slices):
             # the reduce-scatter of dN: each rank's rows of the partials, summed inside its RMSNorm backward
             parts = None if self.fuse else [sh["dN_part"][lo:hi] for sh in self.shards]
@@ -527,7 +531,7 @@ class SequenceParallelStep(ShardedStep):
         if microbatches != 1:
             raise ValueError("the sequence-parallel step takes the whole batch")
         self.forward(mode)
-        self.backward(mode)
+        self.backward(mode, fused_update=self.fused_sgd and update and mode == "equivalence")
         if update and mode == "equivalence":
             self.sgd()
 

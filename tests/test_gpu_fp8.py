@@ -296,7 +296,7 @@ def test_fp8_backward_strict(act):
     """The backward's d_act GEMM with the activation backward fused, and the
     down-weight gradient, on codes of given tensors (d_out, act, the weights):
     d_pre within the bf16 tolerance, d_w_down within the FP8 GEMM bound, the
-    d_out codes bit for bit.  The two GEMMs on the codes of d_pre follow the
+    d_out codes and d_pre's codes (formed in the d_act epilogue) bit for bit.  The two GEMMs on the codes of d_pre follow the
     step criterion (d_pre is computed, its codes can flip)."""
     from tensor_transformer_mlp_rmsnorm_amd import _lib as L
     T, H, F = 136, 256, 144
@@ -364,6 +364,14 @@ def test_fp8_backward_strict(act):
     if act == "gelu":
         check("d_b_in", outs["d_b_in"].cpu(), np.sum(dP, axis=0), "bf16", report=report)
     assert metas["d_out"].cpu().numpy()[2] == np.float32(np.abs(dy).max())
+    # d_pre's codes, formed in the d_act GEMM's epilogue: the oracle's quantisation of the stored d_pre, bit for
+    # bit (row copy, transposed copy, zero padding columns T .. Tp-1), and its amax in the meta
+    dp_gpu = outs["d_pre"].cpu().double().numpy()
+    dpq_gpu = fp8.quantize(dp_gpu, sc["d_pre"], fp8.E5M2)
+    np.testing.assert_array_equal(codes["d_pre_q"].cpu().numpy(), dpq_gpu)
+    np.testing.assert_array_equal(codes["d_pre_t"].cpu().numpy()[:, :T], dpq_gpu.T)
+    assert np.all(codes["d_pre_t"].cpu().numpy()[:, T:] == 0)
+    assert metas["d_pre"].cpu().numpy()[2] == np.float32(np.abs(dp_gpu).max())
     say(f"  worst: {report}")
 
 

@@ -122,3 +122,31 @@ def test_sequence_parallel_full_size_sampled():
               "new_w_down_chans", "new_w_in_chans"):
         check(k, got[k], ref[k], w.dtype, report=report)
     say(f"  worst: {max(report.items(), key=lambda kv: kv[1])}")
+
+
+@pytest.mark.parametrize("name", ["small", "llama3_8b_tp8"])
+def test_sequence_parallel_fused_update_bitwise(name):
+    """The sequence-parallel step as bench.py times it (the weight matrices' update taken in their
+    weight-gradient GEMMs) gives the parameters, out and dx of the step that writes the gradients."""
+    from tensor_transformer_mlp_rmsnorm_amd.step import SequenceParallelStep
+    if name == "small":
+        w = synth.Workload("sp_fused_small", tokens=520, hidden=264, ffn_full=4 * 136, shards=4, act="swiglu",
+                           dtype="bf16", w_std=0.05, seed=9)
+    else:
+        w = synth.workload(name)
+    t = synth.draw(w)
+    say(f"[gpu] sp fused update {w.name} T={w.tokens} H={w.hidden} F_full={w.ffn_full} S={w.shards}")
+    ref = SequenceParallelStep(w, t, out_of_place_sgd=True)
+    got = SequenceParallelStep(w, t, out_of_place_sgd=True, fused_sgd=True)
+    ref.step()
+    got.step()
+    torch.cuda.synchronize()
+    bits = lambda x: x.view(torch.int16 if x.element_size() == 2 else torch.int32)
+    for pname, _ in ref._param_list():
+        assert torch.equal(bits(got.new[pname]), bits(ref.new[pname])), pname
+    for key, (tt, _, _) in ref.new_t.items():
+        assert torch.equal(bits(got.new_t[key][0]), bits(tt)), key
+    for attr in ("out", "dx", "d_norm_w", "d_b_down"):
+        assert torch.equal(bits(getattr(got, attr)), bits(getattr(ref, attr))), attr
+    del ref, got
+    torch.cuda.empty_cache()
