@@ -222,3 +222,20 @@ def test_transpose_bf16_exact(shape):
     L.tp_mlp_transpose_bf16(x, out, R, C)
     torch.cuda.synchronize()
     assert_same_bits("transpose", out, x.t().contiguous())
+
+
+@pytest.mark.parametrize("master", [False, True], ids=["plain", "masters"])
+def test_fused_update_empty_tokens(master):
+    """T = 0 with the update fused: every weight gradient is an empty sum, so the fused update (a GEMM with
+    no k) writes back the parameters, their transposed copies and masters unchanged."""
+    w = synth.Workload("fused_empty", tokens=0, hidden=64, ffn_full=128, shards=2, act="swiglu", dtype="bf16",
+                       w_std=0.05, seed=3, master=master)
+    t = synth.draw(w, perturb=True)
+    st = _run(w, t, True, fused=True)
+    for s, sh in enumerate(st.shards):
+        for key in ("w_in", "w_down"):
+            name = f"{key}.{s}"
+            assert_same_bits("new " + name, st.new[name], sh[key])
+            assert_same_bits("transposed " + name, st.new_t[name][0], sh[key + "_t"])
+            if master:
+                assert_same_bits("master " + name, st.new_masters[name], st.masters[name])
