@@ -169,6 +169,9 @@ int forward_checked(const tp_mlp_desc* d, const void* x, const void* norm_w, con
   c.bias = b_down;
   c.ffn = F;
   c.tag = fuse ? "gemm_down_residual" : "gemm_down_partial";
+  // short k (F <= 2048): tiles grouped by 2 tile rows instead of 4 (measured 116.8 -> 108.5 us at T 8192,
+  // H 4096, F 1792; at F 3584 no change, at F 14336 slower)
+  c.tile_group = F <= 2048 ? 2 : 0;
   if (ks > 1) {
     // k split: the slices go to the workspace and are added in index order
     c.ksplit = ks;

@@ -240,20 +240,21 @@ __device__ __forceinline__ uint4 read_frag(const uint4* __restrict__ lds, int ro
 
 // blockIdx -> (tile_m, tile_n, k slice): each of the 8 XCDs gets a contiguous
 // range of ids (workgroups are dealt round-robin over XCDs); k slices are the
-// slowest index, tiles inside a slice are grouped by 4 tile-rows.
-__device__ __forceinline__ void tile_coords(int pid, int ntm, int ntn, int nks, int& tm, int& tn, int& ks) {
+// slowest index, tiles inside a slice are grouped by `group` tile-rows (0: 4).
+__device__ __forceinline__ void tile_coords(int pid, int ntm, int ntn, int nks, int group, int& tm, int& tn,
+                                            int& ks) {
   const int ntiles = ntm * ntn, total = ntiles * nks;
   const int xcd = pid & 7, local = pid >> 3;
   const int per = total >> 3, rem = total & 7;
   const int lin = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
   ks = lin / ntiles;
   const int tile = lin - ks * ntiles;
-  constexpr int kGroup = 4;
-  const int in_group = kGroup * ntn;
-  const int group = tile / in_group;
-  const int first_m = group * kGroup;
-  const int gsize = min(ntm - first_m, kGroup);
-  const int t = tile - group * in_group;
+  const int kg = group > 0 ? group : 4;
+  const int in_group = kg * ntn;
+  const int gi = tile / in_group;
+  const int first_m = gi * kg;
+  const int gsize = min(ntm - first_m, kg);
+  const int t = tile - gi * in_group;
   tm = first_m + t % gsize;
   tn = t / gsize;
 }
@@ -760,7 +761,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_pingpong_kernel(GemmArgs 
   const int wm = wave >> 2, q = wave & 3;
 
   int tm, tn, ks;
-  tile_coords(blockIdx.x, ntm, ntn, g.ksplit, tm, tn, ks);
+  tile_coords(blockIdx.x, ntm, ntn, g.ksplit, g.tile_group, tm, tn, ks);
   const int64_t K = g.K;
   const int64_t kper = ((K + (int64_t)g.ksplit * kK - 1) / ((int64_t)g.ksplit * kK)) * kK;
   const int64_t kbeg = (int64_t)ks * kper;
@@ -877,7 +878,7 @@ __global__ __launch_bounds__(SH::NW * 64, 1) void gemm_bf16_kernel(GemmArgs g, i
   static_assert(SH::NW / SH::GN * SH::WMB * 16 == SH::TM && SH::GN * SH::WNB * 16 == SH::TN, "waves cover the tile");
 
   int tm, tn, ks;
-  tile_coords(blockIdx.x, ntm, ntn, g.ksplit, tm, tn, ks);
+  tile_coords(blockIdx.x, ntm, ntn, g.ksplit, g.tile_group, tm, tn, ks);
 
   const bf16_t* __restrict__ A = static_cast<const bf16_t*>(g.A);
   const bf16_t* __restrict__ B = static_cast<const bf16_t*>(g.B);
@@ -962,7 +963,7 @@ __global__ __launch_bounds__(SH::NW * 64, 1) void gemm_bf16_pipe_kernel(GemmArgs
   const int wm = wave / SH::GN, wn = wave % SH::GN;
 
   int tm, tn, ks;
-  tile_coords(blockIdx.x, ntm, ntn, g.ksplit, tm, tn, ks);
+  tile_coords(blockIdx.x, ntm, ntn, g.ksplit, g.tile_group, tm, tn, ks);
   const bf16_t* __restrict__ A = static_cast<const bf16_t*>(g.A);
   const bf16_t* __restrict__ B = static_cast<const bf16_t*>(g.B);
   const int64_t K = g.K;

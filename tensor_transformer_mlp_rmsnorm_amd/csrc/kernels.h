@@ -96,6 +96,11 @@ struct GemmArgs {
   // multiple of 8); the up half's rows follow the gate half's
   void* pre_t;
   int64_t ld_t;
+  // bf16 GEMMs: tile rows per group in the order workgroups take tiles (0: 4).
+  // Each XCD takes a contiguous run of tiles, row by row inside groups of
+  // this many tile rows, which sets how many operand strips one round of an
+  // XCD's workgroups shares; the best value depends on the shape (measured).
+  int tile_group;
 };
 
 // Number of k-slices for a bf16 fp32-output GEMM: a function of the shape only
